@@ -1,0 +1,230 @@
+"""Seeded synthetic inputs for the ReplaySSM decode path.
+
+This module is the one place that both the HIP path (through the tests and
+bench.py) and the CPU oracle take their inputs from.  It holds random draws
+and storage rounding only -- no step of the method.
+
+Generator
+---------
+Counter-based SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014): element ``i`` of a stream with key ``K`` is
+``mix64(K + (i + 1) * 0x9E3779B97F4A7C15)``.  Uniforms take the top 53 bits,
+``(u >> 11) + 0.5`` times 2^-53, so they lie strictly inside (0, 1).  Normals
+use Box-Muller on the uniform pair (2m, 2m+1): even indices take the cosine
+branch and odd indices the sine branch.  Because every element is a pure
+function of (key, index), any slice of a tensor (a few sequences of a large
+batch, one step of a long run) is generated on its own and equals the same
+slice of the whole tensor.
+
+Keys: ``mix64(config * 2**32 + layer * 2**8 + tensor)`` with the tensor ids in
+``TENSOR``.
+
+Value distributions (the tiny single-layer workload of the task states them;
+every workload here uses them):
+  q, k ~ N(0, 1/N)   v ~ N(0, 1)   dt = softplus(x), x ~ N(0, 1)
+  A_h = -exp(u), u ~ U(0, 1), one per (layer, head), constant over batch/time
+  a = exp(dt * A_h), evaluated in float64 from the stored float32 dt and
+  rounded once to float32.
+q, k, v are rounded once to the storage dtype ("f32" or "bf16", round to
+nearest even); dt and a are float32.  bf16 tensors are returned as their raw
+16-bit patterns (numpy uint16).
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+TENSOR = {"A": 0, "q": 1, "k": 2, "v": 3, "dt": 4, "accept": 5, "S0": 6}
+
+# workload ids used in the keys (one per named workload)
+CONFIG_ID = {"tiny": 0, "decode": 1, "verify": 2, "dual": 3, "stacked": 4, "misc": 9}
+
+
+def _mix64(z: np.ndarray) -> np.ndarray:
+    z = z.astype(np.uint64, copy=True)
+    with np.errstate(over="ignore"):
+        z ^= z >> np.uint64(30)
+        z *= _M1
+        z ^= z >> np.uint64(27)
+        z *= _M2
+        z ^= z >> np.uint64(31)
+    return z
+
+
+def mix64_scalar(x: int) -> int:
+    return int(_mix64(np.array([x & 0xFFFFFFFFFFFFFFFF], dtype=np.uint64))[0])
+
+
+def stream_key(config: int, layer: int, tensor: str) -> int:
+    return mix64_scalar(config * (1 << 32) + layer * (1 << 8) + TENSOR[tensor])
+
+
+def _u64(key: int, idx: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        z = np.uint64(key) + (idx.astype(np.uint64) + np.uint64(1)) * GAMMA
+    return _mix64(z)
+
+
+def uniform(key: int, idx: np.ndarray) -> np.ndarray:
+    """float64 uniforms in (0, 1) at the given stream indices."""
+    u = _u64(key, idx) >> np.uint64(11)
+    return (u.astype(np.float64) + 0.5) * (2.0 ** -53)
+
+
+def _normal_block(key: int, idx: np.ndarray) -> np.ndarray:
+    idx = idx.astype(np.uint64)
+    pair = idx >> np.uint64(1)
+    u1 = uniform(key, pair * np.uint64(2))
+    u2 = uniform(key, pair * np.uint64(2) + np.uint64(1))
+    r = np.sqrt(-2.0 * np.log(u1))
+    th = (2.0 * math.pi) * u2
+    odd = (idx & np.uint64(1)).astype(bool)
+    return np.where(odd, r * np.sin(th), r * np.cos(th))
+
+
+_POOL = None
+
+
+def _pool() -> ThreadPoolExecutor:
+    global _POOL
+    if _POOL is None:
+        _POOL = ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4))
+    return _POOL
+
+
+def normal(key: int, idx: np.ndarray) -> np.ndarray:
+    """float64 standard normals at the given stream indices (any shape)."""
+    flat = np.ascontiguousarray(idx).reshape(-1)
+    n = flat.size
+    if n < (1 << 20):
+        out = _normal_block(key, flat)
+    else:
+        chunk = 1 << 18
+        parts = [flat[i:i + chunk] for i in range(0, n, chunk)]
+        out = np.concatenate(list(_pool().map(lambda p: _normal_block(key, p), parts)))
+    return out.reshape(np.shape(idx))
+
+
+def round_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float64/float32 -> bf16 bit patterns (uint16), via float32 then torch's
+    round-to-nearest-even conversion (storage rounding of generated inputs)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def store(x: np.ndarray, io_dtype: str) -> np.ndarray:
+    if io_dtype == "f32":
+        return x.astype(np.float32)
+    if io_dtype == "bf16":
+        return round_bf16_bits(x)
+    raise ValueError(io_dtype)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape of one SSM layer's decode state, plus the keys' identity."""
+    batch: int
+    heads: int
+    groups: int
+    head_dim: int      # P
+    state_dim: int     # N
+    ring_len: int      # L
+    io_dtype: str = "bf16"
+    config: int = CONFIG_ID["misc"]
+    layer: int = 0
+    dt_scale: float = 1.0   # multiplies dt before a = exp(dt*A); 1.0 is the plain recipe
+
+    def key(self, tensor: str) -> int:
+        return stream_key(self.config, self.layer, tensor)
+
+
+def _flat_index(sizes, sel):
+    """Row-major flat index over full `sizes` for the Cartesian product of the
+    per-axis selections `sel` (each a 1-D int array)."""
+    idx = np.zeros([len(s) for s in sel], dtype=np.uint64)
+    mult = 1
+    for ax in range(len(sizes) - 1, -1, -1):
+        shape = [1] * len(sizes)
+        shape[ax] = len(sel[ax])
+        idx += (np.asarray(sel[ax], dtype=np.uint64) * np.uint64(mult)).reshape(shape)
+        mult *= sizes[ax]
+    return idx
+
+
+def decay_A(w: Workload) -> np.ndarray:
+    """A_h = -exp(u), u ~ U(0,1): float64 [H]."""
+    return -np.exp(uniform(w.key("A"), np.arange(w.heads, dtype=np.uint64)))
+
+
+def step_inputs(w: Workload, t0: int, t1: int, seqs=None) -> dict:
+    """Inputs of tokens t0..t1-1 (absolute token-stream rows) for the chosen
+    sequences (default: all).  Returns storage arrays:
+      q, k : [T][b][G][N]   v : [T][b][H][P]   dt, a : [T][b][H] float32
+    The full-batch row-major index is used for every element, so a subset of
+    sequences equals the same rows of the whole batch."""
+    B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
+    ts = np.arange(t0, t1, dtype=np.int64)
+    bs = np.arange(B, dtype=np.int64) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    Tn = 1 << 40  # time axis is unbounded; index = t*(B*...) + ...
+    iq = _flat_index([Tn, B, G, N], [ts, bs, np.arange(G), np.arange(N)])
+    q = normal(w.key("q"), iq) * math.sqrt(1.0 / N)
+    k = normal(w.key("k"), iq) * math.sqrt(1.0 / N)
+    iv = _flat_index([Tn, B, H, P], [ts, bs, np.arange(H), np.arange(P)])
+    v = normal(w.key("v"), iv)
+    idt = _flat_index([Tn, B, H], [ts, bs, np.arange(H)])
+    x = normal(w.key("dt"), idt)
+    # softplus, times the optional scale, rounded once to float32
+    dt32 = (np.logaddexp(0.0, x) * w.dt_scale).astype(np.float32)
+    A = decay_A(w)
+    a32 = np.exp(dt32.astype(np.float64) * A[None, None, :]).astype(np.float32)
+    return {
+        "q": store(q, w.io_dtype),
+        "k": store(k, w.io_dtype),
+        "v": store(v, w.io_dtype),
+        "dt": dt32,
+        "a": a32,
+    }
+
+
+def accept_counts(w: Workload, rounds: int, W: int, r0: int = 0) -> np.ndarray:
+    """Accepted drafts per (round, sequence) ~ Uniform{0..W}: int32 [R][B]."""
+    idx = _flat_index([1 << 40, w.batch], [np.arange(r0, r0 + rounds), np.arange(w.batch)])
+    u = uniform(w.key("accept"), idx)
+    return np.minimum((u * (W + 1)).astype(np.int64), W).astype(np.int32)
+
+
+def checkpoint_state(w: Workload, scale: float = 1.0, seqs=None) -> np.ndarray:
+    """A float32 checkpoint [b][H][P][N] ~ scale * N(0, 1), e.g. a state that
+    a prefill handed over."""
+    B, H, P, N = w.batch, w.heads, w.head_dim, w.state_dim
+    bs = np.arange(B) if seqs is None else np.asarray(seqs)
+    idx = _flat_index([B, H, P, N], [bs, np.arange(H), np.arange(P), np.arange(N)])
+    return (normal(w.key("S0"), idx) * scale).astype(np.float32)
+
+
+def named(name: str, **over) -> Workload:
+    """The workloads the task names, by what they are."""
+    base = {
+        # tiny single layer: B=1 H=4 G=1 P=16 N=16 L=4, all float32
+        "tiny": dict(batch=1, heads=4, groups=1, head_dim=16, state_dim=16, ring_len=4, io_dtype="f32"),
+        # Mamba-2-shaped layer, standard decode: B=256 H=128 G=8 P=64 N=128 L=16, bf16 q/k/v
+        "decode": dict(batch=256, heads=128, groups=8, head_dim=64, state_dim=128, ring_len=16, io_dtype="bf16"),
+        # speculative verify: B=256 H=64 G=8 P=64 N=128 L=16, W=5
+        "verify": dict(batch=256, heads=64, groups=8, head_dim=64, state_dim=128, ring_len=16, io_dtype="bf16"),
+        # dual precision: decode shapes, 1024 steps
+        "dual": dict(batch=256, heads=128, groups=8, head_dim=64, state_dim=128, ring_len=16, io_dtype="bf16"),
+        # stacked sweep: 8 layers, B=512 H=64 G=8 P=128 N=128, L in {8,16,32}
+        "stacked": dict(batch=512, heads=64, groups=8, head_dim=128, state_dim=128, ring_len=16, io_dtype="bf16"),
+    }[name]
+    base.update(over)
+    base.setdefault("config", CONFIG_ID[name])
+    return Workload(**base)
