@@ -1,0 +1,214 @@
+/*
+ * replayssm.h -- C ABI of the ReplaySSM decode path for Mamba-2-style SSM
+ * layers on AMD Instinct MI355X (gfx950).
+ *
+ * Method (page "ReplaySSM: Cache SSM Inputs, Not State", arXiv 2610.13778
+ * abstract page, Abstract; page "ReplaySSM: Cachear Inputs, No Estado",
+ * sections "La solucion", "Los dos caminos", "Como funciona en la practica"):
+ * the recurrent state of every (sequence, head) is held as a checkpoint S0
+ * plus a ring of the most recent inputs (q, k, v, dt, a).  Outputs are
+ * produced without materialising the state,
+ *
+ *     y_t = abar_t (S0 q_t) + sum_{j<=t} s_{j,t} v_j (k_j . q_t),
+ *     abar_t = prod_{m=1..t} a_m,   s_{j,t} = dt_j prod_{m=j+1..t} a_m,
+ *
+ * with j counting the ring entries since the checkpoint (eq. "Ruta solo
+ * salida"; abar and s are not defined on the pages -- this is the reading
+ * that equals the eager recurrence S_t = a_t S_{t-1} + dt_t v_t k_t^T,
+ * y_t = S_t q_t, eq. "Forma resumen").  A flush folds the ring into the
+ * checkpoint once (eq. "Ruta estado y salida"); a speculative rollback only
+ * moves the ring pointer back.
+ *
+ * Shapes: B sequences, H heads, G groups (heads h share the k, q of group
+ * floor(h*G/H)), P = head_dim, N = state_dim, L = ring_len.
+ * S is stored [P][N] per head, N fastest.
+ *
+ * Conventions for every call below
+ *  - Every tensor pointer is HIP device memory owned by the caller; the
+ *    library never allocates or frees device memory.  A handle borrows the
+ *    buffers given to replay_init: they must outlive it.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call that
+ *    enqueues work is asynchronous on that stream and performs no host
+ *    synchronisation, except replay_get_error and replay_destroy, which
+ *    synchronise the given stream.
+ *  - Argument problems the host can see (NULL pointer, a misaligned pointer,
+ *    a size outside the compiled specialisations, W out of range) return an
+ *    error status and enqueue nothing.  State tiles, ring buffers and the
+ *    q / k / v arguments of replay_append must be 16-byte aligned; scalar
+ *    arrays (dt, a, y, n_reject, n_accept) 4-byte aligned.
+ *  - Per-sequence problems only the device can see set that sequence's bits
+ *    in the caller's error buffer and leave that sequence unchanged; read and
+ *    clear them with replay_get_error.
+ *  - A handle is not thread-safe; distinct handles are independent.  Calls on
+ *    one handle must be issued in order on one stream (or ordered by the
+ *    caller across streams).
+ *  - Specialisations: (P, N) in {(16,16), (64,64), (64,128), (128,128)},
+ *    1 <= L <= 32, 1 <= G <= H with H % G == 0, verify windows 1 <= W <= 8.
+ */
+#ifndef REPLAYSSM_H
+#define REPLAYSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define REPLAY_ABI_VERSION 1
+
+typedef enum {
+    REPLAY_OK = 0,
+    REPLAY_ERR_INVALID_ARG = 1,   /* NULL / misaligned pointer, bad size, W out of range */
+    REPLAY_ERR_UNSUPPORTED = 2,   /* shape or dtype outside the compiled specialisations */
+    REPLAY_ERR_HIP = 3            /* a HIP runtime call failed (launch, copy, sync) */
+} replay_status;
+
+/* Per-sequence error bits (device side, sticky until replay_get_error). */
+#define REPLAY_SEQERR_RING_OVERFLOW  1  /* append(W) with count + W > L */
+#define REPLAY_SEQERR_ROLLBACK_RANGE 2  /* rollback(r) with r < 0 or r > count */
+#define REPLAY_SEQERR_TOO_FEW        4  /* decode / verify(W) with count < W; y of that sequence is NaN */
+#define REPLAY_SEQERR_POS_OVERFLOW   8  /* append would take pos past 2^31 - 1 */
+
+typedef enum {
+    REPLAY_NONE = -1,
+    REPLAY_F32 = 0,
+    REPLAY_BF16 = 1,
+    REPLAY_FP8_E4M3 = 2           /* OCP E4M3 (e4m3fn), largest finite 448 */
+} replay_dtype;
+
+typedef struct {
+    int32_t batch;        /* B */
+    int32_t heads;        /* H */
+    int32_t groups;       /* G */
+    int32_t head_dim;     /* P */
+    int32_t state_dim;    /* N */
+    int32_t ring_len;     /* L */
+    int32_t io_dtype;     /* REPLAY_F32 or REPLAY_BF16: q, k, v inputs and their ring */
+    int32_t read_copy;    /* REPLAY_NONE: outputs read the float32 master checkpoint;
+                             REPLAY_BF16 / REPLAY_FP8_E4M3: outputs read a low-precision
+                             copy, rewritten from the new checkpoint at every flush */
+    int32_t shared_lowp;  /* 0: separated precisions (the float32 master takes every flush);
+                             1: shared -- the low-precision copy is the only checkpoint and
+                             each flush starts from it (needs read_copy != NONE) */
+} replay_config;
+
+/* Device buffers of one layer's decode state.  Sizes in elements; use
+   replay_buffer_bytes for bytes.  Every pointer 16-byte aligned. */
+typedef struct {
+    float   *s_master;  /* [B][H][P][N] f32 checkpoint; NULL iff shared_lowp */
+    void    *s_copy;    /* [B][H][P][N] bf16 or e4m3 copy; NULL iff read_copy == NONE */
+    float   *s_scale;   /* [B][H] per-head scale of an e4m3 copy (value = code * scale);
+                           NULL unless read_copy == FP8_E4M3 */
+    void    *ring_q;    /* [B][G][L][N] io dtype */
+    void    *ring_k;    /* [B][G][L][N] io dtype */
+    void    *ring_v;    /* [B][H][L][P] io dtype */
+    float   *ring_dt;   /* [B][H][L] */
+    float   *ring_a;    /* [B][H][L] */
+    int32_t *pos;       /* [B] tokens appended and not rolled back */
+    int32_t *base;      /* [B] pos at the last flush; count = pos - base */
+    int32_t *err;       /* [B + 1] error bits: err[0] = OR over sequences, err[1 + b] per sequence */
+} replay_buffers;
+
+typedef struct replay_handle replay_handle;
+
+/* Human-readable name of a status.  Never NULL. */
+const char *replay_status_string(replay_status s);
+
+/* REPLAY_ABI_VERSION of the built library. */
+int32_t replay_abi_version(void);
+
+/* Bytes needed by each replay_buffers field, in field order (11 entries);
+   0 for a field the configuration does not use.  Host only. */
+replay_status replay_buffer_bytes(const replay_config *cfg, size_t bytes[11]);
+
+/* Validate `cfg` and `bufs`, create a handle, and enqueue the initial state:
+   checkpoint 0 (page "ReplaySSM: Cachear Inputs, No Estado", eq. "Forma
+   historia" starts from a zero state), copy 0 with scale 1, pos = base = 0,
+   error bits 0.  Ring contents are left as they are (never read before
+   being written).  On success *out owns a small host object. */
+replay_status replay_init(const replay_config *cfg, const replay_buffers *bufs,
+                          void *stream, replay_handle **out);
+
+/* Synchronise `stream` and free the host handle (device buffers untouched). */
+replay_status replay_destroy(replay_handle *h, void *stream);
+
+/* Replace every sequence's checkpoint by `s_src` ([B][H][P][N] f32, e.g. the
+   state a prefill produced), empty the ring (base = pos) and rewrite the
+   low-precision copy from it (page "ReplaySSM: Cachear Inputs, No Estado",
+   "Decodificacion estandar": the checkpoint is the state accumulated up to
+   the last flush).  In shared mode only the copy is written. */
+replay_status replay_load_checkpoint(replay_handle *h, const float *s_src, void *stream);
+
+/* Append W tokens to every sequence's ring (same page, "Decodificacion
+   estandar": recent (v, dt, k) go to the buffer; q and a are kept too).
+   q, k: [B][W][G][N]; v: [B][W][H][P] (io dtype); dt, a: [B][W][H] f32.
+   Token i of sequence b goes to slot (pos[b] + i) mod L; then pos[b] += W.
+   Needs count + W <= L per sequence (else RING_OVERFLOW, sequence
+   unchanged).  1 <= W <= L. */
+replay_status replay_append(replay_handle *h, int32_t W, const void *q, const void *k,
+                            const void *v, const float *dt, const float *a, void *stream);
+
+/* Output of the newest token of every sequence by the output-only route
+   (same page, section "Los dos caminos", eq. "Ruta solo salida"): reads the
+   checkpoint (or its copy) once, writes no state.  y: [B][H][P] f32.
+   Needs count >= 1 (else TOO_FEW and y of that sequence is NaN). */
+replay_status replay_decode(replay_handle *h, float *y, void *stream);
+
+/* Outputs of the W newest ring entries of every sequence against one read of
+   the checkpoint (same page, "Paralelismo": all positions of a speculative
+   window read the same checkpoint and buffer, entry j is visible to position
+   t only when j <= t; abstract page: output-only verification).
+   Position w (0-based) is ring entry t_w = count - W + 1 + w.
+   y: [B][W][H][P] f32.  1 <= W <= min(8, L); needs count >= W per sequence
+   (else TOO_FEW, NaN outputs for that sequence). */
+replay_status replay_verify(replay_handle *h, int32_t W, float *y, void *stream);
+
+/* Drop the n_reject[b] newest entries of every sequence by moving the pointer
+   back: pos[b] -= n_reject[b] (same page, "Rollback"; page "The SSM Layer
+   Nobody Made Fast (Until Now): ReplaySSM Explained", key technical
+   takeaways: an O(1) pointer decrement).  n_reject: device int32 [B].
+   Needs 0 <= n_reject[b] <= count (else ROLLBACK_RANGE, unchanged). */
+replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *stream);
+
+/* Fold the ring into the checkpoint for every sequence with
+   count >= max(min_count, 1) (same page, "Decodificacion estandar", step 4;
+   eq. "Ruta estado y salida"): S0 <- abar_c S0 + sum_j s_{j,c} v_j k_j^T over
+   the c = count entries, then base = pos, and the copy (and its per-head
+   scale) is rewritten from the new checkpoint.  Other sequences: no-op. */
+replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream);
+
+/* Synchronise `stream`, copy the error bits to the host and clear them on the
+   device.  *word = OR over sequences; per_seq (may be NULL): host int32 [B]. */
+replay_status replay_get_error(replay_handle *h, int32_t *word, int32_t *per_seq, void *stream);
+
+/* Eager baseline step (page "ReplaySSM: Cachear Inputs, No Estado", eq.
+   "Forma resumen"; section "El problema": the whole state is read and
+   written every token):  S_out = a S_in + dt v k^T,  y = S_out q.
+   s_in, s_out: [B][H][P][N] f32 (equal pointers = in place, else they must
+   not overlap); q, k: [B][G][N]; v: [B][H][P] (cfg->io_dtype); dt, a:
+   [B][H] f32; y: [B][H][P] f32.  Uses only the shape fields of cfg. */
+replay_status replay_eager_step(const replay_config *cfg, const float *s_in, float *s_out,
+                                const void *q, const void *k, const void *v,
+                                const float *dt, const float *a, float *y, void *stream);
+
+/* Eager speculative restore (same page, "Rollback": without the buffer, a
+   rejected draft means restoring a full stored state).  snaps: [W][B][H][P][N]
+   f32, snapshot w = state after draft w+1; n_accept: device int32 [B] in
+   0..W.  For every b with n_accept[b] >= 1: s[b] <- snaps[n_accept[b]-1][b];
+   n_accept[b] == 0 leaves s[b].  Values outside 0..W are ignored. */
+replay_status replay_eager_select(const replay_config *cfg, const float *snaps, int32_t W,
+                                  const int32_t *n_accept, float *s, void *stream);
+
+/* HBM stream probe, the bandwidth ceiling the other kernels are quoted
+   against.  mode 0: read `bytes` from src and write one float per
+   workgroup into dst (needs 4 * 2048 bytes); mode 1: copy `bytes` from src
+   to dst.  bytes must be a multiple of 16. */
+replay_status replay_stream_probe(int32_t mode, const void *src, void *dst, size_t bytes,
+                                  void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REPLAYSSM_H */

@@ -1,0 +1,314 @@
+// abi.hip -- the extern "C" boundary of libreplayssm: host-side validation,
+// launch configuration and the handle.  Every compute step runs in the
+// kernels of decode.hip, flush.hip, ring.hip, eager.hip and probe.hip.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+using namespace replay;
+
+struct replay_handle {
+    replay_config cfg;
+    replay_buffers bufs;
+};
+
+namespace {
+
+constexpr int kNumBufferFields = 11;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+replay_status from_hip(hipError_t e) { return e == hipSuccess ? REPLAY_OK : REPLAY_ERR_HIP; }
+
+int io_bytes(const replay_config &c) { return c.io_dtype == REPLAY_BF16 ? 2 : 4; }
+
+int state_kind(int32_t dtype) {
+    return dtype == REPLAY_BF16 ? ST_BF16 : (dtype == REPLAY_FP8_E4M3 ? ST_FP8 : ST_F32);
+}
+
+// Shape and dtype checks shared by every entry point that takes a config.
+replay_status check_shape(const replay_config *c) {
+    if (!c) return REPLAY_ERR_INVALID_ARG;
+    if (c->batch < 1 || c->heads < 1 || c->groups < 1 || c->head_dim < 1 || c->state_dim < 1)
+        return REPLAY_ERR_INVALID_ARG;
+    if (c->heads % c->groups != 0) return REPLAY_ERR_INVALID_ARG;
+    if ((int64_t)c->batch * c->heads > INT32_MAX) return REPLAY_ERR_UNSUPPORTED;
+    if (!shape_supported(c->head_dim, c->state_dim)) return REPLAY_ERR_UNSUPPORTED;
+    if (c->io_dtype != REPLAY_F32 && c->io_dtype != REPLAY_BF16) return REPLAY_ERR_UNSUPPORTED;
+    return REPLAY_OK;
+}
+
+replay_status check_config(const replay_config *c) {
+    replay_status st = check_shape(c);
+    if (st != REPLAY_OK) return st;
+    if (c->ring_len < 1) return REPLAY_ERR_INVALID_ARG;
+    if (c->ring_len > kMaxRing) return REPLAY_ERR_UNSUPPORTED;
+    if (c->read_copy != REPLAY_NONE && c->read_copy != REPLAY_BF16 && c->read_copy != REPLAY_FP8_E4M3)
+        return REPLAY_ERR_UNSUPPORTED;
+    if (c->shared_lowp != 0 && c->shared_lowp != 1) return REPLAY_ERR_INVALID_ARG;
+    if (c->shared_lowp && c->read_copy == REPLAY_NONE) return REPLAY_ERR_INVALID_ARG;
+    return REPLAY_OK;
+}
+
+void buffer_bytes(const replay_config &c, size_t out[kNumBufferFields]) {
+    const size_t B = c.batch, H = c.heads, G = c.groups, P = c.head_dim, N = c.state_dim,
+                 L = c.ring_len, esz = io_bytes(c);
+    const size_t state = B * H * P * N;
+    out[0] = c.shared_lowp ? 0 : state * 4;                                            // s_master
+    out[1] = c.read_copy == REPLAY_NONE ? 0 : state * (c.read_copy == REPLAY_BF16 ? 2 : 1);  // s_copy
+    out[2] = c.read_copy == REPLAY_FP8_E4M3 ? B * H * 4 : 0;                            // s_scale
+    out[3] = B * G * L * N * esz;                                                       // ring_q
+    out[4] = B * G * L * N * esz;                                                       // ring_k
+    out[5] = B * H * L * P * esz;                                                       // ring_v
+    out[6] = B * H * L * 4;                                                             // ring_dt
+    out[7] = B * H * L * 4;                                                             // ring_a
+    out[8] = B * 4;                                                                     // pos
+    out[9] = B * 4;                                                                     // base
+    out[10] = (B + 1) * 4;                                                              // err
+}
+
+const void *field(const replay_buffers &b, int i) {
+    const void *f[kNumBufferFields] = {b.s_master, b.s_copy, b.s_scale, b.ring_q, b.ring_k, b.ring_v,
+                                       b.ring_dt,  b.ring_a, b.pos,     b.base,   b.err};
+    return f[i];
+}
+
+RingView ring_view(const replay_handle *h) {
+    RingView r;
+    r.q = h->bufs.ring_q;
+    r.k = h->bufs.ring_k;
+    r.v = h->bufs.ring_v;
+    r.dt = h->bufs.ring_dt;
+    r.a = h->bufs.ring_a;
+    r.pos = h->bufs.pos;
+    r.base = h->bufs.base;
+    r.err = h->bufs.err;
+    r.B = h->cfg.batch;
+    r.H = h->cfg.heads;
+    r.G = h->cfg.groups;
+    r.L = h->cfg.ring_len;
+    r.io_bf16 = h->cfg.io_dtype == REPLAY_BF16;
+    return r;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+// Fold (or load) into the checkpoint and rewrite the copy, then move base.
+replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_count, hipStream_t s) {
+    const replay_config &c = h->cfg;
+    FlushArgs a;
+    a.r = ring_view(h);
+    a.min_count = min_count;
+    a.force_empty = load_src != nullptr;
+    a.S_out = c.shared_lowp ? nullptr : h->bufs.s_master;
+    a.copy_out = c.read_copy == REPLAY_NONE ? nullptr : h->bufs.s_copy;
+    a.scale_out = c.read_copy == REPLAY_FP8_E4M3 ? h->bufs.s_scale : nullptr;
+    int st_in;
+    if (load_src) {
+        a.S_in = load_src;
+        a.scale_in = nullptr;
+        st_in = ST_F32;
+    } else if (c.shared_lowp) {
+        a.S_in = h->bufs.s_copy;
+        a.scale_in = h->bufs.s_scale;
+        st_in = state_kind(c.read_copy);
+    } else {
+        a.S_in = h->bufs.s_master;
+        a.scale_in = nullptr;
+        st_in = ST_F32;
+    }
+    const int st_copy = c.read_copy == REPLAY_NONE ? -1 : state_kind(c.read_copy);
+    hipError_t e = launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s);
+    if (e != hipSuccess) return REPLAY_ERR_HIP;
+    return from_hip(launch_commit(a.r, h->bufs.base, min_count, a.force_empty, s));
+}
+
+replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
+    const replay_config &c = h->cfg;
+    if (!y || !aligned4(y)) return REPLAY_ERR_INVALID_ARG;
+    if (W < 1 || W > kMaxWindow || W > c.ring_len) return REPLAY_ERR_INVALID_ARG;
+    DecodeArgs a;
+    a.r = ring_view(h);
+    a.S = c.read_copy == REPLAY_NONE ? static_cast<const void *>(h->bufs.s_master) : h->bufs.s_copy;
+    a.scale = h->bufs.s_scale;
+    a.y = y;
+    a.W = W;
+    return from_hip(launch_decode(c.head_dim, c.state_dim, state_kind(c.read_copy), a, s));
+}
+
+}  // namespace
+
+namespace replay {
+bool shape_supported(int P, int N) {
+    return (P == 16 && N == 16) || (P == 64 && N == 64) || (P == 64 && N == 128) || (P == 128 && N == 128);
+}
+}  // namespace replay
+
+extern "C" {
+
+const char *replay_status_string(replay_status s) {
+    switch (s) {
+        case REPLAY_OK: return "ok";
+        case REPLAY_ERR_INVALID_ARG: return "invalid argument";
+        case REPLAY_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case REPLAY_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int32_t replay_abi_version(void) { return REPLAY_ABI_VERSION; }
+
+replay_status replay_buffer_bytes(const replay_config *cfg, size_t bytes[11]) {
+    replay_status st = check_config(cfg);
+    if (st != REPLAY_OK) return st;
+    if (!bytes) return REPLAY_ERR_INVALID_ARG;
+    buffer_bytes(*cfg, bytes);
+    return REPLAY_OK;
+}
+
+replay_status replay_init(const replay_config *cfg, const replay_buffers *bufs, void *stream,
+                          replay_handle **out) {
+    replay_status st = check_config(cfg);
+    if (st != REPLAY_OK) return st;
+    if (!bufs || !out) return REPLAY_ERR_INVALID_ARG;
+    size_t need[kNumBufferFields];
+    buffer_bytes(*cfg, need);
+    for (int i = 0; i < kNumBufferFields; ++i) {
+        const void *p = field(*bufs, i);
+        if (need[i] == 0) continue;
+        if (!p || !aligned16(p)) return REPLAY_ERR_INVALID_ARG;
+    }
+    replay_handle *h = new (std::nothrow) replay_handle;
+    if (!h) return REPLAY_ERR_INVALID_ARG;
+    h->cfg = *cfg;
+    h->bufs = *bufs;
+    if (cfg->shared_lowp) h->bufs.s_master = nullptr;
+    if (cfg->read_copy == REPLAY_NONE) h->bufs.s_copy = nullptr;
+    if (cfg->read_copy != REPLAY_FP8_E4M3) h->bufs.s_scale = nullptr;
+
+    hipStream_t s = as_stream(stream);
+    hipError_t e = hipSuccess;
+    if (h->bufs.s_master) e = launch_fill_u32(h->bufs.s_master, 0u, need[0] / 4, s);
+    if (e == hipSuccess && h->bufs.s_copy) e = launch_fill_u32(h->bufs.s_copy, 0u, need[1] / 4, s);
+    if (e == hipSuccess && h->bufs.s_scale) e = launch_fill_u32(h->bufs.s_scale, 0x3f800000u, need[2] / 4, s);
+    if (e == hipSuccess) e = launch_fill_u32(h->bufs.pos, 0u, need[8] / 4, s);
+    if (e == hipSuccess) e = launch_fill_u32(h->bufs.base, 0u, need[9] / 4, s);
+    if (e == hipSuccess) e = launch_fill_u32(h->bufs.err, 0u, need[10] / 4, s);
+    if (e != hipSuccess) {
+        delete h;
+        return REPLAY_ERR_HIP;
+    }
+    *out = h;
+    return REPLAY_OK;
+}
+
+replay_status replay_destroy(replay_handle *h, void *stream) {
+    if (!h) return REPLAY_ERR_INVALID_ARG;
+    hipError_t e = hipStreamSynchronize(as_stream(stream));
+    delete h;
+    return from_hip(e);
+}
+
+replay_status replay_load_checkpoint(replay_handle *h, const float *s_src, void *stream) {
+    if (!h || !s_src || !aligned16(s_src)) return REPLAY_ERR_INVALID_ARG;
+    return run_flush(h, s_src, 0, as_stream(stream));
+}
+
+replay_status replay_append(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
+                            const float *dt, const float *a, void *stream) {
+    if (!h || !q || !k || !v || !dt || !a) return REPLAY_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a))
+        return REPLAY_ERR_INVALID_ARG;
+    if (W < 1 || W > h->cfg.ring_len) return REPLAY_ERR_INVALID_ARG;
+    const RingView r = ring_view(h);
+    return from_hip(launch_append(h->cfg.head_dim, h->cfg.state_dim, r, h->bufs.ring_q, h->bufs.ring_k,
+                                  h->bufs.ring_v, h->bufs.ring_dt, h->bufs.ring_a, h->bufs.pos, W, q, k, v,
+                                  dt, a, as_stream(stream)));
+}
+
+replay_status replay_decode(replay_handle *h, float *y, void *stream) {
+    if (!h) return REPLAY_ERR_INVALID_ARG;
+    return run_verify(h, 1, y, as_stream(stream));
+}
+
+replay_status replay_verify(replay_handle *h, int32_t W, float *y, void *stream) {
+    if (!h) return REPLAY_ERR_INVALID_ARG;
+    return run_verify(h, W, y, as_stream(stream));
+}
+
+replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *stream) {
+    if (!h || !n_reject || !aligned4(n_reject)) return REPLAY_ERR_INVALID_ARG;
+    return from_hip(launch_rollback(ring_view(h), h->bufs.pos, n_reject, as_stream(stream)));
+}
+
+replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream) {
+    if (!h) return REPLAY_ERR_INVALID_ARG;
+    return run_flush(h, nullptr, min_count, as_stream(stream));
+}
+
+replay_status replay_get_error(replay_handle *h, int32_t *word, int32_t *per_seq, void *stream) {
+    if (!h || !word) return REPLAY_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    const int B = h->cfg.batch;
+    int32_t *host = new (std::nothrow) int32_t[B + 1];
+    if (!host) return REPLAY_ERR_INVALID_ARG;
+    hipError_t e = hipMemcpyAsync(host, h->bufs.err, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = launch_fill_u32(h->bufs.err, 0u, (size_t)B + 1, s);
+    if (e == hipSuccess) {
+        *word = host[0];
+        if (per_seq) std::memcpy(per_seq, host + 1, sizeof(int32_t) * B);
+    }
+    delete[] host;
+    return from_hip(e);
+}
+
+replay_status replay_eager_step(const replay_config *cfg, const float *s_in, float *s_out, const void *q,
+                                const void *k, const void *v, const float *dt, const float *a, float *y,
+                                void *stream) {
+    replay_status st = check_shape(cfg);
+    if (st != REPLAY_OK) return st;
+    const void *vec_ptrs[] = {s_in, s_out, q, k};
+    for (const void *p : vec_ptrs)
+        if (!p || !aligned16(p)) return REPLAY_ERR_INVALID_ARG;
+    const void *scalar_ptrs[] = {v, dt, a, y};
+    for (const void *p : scalar_ptrs)
+        if (!p || !aligned4(p)) return REPLAY_ERR_INVALID_ARG;
+    EagerArgs ea;
+    ea.S_in = s_in;
+    ea.S_out = s_out;
+    ea.q = q;
+    ea.k = k;
+    ea.v = v;
+    ea.dt = dt;
+    ea.a = a;
+    ea.y = y;
+    ea.B = cfg->batch;
+    ea.H = cfg->heads;
+    ea.G = cfg->groups;
+    ea.io_bf16 = cfg->io_dtype == REPLAY_BF16;
+    return from_hip(launch_eager(cfg->head_dim, cfg->state_dim, ea, as_stream(stream)));
+}
+
+replay_status replay_eager_select(const replay_config *cfg, const float *snaps, int32_t W,
+                                  const int32_t *n_accept, float *s, void *stream) {
+    replay_status st = check_shape(cfg);
+    if (st != REPLAY_OK) return st;
+    if (!snaps || !n_accept || !s || !aligned16(snaps) || !aligned16(s) || W < 1)
+        return REPLAY_ERR_INVALID_ARG;
+    const size_t per_seq = (size_t)cfg->heads * cfg->head_dim * cfg->state_dim;
+    return from_hip(launch_eager_select(snaps, W, n_accept, s, cfg->batch, per_seq, as_stream(stream)));
+}
+
+replay_status replay_stream_probe(int32_t mode, const void *src, void *dst, size_t bytes, void *stream) {
+    if ((mode != 0 && mode != 1) || !src || !dst || !aligned16(src) || !aligned16(dst) || bytes % 16 != 0)
+        return REPLAY_ERR_INVALID_ARG;
+    return from_hip(launch_probe(mode, src, dst, bytes, as_stream(stream)));
+}
+
+}  // extern "C"

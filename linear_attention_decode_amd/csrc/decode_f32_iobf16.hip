@@ -1,0 +1,7 @@
+// decode_f32_iobf16.hip -- decode / verify kernels for a f32 checkpoint tile and
+// bf16 q / k / v.
+#include "decode_impl.h"
+
+namespace replay {
+template hipError_t launch_decode_st<ST_F32, true>(int P, int N, const DecodeArgs &a, hipStream_t s);
+}  // namespace replay

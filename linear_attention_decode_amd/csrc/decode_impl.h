@@ -1,0 +1,307 @@
+// decode_impl.h -- output-only decode and speculative verify for gfx950.
+//
+// Computes, for the W newest ring entries t_w = count-W+1+w of every
+// (sequence, head),
+//     y_w = abar_{t_w} (S0 q_{t_w}) + sum_{j<=t_w} s_{j,t_w} v_j (k_j . q_{t_w})
+// (page "ReplaySSM: Cachear Inputs, No Estado", section "Los dos caminos",
+// eq. "Ruta solo salida"; "Paralelismo": every window position reads the
+// same checkpoint and buffer, entry j is visible to position t when j <= t),
+// with abar_t = prod_{m<=t} a_m and s_{j,t} = dt_j prod_{j<m<=t} a_m.
+// Decode is W = 1.  The checkpoint (or its bf16 / e4m3 copy) is read once
+// per call and never written.
+//
+// One workgroup per (sequence, head).  The head's P x N tile streams through
+// registers in coalesced 16-byte chunks (the whole workgroup covers NT*16
+// contiguous bytes per iteration), all chunk loads are issued before any
+// other work so they overlap the ring arithmetic.  k_j . q is formed per
+// group by the workgroup itself from the group's k ring (L2-resident: the
+// XCD-aware block order keeps a group's heads on one XCD).  Row sums are
+// finished with a transposed halving reduction across the lanes of a row.
+#pragma once
+#include "device_common.h"
+
+namespace replay {
+
+template <int P, int N, int ST, int WM>
+struct DecodeShape {
+    static constexpr int base_vec = ST == ST_F32 ? 4 : (ST == ST_BF16 ? 8 : (WM == 1 ? 16 : 8));
+    // at least one full wavefront of chunks per head
+    static constexpr int VEC = (P * N / base_vec >= 64) ? base_vec
+                             : ((P * N / (base_vec / 2) >= 64) ? base_vec / 2 : base_vec / 4);
+    static constexpr int CHUNKS = P * N / VEC;
+    static constexpr int NTS = CHUNKS < 256 ? CHUNKS : 256;   // streaming threads
+    static constexpr int NT = NTS + 64;                       // + one ring wavefront
+    static constexpr int ITER = CHUNKS / NTS;
+    static constexpr int LPR = N / VEC;     // lanes per state row
+    static constexpr int RPI = NTS / LPR;   // rows per iteration
+    static_assert(VEC >= 4, "chunk too small");
+    static_assert(CHUNKS % NTS == 0 && NTS % 64 == 0, "bad tiling");
+    static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row group must sit in a wavefront");
+};
+
+__device__ __forceinline__ float bcast(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// The ring wavefront's work for one (sequence, head): group dots, segment
+// weights and the ring term, all in registers; results go to LDS.
+//   s_r[w][p] = sum_{j<=t_w} s_{j,t_w} (k_j . q_{t_w}) v_j[p],   s_abar[w] = abar_{t_w}
+template <int P, int N, int WM, int LM, bool IOB>
+__device__ __forceinline__ void ring_wave(const RingView &r, int lane, int b, int g, size_t bh, int base,
+                                          int count, float (*s_r)[P], float *s_abar) {
+    constexpr int W = WM;
+    constexpr int TS = N / 8;               // lanes per k.q dot (8 elements each)
+    constexpr int RPW = 64 / TS;            // ring entries per k instruction
+    constexpr int KI = (LM + RPW - 1) / RPW;
+    constexpr int VR = (P + 63) / 64;       // state rows per lane in the ring term
+    static_assert(TS >= 1 && 64 % TS == 0, "dot teams");
+    const int L = r.L;
+    const size_t gring = ((size_t)b * r.G + g) * L;
+    const size_t hring = bh * L;
+    const int t0 = count - W;               // window position w is entry t0 + w (0-based)
+    const int bmod = base % L;
+    auto slot = [&](int j) { return ring_slot(bmod, j, L); };
+
+    // every load first, from valid entries only (indices clamped to the live
+    // range; values of clamped lanes are masked out below, never used)
+    const int last = count - 1;
+    float aj, dtj;
+    {
+        const int sl = slot(lane < count ? lane : last);
+        aj = r.a[hring + sl];
+        dtj = r.dt[hring + sl];
+    }
+    const int tl = lane % TS, te = lane / TS;
+    IoVec<IOB, 8> kraw[KI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+        const int j = i * RPW + te;
+        kraw[i].load(r.k, (gring + slot(j < count ? j : last)) * N + tl * 8);
+    }
+    IoVec<IOB, 8> qraw[WM];
+#pragma unroll
+    for (int w = 0; w < WM; ++w) qraw[w].load(r.q, (gring + slot(t0 + (w < W ? w : W - 1))) * N + tl * 8);
+    IoVec<IOB, 1> vraw[VR][LM];
+#pragma unroll
+    for (int rr = 0; rr < VR; ++rr)
+#pragma unroll
+        for (int j = 0; j < LM; ++j) {
+            const int p = lane + 64 * rr;
+            vraw[rr][j].load(r.v, (hring + slot(j < count ? j : last)) * P + (p < P ? p : P - 1));
+        }
+    if (lane >= count) {
+        aj = 1.f;
+        dtj = 0.f;
+    }
+
+    // dots c[w][j], then moved so that lane j holds c[w][j]
+    float qq[WM][8];
+#pragma unroll
+    for (int w = 0; w < WM; ++w) qraw[w].widen(qq[w]);
+    float cw[WM];
+#pragma unroll
+    for (int w = 0; w < WM; ++w) cw[w] = 0.f;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+        float kk[8];
+        kraw[i].widen(kk);
+#pragma unroll
+        for (int w = 0; w < WM; ++w) {
+            if (w < W) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) d = fmaf(kk[e], qq[w][e], d);
+                d = group_sum<TS>(d);
+                const float moved = __shfl(d, (lane % RPW) * TS);
+                if (lane / RPW == i) cw[w] = moved;
+            }
+        }
+    }
+
+    // segment weights, left to right: s_{j,t} = dt_j a_{j+1} ... a_t, abar_t = a_0 ... a_t
+    float sw[WM], ab[WM];
+    float prod = dtj, run = 1.f;
+#pragma unroll
+    for (int w = 0; w < WM; ++w) sw[w] = ab[w] = 0.f;
+#pragma unroll
+    for (int m = 0; m < LM; ++m) {
+        if (m < count) {
+            const float am = bcast(aj, m);
+            if (m > lane) prod *= am;
+            run *= am;
+#pragma unroll
+            for (int w = 0; w < WM; ++w)
+                if (m == t0 + w) {
+                    sw[w] = prod;
+                    ab[w] = run;
+                }
+        }
+    }
+    float coef[WM];
+#pragma unroll
+    for (int w = 0; w < WM; ++w) coef[w] = (w < W && lane <= t0 + w) ? sw[w] * cw[w] : 0.f;
+
+    // ring term, entries in order
+    float acc[VR][WM];
+#pragma unroll
+    for (int rr = 0; rr < VR; ++rr)
+#pragma unroll
+        for (int w = 0; w < WM; ++w) acc[rr][w] = 0.f;
+#pragma unroll
+    for (int j = 0; j < LM; ++j) {
+        if (j < count) {
+#pragma unroll
+            for (int w = 0; w < WM; ++w) {
+                if (w < W && j <= t0 + w) {
+                    const float cj = bcast(coef[w], j);
+#pragma unroll
+                    for (int rr = 0; rr < VR; ++rr) acc[rr][w] = fmaf(cj, vraw[rr][j].value(), acc[rr][w]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < VR; ++rr) {
+        const int p = lane + 64 * rr;
+        if (p < P) {
+#pragma unroll
+            for (int w = 0; w < WM; ++w)
+                if (w < W) s_r[w][p] = acc[rr][w];
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int w = 0; w < WM; ++w)
+            if (w < W) s_abar[w] = ab[w];
+    }
+}
+
+template <int P, int N, int ST, int WM, int LM, bool IOB>
+__global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NT)) void decode_kernel(DecodeArgs args) {
+    using Sh = DecodeShape<P, N, ST, WM>;
+    constexpr int W = WM;
+    constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+    using RR = RowReduce<ITER, LPR>;
+
+    __shared__ float s_r[WM][P];
+    __shared__ float s_abar[WM];
+
+    const RingView &r = args.r;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = lid / r.H, h = lid % r.H;
+    const int g = (h * r.G) / r.H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int L = r.L, H = r.H;
+    const size_t bh = (size_t)b * H + h;
+
+    // pointer pair first, then the state tile (which does not depend on it)
+    const int base = r.base[b];
+    const int pos = r.pos[b];
+    Chunk<ST, VEC> ch[ITER];
+    const size_t tile = bh * (size_t)(P * N);
+    if (tid < NTS) {
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
+    }
+    const int count = pos - base;
+    if (count < W) {  // uniform over the workgroup
+        for (int i = tid; i < W * P; i += Sh::NT) {
+            const int w = i / P, p = i % P;
+            args.y[(((size_t)b * W + w) * H + h) * P + p] = __builtin_nanf("");
+        }
+        if (tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_TOO_FEW);
+        return;
+    }
+
+    float part[ITER][WM];
+    if (tid < NTS) {
+        // queries of the window positions at this lane's columns
+        const int col0 = (tid % LPR) * VEC;
+        const size_t gring = ((size_t)b * r.G + g) * L;
+        IoVec<IOB, 4> qraw[WM][VEC / 4];
+        const int bmod = base % L;
+#pragma unroll
+        for (int w = 0; w < WM; ++w) {
+            const size_t off = (gring + ring_slot(bmod, count - W + (w < W ? w : W - 1), L)) * N + col0;
+#pragma unroll
+            for (int e = 0; e < VEC / 4; ++e) qraw[w][e].load(r.q, off + 4 * e);
+        }
+        float qv[WM][VEC];
+#pragma unroll
+        for (int w = 0; w < WM; ++w)
+#pragma unroll
+            for (int e = 0; e < VEC / 4; ++e) qraw[w][e].widen(&qv[w][4 * e]);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            float x[VEC];
+            ch[i].widen(x, 1.0f);
+#pragma unroll
+            for (int w = 0; w < WM; ++w) {
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc = fmaf(x[e], qv[w][e], acc);
+                part[i][w] = acc;
+            }
+        }
+        RR::template run<WM>(part, lane);
+    } else {
+        ring_wave<P, N, WM, LM, IOB>(r, lane, b, g, bh, base, count, s_r, s_abar);
+    }
+    __syncthreads();
+
+    if (tid < NTS && RR::writer(lane)) {
+        const float sc = (ST == ST_FP8) ? args.scale[bh] : 1.0f;
+        const int hi = RR::halving_index(lane);
+#pragma unroll
+        for (int e = 0; e < RR::FINAL; ++e) {
+            const int row = (e + RR::FINAL * hi) * RPI + tid / LPR;
+#pragma unroll
+            for (int w = 0; w < WM; ++w) {
+                if (w < W) {
+                    args.y[(((size_t)b * W + w) * H + h) * P + row] =
+                        s_abar[w] * (sc * part[e][w]) + s_r[w][row];
+                }
+            }
+        }
+    }
+}
+
+template <int P, int N, int ST, int WM, int LM, bool IOB>
+static hipError_t launch_one(const DecodeArgs &a, hipStream_t s) {
+    using Sh = DecodeShape<P, N, ST, WM>;
+    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
+    decode_kernel<P, N, ST, WM, LM, IOB><<<blocks, Sh::NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int P, int N, int ST, int WM, bool IOB>
+static hipError_t launch_l(const DecodeArgs &a, hipStream_t s) {
+    if (a.r.L <= 16) return launch_one<P, N, ST, WM, 16, IOB>(a, s);
+    return launch_one<P, N, ST, WM, kMaxRing, IOB>(a, s);
+}
+
+template <int P, int N, int ST, bool IOB>
+static hipError_t launch_w(const DecodeArgs &a, hipStream_t s) {
+    switch (a.W) {
+        case 1: return launch_l<P, N, ST, 1, IOB>(a, s);
+        case 2: return launch_l<P, N, ST, 2, IOB>(a, s);
+        case 3: return launch_l<P, N, ST, 3, IOB>(a, s);
+        case 4: return launch_l<P, N, ST, 4, IOB>(a, s);
+        case 5: return launch_l<P, N, ST, 5, IOB>(a, s);
+        case 6: return launch_l<P, N, ST, 6, IOB>(a, s);
+        case 7: return launch_l<P, N, ST, 7, IOB>(a, s);
+        case 8: return launch_l<P, N, ST, 8, IOB>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int ST, bool IOB>
+hipError_t launch_decode_st(int P, int N, const DecodeArgs &a, hipStream_t s) {
+    if (P == 16 && N == 16) return launch_w<16, 16, ST, IOB>(a, s);
+    if (P == 64 && N == 64) return launch_w<64, 64, ST, IOB>(a, s);
+    if (P == 64 && N == 128) return launch_w<64, 128, ST, IOB>(a, s);
+    if (P == 128 && N == 128) return launch_w<128, 128, ST, IOB>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace replay

@@ -1,0 +1,344 @@
+// device_common.h -- device helpers for the gfx950 kernels of libreplayssm.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace replay {
+
+// ---- workgroup -> work mapping ------------------------------------------
+// The dispatcher hands workgroup i to XCD (i mod 8).  Remapping gives each
+// XCD a contiguous range of logical ids, so heads that share a group's k/q
+// ring (consecutive ids) run on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    constexpr int kXcd = 8;
+    const int x = bid % kXcd, local = bid / kXcd;
+    const int q = nblocks / kXcd, r = nblocks % kXcd;
+    return x * q + (x < r ? x : r) + local;
+}
+
+// ---- number formats ------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+
+// float32 -> bf16 bits, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// four e4m3 codes packed in a word -> floats (hardware OCP e4m3 conversion)
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float *out) {
+    auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    out[0] = lo[0];
+    out[1] = lo[1];
+    out[2] = hi[0];
+    out[3] = hi[1];
+}
+
+// four floats -> packed e4m3 codes, round to nearest even, saturating to +-448
+__device__ __forceinline__ uint32_t f32x4_to_fp8(float a, float b, float c, float d) {
+    a = __builtin_amdgcn_fmed3f(a, 448.0f, -448.0f);
+    b = __builtin_amdgcn_fmed3f(b, 448.0f, -448.0f);
+    c = __builtin_amdgcn_fmed3f(c, 448.0f, -448.0f);
+    d = __builtin_amdgcn_fmed3f(d, 448.0f, -448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// ---- io loads (q, k, v: float32 or bf16, fixed at compile time) ----------
+// Load 4 consecutive io elements starting at element index `i` (i % 4 == 0).
+template <bool BF16>
+__device__ __forceinline__ void load_io4(const void *base, size_t i, float *out) {
+    if constexpr (BF16) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + i);
+        out[0] = bf16_bits_to_f32(w.x & 0xffffu);
+        out[1] = bf16_bits_to_f32(w.x >> 16);
+        out[2] = bf16_bits_to_f32(w.y & 0xffffu);
+        out[3] = bf16_bits_to_f32(w.y >> 16);
+    } else {
+        const float4 f = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + i);
+        out[0] = f.x;
+        out[1] = f.y;
+        out[2] = f.z;
+        out[3] = f.w;
+    }
+}
+
+// Load 8 consecutive io elements starting at element index `i` (i % 8 == 0).
+template <bool BF16>
+__device__ __forceinline__ void load_io8(const void *base, size_t i, float *out) {
+    if constexpr (BF16) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + i);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            out[2 * k] = bf16_bits_to_f32(u[k] & 0xffffu);
+            out[2 * k + 1] = bf16_bits_to_f32(u[k] >> 16);
+        }
+    } else {
+        load_io4<false>(base, i, out);
+        load_io4<false>(base, i + 4, out + 4);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_io1(const void *base, size_t i) {
+    if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t *>(base)[i]);
+    return static_cast<const float *>(base)[i];
+}
+
+// Raw io vectors: E consecutive io elements loaded as raw bits and widened
+// to float only where they are used, so a load never forces a wait at the
+// place it is issued.
+template <bool BF16, int E>
+struct IoVec;
+
+template <>
+struct IoVec<true, 8> {
+    uint4 r;
+    __device__ __forceinline__ void load(const void *base, size_t i) {
+        r = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + i);
+    }
+    __device__ __forceinline__ void widen(float *out) const {
+        const uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            out[2 * k] = bf16_bits_to_f32(u[k] & 0xffffu);
+            out[2 * k + 1] = bf16_bits_to_f32(u[k] >> 16);
+        }
+    }
+};
+
+template <>
+struct IoVec<false, 8> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const void *base, size_t i) {
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + i);
+        a = p[0];
+        b = p[1];
+    }
+    __device__ __forceinline__ void widen(float *out) const {
+        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+        out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+    }
+};
+
+template <>
+struct IoVec<true, 4> {
+    uint2 r;
+    __device__ __forceinline__ void load(const void *base, size_t i) {
+        r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + i);
+    }
+    __device__ __forceinline__ void widen(float *out) const {
+        out[0] = bf16_bits_to_f32(r.x & 0xffffu);
+        out[1] = bf16_bits_to_f32(r.x >> 16);
+        out[2] = bf16_bits_to_f32(r.y & 0xffffu);
+        out[3] = bf16_bits_to_f32(r.y >> 16);
+    }
+};
+
+template <>
+struct IoVec<false, 4> {
+    float4 a;
+    __device__ __forceinline__ void load(const void *base, size_t i) {
+        a = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + i);
+    }
+    __device__ __forceinline__ void widen(float *out) const {
+        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    }
+};
+
+template <>
+struct IoVec<true, 1> {
+    uint32_t r;
+    __device__ __forceinline__ void load(const void *base, size_t i) { r = static_cast<const uint16_t *>(base)[i]; }
+    __device__ __forceinline__ float value() const { return bf16_bits_to_f32(r); }
+};
+
+template <>
+struct IoVec<false, 1> {
+    float r;
+    __device__ __forceinline__ void load(const void *base, size_t i) { r = static_cast<const float *>(base)[i]; }
+    __device__ __forceinline__ float value() const { return r; }
+};
+
+// Ring slot of entry j (0-based, oldest first) for a ring that starts at
+// slot bmod = base mod L; valid for 0 <= j < L.
+__device__ __forceinline__ int ring_slot(int bmod, int j, int L) {
+    const int s = bmod + j;
+    return s >= L ? s - L : s;
+}
+
+// Native vector types (the nontemporal builtins take these, not HIP's
+// struct vectors).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- state tile chunks ---------------------------------------------------
+// A chunk is VEC consecutive elements of one state row, loaded with one
+// vector load and widened to float.
+template <int ST, int VEC>
+struct Chunk;
+
+template <int VEC>
+struct Chunk<ST_F32, VEC> {
+    static_assert(VEC == 4, "f32 chunks are 16 bytes");
+    f32x4 raw;
+    __device__ __forceinline__ void load(const void *S, size_t e) {
+        raw = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(static_cast<const float *>(S) + e));
+    }
+    __device__ __forceinline__ void widen(float *out, float) const {
+        out[0] = raw.x; out[1] = raw.y; out[2] = raw.z; out[3] = raw.w;
+    }
+};
+
+template <int VEC>
+struct Chunk<ST_BF16, VEC> {
+    static_assert(VEC == 8 || VEC == 4, "bf16 chunks are 16 or 8 bytes");
+    uint32_t raw[VEC / 2];
+    __device__ __forceinline__ void load(const void *S, size_t e) {
+        const uint16_t *p = static_cast<const uint16_t *>(S) + e;
+        if constexpr (VEC == 8) {
+            u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+            raw[0] = w.x; raw[1] = w.y; raw[2] = w.z; raw[3] = w.w;
+        } else {
+            u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+            raw[0] = w.x; raw[1] = w.y;
+        }
+    }
+    __device__ __forceinline__ void widen(float *out, float) const {
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) {
+            out[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu);
+            out[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
+        }
+    }
+};
+
+template <int VEC>
+struct Chunk<ST_FP8, VEC> {
+    static_assert(VEC == 16 || VEC == 8 || VEC == 4, "e4m3 chunks are 16, 8 or 4 bytes");
+    uint32_t raw[VEC / 4];
+    __device__ __forceinline__ void load(const void *S, size_t e) {
+        const uint8_t *p = static_cast<const uint8_t *>(S) + e;
+        if constexpr (VEC == 16) {
+            u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+            raw[0] = w.x; raw[1] = w.y; raw[2] = w.z; raw[3] = w.w;
+        } else if constexpr (VEC == 8) {
+            u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+            raw[0] = w.x; raw[1] = w.y;
+        } else {
+            raw[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+        }
+    }
+    // widened values are the codes' values times the per-head scale
+    __device__ __forceinline__ void widen(float *out, float scale) const {
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) {
+            fp8x4_to_f32(raw[i], out + 4 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) out[i] *= scale;
+    }
+};
+
+// ---- lane exchanges --------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Value of the partner lane for a butterfly step on lane bit `bit`.  The
+// partner differs from this lane in `bit` and possibly in lower bits, never
+// in higher ones: bit 0 -> lane^1, bit 1 -> lane^2 (quad permutes), bit 2 ->
+// lane^7 (row half-mirror), bit 3 -> lane^15 (row mirror), bits 4, 5 ->
+// lane^16, lane^32 (ds_bpermute).  Reduction steps taken from the top bit
+// down therefore always combine lanes that hold the same partial set, and a
+// full sequence of steps covers every lane of the group.
+__device__ __forceinline__ float lane_partner(float x, int bit) {
+    switch (bit) {
+        case 0: return dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+        case 1: return dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+        case 2: return dpp_mov<0x141>(x);   // row_half_mirror
+        case 3: return dpp_mov<0x140>(x);   // row_mirror
+        case 4: return __shfl_xor(x, 16);
+        default: return __shfl_xor(x, 32);
+    }
+}
+
+// Sum over aligned groups of TS lanes (TS a power of two, <= 64); every lane
+// of the group gets the sum.
+template <int TS>
+__device__ __forceinline__ float group_sum(float x) {
+    constexpr int K = __builtin_ctz(TS);
+#pragma unroll
+    for (int bit = K - 1; bit >= 0; --bit) x += lane_partner(x, bit);
+    return x;
+}
+
+// ---- reductions over the lanes that share a state row --------------------
+// v[i][w] holds a lane's partial sum for row-slot i (ITER of them) and query
+// w.  The LPR lanes of a row group (aligned, inside one wavefront) cover one
+// row each iteration.  Halving steps exchange half of the remaining row-slots
+// with the partner lane (top lane bits first), so every exchange moves useful
+// data; once a single slot is left, plain butterfly steps finish it.  On
+// return slots 0..FINAL-1 are complete; slot e of a lane stands for original
+// row-slot  e + FINAL * halving_index(lane).
+template <int ITER, int LPR>
+struct RowReduce {
+    static constexpr int K = __builtin_ctz(LPR);            // lane bits of a group
+    static constexpr int I = __builtin_ctz(ITER);
+    static constexpr int NH = (I < K) ? I : K;              // halving steps
+    static constexpr int FINAL = ITER >> NH;                // slots left per lane
+    static constexpr int PLAIN = K - NH;                    // plain butterfly steps
+
+    static __device__ __forceinline__ int halving_index(int lane) {
+        return NH == 0 ? 0 : ((lane & (LPR - 1)) >> PLAIN) & ((1 << NH) - 1);
+    }
+    // lanes that write the finished sums (the others hold copies)
+    static __device__ __forceinline__ bool writer(int lane) {
+        return (lane & ((1 << PLAIN) - 1)) == 0;
+    }
+
+    template <int WM>
+    static __device__ __forceinline__ void run(float (&v)[ITER][WM], int lane) {
+#pragma unroll
+        for (int s = 0; s < NH; ++s) {
+            const int bit = K - 1 - s;
+            const int half = ITER >> (s + 1);
+            const bool upper = (lane >> bit) & 1;
+#pragma unroll
+            for (int e = 0; e < half; ++e) {
+#pragma unroll
+                for (int w = 0; w < WM; ++w) {
+                    const float keep = upper ? v[e + half][w] : v[e][w];
+                    const float send = upper ? v[e][w] : v[e + half][w];
+                    v[e][w] = keep + lane_partner(send, bit);
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < PLAIN; ++s) {
+            const int bit = PLAIN - 1 - s;
+#pragma unroll
+            for (int w = 0; w < WM; ++w) v[0][w] += lane_partner(v[0][w], bit);
+        }
+    }
+};
+
+// ---- per-sequence error bits ----------------------------------------------
+__device__ __forceinline__ void raise_seq_error(int32_t *err, int b, int bits) {
+    atomicOr(err, bits);
+    atomicOr(err + 1 + b, bits);
+}
+
+}  // namespace replay

@@ -1,0 +1,267 @@
+// flush.hip -- rank-c checkpoint update and low-precision copy for gfx950.
+//
+// For every (sequence, head) whose ring holds c >= max(min_count, 1) entries:
+//     S0 <- abar_c S0 + sum_{j=1..c} s_{j,c} v_j k_j^T
+// (page "ReplaySSM: Cachear Inputs, No Estado", section "Los dos caminos",
+// eq. "Ruta estado y salida"; "Decodificacion estandar", step 4: the
+// buffer is folded into the checkpoint and written once), with
+// abar_c = prod_{m<=c} a_m and s_{j,c} = dt_j prod_{j<m<=c} a_m.  The new
+// checkpoint is written to the float32 master and/or a bf16 / e4m3 copy
+// (page "ReplaySSM: Cache SSM Inputs, Not State", Abstract: a low-precision
+// copy serves outputs, a higher-precision checkpoint takes the updates).
+// e4m3 copies carry one scale per head: scale = amax/448 (1 if amax = 0),
+// code = e4m3(x / scale), round to nearest even, saturating.
+//
+// One workgroup per head.  The tile streams through registers (16-byte
+// master chunks); s_j v_j (P x c) and k_j (c x N) are staged in LDS, so each
+// state element costs c FMAs against two LDS broadcasts per ring entry.
+// A second small kernel moves the base pointer once every head of the
+// sequence has read it.
+#include "device_common.h"
+
+namespace replay {
+
+template <int P, int N>
+struct FlushShape {
+    static constexpr int VEC = 4;
+    static constexpr int CHUNKS = P * N / VEC;
+    static constexpr int NT = CHUNKS < 256 ? CHUNKS : 256;
+    static constexpr int ITER = CHUNKS / NT;
+    static constexpr int LPR = N / VEC;
+    static constexpr int RPI = NT / LPR;
+    static_assert(CHUNKS % NT == 0 && NT % 64 == 0, "bad tiling");
+    static_assert(LPR <= 64 && 64 % LPR == 0, "row group must sit in a wavefront");
+};
+
+template <int P, int N, int SIN, int COPY, bool WRITE_MASTER, bool IOB>
+__global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs args) {
+    using Sh = FlushShape<P, N>;
+    constexpr int VEC = Sh::VEC, NT = Sh::NT, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+
+    extern __shared__ __align__(16) float smem[];   // U [P][c] then K [c][N]
+    __shared__ float s_a[kMaxRing], s_dt[kMaxRing], s_w[kMaxRing];
+    __shared__ float s_abar;
+    __shared__ float s_red[NT / 64];
+
+    constexpr int JG = NT / P;                      // thread groups over ring entries
+    constexpr int JPG = (kMaxRing + JG - 1) / JG;   // v values per thread
+    constexpr int KPT = (kMaxRing * (N / 4) + NT - 1) / NT;   // k pieces per thread
+    static_assert(NT % P == 0, "ring groups");
+
+    const RingView &r = args.r;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int b = lid / r.H, h = lid % r.H;
+    const int g = (h * r.G) / r.H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int L = r.L;
+    const size_t bh = (size_t)b * r.H + h;
+
+    const int base = r.base[b];
+    const int pos = r.pos[b];
+    int count = 0;
+    if (!args.force_empty) {
+        count = pos - base;
+        const int need = args.min_count > 1 ? args.min_count : 1;
+        if (count < need) return;  // uniform: nothing to fold for this sequence
+    }
+
+    // 1. tile loads, then every ring load in one batch
+    Chunk<SIN, VEC> ch[ITER];
+    const size_t tile = bh * (size_t)(P * N);
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) ch[i].load(args.S_in, tile + (size_t)(i * NT + tid) * VEC);
+    const float sc_in = (SIN == ST_FP8) ? args.scale_in[bh] : 1.0f;
+
+    const int bmod = base % L;
+    auto slot = [&](int j) { return ring_slot(bmod, j, L); };   // entry j (0-based) of the ring
+    const size_t gring = ((size_t)b * r.G + g) * L;
+    const size_t hring = bh * L;
+
+    // ring loads, all issued now from valid entries only (clamped indices;
+    // the clamped values are never used)
+    const int last = count > 0 ? count - 1 : 0;
+    float my_a = 1.f, my_dt = 0.f;
+    if (count > 0) {
+        const int sl = slot(tid < count ? tid : last);
+        my_a = r.a[hring + sl];
+        my_dt = r.dt[hring + sl];
+    }
+    const int vp = tid % P, vg = tid / P;
+    IoVec<IOB, 1> vraw[JPG];
+    IoVec<IOB, 4> kraw[KPT];
+    if (count > 0) {
+#pragma unroll
+        for (int i = 0; i < JPG; ++i) {
+            const int j = vg + i * JG;
+            vraw[i].load(r.v, (hring + slot(j < count ? j : last)) * P + vp);
+        }
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int piece = tid + i * NT;
+            const int j = piece / (N / 4), n = (piece % (N / 4)) * 4;
+            kraw[i].load(r.k, (gring + slot(j < count ? j : last)) * N + n);
+        }
+    }
+
+    // 2. segment weights of the c entries
+    if (tid < count) {
+        s_a[tid] = my_a;
+        s_dt[tid] = my_dt;
+    }
+    __syncthreads();
+    if (tid < count) {
+        float s = s_dt[tid];
+        for (int m = tid + 1; m < count; ++m) s *= s_a[m];
+        s_w[tid] = s;
+    }
+    if (tid == 0) {
+        float ab = 1.f;
+        for (int m = 0; m < count; ++m) ab *= s_a[m];
+        s_abar = ab;
+    }
+    __syncthreads();
+
+    // 3. stage U[p][j] = s_j v_j[p] and K[j][n] = k_j[n]
+    float *U = smem;
+    float *Ks = smem + P * count;
+#pragma unroll
+    for (int i = 0; i < JPG; ++i) {
+        const int j = vg + i * JG;
+        if (j < count) U[vp * count + j] = s_w[j] * vraw[i].value();
+    }
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int piece = tid + i * NT;
+        const int j = piece / (N / 4), n = (piece % (N / 4)) * 4;
+        if (j < count) {
+            float kk[4];
+            kraw[i].widen(kk);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ks[j * N + n + e] = kk[e];
+        }
+    }
+    __syncthreads();
+
+    // 4. x = abar * S0 + sum_j U[row][j] K[j][col]
+    const float abar = s_abar;
+    const int col0 = (tid % LPR) * VEC;
+    float x[ITER][VEC];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        ch[i].widen(x[i], sc_in);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[i][e] *= abar;
+    }
+    for (int j = 0; j < count; ++j) {
+        const f32x4 kk = *reinterpret_cast<const f32x4 *>(&Ks[j * N + col0]);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int row = i * RPI + tid / LPR;
+            const float u = U[row * count + j];
+            x[i][0] = fmaf(u, kk.x, x[i][0]);
+            x[i][1] = fmaf(u, kk.y, x[i][1]);
+            x[i][2] = fmaf(u, kk.z, x[i][2]);
+            x[i][3] = fmaf(u, kk.w, x[i][3]);
+        }
+    }
+
+    // 5. float32 master
+    if constexpr (WRITE_MASTER) {
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            f32x4 o = {x[i][0], x[i][1], x[i][2], x[i][3]};
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(args.S_out + tile + (size_t)(i * NT + tid) * VEC));
+        }
+    }
+
+    // 6. low-precision copy
+    if constexpr (COPY == ST_BF16) {
+        uint16_t *cp = static_cast<uint16_t *>(args.copy_out) + tile;
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            u32x2 o;
+            o.x = f32_to_bf16_bits(x[i][0]) | (f32_to_bf16_bits(x[i][1]) << 16);
+            o.y = f32_to_bf16_bits(x[i][2]) | (f32_to_bf16_bits(x[i][3]) << 16);
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(cp + (size_t)(i * NT + tid) * VEC));
+        }
+    } else if constexpr (COPY == ST_FP8) {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < ITER; ++i)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+#pragma unroll
+        for (int bit = 5; bit >= 0; --bit) amax = fmaxf(amax, lane_partner(amax, bit));
+        if (lane == 0) s_red[tid / 64] = amax;
+        __syncthreads();
+        amax = s_red[0];
+#pragma unroll
+        for (int i = 1; i < NT / 64; ++i) amax = fmaxf(amax, s_red[i]);
+        const float sig = amax > 0.f ? amax / 448.0f : 1.0f;   // correctly rounded divide
+        uint8_t *cp = static_cast<uint8_t *>(args.copy_out) + tile;
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const uint32_t o = f32x4_to_fp8(x[i][0] / sig, x[i][1] / sig, x[i][2] / sig, x[i][3] / sig);
+            __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(cp + (size_t)(i * NT + tid) * VEC));
+        }
+        if (tid == 0) args.scale_out[bh] = sig;
+    }
+}
+
+// base = pos for the sequences the flush kernel folded
+__global__ void commit_kernel(const int32_t *pos, int32_t *base, int32_t B, int32_t min_count,
+                              int32_t force_empty) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int p = pos[b];
+    const int need = min_count > 1 ? min_count : 1;
+    if (force_empty || p - base[b] >= need) base[b] = p;
+}
+
+template <int P, int N, int SIN, int COPY, bool WM>
+static hipError_t launch_one(const FlushArgs &a, hipStream_t s) {
+    using Sh = FlushShape<P, N>;
+    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
+    const size_t lds = (size_t)(P + N) * a.r.L * sizeof(float);
+    if (a.r.io_bf16)
+        flush_kernel<P, N, SIN, COPY, WM, true><<<blocks, Sh::NT, lds, s>>>(a);
+    else
+        flush_kernel<P, N, SIN, COPY, WM, false><<<blocks, Sh::NT, lds, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int P, int N>
+static hipError_t launch_pn(int st_in, int st_copy, bool wm, const FlushArgs &a, hipStream_t s) {
+    if (st_in == ST_F32 && wm) {           // separated: the float32 master takes the update
+        if (st_copy == ST_BF16) return launch_one<P, N, ST_F32, ST_BF16, true>(a, s);
+        if (st_copy == ST_FP8) return launch_one<P, N, ST_F32, ST_FP8, true>(a, s);
+        return launch_one<P, N, ST_F32, -1, true>(a, s);
+    }
+    if (st_in == ST_F32) {                 // shared mode, loading a float32 checkpoint
+        if (st_copy == ST_BF16) return launch_one<P, N, ST_F32, ST_BF16, false>(a, s);
+        if (st_copy == ST_FP8) return launch_one<P, N, ST_F32, ST_FP8, false>(a, s);
+        return hipErrorInvalidValue;
+    }
+    if (wm) return hipErrorInvalidValue;   // shared mode: the copy is the only checkpoint
+    if (st_in == ST_BF16 && st_copy == ST_BF16) return launch_one<P, N, ST_BF16, ST_BF16, false>(a, s);
+    if (st_in == ST_FP8 && st_copy == ST_FP8) return launch_one<P, N, ST_FP8, ST_FP8, false>(a, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_flush(int P, int N, int st_in, int st_copy, bool write_master, const FlushArgs &a,
+                        hipStream_t s) {
+    if (P == 16 && N == 16) return launch_pn<16, 16>(st_in, st_copy, write_master, a, s);
+    if (P == 64 && N == 64) return launch_pn<64, 64>(st_in, st_copy, write_master, a, s);
+    if (P == 64 && N == 128) return launch_pn<64, 128>(st_in, st_copy, write_master, a, s);
+    if (P == 128 && N == 128) return launch_pn<128, 128>(st_in, st_copy, write_master, a, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_commit(const RingView &r, int32_t *base, int32_t min_count, int32_t force_empty,
+                         hipStream_t s) {
+    const int nt = 256;
+    commit_kernel<<<(r.B + nt - 1) / nt, nt, 0, s>>>(r.pos, base, r.B, min_count, force_empty);
+    return hipGetLastError();
+}
+
+}  // namespace replay

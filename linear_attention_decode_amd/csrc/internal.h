@@ -1,0 +1,79 @@
+// internal.h -- private declarations shared by the HIP sources of libreplayssm.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/replayssm.h"
+
+namespace replay {
+
+// Storage kinds of a state tile.
+enum StateKind : int { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2 };
+
+// Largest ring and verify window the kernels are built for.
+constexpr int kMaxRing = 32;
+constexpr int kMaxWindow = 8;
+
+// Everything a kernel needs to find one layer's ring.
+struct RingView {
+    const void *q;      // [B][G][L][N]
+    const void *k;      // [B][G][L][N]
+    const void *v;      // [B][H][L][P]
+    const float *dt;    // [B][H][L]
+    const float *a;     // [B][H][L]
+    const int32_t *pos;
+    const int32_t *base;
+    int32_t *err;       // [B+1]
+    int32_t B, H, G, L;
+    int32_t io_bf16;
+};
+
+struct DecodeArgs {
+    RingView r;
+    const void *S;          // state tile source: f32 master or the copy
+    const float *scale;     // [B][H] for an e4m3 copy, else unused
+    float *y;               // [B][W][H][P]
+    int32_t W;
+};
+
+struct FlushArgs {
+    RingView r;
+    const void *S_in;       // f32 master (separated) or the copy (shared) or a load source
+    const float *scale_in;  // old per-head scale when S_in is an e4m3 copy
+    float *S_out;           // f32 master to write, or nullptr
+    void *copy_out;         // copy to write, or nullptr
+    float *scale_out;       // per-head scale to write (e4m3 copy), or nullptr
+    int32_t min_count;      // flush sequences with count >= max(min_count, 1)
+    int32_t force_empty;    // 1: treat every sequence as due with an empty ring (checkpoint load)
+};
+
+struct EagerArgs {
+    const float *S_in;
+    float *S_out;
+    const void *q, *k, *v;  // [B][G][N], [B][G][N], [B][H][P]
+    const float *dt, *a;    // [B][H]
+    float *y;               // [B][H][P]
+    int32_t B, H, G;
+    int32_t io_bf16;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_decode(int P, int N, int st, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_flush(int P, int N, int st_in, int st_copy, bool write_master, const FlushArgs &a,
+                        hipStream_t s);
+hipError_t launch_commit(const RingView &r, int32_t *base, int32_t min_count, int32_t force_empty,
+                         hipStream_t s);
+hipError_t launch_append(int P, int N, const RingView &r, void *ring_q, void *ring_k, void *ring_v,
+                         float *ring_dt, float *ring_a, int32_t *pos, int32_t W, const void *q,
+                         const void *k, const void *v, const float *dt, const float *a, hipStream_t s);
+hipError_t launch_rollback(const RingView &r, int32_t *pos, const int32_t *n_reject, hipStream_t s);
+hipError_t launch_fill_u32(void *dst, uint32_t value, size_t count, hipStream_t s);
+hipError_t launch_eager(int P, int N, const EagerArgs &a, hipStream_t s);
+hipError_t launch_eager_select(const float *snaps, int32_t W, const int32_t *n_accept, float *s,
+                               int32_t B, size_t head_elems_per_seq, hipStream_t st);
+hipError_t launch_probe(int mode, const void *src, void *dst, size_t bytes, hipStream_t s);
+
+bool shape_supported(int P, int N);
+
+}  // namespace replay

@@ -228,3 +228,26 @@ def named(name: str, **over) -> Workload:
     base.update(over)
     base.setdefault("config", CONFIG_ID[name])
     return Workload(**base)
+
+
+def dyadic_inputs(w: Workload, t0: int, t1: int, seqs=None) -> dict:
+    """Inputs whose every product and sum in the recurrence is exact in
+    float32 for short runs: a in {1, 1/2}, dt in {1, 2}, v integers in
+    [-4, 4], k and q one-hot.  Same layout and storage as step_inputs."""
+    B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
+    ts = np.arange(t0, t1, dtype=np.int64)
+    bs = np.arange(B, dtype=np.int64) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    Tn = 1 << 40
+    ig = _flat_index([Tn, B, G], [ts, bs, np.arange(G)])
+    hot_q = np.minimum((uniform(w.key("q"), ig) * N).astype(np.int64), N - 1)
+    hot_k = np.minimum((uniform(w.key("k"), ig) * N).astype(np.int64), N - 1)
+    q = (np.arange(N) == hot_q[..., None]).astype(np.float64)
+    k = (np.arange(N) == hot_k[..., None]).astype(np.float64)
+    iv = _flat_index([Tn, B, H, P], [ts, bs, np.arange(H), np.arange(P)])
+    v = np.floor(uniform(w.key("v"), iv) * 9.0) - 4.0
+    ih = _flat_index([Tn, B, H], [ts, bs, np.arange(H)])
+    u = uniform(w.key("dt"), ih)
+    dt = np.where(u < 0.5, 1.0, 2.0).astype(np.float32)
+    a = np.where(uniform(w.key("A"), ih) < 0.5, 1.0, 0.5).astype(np.float32)
+    return {"q": store(q, w.io_dtype), "k": store(k, w.io_dtype), "v": store(v, w.io_dtype),
+            "dt": dt, "a": a}
