@@ -251,3 +251,95 @@ def dyadic_inputs(w: Workload, t0: int, t1: int, seqs=None) -> dict:
     a = np.where(uniform(w.key("A"), ih) < 0.5, 1.0, 0.5).astype(np.float32)
     return {"q": store(q, w.io_dtype), "k": store(k, w.io_dtype), "v": store(v, w.io_dtype),
             "dt": dt, "a": a}
+
+
+# ---------------------------------------------------------------------------
+# The same recipe evaluated with torch on a device, for long full-batch runs.
+# Integer steps are bit-identical to the numpy path (uint64 arithmetic done
+# in int64 two's complement); the float64 transcendental functions of the
+# device may differ from the host's in the last bit, so a test that feeds
+# the oracle from this path copies the very device tensors back to the host.
+
+def _s64(x: int) -> int:
+    x &= 0xFFFFFFFFFFFFFFFF
+    return x - (1 << 64) if x >= (1 << 63) else x
+
+
+_GAMMA_S = _s64(0x9E3779B97F4A7C15)
+_M1_S = _s64(0xBF58476D1CE4E5B9)
+_M2_S = _s64(0x94D049BB133111EB)
+
+
+def _t_srl(z, s: int):
+    """logical right shift of int64 tensors"""
+    return (z >> s) & ((1 << (64 - s)) - 1)
+
+
+def _t_mix64(z):
+    z = z ^ _t_srl(z, 30)
+    z = z * _M1_S
+    z = z ^ _t_srl(z, 27)
+    z = z * _M2_S
+    return z ^ _t_srl(z, 31)
+
+
+def _t_uniform(key: int, idx):
+    z = _t_mix64(idx.mul(_GAMMA_S).add(_s64(key + _GAMMA_S)))   # key + (idx + 1) * gamma
+    import torch
+    return (_t_srl(z, 11).to(torch.float64) + 0.5) * (2.0 ** -53)
+
+
+def _t_normal(key: int, idx):
+    import torch
+    pair = idx >> 1
+    u1 = _t_uniform(key, pair * 2)
+    u2 = _t_uniform(key, pair * 2 + 1)
+    r = torch.sqrt(-2.0 * torch.log(u1))
+    th = (2.0 * math.pi) * u2
+    return torch.where((idx & 1).bool(), r * torch.sin(th), r * torch.cos(th))
+
+
+def _t_index(sizes, sel, device):
+    import torch
+    idx = torch.zeros([len(s) for s in sel], dtype=torch.int64, device=device)
+    mult = 1
+    for ax in range(len(sizes) - 1, -1, -1):
+        shape = [1] * len(sizes)
+        shape[ax] = len(sel[ax])
+        idx += (torch.as_tensor(np.asarray(sel[ax]), dtype=torch.int64, device=device) * mult).reshape(shape)
+        mult *= sizes[ax]
+    return idx
+
+
+def step_inputs_torch(w: Workload, t0: int, t1: int, device="cuda") -> dict:
+    """step_inputs evaluated on `device`; q, k, v come back as torch
+    bfloat16 / float32 tensors, dt and a as float32."""
+    import torch
+    B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
+    ts, bs = np.arange(t0, t1), np.arange(B)
+    Tn = 1 << 40
+    iq = _t_index([Tn, B, G, N], [ts, bs, np.arange(G), np.arange(N)], device)
+    q = _t_normal(w.key("q"), iq) * math.sqrt(1.0 / N)
+    k = _t_normal(w.key("k"), iq) * math.sqrt(1.0 / N)
+    del iq
+    iv = _t_index([Tn, B, H, P], [ts, bs, np.arange(H), np.arange(P)], device)
+    v = _t_normal(w.key("v"), iv)
+    del iv
+    idt = _t_index([Tn, B, H], [ts, bs, np.arange(H)], device)
+    x = _t_normal(w.key("dt"), idt)
+    dt32 = (torch.nn.functional.softplus(x) * w.dt_scale).to(torch.float32)
+    A = torch.as_tensor(decay_A(w), dtype=torch.float64, device=device)
+    a32 = torch.exp(dt32.to(torch.float64) * A).to(torch.float32)
+    io = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
+    return {"q": q.to(torch.float32).to(io), "k": k.to(torch.float32).to(io),
+            "v": v.to(torch.float32).to(io), "dt": dt32, "a": a32}
+
+
+def to_storage(t) -> np.ndarray:
+    """A device tensor from step_inputs_torch -> the numpy storage array the
+    oracle widens (bf16 as uint16 patterns)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
