@@ -138,6 +138,35 @@ DECODE_SOURCES = ["linear_attention_decode_amd/csrc/decode_impl.h",
                   "linear_attention_decode_amd/csrc/device_common.h"]
 
 
+def _bench_eager(args, w, pool, y):
+    """The eager per-token baseline on the same inputs, timed like the steps."""
+    import torch
+    import linear_attention_decode_amd as lad
+    B, H, G, P, N, L = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len
+    cfg = lad.ReplayConfig(B, H, G, P, N, L, lad.BF16, lad.NONE, 0)
+    S = torch.zeros((B, H, P, N), dtype=torch.float32, device="cuda")
+
+    def estep(t):
+        i = t % POOL_STEPS
+        lad.replay_eager_step(cfg, S, S, pool["q"][i], pool["k"][i], pool["v"][i], pool["dt"][i],
+                              pool["a"][i], y)
+    for t in range(args.warmup):
+        estep(t)
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    for k in range(args.steps):
+        estep(args.warmup + k)
+    torch.cuda.synchronize()
+    e1 = time.perf_counter()
+    eager_tps = B * args.steps / (e1 - e0)
+    eager_gbs = eager_bytes(w) * args.steps / (e1 - e0) / 1e9
+    del S
+    torch.cuda.empty_cache()
+    return {"value": eager_tps, "unit": "tokens/s", "ms_per_step": 1e3 * (e1 - e0) / args.steps,
+            "achieved_GBs": eager_gbs}
+
+
+
 # ---------------------------------------------------------------------------
 def bench_decode(args):
     import torch
@@ -190,24 +219,7 @@ def bench_decode(args):
     del layer
     torch.cuda.empty_cache()
 
-    # eager baseline on the same inputs
-    cfg = lad.ReplayConfig(B, H, G, P, N, L, lad.BF16, lad.NONE, 0)
-    S = torch.zeros((B, H, P, N), dtype=torch.float32, device="cuda")
-
-    def estep(t):
-        i = t % POOL_STEPS
-        lad.replay_eager_step(cfg, S, S, pool["q"][i], pool["k"][i], pool["v"][i], pool["dt"][i],
-                              pool["a"][i], y)
-    for t in range(args.warmup):
-        estep(t)
-    torch.cuda.synchronize()
-    e0 = time.perf_counter()
-    for k in range(args.steps):
-        estep(args.warmup + k)
-    torch.cuda.synchronize()
-    e1 = time.perf_counter()
-    eager_tps = B * args.steps / (e1 - e0)
-    eager_gbs = eager_bytes(w) * args.steps / (e1 - e0) / 1e9
+    eager_out = None if args.no_eager else _bench_eager(args, w, pool, y)
 
     window_replay = sum(decode_bytes(w, c, 1, st_bytes) for c in range(1, L + 1)) \
         + flush_bytes(w, L, 0 if st_bytes == 4 else st_bytes) \
@@ -235,9 +247,8 @@ def bench_decode(args):
                      "kernel": "decode (output-only)", "avg_launch_us": avg_dec_us,
                      "algorithmic_bytes_per_launch": dec_bytes / len(counts)},
         "flush_avg_us": 1e3 * sum(fl_ms) / max(1, len(fl_ms)),
-        "eager": {"value": eager_tps, "unit": "tokens/s", "ms_per_step": 1e3 * (e1 - e0) / args.steps,
-                  "achieved_GBs": eager_gbs},
-        "speedup_vs_eager": (B * args.steps / elapsed) / eager_tps,
+        "eager": eager_out,
+        "speedup_vs_eager": (B * args.steps / elapsed) / eager_out["value"] if eager_out else None,
         "window_bytes_ratio_vs_eager": window_replay / window_eager,
     }
     if not args.no_cpu_baseline:
@@ -254,6 +265,9 @@ def main():
     ap.add_argument("--read", default="f32", choices=["f32", "bf16", "fp8"],
                     help="checkpoint the outputs read: the float32 master or a bf16 / e4m3 copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-eager", action="store_true", help="skip the eager baseline timing")
+    ap.add_argument("--probe-copy-gib", type=float, default=0.0,
+                    help="first run the plain copy probe over this many GiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path needs no collective and this build runs "
@@ -263,6 +277,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.probe_copy_gib > 0:
+        import linear_attention_decode_amd as lad
+        nbytes = int(args.probe_copy_gib * (1 << 30)) // 16 * 16
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        lad.replay_stream_probe(1, src, dst, nbytes)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     out = bench_decode(args)
     print(json.dumps(out))
 
