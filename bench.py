@@ -61,6 +61,16 @@ def flush_bytes(w, count, copy_bytes=0, io=2):
         + (B * H * 4 if copy_bytes == 1 else 0)
 
 
+def step_bytes(w, count, fold, io=2):
+    """One fused step launch; `count` includes this step's token, which is read
+    from the inputs and written to the ring."""
+    B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
+    per_entry = H * P * io + H * 8 + G * N * io
+    token = H * P * io + H * 8 + 2 * G * N * io          # v, (dt, a), q, k of the new token
+    return (state_bytes(w) * (2 if fold else 1)
+            + B * ((count - 1) * per_entry + 2 * token + H * P * 4))
+
+
 def eager_bytes(w, io=2):
     B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
     return 2 * state_bytes(w) + B * (H * P * io + H * 8 + 2 * G * N * io + H * P * 4)
@@ -136,6 +146,8 @@ def _counter_traffic(kernel_files, summary_name):
 
 DECODE_SOURCES = ["linear_attention_decode_amd/csrc/decode_impl.h",
                   "linear_attention_decode_amd/csrc/device_common.h"]
+STEP_SOURCES = ["linear_attention_decode_amd/csrc/step.hip",
+                "linear_attention_decode_amd/csrc/device_common.h"]
 
 
 def _bench_eager(args, w, pool, y):
@@ -183,7 +195,16 @@ def bench_decode(args):
 
     def step(t, ev=None):
         i = t % POOL_STEPS
-        layer.append(1, pool["q"][i], pool["k"][i], pool["v"][i], pool["dt"][i], pool["a"][i])
+        args_t = (pool["q"][i], pool["k"][i], pool["v"][i], pool["dt"][i], pool["a"][i])
+        if args.api == "step":
+            # one fused launch: append + decode, or append + fold when the ring fills
+            if ev is not None:
+                ev[0].record(stream)
+            layer.step(*args_t, y, flush_at=L)
+            if ev is not None:
+                ev[1].record(stream)
+            return
+        layer.append(1, *args_t)
         if ev is not None:
             ev[0].record(stream)
         layer.decode(y)
@@ -208,13 +229,25 @@ def bench_decode(args):
     word, _ = layer.get_error()
     assert word == 0, f"device error bits {word}"
     elapsed = t1 - t0
-    dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    fl_ms = [evs[k][2].elapsed_time(evs[k][3]) for k in range(args.steps) if (args.warmup + k + 1) % L == 0]
     counts = [((args.warmup + k) % L) + 1 for k in range(args.steps)]
-    dec_bytes = sum(decode_bytes(w, c, 1, st_bytes) for c in counts)
-    dec_time = sum(dec_ms) / 1e3
-    avg_dec_us = 1e3 * sum(dec_ms) / len(dec_ms)
-    achieved = dec_bytes / dec_time / 1e9
+    if args.api == "step":
+        # the dominant kernel is the fused step kernel itself
+        step_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        folds = [c >= L for c in counts]
+        dec_ms = [m for m, f in zip(step_ms, folds) if not f]
+        fl_ms = [m for m, f in zip(step_ms, folds) if f]
+        kernel_bytes = sum(step_bytes(w, c, c >= L) for c in counts)
+        kernel_time = sum(step_ms) / 1e3
+        avg_us = 1e3 * sum(step_ms) / len(step_ms)
+        kernel_name = "step (append + output-only decode, or append + fold on full rings)"
+    else:
+        dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        fl_ms = [evs[k][2].elapsed_time(evs[k][3]) for k in range(args.steps) if (args.warmup + k + 1) % L == 0]
+        kernel_bytes = sum(decode_bytes(w, c, 1, st_bytes) for c in counts)
+        kernel_time = sum(dec_ms) / 1e3
+        avg_us = 1e3 * sum(dec_ms) / len(dec_ms)
+        kernel_name = "decode (output-only)"
+    achieved = kernel_bytes / kernel_time / 1e9
     layer.close()
     del layer
     torch.cuda.empty_cache()
@@ -225,7 +258,10 @@ def bench_decode(args):
         + flush_bytes(w, L, 0 if st_bytes == 4 else st_bytes) \
         + B * L * 2 * (H * P * 2 + H * 8 + 2 * G * N * 2)            # appends: read input + write ring
     window_eager = L * eager_bytes(w)
-    traffic = _counter_traffic(DECODE_SOURCES, f"decode_kernel_{args.read}_b256_h128_counters.txt")
+    if args.api == "step":
+        traffic = _counter_traffic(STEP_SOURCES, "step_kernel_f32_b256_h128_counters.txt")
+    else:
+        traffic = _counter_traffic(DECODE_SOURCES, f"decode_kernel_{args.read}_b256_h128_counters.txt")
     out = {
         "metric": METRIC,
         "value": B * args.steps / elapsed,
@@ -241,11 +277,12 @@ def bench_decode(args):
         "data": f"synthetic (seeded SplitMix64/Box-Muller, {POOL_STEPS} distinct steps cycled)",
         "config": {"workload": "Mamba-2-shaped SSM layer, standard decode", "batch": B, "heads": H,
                    "groups": G, "head_dim": P, "state_dim": N, "ring_len": L, "io": "bf16",
-                   "checkpoint": "f32", "read_copy": args.read, "flush_every": L},
+                   "checkpoint": "f32", "read_copy": args.read, "flush_every": L, "api": args.api},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "decode (output-only)", "avg_launch_us": avg_dec_us,
-                     "algorithmic_bytes_per_launch": dec_bytes / len(counts)},
+                     "kernel": kernel_name, "avg_launch_us": avg_us,
+                     "algorithmic_bytes_per_launch": kernel_bytes / len(counts)},
+        "decode_avg_us": 1e3 * sum(dec_ms) / max(1, len(dec_ms)),
         "flush_avg_us": 1e3 * sum(fl_ms) / max(1, len(fl_ms)),
         "eager": eager_out,
         "speedup_vs_eager": (B * args.steps / elapsed) / eager_out["value"] if eager_out else None,
@@ -262,6 +299,8 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="decode", choices=["decode"])
+    ap.add_argument("--api", default="step", choices=["step", "calls"],
+                    help="step: one fused replay_step launch per step; calls: append, decode, flush")
     ap.add_argument("--read", default="f32", choices=["f32", "bf16", "fp8"],
                     help="checkpoint the outputs read: the float32 master or a bf16 / e4m3 copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define REPLAY_ABI_VERSION 1
+#define REPLAY_ABI_VERSION 2
 
 typedef enum {
     REPLAY_OK = 0,
@@ -108,6 +108,8 @@ typedef struct {
     int32_t *pos;       /* [B] tokens appended and not rolled back */
     int32_t *base;      /* [B] pos at the last flush; count = pos - base */
     int32_t *err;       /* [B + 1] error bits: err[0] = OR over sequences, err[1 + b] per sequence */
+    int32_t *sync;      /* [B] arrival counters of replay_step; zeroed by replay_init and zero
+                           again whenever no call is in flight */
 } replay_buffers;
 
 typedef struct replay_handle replay_handle;
@@ -118,9 +120,9 @@ const char *replay_status_string(replay_status s);
 /* REPLAY_ABI_VERSION of the built library. */
 int32_t replay_abi_version(void);
 
-/* Bytes needed by each replay_buffers field, in field order (11 entries);
+/* Bytes needed by each replay_buffers field, in field order (12 entries);
    0 for a field the configuration does not use.  Host only. */
-replay_status replay_buffer_bytes(const replay_config *cfg, size_t bytes[11]);
+replay_status replay_buffer_bytes(const replay_config *cfg, size_t bytes[12]);
 
 /* Validate `cfg` and `bufs`, create a handle, and enqueue the initial state:
    checkpoint 0 (page "ReplaySSM: Cachear Inputs, No Estado", eq. "Forma
@@ -177,6 +179,22 @@ replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *s
    the c = count entries, then base = pos, and the copy (and its per-head
    scale) is rewritten from the new checkpoint.  Other sequences: no-op. */
 replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream);
+
+/* One standard decode step for every sequence: append one token, produce its
+   output and, where the ring then holds count >= max(flush_at, 1) entries,
+   fold it into the checkpoint (page "ReplaySSM: Cachear Inputs, No Estado",
+   "Decodificacion estandar": buffer the inputs, output by the output-only
+   route, flush when the buffer is full).  The output of a folding step is
+   taken from the new checkpoint, y = S_new q (eq. "Ruta estado y salida",
+   the route the flush needs), so the checkpoint is read once per step.
+   Equivalent to replay_append(W=1); replay_decode; replay_flush(flush_at)
+   up to the rounding of that route.  q, k: [B][G][N]; v: [B][H][P] (io
+   dtype); dt, a: [B][H] f32; y: [B][H][P] f32.  With a float32 checkpoint
+   read (read_copy == NONE) it is one kernel launch; with a copy it runs the
+   append, decode and flush kernels in turn.  Errors as for replay_append
+   (the sequence is unchanged and its y is NaN). */
+replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v,
+                          const float *dt, const float *a, float *y, int32_t flush_at, void *stream);
 
 /* Synchronise `stream`, copy the error bits to the host and clear them on the
    device.  *word = OR over sequences; per_seq (may be NULL): host int32 [B]. */

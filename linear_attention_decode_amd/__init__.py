@@ -20,7 +20,7 @@ __all__ = [
     "SEQERR_TOO_FEW", "SEQERR_POS_OVERFLOW", "EXPORTS",
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
-    "replay_verify", "replay_rollback", "replay_flush", "replay_get_error",
+    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 ]
 
@@ -33,7 +33,7 @@ SEQERR_RING_OVERFLOW, SEQERR_ROLLBACK_RANGE, SEQERR_TOO_FEW, SEQERR_POS_OVERFLOW
 EXPORTS = (
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
-    "replay_verify", "replay_rollback", "replay_flush", "replay_get_error",
+    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 )
 
@@ -48,7 +48,7 @@ class ReplayConfig(ctypes.Structure):
 
 
 BUFFER_FIELDS = ("s_master", "s_copy", "s_scale", "ring_q", "ring_k", "ring_v", "ring_dt",
-                 "ring_a", "pos", "base", "err")
+                 "ring_a", "pos", "base", "err", "sync")
 
 
 class ReplayBuffers(ctypes.Structure):
@@ -77,6 +77,7 @@ def _load():
     L.replay_verify.argtypes = [_VP, _I32, _VP, _VP]
     L.replay_rollback.argtypes = [_VP, _VP, _VP]
     L.replay_flush.argtypes = [_VP, _I32, _VP]
+    L.replay_step.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
     L.replay_get_error.argtypes = [_VP, ctypes.POINTER(_I32), _VP, _VP]
     L.replay_eager_step.argtypes = [ctypes.POINTER(ReplayConfig)] + [_VP] * 9
     L.replay_eager_select.argtypes = [ctypes.POINTER(ReplayConfig), _VP, _I32, _VP, _VP, _VP]
@@ -124,7 +125,7 @@ def replay_abi_version() -> int:
 
 
 def replay_buffer_bytes(cfg: ReplayConfig):
-    out = (ctypes.c_size_t * 11)()
+    out = (ctypes.c_size_t * len(BUFFER_FIELDS))()
     _check(lib.replay_buffer_bytes(ctypes.byref(cfg), out), "replay_buffer_bytes")
     return dict(zip(BUFFER_FIELDS, [int(x) for x in out]))
 
@@ -165,6 +166,11 @@ def replay_flush(h, min_count, stream=None):
     _check(lib.replay_flush(h, min_count, _stream(stream)), "replay_flush")
 
 
+def replay_step(h, q, k, v, dt, a, y, flush_at, stream=None):
+    _check(lib.replay_step(h, _ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a), _ptr(y), flush_at,
+                           _stream(stream)), "replay_step")
+
+
 def replay_get_error(h, batch: int, stream=None):
     """Returns (word, per_sequence list)."""
     word = _I32()
@@ -199,7 +205,8 @@ class ReplayLayer:
     Tensors (torch, on `device`): s_master [B,H,P,N] f32 (absent in shared
     mode), s_copy [B,H,P,N] bf16/uint8 (when read_copy is set), s_scale
     [B,H] f32 (e4m3 copy), ring_q/ring_k [B,G,L,N], ring_v [B,H,L,P] (io
-    dtype), ring_dt/ring_a [B,H,L] f32, pos/base [B] int32, err [B+1] int32.
+    dtype), ring_dt/ring_a [B,H,L] f32, pos/base [B] int32, err [B+1] int32,
+    sync [B] int32.
     """
 
     def __init__(self, batch, heads, groups, head_dim, state_dim, ring_len, io_dtype="bf16",
@@ -219,6 +226,7 @@ class ReplayLayer:
             "ring_k": ((B, G, L, N), iot), "ring_v": ((B, H, L, P), iot),
             "ring_dt": ((B, H, L), torch.float32), "ring_a": ((B, H, L), torch.float32),
             "pos": ((B,), torch.int32), "base": ((B,), torch.int32), "err": ((B + 1,), torch.int32),
+            "sync": ((B,), torch.int32),
         }
         self.t = {}
         for name in BUFFER_FIELDS:
@@ -252,6 +260,9 @@ class ReplayLayer:
 
     def flush(self, min_count, stream=None):
         replay_flush(self.h, min_count, stream)
+
+    def step(self, q, k, v, dt, a, y, flush_at=None, stream=None):
+        replay_step(self.h, q, k, v, dt, a, y, self.cfg.ring_len if flush_at is None else flush_at, stream)
 
     def load_checkpoint(self, s_src, stream=None):
         replay_load_checkpoint(self.h, s_src, stream)

@@ -18,7 +18,7 @@ struct replay_handle {
 
 namespace {
 
-constexpr int kNumBufferFields = 11;
+constexpr int kNumBufferFields = 12;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -70,11 +70,12 @@ void buffer_bytes(const replay_config &c, size_t out[kNumBufferFields]) {
     out[8] = B * 4;                                                                     // pos
     out[9] = B * 4;                                                                     // base
     out[10] = (B + 1) * 4;                                                              // err
+    out[11] = B * 4;                                                                    // sync
 }
 
 const void *field(const replay_buffers &b, int i) {
     const void *f[kNumBufferFields] = {b.s_master, b.s_copy, b.s_scale, b.ring_q, b.ring_k, b.ring_v,
-                                       b.ring_dt,  b.ring_a, b.pos,     b.base,   b.err};
+                                       b.ring_dt,  b.ring_a, b.pos,     b.base,   b.err,    b.sync};
     return f[i];
 }
 
@@ -163,7 +164,7 @@ const char *replay_status_string(replay_status s) {
 
 int32_t replay_abi_version(void) { return REPLAY_ABI_VERSION; }
 
-replay_status replay_buffer_bytes(const replay_config *cfg, size_t bytes[11]) {
+replay_status replay_buffer_bytes(const replay_config *cfg, size_t bytes[12]) {
     replay_status st = check_config(cfg);
     if (st != REPLAY_OK) return st;
     if (!bytes) return REPLAY_ERR_INVALID_ARG;
@@ -199,6 +200,7 @@ replay_status replay_init(const replay_config *cfg, const replay_buffers *bufs, 
     if (e == hipSuccess) e = launch_fill_u32(h->bufs.pos, 0u, need[8] / 4, s);
     if (e == hipSuccess) e = launch_fill_u32(h->bufs.base, 0u, need[9] / 4, s);
     if (e == hipSuccess) e = launch_fill_u32(h->bufs.err, 0u, need[10] / 4, s);
+    if (e == hipSuccess) e = launch_fill_u32(h->bufs.sync, 0u, need[11] / 4, s);
     if (e != hipSuccess) {
         delete h;
         return REPLAY_ERR_HIP;
@@ -249,6 +251,47 @@ replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *s
 replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream) {
     if (!h) return REPLAY_ERR_INVALID_ARG;
     return run_flush(h, nullptr, min_count, as_stream(stream));
+}
+
+replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v, const float *dt,
+                          const float *a, float *y, int32_t flush_at, void *stream) {
+    if (!h || !q || !k || !v || !dt || !a || !y) return REPLAY_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a) || !aligned4(y))
+        return REPLAY_ERR_INVALID_ARG;
+    const replay_config &c = h->cfg;
+    hipStream_t s = as_stream(stream);
+    if (c.read_copy != REPLAY_NONE) {
+        // copies: the append, decode and flush kernels in turn
+        replay_status st = replay_append(h, 1, q, k, v, dt, a, stream);
+        if (st != REPLAY_OK) return st;
+        st = run_verify(h, 1, y, s);
+        if (st != REPLAY_OK) return st;
+        return run_flush(h, nullptr, flush_at, s);
+    }
+    StepArgs sa;
+    sa.ring_q = h->bufs.ring_q;
+    sa.ring_k = h->bufs.ring_k;
+    sa.ring_v = h->bufs.ring_v;
+    sa.ring_dt = h->bufs.ring_dt;
+    sa.ring_a = h->bufs.ring_a;
+    sa.pos = h->bufs.pos;
+    sa.base = h->bufs.base;
+    sa.err = h->bufs.err;
+    sa.sync = h->bufs.sync;
+    sa.S = h->bufs.s_master;
+    sa.q = q;
+    sa.k = k;
+    sa.v = v;
+    sa.dt = dt;
+    sa.a = a;
+    sa.y = y;
+    sa.B = c.batch;
+    sa.H = c.heads;
+    sa.G = c.groups;
+    sa.L = c.ring_len;
+    sa.flush_at = flush_at;
+    sa.io_bf16 = c.io_dtype == REPLAY_BF16;
+    return from_hip(launch_step(c.head_dim, c.state_dim, sa, s));
 }
 
 replay_status replay_get_error(replay_handle *h, int32_t *word, int32_t *per_seq, void *stream) {

@@ -39,10 +39,6 @@ struct DecodeShape {
     static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row group must sit in a wavefront");
 };
 
-__device__ __forceinline__ float bcast(float x, int lane) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
-}
-
 // The ring wavefront's work for one (sequence, head): group dots, segment
 // weights and the ring term, all in registers; results go to LDS.
 //   s_r[w][p] = sum_{j<=t_w} s_{j,t_w} (k_j . q_{t_w}) v_j[p],   s_abar[w] = abar_{t_w}
@@ -95,22 +91,15 @@ __device__ __forceinline__ void ring_wave(const RingView &r, int lane, int b, in
     }
 
     // dots c[w][j], then moved so that lane j holds c[w][j]
-    float qq[WM][8];
-#pragma unroll
-    for (int w = 0; w < WM; ++w) qraw[w].widen(qq[w]);
     float cw[WM];
 #pragma unroll
     for (int w = 0; w < WM; ++w) cw[w] = 0.f;
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
-        float kk[8];
-        kraw[i].widen(kk);
 #pragma unroll
         for (int w = 0; w < WM; ++w) {
             if (w < W) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) d = fmaf(kk[e], qq[w][e], d);
+                float d = dot8(kraw[i], qraw[w]);
                 d = group_sum<TS>(d);
                 const float moved = __shfl(d, (lane % RPW) * TS);
                 if (lane / RPW == i) cw[w] = moved;

@@ -170,6 +170,34 @@ struct IoVec<false, 1> {
     __device__ __forceinline__ float value() const { return r; }
 };
 
+// k . q over 8 io elements held raw.  bf16 pairs go through the packed bf16
+// dot instruction (v_dot2c_f32_bf16: the products of bf16 values are exact in
+// float32), float32 elements through an FMA chain; no widened copies are
+// kept in registers.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot8(const IoVec<true, 8> &k, const IoVec<true, 8> &q) {
+    float d = 0.f;
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.r.x), __builtin_bit_cast(bf16x2_t, q.r.x), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.r.y), __builtin_bit_cast(bf16x2_t, q.r.y), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.r.z), __builtin_bit_cast(bf16x2_t, q.r.z), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.r.w), __builtin_bit_cast(bf16x2_t, q.r.w), d, false);
+    return d;
+}
+
+__device__ __forceinline__ float dot8(const IoVec<false, 8> &k, const IoVec<false, 8> &q) {
+    float d = 0.f;
+    d = fmaf(k.a.x, q.a.x, d);
+    d = fmaf(k.a.y, q.a.y, d);
+    d = fmaf(k.a.z, q.a.z, d);
+    d = fmaf(k.a.w, q.a.w, d);
+    d = fmaf(k.b.x, q.b.x, d);
+    d = fmaf(k.b.y, q.b.y, d);
+    d = fmaf(k.b.z, q.b.z, d);
+    d = fmaf(k.b.w, q.b.w, d);
+    return d;
+}
+
 // Ring slot of entry j (0-based, oldest first) for a ring that starts at
 // slot bmod = base mod L; valid for 0 <= j < L.
 __device__ __forceinline__ int ring_slot(int bmod, int j, int L) {
@@ -275,6 +303,11 @@ __device__ __forceinline__ float lane_partner(float x, int bit) {
     }
 }
 
+// Value of lane `lane` (a wavefront-uniform index) broadcast to all lanes.
+__device__ __forceinline__ float bcast(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
 // Sum over aligned groups of TS lanes (TS a power of two, <= 64); every lane
 // of the group gets the sum.
 template <int TS>
@@ -334,6 +367,17 @@ struct RowReduce {
         }
     }
 };
+
+// ---- barriers -------------------------------------------------------------
+// Workgroup barrier that publishes LDS only.  __syncthreads() also waits for
+// every outstanding global store and atomic of the arriving wavefronts; where
+// those need not be visible inside the workgroup, this one lets them finish
+// in the background.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ---- per-sequence error bits ----------------------------------------------
 __device__ __forceinline__ void raise_seq_error(int32_t *err, int b, int bits) {

@@ -48,6 +48,20 @@ struct FlushArgs {
     int32_t force_empty;    // 1: treat every sequence as due with an empty ring (checkpoint load)
 };
 
+// One fused standard decode step (float32 checkpoint).
+struct StepArgs {
+    void *ring_q, *ring_k, *ring_v;   // [B][G][L][N] x2, [B][H][L][P]
+    float *ring_dt, *ring_a;          // [B][H][L]
+    int32_t *pos, *base, *err, *sync;
+    float *S;                         // [B][H][P][N] master, read and (when folding) written
+    const void *q, *k, *v;            // [B][G][N] x2, [B][H][P]
+    const float *dt, *a;              // [B][H]
+    float *y;                         // [B][H][P]
+    int32_t B, H, G, L;
+    int32_t flush_at;
+    int32_t io_bf16;
+};
+
 struct EagerArgs {
     const float *S_in;
     float *S_out;
@@ -70,6 +84,7 @@ hipError_t launch_append(int P, int N, const RingView &r, void *ring_q, void *ri
 hipError_t launch_rollback(const RingView &r, int32_t *pos, const int32_t *n_reject, hipStream_t s);
 hipError_t launch_fill_u32(void *dst, uint32_t value, size_t count, hipStream_t s);
 hipError_t launch_eager(int P, int N, const EagerArgs &a, hipStream_t s);
+hipError_t launch_step(int P, int N, const StepArgs &a, hipStream_t s);
 hipError_t launch_eager_select(const float *snaps, int32_t W, const int32_t *n_accept, float *s,
                                int32_t B, size_t head_elems_per_seq, hipStream_t st);
 hipError_t launch_probe(int mode, const void *src, void *dst, size_t bytes, hipStream_t s);

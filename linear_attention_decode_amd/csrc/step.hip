@@ -1,0 +1,347 @@
+// step.hip -- one fused standard decode step for a float32 checkpoint.
+//
+// For every (sequence, head), in one launch: append this step's token to
+// the ring, then either
+//   output-only route  y = abar_t (S0 q) + sum_{j<=t} s_{j,t} v_j (k_j . q)
+//   (page "ReplaySSM: Cachear Inputs, No Estado", section "Los dos caminos",
+//   eq. "Ruta solo salida"), or, when the ring then holds count >= flush_at
+//   entries, the state-and-output route that the flush needs (same section,
+//   eq. "Ruta estado y salida"):
+//     S_new = abar_c S0 + sum_j s_{j,c} v_j k_j^T   (written back once)
+//     y     = S_new q
+// with abar_t = prod_{m<=t} a_m, s_{j,t} = dt_j prod_{j<m<=t} a_m ("Decodificacion
+// estandar": buffer the inputs, output by the output-only route, flush when
+// the buffer is full).  The checkpoint is read once per step either way.
+//
+// Workgroup = 4 streaming wavefronts (the head's tile, 16-byte chunks) + 1
+// ring wavefront (decays, group dots, ring term or the rank-c staging, and
+// the ring write of the new token).  The new token is taken from the inputs,
+// so the streaming wavefronts never wait for the ring pointer.  The pointer
+// of a sequence moves when its last workgroup arrives (per-sequence counter).
+#include "device_common.h"
+
+namespace replay {
+
+template <int P, int N>
+struct StepShape {
+    static constexpr int VEC = 4;
+    static constexpr int CHUNKS = P * N / VEC;
+    static constexpr int NTS = CHUNKS < 256 ? CHUNKS : 256;   // streaming threads
+    static constexpr int NT = NTS + 64;
+    static constexpr int ITER = CHUNKS / NTS;
+    static constexpr int LPR = N / VEC;
+    static constexpr int RPI = NTS / LPR;
+    static_assert(CHUNKS % NTS == 0 && NTS % 64 == 0, "bad tiling");
+    static_assert(LPR <= 64 && 64 % LPR == 0, "row group must sit in a wavefront");
+};
+
+// Raw 32-bit words of one io row (N elements), copied by the 64 lanes.
+template <int N, bool IOB>
+struct RowWords {
+    static constexpr int WORDS = N * (IOB ? 2 : 4) / 4;
+    static constexpr int WPL = (WORDS + 63) / 64;
+    uint32_t w[WPL];
+    __device__ __forceinline__ void load(const void *row, int lane) {
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) {
+            const int k = lane + 64 * i;
+            w[i] = static_cast<const uint32_t *>(row)[k < WORDS ? k : WORDS - 1];
+        }
+    }
+    __device__ __forceinline__ void store(void *row, int lane) const {
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) {
+            const int k = lane + 64 * i;
+            if (k < WORDS) static_cast<uint32_t *>(row)[k] = w[i];
+        }
+    }
+};
+
+template <int P, int N, int LM, bool IOB>
+__device__ __forceinline__ void step_ring_wave(const StepArgs &A, int lane, int b, int g, int h, size_t bh,
+                                               int base, int cold, bool fold, float *s_r, float *s_abar,
+                                               float (*s_U)[LM + 1], float (*s_K)[N]) {
+    constexpr int TS = N / 8;
+    constexpr int RPW = 64 / TS;
+    constexpr int KI = (LM + RPW - 1) / RPW;
+    constexpr int VR = (P + 63) / 64;
+    const int L = A.L, count = cold + 1;
+    const size_t gring = ((size_t)b * A.G + g) * L;
+    const size_t hring = bh * L;
+    const size_t gin = (size_t)b * A.G + g;
+    const int bmod = base % L;
+    auto slot = [&](int j) { return ring_slot(bmod, j, L); };
+    const int lastr = cold > 0 ? cold - 1 : 0;   // clamp for ring loads (never used when cold == 0)
+    const int tl = lane % TS, te = lane / TS;
+
+    // 1. every load, issued before any value is used
+    const float a_in = A.a[bh], dt_in = A.dt[bh];
+    const int sla = slot(lane < cold ? lane : lastr);
+    const float a_r = A.ring_a[hring + sla], dt_r = A.ring_dt[hring + sla];
+    IoVec<IOB, 8> kraw[KI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+        const int j = i * RPW + te;   // entries < cold from the ring, the rest from this step's k
+        const bool old = j < cold;
+        kraw[i].load(old ? A.ring_k : A.k, old ? (gring + slot(j)) * N + tl * 8 : gin * N + tl * 8);
+    }
+    IoVec<IOB, 8> qraw;
+    qraw.load(A.q, gin * N + tl * 8);
+    IoVec<IOB, 1> vraw[VR][LM];
+    IoVec<IOB, 1> vnew[VR];
+#pragma unroll
+    for (int rr = 0; rr < VR; ++rr) {
+        const int p = (lane + 64 * rr) < P ? lane + 64 * rr : P - 1;
+        vnew[rr].load(A.v, bh * P + p);
+#pragma unroll
+        for (int j = 0; j < LM; ++j) {
+            if (j < cold)
+                vraw[rr][j].load(A.ring_v, (hring + slot(j)) * P + p);
+            else
+                vraw[rr][j] = vnew[rr];
+        }
+    }
+    const bool group_writer = (h % (A.H / A.G)) == 0;
+    RowWords<N, IOB> qrow, krow;
+    if (group_writer) {
+        qrow.load(static_cast<const char *>(A.q) + gin * N * (IOB ? 2 : 4), lane);
+        krow.load(static_cast<const char *>(A.k) + gin * N * (IOB ? 2 : 4), lane);
+    }
+
+    // 2. decays of entries 0..count-1 (entry cold is this step's token)
+    const float aj = lane < cold ? a_r : (lane == cold ? a_in : 1.f);
+    const float dtj = lane < cold ? dt_r : (lane == cold ? dt_in : 0.f);
+    float prod = dtj, run = 1.f, sw = 0.f, ab = 0.f;
+#pragma unroll
+    for (int m = 0; m < LM; ++m) {
+        if (m < count) {
+            const float am = bcast(aj, m);
+            if (m > lane) prod *= am;
+            run *= am;
+            if (m == count - 1) {
+                sw = prod;
+                ab = run;
+            }
+        }
+    }
+    if (lane == 0) *s_abar = ab;
+
+    if (!fold) {
+        // output-only route: group dots, coefficients, ring term
+        float cw = 0.f;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+            float d = dot8(kraw[i], qraw);
+            d = group_sum<TS>(d);
+            const float moved = __shfl(d, (lane % RPW) * TS);
+            if (lane / RPW == i) cw = moved;
+        }
+        const float coef = lane < count ? sw * cw : 0.f;
+        float acc[VR];
+#pragma unroll
+        for (int rr = 0; rr < VR; ++rr) acc[rr] = 0.f;
+#pragma unroll
+        for (int j = 0; j < LM; ++j) {
+            if (j < count) {
+                const float cj = bcast(coef, j);
+#pragma unroll
+                for (int rr = 0; rr < VR; ++rr) acc[rr] = fmaf(cj, vraw[rr][j].value(), acc[rr]);
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < VR; ++rr)
+            if (lane + 64 * rr < P) s_r[lane + 64 * rr] = acc[rr];
+    } else {
+        // state-and-output route: stage U[p][j] = s_j v_j[p] and K[j][n] = k_j[n]
+#pragma unroll
+        for (int j = 0; j < LM; ++j) {
+            if (j < count) {
+                const float sj = bcast(sw, j);
+#pragma unroll
+                for (int rr = 0; rr < VR; ++rr)
+                    if (lane + 64 * rr < P) s_U[lane + 64 * rr][j] = sj * vraw[rr][j].value();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+            const int j = i * RPW + te;
+            if (j < count) {
+                float kk[8];
+                kraw[i].widen(kk);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s_K[j][tl * 8 + e] = kk[e];
+            }
+        }
+    }
+
+    // 3. this step's token goes into ring slot (pos mod L) = entry cold
+    const int sn = slot(cold);
+#pragma unroll
+    for (int rr = 0; rr < VR; ++rr) {
+        const int p = lane + 64 * rr;
+        if (p < P) {
+            if constexpr (IOB)
+                static_cast<uint16_t *>(A.ring_v)[(hring + sn) * P + p] = (uint16_t)vnew[rr].r;
+            else
+                static_cast<float *>(A.ring_v)[(hring + sn) * P + p] = vnew[rr].r;
+        }
+    }
+    if (lane == 0) {
+        A.ring_dt[hring + sn] = dt_in;
+        A.ring_a[hring + sn] = a_in;
+    }
+    if (group_writer) {
+        const size_t off = (gring + sn) * N * (IOB ? 2 : 4);
+        qrow.store(static_cast<char *>(A.ring_q) + off, lane);
+        krow.store(static_cast<char *>(A.ring_k) + off, lane);
+    }
+}
+
+template <int P, int N, int LM, bool IOB>
+__global__ __launch_bounds__((StepShape<P, N>::NT)) void step_kernel(StepArgs args) {
+    using Sh = StepShape<P, N>;
+    constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+    using RR = RowReduce<ITER, LPR>;
+
+    __shared__ float s_r[P];
+    __shared__ float s_abar;
+    __shared__ int s_count;
+    __shared__ float s_U[P][LM + 1];
+    __shared__ __align__(16) float s_K[LM][N];
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int H = args.H, L = args.L;
+    const int b = lid / H, h = lid % H;
+    const int g = (h * args.G) / H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const size_t bh = (size_t)b * H + h;
+    const size_t tile = bh * (size_t)(P * N);
+
+    // Only the ring wavefront reads the pointer.  It announces this
+    // workgroup's arrival right after that read, so the atomic's latency
+    // overlaps the rest of the work; the streaming wavefronts learn the route
+    // (output-only, fold, or a per-sequence error) from LDS after the barrier.
+    // Each role loads only what it uses inside its own branch, so the tile's
+    // registers are never live across the ring wavefront's code.
+    __shared__ int s_route;   // 0 output-only, 1 fold, 2 error (sequence left unchanged)
+    const int col0 = (tid % LPR) * VEC;
+    Chunk<ST_F32, VEC> ch[ITER];
+    float qv[VEC];
+    float part[ITER][1];
+    int pos = 0, prev = -1, route = 0;
+    if (tid < NTS) {
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
+        IoVec<IOB, 4> qraw;
+        qraw.load(args.q, ((size_t)b * args.G + g) * N + col0);
+        qraw.widen(qv);
+        // S0 q partials (used by the output-only route; cheap beside the loads)
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            float x[VEC];
+            ch[i].widen(x, 1.0f);
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc = fmaf(x[e], qv[e], acc);
+            part[i][0] = acc;
+        }
+        RR::template run<1>(part, lane);
+    } else {
+        const int base = args.base[b];
+        pos = args.pos[b];
+        const int cold = pos - base;
+        const bool bad = cold + 1 > L || pos == 2147483647;
+        const int need = args.flush_at > 1 ? args.flush_at : 1;
+        route = bad ? 2 : (cold + 1 >= need ? 1 : 0);
+        if (lane == 0) {
+            s_route = route;
+            s_count = cold + 1;
+            if (!bad) prev = atomicAdd(&args.sync[b], 1);
+            else raise_seq_error(args.err, b, cold + 1 > L ? REPLAY_SEQERR_RING_OVERFLOW : REPLAY_SEQERR_POS_OVERFLOW);
+        }
+        if (!bad)
+            step_ring_wave<P, N, LM, IOB>(args, lane, b, g, h, bh, base, cold, route == 1, s_r, &s_abar, s_U, s_K);
+    }
+    // LDS-only barrier: the ring wavefront's write-back of the new token and
+    // its arrival atomic complete in the background
+    lds_barrier();
+    if (tid < NTS) route = s_route;
+
+    if (tid < NTS && route == 2) {
+        for (int i = tid; i < P; i += NTS) args.y[bh * P + i] = __builtin_nanf("");
+    } else if (tid < NTS) {
+        if (route == 1) {
+            const float abar = s_abar;
+            float x[ITER][VEC];
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                ch[i].widen(x[i], 1.0f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) x[i][e] *= abar;
+            }
+            const int count = s_count;
+            for (int j = 0; j < count; ++j) {
+                const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_K[j][col0]);
+#pragma unroll
+                for (int i = 0; i < ITER; ++i) {
+                    const float u = s_U[i * RPI + tid / LPR][j];
+                    x[i][0] = fmaf(u, kk.x, x[i][0]);
+                    x[i][1] = fmaf(u, kk.y, x[i][1]);
+                    x[i][2] = fmaf(u, kk.z, x[i][2]);
+                    x[i][3] = fmaf(u, kk.w, x[i][3]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                f32x4 o = {x[i][0], x[i][1], x[i][2], x[i][3]};
+                __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(args.S + tile + (size_t)(i * NTS + tid) * VEC));
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc = fmaf(x[i][e], qv[e], acc);
+                part[i][0] = acc;
+            }
+            RR::template run<1>(part, lane);
+        }
+        if (RR::writer(lane)) {
+            const int hi = RR::halving_index(lane);
+            const float abar = s_abar;
+#pragma unroll
+            for (int e = 0; e < RR::FINAL; ++e) {
+                const int row = (e + RR::FINAL * hi) * RPI + tid / LPR;
+                args.y[bh * P + row] = route == 1 ? part[e][0] : abar * part[e][0] + s_r[row];
+            }
+        }
+    } else if (lane == 0 && prev == H - 1) {
+        // Last workgroup of the sequence to arrive: every workgroup of it has
+        // read the pointer (each arrived right after its read), so it moves.
+        atomicExch(&args.sync[b], 0);
+        args.pos[b] = pos + 1;
+        if (route == 1) args.base[b] = pos + 1;
+    }
+}
+
+template <int P, int N, int LM>
+static hipError_t launch_lm(const StepArgs &a, hipStream_t s) {
+    const unsigned blocks = (unsigned)((size_t)a.B * a.H);
+    if (a.io_bf16)
+        step_kernel<P, N, LM, true><<<blocks, StepShape<P, N>::NT, 0, s>>>(a);
+    else
+        step_kernel<P, N, LM, false><<<blocks, StepShape<P, N>::NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int P, int N>
+static hipError_t launch_pn(const StepArgs &a, hipStream_t s) {
+    if (a.L <= 16) return launch_lm<P, N, 16>(a, s);
+    return launch_lm<P, N, kMaxRing>(a, s);
+}
+
+hipError_t launch_step(int P, int N, const StepArgs &a, hipStream_t s) {
+    if (P == 16 && N == 16) return launch_pn<16, 16>(a, s);
+    if (P == 64 && N == 64) return launch_pn<64, 64>(a, s);
+    if (P == 64 && N == 128) return launch_pn<64, 128>(a, s);
+    if (P == 128 && N == 128) return launch_pn<128, 128>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace replay

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lad):
 
 
 def test_version_and_status_strings(lad):
-    assert lad.replay_abi_version() == 1
+    assert lad.replay_abi_version() == 2
     for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "HIP")]:
         assert text in lad.replay_status_string(s)
     assert lad.replay_status_string(99) == "unknown status"
@@ -48,7 +48,7 @@ def test_buffer_bytes_match_the_layout(lad):
     assert b["ring_q"] == b["ring_k"] == 256 * 8 * 16 * 128 * 2
     assert b["ring_v"] == 256 * 128 * 16 * 64 * 2
     assert b["ring_dt"] == b["ring_a"] == 256 * 128 * 16 * 4
-    assert b["pos"] == b["base"] == 256 * 4 and b["err"] == 257 * 4
+    assert b["pos"] == b["base"] == 256 * 4 and b["err"] == 257 * 4 and b["sync"] == 256 * 4
     c8 = lad.ReplayConfig(4, 8, 2, 128, 128, 32, lad.F32, lad.FP8_E4M3, 1)
     b8 = lad.replay_buffer_bytes(c8)
     assert b8["s_master"] == 0 and b8["s_copy"] == 4 * 8 * 128 * 128 and b8["s_scale"] == 4 * 8 * 4
@@ -79,7 +79,7 @@ def test_init_rejects_missing_or_misaligned_buffers(lad):
     c = lad.ReplayConfig(2, 4, 1, 64, 128, 16, lad.BF16, lad.NONE, 0)
     with pytest.raises(lad.ReplayError, match="status 1"):
         lad.replay_init(c, lad.ReplayBuffers(), 0)                 # all NULL
-    bufs = lad.ReplayBuffers(*([0x1000] * 11))
+    bufs = lad.ReplayBuffers(*([0x1000] * 12))
     bufs.ring_v = 0x1008                                            # misaligned
     with pytest.raises(lad.ReplayError, match="status 1"):
         lad.replay_init(c, bufs, 0)
@@ -93,7 +93,8 @@ def test_calls_validate_before_touching_the_device(lad):
                      (lad.lib.replay_flush, (None, 1, None)),
                      (lad.lib.replay_rollback, (None, 0x1000, None)),
                      (lad.lib.replay_load_checkpoint, (None, 0x1000, None)),
-                     (lad.lib.replay_append, (None, 1, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None))]:
+                     (lad.lib.replay_append, (None, 1, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None)),
+                     (lad.lib.replay_step, (None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 16, None))]:
         assert fn(*args) == 1
     # eager step: misaligned state pointer, unsupported shape
     assert lad.lib.replay_eager_step(ctypes.byref(c), 0x1004, 0x1000, 0x1000, 0x1000, 0x1000,

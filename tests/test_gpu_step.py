@@ -1,0 +1,145 @@
+"""The fused standard decode step (replay_step) on the GPU: one launch per
+step that appends, decodes and, on full rings, folds the ring into the
+checkpoint with the state-and-output route.  Checked against
+
+* the separate calls (append, decode, flush) on the same inputs: outputs of
+  non-folding steps and every checkpoint bit for bit, outputs of folding
+  steps (a different but exact route) to 1e-5;
+* the float64 oracle (1e-4 per token) and the integer ring model (exact);
+* error paths: a step that would overflow the ring leaves the sequence
+  unchanged and outputs NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ring as oring
+from oracle import runs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(w, **kw):
+    import linear_attention_decode_amd as lad
+    return lad.ReplayLayer(w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len,
+                           io_dtype=w.io_dtype, device=gu.DEV, **kw)
+
+
+def _run_step(layer, w, dev, T, flush_at, model=None):
+    y = torch.empty((T, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
+    for t in range(T):
+        layer.step(*dev.step(t), y[t], flush_at=flush_at)
+        if model is not None:
+            model.append(1)
+            model.flush(flush_at)
+            gu.check_ring(layer, model, f"step {t}")
+    return y
+
+
+def test_step_matches_separate_calls_on_decode_workload():
+    """Mamba-2-shaped layer (B=256, H=128, G=8, P=64, N=128, L=16), 48 steps."""
+    w = synth.named("decode")
+    T, L = 48, 16
+    gu.note("fused step vs separate calls")
+    dev = gu.DevInputs(w, 0, T)
+    a = _layer(w)
+    b = _layer(w)
+    ya = torch.empty((T, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
+    yb = torch.empty_like(ya)
+    for t in range(T):
+        a.step(*dev.step(t), ya[t], flush_at=L)
+        q, k, v, dt, aa = dev.step(t)
+        b.append(1, q, k, v, dt, aa)
+        b.decode(yb[t])
+        b.flush(L)
+        if t % L == L - 1:
+            torch.cuda.synchronize()
+            assert torch.equal(a.s_master, b.s_master), f"checkpoint differs after step {t}"
+    torch.cuda.synchronize()
+    assert a.get_error()[0] == 0 and b.get_error()[0] == 0
+    assert torch.equal(a.pos, b.pos) and torch.equal(a.base, b.base)
+    assert torch.equal(a.sync, torch.zeros_like(a.sync))
+    folding = [t for t in range(T) if t % L == L - 1]
+    plain = [t for t in range(T) if t % L != L - 1]
+    assert torch.equal(ya[plain], yb[plain])
+    e = runs.normwise_rel_err(ya[folding].cpu().numpy(), yb[folding].cpu().numpy().astype(np.float64))
+    assert float(np.max(e)) <= 1e-5
+    seqs = [0, 131, 255]
+    x = gu.oracle_inputs(w, 0, T, seqs)
+    y_ref = runs.standard(x, np.zeros((3, w.heads, w.head_dim, w.state_dim)))
+    tok, vec, _ = gu.errors(ya.cpu().numpy()[:, seqs], y_ref)
+    print(f"  per-token max {tok:.3e} per-head max {vec:.3e}")
+    assert tok <= 1e-4
+    a.close()
+    b.close()
+
+
+@pytest.mark.parametrize("P,N,io,L,flush_at,B,H,G,copy", [
+    (16, 16, "f32", 4, 4, 3, 6, 3, None),
+    (64, 64, "bf16", 5, 5, 5, 4, 2, None),
+    (64, 128, "f32", 7, 3, 2, 8, 4, None),
+    (64, 128, "bf16", 32, 32, 2, 16, 8, None),
+    (128, 128, "bf16", 8, 8, 3, 4, 2, None),
+    (64, 128, "bf16", 6, 1, 3, 8, 8, None),
+    (64, 128, "bf16", 8, 8, 3, 8, 2, "bf16"),
+    (64, 128, "bf16", 8, 8, 3, 8, 2, "fp8"),
+])
+def test_step_ragged(P, N, io, L, flush_at, B, H, G, copy):
+    w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype=io,
+                       config=synth.CONFIG_ID["misc"], layer=200 + P + L + flush_at)
+    T = 3 * L + 2
+    gu.note(f"step {w} flush_at={flush_at} copy={copy}")
+    dev = gu.DevInputs(w, 0, T)
+    layer = _layer(w, read_copy=copy)
+    model = oring.RingModel(B, L)
+    y = _run_step(layer, w, dev, T, flush_at, model)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = gu.oracle_inputs(w, 0, T, list(range(B)))
+    S0 = np.zeros((B, H, P, N))
+    if copy is None:
+        y_ref, tol = runs.standard(x, S0), 1e-4
+    else:
+        # with copies the step runs the separate kernels; with this few heads the
+        # per-token error against exact is the format's own, so compare with the
+        # oracle's emulation of the same copy
+        y_ref, tol = runs.separated(x, S0, flush_at, copy), {"bf16": 1e-3, "fp8": 1e-2}[copy]
+    tok, vec, _ = gu.errors(y.cpu().numpy(), y_ref)
+    print(f"  per-token max {tok:.3e} per-head max {vec:.3e}")
+    assert tok <= tol
+    layer.close()
+
+
+def test_step_overflow_leaves_sequence_unchanged():
+    import linear_attention_decode_amd as lad
+    w = synth.Workload(batch=3, heads=4, groups=2, head_dim=64, state_dim=128, ring_len=4,
+                       io_dtype="bf16", config=synth.CONFIG_ID["misc"], layer=211)
+    gu.note("step overflow")
+    dev = gu.DevInputs(w, 0, 8)
+    layer = _layer(w)
+    y = torch.empty((8, 3, 4, 64), dtype=torch.float32, device=gu.DEV)
+    for t in range(4):
+        layer.step(*dev.step(t), y[t], flush_at=5)     # never folds: ring fills up
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    S_before = layer.s_master.clone()
+    layer.step(*dev.step(4), y[4], flush_at=5)         # count would be 5 > L
+    torch.cuda.synchronize()
+    word, per = layer.get_error()
+    assert per == [lad.SEQERR_RING_OVERFLOW] * 3
+    assert torch.isnan(y[4]).all()
+    assert layer.pos.cpu().tolist() == [4, 4, 4] and layer.base.cpu().tolist() == [0, 0, 0]
+    assert torch.equal(layer.s_master, S_before)
+    assert torch.equal(layer.sync, torch.zeros_like(layer.sync))
+    # folding frees the ring and the next step proceeds
+    layer.flush(1)
+    layer.step(*dev.step(4), y[5], flush_at=5)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = gu.oracle_inputs(w, 0, 5, [0, 1, 2])
+    y_ref = runs.standard(x, np.zeros((3, 4, 64, 128)))
+    tok, _, _ = gu.errors(torch.cat([y[:4], y[5:6]]).cpu().numpy(), y_ref)
+    assert tok <= 1e-4
+    layer.close()
