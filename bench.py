@@ -85,10 +85,10 @@ def _dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def input_pool(w, nsteps):
-    """nsteps seeded steps, resident on the device: q,k [T][B][G][N] ..."""
-    inp = synth.step_inputs(w, 0, nsteps)
-    return {k: _dev(v) for k, v in inp.items()}
+def input_pool(w, nsteps, t0=0):
+    """nsteps seeded steps, resident on the device: q,k [T][B][G][N] ...
+    (the seeded recipe evaluated on the device)."""
+    return synth.step_inputs_torch(w, t0, t0 + nsteps, device="cuda")
 
 
 def cpu_baseline(w, target_s=12.0, steps=256, chunk=32):
@@ -293,12 +293,275 @@ def bench_decode(args):
     return out
 
 
+
+# ---------------------------------------------------------------------------
+def _events(n):
+    import torch
+    return [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+
+
+def bench_verify(args):
+    """Speculative verify: B=256, H=64, G=8, P=64, N=128, L=16, W=5 drafts per
+    round, accepted drafts ~ Uniform{0..5}; each round = flush(L-W+1),
+    append(W), verify(W), rollback(W - accepted).  The eager baseline drafts
+    with W per-token steps into snapshots and restores the accepted one."""
+    import torch
+    import linear_attention_decode_amd as lad
+    w = synth.named("verify")
+    B, H, G, P, N, L, W = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len, 5
+    R = args.steps if args.steps_given else 128
+    WU = args.warmup
+    toks = input_pool(w, (R + WU) * W)
+    acc_np = synth.accept_counts(w, R + WU, W)
+    accept = torch.from_numpy(acc_np).cuda()
+    nrej = (W - accept).to(torch.int32).contiguous()
+    win = {k: v.view((R + WU), W, *v.shape[1:]).transpose(1, 2).contiguous() for k, v in toks.items()}
+    layer = lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16")
+    y = torch.empty((B, W, H, P), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def round_(r, ev=None):
+        layer.flush(L - W + 1)
+        layer.append(W, win["q"][r], win["k"][r], win["v"][r], win["dt"][r], win["a"][r])
+        if ev is not None:
+            ev[0].record(stream)
+        layer.verify(W, y)
+        if ev is not None:
+            ev[1].record(stream)
+        layer.rollback(nrej[r])
+
+    for r in range(WU):
+        round_(r)
+    torch.cuda.synchronize()
+    evs = _events(R)
+    t0 = time.perf_counter()
+    for k in range(R):
+        round_(WU + k, evs[k])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    assert layer.get_error()[0] == 0
+    ver_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    # counts at verify time (ring model, host side)
+    from_model = _verify_counts(B, L, W, acc_np)
+    vbytes = sum(float(np.mean([decode_bytes(w, c, W) / B for c in from_model[WU + k]])) * B for k in range(R))
+    achieved = vbytes / (sum(ver_ms) / 1e3) / 1e9
+    layer.close()
+    del layer
+    torch.cuda.empty_cache()
+
+    # eager: W per-token steps into snapshots, then restore the accepted one
+    cfg = lad.ReplayConfig(B, H, G, P, N, L, lad.BF16, lad.NONE, 0)
+    S = torch.zeros((B, H, P, N), dtype=torch.float32, device="cuda")
+    snaps = torch.empty((W, B, H, P, N), dtype=torch.float32, device="cuda")
+    ye = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
+
+    def eround(r):
+        for i in range(W):
+            t = r * W + i
+            lad.replay_eager_step(cfg, S if i == 0 else snaps[i - 1], snaps[i], toks["q"][t], toks["k"][t],
+                                  toks["v"][t], toks["dt"][t], toks["a"][t], ye)
+        lad.replay_eager_select(cfg, snaps, W, accept[r], S)
+    for r in range(WU):
+        eround(r)
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    for k in range(R):
+        eround(WU + k)
+    torch.cuda.synchronize()
+    eel = time.perf_counter() - e0
+    acc_total = float(acc_np[WU:].sum())
+    replay_round_bytes = (state_bytes(w) + B * (W * (H * P * 2 + H * 8 + 2 * G * N * 2)) * 2
+                          + vbytes / R)
+    eager_round_bytes = W * eager_bytes(w) + float(np.mean(acc_np[WU:] >= 1)) * 2 * state_bytes(w)
+    return {
+        "metric": "speculative verify: scored draft positions/s at B=256",
+        "value": B * W * R / el, "unit": "positions/s", "n_gpus": 1, "steps": R, "warmup": WU,
+        "ms_per_step": 1e3 * el / R, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded), accepted drafts ~ Uniform{0..5}",
+        "config": {"workload": "speculative verify, one SSM layer", "batch": B, "heads": H, "groups": G,
+                   "head_dim": P, "state_dim": N, "ring_len": L, "window": W, "rounds": R},
+        "accepted_tokens_per_s": acc_total / el,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "verify (W=5)",
+                     "avg_launch_us": 1e3 * sum(ver_ms) / len(ver_ms)},
+        "eager": {"positions_per_s": B * W * R / eel, "accepted_tokens_per_s": acc_total / eel,
+                  "ms_per_round": 1e3 * eel / R},
+        "speedup_vs_eager": eel / el,
+        "round_bytes_ratio_vs_eager": replay_round_bytes / eager_round_bytes,
+    }
+
+
+def _verify_counts(B, L, W, acc):
+    """Ring counts at verify time for every round and sequence: each round
+    folds a ring holding at least L-W+1 entries, appends W drafts, verifies,
+    then drops the W - accepted rejected drafts."""
+    c = np.zeros(B, dtype=np.int64)
+    out = []
+    for r in range(acc.shape[0]):
+        c = np.where(c >= L - W + 1, 0, c) + W
+        out.append(c.copy())
+        c = c - (W - acc[r])
+    return out
+
+
+def _tok_err(y, ref):
+    """Per token: max over heads x P of |y - ref|, over max |ref|."""
+    d = (y.double() - ref.double()).abs().amax(dim=(-2, -1))
+    return d / ref.double().abs().amax(dim=(-2, -1)).clamp_min(1e-300)
+
+
+def bench_dual(args):
+    """Dual precision: decode shapes, T=1024 steps per mode; float32 master
+    with reads from the master, a bf16 copy or an e4m3 copy (separated), and
+    the shared low-precision checkpoint.  Each mode's outputs on sampled
+    sequences are compared with the float32-master path's outputs per window
+    (the float64 oracle comparison lives in the tests)."""
+    import torch
+    import linear_attention_decode_amd as lad
+    T = args.steps if args.steps_given else 1024
+    out_modes = {}
+    for dt_scale in ([1.0, 0.01] if not args.quick else [1.0]):
+        w = synth.named("dual", dt_scale=dt_scale)
+        B, H, G, P, N, L = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len
+        seqs = [0, 101, 202]
+        chunk = 128
+        pools = [input_pool(w, chunk, t0=c0) for c0 in range(0, T, chunk)]
+        ys_master = None
+        for mode, rc, shared in [("f32", None, False), ("bf16-separated", "bf16", False),
+                                 ("fp8-separated", "fp8", False), ("bf16-shared", "bf16", True),
+                                 ("fp8-shared", "fp8", True)]:
+            y = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
+            sel = torch.tensor(seqs, device="cuda")
+
+            def run(capture):
+                layer = lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16", read_copy=rc, shared_lowp=shared)
+                ys = torch.empty((T, len(seqs), H, P), dtype=torch.float32, device="cuda")
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for t in range(T):
+                    p = pools[t // chunk]
+                    i = t % chunk
+                    layer.step(p["q"][i], p["k"][i], p["v"][i], p["dt"][i], p["a"][i], y, flush_at=L)
+                    if capture:
+                        ys[t] = y.index_select(0, sel)
+                torch.cuda.synchronize()
+                el = time.perf_counter() - t0
+                assert layer.get_error()[0] == 0
+                layer.close()
+                return el, ys
+            el, _ = run(False)          # timed pass
+            _, ys = run(True)           # pass that keeps the sampled outputs
+            key = mode if dt_scale == 1.0 else f"{mode} (dt x{dt_scale})"
+            rec = {"tokens_per_s": B * T / el}
+            if ys_master is None:
+                ys_master = ys
+            else:
+                e_tok = _tok_err(ys, ys_master).cpu().numpy()               # [T][b]
+                nw = T // L
+                per_win = e_tok[: nw * L].reshape(nw, L, -1)
+                rec.update({"max_err_vs_master": float(e_tok.max()), "mean_err_vs_master": float(e_tok.mean()),
+                            "drift_max_mean": {f"window_{i}": [float(per_win[i].max()), float(per_win[i].mean())]
+                                               for i in sorted({0, nw // 2, nw - 1})}})
+            out_modes[key] = rec
+            torch.cuda.empty_cache()
+    first = out_modes["fp8-separated"]
+    return {
+        "metric": "dual-precision decode tokens/s at B=256 (+ error drift vs the float32 master path)",
+        "value": first["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": T, "warmup": 0,
+        "ms_per_step": 1e3 * 256 / first["tokens_per_s"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded)",
+        "config": {"workload": "dual-precision decode, one SSM layer", "batch": 256, "heads": 128,
+                   "groups": 8, "head_dim": 64, "state_dim": 128, "ring_len": 16, "steps": T,
+                   "value_is": "fp8-separated", "error_metric": "per token, max|dy|/max|y| over heads x P"},
+        "modes": out_modes,
+    }
+
+
+def bench_stacked(args):
+    """Stacked sweep: 8 SSM layers, B=512, H=64, G=8, P=N=128, ring L in
+    {8, 16, 32}; T=512 steps, each layer cycling 64 pre-generated steps of its
+    own seeded inputs; ReplaySSM (fused step) against the eager per-token
+    baseline."""
+    import torch
+    import linear_attention_decode_amd as lad
+    T = args.steps if args.steps_given else 512
+    pool_n = 64
+    res = {}
+    Ls = [8, 16, 32] if not args.quick else [16]
+    pools = [input_pool(synth.named("stacked", layer=li), pool_n) for li in range(8)]
+    for L in Ls:
+        w = synth.named("stacked", ring_len=L)
+        B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
+        layers = [lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16") for _ in range(8)]
+        y = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
+
+        def step(t):
+            i = t % pool_n
+            for li in range(8):
+                p = pools[li]
+                layers[li].step(p["q"][i], p["k"][i], p["v"][i], p["dt"][i], p["a"][i], y, flush_at=L)
+        for t in range(L):
+            step(t)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(L, L + T):
+            step(t)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        for lay in layers:
+            assert lay.get_error()[0] == 0
+            lay.close()
+        del layers
+        torch.cuda.empty_cache()
+        window_replay = (sum(step_bytes(w, c, c >= L) for c in range(1, L + 1))) * 8
+        window_eager = L * eager_bytes(w) * 8
+        res[f"L={L}"] = {"tokens_per_s": B * T / el, "ms_per_step": 1e3 * el / T,
+                         "window_bytes_ratio_vs_eager": window_replay / window_eager,
+                         "achieved_GBs": window_replay / L * T / el / 1e9}
+    # eager baseline (does not depend on L)
+    w = synth.named("stacked")
+    B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
+    cfg = lad.ReplayConfig(B, H, G, P, N, 16, lad.BF16, lad.NONE, 0)
+    Ss = [torch.zeros((B, H, P, N), dtype=torch.float32, device="cuda") for _ in range(8)]
+    y = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
+
+    def estep(t):
+        i = t % pool_n
+        for li in range(8):
+            p = pools[li]
+            lad.replay_eager_step(cfg, Ss[li], Ss[li], p["q"][i], p["k"][i], p["v"][i], p["dt"][i], p["a"][i], y)
+    for t in range(8):
+        estep(t)
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    Te = min(T, 128)
+    for t in range(Te):
+        estep(t)
+    torch.cuda.synchronize()
+    eel = time.perf_counter() - e0
+    eager = {"tokens_per_s": B * Te / eel, "ms_per_step": 1e3 * eel / Te,
+             "achieved_GBs": eager_bytes(w) * 8 * Te / eel / 1e9}
+    best = max(res.values(), key=lambda r: r["tokens_per_s"])
+    return {
+        "metric": "8-layer stacked decode tokens/s at B=512 per ring length vs eager",
+        "value": res.get("L=16", best)["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": T,
+        "warmup": 0, "ms_per_step": res.get("L=16", best)["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": f"synthetic (seeded, {pool_n} distinct steps per layer cycled)",
+        "config": {"workload": "8 stacked SSM layers", "batch": 512, "heads": 64, "groups": 8,
+                   "head_dim": 128, "state_dim": 128, "ring_len": "8/16/32", "value_is": "L=16"},
+        "per_ring_len": res, "eager": eager,
+        "speedup_vs_eager_L16": res.get("L=16", best)["tokens_per_s"] / eager["tokens_per_s"],
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="decode", choices=["decode"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "verify", "dual", "stacked"])
+    ap.add_argument("--quick", action="store_true", help="dual/stacked: one variant only")
     ap.add_argument("--api", default="step", choices=["step", "calls"],
                     help="step: one fused replay_step launch per step; calls: append, decode, flush")
     ap.add_argument("--read", default="f32", choices=["f32", "bf16", "fp8"],
@@ -308,6 +571,7 @@ def main():
     ap.add_argument("--probe-copy-gib", type=float, default=0.0,
                     help="first run the plain copy probe over this many GiB (counter calibration)")
     args = ap.parse_args()
+    args.steps_given = any(a.startswith("--steps") for a in sys.argv[1:])
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path needs no collective and this build runs "
               "on a single MI355X; --gpus must be 1", file=sys.stderr)
@@ -325,7 +589,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
-    out = bench_decode(args)
+    out = {"decode": bench_decode, "verify": bench_verify, "dual": bench_dual,
+           "stacked": bench_stacked}[args.workload](args)
     print(json.dumps(out))
 
 
