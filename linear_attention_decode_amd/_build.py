@@ -21,6 +21,13 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(HERE, "..", "include")]
 
 
+# Per-file extra flags.  step.hip: one lane per workgroup adds to a
+# per-sequence arrival counter and needs the old value only at its very end;
+# the atomic optimizer would rewrite that add into a wave-wide form whose
+# readfirstlane waits for the atomic where it is issued.
+EXTRA = {"step.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     return os.path.join(rocm, "bin", "hipcc")
@@ -33,7 +40,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(pair):
         src, obj = pair
-        cmd = [_hipcc(), *CFLAGS, "-c", src, "-o", obj]
+        cmd = [_hipcc(), *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {os.path.basename(src)}:\n{r.stderr}")

@@ -156,10 +156,23 @@ struct IoVec<false, 4> {
     }
 };
 
+// Buffer resource over [base, base + bytes) (bytes < 2^32).  A load through
+// it takes a 32-bit per-lane byte offset and a wave-uniform byte offset held
+// in a scalar register, so a wavefront that reads many rows of one region
+// keeps a single address register instead of a 64-bit address per load.
+// Offsets at or past `bytes` read zero.  Word 3 is the gfx9-family setting
+// for untyped (raw) buffer access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <>
 struct IoVec<true, 1> {
     uint32_t r;
     __device__ __forceinline__ void load(const void *base, size_t i) { r = static_cast<const uint16_t *>(base)[i]; }
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+        r = __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0);
+    }
     __device__ __forceinline__ float value() const { return bf16_bits_to_f32(r); }
 };
 
@@ -167,6 +180,9 @@ template <>
 struct IoVec<false, 1> {
     float r;
     __device__ __forceinline__ void load(const void *base, size_t i) { r = static_cast<const float *>(base)[i]; }
+    __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff) {
+        r = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0));
+    }
     __device__ __forceinline__ float value() const { return r; }
 };
 

@@ -58,9 +58,9 @@ struct RowWords {
 };
 
 template <int P, int N, int LM, bool IOB>
-__device__ __forceinline__ void step_ring_wave(const StepArgs &A, int lane, int b, int g, int h, size_t bh,
-                                               int base, int cold, bool fold, float *s_r, float *s_abar,
-                                               float (*s_U)[LM + 1], float (*s_K)[N]) {
+__device__ __forceinline__ int step_ring_wave(const StepArgs &A, int lane, int b, int g, int h, size_t bh,
+                                              int base, int cold, bool fold, float *s_r, float *s_abar,
+                                              float (*s_U)[LM + 1], float (*s_K)[N]) {
     constexpr int TS = N / 8;
     constexpr int RPW = 64 / TS;
     constexpr int KI = (LM + RPW - 1) / RPW;
@@ -74,8 +74,18 @@ __device__ __forceinline__ void step_ring_wave(const StepArgs &A, int lane, int 
     const int lastr = cold > 0 ? cold - 1 : 0;   // clamp for ring loads (never used when cold == 0)
     const int tl = lane % TS, te = lane / TS;
 
-    // 1. every load, issued before any value is used
+    // 1. every load, issued before any value is used: this step's token
+    // first, then the ring
     const float a_in = A.a[bh], dt_in = A.dt[bh];
+    IoVec<IOB, 1> vnew[VR];
+#pragma unroll
+    for (int rr = 0; rr < VR; ++rr) vnew[rr].load(A.v, bh * P + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
+    const bool group_writer = (h % (A.H / A.G)) == 0;
+    RowWords<N, IOB> qrow, krow;
+    if (group_writer) {
+        qrow.load(static_cast<const char *>(A.q) + gin * N * (IOB ? 2 : 4), lane);
+        krow.load(static_cast<const char *>(A.k) + gin * N * (IOB ? 2 : 4), lane);
+    }
     const int sla = slot(lane < cold ? lane : lastr);
     const float a_r = A.ring_a[hring + sla], dt_r = A.ring_dt[hring + sla];
     IoVec<IOB, 8> kraw[KI];
@@ -87,28 +97,51 @@ __device__ __forceinline__ void step_ring_wave(const StepArgs &A, int lane, int 
     }
     IoVec<IOB, 8> qraw;
     qraw.load(A.q, gin * N + tl * 8);
+    // ring values of entries < cold; the loads are unconditional from a
+    // clamped, always-valid slot so that no branch or early wait sits between
+    // them, and entry cold (this step's token) is selected at use
+    constexpr uint32_t ES = IOB ? 2 : 4;
+    const auto vres = make_rsrc(static_cast<const char *>(A.ring_v) + hring * P * ES, (uint32_t)(L * P * ES));
     IoVec<IOB, 1> vraw[VR][LM];
-    IoVec<IOB, 1> vnew[VR];
 #pragma unroll
     for (int rr = 0; rr < VR; ++rr) {
-        const int p = (lane + 64 * rr) < P ? lane + 64 * rr : P - 1;
-        vnew[rr].load(A.v, bh * P + p);
+        const uint32_t voff = ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1) * ES;
 #pragma unroll
-        for (int j = 0; j < LM; ++j) {
-            if (j < cold)
-                vraw[rr][j].load(A.ring_v, (hring + slot(j)) * P + p);
+        for (int j = 0; j < LM; ++j) vraw[rr][j].load_buf(vres, voff, (uint32_t)slot(j < cold ? j : lastr) * P * ES);
+    }
+    auto vval = [&](int rr, int j) { return j < cold ? vraw[rr][j].value() : vnew[rr].value(); };
+
+    // 2. this step's token goes into ring slot (pos mod L) = entry cold,
+    // as soon as it has arrived: a wavefront ends only once its stores have
+    // completed, so they are issued before the ring loads are waited for.
+    // No ring value read above comes from slot sn (entries < cold only; the
+    // clamped loads of an empty ring read it, but those values are unused).
+    const int sn = slot(cold);
+#pragma unroll
+    for (int rr = 0; rr < VR; ++rr) {
+        const int p = lane + 64 * rr;
+        if (p < P) {
+            if constexpr (IOB)
+                static_cast<uint16_t *>(A.ring_v)[(hring + sn) * P + p] = (uint16_t)vnew[rr].r;
             else
-                vraw[rr][j] = vnew[rr];
+                static_cast<float *>(A.ring_v)[(hring + sn) * P + p] = vnew[rr].r;
         }
     }
-    const bool group_writer = (h % (A.H / A.G)) == 0;
-    RowWords<N, IOB> qrow, krow;
-    if (group_writer) {
-        qrow.load(static_cast<const char *>(A.q) + gin * N * (IOB ? 2 : 4), lane);
-        krow.load(static_cast<const char *>(A.k) + gin * N * (IOB ? 2 : 4), lane);
+    if (lane == 0) {
+        A.ring_dt[hring + sn] = dt_in;
+        A.ring_a[hring + sn] = a_in;
     }
+    if (group_writer) {
+        const size_t off = (gring + sn) * N * (IOB ? 2 : 4);
+        qrow.store(static_cast<char *>(A.ring_q) + off, lane);
+        krow.store(static_cast<char *>(A.ring_k) + off, lane);
+    }
+    // Arrival of this workgroup (its pointer read is done: the loads above
+    // depend on it).  Its result is needed only at the very end.
+    int prev = -1;
+    if (lane == 0) prev = atomicAdd(&A.sync[b], 1);
 
-    // 2. decays of entries 0..count-1 (entry cold is this step's token)
+    // 3. decays of entries 0..count-1 (entry cold is this step's token)
     const float aj = lane < cold ? a_r : (lane == cold ? a_in : 1.f);
     const float dtj = lane < cold ? dt_r : (lane == cold ? dt_in : 0.f);
     float prod = dtj, run = 1.f, sw = 0.f, ab = 0.f;
@@ -145,7 +178,7 @@ __device__ __forceinline__ void step_ring_wave(const StepArgs &A, int lane, int 
             if (j < count) {
                 const float cj = bcast(coef, j);
 #pragma unroll
-                for (int rr = 0; rr < VR; ++rr) acc[rr] = fmaf(cj, vraw[rr][j].value(), acc[rr]);
+                for (int rr = 0; rr < VR; ++rr) acc[rr] = fmaf(cj, vval(rr, j), acc[rr]);
             }
         }
 #pragma unroll
@@ -159,7 +192,7 @@ __device__ __forceinline__ void step_ring_wave(const StepArgs &A, int lane, int 
                 const float sj = bcast(sw, j);
 #pragma unroll
                 for (int rr = 0; rr < VR; ++rr)
-                    if (lane + 64 * rr < P) s_U[lane + 64 * rr][j] = sj * vraw[rr][j].value();
+                    if (lane + 64 * rr < P) s_U[lane + 64 * rr][j] = sj * vval(rr, j);
             }
         }
 #pragma unroll
@@ -174,31 +207,20 @@ __device__ __forceinline__ void step_ring_wave(const StepArgs &A, int lane, int 
         }
     }
 
-    // 3. this step's token goes into ring slot (pos mod L) = entry cold
-    const int sn = slot(cold);
-#pragma unroll
-    for (int rr = 0; rr < VR; ++rr) {
-        const int p = lane + 64 * rr;
-        if (p < P) {
-            if constexpr (IOB)
-                static_cast<uint16_t *>(A.ring_v)[(hring + sn) * P + p] = (uint16_t)vnew[rr].r;
-            else
-                static_cast<float *>(A.ring_v)[(hring + sn) * P + p] = vnew[rr].r;
-        }
-    }
-    if (lane == 0) {
-        A.ring_dt[hring + sn] = dt_in;
-        A.ring_a[hring + sn] = a_in;
-    }
-    if (group_writer) {
-        const size_t off = (gring + sn) * N * (IOB ? 2 : 4);
-        qrow.store(static_cast<char *>(A.ring_q) + off, lane);
-        krow.store(static_cast<char *>(A.ring_k) + off, lane);
-    }
+    return prev;
+}
+
+// Waves per SIMD to ask the register allocator for: 8 (the hardware maximum,
+// 64 registers a lane) where the kernel fits without spilling to scratch,
+// otherwise no request.
+template <int P, int N, int LM, bool IOB>
+constexpr int step_waves() {
+    return (P * N <= 64 * 64 || (P == 64 && N == 128 && LM == 16 && IOB)) && !(LM == 32 && P * N > 16 * 16) ? 8 : 1;
 }
 
 template <int P, int N, int LM, bool IOB>
-__global__ __launch_bounds__((StepShape<P, N>::NT)) void step_kernel(StepArgs args) {
+__global__ __launch_bounds__((StepShape<P, N>::NT))
+__attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kernel(StepArgs args) {
     using Sh = StepShape<P, N>;
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
     using RR = RowReduce<ITER, LPR>;
@@ -218,8 +240,8 @@ __global__ __launch_bounds__((StepShape<P, N>::NT)) void step_kernel(StepArgs ar
     const size_t tile = bh * (size_t)(P * N);
 
     // Only the ring wavefront reads the pointer.  It announces this
-    // workgroup's arrival right after that read, so the atomic's latency
-    // overlaps the rest of the work; the streaming wavefronts learn the route
+    // workgroup's arrival once its ring loads are issued, so the atomic's
+    // latency overlaps the rest of the work; the streaming wavefronts learn the route
     // (output-only, fold, or a per-sequence error) from LDS after the barrier.
     // Each role loads only what it uses inside its own branch, so the tile's
     // registers are never live across the ring wavefront's code.
@@ -256,11 +278,10 @@ __global__ __launch_bounds__((StepShape<P, N>::NT)) void step_kernel(StepArgs ar
         if (lane == 0) {
             s_route = route;
             s_count = cold + 1;
-            if (!bad) prev = atomicAdd(&args.sync[b], 1);
-            else raise_seq_error(args.err, b, cold + 1 > L ? REPLAY_SEQERR_RING_OVERFLOW : REPLAY_SEQERR_POS_OVERFLOW);
+            if (bad) raise_seq_error(args.err, b, cold + 1 > L ? REPLAY_SEQERR_RING_OVERFLOW : REPLAY_SEQERR_POS_OVERFLOW);
         }
         if (!bad)
-            step_ring_wave<P, N, LM, IOB>(args, lane, b, g, h, bh, base, cold, route == 1, s_r, &s_abar, s_U, s_K);
+            prev = step_ring_wave<P, N, LM, IOB>(args, lane, b, g, h, bh, base, cold, route == 1, s_r, &s_abar, s_U, s_K);
     }
     // LDS-only barrier: the ring wavefront's write-back of the new token and
     // its arrival atomic complete in the background
