@@ -15,10 +15,12 @@
 // contiguous bytes per iteration), all chunk loads are issued before any
 // other work so they overlap the ring arithmetic.  k_j . q is formed per
 // group by the workgroup itself from the group's k ring (L2-resident: the
-// XCD-aware block order keeps a group's heads on one XCD).  Row sums are
-// finished with a transposed halving reduction across the lanes of a row.
+// XCD-aware block order keeps a group's heads on one XCD); with bf16 io the
+// ring wavefront forms the dots and the ring term on the matrix cores.  Row
+// sums are finished with a transposed halving reduction across the lanes of a
+// row.
 #pragma once
-#include "device_common.h"
+#include "ring_mx.h"
 
 namespace replay {
 
@@ -165,6 +167,61 @@ __device__ __forceinline__ void ring_wave(const RingView &r, int lane, int b, in
     }
 }
 
+// The same work for bf16 io on the matrix cores (ring_mx.h), operands read
+// from the ring: every entry and query from its ring slot, indices clamped to
+// the live range.
+template <int P, int N, int WM, int LM>
+__device__ __forceinline__ void ring_wave_mx(const RingView &r, int lane, int b, int g, size_t bh, int base,
+                                             int count, float (*s_r)[P], float *s_abar, float (*s_sw)[LM]) {
+    using MX = MxRing<P, N, WM, LM>;
+    const int L = r.L;
+    const size_t gring = ((size_t)b * r.G + g) * L;
+    const size_t hring = bh * L;
+    const int t0 = count - WM;
+    const int bmod = base % L;
+    auto slot = [&](int j) { return ring_slot(bmod, j, L); };
+    const int last = count - 1;
+    const int lr = lane & 15, lq = lane >> 4;
+
+    MX m;
+    {
+        const int sl = slot(lane < count ? lane : last);
+        m.aj = r.a[hring + sl];
+        m.dtj = r.dt[hring + sl];
+    }
+#pragma unroll
+    for (int kb = 0; kb < MX::KB; ++kb) {
+        const int c = MX::col(kb, lane);
+#pragma unroll
+        for (int jb = 0; jb < MX::JB; ++jb) {
+            const int j = 16 * jb + lr;
+            m.ka[jb][kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.k) +
+                                                            (gring + slot(j < count ? j : last)) * N + c);
+        }
+        m.qb[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.q) +
+                                                    (gring + slot(t0 + (lr < WM ? lr : WM - 1))) * N + c);
+    }
+    const auto vres = make_rsrc(static_cast<const uint16_t *>(r.v) + hring * P, (uint32_t)(L * P * 2));
+#pragma unroll
+    for (int jb = 0; jb < MX::JB; ++jb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int j = 16 * jb + 4 * lq + kk;
+            const uint32_t row = (uint32_t)slot(j < count ? j : last) * P;
+#pragma unroll
+            for (int pw = 0; pw < MX::PW; ++pw)
+                m.vw[jb][kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * 2, 0, 0);
+        }
+    if (lane >= count) {
+        m.aj = 1.f;
+        m.dtj = 0.f;
+    }
+    f32x4 dk[MX::JB];
+    m.dots(lane, dk);
+    m.weights(lane, count, s_abar, s_sw);
+    m.term(lane, dk, s_r, s_sw);
+}
+
 template <int P, int N, int ST, int WM, int LM, bool IOB>
 __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NT)) void decode_kernel(DecodeArgs args) {
     using Sh = DecodeShape<P, N, ST, WM>;
@@ -174,6 +231,7 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NT)) void decode_kernel
 
     __shared__ float s_r[WM][P];
     __shared__ float s_abar[WM];
+    __shared__ __align__(16) float s_sw[IOB ? WM : 1][IOB ? LM : 4];
 
     const RingView &r = args.r;
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -234,7 +292,10 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NT)) void decode_kernel
         }
         RR::template run<WM>(part, lane);
     } else {
-        ring_wave<P, N, WM, LM, IOB>(r, lane, b, g, bh, base, count, s_r, s_abar);
+        if constexpr (IOB)
+            ring_wave_mx<P, N, WM, LM>(r, lane, b, g, bh, base, count, s_r, s_abar, s_sw);
+        else
+            ring_wave<P, N, WM, LM, IOB>(r, lane, b, g, bh, base, count, s_r, s_abar);
     }
     __syncthreads();
 

@@ -1,0 +1,136 @@
+// ring_mx.h -- the ring part of the output-only route on the matrix cores
+// (bf16 io): for the W newest entries t_w = count-W+w of one (sequence, head)
+//     R[w][p] = sum_{j<=t_w} s_{j,t_w} (k_j . q_{t_w}) v_j[p],   abar_w = prod_{m<=t_w} a_m
+// (page "ReplaySSM: Cachear Inputs, No Estado", section "Los dos caminos",
+// eq. "Ruta solo salida", its sum over the buffer; s_{j,t} = dt_j
+// prod_{j<m<=t} a_m, products taken left to right).
+//
+// Two small products, both in 16x16 MFMA tiles (lane l: row l%16, k-group
+// l/16):
+//   dots  D[j][w] = k_j . q_{t_w}     v_mfma_f32_16x16x32_bf16, A = k rows of
+//                                     entries 16jb..16jb+15, B = the W queries
+//                                     (columns w >= W are clamped copies, weighted 0)
+//   term  R[w][p] = sum_j c[w][j] v_j[p],  c[w][j] = s_{j,t_w} D[j][w] (0 for j > t_w)
+//                                     v_mfma_f32_16x16x4_f32, A = c, B = v rows
+//                                     (a lane holds one bf16 pair: columns n of the
+//                                     two products of a 32-wide block are p = 2n, 2n+1)
+// The contraction slot k of the second product at lane (row, k) stands for
+// entry 16jb + 4k + kk, which is where output register kk of the first
+// product already holds D[j][w] for that lane, so c never moves between lanes.
+// Segment weights are formed with lane = entry and handed over through LDS.
+// bf16 products are exact in float32; only the order of the sums differs
+// from a sequential evaluation.
+#pragma once
+#include "device_common.h"
+
+namespace replay {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+template <int P, int N, int WM, int LM>
+struct MxRing {
+    static constexpr int JB = LM / 16;            // 16-entry blocks
+    static constexpr int KB = (N + 31) / 32;      // 32-column blocks of k . q
+    static constexpr int PW = (P + 31) / 32;      // 32-column blocks of v, one bf16 pair per lane
+    static_assert(LM % 16 == 0 && P % 16 == 0 && N % 16 == 0, "tile shape");
+
+    // Operands, filled by the caller with raw bf16 bits.  Lane l = r + 16 g:
+    uint4 ka[JB][KB];               // k_{16jb + r}[32kb + 8g .. +7]      (entries past the live ones: any finite row)
+    uint4 qb[KB];                   // q_{t_min(r, W-1)}[32kb + 8g .. +7]
+    uint32_t vw[JB][4][PW];         // v_{16jb + 4g + kk}[32pw + 2r .. +1] (same; pairs past P: any finite word)
+    float aj, dtj;                  // lane j: a_j, dt_j; 1 and 0 for j >= count
+
+    // word index of lane l's v pair in block pw, clamped into the row
+    static __device__ __forceinline__ int vword(int pw, int lane) {
+        const int w = 16 * pw + (lane & 15);
+        return w < P / 2 ? w : P / 2 - 1;
+    }
+
+    static __device__ __forceinline__ float vval(uint32_t word, int half) {
+        return half ? __uint_as_float(word & 0xffff0000u) : __uint_as_float(word << 16);
+    }
+
+    static __device__ __forceinline__ int col(int kb, int lane) {
+        const int c = 32 * kb + 8 * (lane >> 4);
+        return c < N ? c : 0;
+    }
+
+    __device__ __forceinline__ void dots(int lane, f32x4 (&dk)[JB]) const {
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+            dk[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                uint4 a = ka[jb][kb];
+                if (32 * kb + 8 * (lane >> 4) >= N) a = uint4{0u, 0u, 0u, 0u};   // only when N < 32
+                dk[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[kb]), dk[jb], 0, 0, 0);
+            }
+        }
+    }
+
+    // s_sw[w][j] = s_{j,t_w} (0 for j > t_w or j >= count), s_abar[w] = abar_{t_w}
+    __device__ __forceinline__ void weights(int lane, int count, float *s_abar, float (*s_sw)[LM]) const {
+        const int t0 = count - WM;
+        float sw[WM], ab[WM];
+        float prod = dtj, run = 1.f;
+#pragma unroll
+        for (int w = 0; w < WM; ++w) sw[w] = ab[w] = 0.f;
+#pragma unroll
+        for (int m = 0; m < LM; ++m) {
+            if (m < count) {
+                const float am = bcast(aj, m);
+                if (m > lane) prod *= am;
+                run *= am;
+#pragma unroll
+                for (int w = 0; w < WM; ++w)
+                    if (m == t0 + w) {
+                        sw[w] = prod;
+                        ab[w] = run;
+                    }
+            }
+        }
+        if (lane < LM) {
+#pragma unroll
+            for (int w = 0; w < WM; ++w) s_sw[w][lane] = lane <= t0 + w ? sw[w] : 0.f;
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int w = 0; w < WM; ++w) s_abar[w] = ab[w];
+        }
+    }
+
+    // s_r[w][p] = R[w][p]; reads the weights this wavefront wrote to s_sw
+    // (a wavefront's own LDS accesses complete in order)
+    __device__ __forceinline__ void term(int lane, const f32x4 (&dk)[JB], float (*s_r)[P],
+                                         const float (*s_sw)[LM]) const {
+        const int lr = lane & 15, lq = lane >> 4;
+        f32x4 cf[JB];
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb) {
+            const f32x4 wv = *reinterpret_cast<const f32x4 *>(&s_sw[lr < WM ? lr : 0][16 * jb + 4 * lq]);
+            cf[jb] = lr < WM ? wv * dk[jb] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // column n of block (pw, half) is p = 32pw + 2n + half
+#pragma unroll
+        for (int pw = 0; pw < PW; ++pw)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cf[jb][kk], vval(vw[jb][kk][pw], half), acc, 0, 0, 0);
+                const int p = 32 * pw + 2 * lr + half;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int w = 4 * lq + rr;
+                    if (w < WM && p < P) s_r[w][p] = acc[rr];
+                }
+            }
+    }
+};
+
+}  // namespace replay

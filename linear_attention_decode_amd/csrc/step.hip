@@ -18,7 +18,7 @@
 // the ring write of the new token).  The new token is taken from the inputs,
 // so the streaming wavefronts never wait for the ring pointer.  The pointer
 // of a sequence moves when its last workgroup arrives (per-sequence counter).
-#include "device_common.h"
+#include "ring_mx.h"
 
 namespace replay {
 
@@ -210,6 +210,154 @@ __device__ __forceinline__ int step_ring_wave(const StepArgs &A, int lane, int b
     return prev;
 }
 
+// The ring wavefront for bf16 io: the same work with the output-only route
+// on the matrix cores (ring_mx.h).  Entry cold, this step's token, comes from
+// the inputs (k row, query, v); the other operands from the ring, as in
+// ring_wave_mx of the decode kernel, and every lane, clamped ones included,
+// holds the values the decode kernel holds after an append, so the output
+// of a non-folding step equals decode's bit for bit.
+template <int P, int N, int LM>
+__device__ __forceinline__ int step_ring_wave_mx(const StepArgs &A, int lane, int b, int g, int h, size_t bh,
+                                                 int base, int cold, bool fold, float *s_r, float *s_abar,
+                                                 float (*s_U)[LM + 1], float (*s_K)[N], float (*s_sw)[LM]) {
+    using MX = MxRing<P, N, 1, LM>;
+    constexpr int VR = (P + 63) / 64;
+    constexpr uint32_t ES = 2;
+    const int L = A.L, count = cold + 1;
+    const size_t gring = ((size_t)b * A.G + g) * L;
+    const size_t hring = bh * L;
+    const size_t gin = (size_t)b * A.G + g;
+    const int bmod = base % L;
+    auto slot = [&](int j) { return ring_slot(bmod, j, L); };
+    const int lastr = cold > 0 ? cold - 1 : 0;   // clamp for ring loads (never used when cold == 0)
+    const int lr = lane & 15, lq = lane >> 4;
+
+    // 1. every load, issued before any value is used: this step's token
+    // first, then the ring
+    const float a_in = A.a[bh], dt_in = A.dt[bh];
+    IoVec<true, 1> vnew[VR];     // lane p: the new v (ring write)
+#pragma unroll
+    for (int rr = 0; rr < VR; ++rr) vnew[rr].load(A.v, bh * P + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
+    const bool group_writer = (h % (A.H / A.G)) == 0;
+    RowWords<N, true> qrow, krow;   // lane i: words i of the new q and k rows
+    static_assert(RowWords<N, true>::WPL == 1, "one word of a row per lane");
+    qrow.load(static_cast<const char *>(A.q) + gin * N * ES, lane);
+    if (group_writer) krow.load(static_cast<const char *>(A.k) + gin * N * ES, lane);
+    MX m;
+    const int sla = slot(lane < cold ? lane : lastr);
+    const float a_r = A.ring_a[hring + sla], dt_r = A.ring_dt[hring + sla];
+#pragma unroll
+    for (int kb = 0; kb < MX::KB; ++kb) {
+        const int c = MX::col(kb, lane);
+#pragma unroll
+        for (int jb = 0; jb < MX::JB; ++jb) {
+            const int j = 16 * jb + lr;   // entries < cold from the ring, the rest from this step's k
+            const bool old = j < cold;
+            m.ka[jb][kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(old ? A.ring_k : A.k) +
+                                                            (old ? (gring + slot(j)) * N : gin * N) + c);
+        }
+    }
+    const auto vres = make_rsrc(static_cast<const char *>(A.ring_v) + hring * P * ES, (uint32_t)(L * P * ES));
+#pragma unroll
+    for (int jb = 0; jb < MX::JB; ++jb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int j = 16 * jb + 4 * lq + kk;
+            const uint32_t row = (uint32_t)slot(j < cold ? j : lastr) * P;
+#pragma unroll
+            for (int pw = 0; pw < MX::PW; ++pw)
+                m.vw[jb][kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * ES, 0, 0);
+        }
+    uint32_t vin[MX::PW];   // this step's v in the same pair layout (operand of entry cold)
+#pragma unroll
+    for (int pw = 0; pw < MX::PW; ++pw) vin[pw] = static_cast<const uint32_t *>(A.v)[(bh * P) / 2 + MX::vword(pw, lane)];
+
+    // 2. this step's token goes into ring slot (pos mod L) = entry cold, as
+    // soon as it has arrived (no ring value used above comes from that slot)
+    const int sn = slot(cold);
+#pragma unroll
+    for (int rr = 0; rr < VR; ++rr) {
+        const int p = lane + 64 * rr;
+        if (p < P) static_cast<uint16_t *>(A.ring_v)[(hring + sn) * P + p] = (uint16_t)vnew[rr].r;
+    }
+    if (lane == 0) {
+        A.ring_dt[hring + sn] = dt_in;
+        A.ring_a[hring + sn] = a_in;
+    }
+    if (group_writer) {
+        const size_t off = (gring + sn) * N * ES;
+        qrow.store(static_cast<char *>(A.ring_q) + off, lane);
+        krow.store(static_cast<char *>(A.ring_k) + off, lane);
+    }
+    // Arrival of this workgroup (its pointer read is done: the loads above
+    // depend on it).  Its result is needed only at the very end.
+    int prev = -1;
+    if (lane == 0) prev = atomicAdd(&A.sync[b], 1);
+
+    // 3. entry cold and past it: this step's token (the query, the B operand
+    // of every column, gathered from the row's words)
+#pragma unroll
+    for (int kb = 0; kb < MX::KB; ++kb) {
+        const int w0 = MX::col(kb, lane) / 2;
+        m.qb[kb] = uint4{(uint32_t)__shfl((int)qrow.w[0], w0), (uint32_t)__shfl((int)qrow.w[0], w0 + 1),
+                         (uint32_t)__shfl((int)qrow.w[0], w0 + 2), (uint32_t)__shfl((int)qrow.w[0], w0 + 3)};
+    }
+    m.aj = lane < cold ? a_r : (lane == cold ? a_in : 1.f);
+    m.dtj = lane < cold ? dt_r : (lane == cold ? dt_in : 0.f);
+#pragma unroll
+    for (int jb = 0; jb < MX::JB; ++jb)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int pw = 0; pw < MX::PW; ++pw)
+                if (16 * jb + 4 * lq + kk >= cold) m.vw[jb][kk][pw] = vin[pw];
+
+    if (!fold) {
+        f32x4 dk[MX::JB];
+        m.dots(lane, dk);
+        m.weights(lane, count, s_abar, s_sw);
+        m.term(lane, dk, reinterpret_cast<float (*)[P]>(s_r), s_sw);
+    } else {
+        // state-and-output route: stage U[p][j] = s_j v_j[p] and K[j][n] = k_j[n]
+        m.weights(lane, count, s_abar, s_sw);
+#pragma unroll
+        for (int jb = 0; jb < MX::JB; ++jb)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int j = 16 * jb + 4 * lq + kk;
+                if (j < count) {
+                    const float sj = s_sw[0][j];
+#pragma unroll
+                    for (int pw = 0; pw < MX::PW; ++pw)
+#pragma unroll
+                        for (int half = 0; half < 2; ++half) {
+                            const int p = 32 * pw + 2 * lr + half;
+                            if (p < P) s_U[p][j] = sj * MX::vval(m.vw[jb][kk][pw], half);
+                        }
+                }
+            }
+#pragma unroll
+        for (int jb = 0; jb < MX::JB; ++jb) {
+            const int j = 16 * jb + lr;
+            if (j < count) {
+#pragma unroll
+                for (int kb = 0; kb < MX::KB; ++kb) {
+                    const int c = 32 * kb + 8 * lq;
+                    if (c < N) {
+                        IoVec<true, 8> kv;
+                        kv.r = m.ka[jb][kb];
+                        float kk8[8];
+                        kv.widen(kk8);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) s_K[j][c + e] = kk8[e];
+                    }
+                }
+            }
+        }
+    }
+    return prev;
+}
+
 // Waves per SIMD to ask the register allocator for: 8 (the hardware maximum,
 // 64 registers a lane) where the kernel fits without spilling to scratch,
 // otherwise no request.
@@ -230,6 +378,7 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
     __shared__ int s_count;
     __shared__ float s_U[P][LM + 1];
     __shared__ __align__(16) float s_K[LM][N];
+    __shared__ __align__(16) float s_sw[1][IOB ? LM : 4];
 
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int H = args.H, L = args.L;
@@ -280,8 +429,14 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
             s_count = cold + 1;
             if (bad) raise_seq_error(args.err, b, cold + 1 > L ? REPLAY_SEQERR_RING_OVERFLOW : REPLAY_SEQERR_POS_OVERFLOW);
         }
-        if (!bad)
-            prev = step_ring_wave<P, N, LM, IOB>(args, lane, b, g, h, bh, base, cold, route == 1, s_r, &s_abar, s_U, s_K);
+        if (!bad) {
+            if constexpr (IOB)
+                prev = step_ring_wave_mx<P, N, LM>(args, lane, b, g, h, bh, base, cold, route == 1, s_r, &s_abar,
+                                                   s_U, s_K, reinterpret_cast<float (*)[LM]>(&s_sw[0][0]));
+            else
+                prev = step_ring_wave<P, N, LM, IOB>(args, lane, b, g, h, bh, base, cold, route == 1, s_r, &s_abar,
+                                                     s_U, s_K);
+        }
     }
     // LDS-only barrier: the ring wavefront's write-back of the new token and
     // its arrival atomic complete in the background
