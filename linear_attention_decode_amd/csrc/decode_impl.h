@@ -31,7 +31,8 @@ struct DecodeShape {
     static constexpr int VEC = (P * N / base_vec >= 64) ? base_vec
                              : ((P * N / (base_vec / 2) >= 64) ? base_vec / 2 : base_vec / 4);
     static constexpr int CHUNKS = P * N / VEC;
-    static constexpr int NTS = CHUNKS < 256 ? CHUNKS : 256;   // streaming threads
+    // streaming threads: at most 8 chunks a lane (4096 chunks: 8 wavefronts)
+    static constexpr int NTS = CHUNKS >= 4096 ? 512 : (CHUNKS < 256 ? CHUNKS : 256);
     static constexpr int NT = NTS + 64;                       // + one ring wavefront
     static constexpr int ITER = CHUNKS / NTS;
     static constexpr int LPR = N / VEC;     // lanes per state row

@@ -13,9 +13,9 @@
 // estandar": buffer the inputs, output by the output-only route, flush when
 // the buffer is full).  The checkpoint is read once per step either way.
 //
-// Workgroup = 4 streaming wavefronts (the head's tile, 16-byte chunks) + 1
-// ring wavefront (decays, group dots, ring term or the rank-c staging, and
-// the ring write of the new token).  The new token is taken from the inputs,
+// Workgroup = 4 streaming wavefronts (8 for a 128 x 128 tile; the head's tile
+// in 16-byte chunks) + 1 ring wavefront (decays, group dots, ring term or the
+// rank-c staging, and the ring write of the new token).  The new token is taken from the inputs,
 // so the streaming wavefronts never wait for the ring pointer.  The pointer
 // of a sequence moves when its last workgroup arrives (per-sequence counter).
 #include "ring_mx.h"
@@ -26,7 +26,8 @@ template <int P, int N>
 struct StepShape {
     static constexpr int VEC = 4;
     static constexpr int CHUNKS = P * N / VEC;
-    static constexpr int NTS = CHUNKS < 256 ? CHUNKS : 256;   // streaming threads
+    // streaming threads: at most 8 chunks a lane (4096 chunks: 8 wavefronts)
+    static constexpr int NTS = CHUNKS >= 4096 ? 512 : (CHUNKS < 256 ? CHUNKS : 256);
     static constexpr int NT = NTS + 64;
     static constexpr int ITER = CHUNKS / NTS;
     static constexpr int LPR = N / VEC;
@@ -363,7 +364,7 @@ __device__ __forceinline__ int step_ring_wave_mx(const StepArgs &A, int lane, in
 // otherwise no request.
 template <int P, int N, int LM, bool IOB>
 constexpr int step_waves() {
-    return (P * N <= 64 * 64 || (P == 64 && N == 128 && LM == 16 && IOB)) && !(LM == 32 && P * N > 16 * 16) ? 8 : 1;
+    return (P * N <= 64 * 64 || (N == 128 && LM == 16 && IOB)) && !(LM == 32 && P * N > 16 * 16) ? 8 : 1;
 }
 
 template <int P, int N, int LM, bool IOB>
