@@ -145,8 +145,10 @@ def _counter_traffic(kernel_files, summary_name):
 
 
 DECODE_SOURCES = ["linear_attention_decode_amd/csrc/decode_impl.h",
+                  "linear_attention_decode_amd/csrc/ring_mx.h",
                   "linear_attention_decode_amd/csrc/device_common.h"]
 STEP_SOURCES = ["linear_attention_decode_amd/csrc/step.hip",
+                "linear_attention_decode_amd/csrc/ring_mx.h",
                 "linear_attention_decode_amd/csrc/device_common.h"]
 
 
@@ -282,8 +284,10 @@ def bench_decode(args):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kernel_name, "avg_launch_us": avg_us,
                      "algorithmic_bytes_per_launch": kernel_bytes / len(counts)},
-        "decode_avg_us": 1e3 * sum(dec_ms) / max(1, len(dec_ms)),
-        "flush_avg_us": 1e3 * sum(fl_ms) / max(1, len(fl_ms)),
+        ("output_only_launch_avg_us" if args.api == "step" else "decode_avg_us"):
+            1e3 * sum(dec_ms) / max(1, len(dec_ms)),
+        ("fold_launch_avg_us" if args.api == "step" else "flush_avg_us"):
+            1e3 * sum(fl_ms) / max(1, len(fl_ms)),
         "eager": eager_out,
         "speedup_vs_eager": (B * args.steps / elapsed) / eager_out["value"] if eager_out else None,
         "window_bytes_ratio_vs_eager": window_replay / window_eager,
