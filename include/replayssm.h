@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define REPLAY_ABI_VERSION 2
+#define REPLAY_ABI_VERSION 3
 
 typedef enum {
     REPLAY_OK = 0,
@@ -108,8 +108,10 @@ typedef struct {
     int32_t *pos;       /* [B] tokens appended and not rolled back */
     int32_t *base;      /* [B] pos at the last flush; count = pos - base */
     int32_t *err;       /* [B + 1] error bits: err[0] = OR over sequences, err[1 + b] per sequence */
-    int32_t *sync;      /* [B] arrival counters of replay_step; zeroed by replay_init and zero
-                           again whenever no call is in flight */
+    int32_t *sync;      /* [B][32] arrival counters of replay_step, one per 128-byte line
+                           (element [b][0]; the rest is padding so that no two sequences'
+                           counters share a line); zeroed by replay_init and zero again
+                           whenever no call is in flight */
 } replay_buffers;
 
 typedef struct replay_handle replay_handle;

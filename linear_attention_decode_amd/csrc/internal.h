@@ -15,6 +15,11 @@ enum StateKind : int { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2 };
 constexpr int kMaxRing = 32;
 constexpr int kMaxWindow = 8;
 
+// Arrival counters of the fused step: one int32 per 128-byte line.  Packed
+// counters put 32 sequences' atomics on one line, and the device-scope
+// atomics of all their workgroups then queue behind each other.
+constexpr int kSyncStride = 32;
+
 // Everything a kernel needs to find one layer's ring.
 struct RingView {
     const void *q;      // [B][G][L][N]
@@ -52,7 +57,7 @@ struct FlushArgs {
 struct StepArgs {
     void *ring_q, *ring_k, *ring_v;   // [B][G][L][N] x2, [B][H][L][P]
     float *ring_dt, *ring_a;          // [B][H][L]
-    int32_t *pos, *base, *err, *sync;
+    int32_t *pos, *base, *err, *sync;  // sync: [B][kSyncStride], element [b][0]
     float *S;                         // [B][H][P][N] master, read and (when folding) written
     const void *q, *k, *v;            // [B][G][N] x2, [B][H][P]
     const float *dt, *a;              // [B][H]

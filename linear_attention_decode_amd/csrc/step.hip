@@ -140,7 +140,7 @@ __device__ __forceinline__ int step_ring_wave(const StepArgs &A, int lane, int b
     // Arrival of this workgroup (its pointer read is done: the loads above
     // depend on it).  Its result is needed only at the very end.
     int prev = -1;
-    if (lane == 0) prev = atomicAdd(&A.sync[b], 1);
+    if (lane == 0) prev = atomicAdd(&A.sync[(size_t)b * kSyncStride], 1);
 
     // 3. decays of entries 0..count-1 (entry cold is this step's token)
     const float aj = lane < cold ? a_r : (lane == cold ? a_in : 1.f);
@@ -293,7 +293,7 @@ __device__ __forceinline__ int step_ring_wave_mx(const StepArgs &A, int lane, in
     // Arrival of this workgroup (its pointer read is done: the loads above
     // depend on it).  Its result is needed only at the very end.
     int prev = -1;
-    if (lane == 0) prev = atomicAdd(&A.sync[b], 1);
+    if (lane == 0) prev = atomicAdd(&A.sync[(size_t)b * kSyncStride], 1);
 
     // 3. entry cold and past it: this step's token (the query, the B operand
     // of every column, gathered from the row's words)
@@ -491,7 +491,7 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
     } else if (lane == 0 && prev == H - 1) {
         // Last workgroup of the sequence to arrive: every workgroup of it has
         // read the pointer (each arrived right after its read), so it moves.
-        atomicExch(&args.sync[b], 0);
+        atomicExch(&args.sync[(size_t)b * kSyncStride], 0);
         args.pos[b] = pos + 1;
         if (route == 1) args.base[b] = pos + 1;
     }

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lad):
 
 
 def test_version_and_status_strings(lad):
-    assert lad.replay_abi_version() == 2
+    assert lad.replay_abi_version() == 3
     for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "HIP")]:
         assert text in lad.replay_status_string(s)
     assert lad.replay_status_string(99) == "unknown status"
@@ -48,7 +48,7 @@ def test_buffer_bytes_match_the_layout(lad):
     assert b["ring_q"] == b["ring_k"] == 256 * 8 * 16 * 128 * 2
     assert b["ring_v"] == 256 * 128 * 16 * 64 * 2
     assert b["ring_dt"] == b["ring_a"] == 256 * 128 * 16 * 4
-    assert b["pos"] == b["base"] == 256 * 4 and b["err"] == 257 * 4 and b["sync"] == 256 * 4
+    assert b["pos"] == b["base"] == 256 * 4 and b["err"] == 257 * 4 and b["sync"] == 256 * 128
     c8 = lad.ReplayConfig(4, 8, 2, 128, 128, 32, lad.F32, lad.FP8_E4M3, 1)
     b8 = lad.replay_buffer_bytes(c8)
     assert b8["s_master"] == 0 and b8["s_copy"] == 4 * 8 * 128 * 128 and b8["s_scale"] == 4 * 8 * 4
