@@ -206,7 +206,7 @@ class ReplayLayer:
     mode), s_copy [B,H,P,N] bf16/uint8 (when read_copy is set), s_scale
     [B,H] f32 (e4m3 copy), ring_q/ring_k [B,G,L,N], ring_v [B,H,L,P] (io
     dtype), ring_dt/ring_a [B,H,L] f32, pos/base [B] int32, err [B+1] int32,
-    sync [B, 32] int32 (one arrival counter per 128-byte line).
+    sync [B, G+1, 32] int32 (arrival counters, one per 128-byte line).
     """
 
     def __init__(self, batch, heads, groups, head_dim, state_dim, ring_len, io_dtype="bf16",
@@ -226,7 +226,7 @@ class ReplayLayer:
             "ring_k": ((B, G, L, N), iot), "ring_v": ((B, H, L, P), iot),
             "ring_dt": ((B, H, L), torch.float32), "ring_a": ((B, H, L), torch.float32),
             "pos": ((B,), torch.int32), "base": ((B,), torch.int32), "err": ((B + 1,), torch.int32),
-            "sync": ((B, 32), torch.int32),
+            "sync": ((B, G + 1, 32), torch.int32),
         }
         self.t = {}
         for name in BUFFER_FIELDS:

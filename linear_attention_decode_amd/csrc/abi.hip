@@ -70,7 +70,7 @@ void buffer_bytes(const replay_config &c, size_t out[kNumBufferFields]) {
     out[8] = B * 4;                                                                     // pos
     out[9] = B * 4;                                                                     // base
     out[10] = (B + 1) * 4;                                                              // err
-    out[11] = B * 4 * kSyncStride;                                                      // sync
+    out[11] = B * (size_t)(c.groups + 1) * 4 * kSyncStride;                             // sync
 }
 
 const void *field(const replay_buffers &b, int i) {

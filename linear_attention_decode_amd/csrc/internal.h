@@ -15,9 +15,10 @@ enum StateKind : int { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2 };
 constexpr int kMaxRing = 32;
 constexpr int kMaxWindow = 8;
 
-// Arrival counters of the fused step: one int32 per 128-byte line.  Packed
-// counters put 32 sequences' atomics on one line, and the device-scope
-// atomics of all their workgroups then queue behind each other.
+// Arrival counters of the fused step, [B][G + 1] of them, one int32 per
+// 128-byte line: a workgroup arrives at its group's counter, the last head
+// of a group at the sequence's.  Counters that share a line, or one counter
+// for all H heads, make the device-scope atomics queue behind each other.
 constexpr int kSyncStride = 32;
 
 // Everything a kernel needs to find one layer's ring.
@@ -57,7 +58,7 @@ struct FlushArgs {
 struct StepArgs {
     void *ring_q, *ring_k, *ring_v;   // [B][G][L][N] x2, [B][H][L][P]
     float *ring_dt, *ring_a;          // [B][H][L]
-    int32_t *pos, *base, *err, *sync;  // sync: [B][kSyncStride], element [b][0]
+    int32_t *pos, *base, *err, *sync;  // sync: [B][G + 1][kSyncStride], element [..][0]
     float *S;                         // [B][H][P][N] master, read and (when folding) written
     const void *q, *k, *v;            // [B][G][N] x2, [B][H][P]
     const float *dt, *a;              // [B][H]

@@ -140,7 +140,7 @@ __device__ __forceinline__ int step_ring_wave(const StepArgs &A, int lane, int b
     // Arrival of this workgroup (its pointer read is done: the loads above
     // depend on it).  Its result is needed only at the very end.
     int prev = -1;
-    if (lane == 0) prev = atomicAdd(&A.sync[(size_t)b * kSyncStride], 1);
+    if (lane == 0) prev = atomicAdd(&A.sync[((size_t)b * (A.G + 1) + g) * kSyncStride], 1);
 
     // 3. decays of entries 0..count-1 (entry cold is this step's token)
     const float aj = lane < cold ? a_r : (lane == cold ? a_in : 1.f);
@@ -293,7 +293,7 @@ __device__ __forceinline__ int step_ring_wave_mx(const StepArgs &A, int lane, in
     // Arrival of this workgroup (its pointer read is done: the loads above
     // depend on it).  Its result is needed only at the very end.
     int prev = -1;
-    if (lane == 0) prev = atomicAdd(&A.sync[(size_t)b * kSyncStride], 1);
+    if (lane == 0) prev = atomicAdd(&A.sync[((size_t)b * (A.G + 1) + g) * kSyncStride], 1);
 
     // 3. entry cold and past it: this step's token (the query, the B operand
     // of every column, gathered from the row's words)
@@ -386,6 +386,11 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
     const int b = lid / H, h = lid % H;
     const int g = (h * args.G) / H;
     const int tid = threadIdx.x, lane = tid & 63;
+    // the role of this wavefront, as a wave-uniform value: the branches on it
+    // are scalar, so the ring wavefront's pointer reads go through the scalar
+    // cache instead of queueing behind the tile loads of every wavefront on
+    // the CU
+    const bool streamer = __builtin_amdgcn_readfirstlane(tid >> 6) < NTS / 64;
     const size_t bh = (size_t)b * H + h;
     const size_t tile = bh * (size_t)(P * N);
 
@@ -401,7 +406,7 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
     float qv[VEC];
     float part[ITER][1];
     int pos = 0, prev = -1, route = 0;
-    if (tid < NTS) {
+    if (streamer) {
 #pragma unroll
         for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
         IoVec<IOB, 4> qraw;
@@ -442,11 +447,11 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
     // LDS-only barrier: the ring wavefront's write-back of the new token and
     // its arrival atomic complete in the background
     lds_barrier();
-    if (tid < NTS) route = s_route;
+    if (streamer) route = s_route;
 
-    if (tid < NTS && route == 2) {
+    if (streamer && route == 2) {
         for (int i = tid; i < P; i += NTS) args.y[bh * P + i] = __builtin_nanf("");
-    } else if (tid < NTS) {
+    } else if (streamer) {
         if (route == 1) {
             const float abar = s_abar;
             float x[ITER][VEC];
@@ -488,12 +493,18 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
                 args.y[bh * P + row] = route == 1 ? part[e][0] : abar * part[e][0] + s_r[row];
             }
         }
-    } else if (lane == 0 && prev == H - 1) {
-        // Last workgroup of the sequence to arrive: every workgroup of it has
-        // read the pointer (each arrived right after its read), so it moves.
-        atomicExch(&args.sync[(size_t)b * kSyncStride], 0);
-        args.pos[b] = pos + 1;
-        if (route == 1) args.base[b] = pos + 1;
+    } else if (lane == 0 && prev == H / args.G - 1) {
+        // Last head of its group to arrive: the group arrives at the
+        // sequence's counter.  The last group to arrive means every workgroup
+        // of the sequence has read the pointer (each arrived after its read),
+        // so the pointer moves.
+        int32_t *seq = args.sync + (size_t)b * (args.G + 1) * kSyncStride;
+        atomicExch(seq + (size_t)g * kSyncStride, 0);
+        if (atomicAdd(seq + (size_t)args.G * kSyncStride, 1) == args.G - 1) {
+            atomicExch(seq + (size_t)args.G * kSyncStride, 0);
+            args.pos[b] = pos + 1;
+            if (route == 1) args.base[b] = pos + 1;
+        }
     }
 }
 

@@ -48,7 +48,7 @@ def test_buffer_bytes_match_the_layout(lad):
     assert b["ring_q"] == b["ring_k"] == 256 * 8 * 16 * 128 * 2
     assert b["ring_v"] == 256 * 128 * 16 * 64 * 2
     assert b["ring_dt"] == b["ring_a"] == 256 * 128 * 16 * 4
-    assert b["pos"] == b["base"] == 256 * 4 and b["err"] == 257 * 4 and b["sync"] == 256 * 128
+    assert b["pos"] == b["base"] == 256 * 4 and b["err"] == 257 * 4 and b["sync"] == 256 * 9 * 128
     c8 = lad.ReplayConfig(4, 8, 2, 128, 128, 32, lad.F32, lad.FP8_E4M3, 1)
     b8 = lad.replay_buffer_bytes(c8)
     assert b8["s_master"] == 0 and b8["s_copy"] == 4 * 8 * 128 * 128 and b8["s_scale"] == 4 * 8 * 4
