@@ -152,6 +152,27 @@ STEP_SOURCES = ["linear_attention_decode_amd/csrc/step.hip",
                 "linear_attention_decode_amd/csrc/device_common.h"]
 
 
+def read_ceiling_gbs(nbytes=1 << 30, reps=7):
+    """Read-bandwidth ceiling measured by the library's stream probe (mode 0:
+    32 KiB tiles, all loads in flight, non-temporal), median of reps."""
+    import torch
+    import linear_attention_decode_amd as lad
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty((nbytes + 32767) // 32768, dtype=torch.float32, device="cuda")
+    ts = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        lad.replay_stream_probe(0, src, dst, nbytes)
+        e.record()
+        ts.append((s, e))
+    torch.cuda.synchronize()
+    us = sorted(s.elapsed_time(e) * 1e3 for s, e in ts)[reps // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return nbytes / us / 1e3
+
+
 def _bench_eager(args, w, pool, y):
     """The eager per-token baseline on the same inputs, timed like the steps."""
     import torch
@@ -255,6 +276,7 @@ def bench_decode(args):
     torch.cuda.empty_cache()
 
     eager_out = None if args.no_eager else _bench_eager(args, w, pool, y)
+    ceiling = read_ceiling_gbs()
 
     window_replay = sum(decode_bytes(w, c, 1, st_bytes) for c in range(1, L + 1)) \
         + flush_bytes(w, L, 0 if st_bytes == 4 else st_bytes) \
@@ -283,7 +305,8 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kernel_name, "avg_launch_us": avg_us,
-                     "algorithmic_bytes_per_launch": kernel_bytes / len(counts)},
+                     "algorithmic_bytes_per_launch": kernel_bytes / len(counts),
+                     "read_ceiling_GBs": ceiling, "frac_of_read_ceiling": achieved / ceiling},
         ("output_only_launch_avg_us" if args.api == "step" else "decode_avg_us"):
             1e3 * sum(dec_ms) / max(1, len(dec_ms)),
         ("fold_launch_avg_us" if args.api == "step" else "flush_avg_us"):

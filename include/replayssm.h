@@ -221,10 +221,13 @@ replay_status replay_eager_step(const replay_config *cfg, const float *s_in, flo
 replay_status replay_eager_select(const replay_config *cfg, const float *snaps, int32_t W,
                                   const int32_t *n_accept, float *s, void *stream);
 
-/* HBM stream probe, the bandwidth ceiling the other kernels are quoted
-   against.  mode 0: read `bytes` from src and write one float per
-   workgroup into dst (needs 4 * 2048 bytes); mode 1: copy `bytes` from src
-   to dst.  bytes must be a multiple of 16. */
+/* HBM stream probes, the bandwidth ceilings the other kernels are quoted
+   against: every workgroup streams one 32 KiB tile with all its loads in
+   flight, as the checkpoint stream of decode does.  mode 0: read `bytes`
+   from src (dst: 4 * ceil(bytes / 32768) bytes, written only in the
+   practically impossible case that a tile's xor equals a fixed constant);
+   mode 1: copy `bytes` from src to dst (must not overlap).  bytes must be a
+   multiple of 16. */
 replay_status replay_stream_probe(int32_t mode, const void *src, void *dst, size_t bytes,
                                   void *stream);
 

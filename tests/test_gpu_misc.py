@@ -229,6 +229,6 @@ def test_stream_probe_copy():
     lad.replay_stream_probe(1, src, dst, n)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
-    out = torch.zeros(2048, dtype=torch.float32, device=gu.DEV)
+    out = torch.zeros((n + 32767) // 32768, dtype=torch.float32, device=gu.DEV)
     lad.replay_stream_probe(0, src, out, n)
     torch.cuda.synchronize()
