@@ -33,7 +33,6 @@ struct DecodeShape {
     static constexpr int CHUNKS = P * N / VEC;
     // streaming threads: at most 8 chunks a lane (4096 chunks: 8 wavefronts)
     static constexpr int NTS = CHUNKS >= 4096 ? 512 : (CHUNKS < 256 ? CHUNKS : 256);
-    static constexpr int NT = NTS + 64;                       // + one ring wavefront
     static constexpr int ITER = CHUNKS / NTS;
     static constexpr int LPR = N / VEC;     // lanes per state row
     static constexpr int RPI = NTS / LPR;   // rows per iteration
@@ -170,10 +169,11 @@ __device__ __forceinline__ void ring_wave(const RingView &r, int lane, int b, in
 
 // The same work for bf16 io on the matrix cores (ring_mx.h), operands read
 // from the ring: every entry and query from its ring slot, indices clamped to
-// the live range.
+// the live range.  This wavefront covers entries j0..j0+15.
 template <int P, int N, int WM, int LM>
-__device__ __forceinline__ void ring_wave_mx(const RingView &r, int lane, int b, int g, size_t bh, int base,
-                                             int count, float (*s_r)[P], float *s_abar, float (*s_sw)[LM]) {
+__device__ __forceinline__ void ring_wave_mx(const RingView &r, int lane, int j0, int b, int g, size_t bh,
+                                             int base, int count, float (*s_r)[P], float *s_abar,
+                                             float (*s_sw)[LM]) {
     using MX = MxRing<P, N, WM, LM>;
     const int L = r.L;
     const size_t gring = ((size_t)b * r.G + g) * L;
@@ -185,6 +185,7 @@ __device__ __forceinline__ void ring_wave_mx(const RingView &r, int lane, int b,
     const int lr = lane & 15, lq = lane >> 4;
 
     MX m;
+    m.j0 = j0;
     {
         const int sl = slot(lane < count ? lane : last);
         m.aj = r.a[hring + sl];
@@ -193,44 +194,45 @@ __device__ __forceinline__ void ring_wave_mx(const RingView &r, int lane, int b,
 #pragma unroll
     for (int kb = 0; kb < MX::KB; ++kb) {
         const int c = MX::col(kb, lane);
-#pragma unroll
-        for (int jb = 0; jb < MX::JB; ++jb) {
-            const int j = 16 * jb + lr;
-            m.ka[jb][kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.k) +
-                                                            (gring + slot(j < count ? j : last)) * N + c);
-        }
+        const int j = j0 + lr;
+        m.ka[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.k) +
+                                                    (gring + slot(j < count ? j : last)) * N + c);
         m.qb[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.q) +
                                                     (gring + slot(t0 + (lr < WM ? lr : WM - 1))) * N + c);
     }
     const auto vres = make_rsrc(static_cast<const uint16_t *>(r.v) + hring * P, (uint32_t)(L * P * 2));
 #pragma unroll
-    for (int jb = 0; jb < MX::JB; ++jb)
+    for (int kk = 0; kk < 4; ++kk) {
+        const int j = j0 + 4 * lq + kk;
+        const uint32_t row = (uint32_t)slot(j < count ? j : last) * P;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int j = 16 * jb + 4 * lq + kk;
-            const uint32_t row = (uint32_t)slot(j < count ? j : last) * P;
-#pragma unroll
-            for (int pw = 0; pw < MX::PW; ++pw)
-                m.vw[jb][kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * 2, 0, 0);
-        }
+        for (int pw = 0; pw < MX::PW; ++pw)
+            m.vw[kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * 2, 0, 0);
+    }
     if (lane >= count) {
         m.aj = 1.f;
         m.dtj = 0.f;
     }
-    f32x4 dk[MX::JB];
-    m.dots(lane, dk);
+    const f32x4 dk = m.dots(lane);
     m.weights(lane, count, s_abar, s_sw);
     m.term(lane, dk, s_r, s_sw);
 }
 
+// Ring wavefronts of the decode kernel: two for a 32-entry ring with bf16 io
+// (one per 16-entry block), else one.
+template <int LM, bool IOB>
+constexpr int ring_waves() { return IOB ? LM / 16 : 1; }
+
 template <int P, int N, int ST, int WM, int LM, bool IOB>
-__global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NT)) void decode_kernel(DecodeArgs args) {
+__global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NTS + 64 * ring_waves<LM, IOB>())) void decode_kernel(
+    DecodeArgs args) {
     using Sh = DecodeShape<P, N, ST, WM>;
     constexpr int W = WM;
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+    constexpr int NR = ring_waves<LM, IOB>(), NT = NTS + 64 * NR;
     using RR = RowReduce<ITER, LPR>;
 
-    __shared__ float s_r[WM][P];
+    __shared__ float s_r[NR][WM][P];
     __shared__ float s_abar[WM];
     __shared__ __align__(16) float s_sw[IOB ? WM : 1][IOB ? LM : 4];
 
@@ -253,7 +255,7 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NT)) void decode_kernel
     }
     const int count = pos - base;
     if (count < W) {  // uniform over the workgroup
-        for (int i = tid; i < W * P; i += Sh::NT) {
+        for (int i = tid; i < W * P; i += NT) {
             const int w = i / P, p = i % P;
             args.y[(((size_t)b * W + w) * H + h) * P + p] = __builtin_nanf("");
         }
@@ -293,10 +295,12 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NT)) void decode_kernel
         }
         RR::template run<WM>(part, lane);
     } else {
-        if constexpr (IOB)
-            ring_wave_mx<P, N, WM, LM>(r, lane, b, g, bh, base, count, s_r, s_abar, s_sw);
-        else
-            ring_wave<P, N, WM, LM, IOB>(r, lane, b, g, bh, base, count, s_r, s_abar);
+        if constexpr (IOB) {
+            const int rw = (tid - NTS) >> 6;
+            ring_wave_mx<P, N, WM, LM>(r, lane, 16 * rw, b, g, bh, base, count, s_r[rw], s_abar, s_sw);
+        } else {
+            ring_wave<P, N, WM, LM, IOB>(r, lane, b, g, bh, base, count, s_r[0], s_abar);
+        }
     }
     __syncthreads();
 
@@ -309,8 +313,9 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NT)) void decode_kernel
 #pragma unroll
             for (int w = 0; w < WM; ++w) {
                 if (w < W) {
-                    args.y[(((size_t)b * W + w) * H + h) * P + row] =
-                        s_abar[w] * (sc * part[e][w]) + s_r[w][row];
+                    float rt = s_r[0][w][row];
+                    if constexpr (NR == 2) rt += s_r[1][w][row];   // block 0 + block 1
+                    args.y[(((size_t)b * W + w) * H + h) * P + row] = s_abar[w] * (sc * part[e][w]) + rt;
                 }
             }
         }
@@ -321,7 +326,7 @@ template <int P, int N, int ST, int WM, int LM, bool IOB>
 static hipError_t launch_one(const DecodeArgs &a, hipStream_t s) {
     using Sh = DecodeShape<P, N, ST, WM>;
     const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
-    decode_kernel<P, N, ST, WM, LM, IOB><<<blocks, Sh::NT, 0, s>>>(a);
+    decode_kernel<P, N, ST, WM, LM, IOB><<<blocks, Sh::NTS + 64 * ring_waves<LM, IOB>(), 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -365,12 +365,17 @@ struct RowReduce {
             const int bit = K - 1 - s;
             const int half = ITER >> (s + 1);
             const bool upper = (lane >> bit) & 1;
+            // bitwise selects: a select between two elements of v can be
+            // rewritten into a load at a selected index, which sends v to
+            // scratch memory
+            const uint32_t mk = upper ? 0xffffffffu : 0u;
 #pragma unroll
             for (int e = 0; e < half; ++e) {
 #pragma unroll
                 for (int w = 0; w < WM; ++w) {
-                    const float keep = upper ? v[e + half][w] : v[e][w];
-                    const float send = upper ? v[e][w] : v[e + half][w];
+                    const uint32_t lo = __float_as_uint(v[e][w]), hi = __float_as_uint(v[e + half][w]);
+                    const float keep = __uint_as_float((hi & mk) | (lo & ~mk));
+                    const float send = __uint_as_float((lo & mk) | (hi & ~mk));
                     v[e][w] = keep + lane_partner(send, bit);
                 }
             }

@@ -29,18 +29,22 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+// One ring wavefront's share: the 16 entries j0..j0+15 (a 32-entry ring
+// has two such wavefronts; their terms are added by the caller, block 0 +
+// block 1).
 template <int P, int N, int WM, int LM>
 struct MxRing {
-    static constexpr int JB = LM / 16;            // 16-entry blocks
     static constexpr int KB = (N + 31) / 32;      // 32-column blocks of k . q
     static constexpr int PW = (P + 31) / 32;      // 32-column blocks of v, one bf16 pair per lane
+    static constexpr int NR = LM / 16;            // ring wavefronts per (sequence, head)
     static_assert(LM % 16 == 0 && P % 16 == 0 && N % 16 == 0, "tile shape");
 
     // Operands, filled by the caller with raw bf16 bits.  Lane l = r + 16 g:
-    uint4 ka[JB][KB];               // k_{16jb + r}[32kb + 8g .. +7]      (entries past the live ones: any finite row)
+    int j0;                         // first entry of this wavefront's block
+    uint4 ka[KB];                   // k_{j0 + r}[32kb + 8g .. +7]        (entries past the live ones: any finite row)
     uint4 qb[KB];                   // q_{t_min(r, W-1)}[32kb + 8g .. +7]
-    uint32_t vw[JB][4][PW];         // v_{16jb + 4g + kk}[32pw + 2r .. +1] (same; pairs past P: any finite word)
-    float aj, dtj;                  // lane j: a_j, dt_j; 1 and 0 for j >= count
+    uint32_t vw[4][PW];             // v_{j0 + 4g + kk}[32pw + 2r .. +1]   (same; pairs past P: any finite word)
+    float aj, dtj;                  // lane j (all LM entries): a_j, dt_j; 1 and 0 for j >= count
 
     // word index of lane l's v pair in block pw, clamped into the row
     static __device__ __forceinline__ int vword(int pw, int lane) {
@@ -57,20 +61,19 @@ struct MxRing {
         return c < N ? c : 0;
     }
 
-    __device__ __forceinline__ void dots(int lane, f32x4 (&dk)[JB]) const {
+    __device__ __forceinline__ f32x4 dots(int lane) const {
+        f32x4 dk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
-            dk[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                uint4 a = ka[jb][kb];
-                if (32 * kb + 8 * (lane >> 4) >= N) a = uint4{0u, 0u, 0u, 0u};   // only when N < 32
-                dk[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[kb]), dk[jb], 0, 0, 0);
-            }
+        for (int kb = 0; kb < KB; ++kb) {
+            uint4 a = ka[kb];
+            if (32 * kb + 8 * (lane >> 4) >= N) a = uint4{0u, 0u, 0u, 0u};   // only when N < 32
+            dk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[kb]), dk, 0, 0, 0);
         }
+        return dk;
     }
 
-    // s_sw[w][j] = s_{j,t_w} (0 for j > t_w or j >= count), s_abar[w] = abar_{t_w}
+    // s_sw[w][j] = s_{j,t_w} (0 for j > t_w or j >= count) for this block's
+    // entries; s_abar[w] = abar_{t_w} from the block-0 wavefront
     __device__ __forceinline__ void weights(int lane, int count, float *s_abar, float (*s_sw)[LM]) const {
         const int t0 = count - WM;
         float sw[WM], ab[WM];
@@ -91,27 +94,22 @@ struct MxRing {
                     }
             }
         }
-        if (lane < LM) {
+        if (lane >= j0 && lane < j0 + 16) {
 #pragma unroll
             for (int w = 0; w < WM; ++w) s_sw[w][lane] = lane <= t0 + w ? sw[w] : 0.f;
         }
-        if (lane == 0) {
+        if (j0 == 0 && lane == 0) {
 #pragma unroll
             for (int w = 0; w < WM; ++w) s_abar[w] = ab[w];
         }
     }
 
-    // s_r[w][p] = R[w][p]; reads the weights this wavefront wrote to s_sw
-    // (a wavefront's own LDS accesses complete in order)
-    __device__ __forceinline__ void term(int lane, const f32x4 (&dk)[JB], float (*s_r)[P],
-                                         const float (*s_sw)[LM]) const {
+    // s_r[w][p] = this block's part of R[w][p]; reads the weights this
+    // wavefront wrote to s_sw (a wavefront's own LDS accesses complete in order)
+    __device__ __forceinline__ void term(int lane, f32x4 dk, float (*s_r)[P], const float (*s_sw)[LM]) const {
         const int lr = lane & 15, lq = lane >> 4;
-        f32x4 cf[JB];
-#pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
-            const f32x4 wv = *reinterpret_cast<const f32x4 *>(&s_sw[lr < WM ? lr : 0][16 * jb + 4 * lq]);
-            cf[jb] = lr < WM ? wv * dk[jb] : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        const f32x4 wv = *reinterpret_cast<const f32x4 *>(&s_sw[lr < WM ? lr : 0][j0 + 4 * lq]);
+        const f32x4 cf = lr < WM ? wv * dk : f32x4{0.f, 0.f, 0.f, 0.f};
         // column n of block (pw, half) is p = 32pw + 2n + half
 #pragma unroll
         for (int pw = 0; pw < PW; ++pw)
@@ -119,10 +117,8 @@ struct MxRing {
             for (int half = 0; half < 2; ++half) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cf[jb][kk], vval(vw[jb][kk][pw], half), acc, 0, 0, 0);
+                for (int kk = 0; kk < 4; ++kk)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cf[kk], vval(vw[kk][pw], half), acc, 0, 0, 0);
                 const int p = 32 * pw + 2 * lr + half;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {

@@ -28,7 +28,6 @@ struct StepShape {
     static constexpr int CHUNKS = P * N / VEC;
     // streaming threads: at most 8 chunks a lane (4096 chunks: 8 wavefronts)
     static constexpr int NTS = CHUNKS >= 4096 ? 512 : (CHUNKS < 256 ? CHUNKS : 256);
-    static constexpr int NT = NTS + 64;
     static constexpr int ITER = CHUNKS / NTS;
     static constexpr int LPR = N / VEC;
     static constexpr int RPI = NTS / LPR;
@@ -211,121 +210,131 @@ __device__ __forceinline__ int step_ring_wave(const StepArgs &A, int lane, int b
     return prev;
 }
 
-// The ring wavefront for bf16 io: the same work with the output-only route
-// on the matrix cores (ring_mx.h).  Entry cold, this step's token, comes from
-// the inputs (k row, query, v); the other operands from the ring, as in
+// The ring wavefronts for bf16 io: the same work with the output-only route
+// on the matrix cores (ring_mx.h); wavefront rw covers entries 16rw..16rw+15
+// (two wavefronts for a 32-entry ring).  Entry cold, this step's token, comes
+// from the inputs (k row, query, v); the other operands from the ring, as in
 // ring_wave_mx of the decode kernel, and every lane, clamped ones included,
 // holds the values the decode kernel holds after an append, so the output
-// of a non-folding step equals decode's bit for bit.
+// of a non-folding step equals decode's bit for bit.  load() issues every
+// load; finish() (wavefront 0: write the token into the ring) arrives and
+// does the rest.
 template <int P, int N, int LM>
-__device__ __forceinline__ int step_ring_wave_mx(const StepArgs &A, int lane, int b, int g, int h, size_t bh,
-                                                 int base, int cold, bool fold, float *s_r, float *s_abar,
-                                                 float (*s_U)[LM + 1], float (*s_K)[N], float (*s_sw)[LM]) {
+struct StepRingMx {
     using MX = MxRing<P, N, 1, LM>;
-    constexpr int VR = (P + 63) / 64;
-    constexpr uint32_t ES = 2;
-    const int L = A.L, count = cold + 1;
-    const size_t gring = ((size_t)b * A.G + g) * L;
-    const size_t hring = bh * L;
-    const size_t gin = (size_t)b * A.G + g;
-    const int bmod = base % L;
-    auto slot = [&](int j) { return ring_slot(bmod, j, L); };
-    const int lastr = cold > 0 ? cold - 1 : 0;   // clamp for ring loads (never used when cold == 0)
-    const int lr = lane & 15, lq = lane >> 4;
-
-    // 1. every load, issued before any value is used: this step's token
-    // first, then the ring
-    const float a_in = A.a[bh], dt_in = A.dt[bh];
-    IoVec<true, 1> vnew[VR];     // lane p: the new v (ring write)
-#pragma unroll
-    for (int rr = 0; rr < VR; ++rr) vnew[rr].load(A.v, bh * P + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
-    const bool group_writer = (h % (A.H / A.G)) == 0;
-    RowWords<N, true> qrow, krow;   // lane i: words i of the new q and k rows
-    static_assert(RowWords<N, true>::WPL == 1, "one word of a row per lane");
-    qrow.load(static_cast<const char *>(A.q) + gin * N * ES, lane);
-    if (group_writer) krow.load(static_cast<const char *>(A.k) + gin * N * ES, lane);
+    static constexpr int VR = (P + 63) / 64;
+    static constexpr uint32_t ES = 2;
     MX m;
-    const int sla = slot(lane < cold ? lane : lastr);
-    const float a_r = A.ring_a[hring + sla], dt_r = A.ring_dt[hring + sla];
+    float a_in, dt_in, a_r, dt_r;
+    IoVec<true, 1> vnew[VR];         // wavefront 0, lane p: the new v (ring write)
+    RowWords<N, true> qrow, krow;    // lane i: words i of the new q (and, group writer, k) rows
+    uint32_t vin[MX::PW];            // the new v in the operand's pair layout (entry cold)
+    static_assert(RowWords<N, true>::WPL == 1, "one word of a row per lane");
+
+    __device__ __forceinline__ void load(const StepArgs &A, int lane, int rw, int b, int g, int h, size_t bh,
+                                         int base, int cold) {
+        const int L = A.L;
+        const size_t gring = ((size_t)b * A.G + g) * L;
+        const size_t hring = bh * L;
+        const size_t gin = (size_t)b * A.G + g;
+        const int bmod = base % L;
+        auto slot = [&](int j) { return ring_slot(bmod, j, L); };
+        const int lastr = cold > 0 ? cold - 1 : 0;   // clamp for ring loads (never used when cold == 0)
+        const int lr = lane & 15, lq = lane >> 4;
+        m.j0 = 16 * rw;
+        // this step's token first, then the ring
+        a_in = A.a[bh];
+        dt_in = A.dt[bh];
+        if (rw == 0) {
 #pragma unroll
-    for (int kb = 0; kb < MX::KB; ++kb) {
-        const int c = MX::col(kb, lane);
-#pragma unroll
-        for (int jb = 0; jb < MX::JB; ++jb) {
-            const int j = 16 * jb + lr;   // entries < cold from the ring, the rest from this step's k
-            const bool old = j < cold;
-            m.ka[jb][kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(old ? A.ring_k : A.k) +
-                                                            (old ? (gring + slot(j)) * N : gin * N) + c);
+            for (int rr = 0; rr < VR; ++rr) vnew[rr].load(A.v, bh * P + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
+            if ((h % (A.H / A.G)) == 0) krow.load(static_cast<const char *>(A.k) + gin * N * ES, lane);
         }
-    }
-    const auto vres = make_rsrc(static_cast<const char *>(A.ring_v) + hring * P * ES, (uint32_t)(L * P * ES));
+        qrow.load(static_cast<const char *>(A.q) + gin * N * ES, lane);
+        const int sla = slot(lane < cold ? lane : lastr);
+        a_r = A.ring_a[hring + sla];
+        dt_r = A.ring_dt[hring + sla];
 #pragma unroll
-    for (int jb = 0; jb < MX::JB; ++jb)
+        for (int kb = 0; kb < MX::KB; ++kb) {
+            const int c = MX::col(kb, lane);
+            const int j = m.j0 + lr;   // entries < cold from the ring, the rest from this step's k
+            const bool old = j < cold;
+            m.ka[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(old ? A.ring_k : A.k) +
+                                                        (old ? (gring + slot(j)) * N : gin * N) + c);
+        }
+        const auto vres = make_rsrc(static_cast<const char *>(A.ring_v) + hring * P * ES, (uint32_t)(L * P * ES));
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const int j = 16 * jb + 4 * lq + kk;
+            const int j = m.j0 + 4 * lq + kk;
             const uint32_t row = (uint32_t)slot(j < cold ? j : lastr) * P;
 #pragma unroll
             for (int pw = 0; pw < MX::PW; ++pw)
-                m.vw[jb][kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * ES, 0, 0);
+                m.vw[kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * ES, 0, 0);
         }
-    uint32_t vin[MX::PW];   // this step's v in the same pair layout (operand of entry cold)
 #pragma unroll
-    for (int pw = 0; pw < MX::PW; ++pw) vin[pw] = static_cast<const uint32_t *>(A.v)[(bh * P) / 2 + MX::vword(pw, lane)];
+        for (int pw = 0; pw < MX::PW; ++pw) vin[pw] = static_cast<const uint32_t *>(A.v)[(bh * P) / 2 + MX::vword(pw, lane)];
+    }
 
-    // 2. this step's token goes into ring slot (pos mod L) = entry cold, as
-    // soon as it has arrived (no ring value used above comes from that slot)
-    const int sn = slot(cold);
+    // Returns this wavefront's arrival: the old count of its group counter.
+    __device__ __forceinline__ int finish(const StepArgs &A, int lane, int b, int g, int h, size_t bh, int base,
+                                          int cold, bool fold, float (*s_r)[P], float *s_abar,
+                                          float (*s_U)[LM + 1], float (*s_K)[N], float (*s_sw)[LM]) {
+        const int L = A.L, count = cold + 1;
+        const size_t gring = ((size_t)b * A.G + g) * L;
+        const size_t hring = bh * L;
+        const int lr = lane & 15, lq = lane >> 4;
+        int prev = -1;
+        if (m.j0 == 0) {
+            // this step's token goes into ring slot (pos mod L) = entry cold, as
+            // soon as it has arrived (no ring value used here comes from that slot)
+            const int sn = ring_slot(base % L, cold, L);
 #pragma unroll
-    for (int rr = 0; rr < VR; ++rr) {
-        const int p = lane + 64 * rr;
-        if (p < P) static_cast<uint16_t *>(A.ring_v)[(hring + sn) * P + p] = (uint16_t)vnew[rr].r;
-    }
-    if (lane == 0) {
-        A.ring_dt[hring + sn] = dt_in;
-        A.ring_a[hring + sn] = a_in;
-    }
-    if (group_writer) {
-        const size_t off = (gring + sn) * N * ES;
-        qrow.store(static_cast<char *>(A.ring_q) + off, lane);
-        krow.store(static_cast<char *>(A.ring_k) + off, lane);
-    }
-    // Arrival of this workgroup (its pointer read is done: the loads above
-    // depend on it).  Its result is needed only at the very end.
-    int prev = -1;
-    if (lane == 0) prev = atomicAdd(&A.sync[((size_t)b * (A.G + 1) + g) * kSyncStride], 1);
+            for (int rr = 0; rr < VR; ++rr) {
+                const int p = lane + 64 * rr;
+                if (p < P) static_cast<uint16_t *>(A.ring_v)[(hring + sn) * P + p] = (uint16_t)vnew[rr].r;
+            }
+            if (lane == 0) {
+                A.ring_dt[hring + sn] = dt_in;
+                A.ring_a[hring + sn] = a_in;
+            }
+            if ((h % (A.H / A.G)) == 0) {
+                const size_t off = (gring + sn) * N * ES;
+                qrow.store(static_cast<char *>(A.ring_q) + off, lane);
+                krow.store(static_cast<char *>(A.ring_k) + off, lane);
+            }
+        }
+        // Arrival of this ring wavefront (every ring wavefront arrives after
+        // its own pointer read, which the loads above depend on).  Its result
+        // is needed only at the very end.
+        if (lane == 0) prev = atomicAdd(&A.sync[((size_t)b * (A.G + 1) + g) * kSyncStride], 1);
 
-    // 3. entry cold and past it: this step's token (the query, the B operand
-    // of every column, gathered from the row's words)
+        // entry cold and past it: this step's token (the query, the B operand
+        // of every column, gathered from the row's words)
 #pragma unroll
-    for (int kb = 0; kb < MX::KB; ++kb) {
-        const int w0 = MX::col(kb, lane) / 2;
-        m.qb[kb] = uint4{(uint32_t)__shfl((int)qrow.w[0], w0), (uint32_t)__shfl((int)qrow.w[0], w0 + 1),
-                         (uint32_t)__shfl((int)qrow.w[0], w0 + 2), (uint32_t)__shfl((int)qrow.w[0], w0 + 3)};
-    }
-    m.aj = lane < cold ? a_r : (lane == cold ? a_in : 1.f);
-    m.dtj = lane < cold ? dt_r : (lane == cold ? dt_in : 0.f);
-#pragma unroll
-    for (int jb = 0; jb < MX::JB; ++jb)
+        for (int kb = 0; kb < MX::KB; ++kb) {
+            const int w0 = MX::col(kb, lane) / 2;
+            m.qb[kb] = uint4{(uint32_t)__shfl((int)qrow.w[0], w0), (uint32_t)__shfl((int)qrow.w[0], w0 + 1),
+                             (uint32_t)__shfl((int)qrow.w[0], w0 + 2), (uint32_t)__shfl((int)qrow.w[0], w0 + 3)};
+        }
+        m.aj = lane < cold ? a_r : (lane == cold ? a_in : 1.f);
+        m.dtj = lane < cold ? dt_r : (lane == cold ? dt_in : 0.f);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
             for (int pw = 0; pw < MX::PW; ++pw)
-                if (16 * jb + 4 * lq + kk >= cold) m.vw[jb][kk][pw] = vin[pw];
+                if (m.j0 + 4 * lq + kk >= cold) m.vw[kk][pw] = vin[pw];
 
-    if (!fold) {
-        f32x4 dk[MX::JB];
-        m.dots(lane, dk);
-        m.weights(lane, count, s_abar, s_sw);
-        m.term(lane, dk, reinterpret_cast<float (*)[P]>(s_r), s_sw);
-    } else {
-        // state-and-output route: stage U[p][j] = s_j v_j[p] and K[j][n] = k_j[n]
-        m.weights(lane, count, s_abar, s_sw);
-#pragma unroll
-        for (int jb = 0; jb < MX::JB; ++jb)
+        if (!fold) {
+            const f32x4 dk = m.dots(lane);
+            m.weights(lane, count, s_abar, s_sw);
+            m.term(lane, dk, s_r, s_sw);
+        } else {
+            // state-and-output route: stage U[p][j] = s_j v_j[p] and K[j][n] = k_j[n]
+            // for this wavefront's entries
+            m.weights(lane, count, s_abar, s_sw);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const int j = 16 * jb + 4 * lq + kk;
+                const int j = m.j0 + 4 * lq + kk;
                 if (j < count) {
                     const float sj = s_sw[0][j];
 #pragma unroll
@@ -333,20 +342,18 @@ __device__ __forceinline__ int step_ring_wave_mx(const StepArgs &A, int lane, in
 #pragma unroll
                         for (int half = 0; half < 2; ++half) {
                             const int p = 32 * pw + 2 * lr + half;
-                            if (p < P) s_U[p][j] = sj * MX::vval(m.vw[jb][kk][pw], half);
+                            if (p < P) s_U[p][j] = sj * MX::vval(m.vw[kk][pw], half);
                         }
                 }
             }
-#pragma unroll
-        for (int jb = 0; jb < MX::JB; ++jb) {
-            const int j = 16 * jb + lr;
+            const int j = m.j0 + lr;
             if (j < count) {
 #pragma unroll
                 for (int kb = 0; kb < MX::KB; ++kb) {
                     const int c = 32 * kb + 8 * lq;
                     if (c < N) {
                         IoVec<true, 8> kv;
-                        kv.r = m.ka[jb][kb];
+                        kv.r = m.ka[kb];
                         float kk8[8];
                         kv.widen(kk8);
 #pragma unroll
@@ -355,9 +362,9 @@ __device__ __forceinline__ int step_ring_wave_mx(const StepArgs &A, int lane, in
                 }
             }
         }
+        return prev;
     }
-    return prev;
-}
+};
 
 // Waves per SIMD to ask the register allocator for: 8 (the hardware maximum,
 // 64 registers a lane) where the kernel fits without spilling to scratch,
@@ -367,14 +374,20 @@ constexpr int step_waves() {
     return (P * N <= 64 * 64 || (N == 128 && LM == 16 && IOB)) && !(LM == 32 && P * N > 16 * 16) ? 8 : 1;
 }
 
+// Ring wavefronts of the fused step: two for a 32-entry ring with bf16 io
+// (one per 16-entry block), else one.
+template <int LM, bool IOB>
+constexpr int step_ring_waves() { return IOB ? LM / 16 : 1; }
+
 template <int P, int N, int LM, bool IOB>
-__global__ __launch_bounds__((StepShape<P, N>::NT))
+__global__ __launch_bounds__((StepShape<P, N>::NTS + 64 * step_ring_waves<LM, IOB>()))
 __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kernel(StepArgs args) {
     using Sh = StepShape<P, N>;
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+    constexpr int NR = step_ring_waves<LM, IOB>();
     using RR = RowReduce<ITER, LPR>;
 
-    __shared__ float s_r[P];
+    __shared__ float s_r[NR][P];
     __shared__ float s_abar;
     __shared__ int s_count;
     __shared__ float s_U[P][LM + 1];
@@ -387,29 +400,32 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
     const int g = (h * args.G) / H;
     const int tid = threadIdx.x, lane = tid & 63;
     // the role of this wavefront, as a wave-uniform value: the branches on it
-    // are scalar, so the ring wavefront's pointer reads go through the scalar
+    // are scalar, so the ring wavefronts' pointer reads go through the scalar
     // cache instead of queueing behind the tile loads of every wavefront on
     // the CU
-    const bool streamer = __builtin_amdgcn_readfirstlane(tid >> 6) < NTS / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool streamer = wave < NTS / 64;
+    const int rw = wave - NTS / 64;   // ring wavefront index
     const size_t bh = (size_t)b * H + h;
     const size_t tile = bh * (size_t)(P * N);
 
-    // Only the ring wavefront reads the pointer.  It announces this
-    // workgroup's arrival once its ring loads are issued, so the atomic's
-    // latency overlaps the rest of the work; the streaming wavefronts learn the route
-    // (output-only, fold, or a per-sequence error) from LDS after the barrier.
-    // Each role loads only what it uses inside its own branch, so the tile's
-    // registers are never live across the ring wavefront's code.
+    // Only the ring wavefronts read the pointer.  Each announces its arrival
+    // once its ring loads are issued (the group's counter expects NR arrivals
+    // per head), so the atomic's latency overlaps the rest of the work; the
+    // streaming wavefronts learn the route (output-only, fold, or a
+    // per-sequence error) from LDS after the barrier.  Each role loads only what it uses
+    // inside its own branch, so the tile's registers are never live across
+    // the ring wavefronts' code.
     __shared__ int s_route;   // 0 output-only, 1 fold, 2 error (sequence left unchanged)
     const int col0 = (tid % LPR) * VEC;
     Chunk<ST_F32, VEC> ch[ITER];
+    IoVec<IOB, 4> qraw;
     float qv[VEC];
     float part[ITER][1];
     int pos = 0, prev = -1, route = 0;
     if (streamer) {
 #pragma unroll
         for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
-        IoVec<IOB, 4> qraw;
         qraw.load(args.q, ((size_t)b * args.G + g) * N + col0);
         qraw.widen(qv);
         // S0 q partials (used by the output-only route; cheap beside the loads)
@@ -430,18 +446,21 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
         const bool bad = cold + 1 > L || pos == 2147483647;
         const int need = args.flush_at > 1 ? args.flush_at : 1;
         route = bad ? 2 : (cold + 1 >= need ? 1 : 0);
-        if (lane == 0) {
+        if (rw == 0 && lane == 0) {
             s_route = route;
             s_count = cold + 1;
             if (bad) raise_seq_error(args.err, b, cold + 1 > L ? REPLAY_SEQERR_RING_OVERFLOW : REPLAY_SEQERR_POS_OVERFLOW);
         }
         if (!bad) {
-            if constexpr (IOB)
-                prev = step_ring_wave_mx<P, N, LM>(args, lane, b, g, h, bh, base, cold, route == 1, s_r, &s_abar,
-                                                   s_U, s_K, reinterpret_cast<float (*)[LM]>(&s_sw[0][0]));
-            else
-                prev = step_ring_wave<P, N, LM, IOB>(args, lane, b, g, h, bh, base, cold, route == 1, s_r, &s_abar,
-                                                     s_U, s_K);
+            if constexpr (IOB) {
+                StepRingMx<P, N, LM> sr;
+                sr.load(args, lane, rw, b, g, h, bh, base, cold);
+                prev = sr.finish(args, lane, b, g, h, bh, base, cold, route == 1, &s_r[rw], &s_abar, s_U, s_K,
+                                 reinterpret_cast<float (*)[LM]>(&s_sw[0][0]));
+            } else {
+                prev = step_ring_wave<P, N, LM, IOB>(args, lane, b, g, h, bh, base, cold, route == 1, s_r[0],
+                                                     &s_abar, s_U, s_K);
+            }
         }
     }
     // LDS-only barrier: the ring wavefront's write-back of the new token and
@@ -490,14 +509,16 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
 #pragma unroll
             for (int e = 0; e < RR::FINAL; ++e) {
                 const int row = (e + RR::FINAL * hi) * RPI + tid / LPR;
-                args.y[bh * P + row] = route == 1 ? part[e][0] : abar * part[e][0] + s_r[row];
+                float rt = s_r[0][row];
+                if constexpr (NR == 2) rt += s_r[1][row];   // block 0 + block 1
+                args.y[bh * P + row] = route == 1 ? part[e][0] : abar * part[e][0] + rt;
             }
         }
-    } else if (lane == 0 && prev == H / args.G - 1) {
-        // Last head of its group to arrive: the group arrives at the
-        // sequence's counter.  The last group to arrive means every workgroup
-        // of the sequence has read the pointer (each arrived after its read),
-        // so the pointer moves.
+    } else if (lane == 0 && prev == NR * (H / args.G) - 1) {
+        // Last ring wavefront of its group to arrive: the group arrives at
+        // the sequence's counter.  The last group to arrive means every ring
+        // wavefront of the sequence has read the pointer (each arrived after
+        // its read), so the pointer moves.
         int32_t *seq = args.sync + (size_t)b * (args.G + 1) * kSyncStride;
         atomicExch(seq + (size_t)g * kSyncStride, 0);
         if (atomicAdd(seq + (size_t)args.G * kSyncStride, 1) == args.G - 1) {
@@ -512,9 +533,9 @@ template <int P, int N, int LM>
 static hipError_t launch_lm(const StepArgs &a, hipStream_t s) {
     const unsigned blocks = (unsigned)((size_t)a.B * a.H);
     if (a.io_bf16)
-        step_kernel<P, N, LM, true><<<blocks, StepShape<P, N>::NT, 0, s>>>(a);
+        step_kernel<P, N, LM, true><<<blocks, StepShape<P, N>::NTS + 64 * step_ring_waves<LM, true>(), 0, s>>>(a);
     else
-        step_kernel<P, N, LM, false><<<blocks, StepShape<P, N>::NT, 0, s>>>(a);
+        step_kernel<P, N, LM, false><<<blocks, StepShape<P, N>::NTS + 64 * step_ring_waves<LM, false>(), 0, s>>>(a);
     return hipGetLastError();
 }
 
