@@ -108,11 +108,11 @@ typedef struct {
     int32_t *pos;       /* [B] tokens appended and not rolled back */
     int32_t *base;      /* [B] pos at the last flush; count = pos - base */
     int32_t *err;       /* [B + 1] error bits: err[0] = OR over sequences, err[1 + b] per sequence */
-    int32_t *sync;      /* [B][G + 1][32] arrival counters of replay_step, one per
-                           128-byte line (element [b][g][0] per group, [b][G][0] per
-                           sequence; the rest is padding so that no two counters share a
-                           line); zeroed by replay_init and zero again whenever no call
-                           is in flight */
+    int32_t *sync;      /* [B][G + 1][32] arrival counters of replay_step,
+                           replay_append and the flush, one per 128-byte line (element [b][g][0] per
+                           group, [b][G][0] per sequence; the rest is padding so that no
+                           two counters share a line); zeroed by replay_init and zero
+                           again whenever no call is in flight */
 } replay_buffers;
 
 typedef struct replay_handle replay_handle;

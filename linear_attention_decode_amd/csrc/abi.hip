@@ -106,6 +106,8 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
     a.r = ring_view(h);
     a.min_count = min_count;
     a.force_empty = load_src != nullptr;
+    a.base_out = h->bufs.base;
+    a.sync = h->bufs.sync;
     a.S_out = c.shared_lowp ? nullptr : h->bufs.s_master;
     a.copy_out = c.read_copy == REPLAY_NONE ? nullptr : h->bufs.s_copy;
     a.scale_out = c.read_copy == REPLAY_FP8_E4M3 ? h->bufs.s_scale : nullptr;
@@ -124,9 +126,7 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
         st_in = ST_F32;
     }
     const int st_copy = c.read_copy == REPLAY_NONE ? -1 : state_kind(c.read_copy);
-    hipError_t e = launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s);
-    if (e != hipSuccess) return REPLAY_ERR_HIP;
-    return from_hip(launch_commit(a.r, h->bufs.base, min_count, a.force_empty, s));
+    return from_hip(launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s));
 }
 
 replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
@@ -229,8 +229,8 @@ replay_status replay_append(replay_handle *h, int32_t W, const void *q, const vo
     if (W < 1 || W > h->cfg.ring_len) return REPLAY_ERR_INVALID_ARG;
     const RingView r = ring_view(h);
     return from_hip(launch_append(h->cfg.head_dim, h->cfg.state_dim, r, h->bufs.ring_q, h->bufs.ring_k,
-                                  h->bufs.ring_v, h->bufs.ring_dt, h->bufs.ring_a, h->bufs.pos, W, q, k, v,
-                                  dt, a, as_stream(stream)));
+                                  h->bufs.ring_v, h->bufs.ring_dt, h->bufs.ring_a, h->bufs.pos, h->bufs.sync, W,
+                                  q, k, v, dt, a, as_stream(stream)));
 }
 
 replay_status replay_decode(replay_handle *h, float *y, void *stream) {

@@ -64,6 +64,10 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
         const int need = args.min_count > 1 ? args.min_count : 1;
         if (count < need) return;  // uniform: nothing to fold for this sequence
     }
+    // Arrival of this workgroup at its group's counter (after its pointer
+    // read); the last arrival of the sequence moves base at the very end.
+    int prev = -1;
+    if (tid == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
 
     // 1. tile loads, then every ring load in one batch
     Chunk<SIN, VEC> ch[ITER];
@@ -206,16 +210,17 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
         }
         if (tid == 0) args.scale_out[bh] = sig;
     }
-}
 
-// base = pos for the sequences the flush kernel folded
-__global__ void commit_kernel(const int32_t *pos, int32_t *base, int32_t B, int32_t min_count,
-                              int32_t force_empty) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= B) return;
-    const int p = pos[b];
-    const int need = min_count > 1 ? min_count : 1;
-    if (force_empty || p - base[b] >= need) base[b] = p;
+    // Last head of its group: the group arrives at the sequence's counter;
+    // the last group means every workgroup of the sequence has read base.
+    if (tid == 0 && prev == r.H / r.G - 1) {
+        int32_t *seq = args.sync + (size_t)b * (r.G + 1) * kSyncStride;
+        atomicExch(seq + (size_t)g * kSyncStride, 0);
+        if (atomicAdd(seq + (size_t)r.G * kSyncStride, 1) == r.G - 1) {
+            atomicExch(seq + (size_t)r.G * kSyncStride, 0);
+            args.base_out[b] = pos;
+        }
+    }
 }
 
 template <int P, int N, int SIN, int COPY, bool WM>
@@ -255,13 +260,6 @@ hipError_t launch_flush(int P, int N, int st_in, int st_copy, bool write_master,
     if (P == 64 && N == 128) return launch_pn<64, 128>(st_in, st_copy, write_master, a, s);
     if (P == 128 && N == 128) return launch_pn<128, 128>(st_in, st_copy, write_master, a, s);
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_commit(const RingView &r, int32_t *base, int32_t min_count, int32_t force_empty,
-                         hipStream_t s) {
-    const int nt = 256;
-    commit_kernel<<<(r.B + nt - 1) / nt, nt, 0, s>>>(r.pos, base, r.B, min_count, force_empty);
-    return hipGetLastError();
 }
 
 }  // namespace replay

@@ -52,6 +52,8 @@ struct FlushArgs {
     float *scale_out;       // per-head scale to write (e4m3 copy), or nullptr
     int32_t min_count;      // flush sequences with count >= max(min_count, 1)
     int32_t force_empty;    // 1: treat every sequence as due with an empty ring (checkpoint load)
+    int32_t *base_out;      // base, set to pos by the last workgroup of a folded sequence
+    int32_t *sync;          // arrival counters [B][G + 1][kSyncStride]
 };
 
 // One fused standard decode step (float32 checkpoint).
@@ -82,10 +84,8 @@ struct EagerArgs {
 hipError_t launch_decode(int P, int N, int st, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_flush(int P, int N, int st_in, int st_copy, bool write_master, const FlushArgs &a,
                         hipStream_t s);
-hipError_t launch_commit(const RingView &r, int32_t *base, int32_t min_count, int32_t force_empty,
-                         hipStream_t s);
 hipError_t launch_append(int P, int N, const RingView &r, void *ring_q, void *ring_k, void *ring_v,
-                         float *ring_dt, float *ring_a, int32_t *pos, int32_t W, const void *q,
+                         float *ring_dt, float *ring_a, int32_t *pos, int32_t *sync, int32_t W, const void *q,
                          const void *k, const void *v, const float *dt, const float *a, hipStream_t s);
 hipError_t launch_rollback(const RingView &r, int32_t *pos, const int32_t *n_reject, hipStream_t s);
 hipError_t launch_fill_u32(void *dst, uint32_t value, size_t count, hipStream_t s);

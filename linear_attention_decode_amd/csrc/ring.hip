@@ -12,68 +12,85 @@
 
 namespace replay {
 
-// One workgroup per sequence: copies the sequence's W tokens into its ring
-// and then advances its pointer; no other workgroup touches that pointer.
+// kAppendSlices workgroups per sequence, each copying the tokens of its
+// share of the heads (v, dt, a) and of the groups (q, k); the last slice to
+// arrive at the sequence's counter advances the pointer (every slice arrives
+// after reading it, so none reads a moved pointer).
+constexpr int kAppendSlices = 8;
+
 __global__ __launch_bounds__(256) void append_kernel(RingView r, void *ring_q, void *ring_k,
                                                      void *ring_v, float *ring_dt, float *ring_a,
-                                                     int32_t *pos, int32_t W, const void *q,
+                                                     int32_t *pos, int32_t *sync, int32_t W, const void *q,
                                                      const void *k, const void *v, const float *dt,
                                                      const float *a, int32_t P, int32_t N) {
-    const int b = blockIdx.x;
+    const int b = blockIdx.x, sl = blockIdx.y;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int H = r.H, G = r.G, L = r.L;
     const int p0 = pos[b];
     const int count = p0 - r.base[b];
     if (count + W > L) {
-        if (tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_RING_OVERFLOW);
+        if (sl == 0 && tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_RING_OVERFLOW);
         return;
     }
     if ((long long)p0 + W > 2147483647LL) {
-        if (tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_POS_OVERFLOW);
+        if (sl == 0 && tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_POS_OVERFLOW);
         return;
     }
     const int esz = r.io_bf16 ? 2 : 4;
+    const int h0 = sl * H / kAppendSlices, h1 = (sl + 1) * H / kAppendSlices;
+    const int g0 = sl * G / kAppendSlices, g1 = (sl + 1) * G / kAppendSlices;
 
-    // v rows: [B][W][H][P] -> [B][H][L][P]; 16-byte pieces
+    // v rows of heads h0..h1-1: [B][W][H][P] -> [B][H][L][P]; 16-byte pieces
     {
         const int vec_per_row = P * esz / 16;
-        const int total = W * H * vec_per_row;
+        const int nh = h1 - h0;
+        const int total = W * nh * vec_per_row;
         const uint4 *src = reinterpret_cast<const uint4 *>(static_cast<const char *>(v) + (size_t)b * W * H * P * esz);
         for (int i = tid; i < total; i += nt) {
             const int row = i / vec_per_row, c = i % vec_per_row;
-            const int t = row / H, h = row % H;
-            const int sl = (p0 + t) % L;
+            const int t = row / nh, h = h0 + row % nh;
+            const int slot = (p0 + t) % L;
             uint4 *dst = reinterpret_cast<uint4 *>(static_cast<char *>(ring_v) +
-                                                   (((size_t)b * H + h) * L + sl) * P * esz);
-            dst[c] = src[(size_t)row * vec_per_row + c];
+                                                   (((size_t)b * H + h) * L + slot) * P * esz);
+            dst[c] = src[((size_t)t * H + h) * vec_per_row + c];
         }
     }
-    // q, k rows: [B][W][G][N] -> [B][G][L][N]
+    // q, k rows of groups g0..g1-1: [B][W][G][N] -> [B][G][L][N]
     {
         const int vec_per_row = N * esz / 16;
-        const int total = W * G * vec_per_row;
+        const int ng = g1 - g0;
+        const int total = W * ng * vec_per_row;
         const size_t in_off = (size_t)b * W * G * N * esz;
         const uint4 *sq = reinterpret_cast<const uint4 *>(static_cast<const char *>(q) + in_off);
         const uint4 *sk = reinterpret_cast<const uint4 *>(static_cast<const char *>(k) + in_off);
         for (int i = tid; i < total; i += nt) {
             const int row = i / vec_per_row, c = i % vec_per_row;
-            const int t = row / G, gg = row % G;
-            const int sl = (p0 + t) % L;
-            const size_t out_off = (((size_t)b * G + gg) * L + sl) * N * esz;
-            reinterpret_cast<uint4 *>(static_cast<char *>(ring_q) + out_off)[c] = sq[(size_t)row * vec_per_row + c];
-            reinterpret_cast<uint4 *>(static_cast<char *>(ring_k) + out_off)[c] = sk[(size_t)row * vec_per_row + c];
+            const int t = row / ng, gg = g0 + row % ng;
+            const int slot = (p0 + t) % L;
+            const size_t out_off = (((size_t)b * G + gg) * L + slot) * N * esz;
+            const size_t in_row = ((size_t)t * G + gg) * vec_per_row + c;
+            reinterpret_cast<uint4 *>(static_cast<char *>(ring_q) + out_off)[c] = sq[in_row];
+            reinterpret_cast<uint4 *>(static_cast<char *>(ring_k) + out_off)[c] = sk[in_row];
         }
     }
-    // dt, a: [B][W][H] -> [B][H][L]
-    for (int i = tid; i < W * H; i += nt) {
-        const int t = i / H, h = i % H;
-        const int sl = (p0 + t) % L;
-        const size_t o = ((size_t)b * H + h) * L + sl;
-        ring_dt[o] = dt[(size_t)b * W * H + i];
-        ring_a[o] = a[(size_t)b * W * H + i];
+    // dt, a of heads h0..h1-1: [B][W][H] -> [B][H][L]
+    {
+        const int nh = h1 - h0;
+        for (int i = tid; i < W * nh; i += nt) {
+            const int t = i / nh, h = h0 + i % nh;
+            const int slot = (p0 + t) % L;
+            const size_t o = ((size_t)b * H + h) * L + slot;
+            ring_dt[o] = dt[((size_t)b * W + t) * H + h];
+            ring_a[o] = a[((size_t)b * W + t) * H + h];
+        }
     }
-    __syncthreads();
-    if (tid == 0) pos[b] = p0 + W;
+    if (tid == 0) {
+        int32_t *cnt = sync + ((size_t)b * (G + 1) + G) * kSyncStride;
+        if (atomicAdd(cnt, 1) == kAppendSlices - 1) {
+            atomicExch(cnt, 0);
+            pos[b] = p0 + W;
+        }
+    }
 }
 
 __global__ void rollback_kernel(const int32_t *base, int32_t *pos, const int32_t *n_reject,
@@ -109,10 +126,10 @@ __global__ void eager_select_kernel(const float *snaps, int32_t W, const int32_t
 }
 
 hipError_t launch_append(int P, int N, const RingView &r, void *ring_q, void *ring_k, void *ring_v,
-                         float *ring_dt, float *ring_a, int32_t *pos, int32_t W, const void *q,
+                         float *ring_dt, float *ring_a, int32_t *pos, int32_t *sync, int32_t W, const void *q,
                          const void *k, const void *v, const float *dt, const float *a, hipStream_t s) {
-    append_kernel<<<r.B, 256, 0, s>>>(r, ring_q, ring_k, ring_v, ring_dt, ring_a, pos, W, q, k, v, dt,
-                                      a, P, N);
+    append_kernel<<<dim3(r.B, kAppendSlices), 256, 0, s>>>(r, ring_q, ring_k, ring_v, ring_dt, ring_a, pos, sync,
+                                                           W, q, k, v, dt, a, P, N);
     return hipGetLastError();
 }
 
