@@ -143,3 +143,81 @@ def test_step_overflow_leaves_sequence_unchanged():
     tok, _, _ = gu.errors(torch.cat([y[:4], y[5:6]]).cpu().numpy(), y_ref)
     assert tok <= 1e-4
     layer.close()
+
+
+def test_flush_schedule_invariance():
+    """The outputs do not depend on when the ring is folded: the same token
+    stream through the fused step with flush_at = 1 (fold every step), 3 and
+    L = 8 (fold when full), and through the separate calls flushing at L,
+    agree with each other to float32 rounding and with the oracle (1e-4)."""
+    w = synth.Workload(batch=4, heads=8, groups=2, head_dim=64, state_dim=128, ring_len=8, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=240)
+    T = 30
+    gu.note("flush schedule invariance")
+    dev = gu.DevInputs(w, 0, T)
+    outs = {}
+    for flush_at in (1, 3, 8):
+        layer = _layer(w)
+        outs[flush_at] = _run_step(layer, w, dev, T, flush_at).cpu().numpy()
+        torch.cuda.synchronize()
+        assert layer.get_error()[0] == 0
+        layer.close()
+    layer = _layer(w)
+    y = torch.empty((T, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
+    for t in range(T):
+        layer.append(1, *dev.step(t))
+        layer.decode(y[t])
+        layer.flush(w.ring_len)
+    torch.cuda.synchronize()
+    outs["calls"] = y.cpu().numpy()
+    layer.close()
+    x = gu.oracle_inputs(w, 0, T, list(range(w.batch)))
+    y_ref = runs.standard(x, np.zeros((w.batch, w.heads, w.head_dim, w.state_dim)))
+    for k, yk in outs.items():
+        tok, _, _ = gu.errors(yk, y_ref)
+        print(f"  schedule {k}: per-token max vs oracle {tok:.3e}")
+        assert tok <= 1e-4
+        e = runs.normwise_rel_err(yk, outs[8].astype(np.float64))
+        assert float(np.max(e)) <= 1e-5, k
+
+
+def test_step_ignores_nan_in_unused_slots():
+    """Every ring slot starts as NaN, and after each step every slot outside
+    the live range is poisoned again; the fused step's outputs and final
+    checkpoint stay bit-identical to the clean run (it never reads a slot it
+    must not)."""
+    w = synth.Workload(batch=5, heads=8, groups=4, head_dim=64, state_dim=128, ring_len=6, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=241)
+    T = 20
+    gu.note("step nan poison")
+    dev = gu.DevInputs(w, 0, T)
+
+    def run(poison):
+        layer = _layer(w)
+        model = oring.RingModel(w.batch, w.ring_len)
+        if poison:
+            for name in ("ring_q", "ring_k", "ring_v", "ring_dt", "ring_a"):
+                layer.t[name].fill_(float("nan"))
+        y = torch.empty((T, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
+        for t in range(T):
+            layer.step(*dev.step(t), y[t], flush_at=4)
+            model.append(1)
+            model.flush(4)
+            if poison:
+                torch.cuda.synchronize()
+                for b in range(w.batch):
+                    live = set(model.live_slots(b))
+                    for s in range(w.ring_len):
+                        if s not in live:
+                            for name in ("ring_v", "ring_dt", "ring_a", "ring_q", "ring_k"):
+                                layer.t[name][b, :, s] = float("nan")
+        torch.cuda.synchronize()
+        assert layer.get_error()[0] == 0
+        out = y.cpu().numpy(), layer.s_master.cpu().numpy()
+        layer.close()
+        return out
+
+    y0, s0 = run(False)
+    y1, s1 = run(True)
+    assert np.isfinite(y0).all() and np.isfinite(s0).all()
+    assert np.array_equal(y0, y1) and np.array_equal(s0, s1)
