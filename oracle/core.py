@@ -53,6 +53,10 @@ def lib():
             L.oracle_e4m3_encode_n.argtypes = [_F32P, _U8P, _I64]
             L.oracle_e4m3_decode_n.argtypes = [_U8P, _F32P, _I64]
             L.oracle_quant_heads_e4m3.argtypes = [_F32P, _I64, _I64, _U8P, _F32P]
+            L.oracle_e2m1_decode_n.argtypes = [_U8P, _F32P, _I64]
+            L.oracle_e2m1_encode_n.argtypes = [_F64P, _U8P, _I64]
+            L.oracle_quant_blocks_mxfp4.argtypes = [_F32P, _I64, _U8P, _U8P]
+            L.oracle_dequant_blocks_mxfp4.argtypes = [_U8P, _U8P, _I64, _F32P]
             _LIB = L
     return _LIB
 
@@ -103,6 +107,45 @@ def quant_heads_e4m3(x: np.ndarray):
     scale = np.empty(lead, dtype=np.float32)
     lib().oracle_quant_heads_e4m3(_p(x, _F32P), heads, n, _p(codes, _U8P), _p(scale, _F32P))
     return codes, scale
+
+
+def e2m1_decode(c: np.ndarray) -> np.ndarray:
+    """4-bit codes (low nibble of each byte) -> float32 values."""
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    out = np.empty(c.shape, dtype=np.float32)
+    lib().oracle_e2m1_decode_n(_p(c, _U8P), _p(out, _F32P), c.size)
+    return out
+
+
+def e2m1_encode(x: np.ndarray) -> np.ndarray:
+    """float64 values -> 4-bit codes (nearest, ties to even, saturating)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().oracle_e2m1_encode_n(_p(x, _F64P), _p(out, _U8P), x.size)
+    return out
+
+
+def quant_blocks_mxfp4(x: np.ndarray):
+    """x: float32 [..., P, N] (P*N a multiple of 32) -> (packed codes uint8
+    [..., P*N/2], E8M0 scales uint8 [..., P*N/32]); blocks of 32 consecutive
+    values of each head's row-major tile."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    lead = x.shape[:-2]
+    n = x.shape[-1] * x.shape[-2]
+    assert n % 32 == 0
+    nblk = x.size // 32
+    packed = np.empty(lead + (n // 2,), dtype=np.uint8)
+    scale = np.empty(lead + (n // 32,), dtype=np.uint8)
+    lib().oracle_quant_blocks_mxfp4(_p(x, _F32P), nblk, _p(packed, _U8P), _p(scale, _U8P))
+    return packed, scale
+
+
+def dequant_blocks_mxfp4(packed: np.ndarray, scale: np.ndarray, shape) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint8)
+    out = np.empty(shape, dtype=np.float32)
+    lib().oracle_dequant_blocks_mxfp4(_p(packed, _U8P), _p(scale, _U8P), scale.size, _p(out, _F32P))
+    return out
 
 
 def widen(arr: np.ndarray, io_dtype: str) -> np.ndarray:

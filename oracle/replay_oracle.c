@@ -30,6 +30,15 @@
  *              nearest, ties to even, saturating to +-448.
  *   per-head : sigma = amax|x| / 448 in float32 (1 when amax is 0), and
  *              code = e4m3(x / sigma) with a correctly rounded float32 divide.
+ *   e2m1     : the OCP 4-bit float E2M1 (bias 1, 1 mantissa bit, no
+ *              infinities or NaN, largest 6); round to nearest, ties to even,
+ *              saturating to +-6.
+ *   MX blocks: 32 consecutive values of a head's row-major tile share a
+ *              power-of-two scale X = 2^(floor(log2 amax) - 2) (2 = exponent
+ *              of E2M1's largest value; X = 2^-127 when amax is 0, exponent
+ *              clamped to -127..127), stored as its biased exponent byte
+ *              (E8M0); code = e2m1(x / X), exact division.  Two codes per
+ *              byte, the first in the low nibble.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
@@ -206,5 +215,90 @@ void oracle_quant_heads_e4m3(const float *x, int64_t heads, int64_t n,
         const float s = (amax > 0.0f) ? amax / 448.0f : 1.0f;
         scale[i] = s;
         for (int64_t j = 0; j < n; ++j) codes[i * n + j] = oracle_e4m3_encode(xi[j] / s);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* OCP E2M1 (FP4) and MX block scaling                                       */
+/* ------------------------------------------------------------------------ */
+
+/* code (low 4 bits) -> value, from the format: sign, exponent e (2 bits,
+   bias 1), mantissa m (1 bit); e == 0 is subnormal: m/2. */
+float oracle_e2m1_decode(uint8_t c)
+{
+    const int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+    const double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return (float)(s ? -mag : mag);
+}
+
+/* value -> code: nearest of the eight magnitudes, ties to the even code,
+   magnitudes above 6 saturate to 6.  The comparison is exact (double). */
+uint8_t oracle_e2m1_encode(double x)
+{
+    const uint8_t sign = signbit(x) ? 0x8 : 0x0;
+    const double ax = fabs(x);
+    if (!(ax < 6.0)) return (uint8_t)(sign | 7);   /* saturate (NaN too) */
+    int lo = 0;
+    while (lo < 7 && (double)oracle_e2m1_decode((uint8_t)(lo + 1)) <= ax) ++lo;
+    const double vl = oracle_e2m1_decode((uint8_t)lo), vh = oracle_e2m1_decode((uint8_t)(lo + 1));
+    int c;
+    if (ax - vl < vh - ax) c = lo;
+    else if (vh - ax < ax - vl) c = lo + 1;
+    else c = (lo & 1) ? lo + 1 : lo;
+    return (uint8_t)(sign | c);
+}
+
+void oracle_e2m1_decode_n(const uint8_t *c, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_decode(c[i]);
+}
+
+void oracle_e2m1_encode_n(const double *x, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_encode(x[i]);
+}
+
+/* MX FP4 quantisation of nblk blocks of 32 float32 values:
+   packed[16 * i + j] holds the codes of x[32 i + 2 j] (low nibble) and
+   x[32 i + 2 j + 1] (high nibble); scale[i] = biased exponent of X_i. */
+void oracle_quant_blocks_mxfp4(const float *x, int64_t nblk, uint8_t *packed, uint8_t *scale)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < nblk; ++i) {
+        const float *xi = x + 32 * i;
+        float amax = 0.0f;
+        for (int j = 0; j < 32; ++j) {
+            const float m = fabsf(xi[j]);
+            if (m > amax) amax = m;
+        }
+        int se = -127;
+        if (amax > 0.0f) {
+            int e;
+            (void)frexp((double)amax, &e);   /* amax = f 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+            se = (e - 1) - 2;
+            if (se < -127) se = -127;
+            if (se > 127) se = 127;
+        }
+        scale[i] = (uint8_t)(se + 127);
+        const double X = ldexp(1.0, se);
+        for (int j = 0; j < 16; ++j) {
+            const uint8_t c0 = oracle_e2m1_encode((double)xi[2 * j] / X);
+            const uint8_t c1 = oracle_e2m1_encode((double)xi[2 * j + 1] / X);
+            packed[16 * i + j] = (uint8_t)(c0 | (c1 << 4));
+        }
+    }
+}
+
+/* values of MX FP4 blocks: out[32 i + k] = e2m1(code) * 2^(scale[i] - 127) */
+void oracle_dequant_blocks_mxfp4(const uint8_t *packed, const uint8_t *scale, int64_t nblk, float *out)
+{
+    for (int64_t i = 0; i < nblk; ++i) {
+        const double X = ldexp(1.0, (int)scale[i] - 127);
+        for (int j = 0; j < 16; ++j) {
+            const uint8_t b = packed[16 * i + j];
+            out[32 * i + 2 * j] = (float)(oracle_e2m1_decode(b & 0xF) * X);
+            out[32 * i + 2 * j + 1] = (float)(oracle_e2m1_decode(b >> 4) * X);
+        }
     }
 }

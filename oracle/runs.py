@@ -92,6 +92,9 @@ def quant_dequant(S: np.ndarray, fmt: str) -> np.ndarray:
     if fmt == "fp8":
         codes, scale = core.quant_heads_e4m3(s32)
         return core.e4m3_decode(codes).astype(np.float64) * scale.astype(np.float64)[..., None, None]
+    if fmt == "fp4":
+        packed, scale = core.quant_blocks_mxfp4(s32)
+        return core.dequant_blocks_mxfp4(packed, scale, s32.shape).astype(np.float64)
     raise ValueError(fmt)
 
 

@@ -113,3 +113,81 @@ def test_quant_heads_scale_and_extremes():
     # dequantised values are within half a code step of the inputs
     deq = oracle.e4m3_decode(codes) * scale[..., None, None]
     assert np.all(np.abs(deq - x) <= np.abs(x) * 2.0 ** -4 + scale[..., None, None] * 2.0 ** -10)
+
+
+# ---- E2M1 (FP4) and MX block scaling -----------------------------------------
+# The OCP MX specification's table of E2M1 magnitudes (codes 0..7); codes
+# 8..15 are their negatives.  The oracle's decoder is built from the bit
+# fields, so this table pins it from outside.
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_is_the_published_table():
+    vals = oracle.core.e2m1_decode(np.arange(16, dtype=np.uint8))
+    assert vals[:8].tolist() == E2M1_TABLE
+    assert vals[8:].tolist() == [-v for v in E2M1_TABLE]
+    assert np.signbit(vals[8])
+
+
+def _nearest_even(x):
+    """Brute force: nearest table magnitude, ties to the even code, saturating."""
+    mags = np.array(E2M1_TABLE)
+    out = []
+    for v in x:
+        a = min(abs(v), 6.0)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        c = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+        out.append(c | (8 if np.signbit(v) else 0))
+    return np.array(out, dtype=np.uint8)
+
+
+def test_e2m1_encode_matches_brute_force():
+    rng = np.random.default_rng(11)
+    grid = np.arange(-800, 801) / 100.0                      # every 0.01 in [-8, 8], ties included
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -5.0])
+    x = np.concatenate([grid, mids, rng.uniform(-10, 10, 2000), [100.0, -1e30, 6.0000001, -0.0]])
+    assert np.array_equal(oracle.core.e2m1_encode(x), _nearest_even(x))
+
+
+def test_mx_block_scale_closed_forms():
+    rng = np.random.default_rng(12)
+    # a block whose largest magnitude lies in [4 * 2^k, 8 * 2^k) gets X = 2^k (E8M0 byte 127 + k)
+    for k in (-20, -3, 0, 1, 7, 30):
+        blk = rng.uniform(-1, 1, (1, 32)).astype(np.float32) * np.float32(2.0 ** k)
+        blk[0, 5] = np.float32(rng.uniform(4, 8) * 2.0 ** k)
+        blk = np.clip(blk, -blk[0, 5], blk[0, 5])
+        packed, scale = oracle.core.quant_blocks_mxfp4(blk)
+        assert scale.ravel().tolist() == [127 + k]
+        assert ((packed.ravel()[2] >> 4) & 0x7) in (6, 7)     # the largest element (index 5, high nibble of byte 2)
+    # exactly representable values come back exactly, packing order low nibble first
+    codes = rng.integers(0, 16, 32).astype(np.uint8)
+    codes[3] = 7                                              # amax = 6 X
+    X = 2.0 ** -5
+    blk = (oracle.core.e2m1_decode(codes).astype(np.float64) * X).astype(np.float32).reshape(1, 32)
+    packed, scale = oracle.core.quant_blocks_mxfp4(blk)
+    assert scale.ravel().tolist() == [127 - 5]
+    assert np.array_equal(packed.ravel() & 0xF, codes[0::2])
+    assert np.array_equal(packed.ravel() >> 4, codes[1::2])
+    back = oracle.core.dequant_blocks_mxfp4(packed, scale, blk.shape)
+    assert np.array_equal(np.abs(back), np.abs(blk))
+    # an all-zero block: scale 2^-127, all codes zero
+    packed, scale = oracle.core.quant_blocks_mxfp4(np.zeros((2, 16), np.float32))
+    assert scale.ravel().tolist() == [0] and not packed.any()
+
+
+def test_mx_block_error_bounds():
+    """Round to nearest: |deq - x| <= X/4 below X (spacing X/2) and <= X at
+    the top (spacing 2X between 4X and 6X); saturated values sit at 6X <= amax."""
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((64, 4, 32)) * np.exp(rng.uniform(-8, 8, (64, 1, 1)))).astype(np.float32)
+    packed, scale = oracle.core.quant_blocks_mxfp4(x)
+    back = oracle.core.dequant_blocks_mxfp4(packed, scale, x.shape).astype(np.float64)
+    X = np.exp2(scale.astype(np.float64) - 127).reshape(64, 4, 1)
+    xd = x.astype(np.float64)
+    err = np.abs(back - xd)
+    small = np.abs(xd) < X
+    assert np.all(err[small] <= X.repeat(32, -1)[small] / 4)
+    assert np.all(err <= np.maximum(X, np.abs(xd) - 6 * X) + 0 * err)
+    amax = np.abs(xd).max(-1, keepdims=True)
+    assert np.all((amax >= 4 * X) & (amax < 8 * X))
