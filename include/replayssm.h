@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define REPLAY_ABI_VERSION 3
+#define REPLAY_ABI_VERSION 4
 
 typedef enum {
     REPLAY_OK = 0,
@@ -74,7 +74,9 @@ typedef enum {
     REPLAY_NONE = -1,
     REPLAY_F32 = 0,
     REPLAY_BF16 = 1,
-    REPLAY_FP8_E4M3 = 2           /* OCP E4M3 (e4m3fn), largest finite 448 */
+    REPLAY_FP8_E4M3 = 2,          /* OCP E4M3 (e4m3fn), largest finite 448 */
+    REPLAY_FP4_E2M1 = 3           /* OCP MX FP4: E2M1 codes (largest 6), 32 consecutive values of a
+                                     head's row-major tile sharing one power-of-two scale (E8M0) */
 } replay_dtype;
 
 typedef struct {
@@ -86,20 +88,26 @@ typedef struct {
     int32_t ring_len;     /* L */
     int32_t io_dtype;     /* REPLAY_F32 or REPLAY_BF16: q, k, v inputs and their ring */
     int32_t read_copy;    /* REPLAY_NONE: outputs read the float32 master checkpoint;
-                             REPLAY_BF16 / REPLAY_FP8_E4M3: outputs read a low-precision
-                             copy, rewritten from the new checkpoint at every flush */
+                             REPLAY_BF16 / REPLAY_FP8_E4M3 / REPLAY_FP4_E2M1: outputs read
+                             a low-precision copy, rewritten from the new checkpoint at every
+                             flush (page "The SSM Layer Nobody Made Fast (Until Now):
+                             ReplaySSM Explained", key technical takeaways: FP8/FP4 copies
+                             serve the output reads) */
     int32_t shared_lowp;  /* 0: separated precisions (the float32 master takes every flush);
                              1: shared -- the low-precision copy is the only checkpoint and
-                             each flush starts from it (needs read_copy != NONE) */
+                             each flush starts from it (needs read_copy BF16 or FP8_E4M3) */
 } replay_config;
 
 /* Device buffers of one layer's decode state.  Sizes in elements; use
    replay_buffer_bytes for bytes.  Every pointer 16-byte aligned. */
 typedef struct {
     float   *s_master;  /* [B][H][P][N] f32 checkpoint; NULL iff shared_lowp */
-    void    *s_copy;    /* [B][H][P][N] bf16 or e4m3 copy; NULL iff read_copy == NONE */
-    float   *s_scale;   /* [B][H] per-head scale of an e4m3 copy (value = code * scale);
-                           NULL unless read_copy == FP8_E4M3 */
+    void    *s_copy;    /* [B][H][P][N] bf16 or e4m3 copy, or [B][H][P*N/2] bytes of FP4 codes
+                           (value 2i of a head's tile in the low nibble of byte i, value
+                           2i+1 in the high nibble); NULL iff read_copy == NONE */
+    void    *s_scale;   /* e4m3: float [B][H], the per-head scale (value = code * scale);
+                           FP4: uint8 [B][H][P*N/32], the E8M0 scale of each block of 32
+                           (value = code * 2^(byte - 127)); NULL for the other copies */
     void    *ring_q;    /* [B][G][L][N] io dtype */
     void    *ring_k;    /* [B][G][L][N] io dtype */
     void    *ring_v;    /* [B][H][L][P] io dtype */

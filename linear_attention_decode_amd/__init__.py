@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "ReplayError", "ReplayConfig", "ReplayBuffers", "ReplayLayer", "lib", "LIB_PATH",
-    "F32", "BF16", "FP8_E4M3", "NONE", "SEQERR_RING_OVERFLOW", "SEQERR_ROLLBACK_RANGE",
+    "F32", "BF16", "FP8_E4M3", "FP4_E2M1", "NONE", "SEQERR_RING_OVERFLOW", "SEQERR_ROLLBACK_RANGE",
     "SEQERR_TOO_FEW", "SEQERR_POS_OVERFLOW", "EXPORTS",
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
@@ -26,7 +26,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libreplayssm.so")
 
-NONE, F32, BF16, FP8_E4M3 = -1, 0, 1, 2
+NONE, F32, BF16, FP8_E4M3, FP4_E2M1 = -1, 0, 1, 2, 3
 SEQERR_RING_OVERFLOW, SEQERR_ROLLBACK_RANGE, SEQERR_TOO_FEW, SEQERR_POS_OVERFLOW = 1, 2, 4, 8
 
 # every symbol include/replayssm.h declares
@@ -196,15 +196,16 @@ def replay_stream_probe(mode, src, dst, nbytes, stream=None):
 
 # ---- one layer's state, allocated with torch -------------------------------
 
-_DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, None: NONE, "none": NONE}
+_DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1, None: NONE, "none": NONE}
 
 
 class ReplayLayer:
     """Buffers + handle of one SSM layer's decode state on the current GPU.
 
     Tensors (torch, on `device`): s_master [B,H,P,N] f32 (absent in shared
-    mode), s_copy [B,H,P,N] bf16/uint8 (when read_copy is set), s_scale
-    [B,H] f32 (e4m3 copy), ring_q/ring_k [B,G,L,N], ring_v [B,H,L,P] (io
+    mode), s_copy [B,H,P,N] bf16/uint8 or [B,H,P*N/2] uint8 FP4 codes (when
+    read_copy is set), s_scale [B,H] f32 (e4m3) or [B,H,P*N/32] uint8 E8M0
+    (FP4), ring_q/ring_k [B,G,L,N], ring_v [B,H,L,P] (io
     dtype), ring_dt/ring_a [B,H,L] f32, pos/base [B] int32, err [B+1] int32,
     sync [B, G+1, 32] int32 (arrival counters, one per 128-byte line).
     """
@@ -220,9 +221,12 @@ class ReplayLayer:
         B, H, G, P, N, L = batch, heads, groups, head_dim, state_dim, ring_len
         iot = torch.bfloat16 if io_dtype == "bf16" else torch.float32
         copy_t = torch.bfloat16 if read_copy == "bf16" else torch.uint8
+        fp4 = read_copy == "fp4"
         shapes = {
-            "s_master": ((B, H, P, N), torch.float32), "s_copy": ((B, H, P, N), copy_t),
-            "s_scale": ((B, H), torch.float32), "ring_q": ((B, G, L, N), iot),
+            "s_master": ((B, H, P, N), torch.float32),
+            "s_copy": ((B, H, P * N // 2) if fp4 else (B, H, P, N), copy_t),
+            "s_scale": ((B, H, P * N // 32), torch.uint8) if fp4 else ((B, H), torch.float32),
+            "ring_q": ((B, G, L, N), iot),
             "ring_k": ((B, G, L, N), iot), "ring_v": ((B, H, L, P), iot),
             "ring_dt": ((B, H, L), torch.float32), "ring_a": ((B, H, L), torch.float32),
             "pos": ((B,), torch.int32), "base": ((B,), torch.int32), "err": ((B + 1,), torch.int32),

@@ -28,7 +28,7 @@ replay_status from_hip(hipError_t e) { return e == hipSuccess ? REPLAY_OK : REPL
 int io_bytes(const replay_config &c) { return c.io_dtype == REPLAY_BF16 ? 2 : 4; }
 
 int state_kind(int32_t dtype) {
-    return dtype == REPLAY_BF16 ? ST_BF16 : (dtype == REPLAY_FP8_E4M3 ? ST_FP8 : ST_F32);
+    return dtype == REPLAY_BF16 ? ST_BF16 : (dtype == REPLAY_FP8_E4M3 ? ST_FP8 : (dtype == REPLAY_FP4_E2M1 ? ST_FP4 : ST_F32));
 }
 
 // Shape and dtype checks shared by every entry point that takes a config.
@@ -48,10 +48,12 @@ replay_status check_config(const replay_config *c) {
     if (st != REPLAY_OK) return st;
     if (c->ring_len < 1) return REPLAY_ERR_INVALID_ARG;
     if (c->ring_len > kMaxRing) return REPLAY_ERR_UNSUPPORTED;
-    if (c->read_copy != REPLAY_NONE && c->read_copy != REPLAY_BF16 && c->read_copy != REPLAY_FP8_E4M3)
+    if (c->read_copy != REPLAY_NONE && c->read_copy != REPLAY_BF16 && c->read_copy != REPLAY_FP8_E4M3 &&
+        c->read_copy != REPLAY_FP4_E2M1)
         return REPLAY_ERR_UNSUPPORTED;
     if (c->shared_lowp != 0 && c->shared_lowp != 1) return REPLAY_ERR_INVALID_ARG;
     if (c->shared_lowp && c->read_copy == REPLAY_NONE) return REPLAY_ERR_INVALID_ARG;
+    if (c->shared_lowp && c->read_copy == REPLAY_FP4_E2M1) return REPLAY_ERR_UNSUPPORTED;
     return REPLAY_OK;
 }
 
@@ -60,8 +62,10 @@ void buffer_bytes(const replay_config &c, size_t out[kNumBufferFields]) {
                  L = c.ring_len, esz = io_bytes(c);
     const size_t state = B * H * P * N;
     out[0] = c.shared_lowp ? 0 : state * 4;                                            // s_master
-    out[1] = c.read_copy == REPLAY_NONE ? 0 : state * (c.read_copy == REPLAY_BF16 ? 2 : 1);  // s_copy
-    out[2] = c.read_copy == REPLAY_FP8_E4M3 ? B * H * 4 : 0;                            // s_scale
+    out[1] = c.read_copy == REPLAY_NONE ? 0
+             : (c.read_copy == REPLAY_BF16 ? state * 2 : (c.read_copy == REPLAY_FP4_E2M1 ? state / 2 : state));  // s_copy
+    out[2] = c.read_copy == REPLAY_FP8_E4M3 ? B * H * 4
+             : (c.read_copy == REPLAY_FP4_E2M1 ? state / 32 : 0);                     // s_scale
     out[3] = B * G * L * N * esz;                                                       // ring_q
     out[4] = B * G * L * N * esz;                                                       // ring_k
     out[5] = B * H * L * P * esz;                                                       // ring_v
@@ -110,7 +114,7 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
     a.sync = h->bufs.sync;
     a.S_out = c.shared_lowp ? nullptr : h->bufs.s_master;
     a.copy_out = c.read_copy == REPLAY_NONE ? nullptr : h->bufs.s_copy;
-    a.scale_out = c.read_copy == REPLAY_FP8_E4M3 ? h->bufs.s_scale : nullptr;
+    a.scale_out = (c.read_copy == REPLAY_FP8_E4M3 || c.read_copy == REPLAY_FP4_E2M1) ? h->bufs.s_scale : nullptr;
     int st_in;
     if (load_src) {
         a.S_in = load_src;
@@ -118,7 +122,7 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
         st_in = ST_F32;
     } else if (c.shared_lowp) {
         a.S_in = h->bufs.s_copy;
-        a.scale_in = h->bufs.s_scale;
+        a.scale_in = static_cast<const float *>(h->bufs.s_scale);
         st_in = state_kind(c.read_copy);
     } else {
         a.S_in = h->bufs.s_master;
@@ -190,13 +194,15 @@ replay_status replay_init(const replay_config *cfg, const replay_buffers *bufs, 
     h->bufs = *bufs;
     if (cfg->shared_lowp) h->bufs.s_master = nullptr;
     if (cfg->read_copy == REPLAY_NONE) h->bufs.s_copy = nullptr;
-    if (cfg->read_copy != REPLAY_FP8_E4M3) h->bufs.s_scale = nullptr;
+    if (cfg->read_copy != REPLAY_FP8_E4M3 && cfg->read_copy != REPLAY_FP4_E2M1) h->bufs.s_scale = nullptr;
 
     hipStream_t s = as_stream(stream);
     hipError_t e = hipSuccess;
     if (h->bufs.s_master) e = launch_fill_u32(h->bufs.s_master, 0u, need[0] / 4, s);
     if (e == hipSuccess && h->bufs.s_copy) e = launch_fill_u32(h->bufs.s_copy, 0u, need[1] / 4, s);
-    if (e == hipSuccess && h->bufs.s_scale) e = launch_fill_u32(h->bufs.s_scale, 0x3f800000u, need[2] / 4, s);
+    // e4m3 scales start at 1.0f; FP4 block scales at byte 0 (2^-127), the scale of an all-zero block
+    if (e == hipSuccess && h->bufs.s_scale)
+        e = launch_fill_u32(h->bufs.s_scale, cfg->read_copy == REPLAY_FP8_E4M3 ? 0x3f800000u : 0u, need[2] / 4, s);
     if (e == hipSuccess) e = launch_fill_u32(h->bufs.pos, 0u, need[8] / 4, s);
     if (e == hipSuccess) e = launch_fill_u32(h->bufs.base, 0u, need[9] / 4, s);
     if (e == hipSuccess) e = launch_fill_u32(h->bufs.err, 0u, need[10] / 4, s);

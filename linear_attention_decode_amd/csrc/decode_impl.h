@@ -26,10 +26,12 @@ namespace replay {
 
 template <int P, int N, int ST, int WM>
 struct DecodeShape {
-    static constexpr int base_vec = ST == ST_F32 ? 4 : (ST == ST_BF16 ? 8 : (WM == 1 ? 16 : 8));
+    static constexpr int base_vec = ST == ST_F32 ? 4
+                                  : (ST == ST_BF16 ? 8 : (ST == ST_FP8 ? (WM == 1 ? 16 : 8) : (WM == 1 ? 32 : 8)));
     // at least one full wavefront of chunks per head
     static constexpr int VEC = (P * N / base_vec >= 64) ? base_vec
-                             : ((P * N / (base_vec / 2) >= 64) ? base_vec / 2 : base_vec / 4);
+                             : ((P * N / (base_vec / 2) >= 64) ? base_vec / 2
+                             : ((P * N / (base_vec / 4) >= 64) ? base_vec / 4 : base_vec / 8));
     static constexpr int CHUNKS = P * N / VEC;
     // streaming threads: at most 8 chunks a lane (4096 chunks: 8 wavefronts)
     static constexpr int NTS = CHUNKS >= 4096 ? 512 : (CHUNKS < 256 ? CHUNKS : 256);
@@ -251,7 +253,12 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NTS + 64 * ring_waves<L
     const size_t tile = bh * (size_t)(P * N);
     if (tid < NTS) {
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
+        for (int i = 0; i < ITER; ++i) {
+            if constexpr (ST == ST_FP4)
+                ch[i].load_mx(args.S, args.scale, tile + (size_t)(i * NTS + tid) * VEC);
+            else
+                ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
+        }
     }
     const int count = pos - base;
     if (count < W) {  // uniform over the workgroup
@@ -290,6 +297,7 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NTS + 64 * ring_waves<L
                 float acc = 0.f;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) acc = fmaf(x[e], qv[w][e], acc);
+                if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
                 part[i][w] = acc;
             }
         }
@@ -305,7 +313,7 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NTS + 64 * ring_waves<L
     __syncthreads();
 
     if (tid < NTS && RR::writer(lane)) {
-        const float sc = (ST == ST_FP8) ? args.scale[bh] : 1.0f;
+        const float sc = (ST == ST_FP8) ? static_cast<const float *>(args.scale)[bh] : 1.0f;
         const int hi = RR::halving_index(lane);
 #pragma unroll
         for (int e = 0; e < RR::FINAL; ++e) {

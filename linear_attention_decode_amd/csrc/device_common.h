@@ -295,6 +295,51 @@ struct Chunk<ST_FP8, VEC> {
     }
 };
 
+// Two E2M1 codes (byte `sel` of w) -> their float values (hardware conversion, scale 1).
+__device__ __forceinline__ void fp4_pair_to_f32(uint32_t w, int sel, float *out) {
+    decltype(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0)) v;
+    switch (sel) {
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+    }
+    out[0] = v[0];
+    out[1] = v[1];
+}
+
+// MX FP4 chunk: VEC codes (VEC/2 bytes) of one block of 32 values, with the
+// block's E8M0 scale exponent.  widen() gives the unscaled E2M1 values (the
+// hardware conversion, exact); callers multiply sums by 2^se, which is exact
+// for a power of two, so a block's products are formed once and scaled once.
+template <int VEC>
+struct Chunk<ST_FP4, VEC> {
+    static_assert(VEC == 32 || VEC == 16 || VEC == 8 || VEC == 4, "FP4 chunks are 16, 8, 4 or 2 bytes");
+    static constexpr int WORDS = VEC >= 8 ? VEC / 8 : 1;
+    uint32_t raw[WORDS];
+    int se;
+    // e: element index of the chunk's first value; scales: one byte per block of 32
+    __device__ __forceinline__ void load_mx(const void *S, const void *scales, size_t e) {
+        const uint8_t *p = static_cast<const uint8_t *>(S) + e / 2;
+        if constexpr (VEC == 32) {
+            u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+            raw[0] = w.x; raw[1] = w.y; raw[2] = w.z; raw[3] = w.w;
+        } else if constexpr (VEC == 16) {
+            u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+            raw[0] = w.x; raw[1] = w.y;
+        } else if constexpr (VEC == 8) {
+            raw[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+        } else {
+            raw[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
+        }
+        se = (int)static_cast<const uint8_t *>(scales)[e / 32] - 127;
+    }
+    __device__ __forceinline__ void widen(float *out, float) const {
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) fp4_pair_to_f32(raw[i / 4], i % 4, out + 2 * i);
+    }
+};
+
 // ---- lane exchanges --------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {

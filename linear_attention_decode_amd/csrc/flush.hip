@@ -208,7 +208,31 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
             const uint32_t o = f32x4_to_fp8(x[i][0] / sig, x[i][1] / sig, x[i][2] / sig, x[i][3] / sig);
             __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(cp + (size_t)(i * NT + tid) * VEC));
         }
-        if (tid == 0) args.scale_out[bh] = sig;
+        if (tid == 0) static_cast<float *>(args.scale_out)[bh] = sig;
+    } else if constexpr (COPY == ST_FP4) {
+        // MX FP4: the 32 consecutive values of 8 neighbouring lanes share the
+        // scale X = 2^(floor(log2 amax) - 2); codes are e2m1(x / X), the
+        // division exact (ldexp), converted by the hardware (nearest even,
+        // saturating at 6); first value of a pair in the low nibble
+        uint8_t *cp = static_cast<uint8_t *>(args.copy_out);
+        uint8_t *scl = static_cast<uint8_t *>(args.scale_out);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            float amax = fmaxf(fmaxf(fabsf(x[i][0]), fabsf(x[i][1])), fmaxf(fabsf(x[i][2]), fabsf(x[i][3])));
+#pragma unroll
+            for (int bit = 2; bit >= 0; --bit) amax = fmaxf(amax, lane_partner(amax, bit));
+            int se = -127;
+            if (amax > 0.f) {
+                int ex;
+                (void)frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1)
+                se = ex - 3 < -127 ? -127 : (ex - 3 > 127 ? 127 : ex - 3);
+            }
+            const uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[i][0], -se), ldexpf(x[i][1], -se), 1.0f, 0);
+            const uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[i][2], -se), ldexpf(x[i][3], -se), 1.0f, 0);
+            const size_t e0 = tile + (size_t)(i * NT + tid) * VEC;
+            *reinterpret_cast<uint16_t *>(cp + e0 / 2) = (uint16_t)((lo & 0xffu) | ((hi & 0xffu) << 8));
+            if ((tid & 7) == 0) scl[e0 / 32] = (uint8_t)(se + 127);
+        }
     }
 
     // Last head of its group: the group arrives at the sequence's counter;
@@ -240,6 +264,7 @@ static hipError_t launch_pn(int st_in, int st_copy, bool wm, const FlushArgs &a,
     if (st_in == ST_F32 && wm) {           // separated: the float32 master takes the update
         if (st_copy == ST_BF16) return launch_one<P, N, ST_F32, ST_BF16, true>(a, s);
         if (st_copy == ST_FP8) return launch_one<P, N, ST_F32, ST_FP8, true>(a, s);
+        if (st_copy == ST_FP4) return launch_one<P, N, ST_F32, ST_FP4, true>(a, s);
         return launch_one<P, N, ST_F32, -1, true>(a, s);
     }
     if (st_in == ST_F32) {                 // shared mode, loading a float32 checkpoint

@@ -9,7 +9,7 @@
 namespace replay {
 
 // Storage kinds of a state tile.
-enum StateKind : int { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2 };
+enum StateKind : int { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2, ST_FP4 = 3 };
 
 // Largest ring and verify window the kernels are built for.
 constexpr int kMaxRing = 32;
@@ -38,7 +38,7 @@ struct RingView {
 struct DecodeArgs {
     RingView r;
     const void *S;          // state tile source: f32 master or the copy
-    const float *scale;     // [B][H] for an e4m3 copy, else unused
+    const void *scale;      // float [B][H] for an e4m3 copy, uint8 [B][H][P*N/32] for FP4, else unused
     float *y;               // [B][W][H][P]
     int32_t W;
 };
@@ -49,7 +49,7 @@ struct FlushArgs {
     const float *scale_in;  // old per-head scale when S_in is an e4m3 copy
     float *S_out;           // f32 master to write, or nullptr
     void *copy_out;         // copy to write, or nullptr
-    float *scale_out;       // per-head scale to write (e4m3 copy), or nullptr
+    void *scale_out;        // scales to write: float per head (e4m3), E8M0 byte per block (FP4), or nullptr
     int32_t min_count;      // flush sequences with count >= max(min_count, 1)
     int32_t force_empty;    // 1: treat every sequence as due with an empty ring (checkpoint load)
     int32_t *base_out;      // base, set to pos by the last workgroup of a folded sequence

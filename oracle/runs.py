@@ -134,3 +134,31 @@ def normwise_rel_err(y: np.ndarray, ref: np.ndarray, axes=(-2, -1)) -> np.ndarra
     num = np.max(np.abs(np.asarray(y, dtype=np.float64) - ref), axis=axes)
     den = np.maximum(np.max(np.abs(ref), axis=axes), 1e-30)
     return num / den
+
+
+def verify_rounds_copy(x: dict, accept: np.ndarray, W: int, S0: np.ndarray, L: int, fmt: str) -> np.ndarray:
+    """Speculative rounds whose outputs read a low-precision copy of the last
+    flushed state (separated precisions), per sequence: before each round a
+    ring holding >= L-W+1 accepted tokens is folded into the exact state;
+    the round's W outputs come from the copy of that state followed by the
+    accepted tokens since the fold and the W drafts; the accepted drafts join
+    the ring.  Returns y float64 [R][W][B][H][P]."""
+    R = accept.shape[0]
+    B = S0.shape[0]
+    H, P = x["v"].shape[2], x["v"].shape[3]
+    y = np.empty((R, W, B, H, P))
+    for b in range(B):
+        S_fl = S0[b:b + 1].astype(np.float64).copy()
+        live = []
+        for r in range(R):
+            if len(live) >= L - W + 1:
+                sub = {k: v[live][:, b:b + 1] for k, v in x.items()}
+                core.eager(S_fl, sub["q"], sub["k"], sub["v"], sub["dt"], sub["a"])
+                live = []
+            Sq = np.ascontiguousarray(quant_dequant(S_fl, fmt))
+            rows = live + [r * W + i for i in range(W)]
+            sub = {k: v[rows][:, b:b + 1] for k, v in x.items()}
+            yy = core.eager(Sq, sub["q"], sub["k"], sub["v"], sub["dt"], sub["a"])
+            y[r, :, b] = yy[len(live):, 0]
+            live += [r * W + i for i in range(int(accept[r, b]))]
+    return y

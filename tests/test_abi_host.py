@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lad):
 
 
 def test_version_and_status_strings(lad):
-    assert lad.replay_abi_version() == 3
+    assert lad.replay_abi_version() == 4
     for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "HIP")]:
         assert text in lad.replay_status_string(s)
     assert lad.replay_status_string(99) == "unknown status"
@@ -53,6 +53,10 @@ def test_buffer_bytes_match_the_layout(lad):
     b8 = lad.replay_buffer_bytes(c8)
     assert b8["s_master"] == 0 and b8["s_copy"] == 4 * 8 * 128 * 128 and b8["s_scale"] == 4 * 8 * 4
     assert b8["ring_v"] == 4 * 8 * 32 * 128 * 4
+    c4 = lad.ReplayConfig(4, 8, 2, 64, 128, 16, lad.BF16, lad.FP4_E2M1, 0)
+    b4 = lad.replay_buffer_bytes(c4)
+    assert b4["s_master"] == 4 * 8 * 64 * 128 * 4
+    assert b4["s_copy"] == 4 * 8 * 64 * 128 // 2 and b4["s_scale"] == 4 * 8 * 64 * 128 // 32
 
 
 @pytest.mark.parametrize("fields,status", [
@@ -65,6 +69,7 @@ def test_buffer_bytes_match_the_layout(lad):
     ((2, 4, 1, 64, 128, 16, 2, -1, 0), 2),          # io dtype e4m3
     ((2, 4, 1, 64, 128, 16, 1, 7, 0), 2),           # unknown copy dtype
     ((2, 4, 1, 64, 128, 16, 1, -1, 1), 1),          # shared without a copy
+    ((2, 4, 1, 64, 128, 16, 1, 3, 1), 2),           # shared FP4 copy: not built
 ])
 def test_invalid_configs_are_rejected_on_the_host(lad, fields, status):
     c = lad.ReplayConfig(*fields)

@@ -109,3 +109,21 @@ def test_normwise_rel_err():
     ref = np.array([[1.0, 4.0], [0.0, 0.0]])
     assert runs.normwise_rel_err(y, ref, axes=(-1,)).tolist() == [0.5, 0.0]
     assert runs.normwise_rel_err(y, ref) == 0.5
+
+
+def test_verify_rounds_copy_limits():
+    """The copy emulation under speculative rounds: with a copy that only
+    rounds the state to float32 it reproduces the exact rounds (to that
+    rounding), at ring lengths that fold every round or rarely; with the FP4
+    copy and a zero start it equals the exact rounds until the first fold."""
+    W, R = 3, 8
+    x = _x(W_TINY, R * W)
+    acc = synth.accept_counts(W_TINY, R, W)
+    y_exact = runs.verify_rounds(x, acc, W, _S0(W_TINY))
+    for L in (3, 4, 8, 32):
+        y32 = runs.verify_rounds_copy(x, acc, W, _S0(W_TINY), L, "f32")
+        assert float(np.max(runs.normwise_rel_err(y32, y_exact))) <= 1e-6, L
+    y4 = runs.verify_rounds_copy(x, acc, W, _S0(W_TINY), 32, "fp4")      # never folds: reads Q(0) = 0
+    assert np.allclose(y4, y_exact, rtol=1e-13, atol=1e-15)
+    y4 = runs.verify_rounds_copy(x, acc, W, _S0(W_TINY), 4, "fp4")
+    assert float(np.max(runs.normwise_rel_err(y4, y_exact))) > 1e-3   # folded states are read rounded
