@@ -455,8 +455,8 @@ def bench_dual(args):
         pools = [input_pool(w, chunk, t0=c0) for c0 in range(0, T, chunk)]
         ys_master = None
         for mode, rc, shared in [("f32", None, False), ("bf16-separated", "bf16", False),
-                                 ("fp8-separated", "fp8", False), ("bf16-shared", "bf16", True),
-                                 ("fp8-shared", "fp8", True)]:
+                                 ("fp8-separated", "fp8", False), ("fp4-separated", "fp4", False),
+                                 ("bf16-shared", "bf16", True), ("fp8-shared", "fp8", True)]:
             y = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
             sel = torch.tensor(seqs, device="cuda")
 

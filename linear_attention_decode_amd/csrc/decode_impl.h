@@ -24,10 +24,12 @@
 
 namespace replay {
 
-template <int P, int N, int ST, int WM>
+// NARROW: 8-element chunks for the low-precision tiles (several heads per
+// workgroup, where the register budget goes to the extra chunks in flight).
+template <int P, int N, int ST, int WM, bool NARROW = false>
 struct DecodeShape {
     static constexpr int base_vec = ST == ST_F32 ? 4
-                                  : (ST == ST_BF16 ? 8 : (ST == ST_FP8 ? (WM == 1 ? 16 : 8) : (WM == 1 ? 32 : 8)));
+                                  : (ST == ST_BF16 ? 8 : (NARROW ? 8 : (ST == ST_FP8 ? (WM == 1 ? 16 : 8) : (WM == 1 ? 32 : 8))));
     // at least one full wavefront of chunks per head
     static constexpr int VEC = (P * N / base_vec >= 64) ? base_vec
                              : ((P * N / (base_vec / 2) >= 64) ? base_vec / 2
@@ -225,32 +227,49 @@ __device__ __forceinline__ void ring_wave_mx(const RingView &r, int lane, int j0
 template <int LM, bool IOB>
 constexpr int ring_waves() { return IOB ? LM / 16 : 1; }
 
-template <int P, int N, int ST, int WM, int LM, bool IOB>
-__global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NTS + 64 * ring_waves<LM, IOB>())) void decode_kernel(
-    DecodeArgs args) {
-    using Sh = DecodeShape<P, N, ST, WM>;
-    constexpr int W = WM;
+// Heads per workgroup: low-precision tiles are small, so one workgroup takes
+// HPW heads of one group (their tiles are contiguous in memory and stream as
+// one taller tile); each head keeps its own ring wavefront(s).  The per-
+// workgroup latency of the ring work is then paid once per HPW heads.
+// (Decode only: a verify window's extra queries and partial sums take the
+// registers the extra chunks would need.)
+template <int ST, int WM>
+constexpr int heads_per_wg() { return (ST == ST_F32 || WM > 1) ? 1 : (ST == ST_BF16 ? 2 : 4); }
+
+template <int P, int N, int ST, int WM, int LM, bool IOB, int HPW>
+struct DecodeLaunch {
+    using Sh = DecodeShape<P * HPW, N, ST, WM, (HPW > 1)>;
+    static constexpr int NR = ring_waves<LM, IOB>();      // ring wavefronts per head
+    static constexpr int NT = Sh::NTS + 64 * NR * HPW;
+};
+
+template <int P, int N, int ST, int WM, int LM, bool IOB, int HPW>
+__global__ __launch_bounds__((DecodeLaunch<P, N, ST, WM, LM, IOB, HPW>::NT)) void decode_kernel(DecodeArgs args) {
+    using DL = DecodeLaunch<P, N, ST, WM, LM, IOB, HPW>;
+    using Sh = typename DL::Sh;
+    constexpr int W = WM, PT = P * HPW;
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
-    constexpr int NR = ring_waves<LM, IOB>(), NT = NTS + 64 * NR;
+    constexpr int NR = DL::NR, NT = DL::NT;
     using RR = RowReduce<ITER, LPR>;
 
-    __shared__ float s_r[NR][WM][P];
-    __shared__ float s_abar[WM];
-    __shared__ __align__(16) float s_sw[IOB ? WM : 1][IOB ? LM : 4];
+    __shared__ float s_r[NR][HPW][WM][P];
+    __shared__ float s_abar[HPW][WM];
+    __shared__ __align__(16) float s_sw[HPW][IOB ? WM : 1][IOB ? LM : 4];
 
     const RingView &r = args.r;
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int b = lid / r.H, h = lid % r.H;
-    const int g = (h * r.G) / r.H;
+    const int HW = r.H / HPW;
+    const int b = lid / HW, h0 = (lid % HW) * HPW;
+    const int g = (h0 * r.G) / r.H;   // the HPW heads share this group
     const int tid = threadIdx.x, lane = tid & 63;
     const int L = r.L, H = r.H;
-    const size_t bh = (size_t)b * H + h;
+    const size_t bh0 = (size_t)b * H + h0;
 
-    // pointer pair first, then the state tile (which does not depend on it)
+    // pointer pair first, then the state tiles (which do not depend on it)
     const int base = r.base[b];
     const int pos = r.pos[b];
     Chunk<ST, VEC> ch[ITER];
-    const size_t tile = bh * (size_t)(P * N);
+    const size_t tile = bh0 * (size_t)(P * N);
     if (tid < NTS) {
 #pragma unroll
         for (int i = 0; i < ITER; ++i) {
@@ -262,9 +281,9 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NTS + 64 * ring_waves<L
     }
     const int count = pos - base;
     if (count < W) {  // uniform over the workgroup
-        for (int i = tid; i < W * P; i += NT) {
-            const int w = i / P, p = i % P;
-            args.y[(((size_t)b * W + w) * H + h) * P + p] = __builtin_nanf("");
+        for (int i = tid; i < W * PT; i += NT) {
+            const int w = i / PT, pp = i % PT;
+            args.y[(((size_t)b * W + w) * H + h0) * P + pp] = __builtin_nanf("");
         }
         if (tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_TOO_FEW);
         return;
@@ -303,27 +322,29 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NTS + 64 * ring_waves<L
         }
         RR::template run<WM>(part, lane);
     } else {
-        if constexpr (IOB) {
-            const int rw = (tid - NTS) >> 6;
-            ring_wave_mx<P, N, WM, LM>(r, lane, 16 * rw, b, g, bh, base, count, s_r[rw], s_abar, s_sw);
-        } else {
-            ring_wave<P, N, WM, LM, IOB>(r, lane, b, g, bh, base, count, s_r[0], s_abar);
-        }
+        const int rwave = (tid - NTS) >> 6;          // ring wavefront: head hl, 16-entry block blk
+        const int hl = rwave / NR, blk = rwave % NR;
+        const size_t bh = bh0 + hl;
+        if constexpr (IOB)
+            ring_wave_mx<P, N, WM, LM>(r, lane, 16 * blk, b, g, bh, base, count, s_r[blk][hl], s_abar[hl], s_sw[hl]);
+        else
+            ring_wave<P, N, WM, LM, IOB>(r, lane, b, g, bh, base, count, s_r[0][hl], s_abar[hl]);
     }
     __syncthreads();
 
     if (tid < NTS && RR::writer(lane)) {
-        const float sc = (ST == ST_FP8) ? static_cast<const float *>(args.scale)[bh] : 1.0f;
         const int hi = RR::halving_index(lane);
 #pragma unroll
         for (int e = 0; e < RR::FINAL; ++e) {
-            const int row = (e + RR::FINAL * hi) * RPI + tid / LPR;
+            const int row = (e + RR::FINAL * hi) * RPI + tid / LPR;   // of the HPW stacked tiles
+            const int hl = HPW == 1 ? 0 : row / P, p = HPW == 1 ? row : row % P;
+            const float sc = (ST == ST_FP8) ? static_cast<const float *>(args.scale)[bh0 + hl] : 1.0f;
 #pragma unroll
             for (int w = 0; w < WM; ++w) {
                 if (w < W) {
-                    float rt = s_r[0][w][row];
-                    if constexpr (NR == 2) rt += s_r[1][w][row];   // block 0 + block 1
-                    args.y[(((size_t)b * W + w) * H + h) * P + row] = s_abar[w] * (sc * part[e][w]) + rt;
+                    float rt = s_r[0][hl][w][p];
+                    if constexpr (NR == 2) rt += s_r[1][hl][w][p];   // block 0 + block 1
+                    args.y[(((size_t)b * W + w) * H + h0) * P + row] = s_abar[hl][w] * (sc * part[e][w]) + rt;
                 }
             }
         }
@@ -332,9 +353,17 @@ __global__ __launch_bounds__((DecodeShape<P, N, ST, WM>::NTS + 64 * ring_waves<L
 
 template <int P, int N, int ST, int WM, int LM, bool IOB>
 static hipError_t launch_one(const DecodeArgs &a, hipStream_t s) {
-    using Sh = DecodeShape<P, N, ST, WM>;
-    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
-    decode_kernel<P, N, ST, WM, LM, IOB><<<blocks, Sh::NTS + 64 * ring_waves<LM, IOB>(), 0, s>>>(a);
+    constexpr int HPW = heads_per_wg<ST, WM>();
+    // several heads per workgroup when they divide a group evenly
+    if (HPW > 1 && (a.r.H / a.r.G) % HPW == 0) {
+        using DL = DecodeLaunch<P, N, ST, WM, LM, IOB, HPW>;
+        const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H / HPW);
+        decode_kernel<P, N, ST, WM, LM, IOB, HPW><<<blocks, DL::NT, 0, s>>>(a);
+    } else {
+        using DL = DecodeLaunch<P, N, ST, WM, LM, IOB, 1>;
+        const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
+        decode_kernel<P, N, ST, WM, LM, IOB, 1><<<blocks, DL::NT, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

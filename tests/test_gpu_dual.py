@@ -126,7 +126,7 @@ def test_dual_precision_drift(dt_scale):
                            for k in chunks[0]}, w.io_dtype)
     y_ref = runs.standard(x, np.zeros((len(seqs), w.heads, w.head_dim, w.state_dim)))
     means = {}
-    for fmt, shared in [("fp8", False), ("fp8", True), ("bf16", False)]:
+    for fmt, shared in [("fp8", False), ("fp8", True), ("bf16", False), ("fp4", False)]:
         layer = _layer(w, read_copy=fmt, shared_lowp=shared)
         y = torch.empty((w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
         ys = torch.empty((T, len(seqs), w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
@@ -142,8 +142,11 @@ def test_dual_precision_drift(dt_scale):
         means[(fmt, shared)] = float(e.mean())
         print(f"  {fmt} {'shared' if shared else 'separated'}: max {e.max():.3e} mean {e.mean():.3e}; "
               + ", ".join(f"window {i}: max {mx:.3e} mean {mn:.3e}" for i, mx, mn in win))
-        if not shared:
+        if not shared and fmt in TOL_VS_EXACT:
             assert float(e.max()) <= TOL_VS_EXACT[fmt]
+        if fmt == "fp4":
+            # separated: the error does not compound -- the last window is no worse than the middle one
+            assert win[-1][1] <= 1.5 * win[1][1] + 1e-6
     if dt_scale < 1.0:
         assert means[("fp8", True)] > 1.2 * means[("fp8", False)]
 
