@@ -33,7 +33,9 @@ struct FlushShape {
     static_assert(LPR <= 64 && 64 % LPR == 0, "row group must sit in a wavefront");
 };
 
-template <int P, int N, int SIN, int COPY, bool WRITE_MASTER, bool IOB>
+// HC heads of one group per workgroup, one after another: a flush that
+// finds nothing due then costs B*H/HC workgroups that only read the pointer.
+template <int P, int N, int SIN, int COPY, bool WRITE_MASTER, bool IOB, int HC>
 __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs args) {
     using Sh = FlushShape<P, N>;
     constexpr int VEC = Sh::VEC, NT = Sh::NT, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
@@ -50,11 +52,11 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
 
     const RingView &r = args.r;
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int b = lid / r.H, h = lid % r.H;
-    const int g = (h * r.G) / r.H;
+    const int HW = r.H / HC;
+    const int b = lid / HW, h0 = (lid % HW) * HC;
+    const int g = (h0 * r.G) / r.H;   // the HC heads share this group
     const int tid = threadIdx.x, lane = tid & 63;
     const int L = r.L;
-    const size_t bh = (size_t)b * r.H + h;
 
     const int base = r.base[b];
     const int pos = r.pos[b];
@@ -69,6 +71,9 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     int prev = -1;
     if (tid == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
 
+    for (int hl = 0; hl < HC; ++hl) {
+    const int h = h0 + hl;
+    const size_t bh = (size_t)b * r.H + h;
     // 1. tile loads, then every ring load in one batch
     Chunk<SIN, VEC> ch[ITER];
     const size_t tile = bh * (size_t)(P * N);
@@ -235,9 +240,12 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
         }
     }
 
-    // Last head of its group: the group arrives at the sequence's counter;
-    // the last group means every workgroup of the sequence has read base.
-    if (tid == 0 && prev == r.H / r.G - 1) {
+    if (HC > 1) __syncthreads();   // LDS is reused by the next head
+    }
+
+    // Last workgroup of its group: the group arrives at the sequence's
+    // counter; the last group means every workgroup of the sequence has read base.
+    if (tid == 0 && prev == r.H / r.G / HC - 1) {
         int32_t *seq = args.sync + (size_t)b * (r.G + 1) * kSyncStride;
         atomicExch(seq + (size_t)g * kSyncStride, 0);
         if (atomicAdd(seq + (size_t)r.G * kSyncStride, 1) == r.G - 1) {
@@ -247,16 +255,29 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     }
 }
 
-template <int P, int N, int SIN, int COPY, bool WM>
-static hipError_t launch_one(const FlushArgs &a, hipStream_t s) {
+template <int P, int N, int SIN, int COPY, bool WM, int HC>
+static hipError_t launch_hc(const FlushArgs &a, hipStream_t s) {
     using Sh = FlushShape<P, N>;
-    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
+    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H / HC);
     const size_t lds = (size_t)(P + N) * a.r.L * sizeof(float);
     if (a.r.io_bf16)
-        flush_kernel<P, N, SIN, COPY, WM, true><<<blocks, Sh::NT, lds, s>>>(a);
+        flush_kernel<P, N, SIN, COPY, WM, true, HC><<<blocks, Sh::NT, lds, s>>>(a);
     else
-        flush_kernel<P, N, SIN, COPY, WM, false><<<blocks, Sh::NT, lds, s>>>(a);
+        flush_kernel<P, N, SIN, COPY, WM, false, HC><<<blocks, Sh::NT, lds, s>>>(a);
     return hipGetLastError();
+}
+
+// Four heads per workgroup only for flushes that fold full rings only
+// (min_count >= L): in the standard schedule those find nothing due on all
+// but one step in L, where the smaller grid saves most; a flush that folds
+// part of the batch every call (speculative rounds) and a checkpoint load
+// keep one head per workgroup, which folds faster.
+template <int P, int N, int SIN, int COPY, bool WM>
+static hipError_t launch_one(const FlushArgs &a, hipStream_t s) {
+    constexpr int HC = 4;
+    if (!a.force_empty && a.min_count >= a.r.L && (a.r.H / a.r.G) % HC == 0)
+        return launch_hc<P, N, SIN, COPY, WM, HC>(a, s);
+    return launch_hc<P, N, SIN, COPY, WM, 1>(a, s);
 }
 
 template <int P, int N>
