@@ -71,6 +71,20 @@ def step_bytes(w, count, fold, io=2):
             + B * ((count - 1) * per_entry + 2 * token + H * P * 4))
 
 
+def verify_step_bytes(w, before, W, io=2):
+    """One fused verify-round launch; `before` = ring counts per sequence at
+    the start of the round (a sequence with count >= L-W+1 folds first: its
+    checkpoint is written and its entries read by the fold; otherwise they
+    are read by the ring term).  The drafts are read from the inputs and
+    written to the ring."""
+    B, H, G, P, N, L = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len
+    per_entry = H * P * io + H * 8 + G * N * io
+    token = H * P * io + H * 8 + 2 * G * N * io
+    folds = int(np.sum(before >= L - W + 1))
+    return (state_bytes(w) * (1 + folds / B)
+            + float(np.sum(before)) * per_entry + B * (2 * W * token + W * H * P * 4))
+
+
 def eager_bytes(w, io=2):
     B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
     return 2 * state_bytes(w) + B * (H * P * io + H * 8 + 2 * G * N * io + H * P * 4)
@@ -330,7 +344,8 @@ def _events(n):
 def bench_verify(args):
     """Speculative verify: B=256, H=64, G=8, P=64, N=128, L=16, W=5 drafts per
     round, accepted drafts ~ Uniform{0..5}; each round = flush(L-W+1),
-    append(W), verify(W), rollback(W - accepted).  The eager baseline drafts
+    append(W), verify(W) (one fused launch with --api step, three launches
+    with --api calls), then rollback(W - accepted).  The eager baseline drafts
     with W per-token steps into snapshots and restores the accepted one."""
     import torch
     import linear_attention_decode_amd as lad
@@ -348,13 +363,22 @@ def bench_verify(args):
     stream = torch.cuda.current_stream()
 
     def round_(r, ev=None):
-        layer.flush(L - W + 1)
-        layer.append(W, win["q"][r], win["k"][r], win["v"][r], win["dt"][r], win["a"][r])
-        if ev is not None:
-            ev[0].record(stream)
-        layer.verify(W, y)
-        if ev is not None:
-            ev[1].record(stream)
+        drafts = (win["q"][r], win["k"][r], win["v"][r], win["dt"][r], win["a"][r])
+        if args.api == "step":
+            # one fused launch: fold if due, append the drafts, score them
+            if ev is not None:
+                ev[0].record(stream)
+            layer.verify_step(W, *drafts, y, flush_at=L - W + 1)
+            if ev is not None:
+                ev[1].record(stream)
+        else:
+            layer.flush(L - W + 1)
+            layer.append(W, *drafts)
+            if ev is not None:
+                ev[0].record(stream)
+            layer.verify(W, y)
+            if ev is not None:
+                ev[1].record(stream)
         layer.rollback(nrej[r])
 
     for r in range(WU):
@@ -368,9 +392,15 @@ def bench_verify(args):
     el = time.perf_counter() - t0
     assert layer.get_error()[0] == 0
     ver_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    # counts at verify time (ring model, host side)
-    from_model = _verify_counts(B, L, W, acc_np)
-    vbytes = sum(float(np.mean([decode_bytes(w, c, W) / B for c in from_model[WU + k]])) * B for k in range(R))
+    # ring counts at the start of every round and at verify time (host side)
+    before, at_verify = _verify_counts(B, L, W, acc_np)
+    if args.api == "step":
+        vbytes = sum(verify_step_bytes(w, before[WU + k], W) for k in range(R))
+        kernel_name = "verify round (fold if due + append + verify, W=5)"
+    else:
+        vbytes = sum(float(np.mean([decode_bytes(w, c, W) / B for c in at_verify[WU + k]])) * B
+                     for k in range(R))
+        kernel_name = "verify (W=5)"
     achieved = vbytes / (sum(ver_ms) / 1e3) / 1e9
     layer.close()
     del layer
@@ -406,11 +436,12 @@ def bench_verify(args):
         "ms_per_step": 1e3 * el / R, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic (seeded), accepted drafts ~ Uniform{0..5}",
         "config": {"workload": "speculative verify, one SSM layer", "batch": B, "heads": H, "groups": G,
-                   "head_dim": P, "state_dim": N, "ring_len": L, "window": W, "rounds": R},
+                   "head_dim": P, "state_dim": N, "ring_len": L, "window": W, "rounds": R, "api": args.api},
         "accepted_tokens_per_s": acc_total / el,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "verify (W=5)",
-                     "avg_launch_us": 1e3 * sum(ver_ms) / len(ver_ms)},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kernel_name,
+                     "avg_launch_us": 1e3 * sum(ver_ms) / len(ver_ms),
+                     "algorithmic_bytes_per_launch": vbytes / R},
         "eager": {"positions_per_s": B * W * R / eel, "accepted_tokens_per_s": acc_total / eel,
                   "ms_per_round": 1e3 * eel / R},
         "speedup_vs_eager": eel / el,
@@ -419,16 +450,17 @@ def bench_verify(args):
 
 
 def _verify_counts(B, L, W, acc):
-    """Ring counts at verify time for every round and sequence: each round
-    folds a ring holding at least L-W+1 entries, appends W drafts, verifies,
-    then drops the W - accepted rejected drafts."""
+    """Ring counts of every round and sequence, at the round's start and at
+    verify time: each round folds a ring holding at least L-W+1 entries,
+    appends W drafts, verifies, then drops the W - accepted rejected drafts."""
     c = np.zeros(B, dtype=np.int64)
-    out = []
+    before, at_verify = [], []
     for r in range(acc.shape[0]):
+        before.append(c.copy())
         c = np.where(c >= L - W + 1, 0, c) + W
-        out.append(c.copy())
+        at_verify.append(c.copy())
         c = c - (W - acc[r])
-    return out
+    return before, at_verify
 
 
 def _tok_err(y, ref):
@@ -590,7 +622,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["decode", "verify", "dual", "stacked"])
     ap.add_argument("--quick", action="store_true", help="dual/stacked: one variant only")
     ap.add_argument("--api", default="step", choices=["step", "calls"],
-                    help="step: one fused replay_step launch per step; calls: append, decode, flush")
+                    help="step: one fused launch per decode step (replay_step) or verify round "
+                         "(replay_verify_step); calls: the append, decode/verify and flush kernels")
     ap.add_argument("--read", default="f32", choices=["f32", "bf16", "fp8"],
                     help="checkpoint the outputs read: the float32 master or a bf16 / e4m3 copy")
     ap.add_argument("--no-cpu-baseline", action="store_true")

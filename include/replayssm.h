@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define REPLAY_ABI_VERSION 4
+#define REPLAY_ABI_VERSION 5
 
 typedef enum {
     REPLAY_OK = 0,
@@ -206,6 +206,30 @@ replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream);
    (the sequence is unchanged and its y is NaN). */
 replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v,
                           const float *dt, const float *a, float *y, int32_t flush_at, void *stream);
+
+/* One speculative-verify round for every sequence: where the ring holds
+   count >= max(flush_at, 1) entries, fold it into the checkpoint first; then
+   append the W drafts and produce their W outputs against one read of the
+   checkpoint (page "ReplaySSM: Cachear Inputs, No Estado", section
+   "Paralelismo": every draft of the window reads the same checkpoint and
+   buffer, entry j visible to draft t when j <= t; "Decodificacion
+   estandar", step 4, for the fold; section "Rollback": the caller then
+   drops rejected drafts with replay_rollback).  flush_at = L - W + 1 folds
+   exactly when the drafts would not fit otherwise.
+   Equivalent to replay_flush(flush_at); replay_append(W); replay_verify(W),
+   bit for bit.  q, k: [B][W][G][N]; v: [B][W][H][P] (io dtype); dt, a:
+   [B][W][H] f32; y: [B][W][H][P] f32, draft w at [b][w].  1 <= W <= min(8, L).
+   With a float32 checkpoint read, bf16 io and L <= 16 it is one kernel
+   launch that reads each checkpoint once and writes it only where it folds;
+   otherwise it runs the flush, append and verify kernels in turn.  A
+   sequence whose drafts do not fit after the fold (count + W > L with
+   count < flush_at) or whose pointer would pass 2^31 - 1 gets RING_OVERFLOW
+   or POS_OVERFLOW, is left unchanged and its y is NaN (in the single-launch
+   case; the calls in turn leave the verify outputs of such a sequence to
+   replay_verify's rules). */
+replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, const void *k,
+                                 const void *v, const float *dt, const float *a, float *y,
+                                 int32_t flush_at, void *stream);
 
 /* Synchronise `stream`, copy the error bits to the host and clear them on the
    device.  *word = OR over sequences; per_seq (may be NULL): host int32 [B]. */

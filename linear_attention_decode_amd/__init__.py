@@ -20,7 +20,8 @@ __all__ = [
     "SEQERR_TOO_FEW", "SEQERR_POS_OVERFLOW", "EXPORTS",
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
-    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_get_error",
+    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_verify_step",
+    "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 ]
 
@@ -33,7 +34,8 @@ SEQERR_RING_OVERFLOW, SEQERR_ROLLBACK_RANGE, SEQERR_TOO_FEW, SEQERR_POS_OVERFLOW
 EXPORTS = (
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
-    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_get_error",
+    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_verify_step",
+    "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 )
 
@@ -78,6 +80,7 @@ def _load():
     L.replay_rollback.argtypes = [_VP, _VP, _VP]
     L.replay_flush.argtypes = [_VP, _I32, _VP]
     L.replay_step.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
+    L.replay_verify_step.argtypes = [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
     L.replay_get_error.argtypes = [_VP, ctypes.POINTER(_I32), _VP, _VP]
     L.replay_eager_step.argtypes = [ctypes.POINTER(ReplayConfig)] + [_VP] * 9
     L.replay_eager_select.argtypes = [ctypes.POINTER(ReplayConfig), _VP, _I32, _VP, _VP, _VP]
@@ -169,6 +172,11 @@ def replay_flush(h, min_count, stream=None):
 def replay_step(h, q, k, v, dt, a, y, flush_at, stream=None):
     _check(lib.replay_step(h, _ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a), _ptr(y), flush_at,
                            _stream(stream)), "replay_step")
+
+
+def replay_verify_step(h, W, q, k, v, dt, a, y, flush_at, stream=None):
+    _check(lib.replay_verify_step(h, W, _ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a), _ptr(y), flush_at,
+                                  _stream(stream)), "replay_verify_step")
 
 
 def replay_get_error(h, batch: int, stream=None):
@@ -267,6 +275,11 @@ class ReplayLayer:
 
     def step(self, q, k, v, dt, a, y, flush_at=None, stream=None):
         replay_step(self.h, q, k, v, dt, a, y, self.cfg.ring_len if flush_at is None else flush_at, stream)
+
+    def verify_step(self, W, q, k, v, dt, a, y, flush_at=None, stream=None):
+        """Fold if due (count >= flush_at, default L - W + 1), append W drafts, score them."""
+        fa = self.cfg.ring_len - W + 1 if flush_at is None else flush_at
+        replay_verify_step(self.h, W, q, k, v, dt, a, y, fa, stream)
 
     def load_checkpoint(self, s_src, stream=None):
         replay_load_checkpoint(self.h, s_src, stream)

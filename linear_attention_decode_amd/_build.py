@@ -21,11 +21,11 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(HERE, "..", "include")]
 
 
-# Per-file extra flags.  step.hip, flush.hip: one lane per workgroup adds to
-# an arrival counter and needs the old value only at its very end; the atomic
+# Per-file extra flags.  step.hip, verify_step.hip, flush.hip: one lane per
+# workgroup adds to an arrival counter and needs the old value only at its very end; the atomic
 # optimizer would rewrite that add into a wave-wide form whose readfirstlane
 # waits for the atomic where it is issued.
-EXTRA = {f: ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"] for f in ("step.hip", "flush.hip")}
+EXTRA = {f: ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"] for f in ("step.hip", "verify_step.hip", "flush.hip")}
 
 
 def _hipcc() -> str:

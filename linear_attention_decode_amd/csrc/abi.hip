@@ -259,21 +259,9 @@ replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream) {
     return run_flush(h, nullptr, min_count, as_stream(stream));
 }
 
-replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v, const float *dt,
-                          const float *a, float *y, int32_t flush_at, void *stream) {
-    if (!h || !q || !k || !v || !dt || !a || !y) return REPLAY_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a) || !aligned4(y))
-        return REPLAY_ERR_INVALID_ARG;
+static StepArgs step_args(replay_handle *h, const void *q, const void *k, const void *v, const float *dt,
+                          const float *a, float *y, int32_t flush_at, int32_t W) {
     const replay_config &c = h->cfg;
-    hipStream_t s = as_stream(stream);
-    if (c.read_copy != REPLAY_NONE) {
-        // copies: the append, decode and flush kernels in turn
-        replay_status st = replay_append(h, 1, q, k, v, dt, a, stream);
-        if (st != REPLAY_OK) return st;
-        st = run_verify(h, 1, y, s);
-        if (st != REPLAY_OK) return st;
-        return run_flush(h, nullptr, flush_at, s);
-    }
     StepArgs sa;
     sa.ring_q = h->bufs.ring_q;
     sa.ring_k = h->bufs.ring_k;
@@ -297,7 +285,47 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
     sa.L = c.ring_len;
     sa.flush_at = flush_at;
     sa.io_bf16 = c.io_dtype == REPLAY_BF16;
+    sa.W = W;
+    return sa;
+}
+
+replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v, const float *dt,
+                          const float *a, float *y, int32_t flush_at, void *stream) {
+    if (!h || !q || !k || !v || !dt || !a || !y) return REPLAY_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a) || !aligned4(y))
+        return REPLAY_ERR_INVALID_ARG;
+    const replay_config &c = h->cfg;
+    hipStream_t s = as_stream(stream);
+    if (c.read_copy != REPLAY_NONE) {
+        // copies: the append, decode and flush kernels in turn
+        replay_status st = replay_append(h, 1, q, k, v, dt, a, stream);
+        if (st != REPLAY_OK) return st;
+        st = run_verify(h, 1, y, s);
+        if (st != REPLAY_OK) return st;
+        return run_flush(h, nullptr, flush_at, s);
+    }
+    const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, 1);
     return from_hip(launch_step(c.head_dim, c.state_dim, sa, s));
+}
+
+replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
+                                 const float *dt, const float *a, float *y, int32_t flush_at, void *stream) {
+    if (!h || !q || !k || !v || !dt || !a || !y) return REPLAY_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a) || !aligned4(y))
+        return REPLAY_ERR_INVALID_ARG;
+    const replay_config &c = h->cfg;
+    if (W < 1 || W > 8 || W > c.ring_len) return REPLAY_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, W);
+    if (c.read_copy != REPLAY_NONE || !verify_step_fused(c.head_dim, c.state_dim, sa)) {
+        // the flush, append and verify kernels in turn
+        replay_status st = run_flush(h, nullptr, flush_at, s);
+        if (st != REPLAY_OK) return st;
+        st = replay_append(h, W, q, k, v, dt, a, stream);
+        if (st != REPLAY_OK) return st;
+        return run_verify(h, W, y, s);
+    }
+    return from_hip(launch_verify_step(c.head_dim, c.state_dim, sa, s));
 }
 
 replay_status replay_get_error(replay_handle *h, int32_t *word, int32_t *per_seq, void *stream) {

@@ -322,7 +322,9 @@ __global__ __launch_bounds__((DecodeLaunch<P, N, ST, WM, LM, IOB, HPW>::NT)) voi
         }
         RR::template run<WM>(part, lane);
     } else {
-        const int rwave = (tid - NTS) >> 6;          // ring wavefront: head hl, 16-entry block blk
+        // ring wavefront: head hl, 16-entry block blk (wave-uniform, so the
+        // buffer descriptors built from it stay in scalar registers)
+        const int rwave = __builtin_amdgcn_readfirstlane((tid - NTS) >> 6);
         const int hl = rwave / NR, blk = rwave % NR;
         const size_t bh = bh0 + hl;
         if constexpr (IOB)

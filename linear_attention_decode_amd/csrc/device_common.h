@@ -161,9 +161,17 @@ struct IoVec<false, 4> {
 // in a scalar register, so a wavefront that reads many rows of one region
 // keeps a single address register instead of a 64-bit address per load.
 // Offsets at or past `bytes` read zero.  Word 3 is the gfx9-family setting
-// for untyped (raw) buffer access.
+// for untyped (raw) buffer access.  `base` and `bytes` must be the same in
+// every lane: they are taken from the first active lane, so the descriptor
+// is built in scalar registers even where the compiler cannot prove the
+// address uniform (it would otherwise wrap each load in a loop over the
+// lanes' distinct descriptors).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *ub = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 template <>

@@ -56,18 +56,20 @@ struct FlushArgs {
     int32_t *sync;          // arrival counters [B][G + 1][kSyncStride]
 };
 
-// One fused standard decode step (float32 checkpoint).
+// One fused standard decode step (W = 1) or speculative-verify round
+// (W drafts), float32 checkpoint.
 struct StepArgs {
     void *ring_q, *ring_k, *ring_v;   // [B][G][L][N] x2, [B][H][L][P]
     float *ring_dt, *ring_a;          // [B][H][L]
     int32_t *pos, *base, *err, *sync;  // sync: [B][G + 1][kSyncStride], element [..][0]
     float *S;                         // [B][H][P][N] master, read and (when folding) written
-    const void *q, *k, *v;            // [B][G][N] x2, [B][H][P]
-    const float *dt, *a;              // [B][H]
-    float *y;                         // [B][H][P]
+    const void *q, *k, *v;            // [B][W][G][N] x2, [B][W][H][P]
+    const float *dt, *a;              // [B][W][H]
+    float *y;                         // [B][W][H][P]
     int32_t B, H, G, L;
     int32_t flush_at;
     int32_t io_bf16;
+    int32_t W;                        // drafts per round (the verify round; the step takes 1)
 };
 
 struct EagerArgs {
@@ -91,6 +93,8 @@ hipError_t launch_rollback(const RingView &r, int32_t *pos, const int32_t *n_rej
 hipError_t launch_fill_u32(void *dst, uint32_t value, size_t count, hipStream_t s);
 hipError_t launch_eager(int P, int N, const EagerArgs &a, hipStream_t s);
 hipError_t launch_step(int P, int N, const StepArgs &a, hipStream_t s);
+hipError_t launch_verify_step(int P, int N, const StepArgs &a, hipStream_t s);
+bool verify_step_fused(int P, int N, const StepArgs &a);   // the fused round covers this case
 hipError_t launch_eager_select(const float *snaps, int32_t W, const int32_t *n_accept, float *s,
                                int32_t B, size_t head_elems_per_seq, hipStream_t st);
 hipError_t launch_probe(int mode, const void *src, void *dst, size_t bytes, hipStream_t s);

@@ -1,0 +1,482 @@
+// verify_step.hip -- one fused speculative-verify round for a float32
+// checkpoint with bf16 io.
+//
+// For every (sequence, head), in one launch:
+//   1. where the ring holds count >= max(flush_at, 1) entries, fold them into
+//      the checkpoint by the state-and-output route (page "ReplaySSM: Cachear
+//      Inputs, No Estado", section "Los dos caminos", eq. "Ruta estado y
+//      salida"):  S_new = abar_c S0 + sum_j s_{j,c} v_j k_j^T, written back
+//      once, and base = pos;
+//   2. append the W drafts at ring positions pos .. pos+W-1;
+//   3. score the drafts t_w = count'-W+w by the output-only route (eq. "Ruta
+//      solo salida"; section "Paralelismo": every draft reads the same
+//      checkpoint and buffer, entry j is visible to draft t when j <= t):
+//        y_w = abar_{t_w} (S q_w) + sum_{j<=t_w} s_{j,t_w} v_j (k_j . q_w),
+//      with S the checkpoint just read or just folded.
+// The results equal those of the flush, append and verify kernels run in
+// turn, bit for bit; the checkpoint is read once per round and written only
+// where it folds.
+//
+// Workgroup = the streaming wavefronts of the fused step (the head's tile in
+// 16-byte chunks, S q_w for every draft) + 2 ring wavefronts:
+//   term wavefront   group dots and ring term of the window on the matrix
+//                    cores (ring_mx.h); entries kept from before the round
+//                    come from the ring, the drafts from the inputs;
+//   fold wavefront   the fold's segment weights and its s_j v_j / k_j staging
+//                    in LDS, and the drafts' per-head ring entries (v, dt, a).
+// Draft w goes to ring slot (pos + w) mod L.  When the ring folds, those slots
+// can hold entries the fold still reads.  The fold wavefront reads the per-head
+// entries before it writes the drafts' ones.  The group-shared q/k rows, which
+// every head's fold wavefront reads, are written by the group's last ring
+// wavefront to arrive; each ring wavefront arrives only once its loads have
+// returned.  The pointer moves when the sequence's last group arrives.
+#include "step_common.h"
+
+namespace replay {
+
+constexpr int kVsRing = 16;   // ring entries covered by one term wavefront (L <= 16)
+
+// Term wavefront.  Entry j < keep is ring entry j; entry keep + d is draft d
+// (keep = 0 when the ring folds).  Entries past the window are clamped to the
+// newest draft, as the verify kernel clamps them to the newest ring entry, so
+// the matrix-core sums equal that kernel's bit for bit.
+template <int P, int N, int W>
+__device__ __forceinline__ int vs_term_wave(const StepArgs &A, int lane, int b, int g, int h, size_t bh,
+                                            int base, int keep, float (*s_r)[P], float *s_abar,
+                                            float (*s_sw)[kVsRing]) {
+    using MX = MxRing<P, N, W, kVsRing>;
+    constexpr uint32_t ES = 2;
+    const int L = A.L, H = A.H, G = A.G, count = keep + W;
+    const size_t gring = ((size_t)b * G + g) * L;
+    const size_t hring = bh * L;
+    const int bmod = base % L;
+    auto slot = [&](int j) { return ring_slot(bmod, j, L); };
+    auto draft = [&](int j) {
+        const int d = j - keep;
+        return d < 0 ? 0 : (d < W ? d : W - 1);
+    };
+    const int lastr = keep > 0 ? keep - 1 : 0;   // clamp for ring loads (unused when keep == 0)
+    const int lr = lane & 15, lq = lane >> 4;
+
+    MX m;
+    m.j0 = 0;
+    {
+        const bool old = lane < keep;
+        const size_t i = old ? hring + slot(lane) : ((size_t)b * W + draft(lane)) * H + h;
+        m.aj = (old ? A.ring_a : A.a)[i];
+        m.dtj = (old ? A.ring_dt : A.dt)[i];
+    }
+#pragma unroll
+    for (int kb = 0; kb < MX::KB; ++kb) {
+        const int c = MX::col(kb, lane);
+        const bool old = lr < keep;
+        const uint16_t *krow = old ? static_cast<const uint16_t *>(A.ring_k) + (gring + slot(lr)) * N
+                                   : static_cast<const uint16_t *>(A.k) + (((size_t)b * W + draft(lr)) * G + g) * N;
+        m.ka[kb] = *reinterpret_cast<const uint4 *>(krow + c);
+        const int w = lr < W ? lr : W - 1;
+        m.qb[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(A.q) +
+                                                    (((size_t)b * W + w) * G + g) * N + c);
+    }
+    // v pairs: one load from the ring and one from the drafts, selected per entry
+    const auto rres = make_rsrc(static_cast<const char *>(A.ring_v) + hring * P * ES, (uint32_t)(L * P * ES));
+    const auto ires = make_rsrc(static_cast<const char *>(A.v) + ((size_t)b * W * H + h) * P * ES,
+                                (uint32_t)(((W - 1) * H + 1) * P * ES));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const int j = 4 * lq + kk;
+        const bool old = j < keep;
+        const uint32_t rrow = (uint32_t)slot(old ? j : lastr) * P;
+        const uint32_t irow = (uint32_t)(draft(j) * H) * P;
+#pragma unroll
+        for (int pw = 0; pw < MX::PW; ++pw) {
+            const uint32_t e = 2 * MX::vword(pw, lane);
+            const uint32_t wr = __builtin_amdgcn_raw_buffer_load_b32(rres, (rrow + e) * ES, 0, 0);
+            const uint32_t wi = __builtin_amdgcn_raw_buffer_load_b32(ires, (irow + e) * ES, 0, 0);
+            m.vw[kk][pw] = old ? wr : wi;
+        }
+    }
+    // Arrival.  This wavefront reads no ring slot a draft is written to
+    // while it matters: entries < keep lie before the drafts' slots (keep + W
+    // <= L), and with keep == 0 the clamped ring values are not used.
+    int prev = -1;
+    if (lane == 0) prev = atomicAdd(&A.sync[((size_t)b * (G + 1) + g) * kSyncStride], 1);
+    // the workgroup's first barrier, with this wavefront's loads in flight
+    // (the scheduling barrier keeps the work on the loaded values below it,
+    // so the wavefront does not wait for them before the barrier)
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (lane >= count) {
+        m.aj = 1.f;
+        m.dtj = 0.f;
+    }
+    const f32x4 dk = m.dots(lane);
+    m.weights(lane, count, s_abar, s_sw);
+    m.term(lane, dk, s_r, s_sw);
+    return prev;
+}
+
+// Fold wavefront: the drafts' per-head ring entries, and (when folding) the
+// c = cold entries' segment weights, s_fabar = abar_c, U[p][j] = s_{j,c} v_j[p]
+// and K[j][n] = k_j[n], in the flush kernel's order of operations.
+template <int P, int N, int W>
+__device__ __forceinline__ int vs_fold_wave(const StepArgs &A, int lane, int b, int g, int h, size_t bh, int base,
+                                            int pos, int cold, bool fold, float *s_fabar,
+                                            float (*s_U)[kVsRing + 1], float (*s_K)[N]) {
+    constexpr int LM = kVsRing;
+    constexpr int TS = N / 8;
+    constexpr int RPW = 64 / TS;
+    constexpr int KI = (LM + RPW - 1) / RPW;
+    constexpr int VR = (P + 63) / 64;
+    constexpr int VWORDS = W * P / 2, VWPL = (VWORDS + 63) / 64;
+    constexpr uint32_t ES = 2;
+    const int L = A.L, H = A.H, G = A.G;
+    const size_t gring = ((size_t)b * G + g) * L;
+    const size_t hring = bh * L;
+    const int bmod = base % L, pmod = pos % L;
+    auto slot = [&](int j) { return ring_slot(bmod, j, L); };
+    const int c = fold ? cold : 0;
+    const int lastr = c > 0 ? c - 1 : 0;
+    const int tl = lane % TS, te = lane / TS;
+
+    // the drafts' v rows (as words) and dt, a
+    uint32_t vd[VWPL];
+#pragma unroll
+    for (int i = 0; i < VWPL; ++i) {
+        const int idx = lane + 64 * i < VWORDS ? lane + 64 * i : VWORDS - 1;
+        const int w = idx / (P / 2), wd = idx % (P / 2);
+        vd[i] = static_cast<const uint32_t *>(A.v)[(((size_t)b * W + w) * H + h) * (P / 2) + wd];
+    }
+    const int wl = lane < W ? lane : W - 1;
+    const float a_d = A.a[((size_t)b * W + wl) * H + h], dt_d = A.dt[((size_t)b * W + wl) * H + h];
+
+    // the folded entries (clamped to valid ones; values past c are not used)
+    float aj = 1.f, dtj = 0.f;
+    IoVec<true, 8> kraw[KI];
+    IoVec<true, 1> vraw[VR][LM];
+    if (fold) {
+        const int sl = slot(lane < c ? lane : lastr);
+        aj = A.ring_a[hring + sl];
+        dtj = A.ring_dt[hring + sl];
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+            const int j = i * RPW + te;
+            kraw[i].load(A.ring_k, (gring + slot(j < c ? j : lastr)) * N + tl * 8);
+        }
+        const auto vres = make_rsrc(static_cast<const char *>(A.ring_v) + hring * P * ES, (uint32_t)(L * P * ES));
+#pragma unroll
+        for (int rr = 0; rr < VR; ++rr) {
+            const uint32_t voff = ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1) * ES;
+#pragma unroll
+            for (int j = 0; j < LM; ++j)
+                vraw[rr][j].load_buf(vres, voff, (uint32_t)slot(j < c ? j : lastr) * P * ES);
+        }
+    }
+    // the workgroup's first barrier, with this wavefront's loads in flight
+    // (the scheduling barrier keeps the work on the loaded values below it,
+    // so the wavefront does not wait for them before the barrier)
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // Every load above has returned before this wavefront arrives or writes:
+    // the drafts' slots can hold folded entries, and the group's last arrival
+    // overwrites the q/k rows read here.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int prev = -1;
+    if (lane == 0) prev = atomicAdd(&A.sync[((size_t)b * (G + 1) + g) * kSyncStride], 1);
+
+    // the drafts' per-head entries into slots (pos + w) mod L
+#pragma unroll
+    for (int i = 0; i < VWPL; ++i) {
+        const int idx = lane + 64 * i;
+        if (idx < VWORDS) {
+            const int w = idx / (P / 2), wd = idx % (P / 2);
+            static_cast<uint32_t *>(A.ring_v)[(hring + ring_slot(pmod, w, L)) * (P / 2) + wd] = vd[i];
+        }
+    }
+    if (lane < W) {
+        A.ring_dt[hring + ring_slot(pmod, lane, L)] = dt_d;
+        A.ring_a[hring + ring_slot(pmod, lane, L)] = a_d;
+    }
+
+    if (fold) {
+        float prod = dtj, run = 1.f, sw = 0.f, ab = 0.f;
+#pragma unroll
+        for (int m = 0; m < LM; ++m) {
+            if (m < c) {
+                const float am = bcast(aj, m);
+                if (m > lane) prod *= am;
+                run *= am;
+                if (m == c - 1) {
+                    sw = prod;
+                    ab = run;
+                }
+            }
+        }
+        if (lane == 0) *s_fabar = ab;
+#pragma unroll
+        for (int j = 0; j < LM; ++j) {
+            if (j < c) {
+                const float sj = bcast(sw, j);
+#pragma unroll
+                for (int rr = 0; rr < VR; ++rr)
+                    if (lane + 64 * rr < P) s_U[lane + 64 * rr][j] = sj * vraw[rr][j].value();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+            const int j = i * RPW + te;
+            if (j < c) {
+                float kk[8];
+                kraw[i].widen(kk);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s_K[j][tl * 8 + e] = kk[e];
+            }
+        }
+    }
+    return prev;
+}
+
+// Waves per SIMD to ask the register allocator for: 8 (64 registers) for the
+// 64 x 128 tile, which then fits with a few spilled words (measured faster
+// than 67 registers at 7 waves); the other tiles fit or spill too much.
+template <int P, int N>
+constexpr int vs_waves() { return P == 64 && N == 128 ? 8 : 1; }
+
+template <int P, int N, int W>
+__global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu_waves_per_eu(vs_waves<P, N>()))) void verify_step_kernel(StepArgs args) {
+    using Sh = StepShape<P, N>;
+    constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+    constexpr int LM = kVsRing;
+    using RR = RowReduce<ITER, LPR>;
+
+    __shared__ float s_r[W][P];
+    __shared__ float s_abar[W];
+    __shared__ __align__(16) float s_sw[W][LM];
+    __shared__ float s_U[P][LM + 1];
+    __shared__ __align__(16) float s_K[LM][N];
+    __shared__ __align__(16) float s_q[W][N];   // the drafts' queries, widened
+    __shared__ float s_fabar;
+    __shared__ int s_route;   // 0 keep the ring, 1 fold first, 2 error (sequence left unchanged)
+    __shared__ int s_fcount;
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int H = args.H, G = args.G, L = args.L;
+    // (wave-uniform: the buffer descriptors built from them stay scalar)
+    const int b = __builtin_amdgcn_readfirstlane(lid / H), h = __builtin_amdgcn_readfirstlane(lid % H);
+    const int g = (h * G) / H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform role (scalar branches; the ring wavefronts' pointer reads
+    // go through the scalar cache)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool streamer = wave < NTS / 64;
+    const int rw = wave - NTS / 64;
+    const size_t bh = (size_t)b * H + h;
+    const size_t tile = bh * (size_t)(P * N);
+    const int col0 = (tid % LPR) * VEC;
+
+    // Only the ring wavefronts read the pointer (each arrives after its
+    // read).  They publish the route in LDS at a first barrier, which the
+    // streaming wavefronts reach with their tile loads in flight; knowing the
+    // route before the sums lets the route without a fold release each tile
+    // chunk as it is used.  The two roles run in disjoint branches (each
+    // with both barriers), so neither role's registers are live in the
+    // other's code.
+    if (streamer) {
+        using Fin = float[RR::FINAL][W];
+        // The drafts' queries, widened into LDS (published by the first
+        // barrier).  They are loaded before the tile: loads complete in
+        // order, so the wait for them before the LDS write does not wait for
+        // the tile, and the first barrier is not held up by it.
+        constexpr int QP = W * N / 4;   // 4-element pieces
+        constexpr int QI = (QP + NTS - 1) / NTS;
+        IoVec<true, 4> qraw[QI];
+#pragma unroll
+        for (int i = 0; i < QI; ++i) {
+            const int piece = tid + i * NTS < QP ? tid + i * NTS : QP - 1;
+            const int w = piece / (N / 4), c = (piece % (N / 4)) * 4;
+            qraw[i].load(args.q, (((size_t)b * W + w) * G + g) * N + c);
+        }
+        // (the empty asm keeps the compiler from moving the query loads
+        // past the tile loads; lanes past the last piece repeat it, so the
+        // loads and LDS writes are unconditional and stay in place)
+        asm volatile("" ::: "memory");
+        Chunk<ST_F32, VEC> ch[ITER];
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
+#pragma unroll
+        for (int i = 0; i < QI; ++i) {
+            const int piece = tid + i * NTS < QP ? tid + i * NTS : QP - 1;
+            const int w = piece / (N / 4), c = (piece % (N / 4)) * 4;
+            float qf[4];
+            qraw[i].widen(qf);
+            *reinterpret_cast<f32x4 *>(&s_q[w][c]) = f32x4{qf[0], qf[1], qf[2], qf[3]};
+        }
+        // S q_w for every draft, one draft at a time (each draft's partial
+        // sums reduced before the next draft's are formed)
+        auto sums = [&](const auto &tile_chunk, Fin &fin) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const f32x4 qw = *reinterpret_cast<const f32x4 *>(&s_q[w][col0]);
+                float part[ITER][1];
+#pragma unroll
+                for (int i = 0; i < ITER; ++i) {
+                    float x[VEC];
+                    tile_chunk(i, x);
+                    float acc = 0.f;
+                    acc = fmaf(x[0], qw.x, acc);
+                    acc = fmaf(x[1], qw.y, acc);
+                    acc = fmaf(x[2], qw.z, acc);
+                    acc = fmaf(x[3], qw.w, acc);
+                    part[i][0] = acc;
+                }
+                RR::template run<1>(part, lane);
+#pragma unroll
+                for (int e = 0; e < RR::FINAL; ++e) fin[e][w] = part[e][0];
+            }
+        };
+        Fin fin;
+        lds_barrier();
+        const int route = s_route;
+        if (route == 0) sums([&](int i, float *x) { ch[i].widen(x, 1.0f); }, fin);
+        lds_barrier();
+        if (route == 2) {
+            for (int i = tid; i < W * P; i += NTS)
+                args.y[(((size_t)b * W + i / P) * H + h) * P + i % P] = __builtin_nanf("");
+            return;
+        }
+        if (route == 1) {
+            // fold: S_new = abar_c S0 + sum_j U[row][j] K[j][col], written once
+            const float abar = s_fabar;
+            float x[ITER][VEC];
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                ch[i].widen(x[i], 1.0f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) x[i][e] *= abar;
+            }
+            const int c = s_fcount;
+#pragma unroll 1   // keeps the LDS operands of one entry in registers at a time
+            for (int j = 0; j < c; ++j) {
+                const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_K[j][col0]);
+#pragma unroll
+                for (int i = 0; i < ITER; ++i) {
+                    const float u = s_U[i * RPI + tid / LPR][j];
+                    x[i][0] = fmaf(u, kk.x, x[i][0]);
+                    x[i][1] = fmaf(u, kk.y, x[i][1]);
+                    x[i][2] = fmaf(u, kk.z, x[i][2]);
+                    x[i][3] = fmaf(u, kk.w, x[i][3]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                f32x4 o = {x[i][0], x[i][1], x[i][2], x[i][3]};
+                __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(args.S + tile + (size_t)(i * NTS + tid) * VEC));
+            }
+            sums([&](int i, float *xo) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) xo[e] = x[i][e];
+            }, fin);
+        }
+        if (RR::writer(lane)) {
+            const int hi = RR::halving_index(lane);
+#pragma unroll
+            for (int e = 0; e < RR::FINAL; ++e) {
+                const int row = (e + RR::FINAL * hi) * RPI + tid / LPR;
+#pragma unroll
+                for (int w = 0; w < W; ++w)
+                    args.y[(((size_t)b * W + w) * H + h) * P + row] = s_abar[w] * fin[e][w] + s_r[w][row];
+            }
+        }
+    } else {
+        const int base = args.base[b];
+        const int pos = args.pos[b];
+        const int cold = pos - base;
+        const int need = args.flush_at > 1 ? args.flush_at : 1;
+        const bool fold = cold >= need;
+        const int keep = fold ? 0 : cold;
+        const int err = keep + W > L ? REPLAY_SEQERR_RING_OVERFLOW
+                                     : ((long long)pos + W > 2147483647LL ? REPLAY_SEQERR_POS_OVERFLOW : 0);
+        if (rw == 0 && lane == 0) {
+            s_route = err ? 2 : (fold ? 1 : 0);
+            s_fcount = fold ? cold : 0;
+            if (err) raise_seq_error(args.err, b, err);
+        }
+        // the first barrier: inside the ring functions, once their loads are issued
+        int prev = -1;
+        if (err) {
+            lds_barrier();
+        } else {
+            if (rw == 0)
+                prev = vs_term_wave<P, N, W>(args, lane, b, g, h, bh, base, keep, s_r, s_abar, s_sw);
+            else
+                prev = vs_fold_wave<P, N, W>(args, lane, b, g, h, bh, base, pos, cold, fold, &s_fabar, s_U, s_K);
+        }
+        // LDS-only barrier: the ring writes and arrival atomics finish in the background
+        lds_barrier();
+        if (__shfl(prev, 0) == 2 * (H / G) - 1) {
+            // Last ring wavefront of the group to arrive: every ring wavefront
+            // of the group has read what it reads from the ring, so the
+            // drafts' q/k rows go into slots (pos + w) mod L now.  Then the
+            // group arrives at the sequence's counter; the last group moves
+            // the pointer.
+            const size_t gring = ((size_t)b * G + g) * L;
+            const int pmod = pos % L;
+            constexpr int RW = RowWords<N, true>::WORDS;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                RowWords<N, true> qrow, krow;
+                const size_t in = (((size_t)b * W + w) * G + g) * N * 2;
+                qrow.load(static_cast<const char *>(args.q) + in, lane);
+                krow.load(static_cast<const char *>(args.k) + in, lane);
+                const size_t off = (gring + ring_slot(pmod, w, L)) * (size_t)RW * 4;
+                qrow.store(static_cast<char *>(args.ring_q) + off, lane);
+                krow.store(static_cast<char *>(args.ring_k) + off, lane);
+            }
+            if (lane == 0) {
+                int32_t *seq = args.sync + (size_t)b * (G + 1) * kSyncStride;
+                atomicExch(seq + (size_t)g * kSyncStride, 0);
+                if (atomicAdd(seq + (size_t)G * kSyncStride, 1) == G - 1) {
+                    atomicExch(seq + (size_t)G * kSyncStride, 0);
+                    if (fold) args.base[b] = pos;
+                    args.pos[b] = pos + W;
+                }
+            }
+        }
+    }
+}
+
+template <int P, int N, int W>
+static hipError_t launch_vs(const StepArgs &a, hipStream_t s) {
+    const unsigned blocks = (unsigned)((size_t)a.B * a.H);
+    verify_step_kernel<P, N, W><<<blocks, StepShape<P, N>::NTS + 128, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int P, int N>
+static hipError_t launch_vs_w(const StepArgs &a, hipStream_t s) {
+    switch (a.W) {
+        case 1: return launch_vs<P, N, 1>(a, s);
+        case 2: return launch_vs<P, N, 2>(a, s);
+        case 3: return launch_vs<P, N, 3>(a, s);
+        case 4: return launch_vs<P, N, 4>(a, s);
+        case 5: return launch_vs<P, N, 5>(a, s);
+        case 6: return launch_vs<P, N, 6>(a, s);
+        case 7: return launch_vs<P, N, 7>(a, s);
+        case 8: return launch_vs<P, N, 8>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool verify_step_fused(int P, int N, const StepArgs &a) {
+    const bool shape = (P == 16 && N == 16) || (P == 64 && N == 64) || (P == 64 && N == 128) || (P == 128 && N == 128);
+    return shape && a.io_bf16 && a.L <= kVsRing && a.W >= 1 && a.W <= 8 && a.W <= a.L;
+}
+
+hipError_t launch_verify_step(int P, int N, const StepArgs &a, hipStream_t s) {
+    if (!verify_step_fused(P, N, a)) return hipErrorInvalidValue;
+    if (P == 16 && N == 16) return launch_vs_w<16, 16>(a, s);
+    if (P == 64 && N == 64) return launch_vs_w<64, 64>(a, s);
+    if (P == 64 && N == 128) return launch_vs_w<64, 128>(a, s);
+    return launch_vs_w<128, 128>(a, s);
+}
+
+}  // namespace replay

@@ -84,17 +84,22 @@ def errors(y_gpu: np.ndarray, y_ref: np.ndarray):
     return float(np.max(e_tok)), float(np.max(e_vec)), float(np.mean(e_vec))
 
 
-def run_verify(layer, w: synth.Workload, dev: DevInputs, R: int, W: int, accept: np.ndarray, model=None):
-    """Speculative rounds: flush(L-W+1); append(W drafts); verify(W);
+def run_verify(layer, w: synth.Workload, dev: DevInputs, R: int, W: int, accept: np.ndarray, model=None,
+               fused: bool = False):
+    """Speculative rounds: flush(L-W+1); append(W drafts); verify(W) -- as
+    three calls, or as one replay_verify_step with fused=True -- then
     rollback(W - accepted).  Round r drafts tokens rW..rW+W-1.
     Returns y [R][B][W][H][P] (device)."""
     B, H, P, L = w.batch, w.heads, w.head_dim, w.ring_len
     y = torch.empty((R, B, W, H, P), dtype=torch.float32, device=DEV)
     nrej = torch.from_numpy((W - accept).astype(np.int32)).to(DEV)
     for rd in range(R):
-        layer.flush(L - W + 1)
-        layer.append(W, *dev.window(rd * W, W))
-        layer.verify(W, y[rd])
+        if fused:
+            layer.verify_step(W, *dev.window(rd * W, W), y[rd], flush_at=L - W + 1)
+        else:
+            layer.flush(L - W + 1)
+            layer.append(W, *dev.window(rd * W, W))
+            layer.verify(W, y[rd])
         layer.rollback(nrej[rd])
         if model is not None:
             model.flush(L - W + 1)
