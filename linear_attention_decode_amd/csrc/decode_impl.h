@@ -24,8 +24,10 @@
 
 namespace replay {
 
-// NARROW: 8-element chunks for the low-precision tiles (several heads per
-// workgroup, where the register budget goes to the extra chunks in flight).
+// NARROW: 8-element chunks for the low-precision tiles of several heads per
+// workgroup with float32 io (the register budget goes to the extra chunks in
+// flight and to the widened queries).  With bf16 io the queries stay bf16
+// pairs, so full 16-byte chunks fit.
 template <int P, int N, int ST, int WM, bool NARROW = false>
 struct DecodeShape {
     static constexpr int base_vec = ST == ST_F32 ? 4
@@ -238,7 +240,7 @@ constexpr int heads_per_wg() { return (ST == ST_F32 || WM > 1) ? 1 : (ST == ST_B
 
 template <int P, int N, int ST, int WM, int LM, bool IOB, int HPW>
 struct DecodeLaunch {
-    using Sh = DecodeShape<P * HPW, N, ST, WM, (HPW > 1)>;
+    using Sh = DecodeShape<P * HPW, N, ST, WM, (HPW > 1 && !IOB)>;
     static constexpr int NR = ring_waves<LM, IOB>();      // ring wavefronts per head
     static constexpr int NT = Sh::NTS + 64 * NR * HPW;
 };
@@ -294,30 +296,63 @@ __global__ __launch_bounds__((DecodeLaunch<P, N, ST, WM, LM, IOB, HPW>::NT)) voi
         // queries of the window positions at this lane's columns
         const int col0 = (tid % LPR) * VEC;
         const size_t gring = ((size_t)b * r.G + g) * L;
-        IoVec<IOB, 4> qraw[WM][VEC / 4];
         const int bmod = base % L;
-#pragma unroll
-        for (int w = 0; w < WM; ++w) {
-            const size_t off = (gring + ring_slot(bmod, count - W + (w < W ? w : W - 1), L)) * N + col0;
-#pragma unroll
-            for (int e = 0; e < VEC / 4; ++e) qraw[w][e].load(r.q, off + 4 * e);
-        }
-        float qv[WM][VEC];
-#pragma unroll
-        for (int w = 0; w < WM; ++w)
-#pragma unroll
-            for (int e = 0; e < VEC / 4; ++e) qraw[w][e].widen(&qv[w][4 * e]);
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            float x[VEC];
-            ch[i].widen(x, 1.0f);
+        if constexpr (IOB && ST != ST_F32) {
+            // low-precision tile, bf16 queries: the queries stay bf16 pairs
+            // and every chunk goes to bf16 pairs (exact for bf16, e4m3 and
+            // E2M1 values), dotted by v_dot2_f32_bf16
+            constexpr int QW = VEC / 2;   // words of bf16 pairs per query
+            uint32_t qw[WM][QW];
 #pragma unroll
             for (int w = 0; w < WM; ++w) {
-                float acc = 0.f;
+                const uint32_t *row = reinterpret_cast<const uint32_t *>(
+                    static_cast<const uint16_t *>(r.q) +
+                    (gring + ring_slot(bmod, count - W + (w < W ? w : W - 1), L)) * N + col0);
+                if constexpr (QW % 4 == 0) {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) acc = fmaf(x[e], qv[w][e], acc);
-                if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
-                part[i][w] = acc;
+                    for (int e = 0; e < QW / 4; ++e) {
+                        const uint4 u = reinterpret_cast<const uint4 *>(row)[e];
+                        qw[w][4 * e] = u.x; qw[w][4 * e + 1] = u.y; qw[w][4 * e + 2] = u.z; qw[w][4 * e + 3] = u.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < QW; ++e) qw[w][e] = row[e];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+#pragma unroll
+                for (int w = 0; w < WM; ++w) {
+                    float acc = ch[i].dot_bf16(qw[w]);
+                    if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
+                    part[i][w] = acc;
+                }
+            }
+        } else {
+            IoVec<IOB, 4> qraw[WM][VEC / 4];
+#pragma unroll
+            for (int w = 0; w < WM; ++w) {
+                const size_t off = (gring + ring_slot(bmod, count - W + (w < W ? w : W - 1), L)) * N + col0;
+#pragma unroll
+                for (int e = 0; e < VEC / 4; ++e) qraw[w][e].load(r.q, off + 4 * e);
+            }
+            float qv[WM][VEC];
+#pragma unroll
+            for (int w = 0; w < WM; ++w)
+#pragma unroll
+                for (int e = 0; e < VEC / 4; ++e) qraw[w][e].widen(&qv[w][4 * e]);
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                float x[VEC];
+                ch[i].widen(x, 1.0f);
+#pragma unroll
+                for (int w = 0; w < WM; ++w) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc = fmaf(x[e], qv[w][e], acc);
+                    if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
+                    part[i][w] = acc;
+                }
             }
         }
         RR::template run<WM>(part, lane);

@@ -235,6 +235,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// a*b over a bf16 pair each (raw bits, element 0 in the low half) plus acc,
+// by the packed bf16 dot instruction (the products are exact in float32)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
+                                          false);
+}
+
+template <typename V>
+__device__ __forceinline__ uint32_t bf16_pair_bits(V v) { return __builtin_bit_cast(uint32_t, v); }
+
 // ---- state tile chunks ---------------------------------------------------
 // A chunk is VEC consecutive elements of one state row, loaded with one
 // vector load and widened to float.
@@ -274,6 +284,13 @@ struct Chunk<ST_BF16, VEC> {
             out[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
         }
     }
+    // sum_e x[e] q[e] with q given as VEC/2 words of bf16 pairs (element order)
+    __device__ __forceinline__ float dot_bf16(const uint32_t *q) const {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) acc = dot2_bf16(raw[i], q[i], acc);
+        return acc;
+    }
 };
 
 template <int VEC>
@@ -301,6 +318,19 @@ struct Chunk<ST_FP8, VEC> {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) out[i] *= scale;
     }
+    // sum_e code[e] q[e] (unscaled), q as VEC/2 words of bf16 pairs: each code
+    // pair goes to a bf16 pair (exact: e4m3 values are bf16 values)
+    __device__ __forceinline__ float dot_bf16(const uint32_t *q) const {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) {
+            acc = dot2_bf16(bf16_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i], 1.0f, false)),
+                            q[2 * i], acc);
+            acc = dot2_bf16(bf16_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[i], 1.0f, true)),
+                            q[2 * i + 1], acc);
+        }
+        return acc;
+    }
 };
 
 // Two E2M1 codes (byte `sel` of w) -> their float values (hardware conversion, scale 1).
@@ -314,6 +344,16 @@ __device__ __forceinline__ void fp4_pair_to_f32(uint32_t w, int sel, float *out)
     }
     out[0] = v[0];
     out[1] = v[1];
+}
+
+// Two E2M1 codes (byte `sel` of w) -> a bf16 pair (exact), as raw bits.
+__device__ __forceinline__ uint32_t fp4_pair_to_bf16(uint32_t w, int sel) {
+    switch (sel) {
+        case 0: return bf16_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+        case 1: return bf16_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+        case 2: return bf16_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+        default: return bf16_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+    }
 }
 
 // MX FP4 chunk: VEC codes (VEC/2 bytes) of one block of 32 values, with the
@@ -345,6 +385,13 @@ struct Chunk<ST_FP4, VEC> {
     __device__ __forceinline__ void widen(float *out, float) const {
 #pragma unroll
         for (int i = 0; i < VEC / 2; ++i) fp4_pair_to_f32(raw[i / 4], i % 4, out + 2 * i);
+    }
+    // sum_e code[e] q[e] (unscaled), q as VEC/2 words of bf16 pairs
+    __device__ __forceinline__ float dot_bf16(const uint32_t *q) const {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i) acc = dot2_bf16(fp4_pair_to_bf16(raw[i / 4], i % 4), q[i], acc);
+        return acc;
     }
 };
 
