@@ -201,9 +201,13 @@ replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream);
    Equivalent to replay_append(W=1); replay_decode; replay_flush(flush_at)
    up to the rounding of that route.  q, k: [B][G][N]; v: [B][H][P] (io
    dtype); dt, a: [B][H] f32; y: [B][H][P] f32.  With a float32 checkpoint
-   read (read_copy == NONE) it is one kernel launch; with a copy it runs the
-   append, decode and flush kernels in turn.  Errors as for replay_append
-   (the sequence is unchanged and its y is NaN). */
+   read (read_copy == NONE) it is one kernel launch.  With an e4m3 or FP4
+   copy and bf16 io the append and the output-only decode from the copy are
+   one launch (its outputs equal replay_append(1); replay_decode bit for
+   bit), followed by the flush kernel; otherwise (a bf16 copy, or float32
+   io) the append, decode and flush kernels run in turn.  Errors as for
+   replay_append: the sequence is unchanged, and its y is NaN (where the
+   kernels run in turn, replay_decode's rules give y). */
 replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v,
                           const float *dt, const float *a, float *y, int32_t flush_at, void *stream);
 

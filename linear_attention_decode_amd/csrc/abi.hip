@@ -286,6 +286,9 @@ static StepArgs step_args(replay_handle *h, const void *q, const void *k, const 
     sa.flush_at = flush_at;
     sa.io_bf16 = c.io_dtype == REPLAY_BF16;
     sa.W = W;
+    sa.copy = h->bufs.s_copy;
+    sa.copy_scale = h->bufs.s_scale;
+    sa.copy_st = c.read_copy == REPLAY_NONE ? -1 : state_kind(c.read_copy);
     return sa;
 }
 
@@ -296,15 +299,21 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
         return REPLAY_ERR_INVALID_ARG;
     const replay_config &c = h->cfg;
     hipStream_t s = as_stream(stream);
+    const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, 1);
     if (c.read_copy != REPLAY_NONE) {
-        // copies: the append, decode and flush kernels in turn
-        replay_status st = replay_append(h, 1, q, k, v, dt, a, stream);
-        if (st != REPLAY_OK) return st;
-        st = run_verify(h, 1, y, s);
+        // copies: append + decode from an e4m3 or FP4 copy in one launch
+        // (bf16 io), or the append and decode kernels in turn (a bf16 copy:
+        // measured slower in one launch); then the flush kernel
+        replay_status st;
+        if (c.io_dtype == REPLAY_BF16 && c.read_copy != REPLAY_BF16) {
+            st = from_hip(launch_step_copy(c.head_dim, c.state_dim, sa, s));
+        } else {
+            st = replay_append(h, 1, q, k, v, dt, a, stream);
+            if (st == REPLAY_OK) st = run_verify(h, 1, y, s);
+        }
         if (st != REPLAY_OK) return st;
         return run_flush(h, nullptr, flush_at, s);
     }
-    const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, 1);
     return from_hip(launch_step(c.head_dim, c.state_dim, sa, s));
 }
 

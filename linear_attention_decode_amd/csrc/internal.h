@@ -70,6 +70,9 @@ struct StepArgs {
     int32_t flush_at;
     int32_t io_bf16;
     int32_t W;                        // drafts per round (the verify round; the step takes 1)
+    const void *copy;                 // low-precision checkpoint copy the step reads (copy modes)
+    const void *copy_scale;           // its scales: e4m3 float [B][H], FP4 E8M0 bytes [B][H][P*N/32]
+    int32_t copy_st;                  // StateKind of the copy (ST_BF16, ST_FP8, ST_FP4)
 };
 
 struct EagerArgs {
@@ -94,6 +97,7 @@ hipError_t launch_fill_u32(void *dst, uint32_t value, size_t count, hipStream_t 
 hipError_t launch_eager(int P, int N, const EagerArgs &a, hipStream_t s);
 hipError_t launch_step(int P, int N, const StepArgs &a, hipStream_t s);
 hipError_t launch_verify_step(int P, int N, const StepArgs &a, hipStream_t s);
+hipError_t launch_step_copy(int P, int N, const StepArgs &a, hipStream_t s);   // append + decode from the copy
 bool verify_step_fused(int P, int N, const StepArgs &a);   // the fused round covers this case
 hipError_t launch_eager_select(const float *snaps, int32_t W, const int32_t *n_accept, float *s,
                                int32_t B, size_t head_elems_per_seq, hipStream_t st);

@@ -175,162 +175,6 @@ __device__ __forceinline__ int step_ring_wave(const StepArgs &A, int lane, int b
     return prev;
 }
 
-// The ring wavefronts for bf16 io: the same work with the output-only route
-// on the matrix cores (ring_mx.h); wavefront rw covers entries 16rw..16rw+15
-// (two wavefronts for a 32-entry ring).  Entry cold, this step's token, comes
-// from the inputs (k row, query, v); the other operands from the ring, as in
-// ring_wave_mx of the decode kernel, and every lane, clamped ones included,
-// holds the values the decode kernel holds after an append, so the output
-// of a non-folding step equals decode's bit for bit.  load() issues every
-// load; finish() (wavefront 0: write the token into the ring) arrives and
-// does the rest.
-template <int P, int N, int LM>
-struct StepRingMx {
-    using MX = MxRing<P, N, 1, LM>;
-    static constexpr int VR = (P + 63) / 64;
-    static constexpr uint32_t ES = 2;
-    MX m;
-    float a_in, dt_in, a_r, dt_r;
-    IoVec<true, 1> vnew[VR];         // wavefront 0, lane p: the new v (ring write)
-    RowWords<N, true> qrow, krow;    // lane i: words i of the new q (and, group writer, k) rows
-    uint32_t vin[MX::PW];            // the new v in the operand's pair layout (entry cold)
-    static_assert(RowWords<N, true>::WPL == 1, "one word of a row per lane");
-
-    __device__ __forceinline__ void load(const StepArgs &A, int lane, int rw, int b, int g, int h, size_t bh,
-                                         int base, int cold) {
-        const int L = A.L;
-        const size_t gring = ((size_t)b * A.G + g) * L;
-        const size_t hring = bh * L;
-        const size_t gin = (size_t)b * A.G + g;
-        const int bmod = base % L;
-        auto slot = [&](int j) { return ring_slot(bmod, j, L); };
-        const int lastr = cold > 0 ? cold - 1 : 0;   // clamp for ring loads (never used when cold == 0)
-        const int lr = lane & 15, lq = lane >> 4;
-        m.j0 = 16 * rw;
-        // this step's token first, then the ring
-        a_in = A.a[bh];
-        dt_in = A.dt[bh];
-        if (rw == 0) {
-#pragma unroll
-            for (int rr = 0; rr < VR; ++rr) vnew[rr].load(A.v, bh * P + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
-            if ((h % (A.H / A.G)) == 0) krow.load(static_cast<const char *>(A.k) + gin * N * ES, lane);
-        }
-        qrow.load(static_cast<const char *>(A.q) + gin * N * ES, lane);
-        const int sla = slot(lane < cold ? lane : lastr);
-        a_r = A.ring_a[hring + sla];
-        dt_r = A.ring_dt[hring + sla];
-#pragma unroll
-        for (int kb = 0; kb < MX::KB; ++kb) {
-            const int c = MX::col(kb, lane);
-            const int j = m.j0 + lr;   // entries < cold from the ring, the rest from this step's k
-            const bool old = j < cold;
-            m.ka[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(old ? A.ring_k : A.k) +
-                                                        (old ? (gring + slot(j)) * N : gin * N) + c);
-        }
-        const auto vres = make_rsrc(static_cast<const char *>(A.ring_v) + hring * P * ES, (uint32_t)(L * P * ES));
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int j = m.j0 + 4 * lq + kk;
-            const uint32_t row = (uint32_t)slot(j < cold ? j : lastr) * P;
-#pragma unroll
-            for (int pw = 0; pw < MX::PW; ++pw)
-                m.vw[kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * ES, 0, 0);
-        }
-#pragma unroll
-        for (int pw = 0; pw < MX::PW; ++pw) vin[pw] = static_cast<const uint32_t *>(A.v)[(bh * P) / 2 + MX::vword(pw, lane)];
-    }
-
-    // Returns this wavefront's arrival: the old count of its group counter.
-    __device__ __forceinline__ int finish(const StepArgs &A, int lane, int b, int g, int h, size_t bh, int base,
-                                          int cold, bool fold, float (*s_r)[P], float *s_abar,
-                                          float (*s_U)[LM + 1], float (*s_K)[N], float (*s_sw)[LM]) {
-        const int L = A.L, count = cold + 1;
-        const size_t gring = ((size_t)b * A.G + g) * L;
-        const size_t hring = bh * L;
-        const int lr = lane & 15, lq = lane >> 4;
-        int prev = -1;
-        if (m.j0 == 0) {
-            // this step's token goes into ring slot (pos mod L) = entry cold, as
-            // soon as it has arrived (no ring value used here comes from that slot)
-            const int sn = ring_slot(base % L, cold, L);
-#pragma unroll
-            for (int rr = 0; rr < VR; ++rr) {
-                const int p = lane + 64 * rr;
-                if (p < P) static_cast<uint16_t *>(A.ring_v)[(hring + sn) * P + p] = (uint16_t)vnew[rr].r;
-            }
-            if (lane == 0) {
-                A.ring_dt[hring + sn] = dt_in;
-                A.ring_a[hring + sn] = a_in;
-            }
-            if ((h % (A.H / A.G)) == 0) {
-                const size_t off = (gring + sn) * N * ES;
-                qrow.store(static_cast<char *>(A.ring_q) + off, lane);
-                krow.store(static_cast<char *>(A.ring_k) + off, lane);
-            }
-        }
-        // Arrival of this ring wavefront (every ring wavefront arrives after
-        // its own pointer read, which the loads above depend on).  Its result
-        // is needed only at the very end.
-        if (lane == 0) prev = atomicAdd(&A.sync[((size_t)b * (A.G + 1) + g) * kSyncStride], 1);
-
-        // entry cold and past it: this step's token (the query, the B operand
-        // of every column, gathered from the row's words)
-#pragma unroll
-        for (int kb = 0; kb < MX::KB; ++kb) {
-            const int w0 = MX::col(kb, lane) / 2;
-            m.qb[kb] = uint4{(uint32_t)__shfl((int)qrow.w[0], w0), (uint32_t)__shfl((int)qrow.w[0], w0 + 1),
-                             (uint32_t)__shfl((int)qrow.w[0], w0 + 2), (uint32_t)__shfl((int)qrow.w[0], w0 + 3)};
-        }
-        m.aj = lane < cold ? a_r : (lane == cold ? a_in : 1.f);
-        m.dtj = lane < cold ? dt_r : (lane == cold ? dt_in : 0.f);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int pw = 0; pw < MX::PW; ++pw)
-                if (m.j0 + 4 * lq + kk >= cold) m.vw[kk][pw] = vin[pw];
-
-        if (!fold) {
-            const f32x4 dk = m.dots(lane);
-            m.weights(lane, count, s_abar, s_sw);
-            m.term(lane, dk, s_r, s_sw);
-        } else {
-            // state-and-output route: stage U[p][j] = s_j v_j[p] and K[j][n] = k_j[n]
-            // for this wavefront's entries
-            m.weights(lane, count, s_abar, s_sw);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int j = m.j0 + 4 * lq + kk;
-                if (j < count) {
-                    const float sj = s_sw[0][j];
-#pragma unroll
-                    for (int pw = 0; pw < MX::PW; ++pw)
-#pragma unroll
-                        for (int half = 0; half < 2; ++half) {
-                            const int p = 32 * pw + 2 * lr + half;
-                            if (p < P) s_U[p][j] = sj * MX::vval(m.vw[kk][pw], half);
-                        }
-                }
-            }
-            const int j = m.j0 + lr;
-            if (j < count) {
-#pragma unroll
-                for (int kb = 0; kb < MX::KB; ++kb) {
-                    const int c = 32 * kb + 8 * lq;
-                    if (c < N) {
-                        IoVec<true, 8> kv;
-                        kv.r = m.ka[kb];
-                        float kk8[8];
-                        kv.widen(kk8);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) s_K[j][c + e] = kk8[e];
-                    }
-                }
-            }
-        }
-        return prev;
-    }
-};
-
 // Waves per SIMD to ask the register allocator for: 8 (the hardware maximum,
 // 64 registers a lane) where the kernel fits without spilling to scratch,
 // otherwise no request.

@@ -1,0 +1,182 @@
+// step_copy.hip -- append + output-only decode in one launch, reading a
+// low-precision checkpoint copy (bf16, e4m3 or MX FP4) with bf16 io.  The
+// library routes e4m3 and FP4 copies here; with a bf16 copy the append and
+// decode kernels in turn measured faster.
+//
+// For every (sequence, head): this step's token goes into the ring and
+//     y = abar_t (S q_t) + sum_{j<=t} s_{j,t} v_j (k_j . q_t)
+// is produced from the copy S (page "ReplaySSM: Cachear Inputs, No Estado",
+// section "Los dos caminos", eq. "Ruta solo salida"; page "ReplaySSM: Cache
+// SSM Inputs, Not State", Abstract: a low-precision copy serves the outputs
+// while the higher-precision checkpoint takes the updates).  The fold stays
+// with the flush kernel, which runs after this one.
+//
+// The workgroup is the decode kernel's several-head workgroup for the copy
+// (the heads' tiles stream as one taller tile, bf16-pair dot products) with
+// the fused step's ring wavefronts, one per head and 16-entry block: each
+// takes this step's token from the inputs, writes it into ring slot
+// pos mod L and arrives at its group's counter; the last arrival moves pos.
+// Outputs equal those of the append and decode kernels run in turn, bit for
+// bit.
+#include "step_common.h"
+#include "decode_impl.h"
+
+namespace replay {
+
+template <int P, int N, int ST, int LM, int HPW>
+struct StepCopyLaunch {
+    using Sh = DecodeShape<P * HPW, N, ST, 1, false>;
+    static constexpr int NR = LM / 16;                 // ring wavefronts per head
+    static constexpr int NT = Sh::NTS + 64 * NR * HPW;
+};
+
+template <int P, int N, int ST, int LM, int HPW>
+__global__ __launch_bounds__((StepCopyLaunch<P, N, ST, LM, HPW>::NT)) void step_copy_kernel(StepArgs args) {
+    using SL = StepCopyLaunch<P, N, ST, LM, HPW>;
+    using Sh = typename SL::Sh;
+    constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+    constexpr int NR = SL::NR, PT = P * HPW;
+    using RR = RowReduce<ITER, LPR>;
+
+    __shared__ float s_r[NR][HPW][P];
+    __shared__ float s_abar[HPW];
+    __shared__ __align__(16) float s_sw[HPW][LM];
+    __shared__ int s_route;   // 0 output, 2 error (sequence left unchanged)
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int H = args.H, G = args.G, L = args.L;
+    const int HW = H / HPW;
+    const int b = lid / HW, h0 = (lid % HW) * HPW;
+    const int g = (h0 * G) / H;   // the HPW heads share this group
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave-uniform role: scalar branches, and the ring wavefronts' pointer
+    // reads go through the scalar cache
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool streamer = wave < NTS / 64;
+    const int rw = wave - NTS / 64;
+    const size_t bh0 = (size_t)b * H + h0;
+    const size_t tile = bh0 * (size_t)(P * N);
+
+    if (streamer) {
+        // the copy's tile chunks first, then this step's (group-shared) query as bf16 pairs
+        Chunk<ST, VEC> ch[ITER];
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            if constexpr (ST == ST_FP4)
+                ch[i].load_mx(args.copy, args.copy_scale, tile + (size_t)(i * NTS + tid) * VEC);
+            else
+                ch[i].load(args.copy, tile + (size_t)(i * NTS + tid) * VEC);
+        }
+        const int col0 = (tid % LPR) * VEC;
+        constexpr int QW = VEC / 2;
+        uint32_t qw[QW];
+        const uint32_t *row = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(args.q) +
+                                                                  ((size_t)b * G + g) * N + col0);
+        if constexpr (QW % 4 == 0) {
+#pragma unroll
+            for (int e = 0; e < QW / 4; ++e) {
+                const uint4 u = reinterpret_cast<const uint4 *>(row)[e];
+                qw[4 * e] = u.x; qw[4 * e + 1] = u.y; qw[4 * e + 2] = u.z; qw[4 * e + 3] = u.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < QW; ++e) qw[e] = row[e];
+        }
+        float part[ITER][1];
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            float acc = ch[i].dot_bf16(qw);
+            if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
+            part[i][0] = acc;
+        }
+        RR::template run<1>(part, lane);
+        // LDS-only barrier: the ring writes and arrival atomics finish in the background
+        lds_barrier();
+        if (s_route != 0) {
+            for (int i = tid; i < PT; i += NTS) args.y[bh0 * P + i] = __builtin_nanf("");
+            return;
+        }
+        if (RR::writer(lane)) {
+            const int hi = RR::halving_index(lane);
+#pragma unroll
+            for (int e = 0; e < RR::FINAL; ++e) {
+                const int row_ = (e + RR::FINAL * hi) * RPI + tid / LPR;   // of the HPW stacked tiles
+                const int hl = HPW == 1 ? 0 : row_ / P, p = HPW == 1 ? row_ : row_ % P;
+                const float sc = (ST == ST_FP8) ? static_cast<const float *>(args.copy_scale)[bh0 + hl] : 1.0f;
+                float rt = s_r[0][hl][p];
+                if constexpr (NR == 2) rt += s_r[1][hl][p];   // block 0 + block 1
+                args.y[bh0 * P + row_] = s_abar[hl] * (sc * part[e][0]) + rt;
+            }
+        }
+    } else {
+        const int hl = rw / NR, blk = rw % NR;   // head h0 + hl, 16-entry block blk
+        const int h = h0 + hl;
+        const size_t bh = bh0 + hl;
+        const int base = args.base[b];
+        const int pos = args.pos[b];
+        const int cold = pos - base;
+        const bool bad = cold + 1 > L || pos == 2147483647;
+        if (rw == 0 && lane == 0) {
+            s_route = bad ? 2 : 0;
+            if (bad) raise_seq_error(args.err, b, cold + 1 > L ? REPLAY_SEQERR_RING_OVERFLOW : REPLAY_SEQERR_POS_OVERFLOW);
+        }
+        int prev = -1;
+        if (!bad) {
+            StepRingMx<P, N, LM> sr;
+            sr.load(args, lane, blk, b, g, h, bh, base, cold);
+            prev = sr.finish(args, lane, b, g, h, bh, base, cold, false, &s_r[blk][hl], &s_abar[hl],
+                             static_cast<float (*)[LM + 1]>(nullptr), static_cast<float (*)[N]>(nullptr), &s_sw[hl]);
+        }
+        lds_barrier();
+        if (lane == 0 && prev == NR * (H / G) - 1) {
+            // last ring wavefront of the group: the group arrives at the
+            // sequence's counter; the last group moves the pointer
+            int32_t *seq = args.sync + (size_t)b * (G + 1) * kSyncStride;
+            atomicExch(seq + (size_t)g * kSyncStride, 0);
+            if (atomicAdd(seq + (size_t)G * kSyncStride, 1) == G - 1) {
+                atomicExch(seq + (size_t)G * kSyncStride, 0);
+                args.pos[b] = pos + 1;
+            }
+        }
+    }
+}
+
+template <int P, int N, int ST, int LM>
+static hipError_t launch_sc_lm(const StepArgs &a, hipStream_t s) {
+    constexpr int HPW = heads_per_wg<ST, 1>();
+    if (HPW > 1 && (a.H / a.G) % HPW == 0) {
+        const unsigned blocks = (unsigned)((size_t)a.B * a.H / HPW);
+        step_copy_kernel<P, N, ST, LM, HPW><<<blocks, StepCopyLaunch<P, N, ST, LM, HPW>::NT, 0, s>>>(a);
+    } else {
+        const unsigned blocks = (unsigned)((size_t)a.B * a.H);
+        step_copy_kernel<P, N, ST, LM, 1><<<blocks, StepCopyLaunch<P, N, ST, LM, 1>::NT, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+template <int P, int N, int ST>
+static hipError_t launch_sc_st(const StepArgs &a, hipStream_t s) {
+    if (a.L <= 16) return launch_sc_lm<P, N, ST, 16>(a, s);
+    return launch_sc_lm<P, N, ST, kMaxRing>(a, s);
+}
+
+template <int P, int N>
+static hipError_t launch_sc_pn(const StepArgs &a, hipStream_t s) {
+    switch (a.copy_st) {
+        case ST_BF16: return launch_sc_st<P, N, ST_BF16>(a, s);
+        case ST_FP8: return launch_sc_st<P, N, ST_FP8>(a, s);
+        case ST_FP4: return launch_sc_st<P, N, ST_FP4>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_step_copy(int P, int N, const StepArgs &a, hipStream_t s) {
+    if (!a.io_bf16) return hipErrorInvalidValue;
+    if (P == 16 && N == 16) return launch_sc_pn<16, 16>(a, s);
+    if (P == 64 && N == 64) return launch_sc_pn<64, 64>(a, s);
+    if (P == 64 && N == 128) return launch_sc_pn<64, 128>(a, s);
+    if (P == 128 && N == 128) return launch_sc_pn<128, 128>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace replay

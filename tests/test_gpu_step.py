@@ -7,7 +7,9 @@ checkpoint with the state-and-output route.  Checked against
   steps (a different but exact route) to 1e-5;
 * the float64 oracle (1e-4 per token) and the integer ring model (exact);
 * error paths: a step that would overflow the ring leaves the sequence
-  unchanged and outputs NaN.
+  unchanged and outputs NaN;
+* with an e4m3 or FP4 read copy (bf16 io): append + decode from the copy in
+  one launch, then the flush, against the calls in turn, bit for bit.
 """
 import numpy as np
 import pytest
@@ -221,3 +223,70 @@ def test_step_ignores_nan_in_unused_slots():
     y1, s1 = run(True)
     assert np.isfinite(y0).all() and np.isfinite(s0).all()
     assert np.array_equal(y0, y1) and np.array_equal(s0, s1)
+
+
+@pytest.mark.parametrize("P,N,L,flush_at,B,H,G,copy,shared", [
+    (64, 128, 16, 16, 3, 16, 2, "bf16", False),    # 2 heads per workgroup
+    (64, 128, 16, 16, 3, 16, 2, "fp8", False),     # 4 heads per workgroup
+    (64, 128, 16, 16, 3, 16, 2, "fp4", False),
+    (64, 128, 8, 5, 2, 12, 2, "fp8", False),       # 6 heads per group: one head per workgroup
+    (128, 128, 32, 32, 2, 8, 2, "fp4", False),     # two ring wavefronts per head
+    (16, 16, 4, 4, 3, 4, 1, "fp8", False),
+    (64, 64, 6, 6, 2, 8, 2, "bf16", True),         # shared: the copy is the only checkpoint
+    (64, 128, 16, 16, 2, 16, 2, "fp8", True),
+])
+def test_copy_step_equals_calls(P, N, L, flush_at, B, H, G, copy, shared):
+    """With an e4m3 or FP4 copy and bf16 io, replay_step runs append + decode
+    from the copy as one launch, then the flush (a bf16 copy runs the kernels
+    in turn): outputs, checkpoints, copies, scales, pointers and ring slots
+    equal append, decode and flush run in turn, bit for bit."""
+    w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=230 + P + L + flush_at)
+    T = 2 * L + 3
+    gu.note(f"copy step vs calls {w} flush_at={flush_at} copy={copy} shared={shared}")
+    dev = gu.DevInputs(w, 0, T)
+    a = _layer(w, read_copy=copy, shared_lowp=shared)
+    b = _layer(w, read_copy=copy, shared_lowp=shared)
+    for lay in (a, b):
+        for name in ("ring_q", "ring_k", "ring_v", "ring_dt", "ring_a"):
+            lay.t[name].zero_()
+    ya = torch.empty((T, B, H, P), dtype=torch.float32, device=gu.DEV)
+    yb = torch.empty_like(ya)
+    for t in range(T):
+        a.step(*dev.step(t), ya[t], flush_at=flush_at)
+        b.append(1, *dev.step(t))
+        b.decode(yb[t])
+        b.flush(flush_at)
+    torch.cuda.synchronize()
+    assert a.get_error()[0] == 0 and b.get_error()[0] == 0
+    assert torch.equal(ya, yb)
+    assert torch.isfinite(ya).all()
+    for name in ("s_master", "s_copy", "s_scale", "pos", "base", "ring_q", "ring_k", "ring_v", "ring_dt", "ring_a"):
+        if a.t[name] is not None:
+            assert torch.equal(a.t[name], b.t[name]), name
+    assert torch.equal(a.sync, torch.zeros_like(a.sync))
+    a.close()
+    b.close()
+
+
+def test_copy_step_overflow_gives_nan():
+    import linear_attention_decode_amd as lad
+    w = synth.Workload(batch=3, heads=8, groups=2, head_dim=64, state_dim=128, ring_len=4,
+                       io_dtype="bf16", config=synth.CONFIG_ID["misc"], layer=241)
+    gu.note("copy step overflow")
+    dev = gu.DevInputs(w, 0, 6)
+    layer = _layer(w, read_copy="fp8")
+    y = torch.empty((6, 3, 8, 64), dtype=torch.float32, device=gu.DEV)
+    for t in range(4):
+        layer.step(*dev.step(t), y[t], flush_at=5)     # never folds: ring fills up
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    ring_before = layer.ring_v.clone()
+    layer.step(*dev.step(4), y[4], flush_at=5)
+    torch.cuda.synchronize()
+    word, per = layer.get_error()
+    assert per == [lad.SEQERR_RING_OVERFLOW] * 3
+    assert torch.isnan(y[4]).all() and torch.isfinite(y[:4]).all()
+    assert layer.pos.cpu().tolist() == [4, 4, 4]
+    assert torch.equal(layer.ring_v, ring_before)
+    layer.close()
