@@ -162,8 +162,13 @@ DECODE_SOURCES = ["linear_attention_decode_amd/csrc/decode_impl.h",
                   "linear_attention_decode_amd/csrc/ring_mx.h",
                   "linear_attention_decode_amd/csrc/device_common.h"]
 STEP_SOURCES = ["linear_attention_decode_amd/csrc/step.hip",
+                "linear_attention_decode_amd/csrc/step_common.h",
                 "linear_attention_decode_amd/csrc/ring_mx.h",
                 "linear_attention_decode_amd/csrc/device_common.h"]
+VERIFY_STEP_SOURCES = ["linear_attention_decode_amd/csrc/verify_step.hip",
+                       "linear_attention_decode_amd/csrc/step_common.h",
+                       "linear_attention_decode_amd/csrc/ring_mx.h",
+                       "linear_attention_decode_amd/csrc/device_common.h"]
 
 
 def read_ceiling_gbs(nbytes=1 << 30, reps=7):
@@ -407,25 +412,27 @@ def bench_verify(args):
     torch.cuda.empty_cache()
 
     # eager: W per-token steps into snapshots, then restore the accepted one
-    cfg = lad.ReplayConfig(B, H, G, P, N, L, lad.BF16, lad.NONE, 0)
-    S = torch.zeros((B, H, P, N), dtype=torch.float32, device="cuda")
-    snaps = torch.empty((W, B, H, P, N), dtype=torch.float32, device="cuda")
-    ye = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
+    eel = None
+    if not args.no_eager:
+        cfg = lad.ReplayConfig(B, H, G, P, N, L, lad.BF16, lad.NONE, 0)
+        S = torch.zeros((B, H, P, N), dtype=torch.float32, device="cuda")
+        snaps = torch.empty((W, B, H, P, N), dtype=torch.float32, device="cuda")
+        ye = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
 
-    def eround(r):
-        for i in range(W):
-            t = r * W + i
-            lad.replay_eager_step(cfg, S if i == 0 else snaps[i - 1], snaps[i], toks["q"][t], toks["k"][t],
-                                  toks["v"][t], toks["dt"][t], toks["a"][t], ye)
-        lad.replay_eager_select(cfg, snaps, W, accept[r], S)
-    for r in range(WU):
-        eround(r)
-    torch.cuda.synchronize()
-    e0 = time.perf_counter()
-    for k in range(R):
-        eround(WU + k)
-    torch.cuda.synchronize()
-    eel = time.perf_counter() - e0
+        def eround(r):
+            for i in range(W):
+                t = r * W + i
+                lad.replay_eager_step(cfg, S if i == 0 else snaps[i - 1], snaps[i], toks["q"][t], toks["k"][t],
+                                      toks["v"][t], toks["dt"][t], toks["a"][t], ye)
+            lad.replay_eager_select(cfg, snaps, W, accept[r], S)
+        for r in range(WU):
+            eround(r)
+        torch.cuda.synchronize()
+        e0 = time.perf_counter()
+        for k in range(R):
+            eround(WU + k)
+        torch.cuda.synchronize()
+        eel = time.perf_counter() - e0
     acc_total = float(acc_np[WU:].sum())
     replay_round_bytes = (state_bytes(w) + B * (W * (H * P * 2 + H * 8 + 2 * G * N * 2)) * 2
                           + vbytes / R)
@@ -439,12 +446,15 @@ def bench_verify(args):
                    "head_dim": P, "state_dim": N, "ring_len": L, "window": W, "rounds": R, "api": args.api},
         "accepted_tokens_per_s": acc_total / el,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kernel_name,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": (_counter_traffic(VERIFY_STEP_SOURCES, "verify_step_kernel_b256_h64_w5_counters.txt")
+                                 if args.api == "step" else None),
+                     "kernel": kernel_name,
                      "avg_launch_us": 1e3 * sum(ver_ms) / len(ver_ms),
                      "algorithmic_bytes_per_launch": vbytes / R},
-        "eager": {"positions_per_s": B * W * R / eel, "accepted_tokens_per_s": acc_total / eel,
-                  "ms_per_round": 1e3 * eel / R},
-        "speedup_vs_eager": eel / el,
+        "eager": ({"positions_per_s": B * W * R / eel, "accepted_tokens_per_s": acc_total / eel,
+                   "ms_per_round": 1e3 * eel / R} if eel else None),
+        "speedup_vs_eager": eel / el if eel else None,
         "round_bytes_ratio_vs_eager": replay_round_bytes / eager_round_bytes,
     }
 
