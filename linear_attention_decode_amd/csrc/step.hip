@@ -188,9 +188,19 @@ constexpr int step_waves() {
 template <int LM, bool IOB>
 constexpr int step_ring_waves() { return IOB ? LM / 16 : 1; }
 
-template <int P, int N, int LM, bool IOB>
-__global__ __launch_bounds__((StepShape<P, N>::NTS + 64 * step_ring_waves<LM, IOB>()))
-__attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kernel(StepArgs args) {
+// Row splits of a head's tile: a 128-row tile with bf16 io is streamed by two
+// workgroups of 64 rows each (4 + 1 wavefronts instead of 8 + 1, so six
+// workgroups fit a CU where three did); each has its own ring wavefront(s)
+// for its rows.
+template <int P, bool IOB>
+constexpr int step_row_splits() { return IOB && P == 128 ? 2 : 1; }
+
+// PH = rows of the head, RS = workgroups per head (rows P = PH / RS each).
+template <int PH, int N, int LM, bool IOB, int RS>
+__global__ __launch_bounds__((StepShape<PH / RS, N>::NTS + 64 * step_ring_waves<LM, IOB>()))
+__attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void step_kernel(StepArgs args) {
+    constexpr int P = PH / RS;
+    static_assert(RS == 1 || IOB, "row splits need the bf16 ring wavefront");
     using Sh = StepShape<P, N>;
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
     constexpr int NR = step_ring_waves<LM, IOB>();
@@ -205,7 +215,7 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
 
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int H = args.H, L = args.L;
-    const int b = lid / H, h = lid % H;
+    const int b = lid / (H * RS), h = (lid / RS) % H, p0 = (lid % RS) * P;   // rows p0 .. p0+P-1
     const int g = (h * args.G) / H;
     const int tid = threadIdx.x, lane = tid & 63;
     // the role of this wavefront, as a wave-uniform value: the branches on it
@@ -216,7 +226,7 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
     const bool streamer = wave < NTS / 64;
     const int rw = wave - NTS / 64;   // ring wavefront index
     const size_t bh = (size_t)b * H + h;
-    const size_t tile = bh * (size_t)(P * N);
+    const size_t tile = bh * (size_t)(PH * N) + (size_t)p0 * N;
 
     // Only the ring wavefronts read the pointer.  Each announces its arrival
     // once its ring loads are issued (the group's counter expects NR arrivals
@@ -262,8 +272,8 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
         }
         if (!bad) {
             if constexpr (IOB) {
-                StepRingMx<P, N, LM> sr;
-                sr.load(args, lane, rw, b, g, h, bh, base, cold);
+                StepRingMx<P, N, LM, PH> sr;
+                sr.load(args, lane, rw, b, g, h, bh, base, cold, p0);
                 prev = sr.finish(args, lane, b, g, h, bh, base, cold, route == 1, &s_r[rw], &s_abar, s_U, s_K,
                                  reinterpret_cast<float (*)[LM]>(&s_sw[0][0]));
             } else {
@@ -278,7 +288,7 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
     if (streamer) route = s_route;
 
     if (streamer && route == 2) {
-        for (int i = tid; i < P; i += NTS) args.y[bh * P + i] = __builtin_nanf("");
+        for (int i = tid; i < P; i += NTS) args.y[bh * PH + p0 + i] = __builtin_nanf("");
     } else if (streamer) {
         if (route == 1) {
             const float abar = s_abar;
@@ -320,10 +330,10 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
                 const int row = (e + RR::FINAL * hi) * RPI + tid / LPR;
                 float rt = s_r[0][row];
                 if constexpr (NR == 2) rt += s_r[1][row];   // block 0 + block 1
-                args.y[bh * P + row] = route == 1 ? part[e][0] : abar * part[e][0] + rt;
+                args.y[bh * PH + p0 + row] = route == 1 ? part[e][0] : abar * part[e][0] + rt;
             }
         }
-    } else if (lane == 0 && prev == NR * (H / args.G) - 1) {
+    } else if (lane == 0 && prev == NR * RS * (H / args.G) - 1) {
         // Last ring wavefront of its group to arrive: the group arrives at
         // the sequence's counter.  The last group to arrive means every ring
         // wavefront of the sequence has read the pointer (each arrived after
@@ -340,11 +350,15 @@ __attribute__((amdgpu_waves_per_eu(step_waves<P, N, LM, IOB>()))) void step_kern
 
 template <int P, int N, int LM>
 static hipError_t launch_lm(const StepArgs &a, hipStream_t s) {
-    const unsigned blocks = (unsigned)((size_t)a.B * a.H);
-    if (a.io_bf16)
-        step_kernel<P, N, LM, true><<<blocks, StepShape<P, N>::NTS + 64 * step_ring_waves<LM, true>(), 0, s>>>(a);
-    else
-        step_kernel<P, N, LM, false><<<blocks, StepShape<P, N>::NTS + 64 * step_ring_waves<LM, false>(), 0, s>>>(a);
+    if (a.io_bf16) {
+        constexpr int RS = step_row_splits<P, true>();
+        const unsigned blocks = (unsigned)((size_t)a.B * a.H * RS);
+        step_kernel<P, N, LM, true, RS>
+            <<<blocks, StepShape<P / RS, N>::NTS + 64 * step_ring_waves<LM, true>(), 0, s>>>(a);
+    } else {
+        const unsigned blocks = (unsigned)((size_t)a.B * a.H);
+        step_kernel<P, N, LM, false, 1><<<blocks, StepShape<P, N>::NTS + 64 * step_ring_waves<LM, false>(), 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

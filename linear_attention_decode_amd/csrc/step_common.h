@@ -49,12 +49,16 @@ struct RowWords {
 // of a non-folding step equals decode's bit for bit.  load() issues every
 // load; finish() (wavefront 0: write the token into the ring) arrives and
 // does the rest.
-template <int P, int N, int LM>
+// A head of PROW rows can be split over workgroups: this one covers the P
+// rows from p0 (its v values and its part of the ring term); the Δ, a and
+// group q/k rows of the token are written by the p0 == 0 part only.
+template <int P, int N, int LM, int PROW = P>
 struct StepRingMx {
     using MX = MxRing<P, N, 1, LM>;
     static constexpr int VR = (P + 63) / 64;
     static constexpr uint32_t ES = 2;
     MX m;
+    int p0;
     float a_in, dt_in, a_r, dt_r;
     IoVec<true, 1> vnew[VR];         // wavefront 0, lane p: the new v (ring write)
     RowWords<N, true> qrow, krow;    // lane i: words i of the new q (and, group writer, k) rows
@@ -62,7 +66,8 @@ struct StepRingMx {
     static_assert(RowWords<N, true>::WPL == 1, "one word of a row per lane");
 
     __device__ __forceinline__ void load(const StepArgs &A, int lane, int rw, int b, int g, int h, size_t bh,
-                                         int base, int cold) {
+                                         int base, int cold, int p0_ = 0) {
+        p0 = p0_;
         const int L = A.L;
         const size_t gring = ((size_t)b * A.G + g) * L;
         const size_t hring = bh * L;
@@ -77,8 +82,9 @@ struct StepRingMx {
         dt_in = A.dt[bh];
         if (rw == 0) {
 #pragma unroll
-            for (int rr = 0; rr < VR; ++rr) vnew[rr].load(A.v, bh * P + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
-            if ((h % (A.H / A.G)) == 0) krow.load(static_cast<const char *>(A.k) + gin * N * ES, lane);
+            for (int rr = 0; rr < VR; ++rr)
+                vnew[rr].load(A.v, bh * PROW + p0 + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
+            if ((h % (A.H / A.G)) == 0 && p0 == 0) krow.load(static_cast<const char *>(A.k) + gin * N * ES, lane);
         }
         qrow.load(static_cast<const char *>(A.q) + gin * N * ES, lane);
         const int sla = slot(lane < cold ? lane : lastr);
@@ -92,17 +98,18 @@ struct StepRingMx {
             m.ka[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(old ? A.ring_k : A.k) +
                                                         (old ? (gring + slot(j)) * N : gin * N) + c);
         }
-        const auto vres = make_rsrc(static_cast<const char *>(A.ring_v) + hring * P * ES, (uint32_t)(L * P * ES));
+        const auto vres = make_rsrc(static_cast<const char *>(A.ring_v) + hring * PROW * ES, (uint32_t)(L * PROW * ES));
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int j = m.j0 + 4 * lq + kk;
-            const uint32_t row = (uint32_t)slot(j < cold ? j : lastr) * P;
+            const uint32_t row = (uint32_t)slot(j < cold ? j : lastr) * PROW + p0;
 #pragma unroll
             for (int pw = 0; pw < MX::PW; ++pw)
                 m.vw[kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * ES, 0, 0);
         }
 #pragma unroll
-        for (int pw = 0; pw < MX::PW; ++pw) vin[pw] = static_cast<const uint32_t *>(A.v)[(bh * P) / 2 + MX::vword(pw, lane)];
+        for (int pw = 0; pw < MX::PW; ++pw)
+            vin[pw] = static_cast<const uint32_t *>(A.v)[(bh * PROW + p0) / 2 + MX::vword(pw, lane)];
     }
 
     // Returns this wavefront's arrival: the old count of its group counter.
@@ -121,13 +128,13 @@ struct StepRingMx {
 #pragma unroll
             for (int rr = 0; rr < VR; ++rr) {
                 const int p = lane + 64 * rr;
-                if (p < P) static_cast<uint16_t *>(A.ring_v)[(hring + sn) * P + p] = (uint16_t)vnew[rr].r;
+                if (p < P) static_cast<uint16_t *>(A.ring_v)[(hring + sn) * PROW + p0 + p] = (uint16_t)vnew[rr].r;
             }
-            if (lane == 0) {
+            if (lane == 0 && p0 == 0) {
                 A.ring_dt[hring + sn] = dt_in;
                 A.ring_a[hring + sn] = a_in;
             }
-            if ((h % (A.H / A.G)) == 0) {
+            if ((h % (A.H / A.G)) == 0 && p0 == 0) {
                 const size_t off = (gring + sn) * N * ES;
                 qrow.store(static_cast<char *>(A.ring_q) + off, lane);
                 krow.store(static_cast<char *>(A.ring_k) + off, lane);
