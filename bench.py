@@ -262,19 +262,26 @@ def bench_decode(args):
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # HIP events bracket every stride-th launch of the timed region (an event
+    # between two launches holds the second back, so bracketing every launch
+    # would slow the loop being measured).  The default stride L + 1 visits
+    # the ring counts 1..L in turn, the fold included, each equally often
+    # over (L + 1) * L steps.
+    stride = args.event_stride or (L + 1)
+    sampled = [k for k in range(args.steps) if k % stride == 0]
+    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for k in sampled}
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(args.warmup + k, evs[k])
+        step(args.warmup + k, evs.get(k))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     word, _ = layer.get_error()
     assert word == 0, f"device error bits {word}"
     elapsed = t1 - t0
-    counts = [((args.warmup + k) % L) + 1 for k in range(args.steps)]
+    counts = [((args.warmup + k) % L) + 1 for k in sampled]
     if args.api == "step":
         # the dominant kernel is the fused step kernel itself
-        step_ms = [e[0].elapsed_time(e[1]) for e in evs]
+        step_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in sampled]
         folds = [c >= L for c in counts]
         dec_ms = [m for m, f in zip(step_ms, folds) if not f]
         fl_ms = [m for m, f in zip(step_ms, folds) if f]
@@ -283,8 +290,8 @@ def bench_decode(args):
         avg_us = 1e3 * sum(step_ms) / len(step_ms)
         kernel_name = "step (append + output-only decode, or append + fold on full rings)"
     else:
-        dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
-        fl_ms = [evs[k][2].elapsed_time(evs[k][3]) for k in range(args.steps) if (args.warmup + k + 1) % L == 0]
+        dec_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in sampled]
+        fl_ms = [evs[k][2].elapsed_time(evs[k][3]) for k in sampled if (args.warmup + k + 1) % L == 0]
         kernel_bytes = sum(decode_bytes(w, c, 1, st_bytes) for c in counts)
         kernel_time = sum(dec_ms) / 1e3
         avg_us = 1e3 * sum(dec_ms) / len(dec_ms)
@@ -323,7 +330,7 @@ def bench_decode(args):
                    "checkpoint": "f32", "read_copy": args.read, "flush_every": L, "api": args.api},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": kernel_name, "avg_launch_us": avg_us,
+                     "kernel": kernel_name, "avg_launch_us": avg_us, "timed_launches": len(sampled),
                      "algorithmic_bytes_per_launch": kernel_bytes / len(counts),
                      "read_ceiling_GBs": ceiling, "frac_of_read_ceiling": achieved / ceiling},
         ("output_only_launch_avg_us" if args.api == "step" else "decode_avg_us"):
@@ -389,22 +396,26 @@ def bench_verify(args):
     for r in range(WU):
         round_(r)
     torch.cuda.synchronize()
-    evs = _events(R)
+    # HIP events bracket every stride-th round's launch (as in the decode
+    # bench; folds here follow the random accept counts, not the round index)
+    stride = args.event_stride or 4
+    sampled = [k for k in range(R) if k % stride == 0]
+    evs = dict(zip(sampled, _events(len(sampled))))
     t0 = time.perf_counter()
     for k in range(R):
-        round_(WU + k, evs[k])
+        round_(WU + k, evs.get(k))
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     assert layer.get_error()[0] == 0
-    ver_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    ver_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in sampled]
     # ring counts at the start of every round and at verify time (host side)
     before, at_verify = _verify_counts(B, L, W, acc_np)
     if args.api == "step":
-        vbytes = sum(verify_step_bytes(w, before[WU + k], W) for k in range(R))
+        vbytes = sum(verify_step_bytes(w, before[WU + k], W) for k in sampled)
         kernel_name = "verify round (fold if due + append + verify, W=5)"
     else:
         vbytes = sum(float(np.mean([decode_bytes(w, c, W) / B for c in at_verify[WU + k]])) * B
-                     for k in range(R))
+                     for k in sampled)
         kernel_name = "verify (W=5)"
     achieved = vbytes / (sum(ver_ms) / 1e3) / 1e9
     layer.close()
@@ -435,7 +446,7 @@ def bench_verify(args):
         eel = time.perf_counter() - e0
     acc_total = float(acc_np[WU:].sum())
     replay_round_bytes = (state_bytes(w) + B * (W * (H * P * 2 + H * 8 + 2 * G * N * 2)) * 2
-                          + vbytes / R)
+                          + vbytes / len(sampled))
     eager_round_bytes = W * eager_bytes(w) + float(np.mean(acc_np[WU:] >= 1)) * 2 * state_bytes(w)
     return {
         "metric": "speculative verify: scored draft positions/s at B=256",
@@ -451,7 +462,7 @@ def bench_verify(args):
                                  if args.api == "step" else None),
                      "kernel": kernel_name,
                      "avg_launch_us": 1e3 * sum(ver_ms) / len(ver_ms),
-                     "algorithmic_bytes_per_launch": vbytes / R},
+                     "algorithmic_bytes_per_launch": vbytes / len(sampled), "timed_launches": len(sampled)},
         "eager": ({"positions_per_s": B * W * R / eel, "accepted_tokens_per_s": acc_total / eel,
                    "ms_per_round": 1e3 * eel / R} if eel else None),
         "speedup_vs_eager": eel / el if eel else None,
@@ -636,6 +647,9 @@ def main():
                          "(replay_verify_step); calls: the append, decode/verify and flush kernels")
     ap.add_argument("--read", default="f32", choices=["f32", "bf16", "fp8"],
                     help="checkpoint the outputs read: the float32 master or a bf16 / e4m3 copy")
+    ap.add_argument("--event-stride", type=int, default=0,
+                    help="bracket every n-th launch of the timed loop with HIP events for the kernel's "
+                         "launch time (default: L + 1 for decode, which visits every ring count; 4 for verify)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true", help="skip the eager baseline timing")
     ap.add_argument("--probe-copy-gib", type=float, default=0.0,
