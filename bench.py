@@ -169,6 +169,10 @@ VERIFY_STEP_SOURCES = ["linear_attention_decode_amd/csrc/verify_step.hip",
                        "linear_attention_decode_amd/csrc/step_common.h",
                        "linear_attention_decode_amd/csrc/ring_mx.h",
                        "linear_attention_decode_amd/csrc/device_common.h"]
+VERIFY_WIDE_SOURCES = ["linear_attention_decode_amd/csrc/verify_wide.hip",
+                       "linear_attention_decode_amd/csrc/decode_impl.h",
+                       "linear_attention_decode_amd/csrc/ring_mx.h",
+                       "linear_attention_decode_amd/csrc/device_common.h"]
 
 
 def read_ceiling_gbs(nbytes=1 << 30, reps=7):
@@ -355,14 +359,16 @@ def _events(n):
 
 def bench_verify(args):
     """Speculative verify: B=256, H=64, G=8, P=64, N=128, L=16, W=5 drafts per
-    round, accepted drafts ~ Uniform{0..5}; each round = flush(L-W+1),
-    append(W), verify(W) (one fused launch with --api step, three launches
-    with --api calls), then rollback(W - accepted).  The eager baseline drafts
-    with W per-token steps into snapshots and restores the accepted one."""
+    round (--window: up to 16), accepted drafts ~ Uniform{0..W}; each round =
+    flush(L-W+1), append(W), verify(W) (one fused launch with --api step,
+    three launches with --api calls or W > 8), then rollback(W - accepted).
+    The eager baseline drafts with W per-token steps into snapshots and
+    restores the accepted one."""
     import torch
     import linear_attention_decode_amd as lad
     w = synth.named("verify")
-    B, H, G, P, N, L, W = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len, 5
+    B, H, G, P, N, L, W = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len, args.window
+    api = args.api if W <= 8 else "calls"   # windows past 8: flush, append and the matrix-core verify
     R = args.steps if args.steps_given else 128
     WU = args.warmup
     toks = input_pool(w, (R + WU) * W)
@@ -376,7 +382,7 @@ def bench_verify(args):
 
     def round_(r, ev=None):
         drafts = (win["q"][r], win["k"][r], win["v"][r], win["dt"][r], win["a"][r])
-        if args.api == "step":
+        if api == "step":
             # one fused launch: fold if due, append the drafts, score them
             if ev is not None:
                 ev[0].record(stream)
@@ -410,13 +416,13 @@ def bench_verify(args):
     ver_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in sampled]
     # ring counts at the start of every round and at verify time (host side)
     before, at_verify = _verify_counts(B, L, W, acc_np)
-    if args.api == "step":
+    if api == "step":
         vbytes = sum(verify_step_bytes(w, before[WU + k], W) for k in sampled)
-        kernel_name = "verify round (fold if due + append + verify, W=5)"
+        kernel_name = f"verify round (fold if due + append + verify, W={W})"
     else:
         vbytes = sum(float(np.mean([decode_bytes(w, c, W) / B for c in at_verify[WU + k]])) * B
                      for k in sampled)
-        kernel_name = "verify (W=5)"
+        kernel_name = f"verify (W={W}{', matrix cores' if W > 8 else ''})"
     achieved = vbytes / (sum(ver_ms) / 1e3) / 1e9
     layer.close()
     del layer
@@ -452,14 +458,16 @@ def bench_verify(args):
         "metric": "speculative verify: scored draft positions/s at B=256",
         "value": B * W * R / el, "unit": "positions/s", "n_gpus": 1, "steps": R, "warmup": WU,
         "ms_per_step": 1e3 * el / R, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic (seeded), accepted drafts ~ Uniform{0..5}",
+        "dtype": "f32", "data": f"synthetic (seeded), accepted drafts ~ Uniform{{0..{W}}}",
         "config": {"workload": "speculative verify, one SSM layer", "batch": B, "heads": H, "groups": G,
-                   "head_dim": P, "state_dim": N, "ring_len": L, "window": W, "rounds": R, "api": args.api},
+                   "head_dim": P, "state_dim": N, "ring_len": L, "window": W, "rounds": R, "api": api},
         "accepted_tokens_per_s": acc_total / el,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (_counter_traffic(VERIFY_STEP_SOURCES, "verify_step_kernel_b256_h64_w5_counters.txt")
-                                 if args.api == "step" else None),
+                                 if api == "step" and W == 5 else
+                                 _counter_traffic(VERIFY_WIDE_SOURCES, "verify_wide_kernel_b256_h64_w16_counters.txt")
+                                 if W == 16 else None),
                      "kernel": kernel_name,
                      "avg_launch_us": 1e3 * sum(ver_ms) / len(ver_ms),
                      "algorithmic_bytes_per_launch": vbytes / len(sampled), "timed_launches": len(sampled)},
@@ -642,6 +650,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="decode", choices=["decode", "verify", "dual", "stacked"])
     ap.add_argument("--quick", action="store_true", help="dual/stacked: one variant only")
+    ap.add_argument("--window", type=int, default=5,
+                    help="verify: drafts per round (5 is the benchmarked workload; up to 16, windows past 8 "
+                         "on the matrix cores through the separate calls)")
     ap.add_argument("--api", default="step", choices=["step", "calls"],
                     help="step: one fused launch per decode step (replay_step) or verify round "
                          "(replay_verify_step); calls: the append, decode/verify and flush kernels")

@@ -43,7 +43,8 @@
  *    one handle must be issued in order on one stream (or ordered by the
  *    caller across streams).
  *  - Specialisations: (P, N) in {(16,16), (64,64), (64,128), (128,128)},
- *    1 <= L <= 32, 1 <= G <= H with H % G == 0, verify windows 1 <= W <= 8.
+ *    1 <= L <= 32, 1 <= G <= H with H % G == 0, verify windows 1 <= W <= 8
+ *    (up to 16 with bf16 io and a float32, bf16 or e4m3 read; see replay_verify).
  */
 #ifndef REPLAYSSM_H
 #define REPLAYSSM_H
@@ -173,8 +174,11 @@ replay_status replay_decode(replay_handle *h, float *y, void *stream);
    window read the same checkpoint and buffer, entry j is visible to position
    t only when j <= t; abstract page: output-only verification).
    Position w (0-based) is ring entry t_w = count - W + 1 + w.
-   y: [B][W][H][P] f32.  1 <= W <= min(8, L); needs count >= W per sequence
-   (else TOO_FEW, NaN outputs for that sequence). */
+   y: [B][W][H][P] f32.  1 <= W <= min(8, L) for every configuration; with
+   bf16 io and a float32, bf16 or e4m3 read also 9 <= W <= min(16, L) (the
+   window's S Q^T on the matrix cores; other configurations return
+   UNSUPPORTED for W > 8).  Needs count >= W per sequence (else TOO_FEW, NaN
+   outputs for that sequence). */
 replay_status replay_verify(replay_handle *h, int32_t W, float *y, void *stream);
 
 /* Drop the n_reject[b] newest entries of every sequence by moving the pointer
@@ -222,8 +226,9 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
    exactly when the drafts would not fit otherwise.
    Equivalent to replay_flush(flush_at); replay_append(W); replay_verify(W),
    bit for bit.  q, k: [B][W][G][N]; v: [B][W][H][P] (io dtype); dt, a:
-   [B][W][H] f32; y: [B][W][H][P] f32, draft w at [b][w].  1 <= W <= min(8, L).
-   With a float32 checkpoint read, bf16 io and L <= 16 it is one kernel
+   [B][W][H] f32; y: [B][W][H][P] f32, draft w at [b][w].  1 <= W <= min(16, L)
+   (windows past 8 as for replay_verify, through the kernels in turn).
+   With a float32 checkpoint read, bf16 io, L <= 16 and W <= 8 it is one kernel
    launch that reads each checkpoint once and writes it only where it folds;
    otherwise it runs the flush, append and verify kernels in turn.  A
    sequence whose drafts do not fit after the fold (count + W > L with

@@ -136,14 +136,20 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
 replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
     const replay_config &c = h->cfg;
     if (!y || !aligned4(y)) return REPLAY_ERR_INVALID_ARG;
-    if (W < 1 || W > kMaxWindow || W > c.ring_len) return REPLAY_ERR_INVALID_ARG;
+    if (W < 1 || W > kMaxWideWindow || W > c.ring_len) return REPLAY_ERR_INVALID_ARG;
     DecodeArgs a;
     a.r = ring_view(h);
     a.S = c.read_copy == REPLAY_NONE ? static_cast<const void *>(h->bufs.s_master) : h->bufs.s_copy;
     a.scale = h->bufs.s_scale;
     a.y = y;
     a.W = W;
-    return from_hip(launch_decode(c.head_dim, c.state_dim, state_kind(c.read_copy), a, s));
+    const int st = state_kind(c.read_copy);
+    if (W > kMaxWindow) {
+        // wide windows: the matrix-core kernel (bf16 io; float32, bf16 or e4m3 reads)
+        if (!verify_wide_supported(st, a)) return REPLAY_ERR_UNSUPPORTED;
+        return from_hip(launch_verify_wide(c.head_dim, c.state_dim, st, a, s));
+    }
+    return from_hip(launch_decode(c.head_dim, c.state_dim, st, a, s));
 }
 
 }  // namespace
@@ -323,7 +329,7 @@ replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, con
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a) || !aligned4(y))
         return REPLAY_ERR_INVALID_ARG;
     const replay_config &c = h->cfg;
-    if (W < 1 || W > 8 || W > c.ring_len) return REPLAY_ERR_INVALID_ARG;
+    if (W < 1 || W > kMaxWideWindow || W > c.ring_len) return REPLAY_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, W);
     if (c.read_copy != REPLAY_NONE || !verify_step_fused(c.head_dim, c.state_dim, sa)) {

@@ -13,7 +13,8 @@ enum StateKind : int { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2, ST_FP4 = 3 };
 
 // Largest ring and verify window the kernels are built for.
 constexpr int kMaxRing = 32;
-constexpr int kMaxWindow = 8;
+constexpr int kMaxWindow = 8;        // verify windows of the register kernel (decode_impl.h)
+constexpr int kMaxWideWindow = 16;   // wide windows on the matrix cores (verify_wide.hip)
 
 // Arrival counters of the fused step, [B][G + 1] of them, one int32 per
 // 128-byte line: a workgroup arrives at its group's counter, the last head
@@ -87,6 +88,8 @@ struct EagerArgs {
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_decode(int P, int N, int st, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_verify_wide(int P, int N, int st, const DecodeArgs &a, hipStream_t s);   // kMaxWindow < W <= 16
+bool verify_wide_supported(int st, const DecodeArgs &a);
 hipError_t launch_flush(int P, int N, int st_in, int st_copy, bool write_master, const FlushArgs &a,
                         hipStream_t s);
 hipError_t launch_append(int P, int N, const RingView &r, void *ring_q, void *ring_k, void *ring_v,

@@ -73,9 +73,11 @@ struct MxRing {
     }
 
     // s_sw[w][j] = s_{j,t_w} (0 for j > t_w or j >= count) for this block's
-    // entries; s_abar[w] = abar_{t_w} from the block-0 wavefront
-    __device__ __forceinline__ void weights(int lane, int count, float *s_abar, float (*s_sw)[LM]) const {
-        const int t0 = count - WM;
+    // entries; s_abar[w] = abar_{t_w} from the block-0 wavefront.  A window
+    // of W < WM positions leaves columns w >= W at zero (t_w = count-W+w).
+    __device__ __forceinline__ void weights(int lane, int count, float *s_abar, float (*s_sw)[LM],
+                                            int W = WM) const {
+        const int t0 = count - W;
         float sw[WM], ab[WM];
         float prod = dtj, run = 1.f;
 #pragma unroll
@@ -104,12 +106,54 @@ struct MxRing {
         }
     }
 
+    // The same weights in the term's operand layout, without LDS: lane
+    // (w = lane%16, group lq) forms s_{j,t_w} for its four entries j =
+    // j0+4lq+kk and abar_{t_w}, multiplying the same factors in the same
+    // order as weights() (dt_j, then a_m for j < m <= t_w), so the values are
+    // identical.  Columns w >= W get zero weights and abar.
+    __device__ __forceinline__ void weights_cols(int lane, int count, int W, f32x4 &wv, float &abar) const {
+        const int w = lane & 15, jb = j0 + 4 * (lane >> 4);
+        const int t = count - W + w;
+        float pr[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) pr[kk] = __shfl(dtj, jb + kk);
+        float run = 1.f;
+#pragma unroll
+        for (int m = 0; m < LM; ++m) {
+            if (m < count) {
+                const float am = bcast(aj, m);
+                const bool in_t = m <= t;
+                run = in_t ? run * am : run;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    if (in_t && m > jb + kk) pr[kk] *= am;
+            }
+        }
+        const bool valid = w < W;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) wv[kk] = valid && jb + kk <= t ? pr[kk] : 0.f;
+        abar = valid ? run : 0.f;
+    }
+
+    // The ring term with weights already in the operand layout (weights_cols).
+    __device__ __forceinline__ void term_cols(int lane, f32x4 dk, f32x4 wv, float (*s_r)[P]) const {
+        const int lr = lane & 15, lq = lane >> 4;
+        const f32x4 cf = wv * dk;
+        term_coeffs(lr, lq, cf, s_r);
+    }
+
     // s_r[w][p] = this block's part of R[w][p]; reads the weights this
     // wavefront wrote to s_sw (a wavefront's own LDS accesses complete in order)
     __device__ __forceinline__ void term(int lane, f32x4 dk, float (*s_r)[P], const float (*s_sw)[LM]) const {
         const int lr = lane & 15, lq = lane >> 4;
         const f32x4 wv = *reinterpret_cast<const f32x4 *>(&s_sw[lr < WM ? lr : 0][j0 + 4 * lq]);
         const f32x4 cf = lr < WM ? wv * dk : f32x4{0.f, 0.f, 0.f, 0.f};
+        term_coeffs(lr, lq, cf, s_r);
+    }
+
+    // s_r[w][p] = sum_j cf[w][j] v_j[p] from the coefficients in the first
+    // product's output layout
+    __device__ __forceinline__ void term_coeffs(int lr, int lq, f32x4 cf, float (*s_r)[P]) const {
         // column n of block (pw, half) is p = 32pw + 2n + half
 #pragma unroll
         for (int pw = 0; pw < PW; ++pw)

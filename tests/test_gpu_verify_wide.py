@@ -1,0 +1,117 @@
+"""Speculative verify of wide windows (9 <= W <= 16) on the matrix cores.
+
+- Rounds of W drafts with rollback and flushes when the next window would
+  not fit, against the float64 oracle (per token over the layer output:
+  1e-4 for a float32 checkpoint; bf16 / e4m3 copies against the oracle's
+  emulation of the same copy, 1e-3 / 1e-2) and the integer ring model.
+- The same state scored with W = 16 and W = 8: the newest eight positions
+  agree to float32 rounding (the two kernels share nothing but the ring
+  term's code).
+- Errors: count < W gives NaN and TOO_FEW; unsupported configurations (an
+  FP4 copy, float32 io) are rejected by the host."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ring as oring
+from oracle import runs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(w, **kw):
+    import linear_attention_decode_amd as lad
+    return lad.ReplayLayer(w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len,
+                           io_dtype=w.io_dtype, device=gu.DEV, **kw)
+
+
+@pytest.mark.parametrize("P,N,L,W,B,H,G,copy", [
+    (64, 128, 16, 16, 3, 8, 2, None),      # the verify workload's head, W = L
+    (64, 128, 16, 12, 4, 16, 4, None),
+    (64, 64, 20, 9, 3, 4, 2, None),        # two ring blocks
+    (128, 128, 32, 16, 2, 4, 2, None),
+    (16, 16, 16, 11, 3, 6, 3, None),
+    (64, 128, 16, 16, 3, 8, 2, "bf16"),
+    (64, 128, 16, 10, 3, 8, 2, "fp8"),
+    (16, 16, 16, 16, 2, 4, 1, "fp8"),      # e4m3 tile widened (N < 32)
+])
+def test_wide_verify_rounds(P, N, L, W, B, H, G, copy):
+    w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=300 + P + L + W)
+    R = 10
+    gu.note(f"wide verify {w} W={W} copy={copy}")
+    accept = synth.accept_counts(w, R, W)
+    dev = gu.DevInputs(w, 0, R * W)
+    layer = _layer(w, **({} if copy is None else {"read_copy": copy}))
+    model = oring.RingModel(B, L)
+    y = gu.run_verify(layer, w, dev, R, W, accept, model=model)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = gu.oracle_inputs(w, 0, R * W, list(range(B)))
+    S0 = np.zeros((B, H, P, N))
+    if copy is None:
+        y_ref, tol = runs.verify_rounds(x, accept, W, S0), 1e-4
+    else:
+        y_ref, tol = runs.verify_rounds_copy(x, accept, W, S0, L, copy), {"bf16": 1e-3, "fp8": 1e-2}[copy]
+    tok, vec, _ = gu.errors(y.cpu().numpy().transpose(0, 2, 1, 3, 4), y_ref)
+    print(f"  per-token max {tok:.3e} per-head max {vec:.3e}")
+    assert tok <= tol, tok
+    layer.close()
+
+
+@pytest.mark.parametrize("P,N,copy", [(64, 128, None), (128, 128, None), (64, 128, "fp8")])
+def test_wide_window_agrees_with_register_kernel(P, N, copy):
+    """16 entries in the ring: verify(16) on the matrix cores and verify(8) in
+    registers score the newest eight positions of the same state."""
+    w = synth.Workload(batch=3, heads=8, groups=2, head_dim=P, state_dim=N, ring_len=16, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=330 + P)
+    gu.note(f"wide vs register verify P={P} N={N} copy={copy}")
+    dev = gu.DevInputs(w, 0, 40)
+    layer = _layer(w, **({} if copy is None else {"read_copy": copy}))
+    for t in range(24):                        # a non-zero checkpoint first
+        layer.append(1, *dev.step(t))
+        layer.flush(16)
+    layer.flush(1)                             # empty ring, then a full one
+    layer.append(16, *dev.window(24, 16))
+    y16 = torch.empty((3, 16, 8, P), dtype=torch.float32, device=gu.DEV)
+    y8 = torch.empty((3, 8, 8, P), dtype=torch.float32, device=gu.DEV)
+    layer.verify(16, y16)
+    layer.verify(8, y8)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    tok, _, _ = gu.errors(y16[:, 8:].cpu().numpy(), y8.cpu().numpy().astype(np.float64))
+    assert tok <= 1e-5, tok
+    layer.close()
+
+
+def test_wide_verify_errors():
+    import linear_attention_decode_amd as lad
+    w = synth.Workload(batch=3, heads=4, groups=2, head_dim=64, state_dim=128, ring_len=16, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=341)
+    gu.note("wide verify errors")
+    dev = gu.DevInputs(w, 0, 12)
+    layer = _layer(w)
+    layer.append(12, *dev.window(0, 12))
+    y = torch.zeros((3, 13, 4, 64), dtype=torch.float32, device=gu.DEV)
+    layer.verify(13, y)                        # 12 entries < 13: every sequence fails
+    torch.cuda.synchronize()
+    word, per = layer.get_error()
+    assert per == [lad.SEQERR_TOO_FEW] * 3
+    assert torch.isnan(y).all()
+    y12 = torch.zeros((3, 12, 4, 64), dtype=torch.float32, device=gu.DEV)
+    layer.verify(12, y12)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0 and torch.isfinite(y12).all()
+    with pytest.raises(lad.ReplayError):
+        layer.verify(17, torch.zeros((3, 17, 4, 64), dtype=torch.float32, device=gu.DEV))
+    layer.close()
+    for kw in ({"read_copy": "fp4"}, {"io_dtype": "f32"}):
+        wl = synth.Workload(batch=2, heads=4, groups=2, head_dim=64, state_dim=128, ring_len=16,
+                            io_dtype=kw.get("io_dtype", "bf16"), config=synth.CONFIG_ID["misc"], layer=342)
+        lay = lad.ReplayLayer(2, 4, 2, 64, 128, 16, io_dtype=wl.io_dtype, read_copy=kw.get("read_copy"),
+                              device=gu.DEV)
+        with pytest.raises(lad.ReplayError):
+            lay.verify(12, torch.zeros((2, 12, 4, 64), dtype=torch.float32, device=gu.DEV))
+        lay.close()
