@@ -15,9 +15,11 @@
 //
 // Workgroup = 4 streaming wavefronts (8 for a 128 x 128 tile; the head's tile
 // in 16-byte chunks) + 1 ring wavefront (decays, group dots, ring term or the
-// rank-c staging, and the ring write of the new token).  The new token is taken from the inputs,
-// so the streaming wavefronts never wait for the ring pointer.  The pointer
-// of a sequence moves when its last workgroup arrives (per-sequence counter).
+// rank-c staging).  The new token is taken from the inputs, so the streaming
+// wavefronts never wait for the ring pointer.  One writer workgroup per
+// sequence, after every compute workgroup in the grid, copies the token into
+// the ring.  The pointer of a sequence moves when its last workgroup arrives
+// (per-sequence counter).
 #include "step_common.h"
 
 namespace replay {
@@ -45,12 +47,6 @@ __device__ __forceinline__ int step_ring_wave(const StepArgs &A, int lane, int b
     IoVec<IOB, 1> vnew[VR];
 #pragma unroll
     for (int rr = 0; rr < VR; ++rr) vnew[rr].load(A.v, bh * P + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
-    const bool group_writer = (h % (A.H / A.G)) == 0;
-    RowWords<N, IOB> qrow, krow;
-    if (group_writer) {
-        qrow.load(static_cast<const char *>(A.q) + gin * N * (IOB ? 2 : 4), lane);
-        krow.load(static_cast<const char *>(A.k) + gin * N * (IOB ? 2 : 4), lane);
-    }
     const int sla = slot(lane < cold ? lane : lastr);
     const float a_r = A.ring_a[hring + sla], dt_r = A.ring_dt[hring + sla];
     IoVec<IOB, 8> kraw[KI];
@@ -76,31 +72,6 @@ __device__ __forceinline__ int step_ring_wave(const StepArgs &A, int lane, int b
     }
     auto vval = [&](int rr, int j) { return j < cold ? vraw[rr][j].value() : vnew[rr].value(); };
 
-    // 2. this step's token goes into ring slot (pos mod L) = entry cold,
-    // as soon as it has arrived: a wavefront ends only once its stores have
-    // completed, so they are issued before the ring loads are waited for.
-    // No ring value read above comes from slot sn (entries < cold only; the
-    // clamped loads of an empty ring read it, but those values are unused).
-    const int sn = slot(cold);
-#pragma unroll
-    for (int rr = 0; rr < VR; ++rr) {
-        const int p = lane + 64 * rr;
-        if (p < P) {
-            if constexpr (IOB)
-                static_cast<uint16_t *>(A.ring_v)[(hring + sn) * P + p] = (uint16_t)vnew[rr].r;
-            else
-                static_cast<float *>(A.ring_v)[(hring + sn) * P + p] = vnew[rr].r;
-        }
-    }
-    if (lane == 0) {
-        A.ring_dt[hring + sn] = dt_in;
-        A.ring_a[hring + sn] = a_in;
-    }
-    if (group_writer) {
-        const size_t off = (gring + sn) * N * (IOB ? 2 : 4);
-        qrow.store(static_cast<char *>(A.ring_q) + off, lane);
-        krow.store(static_cast<char *>(A.ring_k) + off, lane);
-    }
     // Arrival of this workgroup (its pointer read is done: the loads above
     // depend on it).  Its result is needed only at the very end.
     int prev = -1;
@@ -213,8 +184,13 @@ __attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void ste
     __shared__ __align__(16) float s_K[LM][N];
     __shared__ __align__(16) float s_sw[1][IOB ? LM : 4];
 
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int H = args.H, L = args.L;
+    const int ncomp = args.B * H * RS;   // compute workgroups; one writer per sequence follows
+    if ((int)blockIdx.x >= ncomp) {
+        step_token_writer<PH, N, IOB, true>(args, (int)blockIdx.x - ncomp, threadIdx.x, blockDim.x);
+        return;
+    }
+    const int lid = xcd_remap(blockIdx.x, ncomp);
     const int b = lid / (H * RS), h = (lid / RS) % H, p0 = (lid % RS) * P;   // rows p0 .. p0+P-1
     const int g = (h * args.G) / H;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -274,7 +250,7 @@ __attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void ste
             if constexpr (IOB) {
                 StepRingMx<P, N, LM, PH> sr;
                 sr.load(args, lane, rw, b, g, h, bh, base, cold, p0);
-                prev = sr.finish(args, lane, b, g, h, bh, base, cold, route == 1, &s_r[rw], &s_abar, s_U, s_K,
+                prev = sr.finish(args, lane, b, g, cold, route == 1, &s_r[rw], &s_abar, s_U, s_K,
                                  reinterpret_cast<float (*)[LM]>(&s_sw[0][0]));
             } else {
                 prev = step_ring_wave<P, N, LM, IOB>(args, lane, b, g, h, bh, base, cold, route == 1, s_r[0],
@@ -282,8 +258,8 @@ __attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void ste
             }
         }
     }
-    // LDS-only barrier: the ring wavefront's write-back of the new token and
-    // its arrival atomic complete in the background
+    // LDS-only barrier: the ring wavefront's arrival atomic completes in the
+    // background
     lds_barrier();
     if (streamer) route = s_route;
 
@@ -335,16 +311,10 @@ __attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void ste
         }
     } else if (lane == 0 && prev == NR * RS * (H / args.G) - 1) {
         // Last ring wavefront of its group to arrive: the group arrives at
-        // the sequence's counter.  The last group to arrive means every ring
-        // wavefront of the sequence has read the pointer (each arrived after
-        // its read), so the pointer moves.
-        int32_t *seq = args.sync + (size_t)b * (args.G + 1) * kSyncStride;
-        atomicExch(seq + (size_t)g * kSyncStride, 0);
-        if (atomicAdd(seq + (size_t)args.G * kSyncStride, 1) == args.G - 1) {
-            atomicExch(seq + (size_t)args.G * kSyncStride, 0);
-            args.pos[b] = pos + 1;
-            if (route == 1) args.base[b] = pos + 1;
-        }
+        // the sequence's counter (each ring wavefront arrived after its
+        // pointer read).
+        atomicExch(args.sync + ((size_t)b * (args.G + 1) + g) * kSyncStride, 0);
+        step_seq_arrive(args, b, pos, route == 1);
     }
 }
 
@@ -352,11 +322,11 @@ template <int P, int N, int LM>
 static hipError_t launch_lm(const StepArgs &a, hipStream_t s) {
     if (a.io_bf16) {
         constexpr int RS = step_row_splits<P, true>();
-        const unsigned blocks = (unsigned)((size_t)a.B * a.H * RS);
+        const unsigned blocks = (unsigned)((size_t)a.B * a.H * RS + a.B);
         step_kernel<P, N, LM, true, RS>
             <<<blocks, StepShape<P / RS, N>::NTS + 64 * step_ring_waves<LM, true>(), 0, s>>>(a);
     } else {
-        const unsigned blocks = (unsigned)((size_t)a.B * a.H);
+        const unsigned blocks = (unsigned)((size_t)a.B * a.H + a.B);
         step_kernel<P, N, LM, false, 1><<<blocks, StepShape<P, N>::NTS + 64 * step_ring_waves<LM, false>(), 0, s>>>(a);
     }
     return hipGetLastError();

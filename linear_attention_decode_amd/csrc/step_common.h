@@ -47,11 +47,10 @@ struct RowWords {
 // ring_wave_mx of the decode kernel, and every lane, clamped ones included,
 // holds the values the decode kernel holds after an append, so the output
 // of a non-folding step equals decode's bit for bit.  load() issues every
-// load; finish() (wavefront 0: write the token into the ring) arrives and
-// does the rest.
+// load; finish() arrives and does the rest.  The token itself goes into the
+// ring through the launch's writer workgroups (step_token_writer).
 // A head of PROW rows can be split over workgroups: this one covers the P
-// rows from p0 (its v values and its part of the ring term); the Δ, a and
-// group q/k rows of the token are written by the p0 == 0 part only.
+// rows from p0 (its v values and its part of the ring term).
 template <int P, int N, int LM, int PROW = P>
 struct StepRingMx {
     using MX = MxRing<P, N, 1, LM>;
@@ -60,8 +59,7 @@ struct StepRingMx {
     MX m;
     int p0;
     float a_in, dt_in, a_r, dt_r;
-    IoVec<true, 1> vnew[VR];         // wavefront 0, lane p: the new v (ring write)
-    RowWords<N, true> qrow, krow;    // lane i: words i of the new q (and, group writer, k) rows
+    RowWords<N, true> qrow;          // lane i: word i of the new q row
     uint32_t vin[MX::PW];            // the new v in the operand's pair layout (entry cold)
     static_assert(RowWords<N, true>::WPL == 1, "one word of a row per lane");
 
@@ -80,12 +78,6 @@ struct StepRingMx {
         // this step's token first, then the ring
         a_in = A.a[bh];
         dt_in = A.dt[bh];
-        if (rw == 0) {
-#pragma unroll
-            for (int rr = 0; rr < VR; ++rr)
-                vnew[rr].load(A.v, bh * PROW + p0 + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
-            if ((h % (A.H / A.G)) == 0 && p0 == 0) krow.load(static_cast<const char *>(A.k) + gin * N * ES, lane);
-        }
         qrow.load(static_cast<const char *>(A.q) + gin * N * ES, lane);
         const int sla = slot(lane < cold ? lane : lastr);
         a_r = A.ring_a[hring + sla];
@@ -113,33 +105,12 @@ struct StepRingMx {
     }
 
     // Returns this wavefront's arrival: the old count of its group counter.
-    __device__ __forceinline__ int finish(const StepArgs &A, int lane, int b, int g, int h, size_t bh, int base,
-                                          int cold, bool fold, float (*s_r)[P], float *s_abar,
-                                          float (*s_U)[LM + 1], float (*s_K)[N], float (*s_sw)[LM]) {
-        const int L = A.L, count = cold + 1;
-        const size_t gring = ((size_t)b * A.G + g) * L;
-        const size_t hring = bh * L;
+    __device__ __forceinline__ int finish(const StepArgs &A, int lane, int b, int g, int cold, bool fold,
+                                          float (*s_r)[P], float *s_abar, float (*s_U)[LM + 1], float (*s_K)[N],
+                                          float (*s_sw)[LM]) {
+        const int count = cold + 1;
         const int lr = lane & 15, lq = lane >> 4;
         int prev = -1;
-        if (m.j0 == 0) {
-            // this step's token goes into ring slot (pos mod L) = entry cold, as
-            // soon as it has arrived (no ring value used here comes from that slot)
-            const int sn = ring_slot(base % L, cold, L);
-#pragma unroll
-            for (int rr = 0; rr < VR; ++rr) {
-                const int p = lane + 64 * rr;
-                if (p < P) static_cast<uint16_t *>(A.ring_v)[(hring + sn) * PROW + p0 + p] = (uint16_t)vnew[rr].r;
-            }
-            if (lane == 0 && p0 == 0) {
-                A.ring_dt[hring + sn] = dt_in;
-                A.ring_a[hring + sn] = a_in;
-            }
-            if ((h % (A.H / A.G)) == 0 && p0 == 0) {
-                const size_t off = (gring + sn) * N * ES;
-                qrow.store(static_cast<char *>(A.ring_q) + off, lane);
-                krow.store(static_cast<char *>(A.ring_k) + off, lane);
-            }
-        }
         // Arrival of this ring wavefront (every ring wavefront arrives after
         // its own pointer read, which the loads above depend on).  Its result
         // is needed only at the very end.
@@ -202,5 +173,58 @@ struct StepRingMx {
         return prev;
     }
 };
+
+// Arrival at a sequence's counter: its G groups and its writer workgroup
+// arrive there; the last moves the pointer (every workgroup of the sequence
+// has read it by then).
+__device__ __forceinline__ void step_seq_arrive(const StepArgs &A, int b, int pos, bool fold) {
+    int32_t *seq = A.sync + ((size_t)b * (A.G + 1) + A.G) * kSyncStride;
+    if (atomicAdd(seq, 1) == A.G) {
+        atomicExch(seq, 0);
+        A.pos[b] = pos + 1;
+        if (fold) A.base[b] = pos + 1;
+    }
+}
+
+// The writer workgroup of sequence b: this step's token (the v row, dt and
+// a of every head, the q and k rows of every group) goes into ring slot
+// pos mod L, which no workgroup of this launch reads (entries < count - 1
+// only).  Writers follow every compute workgroup in the grid, so their
+// stores land in the launch's tail instead of between the tile reads.
+// FOLDS: the launch folds rings with count >= flush_at (base moves too).
+template <int PH, int N, bool IOB, bool FOLDS>
+__device__ __forceinline__ void step_token_writer(const StepArgs &A, int b, int tid, int nt) {
+    const int L = A.L, H = A.H, G = A.G;
+    const int base = A.base[b], pos = A.pos[b];
+    const int cold = pos - base;
+    if (cold + 1 > L || pos == 2147483647) return;   // left unchanged; the compute workgroups report it
+    const int sn = ring_slot(base % L, cold, L);
+    constexpr int ES = IOB ? 2 : 4;
+    constexpr int VP = PH * ES / 16;   // 16-byte pieces of a v row
+    constexpr int KP = N * ES / 16;    // of a q or k row
+    static_assert(PH * ES % 16 == 0 && N * ES % 16 == 0, "rows of whole 16-byte pieces");
+    for (int i = tid; i < H * VP; i += nt) {
+        const size_t bh = (size_t)b * H + i / VP;
+        const uint4 x = reinterpret_cast<const uint4 *>(static_cast<const char *>(A.v) + bh * PH * ES)[i % VP];
+        reinterpret_cast<uint4 *>(static_cast<char *>(A.ring_v) + (bh * L + sn) * PH * ES)[i % VP] = x;
+    }
+    for (int i = tid; i < 2 * G * KP; i += nt) {
+        const int r = i % (G * KP);
+        const size_t gi = (size_t)b * G + r / KP;
+        const bool kr = i >= G * KP;
+        const uint4 x = reinterpret_cast<const uint4 *>(static_cast<const char *>(kr ? A.k : A.q) + gi * N * ES)[r % KP];
+        reinterpret_cast<uint4 *>(static_cast<char *>(kr ? A.ring_k : A.ring_q) + (gi * L + sn) * N * ES)[r % KP] = x;
+    }
+    for (int i = tid; i < H; i += nt) {
+        const size_t bh = (size_t)b * H + i;
+        A.ring_dt[bh * L + sn] = A.dt[bh];
+        A.ring_a[bh * L + sn] = A.a[bh];
+    }
+    __syncthreads();   // every wavefront of the workgroup has read the pointer
+    if (tid == 0) {
+        const int need = A.flush_at > 1 ? A.flush_at : 1;
+        step_seq_arrive(A, b, pos, FOLDS && cold + 1 >= need);
+    }
+}
 
 }  // namespace replay

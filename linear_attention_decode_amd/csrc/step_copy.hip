@@ -14,8 +14,10 @@
 // The workgroup is the decode kernel's several-head workgroup for the copy
 // (the heads' tiles stream as one taller tile, bf16-pair dot products) with
 // the fused step's ring wavefronts, one per head and 16-entry block: each
-// takes this step's token from the inputs, writes it into ring slot
-// pos mod L and arrives at its group's counter; the last arrival moves pos.
+// takes this step's token from the inputs and arrives at its group's
+// counter.  A writer workgroup per sequence, after all of them in the grid,
+// copies the token into ring slot pos mod L and arrives too; the last
+// arrival moves pos.
 // Outputs equal those of the append and decode kernels run in turn, bit for
 // bit.
 #include "step_common.h"
@@ -43,9 +45,14 @@ __global__ __launch_bounds__((StepCopyLaunch<P, N, ST, LM, HPW>::NT)) void step_
     __shared__ __align__(16) float s_sw[HPW][LM];
     __shared__ int s_route;   // 0 output, 2 error (sequence left unchanged)
 
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int H = args.H, G = args.G, L = args.L;
     const int HW = H / HPW;
+    const int ncomp = args.B * HW;   // compute workgroups; one writer per sequence follows
+    if ((int)blockIdx.x >= ncomp) {
+        step_token_writer<P, N, true, false>(args, (int)blockIdx.x - ncomp, threadIdx.x, blockDim.x);
+        return;
+    }
+    const int lid = xcd_remap(blockIdx.x, ncomp);
     const int b = lid / HW, h0 = (lid % HW) * HPW;
     const int g = (h0 * G) / H;   // the HPW heads share this group
     const int tid = threadIdx.x, lane = tid & 63;
@@ -124,19 +131,15 @@ __global__ __launch_bounds__((StepCopyLaunch<P, N, ST, LM, HPW>::NT)) void step_
         if (!bad) {
             StepRingMx<P, N, LM> sr;
             sr.load(args, lane, blk, b, g, h, bh, base, cold);
-            prev = sr.finish(args, lane, b, g, h, bh, base, cold, false, &s_r[blk][hl], &s_abar[hl],
+            prev = sr.finish(args, lane, b, g, cold, false, &s_r[blk][hl], &s_abar[hl],
                              static_cast<float (*)[LM + 1]>(nullptr), static_cast<float (*)[N]>(nullptr), &s_sw[hl]);
         }
         lds_barrier();
         if (lane == 0 && prev == NR * (H / G) - 1) {
             // last ring wavefront of the group: the group arrives at the
-            // sequence's counter; the last group moves the pointer
-            int32_t *seq = args.sync + (size_t)b * (G + 1) * kSyncStride;
-            atomicExch(seq + (size_t)g * kSyncStride, 0);
-            if (atomicAdd(seq + (size_t)G * kSyncStride, 1) == G - 1) {
-                atomicExch(seq + (size_t)G * kSyncStride, 0);
-                args.pos[b] = pos + 1;
-            }
+            // sequence's counter
+            atomicExch(args.sync + ((size_t)b * (G + 1) + g) * kSyncStride, 0);
+            step_seq_arrive(args, b, pos, false);
         }
     }
 }
@@ -145,10 +148,10 @@ template <int P, int N, int ST, int LM>
 static hipError_t launch_sc_lm(const StepArgs &a, hipStream_t s) {
     constexpr int HPW = heads_per_wg<ST, 1>();
     if (HPW > 1 && (a.H / a.G) % HPW == 0) {
-        const unsigned blocks = (unsigned)((size_t)a.B * a.H / HPW);
+        const unsigned blocks = (unsigned)((size_t)a.B * a.H / HPW + a.B);
         step_copy_kernel<P, N, ST, LM, HPW><<<blocks, StepCopyLaunch<P, N, ST, LM, HPW>::NT, 0, s>>>(a);
     } else {
-        const unsigned blocks = (unsigned)((size_t)a.B * a.H);
+        const unsigned blocks = (unsigned)((size_t)a.B * a.H + a.B);
         step_copy_kernel<P, N, ST, LM, 1><<<blocks, StepCopyLaunch<P, N, ST, LM, 1>::NT, 0, s>>>(a);
     }
     return hipGetLastError();
