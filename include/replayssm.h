@@ -192,7 +192,11 @@ replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *s
    count >= max(min_count, 1) (same page, "Decodificacion estandar", step 4;
    eq. "Ruta estado y salida"): S0 <- abar_c S0 + sum_j s_{j,c} v_j k_j^T over
    the c = count entries, then base = pos, and the copy (and its per-head
-   scale) is rewritten from the new checkpoint.  Other sequences: no-op. */
+   scale) is rewritten from the new checkpoint.  Other sequences: no-op.
+   The handle keeps host-side bounds on every sequence's count from the calls
+   that move the pointers; a flush that no sequence can be due for enqueues
+   nothing (in the standard schedule, every flush but the one that folds).
+   So pos and base must change only through this library's calls. */
 replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream);
 
 /* One standard decode step for every sequence: append one token, produce its

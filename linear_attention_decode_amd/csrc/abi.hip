@@ -7,6 +7,7 @@
 #include <cstring>
 #include <new>
 
+#include "count_bound.h"
 #include "internal.h"
 
 using namespace replay;
@@ -14,6 +15,7 @@ using namespace replay;
 struct replay_handle {
     replay_config cfg;
     replay_buffers bufs;
+    CountBound bound;   // upper bounds on every sequence's count and pos
 };
 
 namespace {
@@ -130,7 +132,18 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
         st_in = ST_F32;
     }
     const int st_copy = c.read_copy == REPLAY_NONE ? -1 : state_kind(c.read_copy);
-    return from_hip(launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s));
+    // no sequence can be due: the kernel would change nothing
+    if (!load_src && !h->bound.flush_may_fold(min_count)) return REPLAY_OK;
+    const hipError_t e = launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s);
+    if (e != hipSuccess) {
+        h->bound.unknown();
+        return REPLAY_ERR_HIP;
+    }
+    if (load_src)
+        h->bound.load();
+    else
+        h->bound.flush(min_count);
+    return REPLAY_OK;
 }
 
 replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
@@ -198,6 +211,7 @@ replay_status replay_init(const replay_config *cfg, const replay_buffers *bufs, 
     if (!h) return REPLAY_ERR_INVALID_ARG;
     h->cfg = *cfg;
     h->bufs = *bufs;
+    h->bound.reset(cfg->ring_len);
     if (cfg->shared_lowp) h->bufs.s_master = nullptr;
     if (cfg->read_copy == REPLAY_NONE) h->bufs.s_copy = nullptr;
     if (cfg->read_copy != REPLAY_FP8_E4M3 && cfg->read_copy != REPLAY_FP4_E2M1) h->bufs.s_scale = nullptr;
@@ -240,9 +254,15 @@ replay_status replay_append(replay_handle *h, int32_t W, const void *q, const vo
         return REPLAY_ERR_INVALID_ARG;
     if (W < 1 || W > h->cfg.ring_len) return REPLAY_ERR_INVALID_ARG;
     const RingView r = ring_view(h);
-    return from_hip(launch_append(h->cfg.head_dim, h->cfg.state_dim, r, h->bufs.ring_q, h->bufs.ring_k,
-                                  h->bufs.ring_v, h->bufs.ring_dt, h->bufs.ring_a, h->bufs.pos, h->bufs.sync, W,
-                                  q, k, v, dt, a, as_stream(stream)));
+    const hipError_t e = launch_append(h->cfg.head_dim, h->cfg.state_dim, r, h->bufs.ring_q, h->bufs.ring_k,
+                                       h->bufs.ring_v, h->bufs.ring_dt, h->bufs.ring_a, h->bufs.pos, h->bufs.sync,
+                                       W, q, k, v, dt, a, as_stream(stream));
+    if (e != hipSuccess) {
+        h->bound.unknown();
+        return REPLAY_ERR_HIP;
+    }
+    h->bound.append(W);
+    return REPLAY_OK;
 }
 
 replay_status replay_decode(replay_handle *h, float *y, void *stream) {
@@ -257,6 +277,7 @@ replay_status replay_verify(replay_handle *h, int32_t W, float *y, void *stream)
 
 replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *stream) {
     if (!h || !n_reject || !aligned4(n_reject)) return REPLAY_ERR_INVALID_ARG;
+    h->bound.rollback();
     return from_hip(launch_rollback(ring_view(h), h->bufs.pos, n_reject, as_stream(stream)));
 }
 
@@ -313,6 +334,10 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
         replay_status st;
         if (c.io_dtype == REPLAY_BF16 && c.read_copy != REPLAY_BF16) {
             st = from_hip(launch_step_copy(c.head_dim, c.state_dim, sa, s));
+            if (st == REPLAY_OK)
+                h->bound.append(1);
+            else
+                h->bound.unknown();
         } else {
             st = replay_append(h, 1, q, k, v, dt, a, stream);
             if (st == REPLAY_OK) st = run_verify(h, 1, y, s);
@@ -320,7 +345,13 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
         if (st != REPLAY_OK) return st;
         return run_flush(h, nullptr, flush_at, s);
     }
-    return from_hip(launch_step(c.head_dim, c.state_dim, sa, s));
+    const hipError_t e = launch_step(c.head_dim, c.state_dim, sa, s);
+    if (e != hipSuccess) {
+        h->bound.unknown();
+        return REPLAY_ERR_HIP;
+    }
+    h->bound.step(flush_at);
+    return REPLAY_OK;
 }
 
 replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
@@ -340,7 +371,13 @@ replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, con
         if (st != REPLAY_OK) return st;
         return run_verify(h, W, y, s);
     }
-    return from_hip(launch_verify_step(c.head_dim, c.state_dim, sa, s));
+    const hipError_t e = launch_verify_step(c.head_dim, c.state_dim, sa, s);
+    if (e != hipSuccess) {
+        h->bound.unknown();
+        return REPLAY_ERR_HIP;
+    }
+    h->bound.verify_round(flush_at, W);
+    return REPLAY_OK;
 }
 
 replay_status replay_get_error(replay_handle *h, int32_t *word, int32_t *per_seq, void *stream) {

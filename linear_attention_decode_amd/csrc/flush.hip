@@ -33,8 +33,10 @@ struct FlushShape {
     static_assert(LPR <= 64 && 64 % LPR == 0, "row group must sit in a wavefront");
 };
 
-// HC heads of one group per workgroup, one after another: a flush that
-// finds nothing due then costs B*H/HC workgroups that only read the pointer.
+// HC heads of one group per workgroup, pipelined (each head's loads are
+// issued before the previous head is folded; the group's k rows are staged
+// once): a flush that finds nothing due costs B*H/HC workgroups that only
+// read the pointer.
 template <int P, int N, int SIN, int COPY, bool WRITE_MASTER, bool IOB, int HC>
 __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs args) {
     using Sh = FlushShape<P, N>;
@@ -71,39 +73,47 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     int prev = -1;
     if (tid == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
 
-    for (int hl = 0; hl < HC; ++hl) {
-    const int h = h0 + hl;
-    const size_t bh = (size_t)b * r.H + h;
-    // 1. tile loads, then every ring load in one batch
-    Chunk<SIN, VEC> ch[ITER];
-    const size_t tile = bh * (size_t)(P * N);
-#pragma unroll
-    for (int i = 0; i < ITER; ++i) ch[i].load(args.S_in, tile + (size_t)(i * NT + tid) * VEC);
-    const float sc_in = (SIN == ST_FP8) ? args.scale_in[bh] : 1.0f;
-
     const int bmod = base % L;
     auto slot = [&](int j) { return ring_slot(bmod, j, L); };   // entry j (0-based) of the ring
     const size_t gring = ((size_t)b * r.G + g) * L;
-    const size_t hring = bh * L;
-
-    // ring loads, all issued now from valid entries only (clamped indices;
-    // the clamped values are never used)
-    const int last = count > 0 ? count - 1 : 0;
-    float my_a = 1.f, my_dt = 0.f;
-    if (count > 0) {
-        const int sl = slot(tid < count ? tid : last);
-        my_a = r.a[hring + sl];
-        my_dt = r.dt[hring + sl];
-    }
+    const int last = count > 0 ? count - 1 : 0;   // clamp for ring loads (clamped values are never used)
     const int vp = tid % P, vg = tid / P;
-    IoVec<IOB, 1> vraw[JPG];
+
+    // What one head needs from memory: its tile and its ring entries (a, dt,
+    // v).  The HC heads of a workgroup are pipelined: head hl+1's loads are
+    // issued before head hl is folded, so the memory latency is paid once per
+    // workgroup instead of once per head.
+    struct HeadLoads {
+        Chunk<SIN, VEC> ch[ITER];
+        float a, dt;
+        IoVec<IOB, 1> v[JPG];
+    };
+    auto issue = [&](int hl, HeadLoads &hd) {
+        const size_t bh = (size_t)b * r.H + h0 + hl;
+        const size_t tile = bh * (size_t)(P * N);
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) hd.ch[i].load(args.S_in, tile + (size_t)(i * NT + tid) * VEC);
+        hd.a = 1.f;
+        hd.dt = 0.f;
+        if (count > 0) {
+            const size_t hring = bh * L;
+            const int sl = slot(tid < count ? tid : last);
+            hd.a = r.a[hring + sl];
+            hd.dt = r.dt[hring + sl];
+#pragma unroll
+            for (int i = 0; i < JPG; ++i) {
+                const int j = vg + i * JG;
+                hd.v[i].load(r.v, (hring + slot(j < count ? j : last)) * P + vp);
+            }
+        }
+    };
+
+    // 1. the first head's loads, then the group's k rows (shared by the HC
+    // heads: loaded and staged once)
+    HeadLoads cur, nxt;
+    issue(0, cur);
     IoVec<IOB, 4> kraw[KPT];
     if (count > 0) {
-#pragma unroll
-        for (int i = 0; i < JPG; ++i) {
-            const int j = vg + i * JG;
-            vraw[i].load(r.v, (hring + slot(j < count ? j : last)) * P + vp);
-        }
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int piece = tid + i * NT;
@@ -111,11 +121,20 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
             kraw[i].load(r.k, (gring + slot(j < count ? j : last)) * N + n);
         }
     }
+    float *U = smem;
+    float *Ks = smem + P * count;
+
+#pragma unroll
+    for (int hl = 0; hl < HC; ++hl) {
+    const size_t bh = (size_t)b * r.H + h0 + hl;
+    const size_t tile = bh * (size_t)(P * N);
+    const float sc_in = (SIN == ST_FP8) ? args.scale_in[bh] : 1.0f;
+    if (hl + 1 < HC) issue(hl + 1, nxt);
 
     // 2. segment weights of the c entries
     if (tid < count) {
-        s_a[tid] = my_a;
-        s_dt[tid] = my_dt;
+        s_a[tid] = cur.a;
+        s_dt[tid] = cur.dt;
     }
     __syncthreads();
     if (tid < count) {
@@ -130,23 +149,23 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     }
     __syncthreads();
 
-    // 3. stage U[p][j] = s_j v_j[p] and K[j][n] = k_j[n]
-    float *U = smem;
-    float *Ks = smem + P * count;
+    // 3. stage U[p][j] = s_j v_j[p] (and, for the first head, K[j][n] = k_j[n])
 #pragma unroll
     for (int i = 0; i < JPG; ++i) {
         const int j = vg + i * JG;
-        if (j < count) U[vp * count + j] = s_w[j] * vraw[i].value();
+        if (j < count) U[vp * count + j] = s_w[j] * cur.v[i].value();
     }
+    if (hl == 0) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-        const int piece = tid + i * NT;
-        const int j = piece / (N / 4), n = (piece % (N / 4)) * 4;
-        if (j < count) {
-            float kk[4];
-            kraw[i].widen(kk);
+        for (int i = 0; i < KPT; ++i) {
+            const int piece = tid + i * NT;
+            const int j = piece / (N / 4), n = (piece % (N / 4)) * 4;
+            if (j < count) {
+                float kk[4];
+                kraw[i].widen(kk);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Ks[j * N + n + e] = kk[e];
+                for (int e = 0; e < 4; ++e) Ks[j * N + n + e] = kk[e];
+            }
         }
     }
     __syncthreads();
@@ -157,7 +176,7 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     float x[ITER][VEC];
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {
-        ch[i].widen(x[i], sc_in);
+        cur.ch[i].widen(x[i], sc_in);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[i][e] *= abar;
     }
@@ -240,7 +259,10 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
         }
     }
 
-    if (HC > 1) __syncthreads();   // LDS is reused by the next head
+    if (hl + 1 < HC) {
+        __syncthreads();   // LDS is reused by the next head
+        cur = nxt;
+    }
     }
 
     // Last workgroup of its group: the group arrives at the sequence's
