@@ -129,9 +129,19 @@ def cpu_baseline(w, target_s=12.0, steps=256, chunk=32):
     nseq = int(max(4, min(w.batch, target_s / (per_token * steps))))
     S = np.zeros((nseq, w.heads, w.head_dim, w.state_dim))
     dt = run(nseq, steps, S)
-    return {"value": nseq * steps / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    cores = oracle.threads()
+    # the same oracle on one core, over a smaller sample (first 16 sequences x 64 steps)
+    n1, t1 = min(16, w.batch), min(64, steps)
+    oracle.set_threads(1)
+    try:
+        dt1 = run(n1, t1, np.zeros((n1, w.heads, w.head_dim, w.state_dim)))
+    finally:
+        oracle.set_threads(cores)
+    return {"value": nseq * steps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"float64 eager recurrence, first {nseq} of {w.batch} sequences x {steps} steps "
-                      f"of the same layer ({dt:.1f} s host time, input generation excluded)"}
+                      f"of the same layer ({dt:.1f} s host time, input generation excluded)",
+            "one_core": {"value": n1 * t1 / dt1, "unit": "tokens/s", "cores": 1,
+                         "sample": f"first {n1} sequences x {t1} steps ({dt1:.1f} s host time)"}}
 
 
 def _counter_traffic(kernel_files, summary_name):

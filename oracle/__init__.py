@@ -16,9 +16,9 @@ Contents
 
 Parity status of every function is listed in its module docstring.
 """
-from .core import (build, lib, threads, widen, eager, bf16_encode, bf16_decode,
+from .core import (build, lib, threads, set_threads, widen, eager, bf16_encode, bf16_decode,
                    e4m3_encode, e4m3_decode, quant_heads_e4m3)
 from . import forms, ring, runs
 
-__all__ = ["build", "lib", "threads", "widen", "eager", "bf16_encode", "bf16_decode",
+__all__ = ["build", "lib", "threads", "set_threads", "widen", "eager", "bf16_encode", "bf16_decode",
            "e4m3_encode", "e4m3_decode", "quant_heads_e4m3", "forms", "ring", "runs"]

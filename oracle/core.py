@@ -48,6 +48,7 @@ def lib():
             L.oracle_eager.argtypes = [_I64] * 6 + [_F64P] * 7
             L.oracle_eager.restype = None
             L.oracle_threads.restype = ctypes.c_int
+            L.oracle_set_threads.argtypes = [ctypes.c_int]
             L.oracle_bf16_encode_n.argtypes = [_F32P, _U16P, _I64]
             L.oracle_bf16_decode_n.argtypes = [_U16P, _F32P, _I64]
             L.oracle_e4m3_encode_n.argtypes = [_F32P, _U8P, _I64]
@@ -63,6 +64,11 @@ def lib():
 
 def threads() -> int:
     return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for later oracle calls (a timing knob; the results do not depend on it)."""
+    lib().oracle_set_threads(int(n))
 
 
 def _p(a, t):

@@ -99,6 +99,16 @@ int oracle_threads(void)
 #endif
 }
 
+/* Set the number of threads later oracle calls use (timing on one core). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* bf16                                                                      */
 /* ------------------------------------------------------------------------ */
