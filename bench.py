@@ -432,7 +432,7 @@ def bench_verify(args):
     else:
         vbytes = sum(float(np.mean([decode_bytes(w, c, W) / B for c in at_verify[WU + k]])) * B
                      for k in sampled)
-        kernel_name = f"verify (W={W}{', matrix cores' if W > 8 else ''})"
+        kernel_name = f"verify (W={W}{', matrix cores' if W >= 6 else ''})"
     achieved = vbytes / (sum(ver_ms) / 1e3) / 1e9
     layer.close()
     del layer

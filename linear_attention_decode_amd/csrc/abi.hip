@@ -157,11 +157,11 @@ replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
     a.y = y;
     a.W = W;
     const int st = state_kind(c.read_copy);
-    if (W > kMaxWindow) {
-        // wide windows: the matrix-core kernel (bf16 io; float32, bf16 or e4m3 reads)
-        if (!verify_wide_supported(st, a)) return REPLAY_ERR_UNSUPPORTED;
+    // windows from kWideFrom on: the matrix-core kernel where it applies (bf16
+    // io; float32, bf16 or e4m3 reads), else the register kernel up to kMaxWindow
+    if (W >= kWideFrom && verify_wide_supported(st, a))
         return from_hip(launch_verify_wide(c.head_dim, c.state_dim, st, a, s));
-    }
+    if (W > kMaxWindow) return REPLAY_ERR_UNSUPPORTED;
     return from_hip(launch_decode(c.head_dim, c.state_dim, st, a, s));
 }
 

@@ -14,7 +14,9 @@ enum StateKind : int { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2, ST_FP4 = 3 };
 // Largest ring and verify window the kernels are built for.
 constexpr int kMaxRing = 32;
 constexpr int kMaxWindow = 8;        // verify windows of the register kernel (decode_impl.h)
-constexpr int kMaxWideWindow = 16;   // wide windows on the matrix cores (verify_wide.hip)
+constexpr int kMaxWideWindow = 16;   // windows on the matrix cores (verify_wide.hip)
+constexpr int kWideFrom = 6;         // replay_verify takes the matrix cores from this window on
+                                     // (where they are supported; measured faster from W = 5-6)
 
 // Arrival counters of the fused step, [B][G + 1] of them, one int32 per
 // 128-byte line: a workgroup arrives at its group's counter, the last head
@@ -88,7 +90,7 @@ struct EagerArgs {
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_decode(int P, int N, int st, const DecodeArgs &a, hipStream_t s);
-hipError_t launch_verify_wide(int P, int N, int st, const DecodeArgs &a, hipStream_t s);   // kMaxWindow < W <= 16
+hipError_t launch_verify_wide(int P, int N, int st, const DecodeArgs &a, hipStream_t s);   // 1 <= W <= 16
 bool verify_wide_supported(int st, const DecodeArgs &a);
 hipError_t launch_flush(int P, int N, int st_in, int st_copy, bool write_master, const FlushArgs &a,
                         hipStream_t s);

@@ -1,5 +1,5 @@
-// verify_wide.hip -- speculative verify of wide windows (kMaxWindow < W <= 16)
-// on the matrix cores, bf16 io.
+// verify_wide.hip -- speculative verify of windows of up to 16 drafts on the
+// matrix cores, bf16 io (replay_verify takes it from W = kWideFrom on).
 //
 // The same outputs as the verify kernel of decode_impl.h: for the W newest
 // ring entries t_w = count-W+w of every (sequence, head)
@@ -7,13 +7,13 @@
 // against one read of the checkpoint (page "ReplaySSM: Cachear Inputs, No
 // Estado", section "Paralelismo": every window position reads the same
 // checkpoint and buffer, entry j visible to position t when j <= t; eq. "Ruta
-// solo salida").  With W queries every state element enters W products; past
-// eight the per-row partial sums of the register kernel no longer fit, and
-// S Q^T is formed as a matrix product instead:
-//   - streaming wavefront i loads rows 16i..16i+15 of the head's tile straight
-//     into the matrix cores' operand layout (lane (row r, group g) reads 16
-//     bytes of row 16i+r; one load covers 16 rows x 64 bytes), so the tile
-//     never passes through LDS;
+// solo salida").  With W queries every state element enters W products; the
+// register kernel's per-row partial sums grow with W (past eight they no
+// longer fit), and here S Q^T is formed as a matrix product instead:
+//   - streaming wavefront i reads rows 16i..16i+15 of the head's tile in
+//     128-byte row segments (8 lanes to a cache line) and turns each 16-row
+//     chunk into the matrix cores' operand layout (lane (row r, group g): 16
+//     bytes of row 16i+r) through its own small LDS buffer;
 //   - the W queries go to LDS as rows Q[w][n] (rows w >= W zero);
 //   - D = S Q^T for the 16 rows:
 //       float32 tiles: v_mfma_f32_16x16x4_f32, four per 16 columns: the t-th
@@ -48,6 +48,15 @@ struct WideShape {
     static constexpr int TS = BF ? N + 8 : N + 4;                  // LDS row stride of Q, in elements
     static constexpr int NR = LM / 16;
     static constexpr int NT = NTS + 64 * NR;
+    // Coalesced staging (16-byte lane steps, rows of whole 128-byte lines):
+    // the tile is read in 128-byte row segments, 8 lanes to a line, and each
+    // wavefront turns its 16 x 128-byte chunks into the operand layout
+    // through its own LDS buffer.  Loading the operand layout directly makes
+    // every load instruction touch 16 half lines, twice the cache requests.
+    static constexpr int RB = N * ESZ;   // bytes of a tile row
+    static constexpr bool COAL = (ST == ST_F32 || BF) && RB % 128 == 0;
+    static constexpr int TROW = 36;      // staging row stride in words (128 bytes + 16 of padding)
+    static_assert(!COAL || STEPS == 2 * (RB / 128), "two load steps per 128-byte chunk");
     static_assert(P % 16 == 0 && N % 16 == 0 && N % (4 * CVEC) == 0, "tile shape");
 };
 
@@ -112,6 +121,7 @@ struct WideA<ST_F32, false> {   // 4 floats
     __device__ __forceinline__ void load(const void *S, size_t e) {
         v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(static_cast<const float *>(S) + e));
     }
+    __device__ __forceinline__ void set(uint4 u) { v = __builtin_bit_cast(f32x4, u); }
     __device__ __forceinline__ f32x4 f32() const { return v; }
 };
 template <>
@@ -145,6 +155,7 @@ struct WideA<ST, true> {   // 16 bytes: 8 bf16, or 16 e4m3 codes
         const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
         v = uint4{w.x, w.y, w.z, w.w};
     }
+    __device__ __forceinline__ void set(uint4 u) { v = u; }
     // e4m3: codes 8h..8h+7 as bf16 pairs (exact)
     __device__ __forceinline__ uint4 bf16_half(int h) const {
         const uint32_t w0 = h ? v.z : v.x, w1 = h ? v.w : v.y;
@@ -165,6 +176,7 @@ __global__ __launch_bounds__((WideShape<P, N, ST, LM>::NT)) void verify_wide_ker
     __shared__ __align__(16) TE s_Q[kWide][TS];    // the window's queries, Q[w][n]
     __shared__ float s_r[NR][kWide][P];
     __shared__ float s_abar[kWide];
+    __shared__ __align__(16) uint32_t s_T[WS::COAL ? NTS / 64 : 1][16][WS::TROW];   // per-wavefront staging
 
     const RingView &r = args.r;
     const int W = args.W;
@@ -182,10 +194,21 @@ __global__ __launch_bounds__((WideShape<P, N, ST, LM>::NT)) void verify_wide_ker
     const int base = r.base[b];
     const int pos = r.pos[b];
     WideA<ST, BF> at[STEPS];
+    uint4 raw[WS::COAL ? STEPS : 1];   // coalesced: load 2c + hf = rows 8hf + lane/8, bytes 128c + 16 (lane % 8)
     if (wave < NTS / 64) {
-        const size_t row = bh * (size_t)(P * N) + (size_t)(p0 + lr) * N;
+        if constexpr (WS::COAL) {
+            const char *t = static_cast<const char *>(args.S) + (bh * (size_t)(P * N) + (size_t)p0 * N) * WS::ESZ;
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) at[st].load(args.S, row + (size_t)(4 * st + lg) * CVEC);
+            for (int i = 0; i < STEPS; ++i) {
+                const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                    t + (size_t)(8 * (i & 1) + (lane >> 3)) * WS::RB + 128 * (i >> 1) + 16 * (lane & 7)));
+                raw[i] = uint4{w.x, w.y, w.z, w.w};
+            }
+        } else {
+            const size_t row = bh * (size_t)(P * N) + (size_t)(p0 + lr) * N;
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) at[st].load(args.S, row + (size_t)(4 * st + lg) * CVEC);
+        }
     }
     const int count = pos - base;
     if (count < W) {  // uniform over the workgroup
@@ -239,6 +262,22 @@ __global__ __launch_bounds__((WideShape<P, N, ST, LM>::NT)) void verify_wide_ker
     __syncthreads();
 
     {
+        if constexpr (WS::COAL) {
+            // chunk by chunk through this wavefront's buffer: lane (row lr,
+            // group lg) of step st reads row lr, bytes 64 (st % 2) + 16 lg of
+            // chunk st / 2 (a wavefront's own LDS accesses complete in order,
+            // so the next chunk's writes follow this chunk's reads)
+            uint32_t(*T)[WS::TROW] = s_T[wave];
+#pragma unroll
+            for (int c = 0; c < STEPS / 2; ++c) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    *reinterpret_cast<uint4 *>(&T[8 * hf + (lane >> 3)][4 * (lane & 7)]) = raw[2 * c + hf];
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    at[2 * c + s2].set(*reinterpret_cast<const uint4 *>(&T[lr][16 * s2 + 4 * lg]));
+            }
+        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
@@ -299,7 +338,7 @@ static hipError_t launch_wide_pn(int st, const DecodeArgs &a, hipStream_t s) {
 }
 
 bool verify_wide_supported(int st, const DecodeArgs &a) {
-    return a.r.io_bf16 && (st == ST_F32 || st == ST_BF16 || st == ST_FP8) && a.W > kMaxWindow &&
+    return a.r.io_bf16 && (st == ST_F32 || st == ST_BF16 || st == ST_FP8) && a.W >= 1 &&
            a.W <= kMaxWideWindow && a.W <= a.r.L;
 }
 

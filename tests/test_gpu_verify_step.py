@@ -4,7 +4,9 @@ due, append the drafts, score them, in one launch.
 - Bit for bit against the same rounds run as the flush, append and verify
   calls (outputs, checkpoints, pointers and every ring slot), over shapes
   with ragged groups, both routes (fold / no fold) mixed inside one launch,
-  and the configurations that fall back to the calls.
+  and the configurations that fall back to the calls.  Where the fused launch
+  serves W >= 6 (register sums) and replay_verify takes the matrix cores,
+  the outputs agree to 1e-5 per token instead (same products, another order).
 - Against the float64 oracle at the verify workload's full size (B=256,
   H=64, W=5, 128 rounds; sampled sequences) with the ring integers of all
   sequences checked after every round, and at small sizes on every sequence.
@@ -57,7 +59,12 @@ def test_verify_step_equals_calls(P, N, io, L, W, B, H, G, rc):
     y_c = gu.run_verify(calls, w, dev, R, W, accept)
     torch.cuda.synchronize()
     assert fused.get_error()[0] == 0 and calls.get_error()[0] == 0
-    assert np.array_equal(y_f.cpu().numpy(), y_c.cpu().numpy())
+    one_launch = io == "bf16" and L <= 16 and rc is None
+    if one_launch and W >= 6:
+        tok, _, _ = gu.errors(y_f.cpu().numpy(), y_c.cpu().numpy().astype(np.float64))
+        assert tok <= 1e-5, tok
+    else:
+        assert np.array_equal(y_f.cpu().numpy(), y_c.cpu().numpy())
     assert np.isfinite(y_f.cpu().numpy()).all()
     for name in ("s_master", "pos", "base") + RING:
         assert torch.equal(fused.t[name], calls.t[name]), name
