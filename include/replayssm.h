@@ -176,7 +176,7 @@ replay_status replay_decode(replay_handle *h, float *y, void *stream);
    Position w (0-based) is ring entry t_w = count - W + 1 + w.
    y: [B][W][H][P] f32.  1 <= W <= min(8, L) for every configuration; with
    bf16 io and a float32, bf16 or e4m3 read also up to min(16, L), and from
-   W = 6 on such windows take the window's S Q^T on the matrix cores (other
+   W = 5 on such windows take the window's S Q^T on the matrix cores (other
    configurations return UNSUPPORTED for W > 8).  Needs count >= W per
    sequence (else TOO_FEW, NaN outputs for that sequence). */
 replay_status replay_verify(replay_handle *h, int32_t W, float *y, void *stream);
@@ -228,11 +228,8 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
    estandar", step 4, for the fold; section "Rollback": the caller then
    drops rejected drafts with replay_rollback).  flush_at = L - W + 1 folds
    exactly when the drafts would not fit otherwise.
-   Equivalent to replay_flush(flush_at); replay_append(W); replay_verify(W):
-   checkpoints, copies, ring slots and pointers bit for bit, and the outputs
-   too except where the one launch below serves 6 <= W <= 8 (it scores with
-   the register method, replay_verify with the matrix cores: the same sums in
-   another order, equal to float32 rounding).  q, k: [B][W][G][N]; v: [B][W][H][P] (io dtype); dt, a:
+   Equivalent to replay_flush(flush_at); replay_append(W); replay_verify(W),
+   bit for bit.  q, k: [B][W][G][N]; v: [B][W][H][P] (io dtype); dt, a:
    [B][W][H] f32; y: [B][W][H][P] f32, draft w at [b][w].  1 <= W <= min(16, L)
    (windows past 8 as for replay_verify, through the kernels in turn).
    With a float32 checkpoint read, bf16 io, L <= 16 and W <= 8 it is one kernel

@@ -15,7 +15,7 @@ enum StateKind : int { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2, ST_FP4 = 3 };
 constexpr int kMaxRing = 32;
 constexpr int kMaxWindow = 8;        // verify windows of the register kernel (decode_impl.h)
 constexpr int kMaxWideWindow = 16;   // windows on the matrix cores (verify_wide.hip)
-constexpr int kWideFrom = 6;         // replay_verify takes the matrix cores from this window on
+constexpr int kWideFrom = 6;         // replay_verify and the fused verify round take the matrix cores from here on
                                      // (where they are supported; measured faster from W = 5-6)
 
 // Arrival counters of the fused step, [B][G + 1] of them, one int32 per

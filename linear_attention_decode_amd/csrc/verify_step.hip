@@ -31,6 +31,7 @@
 // wavefront to arrive; each ring wavefront arrives only once its loads have
 // returned.  The pointer moves when the sequence's last group arrives.
 #include "step_common.h"
+#include "wide_mx.h"
 
 namespace replay {
 
@@ -235,6 +236,95 @@ __device__ __forceinline__ int vs_fold_wave(const StepArgs &A, int lane, int b, 
     return prev;
 }
 
+// The streaming wavefronts with the window's products on the matrix cores
+// (W >= kWideFrom; wide_mx.h, the same code and operands as the matrix-core
+// verify kernel, so a round equals the flush, append and verify calls bit
+// for bit).  Wavefront i owns rows 16i..16i+15 of the head's tile.  The fold
+// runs on whichever layout holds the rows, element by element in the flush
+// kernel's order (abar_c S0, then the entries' products one after another),
+// writes S_new there and takes the products from it.
+template <int P, int N, int W, class QRows, class TRows>
+__device__ __forceinline__ void verify_step_streamer_mx(const StepArgs &args, int tid, int lane, int wave, int b,
+                                                        int g, int h, size_t bh, size_t tile, QRows s_Q, TRows T,
+                                                        float (*s_r)[P], float *s_abar, float (*s_U)[kVsRing + 1],
+                                                        float (*s_K)[N], float &s_fabar, int &s_route,
+                                                        int &s_fcount) {
+    using WT = WideTile<P, N, ST_F32>;
+    constexpr int NTS = WT::NTS;
+    const int H = args.H, G = args.G;
+    const int p0 = 16 * wave;
+    // the drafts' queries first (rows w < W of Q, 8 elements a thread; rows
+    // past W zero): loads complete in order, so waiting for them before the
+    // LDS write does not wait for the tile
+    constexpr int QP = kWide * N / 8, QI = (QP + NTS - 1) / NTS;
+    uint4 qraw[QI];
+#pragma unroll
+    for (int i = 0; i < QI; ++i) {
+        const int e = (i * NTS + tid < QP ? i * NTS + tid : QP - 1) * 8;
+        const int w = e / N, n = e % N;
+        qraw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(args.q) +
+                                                  (((size_t)b * W + (w < W ? w : W - 1)) * G + g) * N + n);
+    }
+    asm volatile("" ::: "memory");
+    WideRows<P, N, ST_F32> rows;
+    rows.load(args.S, tile, p0, lane);
+#pragma unroll
+    for (int i = 0; i < QI; ++i) {
+        if (i * NTS + tid < QP) {
+            const int e = (i * NTS + tid) * 8;
+            const int w = e / N, n = e % N;
+            wide_put_q<P, N, ST_F32>(s_Q, w, n, w < W ? qraw[i] : uint4{0u, 0u, 0u, 0u});
+        }
+    }
+    lds_barrier();   // the route, the queries
+    const int route = s_route;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (route == 0) {
+        rows.transpose(T, lane);
+        acc = rows.dot(s_Q, lane);
+    }
+    lds_barrier();   // the ring terms and the fold's staging
+    if (route == 2) {
+        for (int i = tid; i < W * P; i += NTS)
+            args.y[(((size_t)b * W + i / P) * H + h) * P + i % P] = __builtin_nanf("");
+        return;
+    }
+    if (route == 1) {
+        // fold: S_new = abar_c S0 + sum_j U[row][j] K[j][col], written once
+        const float abar = s_fabar;
+        const int c = s_fcount;
+        rows.each_f32(lane, [&](f32x4 &x, int, int) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] *= abar;
+        });
+#pragma unroll 1   // keeps the LDS operands of one entry in registers at a time
+        for (int j = 0; j < c; ++j) {
+            rows.each_f32(lane, [&](f32x4 &x, int r, int c0) {
+                const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_K[j][c0]);
+                const float u = s_U[p0 + r][j];
+                x[0] = fmaf(u, kk.x, x[0]);
+                x[1] = fmaf(u, kk.y, x[1]);
+                x[2] = fmaf(u, kk.z, x[2]);
+                x[3] = fmaf(u, kk.w, x[3]);
+            });
+        }
+        rows.each_f32(lane, [&](f32x4 &x, int r, int c0) {
+            __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(args.S + tile + (size_t)(p0 + r) * N + c0));
+        });
+        rows.transpose(T, lane);
+        acc = rows.dot(s_Q, lane);
+    }
+    // D[p0 + 4 lg + rr][w = lane % 16]
+    const int w = lane & 15, lg = lane >> 4;
+    if (w < W) {
+        const float ab = s_abar[w];
+        f32x4 o;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) o[rr] = wide_out(ab, 1.0f, acc[rr], s_r[w][p0 + 4 * lg + rr]);
+        *reinterpret_cast<f32x4 *>(&args.y[(((size_t)b * W + w) * H + h) * P + p0 + 4 * lg]) = o;
+    }
+}
+
 // Waves per SIMD to ask the register allocator for: 8 (64 registers) for the
 // 64 x 128 tile, which then fits with a few spilled words (measured faster
 // than 67 registers at 7 waves); the other tiles fit or spill too much.
@@ -253,7 +343,13 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
     __shared__ __align__(16) float s_sw[W][LM];
     __shared__ float s_U[P][LM + 1];
     __shared__ __align__(16) float s_K[LM][N];
-    __shared__ __align__(16) float s_q[W][N];   // the drafts' queries, widened
+    // the drafts' queries, widened: rows for the register sums (W < kWideFrom),
+    // or the matrix cores' Q (16 rows, past W zero) and per-wavefront staging
+    constexpr bool MX = W >= kWideFrom;
+    using WT = WideTile<P, N, ST_F32>;
+    __shared__ __align__(16) float s_q[MX ? 1 : W][N];
+    __shared__ __align__(16) uint16_t s_Q[MX ? kWide : 1][WT::TS];
+    __shared__ __align__(16) uint32_t s_T[MX && WT::COAL ? NTS / 64 : 1][16][WT::TROW];
     __shared__ float s_fabar;
     __shared__ int s_route;   // 0 keep the ring, 1 fold first, 2 error (sequence left unchanged)
     __shared__ int s_fcount;
@@ -281,6 +377,10 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
     // with both barriers), so neither role's registers are live in the
     // other's code.
     if (streamer) {
+      if constexpr (MX) {
+        verify_step_streamer_mx<P, N, W>(args, tid, lane, wave, b, g, h, bh, tile, s_Q, s_T[WT::COAL ? wave : 0],
+                                         s_r, s_abar, s_U, s_K, s_fabar, s_route, s_fcount);
+      } else {
         using Fin = float[RR::FINAL][W];
         // The drafts' queries, widened into LDS (published by the first
         // barrier).  They are loaded before the tile: loads complete in
@@ -386,6 +486,7 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
                     args.y[(((size_t)b * W + w) * H + h) * P + row] = s_abar[w] * fin[e][w] + s_r[w][row];
             }
         }
+      }
     } else {
         const int base = args.base[b];
         const int pos = args.pos[b];

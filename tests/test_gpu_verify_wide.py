@@ -1,12 +1,12 @@
-"""Speculative verify on the matrix cores (replay_verify from W = 6 on, up
+"""Speculative verify on the matrix cores (replay_verify from W = 5 on, up
 to 16, with bf16 io).
 
 - Rounds of W drafts with rollback and flushes when the next window would
   not fit, against the float64 oracle (per token over the layer output:
   1e-4 for a float32 checkpoint; bf16 / e4m3 copies against the oracle's
   emulation of the same copy, 1e-3 / 1e-2) and the integer ring model.
-- The same state scored with W = 16 here and W = 5 by the register kernel:
-  the newest five positions agree to float32 rounding (the two kernels share
+- The same state scored with W = 16 here and W = 4 by the register kernel:
+  the newest four positions agree to float32 rounding (the two kernels share
   nothing but the ring term's code).
 - Errors: count < W gives NaN and TOO_FEW; configurations the matrix cores
   do not serve (an FP4 copy, float32 io) are rejected past W = 8."""
@@ -37,7 +37,7 @@ def _layer(w, **kw):
     (64, 128, 16, 16, 3, 8, 2, "bf16"),
     (64, 128, 16, 10, 3, 8, 2, "fp8"),
     (16, 16, 16, 16, 2, 4, 1, "fp8"),      # e4m3 tile widened (N < 32)
-    (64, 128, 16, 6, 3, 8, 2, None),       # the smallest window on the matrix cores
+    (64, 128, 16, 5, 3, 8, 2, None),       # the smallest window on the matrix cores
     (64, 128, 8, 8, 2, 8, 2, "bf16"),
 ])
 def test_wide_verify_rounds(P, N, L, W, B, H, G, copy):
@@ -66,8 +66,8 @@ def test_wide_verify_rounds(P, N, L, W, B, H, G, copy):
 
 @pytest.mark.parametrize("P,N,copy", [(64, 128, None), (128, 128, None), (64, 128, "fp8")])
 def test_wide_window_agrees_with_register_kernel(P, N, copy):
-    """16 entries in the ring: verify(16) on the matrix cores and verify(5) in
-    registers score the newest five positions of the same state."""
+    """16 entries in the ring: verify(16) on the matrix cores and verify(4) in
+    registers score the newest four positions of the same state."""
     w = synth.Workload(batch=3, heads=8, groups=2, head_dim=P, state_dim=N, ring_len=16, io_dtype="bf16",
                        config=synth.CONFIG_ID["misc"], layer=330 + P)
     gu.note(f"wide vs register verify P={P} N={N} copy={copy}")
@@ -79,12 +79,12 @@ def test_wide_window_agrees_with_register_kernel(P, N, copy):
     layer.flush(1)                             # empty ring, then a full one
     layer.append(16, *dev.window(24, 16))
     y16 = torch.empty((3, 16, 8, P), dtype=torch.float32, device=gu.DEV)
-    y5 = torch.empty((3, 5, 8, P), dtype=torch.float32, device=gu.DEV)
+    y4 = torch.empty((3, 4, 8, P), dtype=torch.float32, device=gu.DEV)
     layer.verify(16, y16)
-    layer.verify(5, y5)
+    layer.verify(4, y4)
     torch.cuda.synchronize()
     assert layer.get_error()[0] == 0
-    tok, _, _ = gu.errors(y16[:, 11:].cpu().numpy(), y5.cpu().numpy().astype(np.float64))
+    tok, _, _ = gu.errors(y16[:, 12:].cpu().numpy(), y4.cpu().numpy().astype(np.float64))
     assert tok <= 1e-5, tok
     layer.close()
 
