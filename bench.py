@@ -176,10 +176,12 @@ STEP_SOURCES = ["linear_attention_decode_amd/csrc/step.hip",
                 "linear_attention_decode_amd/csrc/ring_mx.h",
                 "linear_attention_decode_amd/csrc/device_common.h"]
 VERIFY_STEP_SOURCES = ["linear_attention_decode_amd/csrc/verify_step.hip",
+                       "linear_attention_decode_amd/csrc/wide_mx.h",
                        "linear_attention_decode_amd/csrc/step_common.h",
                        "linear_attention_decode_amd/csrc/ring_mx.h",
                        "linear_attention_decode_amd/csrc/device_common.h"]
 VERIFY_WIDE_SOURCES = ["linear_attention_decode_amd/csrc/verify_wide.hip",
+                       "linear_attention_decode_amd/csrc/wide_mx.h",
                        "linear_attention_decode_amd/csrc/decode_impl.h",
                        "linear_attention_decode_amd/csrc/ring_mx.h",
                        "linear_attention_decode_amd/csrc/device_common.h"]
