@@ -16,7 +16,8 @@ constexpr int kMaxRing = 32;
 constexpr int kMaxWindow = 8;        // verify windows of the register kernel (decode_impl.h)
 constexpr int kMaxWideWindow = 16;   // windows on the matrix cores (verify_wide.hip)
 constexpr int kWideFrom = 6;         // replay_verify and the fused verify round take the matrix cores from here on
-                                     // (where they are supported; measured faster from W = 5-6)
+                                     // (where supported): both switch together, so a fused round equals the calls
+                                     // bit for bit; at W = 5 the fused round is faster with register sums
 
 // Arrival counters of the fused step, [B][G + 1] of them, one int32 per
 // 128-byte line: a workgroup arrives at its group's counter, the last head

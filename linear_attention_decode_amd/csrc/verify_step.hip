@@ -17,8 +17,10 @@
 // turn, bit for bit; the checkpoint is read once per round and written only
 // where it folds.
 //
-// Workgroup = the streaming wavefronts of the fused step (the head's tile in
-// 16-byte chunks, S q_w for every draft) + 2 ring wavefronts:
+// Workgroup = the streaming wavefronts (the head's tile, S q_w for every
+// draft: register sums over the fused step's 16-byte chunks for W < kWideFrom,
+// the matrix-core products of wide_mx.h from kWideFrom on) + 2 ring
+// wavefronts:
 //   term wavefront   group dots and ring term of the window on the matrix
 //                    cores (ring_mx.h); entries kept from before the round
 //                    come from the ring, the drafts from the inputs;
