@@ -1,4 +1,4 @@
-"""Speculative verify on the matrix cores (replay_verify from W = 5 on, up
+"""Speculative verify on the matrix cores (replay_verify from W = 6 on, up
 to 16, with bf16 io).
 
 - Rounds of W drafts with rollback and flushes when the next window would
@@ -37,7 +37,7 @@ def _layer(w, **kw):
     (64, 128, 16, 16, 3, 8, 2, "bf16"),
     (64, 128, 16, 10, 3, 8, 2, "fp8"),
     (16, 16, 16, 16, 2, 4, 1, "fp8"),      # e4m3 tile widened (N < 32)
-    (64, 128, 16, 5, 3, 8, 2, None),       # the smallest window on the matrix cores
+    (64, 128, 16, 6, 3, 8, 2, None),       # the smallest window on the matrix cores
     (64, 128, 8, 8, 2, 8, 2, "bf16"),
 ])
 def test_wide_verify_rounds(P, N, L, W, B, H, G, copy):
