@@ -305,6 +305,14 @@ def bench_decode(args):
         kernel_time = sum(step_ms) / 1e3
         avg_us = 1e3 * sum(step_ms) / len(step_ms)
         kernel_name = "step (append + output-only decode, or append + fold on full rings)"
+        # the two routes apart: output-only launches (read-bound) and folding ones (read + write)
+        by_route = {}
+        for route, sel in (("output_only", False), ("fold", True)):
+            b_r = sum(step_bytes(w, c, f) for c, f in zip(counts, folds) if f == sel)
+            t_r = sum(m for m, f in zip(step_ms, folds) if f == sel) / 1e3
+            if t_r > 0:
+                by_route[route] = {"achieved": b_r / t_r / 1e9, "frac": b_r / t_r / 1e9 / HBM_PEAK_GBS,
+                                   "launches": sum(1 for f in folds if f == sel)}
     else:
         dec_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in sampled]
         fl_ms = [evs[k][2].elapsed_time(evs[k][3]) for k in sampled if (args.warmup + k + 1) % L == 0]
@@ -312,6 +320,7 @@ def bench_decode(args):
         kernel_time = sum(dec_ms) / 1e3
         avg_us = 1e3 * sum(dec_ms) / len(dec_ms)
         kernel_name = "decode (output-only)"
+        by_route = None
     achieved = kernel_bytes / kernel_time / 1e9
     layer.close()
     del layer
@@ -348,7 +357,8 @@ def bench_decode(args):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kernel_name, "avg_launch_us": avg_us, "timed_launches": len(sampled),
                      "algorithmic_bytes_per_launch": kernel_bytes / len(counts),
-                     "read_ceiling_GBs": ceiling, "frac_of_read_ceiling": achieved / ceiling},
+                     "read_ceiling_GBs": ceiling, "frac_of_read_ceiling": achieved / ceiling,
+                     "by_route": by_route},
         ("output_only_launch_avg_us" if args.api == "step" else "decode_avg_us"):
             1e3 * sum(dec_ms) / max(1, len(dec_ms)),
         ("fold_launch_avg_us" if args.api == "step" else "flush_avg_us"):
