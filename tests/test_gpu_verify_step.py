@@ -39,6 +39,8 @@ def _layer(w, **kw):
     (64, 128, "bf16", 16, 8, 3, 8, 8, None),      # one head per group
     (64, 128, "bf16", 16, 4, 4, 8, 2, None),      # the register sums
     (16, 16, "bf16", 16, 6, 3, 4, 2, None),       # matrix cores, rows shorter than a cache line
+    (128, 128, "bf16", 16, 7, 2, 8, 2, None),     # matrix cores, 8 streaming wavefronts
+    (64, 64, "bf16", 12, 6, 4, 4, 2, None),       # matrix cores, 256-byte rows
     (16, 16, "bf16", 4, 3, 4, 6, 2, None),        # W close to L: folds most rounds
     (64, 64, "bf16", 8, 1, 5, 4, 2, None),
     (128, 128, "bf16", 12, 4, 2, 12, 3, None),

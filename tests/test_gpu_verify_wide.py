@@ -39,6 +39,8 @@ def _layer(w, **kw):
     (16, 16, 16, 16, 2, 4, 1, "fp8"),      # e4m3 tile widened (N < 32)
     (64, 128, 16, 6, 3, 8, 2, None),       # the smallest window on the matrix cores
     (64, 128, 8, 8, 2, 8, 2, "bf16"),
+    (128, 128, 16, 9, 2, 4, 2, "fp8"),
+    (64, 64, 16, 7, 3, 4, 2, "bf16"),
 ])
 def test_wide_verify_rounds(P, N, L, W, B, H, G, copy):
     w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype="bf16",
