@@ -112,8 +112,8 @@ typedef struct {
     void    *ring_q;    /* [B][G][L][N] io dtype */
     void    *ring_k;    /* [B][G][L][N] io dtype */
     void    *ring_v;    /* [B][H][L][P] io dtype */
-    float   *ring_dt;   /* [B][H][L] */
-    float   *ring_a;    /* [B][H][L] */
+    float   *ring_dt;   /* [B][L][H] (slot-major: one step's values of a sequence contiguous) */
+    float   *ring_a;    /* [B][L][H] */
     int32_t *pos;       /* [B] tokens appended and not rolled back */
     int32_t *base;      /* [B] pos at the last flush; count = pos - base */
     int32_t *err;       /* [B + 1] error bits: err[0] = OR over sequences, err[1 + b] per sequence */

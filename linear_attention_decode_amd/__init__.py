@@ -214,7 +214,7 @@ class ReplayLayer:
     mode), s_copy [B,H,P,N] bf16/uint8 or [B,H,P*N/2] uint8 FP4 codes (when
     read_copy is set), s_scale [B,H] f32 (e4m3) or [B,H,P*N/32] uint8 E8M0
     (FP4), ring_q/ring_k [B,G,L,N], ring_v [B,H,L,P] (io
-    dtype), ring_dt/ring_a [B,H,L] f32, pos/base [B] int32, err [B+1] int32,
+    dtype), ring_dt/ring_a [B,L,H] f32 (slot-major), pos/base [B] int32, err [B+1] int32,
     sync [B, G+1, 32] int32 (arrival counters, one per 128-byte line).
     """
 
@@ -236,7 +236,7 @@ class ReplayLayer:
             "s_scale": ((B, H, P * N // 32), torch.uint8) if fp4 else ((B, H), torch.float32),
             "ring_q": ((B, G, L, N), iot),
             "ring_k": ((B, G, L, N), iot), "ring_v": ((B, H, L, P), iot),
-            "ring_dt": ((B, H, L), torch.float32), "ring_a": ((B, H, L), torch.float32),
+            "ring_dt": ((B, L, H), torch.float32), "ring_a": ((B, L, H), torch.float32),
             "pos": ((B,), torch.int32), "base": ((B,), torch.int32), "err": ((B + 1,), torch.int32),
             "sync": ((B, G + 1, 32), torch.int32),
         }

@@ -72,8 +72,8 @@ __device__ __forceinline__ void ring_wave(const RingView &r, int lane, int b, in
     float aj, dtj;
     {
         const int sl = slot(lane < count ? lane : last);
-        aj = r.a[hring + sl];
-        dtj = r.dt[hring + sl];
+        aj = r.a[dta_index(b, bh, r.H, L, sl)];
+        dtj = r.dt[dta_index(b, bh, r.H, L, sl)];
     }
     const int tl = lane % TS, te = lane / TS;
     IoVec<IOB, 8> kraw[KI];
@@ -194,8 +194,8 @@ __device__ __forceinline__ void ring_wave_mx(const RingView &r, int lane, int j0
     m.j0 = j0;
     {
         const int sl = slot(lane < count ? lane : last);
-        m.aj = r.a[hring + sl];
-        m.dtj = r.dt[hring + sl];
+        m.aj = r.a[dta_index(b, bh, r.H, L, sl)];
+        m.dtj = r.dt[dta_index(b, bh, r.H, L, sl)];
     }
 #pragma unroll
     for (int kb = 0; kb < MX::KB; ++kb) {

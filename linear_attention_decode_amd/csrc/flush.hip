@@ -98,8 +98,8 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
         if (count > 0) {
             const size_t hring = bh * L;
             const int sl = slot(tid < count ? tid : last);
-            hd.a = r.a[hring + sl];
-            hd.dt = r.dt[hring + sl];
+            hd.a = r.a[dta_index(b, bh, r.H, L, sl)];
+            hd.dt = r.dt[dta_index(b, bh, r.H, L, sl)];
 #pragma unroll
             for (int i = 0; i < JPG; ++i) {
                 const int j = vg + i * JG;

@@ -8,6 +8,13 @@
 
 namespace replay {
 
+// Index of (sequence b, ring slot, head h) in the ring's dt and a, laid out
+// [B][L][H] (slot-major: the values one step appends for a sequence, every
+// head, are contiguous).  bh = b * H + h.
+__host__ __device__ inline size_t dta_index(size_t b, size_t bh, int H, int L, int slot) {
+    return (b * (size_t)L + (size_t)slot) * (size_t)H + (bh - b * (size_t)H);
+}
+
 // Storage kinds of a state tile.
 enum StateKind : int { ST_F32 = 0, ST_BF16 = 1, ST_FP8 = 2, ST_FP4 = 3 };
 

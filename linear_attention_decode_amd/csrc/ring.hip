@@ -73,13 +73,13 @@ __global__ __launch_bounds__(256) void append_kernel(RingView r, void *ring_q, v
             reinterpret_cast<uint4 *>(static_cast<char *>(ring_k) + out_off)[c] = sk[in_row];
         }
     }
-    // dt, a of heads h0..h1-1: [B][W][H] -> [B][H][L]
+    // dt, a of heads h0..h1-1: [B][W][H] -> [B][L][H]
     {
         const int nh = h1 - h0;
         for (int i = tid; i < W * nh; i += nt) {
             const int t = i / nh, h = h0 + i % nh;
             const int slot = (p0 + t) % L;
-            const size_t o = ((size_t)b * H + h) * L + slot;
+            const size_t o = dta_index(b, (size_t)b * H + h, H, L, slot);
             ring_dt[o] = dt[((size_t)b * W + t) * H + h];
             ring_a[o] = a[((size_t)b * W + t) * H + h];
         }

@@ -48,7 +48,7 @@ __device__ __forceinline__ int step_ring_wave(const StepArgs &A, int lane, int b
 #pragma unroll
     for (int rr = 0; rr < VR; ++rr) vnew[rr].load(A.v, bh * P + ((lane + 64 * rr) < P ? lane + 64 * rr : P - 1));
     const int sla = slot(lane < cold ? lane : lastr);
-    const float a_r = A.ring_a[hring + sla], dt_r = A.ring_dt[hring + sla];
+    const float a_r = A.ring_a[dta_index(b, bh, A.H, L, sla)], dt_r = A.ring_dt[dta_index(b, bh, A.H, L, sla)];
     IoVec<IOB, 8> kraw[KI];
 #pragma unroll
     for (int i = 0; i < KI; ++i) {

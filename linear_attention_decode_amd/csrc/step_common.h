@@ -80,8 +80,8 @@ struct StepRingMx {
         dt_in = A.dt[bh];
         qrow.load(static_cast<const char *>(A.q) + gin * N * ES, lane);
         const int sla = slot(lane < cold ? lane : lastr);
-        a_r = A.ring_a[hring + sla];
-        dt_r = A.ring_dt[hring + sla];
+        a_r = A.ring_a[dta_index(b, bh, A.H, L, sla)];
+        dt_r = A.ring_dt[dta_index(b, bh, A.H, L, sla)];
 #pragma unroll
         for (int kb = 0; kb < MX::KB; ++kb) {
             const int c = MX::col(kb, lane);
@@ -217,8 +217,8 @@ __device__ __forceinline__ void step_token_writer(const StepArgs &A, int b, int 
     }
     for (int i = tid; i < H; i += nt) {
         const size_t bh = (size_t)b * H + i;
-        A.ring_dt[bh * L + sn] = A.dt[bh];
-        A.ring_a[bh * L + sn] = A.a[bh];
+        A.ring_dt[dta_index(b, bh, H, L, sn)] = A.dt[bh];
+        A.ring_a[dta_index(b, bh, H, L, sn)] = A.a[bh];
     }
     __syncthreads();   // every wavefront of the workgroup has read the pointer
     if (tid == 0) {

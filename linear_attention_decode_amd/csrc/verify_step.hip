@@ -65,7 +65,7 @@ __device__ __forceinline__ int vs_term_wave(const StepArgs &A, int lane, int b, 
     m.j0 = 0;
     {
         const bool old = lane < keep;
-        const size_t i = old ? hring + slot(lane) : ((size_t)b * W + draft(lane)) * H + h;
+        const size_t i = old ? dta_index(b, bh, H, L, slot(lane)) : ((size_t)b * W + draft(lane)) * H + h;
         m.aj = (old ? A.ring_a : A.a)[i];
         m.dtj = (old ? A.ring_dt : A.dt)[i];
     }
@@ -158,8 +158,8 @@ __device__ __forceinline__ int vs_fold_wave(const StepArgs &A, int lane, int b, 
     IoVec<true, 1> vraw[VR][LM];
     if (fold) {
         const int sl = slot(lane < c ? lane : lastr);
-        aj = A.ring_a[hring + sl];
-        dtj = A.ring_dt[hring + sl];
+        aj = A.ring_a[dta_index(b, bh, H, L, sl)];
+        dtj = A.ring_dt[dta_index(b, bh, H, L, sl)];
 #pragma unroll
         for (int i = 0; i < KI; ++i) {
             const int j = i * RPW + te;
@@ -196,8 +196,8 @@ __device__ __forceinline__ int vs_fold_wave(const StepArgs &A, int lane, int b, 
         }
     }
     if (lane < W) {
-        A.ring_dt[hring + ring_slot(pmod, lane, L)] = dt_d;
-        A.ring_a[hring + ring_slot(pmod, lane, L)] = a_d;
+        A.ring_dt[dta_index(b, bh, H, L, ring_slot(pmod, lane, L))] = dt_d;
+        A.ring_a[dta_index(b, bh, H, L, ring_slot(pmod, lane, L))] = a_d;
     }
 
     if (fold) {

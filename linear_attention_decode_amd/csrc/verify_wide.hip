@@ -44,8 +44,8 @@ __device__ __forceinline__ void wide_ring_wave(const RingView &r, int lane, int 
     m.j0 = j0;
     {
         const int sl = slot(lane < count ? lane : last);
-        m.aj = r.a[hring + sl];
-        m.dtj = r.dt[hring + sl];
+        m.aj = r.a[dta_index(b, bh, r.H, L, sl)];
+        m.dtj = r.dt[dta_index(b, bh, r.H, L, sl)];
     }
 #pragma unroll
     for (int kb = 0; kb < MX::KB; ++kb) {

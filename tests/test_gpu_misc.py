@@ -178,8 +178,9 @@ def test_nan_poisoned_unused_slots_change_nothing():
                     live = set(model.live_slots(b))
                     for s in range(w.ring_len):
                         if s not in live:
-                            for name in ("ring_v", "ring_dt", "ring_a"):
-                                layer.t[name][b, :, s] = float("nan")
+                            layer.t["ring_v"][b, :, s] = float("nan")
+                            for name in ("ring_dt", "ring_a"):   # [B][L][H]
+                                layer.t[name][b, s] = float("nan")
                     # the group rows too, when no live entry uses the slot
                     for s in range(w.ring_len):
                         if s not in live:

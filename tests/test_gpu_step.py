@@ -211,8 +211,10 @@ def test_step_ignores_nan_in_unused_slots():
                     live = set(model.live_slots(b))
                     for s in range(w.ring_len):
                         if s not in live:
-                            for name in ("ring_v", "ring_dt", "ring_a", "ring_q", "ring_k"):
+                            for name in ("ring_v", "ring_q", "ring_k"):
                                 layer.t[name][b, :, s] = float("nan")
+                            for name in ("ring_dt", "ring_a"):   # [B][L][H]
+                                layer.t[name][b, s] = float("nan")
         torch.cuda.synchronize()
         assert layer.get_error()[0] == 0
         out = y.cpu().numpy(), layer.s_master.cpu().numpy()
