@@ -690,8 +690,8 @@ def main():
     args = ap.parse_args()
     args.steps_given = any(a.startswith("--steps") for a in sys.argv[1:])
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the decode path needs no collective and this build runs "
-              "on a single MI355X; --gpus must be 1", file=sys.stderr)
+        print("bench.py measures one GPU (the decode path needs no collective); --gpus must be 1",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

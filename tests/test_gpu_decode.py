@@ -1,7 +1,7 @@
 """Standard decode on the GPU (append -> output-only decode -> flush every
 L steps) against the float64 oracle, through the C ABI.
 
-Tolerance: the benchmark spec's 1e-4 maximum relative error for a float32
+Tolerance: the stated 1e-4 maximum relative error for a float32
 checkpoint, read per token as max|y - y_ref| / max|y_ref| over the layer's
 whole output (heads x P) for one sequence.  The per-head-vector figure is
 printed beside it.  Ring integers (pos, base) must match the integer model

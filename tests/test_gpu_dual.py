@@ -5,7 +5,7 @@
   scales), ties and zero heads included;
 * outputs read from the copies, separated (float32 master takes the
   updates) and shared (the copy is the only checkpoint), against
-  - the float64 oracle with the benchmark spec's tolerances (2e-2 bf16, 6e-2 e4m3,
+  - the float64 oracle with the stated tolerances (2e-2 bf16, 6e-2 e4m3,
     read per token over the layer output), and
   - the oracle's emulation of the same copy (tight; it differs from the
     GPU only by float32-vs-float64 rounding of the state that is copied).

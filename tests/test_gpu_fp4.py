@@ -9,7 +9,7 @@ takes every flush, outputs read the FP4 copy).
   different sides of a code boundary), and against the exact oracle within
   the format's own error as the emulation realises it (plus that slack).
 
-the benchmark spec states no FP4 tolerance; the bound used is the emulation's own
+No FP4 tolerance is stated; the bound used is the emulation's own
 error: FP4 keeps 2 significant bits, so the copy's error is a property of
 the format, and the kernels must add nothing beyond float32 rounding.
 """
