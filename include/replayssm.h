@@ -42,6 +42,11 @@
  *  - A handle is not thread-safe; distinct handles are independent.  Calls on
  *    one handle must be issued in order on one stream (or ordered by the
  *    caller across streams).
+ *  - Graphs: every call that enqueues work, except replay_get_error and
+ *    replay_destroy, may be recorded into a HIP graph by stream capture and
+ *    replayed: it allocates nothing, records no memset and does not
+ *    synchronise.  Replays read the pointer arguments given at capture, so
+ *    new inputs go into those same buffers before each replay.
  *  - Specialisations: (P, N) in {(16,16), (64,64), (64,128), (128,128)},
  *    1 <= L <= 32, 1 <= G <= H with H % G == 0, verify windows 1 <= W <= 8
  *    (up to 16 with bf16 io and a float32, bf16 or e4m3 read; see replay_verify).
@@ -196,7 +201,10 @@ replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *s
    The handle keeps host-side bounds on every sequence's count from the calls
    that move the pointers; a flush that no sequence can be due for enqueues
    nothing (in the standard schedule, every flush but the one that folds).
-   So pos and base must change only through this library's calls. */
+   So pos and base must change only through this library's calls.  Once a
+   call that moves the pointers has been recorded into a HIP graph, replays
+   move them without the handle seeing it, and from then on every flush is
+   enqueued. */
 replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream);
 
 /* One standard decode step for every sequence: append one token, produce its

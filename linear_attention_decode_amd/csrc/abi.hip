@@ -16,6 +16,7 @@ struct replay_handle {
     replay_config cfg;
     replay_buffers bufs;
     CountBound bound;   // upper bounds on every sequence's count and pos
+    bool graphed = false;   // a call that moves the pointers was recorded into a graph
 };
 
 namespace {
@@ -105,6 +106,16 @@ RingView ring_view(const replay_handle *h) {
 
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
+// A call recorded into a graph (stream capture) moves the pointers again on
+// every replay without passing through the handle, so from then on the
+// host-side count bounds no longer describe the device: the handle stops
+// skipping flushes for good.  A failed query counts as a capture.
+void note_capture(replay_handle *h, hipStream_t s) {
+    if (h->graphed) return;
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone) h->graphed = true;
+}
+
 // Fold (or load) into the checkpoint and rewrite the copy, then move base.
 replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_count, hipStream_t s) {
     const replay_config &c = h->cfg;
@@ -133,7 +144,8 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
     }
     const int st_copy = c.read_copy == REPLAY_NONE ? -1 : state_kind(c.read_copy);
     // no sequence can be due: the kernel would change nothing
-    if (!load_src && !h->bound.flush_may_fold(min_count)) return REPLAY_OK;
+    note_capture(h, s);
+    if (!load_src && !h->graphed && !h->bound.flush_may_fold(min_count)) return REPLAY_OK;
     const hipError_t e = launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s);
     if (e != hipSuccess) {
         h->bound.unknown();
@@ -253,6 +265,7 @@ replay_status replay_append(replay_handle *h, int32_t W, const void *q, const vo
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a))
         return REPLAY_ERR_INVALID_ARG;
     if (W < 1 || W > h->cfg.ring_len) return REPLAY_ERR_INVALID_ARG;
+    note_capture(h, as_stream(stream));
     const RingView r = ring_view(h);
     const hipError_t e = launch_append(h->cfg.head_dim, h->cfg.state_dim, r, h->bufs.ring_q, h->bufs.ring_k,
                                        h->bufs.ring_v, h->bufs.ring_dt, h->bufs.ring_a, h->bufs.pos, h->bufs.sync,
@@ -277,6 +290,7 @@ replay_status replay_verify(replay_handle *h, int32_t W, float *y, void *stream)
 
 replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *stream) {
     if (!h || !n_reject || !aligned4(n_reject)) return REPLAY_ERR_INVALID_ARG;
+    note_capture(h, as_stream(stream));
     h->bound.rollback();
     return from_hip(launch_rollback(ring_view(h), h->bufs.pos, n_reject, as_stream(stream)));
 }
@@ -326,6 +340,7 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
         return REPLAY_ERR_INVALID_ARG;
     const replay_config &c = h->cfg;
     hipStream_t s = as_stream(stream);
+    note_capture(h, s);
     const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, 1);
     if (c.read_copy != REPLAY_NONE) {
         // copies: append + decode from an e4m3 or FP4 copy in one launch
@@ -362,6 +377,7 @@ replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, con
     const replay_config &c = h->cfg;
     if (W < 1 || W > kMaxWideWindow || W > c.ring_len) return REPLAY_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
+    note_capture(h, s);
     const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, W);
     if (c.read_copy != REPLAY_NONE || !verify_step_fused(c.head_dim, c.state_dim, sa)) {
         // the flush, append and verify kernels in turn

@@ -1,0 +1,135 @@
+"""Decode steps and verify rounds recorded into a HIP graph and replayed.
+
+One graph holds a step (or a verify round plus its rollback) of one or
+several stacked layers.  Before each replay the next inputs are copied into
+the buffers the graph was captured with; an eager twin of every layer makes
+the same calls with the same inputs.  After every replay, with the eager
+work and a synchronisation in between, the outputs, pos, base and the error
+bits must equal the twin's bit for bit, and at the end an eager flush of
+both must leave identical checkpoints.  The copy-mode steps end in a flush
+kernel that the handle may skip on its host-side count bounds, so a capture
+taken while no sequence was due must still record it."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+L = 8
+
+
+def _workload(layer):
+    return synth.Workload(batch=4, heads=8, groups=2, head_dim=64, state_dim=128, ring_len=L, io_dtype="bf16",
+                          config=synth.CONFIG_ID["misc"], layer=500 + layer)
+
+
+def _pair(w, rc):
+    import linear_attention_decode_amd as lad
+    kw = {} if rc is None else {"read_copy": rc}
+    mk = lambda: lad.ReplayLayer(w.batch, w.heads, w.groups, w.head_dim, w.state_dim, L, io_dtype="bf16",
+                                 device=gu.DEV, **kw)
+    return mk(), mk()
+
+
+def _same_state(e, g, what):
+    assert torch.equal(e.pos, g.pos) and torch.equal(e.base, g.base), what
+    we, pe = e.get_error()
+    wg, pg = g.get_error()
+    assert (we, pe) == (wg, pg), (what, pe, pg)
+
+
+@pytest.mark.parametrize("rc,layers", [(None, 1), ("fp8", 1), ("bf16", 1), (None, 3)])
+def test_graph_steps(rc, layers):
+    gu.note(f"graph of steps copy={rc} layers={layers}")
+    T0, T = 2, 3 * L + 3
+    ws = [_workload(i) for i in range(layers)]
+    devs = [gu.DevInputs(w, 0, T) for w in ws]
+    pairs = [_pair(w, rc) for w in ws]
+    B, H, P = ws[0].batch, ws[0].heads, ws[0].head_dim
+    ys = [(torch.empty((B, H, P), dtype=torch.float32, device=gu.DEV),
+           torch.empty((B, H, P), dtype=torch.float32, device=gu.DEV)) for _ in ws]
+    for t in range(T0):   # eager on both (count T0 at capture: no sequence due)
+        for (e, g), d, (ye, yg) in zip(pairs, devs, ys):
+            e.step(*d.step(t), ye, flush_at=L)
+            g.step(*d.step(t), yg, flush_at=L)
+    static = [tuple(x.clone() for x in d.step(T0)) for d in devs]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for (_, g), st, (_, yg) in zip(pairs, static, ys):
+            g.step(*st, yg, flush_at=L)
+    for t in range(T0, T):
+        for st, d in zip(static, devs):
+            for dst, src in zip(st, d.step(t)):
+                dst.copy_(src)
+        graph.replay()
+        for (e, _), d, (ye, _) in zip(pairs, devs, ys):
+            e.step(*d.step(t), ye, flush_at=L)
+        torch.cuda.synchronize()
+        for i, ((e, g), (ye, yg)) in enumerate(zip(pairs, ys)):
+            assert torch.equal(ye, yg), (t, i)
+            _same_state(e, g, (t, i))
+    assert int(pairs[0][0].base[0]) >= 2 * L          # the window folded on replays
+    for e, g in pairs:
+        e.flush(1)
+        g.flush(1)    # eager, after replays the handle did not see
+        torch.cuda.synchronize()
+        _same_state(e, g, "final flush")
+        assert int(g.base[0]) == T
+        for name in ("s_master", "s_copy", "s_scale"):
+            if e.t[name] is not None:
+                assert torch.equal(e.t[name], g.t[name]), name
+    del graph
+    for e, g in pairs:
+        e.close()
+        g.close()
+
+
+def test_graph_verify_rounds():
+    """Fused verify round + rollback in one graph; accepted counts change per replay."""
+    W, R = 4, 12
+    gu.note(f"graph of verify rounds W={W}")
+    w = _workload(7)
+    B, H, P = w.batch, w.heads, w.head_dim
+    dev = gu.DevInputs(w, 0, (R + 1) * W)
+    e, g = _pair(w, None)
+    accept = np.random.default_rng(3).integers(0, W + 1, size=(R + 1, B))
+    nrej = [torch.from_numpy((W - a).astype(np.int32)).to(gu.DEV) for a in accept]
+    ye = torch.empty((B, W, H, P), dtype=torch.float32, device=gu.DEV)
+    yg = torch.empty_like(ye)
+    fa = L - W + 1
+    for x in (e, g):   # one eager round on both
+        x.verify_step(W, *dev.window(0, W), ye if x is e else yg, flush_at=fa)
+        x.rollback(nrej[0])
+    static = tuple(x.clone() for x in dev.window(W, W))
+    s_rej = nrej[1].clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.verify_step(W, *static, yg, flush_at=fa)
+        g.rollback(s_rej)
+    folds = 0
+    for r in range(1, R + 1):
+        for dst, src in zip(static, dev.window(r * W, W)):
+            dst.copy_(src)
+        s_rej.copy_(nrej[r])
+        base0 = g.base.clone()
+        graph.replay()
+        e.verify_step(W, *dev.window(r * W, W), ye, flush_at=fa)
+        e.rollback(nrej[r])
+        torch.cuda.synchronize()
+        assert torch.equal(ye, yg), r
+        _same_state(e, g, r)
+        folds += int((g.base != base0).sum())
+    assert folds > 0
+    e.flush(1)
+    g.flush(1)
+    torch.cuda.synchronize()
+    _same_state(e, g, "final flush")
+    assert torch.equal(e.s_master, g.s_master)
+    del graph
+    e.close()
+    g.close()
