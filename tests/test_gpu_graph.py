@@ -88,14 +88,18 @@ def test_graph_steps(rc, layers):
         g.close()
 
 
-def test_graph_verify_rounds():
-    """Fused verify round + rollback in one graph; accepted counts change per replay."""
-    W, R = 4, 12
-    gu.note(f"graph of verify rounds W={W}")
+@pytest.mark.parametrize("rc,W", [(None, 4), (None, 6), ("fp8", 4)])
+def test_graph_verify_rounds(rc, W):
+    """A verify round + rollback in one graph; accepted counts change per
+    replay.  W = 4 and 6: the single-launch round (register sums, matrix
+    cores); an e4m3 copy: flush, append and verify in turn, where the flush
+    is one the bounds would skip at capture."""
+    R = 12
+    gu.note(f"graph of verify rounds copy={rc} W={W}")
     w = _workload(7)
     B, H, P = w.batch, w.heads, w.head_dim
     dev = gu.DevInputs(w, 0, (R + 1) * W)
-    e, g = _pair(w, None)
+    e, g = _pair(w, rc)
     accept = np.random.default_rng(3).integers(0, W + 1, size=(R + 1, B))
     nrej = [torch.from_numpy((W - a).astype(np.int32)).to(gu.DEV) for a in accept]
     ye = torch.empty((B, W, H, P), dtype=torch.float32, device=gu.DEV)
@@ -129,7 +133,9 @@ def test_graph_verify_rounds():
     g.flush(1)
     torch.cuda.synchronize()
     _same_state(e, g, "final flush")
-    assert torch.equal(e.s_master, g.s_master)
+    for name in ("s_master", "s_copy", "s_scale"):
+        if e.t[name] is not None:
+            assert torch.equal(e.t[name], g.t[name]), name
     del graph
     e.close()
     g.close()
