@@ -21,8 +21,8 @@ pytestmark = pytest.mark.gpu
 L = 8
 
 
-def _workload(layer):
-    return synth.Workload(batch=4, heads=8, groups=2, head_dim=64, state_dim=128, ring_len=L, io_dtype="bf16",
+def _workload(layer, P=64, N=128):
+    return synth.Workload(batch=4, heads=8, groups=2, head_dim=P, state_dim=N, ring_len=L, io_dtype="bf16",
                           config=synth.CONFIG_ID["misc"], layer=500 + layer)
 
 
@@ -41,11 +41,13 @@ def _same_state(e, g, what):
     assert (we, pe) == (wg, pg), (what, pe, pg)
 
 
-@pytest.mark.parametrize("rc,layers", [(None, 1), ("fp8", 1), ("bf16", 1), (None, 3)])
-def test_graph_steps(rc, layers):
-    gu.note(f"graph of steps copy={rc} layers={layers}")
+@pytest.mark.parametrize("rc,layers,P,N", [(None, 1, 64, 128), ("fp8", 1, 64, 128), ("bf16", 1, 64, 128),
+                                           (None, 3, 64, 128), (None, 2, 128, 128), ("fp8", 1, 128, 128)])
+def test_graph_steps(rc, layers, P, N):
+    """128 x 128 heads: two workgroups per head in the single-launch step."""
+    gu.note(f"graph of steps copy={rc} layers={layers} P={P} N={N}")
     T0, T = 2, 3 * L + 3
-    ws = [_workload(i) for i in range(layers)]
+    ws = [_workload(i, P, N) for i in range(layers)]
     devs = [gu.DevInputs(w, 0, T) for w in ws]
     pairs = [_pair(w, rc) for w in ws]
     B, H, P = ws[0].batch, ws[0].heads, ws[0].head_dim
