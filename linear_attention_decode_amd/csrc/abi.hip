@@ -1,6 +1,9 @@
 // abi.hip -- the extern "C" boundary of libreplayssm: host-side validation,
 // launch configuration and the handle.  Every compute step runs in the
-// kernels of decode.hip, flush.hip, ring.hip, eager.hip and probe.hip.
+// kernels of decode*.hip (output-only decode and register verify),
+// verify_wide.hip (matrix-core verify), step.hip and step_copy.hip (the
+// fused decode step), verify_step.hip (the fused speculative round),
+// flush.hip, ring.hip (append, rollback, fills), eager.hip and probe.hip.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

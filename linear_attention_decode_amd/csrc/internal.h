@@ -37,8 +37,8 @@ struct RingView {
     const void *q;      // [B][G][L][N]
     const void *k;      // [B][G][L][N]
     const void *v;      // [B][H][L][P]
-    const float *dt;    // [B][H][L]
-    const float *a;     // [B][H][L]
+    const float *dt;    // [B][L][H] (slot-major, dta_index)
+    const float *a;     // [B][L][H]
     const int32_t *pos;
     const int32_t *base;
     int32_t *err;       // [B+1]
@@ -71,7 +71,7 @@ struct FlushArgs {
 // (W drafts), float32 checkpoint.
 struct StepArgs {
     void *ring_q, *ring_k, *ring_v;   // [B][G][L][N] x2, [B][H][L][P]
-    float *ring_dt, *ring_a;          // [B][H][L]
+    float *ring_dt, *ring_a;          // [B][L][H] (slot-major, dta_index)
     int32_t *pos, *base, *err, *sync;  // sync: [B][G + 1][kSyncStride], element [..][0]
     float *S;                         // [B][H][P][N] master, read and (when folding) written
     const void *q, *k, *v;            // [B][W][G][N] x2, [B][W][H][P]

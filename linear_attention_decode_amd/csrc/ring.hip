@@ -14,8 +14,9 @@ namespace replay {
 
 // kAppendSlices workgroups per sequence, each copying the tokens of its
 // share of the heads (v, dt, a) and of the groups (q, k); the last slice to
-// arrive at the sequence's counter advances the pointer (every slice arrives
-// after reading it, so none reads a moved pointer).
+// arrive at the sequence's counter advances the pointer.  A slice arrives
+// only after a workgroup barrier, so every wavefront of every slice has read
+// the pointer before any slice can move it.
 constexpr int kAppendSlices = 8;
 
 __global__ __launch_bounds__(256) void append_kernel(RingView r, void *ring_q, void *ring_k,
@@ -84,6 +85,9 @@ __global__ __launch_bounds__(256) void append_kernel(RingView r, void *ring_q, v
             ring_a[o] = a[((size_t)b * W + t) * H + h];
         }
     }
+    // every wavefront of this slice has read pos[b] (and its overflow checks
+    // agreed: they all read the same value) before the slice arrives
+    __syncthreads();
     if (tid == 0) {
         int32_t *cnt = sync + ((size_t)b * (G + 1) + G) * kSyncStride;
         if (atomicAdd(cnt, 1) == kAppendSlices - 1) {

@@ -48,6 +48,21 @@ class DevInputs:
         return tuple(self.t[n][i:i + W].transpose(0, 1).contiguous() for n in ("q", "k", "v", "dt", "a"))
 
 
+class DevInputsTorch(DevInputs):
+    """As DevInputs, generated on the device (synth.step_inputs_torch) for
+    full-batch runs; the oracle is fed the very bytes the device holds."""
+
+    def __init__(self, w: synth.Workload, t0: int, t1: int):
+        self.w = w
+        self.t0 = t0
+        self.t = synth.step_inputs_torch(w, t0, t1, device=DEV)
+
+    def oracle(self, seqs=None) -> dict:
+        """float64 oracle inputs [T][b][...] of sequences `seqs` (all if None)."""
+        pick = (lambda v: v) if seqs is None else (lambda v: v[:, seqs])
+        return runs.widen_inputs({k: synth.to_storage(pick(v)) for k, v in self.t.items()}, self.w.io_dtype)
+
+
 def oracle_inputs(w: synth.Workload, t0: int, t1: int, seqs) -> dict:
     return runs.widen_inputs(synth.step_inputs(w, t0, t1, seqs=seqs), w.io_dtype)
 
@@ -78,10 +93,27 @@ def run_standard(layer, w: synth.Workload, dev: DevInputs, t0: int, t1: int, mod
 
 
 def errors(y_gpu: np.ndarray, y_ref: np.ndarray):
-    """(max per-token error over the layer output, max per-head-vector error)."""
+    """(max per-token error over the layer output, max per-head-vector error,
+    mean per-head-vector error)."""
     e_tok = runs.normwise_rel_err(y_gpu, y_ref)
     e_vec = runs.normwise_rel_err(y_gpu, y_ref, axes=(-1,))
     return float(np.max(e_tok)), float(np.max(e_vec)), float(np.mean(e_vec))
+
+
+TOL_F32 = 1e-4
+
+
+def assert_f32(y_gpu: np.ndarray, y_ref: np.ndarray, tol: float = TOL_F32, what: str = ""):
+    """Parity of outputs read from a float32 checkpoint against the float64
+    oracle: the maximum relative error rel(b, t, h) = max_p |y - y_ref| /
+    max_p |y_ref| over every (sequence, token, head) -- one head's output
+    vector -- must not exceed `tol` (1e-4), and so must the per-token figure
+    over the layer's whole output.  y arrays end in [..][H][P]."""
+    tok, vec, mean = errors(y_gpu, y_ref)
+    print(f"  {what} per-head max {vec:.3e} mean {mean:.3e}; per-token max {tok:.3e}", flush=True)
+    assert vec <= tol, f"{what} per-head error {vec:.3e} > {tol:.0e}"
+    assert tok <= tol, f"{what} per-token error {tok:.3e} > {tol:.0e}"
+    return tok, vec, mean
 
 
 def run_verify(layer, w: synth.Workload, dev: DevInputs, R: int, W: int, accept: np.ndarray, model=None,

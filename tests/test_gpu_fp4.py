@@ -23,7 +23,7 @@ from oracle import runs
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
-TOL_VS_EMUL = 2e-2
+TOL_VS_EMUL = 1e-3
 
 
 def _layer(w, **kw):

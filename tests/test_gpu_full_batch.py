@@ -1,0 +1,82 @@
+"""Every sequence of the full batch against the float64 oracle.
+
+The other workload-size tests sample a few sequences; per-sequence index
+arithmetic (the XCD-aware workgroup order, the writer workgroups that
+follow the compute grid, the per-sequence arrival counters, pointer reads)
+is covered here on all of them:
+
+* standard decode (B=256, H=128, G=8, P=64, N=128, L=16, bf16 q/k/v,
+  float32 checkpoint), 64 steps (4 folds) through the fused replay_step, the
+  launch sequence the benchmark times: every output of every sequence and
+  head within 1e-4 per head (max_p |y - y_ref| / max_p |y_ref|), and every
+  checkpoint after the last fold within 1e-4 of the oracle state;
+* speculative verify (B=256, H=64, W=5, accepted drafts ~ U{0..5}), 32 fused
+  rounds through replay_verify_step: every draft's output of every sequence
+  within 1e-4 per head, the ring integers of every sequence after every
+  round equal to the integer model's.
+
+Page "ReplaySSM: Cachear Inputs, No Estado", "Los dos caminos": the
+output of a head is y_t = S_t q_t, and the rewriting changes no result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ring as oring
+from oracle import runs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(w, **kw):
+    import linear_attention_decode_amd as lad
+    return lad.ReplayLayer(w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len,
+                           io_dtype=w.io_dtype, device=gu.DEV, **kw)
+
+
+def test_step_every_sequence_decode_workload():
+    w = synth.named("decode")
+    T, L = 64, w.ring_len
+    gu.note(f"full batch: fused step {w} T={T}")
+    dev = gu.DevInputsTorch(w, 0, T)
+    layer = _layer(w)
+    model = oring.RingModel(w.batch, L)
+    y = torch.empty((T, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
+    for t in range(T):
+        layer.step(*dev.step(t), y[t], flush_at=L)
+        model.append(1)
+        model.flush(L)
+        gu.check_ring(layer, model, f"step {t}")
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = dev.oracle()
+    S = np.zeros((w.batch, w.heads, w.head_dim, w.state_dim))
+    y_ref = runs.standard(x, S)
+    gu.assert_f32(y.cpu().numpy(), y_ref, what="all 256 sequences:")
+    del y_ref
+    # T is a multiple of L: the last step folded, so the checkpoint is the state after token T
+    S_gpu = layer.s_master.cpu().numpy()
+    e = runs.normwise_rel_err(S_gpu, S, axes=(-2, -1))
+    print(f"  checkpoint per-head max {float(e.max()):.3e}", flush=True)
+    assert float(e.max()) <= gu.TOL_F32
+    layer.close()
+
+
+def test_verify_step_every_sequence_verify_workload():
+    w = synth.named("verify")
+    R, W = 32, 5
+    gu.note(f"full batch: fused verify rounds {w} R={R} W={W}")
+    accept = synth.accept_counts(w, R, W)
+    dev = gu.DevInputsTorch(w, 0, R * W)
+    layer = _layer(w)
+    model = oring.RingModel(w.batch, w.ring_len)
+    y = gu.run_verify(layer, w, dev, R, W, accept, model=model, fused=True)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = dev.oracle()
+    S = np.zeros((w.batch, w.heads, w.head_dim, w.state_dim))
+    y_ref = runs.verify_rounds(x, accept, W, S)                       # [R][W][B][H][P]
+    gu.assert_f32(y.cpu().numpy().transpose(0, 2, 1, 3, 4), y_ref, what="all 256 sequences:")
+    layer.close()

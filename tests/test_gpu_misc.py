@@ -49,9 +49,7 @@ def test_decode_workload_full_length():
     x = runs.widen_inputs({k: synth.to_storage(v[:, seqs]) for k, v in dev.items()}, w.io_dtype)
     S = np.zeros((len(seqs), w.heads, w.head_dim, w.state_dim))
     y_ref = runs.standard(x, S)
-    tok, vec, mean = gu.errors(y.cpu().numpy()[:, seqs], y_ref)
-    print(f"  per-token max {tok:.3e} per-head max {vec:.3e} mean {mean:.3e}")
-    assert tok <= 1e-4
+    gu.assert_f32(y.cpu().numpy()[:, seqs], y_ref)
     S_gpu = layer.s_master.cpu().numpy()[seqs].astype(np.float64)
     assert float(np.max(runs.normwise_rel_err(S_gpu, S, axes=(-3, -2, -1)))) <= 1e-4
     layer.close()
@@ -83,8 +81,7 @@ def test_eager_step_and_select(P, N, io):
     x = gu.oracle_inputs(w, 0, T, list(range(w.batch)))
     S_ref = np.zeros((w.batch, w.heads, P, N))
     y_ref = runs.standard(x, S_ref.copy())
-    tok, vec, _ = gu.errors(y.cpu().numpy(), y_ref)
-    assert tok <= 1e-4, tok
+    gu.assert_f32(y.cpu().numpy(), y_ref)
     for b in range(w.batch):
         Sb = np.zeros((1, w.heads, P, N))
         runs.standard({k: v[:3 + accept[b], [b]] for k, v in x.items()}, Sb)

@@ -5,7 +5,7 @@ checkpoint with the state-and-output route.  Checked against
 * the separate calls (append, decode, flush) on the same inputs: outputs of
   non-folding steps and every checkpoint bit for bit, outputs of folding
   steps (a different but exact route) to 1e-5;
-* the float64 oracle (1e-4 per token) and the integer ring model (exact);
+* the float64 oracle (1e-4 per head) and the integer ring model (exact);
 * error paths: a step that would overflow the ring leaves the sequence
   unchanged and outputs NaN;
 * with an e4m3 or FP4 read copy (bf16 io): append + decode from the copy in
@@ -71,9 +71,7 @@ def test_step_matches_separate_calls_on_decode_workload():
     seqs = [0, 131, 255]
     x = gu.oracle_inputs(w, 0, T, seqs)
     y_ref = runs.standard(x, np.zeros((3, w.heads, w.head_dim, w.state_dim)))
-    tok, vec, _ = gu.errors(ya.cpu().numpy()[:, seqs], y_ref)
-    print(f"  per-token max {tok:.3e} per-head max {vec:.3e}")
-    assert tok <= 1e-4
+    gu.assert_f32(ya.cpu().numpy()[:, seqs], y_ref)
     a.close()
     b.close()
 
@@ -107,10 +105,13 @@ def test_step_ragged(P, N, io, L, flush_at, B, H, G, copy):
         # with copies the step runs the separate kernels; with this few heads the
         # per-token error against exact is the format's own, so compare with the
         # oracle's emulation of the same copy
-        y_ref, tol = runs.separated(x, S0, flush_at, copy), {"bf16": 1e-3, "fp8": 1e-2}[copy]
-    tok, vec, _ = gu.errors(y.cpu().numpy(), y_ref)
-    print(f"  per-token max {tok:.3e} per-head max {vec:.3e}")
-    assert tok <= tol
+        y_ref, tol = runs.separated(x, S0, flush_at, copy), {"bf16": 1e-3, "fp8": 1e-3}[copy]
+    if copy is None:
+        gu.assert_f32(y.cpu().numpy(), y_ref)
+    else:
+        tok, vec, _ = gu.errors(y.cpu().numpy(), y_ref)
+        print(f"  per-token max {tok:.3e} per-head max {vec:.3e}")
+        assert tok <= tol
     layer.close()
 
 
@@ -142,8 +143,7 @@ def test_step_overflow_leaves_sequence_unchanged():
     assert layer.get_error()[0] == 0
     x = gu.oracle_inputs(w, 0, 5, [0, 1, 2])
     y_ref = runs.standard(x, np.zeros((3, 4, 64, 128)))
-    tok, _, _ = gu.errors(torch.cat([y[:4], y[5:6]]).cpu().numpy(), y_ref)
-    assert tok <= 1e-4
+    gu.assert_f32(torch.cat([y[:4], y[5:6]]).cpu().numpy(), y_ref)
     layer.close()
 
 
@@ -176,9 +176,7 @@ def test_flush_schedule_invariance():
     x = gu.oracle_inputs(w, 0, T, list(range(w.batch)))
     y_ref = runs.standard(x, np.zeros((w.batch, w.heads, w.head_dim, w.state_dim)))
     for k, yk in outs.items():
-        tok, _, _ = gu.errors(yk, y_ref)
-        print(f"  schedule {k}: per-token max vs oracle {tok:.3e}")
-        assert tok <= 1e-4
+        gu.assert_f32(yk, y_ref, what=f"schedule {k}:")
         e = runs.normwise_rel_err(yk, outs[8].astype(np.float64))
         assert float(np.max(e)) <= 1e-5, k
 
