@@ -8,9 +8,10 @@ full (every 16th step).  The timed region is K steps (default 256 = 16
 windows) with all inputs resident in HBM; the eager per-token baseline is
 timed the same way on the same inputs.
 
-Prints ONE JSON line.  `roofline` is the decode kernel (the dominant one):
-algorithmic bytes per launch / its average duration from HIP events on the
-launch stream.  `cpu_baseline` is the float64 oracle on a bounded sample of
+Prints ONE JSON line.  `roofline` is the fused step kernel (the dominant
+one): algorithmic bytes per launch / its average duration, from HIP events
+on the launch stream around whole windows of launches run after the timed
+region (so the figure does not depend on --steps).  `cpu_baseline` is the float64 oracle on a bounded sample of
 the same workload, timed on the host cores.
 
 Other workloads (--workload verify | dual | stacked) print their own line.
@@ -83,6 +84,16 @@ def verify_step_bytes(w, before, W, io=2):
     folds = int(np.sum(before >= L - W + 1))
     return (state_bytes(w) * (1 + folds / B)
             + float(np.sum(before)) * per_entry + B * (2 * W * token + W * H * P * 4))
+
+
+def flop_model(P, N):
+    """Multiply-adds one ring entry costs to reach the outputs (page
+    "ReplaySSM: Cachear Inputs, No Estado", "Los dos caminos"): the state
+    route builds the outer product v k^T into the state (P*N), the
+    output-only route takes k . q (N) and adds the scaled v (P).  Their ratio
+    P*N / (P + N) is 64 at P = N = 128, the pages' figure."""
+    return {"state_route_macs_per_entry": P * N, "output_only_macs_per_entry": P + N,
+            "ratio": P * N / (P + N), "ratio_at_128x128": 128 * 128 / 256}
 
 
 def eager_bytes(w, io=2):
@@ -278,49 +289,77 @@ def bench_decode(args):
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
-    # HIP events bracket every stride-th launch of the timed region (an event
-    # between two launches holds the second back, so bracketing every launch
-    # would slow the loop being measured).  The default stride L + 1 visits
-    # the ring counts 1..L in turn, the fold included, each equally often
-    # over (L + 1) * L steps.
-    stride = args.event_stride or (L + 1)
-    sampled = [k for k in range(args.steps) if k % stride == 0]
-    evs = {k: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for k in sampled}
+    # The timed region: K steps with nothing recorded between launches, and
+    # one pair of HIP events on the launch stream around the whole region.
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    r0.record(stream)
     for k in range(args.steps):
-        step(args.warmup + k, evs.get(k))
+        step(args.warmup + k)
+    r1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    elapsed = t1 - t0
+    region_s = r0.elapsed_time(r1) / 1e3
+    timed_counts = [((args.warmup + k) % L) + 1 for k in range(args.steps)]
+    folds_timed = sum(1 for c in timed_counts if c >= L)
+
+    # The roofline pass, after the timed region and independent of K: the
+    # steps continue to the next window start, then `reps` whole windows
+    # (ring counts 1..L each, the fold included, as in the schedule) run back
+    # to back between one pair of events -> the kernel's average launch time
+    # over the schedule.  Then one more window with every launch between its
+    # own events gives the two routes apart (an event between two launches
+    # holds the second back by a few microseconds, so these read a little slow).
+    t = args.warmup + args.steps
+    while t % L != 0:
+        step(t)
+        t += 1
+    reps = max(1, args.roofline_windows)
+    if args.api == "step":
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        for i in range(reps * L):
+            step(t + i)
+        p1.record(stream)
+        t += reps * L
+    route_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(L)]
+    for i in range(L):
+        step(t + i, route_evs[i])
+    torch.cuda.synchronize()
     word, _ = layer.get_error()
     assert word == 0, f"device error bits {word}"
-    elapsed = t1 - t0
-    counts = [((args.warmup + k) % L) + 1 for k in sampled]
+    counts = list(range(1, L + 1))
     if args.api == "step":
         # the dominant kernel is the fused step kernel itself
-        step_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in sampled]
+        pass_s = p0.elapsed_time(p1) / 1e3
+        kernel_bytes = reps * sum(step_bytes(w, c, c >= L) for c in counts)
+        kernel_time = pass_s
+        n_launch = reps * L
+        avg_us = 1e6 * pass_s / n_launch
+        step_ms = [e[0].elapsed_time(e[1]) for e in route_evs]
         folds = [c >= L for c in counts]
         dec_ms = [m for m, f in zip(step_ms, folds) if not f]
         fl_ms = [m for m, f in zip(step_ms, folds) if f]
-        kernel_bytes = sum(step_bytes(w, c, c >= L) for c in counts)
-        kernel_time = sum(step_ms) / 1e3
-        avg_us = 1e3 * sum(step_ms) / len(step_ms)
         kernel_name = "step (append + output-only decode, or append + fold on full rings)"
-        # the two routes apart: output-only launches (read-bound) and folding ones (read + write)
         by_route = {}
         for route, sel in (("output_only", False), ("fold", True)):
             b_r = sum(step_bytes(w, c, f) for c, f in zip(counts, folds) if f == sel)
             t_r = sum(m for m, f in zip(step_ms, folds) if f == sel) / 1e3
-            if t_r > 0:
-                by_route[route] = {"achieved": b_r / t_r / 1e9, "frac": b_r / t_r / 1e9 / HBM_PEAK_GBS,
-                                   "launches": sum(1 for f in folds if f == sel)}
+            by_route[route] = {"achieved": b_r / t_r / 1e9, "frac": b_r / t_r / 1e9 / HBM_PEAK_GBS,
+                               "launches": sum(1 for f in folds if f == sel),
+                               "avg_launch_us": 1e6 * t_r / sum(1 for f in folds if f == sel)}
+        region_bytes = sum(step_bytes(w, c, c >= L) for c in timed_counts)
     else:
-        dec_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in sampled]
-        fl_ms = [evs[k][2].elapsed_time(evs[k][3]) for k in sampled if (args.warmup + k + 1) % L == 0]
+        dec_ms = [e[0].elapsed_time(e[1]) for e in route_evs]
+        fl_ms = [route_evs[L - 1][2].elapsed_time(route_evs[L - 1][3])]
         kernel_bytes = sum(decode_bytes(w, c, 1, st_bytes) for c in counts)
         kernel_time = sum(dec_ms) / 1e3
+        n_launch = L
         avg_us = 1e3 * sum(dec_ms) / len(dec_ms)
         kernel_name = "decode (output-only)"
         by_route = None
+        region_bytes = None
     achieved = kernel_bytes / kernel_time / 1e9
     layer.close()
     del layer
@@ -355,10 +394,19 @@ def bench_decode(args):
                    "checkpoint": "f32", "read_copy": args.read, "flush_every": L, "api": args.api},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": kernel_name, "avg_launch_us": avg_us, "timed_launches": len(sampled),
-                     "algorithmic_bytes_per_launch": kernel_bytes / len(counts),
+                     "kernel": kernel_name, "avg_launch_us": avg_us, "timed_launches": n_launch,
+                     "launches_from": (f"{reps} whole windows (ring counts 1..{L}, one fold each) back to back "
+                                       "after the timed region, one pair of HIP events around them"
+                                       if args.api == "step" else
+                                       f"one window (ring counts 1..{L}), each decode launch between HIP events"),
+                     "algorithmic_bytes_per_launch": kernel_bytes / n_launch,
                      "read_ceiling_GBs": ceiling, "frac_of_read_ceiling": achieved / ceiling,
                      "by_route": by_route},
+        "timed_region": {"folds": folds_timed, "fold_fraction": folds_timed / args.steps,
+                         "schedule_fold_fraction": 1.0 / L,
+                         "event_ms": 1e3 * region_s,
+                         "achieved_GBs": (region_bytes / region_s / 1e9) if region_bytes else None},
+        "flop_model": flop_model(P, N),
         ("output_only_launch_avg_us" if args.api == "step" else "decode_avg_us"):
             1e3 * sum(dec_ms) / max(1, len(dec_ms)),
         ("fold_launch_avg_us" if args.api == "step" else "flush_avg_us"):
@@ -681,8 +729,9 @@ def main():
     ap.add_argument("--read", default="f32", choices=["f32", "bf16", "fp8"],
                     help="checkpoint the outputs read: the float32 master or a bf16 / e4m3 copy")
     ap.add_argument("--event-stride", type=int, default=0,
-                    help="bracket every n-th launch of the timed loop with HIP events for the kernel's "
-                         "launch time (default: L + 1 for decode, which visits every ring count; 4 for verify)")
+                    help="verify: bracket every n-th round's launch with HIP events (default 4)")
+    ap.add_argument("--roofline-windows", type=int, default=4,
+                    help="decode: whole windows run back to back after the timed region for the roofline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true", help="skip the eager baseline timing")
     ap.add_argument("--probe-copy-gib", type=float, default=0.0,

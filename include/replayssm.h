@@ -29,8 +29,8 @@
  *    buffers given to replay_init: they must outlive it.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call that
  *    enqueues work is asynchronous on that stream and performs no host
- *    synchronisation, except replay_get_error and replay_destroy, which
- *    synchronise the given stream.
+ *    synchronisation, except replay_get_error, replay_destroy and
+ *    replay_set_flush_skipping(enable = 1), which synchronise the given stream.
  *  - Argument problems the host can see (NULL pointer, a misaligned pointer,
  *    a size outside the compiled specialisations, W out of range) return an
  *    error status and enqueue nothing.  State tiles, ring buffers and the
@@ -42,8 +42,8 @@
  *  - A handle is not thread-safe; distinct handles are independent.  Calls on
  *    one handle must be issued in order on one stream (or ordered by the
  *    caller across streams).
- *  - Graphs: every call that enqueues work, except replay_get_error and
- *    replay_destroy, may be recorded into a HIP graph by stream capture and
+ *  - Graphs: every call that enqueues work, except the synchronising ones
+ *    above, may be recorded into a HIP graph by stream capture and
  *    replayed: it allocates nothing, records no memset and does not
  *    synchronise.  Replays read the pointer arguments given at capture, so
  *    new inputs go into those same buffers before each replay.
@@ -201,7 +201,8 @@ replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *s
    The handle keeps host-side bounds on every sequence's count from the calls
    that move the pointers; a flush that no sequence can be due for enqueues
    nothing (in the standard schedule, every flush but the one that folds).
-   So pos and base must change only through this library's calls.  Once a
+   So pos and base must change only through this library's calls, or the
+   caller turns the skipping off with replay_set_flush_skipping.  Once a
    call that moves the pointers has been recorded into a HIP graph, replays
    move them without the handle seeing it, and from then on every flush is
    enqueued. */
@@ -251,6 +252,20 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
 replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, const void *k,
                                  const void *v, const float *dt, const float *a, float *y,
                                  int32_t flush_at, void *stream);
+
+/* The host-side count bounds that let replay_flush skip launches (see
+   replay_flush) hold only while pos and base change through this library.
+   enable = 0: for engines that move pos or base themselves (a sampler that
+   rewinds, a copy of another layer's pointers): from now on every flush is
+   enqueued.  Enqueues nothing; may be called at any time.
+   enable = 1: synchronise `stream`, read every sequence's pos and base back
+   and rebuild the bounds from them, then skip flushes again where no
+   sequence can be due (this also ends the "every flush" mode a graph
+   capture starts: call it only when no recorded graph that moves these
+   pointers will be replayed again).  If some sequence holds pos < 0,
+   base < 0 or a count outside 0..L, returns REPLAY_ERR_INVALID_ARG and
+   every flush stays enqueued.  Synchronising: not for stream capture. */
+replay_status replay_set_flush_skipping(replay_handle *h, int32_t enable, void *stream);
 
 /* Synchronise `stream`, copy the error bits to the host and clear them on the
    device.  *word = OR over sequences; per_seq (may be NULL): host int32 [B]. */

@@ -21,7 +21,7 @@ __all__ = [
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
     "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_verify_step",
-    "replay_get_error",
+    "replay_set_flush_skipping", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 ]
 
@@ -35,7 +35,7 @@ EXPORTS = (
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
     "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_verify_step",
-    "replay_get_error",
+    "replay_set_flush_skipping", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 )
 
@@ -82,6 +82,7 @@ def _load():
     L.replay_step.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
     L.replay_verify_step.argtypes = [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
     L.replay_get_error.argtypes = [_VP, ctypes.POINTER(_I32), _VP, _VP]
+    L.replay_set_flush_skipping.argtypes = [_VP, _I32, _VP]
     L.replay_eager_step.argtypes = [ctypes.POINTER(ReplayConfig)] + [_VP] * 9
     L.replay_eager_select.argtypes = [ctypes.POINTER(ReplayConfig), _VP, _I32, _VP, _VP, _VP]
     L.replay_stream_probe.argtypes = [_I32, _VP, _VP, ctypes.c_size_t, _VP]
@@ -177,6 +178,10 @@ def replay_step(h, q, k, v, dt, a, y, flush_at, stream=None):
 def replay_verify_step(h, W, q, k, v, dt, a, y, flush_at, stream=None):
     _check(lib.replay_verify_step(h, W, _ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a), _ptr(y), flush_at,
                                   _stream(stream)), "replay_verify_step")
+
+
+def replay_set_flush_skipping(h, enable: int, stream=None):
+    _check(lib.replay_set_flush_skipping(h, int(enable), _stream(stream)), "replay_set_flush_skipping")
 
 
 def replay_get_error(h, batch: int, stream=None):
@@ -283,6 +288,9 @@ class ReplayLayer:
 
     def load_checkpoint(self, s_src, stream=None):
         replay_load_checkpoint(self.h, s_src, stream)
+
+    def set_flush_skipping(self, enable: bool, stream=None):
+        replay_set_flush_skipping(self.h, 1 if enable else 0, stream)
 
     def get_error(self, stream=None):
         return replay_get_error(self.h, self.cfg.batch, stream)

@@ -20,6 +20,7 @@ struct replay_handle {
     replay_buffers bufs;
     CountBound bound;   // upper bounds on every sequence's count and pos
     bool graphed = false;   // a call that moves the pointers was recorded into a graph
+    bool untracked = false; // the caller moves pos / base itself (replay_set_flush_skipping(0))
 };
 
 namespace {
@@ -148,7 +149,7 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
     const int st_copy = c.read_copy == REPLAY_NONE ? -1 : state_kind(c.read_copy);
     // no sequence can be due: the kernel would change nothing
     note_capture(h, s);
-    if (!load_src && !h->graphed && !h->bound.flush_may_fold(min_count)) return REPLAY_OK;
+    if (!load_src && !h->graphed && !h->untracked && !h->bound.flush_may_fold(min_count)) return REPLAY_OK;
     const hipError_t e = launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s);
     if (e != hipSuccess) {
         h->bound.unknown();
@@ -396,6 +397,32 @@ replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, con
         return REPLAY_ERR_HIP;
     }
     h->bound.verify_round(flush_at, W);
+    return REPLAY_OK;
+}
+
+replay_status replay_set_flush_skipping(replay_handle *h, int32_t enable, void *stream) {
+    if (!h || (enable != 0 && enable != 1)) return REPLAY_ERR_INVALID_ARG;
+    if (!enable) {
+        h->untracked = true;
+        return REPLAY_OK;
+    }
+    // rebuild the bounds from the pointers on the device
+    hipStream_t s = as_stream(stream);
+    const int B = h->cfg.batch;
+    int32_t *host = new (std::nothrow) int32_t[2 * (size_t)B];
+    if (!host) return REPLAY_ERR_INVALID_ARG;
+    hipError_t e = hipMemcpyAsync(host, h->bufs.pos, sizeof(int32_t) * B, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(host + B, h->bufs.base, sizeof(int32_t) * B, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        delete[] host;
+        return REPLAY_ERR_HIP;
+    }
+    const bool ok = h->bound.from_pointers(host, host + B, B);
+    delete[] host;
+    if (!ok) return REPLAY_ERR_INVALID_ARG;   // pointers outside 0 <= base <= pos, count <= L: stay untracked
+    h->untracked = false;
+    h->graphed = false;
     return REPLAY_OK;
 }
 

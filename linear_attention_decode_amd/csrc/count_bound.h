@@ -38,6 +38,25 @@ struct CountBound {
     }
     // checkpoint load: base = pos everywhere
     void load() { lo = hi = 0; }
+    // rebuilt from every sequence's pointers as read back from the device:
+    // the smallest and largest count and the largest pos.  Pointers outside
+    // 0 <= base <= pos with count <= L leave the bounds as they were (false).
+    bool from_pointers(const int32_t *pos_b, const int32_t *base_b, int32_t B) {
+        int32_t l = L, h = 0;
+        int64_t p = 0;
+        for (int32_t b = 0; b < B; ++b) {
+            const int64_t c = (int64_t)pos_b[b] - base_b[b];
+            if (base_b[b] < 0 || c < 0 || c > L) return false;
+            if (c < l) l = (int32_t)c;
+            if (c > h) h = (int32_t)c;
+            if (pos_b[b] > p) p = pos_b[b];
+        }
+        if (B < 1) l = 0;
+        lo = l;
+        hi = h;
+        pos = p;
+        return true;
+    }
     // rollback: counts drop by amounts only the device knows
     void rollback() { lo = 0; }
 

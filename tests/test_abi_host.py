@@ -99,7 +99,9 @@ def test_calls_validate_before_touching_the_device(lad):
                      (lad.lib.replay_rollback, (None, 0x1000, None)),
                      (lad.lib.replay_load_checkpoint, (None, 0x1000, None)),
                      (lad.lib.replay_append, (None, 1, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None)),
-                     (lad.lib.replay_step, (None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 16, None))]:
+                     (lad.lib.replay_step, (None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 16, None)),
+                     (lad.lib.replay_set_flush_skipping, (None, 0, None)),
+                     (lad.lib.replay_set_flush_skipping, (None, 1, None))]:
         assert fn(*args) == 1
     # eager step: misaligned state pointer, unsupported shape
     assert lad.lib.replay_eager_step(ctypes.byref(c), 0x1004, 0x1000, 0x1000, 0x1000, 0x1000,

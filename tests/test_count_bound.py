@@ -36,6 +36,9 @@ void cb_step(void *h, int f) { static_cast<CountBound *>(h)->step(f); }
 void cb_verify_round(void *h, int f, int W) { static_cast<CountBound *>(h)->verify_round(f, W); }
 void cb_rollback(void *h) { static_cast<CountBound *>(h)->rollback(); }
 void cb_load(void *h) { static_cast<CountBound *>(h)->load(); }
+int cb_from_pointers(void *h, const int *pos, const int *base, int B) {
+    return static_cast<CountBound *>(h)->from_pointers(pos, base, B);
+}
 void cb_get(void *h, long long *out) {
     auto *b = static_cast<CountBound *>(h);
     out[0] = b->lo; out[1] = b->hi; out[2] = b->pos;
@@ -53,6 +56,7 @@ def cb(tmp_path_factory):
                    check=True)
     L = ctypes.CDLL(str(lib))
     L.cb_new.restype = ctypes.c_void_p
+    L.cb_from_pointers.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     for name in ("cb_free", "cb_set_pos", "cb_append", "cb_may_fold", "cb_flush", "cb_step", "cb_verify_round",
                  "cb_rollback", "cb_load", "cb_get"):
         getattr(L, name).argtypes = [ctypes.c_void_p] + {
@@ -178,3 +182,42 @@ def test_standard_schedule_is_exact(cb, L):
                 assert sum(launched) == T // L
         finally:
             cb.cb_free(h)
+
+
+def _from_pointers(cb, h, pos, base):
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    base = np.ascontiguousarray(base, dtype=np.int32)
+    return bool(cb.cb_from_pointers(h, pos.ctypes.data, base.ctypes.data, len(pos)))
+
+
+@pytest.mark.parametrize("L,seed", [(4, 11), (16, 12), (32, 13)])
+def test_bounds_rebuilt_from_pointers(cb, L, seed):
+    """replay_set_flush_skipping(1) rebuilds the range from the pointers read
+    back from the device: after pointers moved behind the handle's back (a
+    rollback of unknown size, an engine's own appends) the rebuilt range is
+    exact -- lo and hi are the smallest and largest count -- and further
+    calls keep it valid.  Pointers outside 0 <= base <= pos, count <= L are
+    refused and leave the range unchanged."""
+    rng = np.random.default_rng(seed)
+    B = 7
+    m = oring.RingModel(B, L)
+    h = cb.cb_new(L)
+    try:
+        for it in range(400):
+            # moves the handle never sees
+            m.pos[:] = m.base + rng.integers(0, L + 1, size=B)
+            assert _from_pointers(cb, h, m.pos, m.base)
+            lo, hi, pb = _get(cb, h)
+            assert (lo, hi, pb) == (int(m.count.min()), int(m.count.max()), int(m.pos.max())), it
+            f = int(rng.integers(-1, L + 3))
+            model_step(m, f)
+            cb.cb_step(h, f)
+            _check(cb, h, m, ("after rebuild", it))
+            m.take_error()
+        before = _get(cb, h)
+        bad = [(m.pos, m.pos + 1), (m.base + L + 1, m.base), (m.pos, np.full(B, -1))]
+        for pos, base in bad:
+            assert not _from_pointers(cb, h, pos, base)
+            assert _get(cb, h) == before
+    finally:
+        cb.cb_free(h)

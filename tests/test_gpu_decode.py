@@ -3,7 +3,8 @@ L steps) against the float64 oracle, through the C ABI.
 
 Tolerance: the stated 1e-4 maximum relative error for a float32
 checkpoint, per head: max_p |y - y_ref| / max_p |y_ref| for every
-(sequence, token, head); the per-token figure over the layer's whole
+(sequence, token, head), the denominator floored at 1 % of the head's term
+magnitude (tests/parity.py); the per-token figure over the layer's whole
 output (heads x P) must meet it too.  Ring integers (pos, base) must match the integer model
 bit for bit after every call.
 """
@@ -38,7 +39,7 @@ def _standard_case(w, T, seqs):
     S = np.zeros((len(seqs), w.heads, w.head_dim, w.state_dim))
     y_ref = runs.standard(x, S)
     y_gpu = y.cpu().numpy()[:, seqs]
-    gu.assert_f32(y_gpu, y_ref)
+    gu.assert_f32(y_gpu, y_ref, gu.y_abs_standard(x, S.shape))
     # the checkpoint after the last flush equals the oracle state there
     last_flush = (T // w.ring_len) * w.ring_len
     if last_flush > 0:

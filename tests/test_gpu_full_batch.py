@@ -8,8 +8,9 @@ is covered here on all of them:
 * standard decode (B=256, H=128, G=8, P=64, N=128, L=16, bf16 q/k/v,
   float32 checkpoint), 64 steps (4 folds) through the fused replay_step, the
   launch sequence the benchmark times: every output of every sequence and
-  head within 1e-4 per head (max_p |y - y_ref| / max_p |y_ref|), and every
-  checkpoint after the last fold within 1e-4 of the oracle state;
+  head within 1e-4 per head (max_p |y - y_ref| / max_p |y_ref|, floored at
+  1 % of the head's term magnitude: tests/parity.py), and every checkpoint
+  after the last fold within 1e-4 of the oracle state;
 * speculative verify (B=256, H=64, W=5, accepted drafts ~ U{0..5}), 32 fused
   rounds through replay_verify_step: every draft's output of every sequence
   within 1e-4 per head, the ring integers of every sequence after every
@@ -54,7 +55,7 @@ def test_step_every_sequence_decode_workload():
     x = dev.oracle()
     S = np.zeros((w.batch, w.heads, w.head_dim, w.state_dim))
     y_ref = runs.standard(x, S)
-    gu.assert_f32(y.cpu().numpy(), y_ref, what="all 256 sequences:")
+    gu.assert_f32(y.cpu().numpy(), y_ref, gu.y_abs_standard(x, S.shape), what="all 256 sequences:")
     del y_ref
     # T is a multiple of L: the last step folded, so the checkpoint is the state after token T
     S_gpu = layer.s_master.cpu().numpy()
@@ -78,5 +79,6 @@ def test_verify_step_every_sequence_verify_workload():
     x = dev.oracle()
     S = np.zeros((w.batch, w.heads, w.head_dim, w.state_dim))
     y_ref = runs.verify_rounds(x, accept, W, S)                       # [R][W][B][H][P]
-    gu.assert_f32(y.cpu().numpy().transpose(0, 2, 1, 3, 4), y_ref, what="all 256 sequences:")
+    y_abs = gu.y_abs_verify(x, accept, W, S.shape)
+    gu.assert_f32(y.cpu().numpy().transpose(0, 2, 1, 3, 4), y_ref, y_abs, what="all 256 sequences:")
     layer.close()

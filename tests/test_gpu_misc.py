@@ -49,7 +49,7 @@ def test_decode_workload_full_length():
     x = runs.widen_inputs({k: synth.to_storage(v[:, seqs]) for k, v in dev.items()}, w.io_dtype)
     S = np.zeros((len(seqs), w.heads, w.head_dim, w.state_dim))
     y_ref = runs.standard(x, S)
-    gu.assert_f32(y.cpu().numpy()[:, seqs], y_ref)
+    gu.assert_f32(y.cpu().numpy()[:, seqs], y_ref, gu.y_abs_standard(x, S.shape))
     S_gpu = layer.s_master.cpu().numpy()[seqs].astype(np.float64)
     assert float(np.max(runs.normwise_rel_err(S_gpu, S, axes=(-3, -2, -1)))) <= 1e-4
     layer.close()
@@ -81,7 +81,7 @@ def test_eager_step_and_select(P, N, io):
     x = gu.oracle_inputs(w, 0, T, list(range(w.batch)))
     S_ref = np.zeros((w.batch, w.heads, P, N))
     y_ref = runs.standard(x, S_ref.copy())
-    gu.assert_f32(y.cpu().numpy(), y_ref)
+    gu.assert_f32(y.cpu().numpy(), y_ref, gu.y_abs_standard(x, S_ref.shape))
     for b in range(w.batch):
         Sb = np.zeros((1, w.heads, P, N))
         runs.standard({k: v[:3 + accept[b], [b]] for k, v in x.items()}, Sb)
@@ -230,3 +230,43 @@ def test_stream_probe_copy():
     out = torch.zeros((n + 32767) // 32768, dtype=torch.float32, device=gu.DEV)
     lad.replay_stream_probe(0, src, out, n)
     torch.cuda.synchronize()
+
+
+def test_flush_skipping_for_pointers_moved_outside_the_library():
+    """An engine that moves pos itself (here: two tokens appended behind the
+    handle's back) makes the handle's count bounds stale, so a due flush
+    would be skipped.  replay_set_flush_skipping(0) enqueues every flush (the
+    ring folds); replay_set_flush_skipping(1) reads the pointers back and
+    skips again where nothing can be due; pos and base follow the integer
+    ring model throughout."""
+    w = synth.Workload(batch=3, heads=4, groups=2, head_dim=64, state_dim=128, ring_len=4,
+                       io_dtype="bf16", config=synth.CONFIG_ID["misc"], layer=93)
+    gu.note("flush skipping with external pointer moves")
+    dev = gu.DevInputs(w, 0, 12)
+    layer = _layer(w)
+    for name in ("ring_q", "ring_k", "ring_v", "ring_dt", "ring_a"):
+        layer.t[name].zero_()
+    model = oring.RingModel(w.batch, w.ring_len)
+    for t in range(2):
+        layer.append(1, *dev.step(t))
+        model.append(1)
+    torch.cuda.synchronize()
+    layer.pos += 2                      # the engine's own appends (zeroed slots)
+    model.pos += 2
+    layer.set_flush_skipping(False)
+    layer.flush(4)                      # due on the device; the handle's bounds say count 2
+    model.flush(4)
+    gu.check_ring(layer, model, "flush with skipping off")
+    assert layer.base.cpu().tolist() == [4, 4, 4]
+    layer.set_flush_skipping(True)      # bounds rebuilt from the device: count 0 everywhere
+    for t in range(2, 6):
+        layer.append(1, *dev.step(t))
+        model.append(1)
+        layer.flush(4)
+        model.flush(4)
+        gu.check_ring(layer, model, f"step {t} after the rebuild")
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    assert layer.base.cpu().tolist() == [8, 8, 8]
+    assert torch.isfinite(layer.s_master).all()
+    layer.close()
