@@ -61,13 +61,15 @@
 extern "C" {
 #endif
 
-#define REPLAY_ABI_VERSION 5
+#define REPLAY_ABI_VERSION 6
 
 typedef enum {
     REPLAY_OK = 0,
     REPLAY_ERR_INVALID_ARG = 1,   /* NULL / misaligned pointer, bad size, W out of range */
     REPLAY_ERR_UNSUPPORTED = 2,   /* shape or dtype outside the compiled specialisations */
-    REPLAY_ERR_HIP = 3            /* a HIP runtime call failed (launch, copy, sync) */
+    REPLAY_ERR_HIP = 3,           /* a HIP runtime call failed (launch, copy, sync) */
+    REPLAY_ERR_TOO_LARGE = 4      /* replay_step_static: the layer needs more arrival counters
+                                     than the library's static array holds */
 } replay_status;
 
 /* Per-sequence error bits (device side, sticky until replay_get_error). */
@@ -126,7 +128,11 @@ typedef struct {
                            replay_append and the flush, one per 128-byte line (element [b][g][0] per
                            group, [b][G][0] per sequence; the rest is padding so that no
                            two counters share a line); zeroed by replay_init and zero
-                           again whenever no call is in flight */
+                           again whenever no call is in flight.  May be NULL: then
+                           replay_append, replay_flush, replay_load_checkpoint,
+                           replay_step and replay_verify_step return
+                           REPLAY_ERR_INVALID_ARG for the handle, and replay_step_static
+                           steps the layer */
 } replay_buffers;
 
 typedef struct replay_handle replay_handle;
@@ -227,6 +233,22 @@ replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream);
    kernels run in turn, replay_decode's rules give y). */
 replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v,
                           const float *dt, const float *a, float *y, int32_t flush_at, void *stream);
+
+/* replay_step for callers that cannot allocate device memory (code under
+   HIP graph capture, serving loops that forbid allocation): the same
+   kernels, results equal replay_step's bit for bit, but the arrival counters
+   live in a static array inside the library instead of the layer's `sync`
+   buffer, which may then be NULL.  The array is 2 MiB per GPU (held by
+   every GPU the library runs on until the process ends); a layer needs
+   B * (G + 1) * 128 bytes of it, and a larger one returns
+   REPLAY_ERR_TOO_LARGE and enqueues nothing (B * (G + 1) <= 16384, e.g.
+   B = 1820 at G = 8).  Every call first clears the counters it uses with a
+   fill kernel on `stream`; the array is shared by every handle on that GPU,
+   so calls of replay_step_static that can overlap on one GPU (other streams,
+   other threads) race and must be ordered by the caller.  Allocates
+   nothing: no hipMalloc, hipFree or allocating library call. */
+replay_status replay_step_static(replay_handle *h, const void *q, const void *k, const void *v,
+                                 const float *dt, const float *a, float *y, int32_t flush_at, void *stream);
 
 /* One speculative-verify round for every sequence: where the ring holds
    count >= max(flush_at, 1) entries, fold it into the checkpoint first; then

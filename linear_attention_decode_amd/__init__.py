@@ -20,8 +20,8 @@ __all__ = [
     "SEQERR_TOO_FEW", "SEQERR_POS_OVERFLOW", "EXPORTS",
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
-    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_verify_step",
-    "replay_set_flush_skipping", "replay_get_error",
+    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_step_static",
+    "replay_verify_step", "replay_set_flush_skipping", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 ]
 
@@ -34,8 +34,8 @@ SEQERR_RING_OVERFLOW, SEQERR_ROLLBACK_RANGE, SEQERR_TOO_FEW, SEQERR_POS_OVERFLOW
 EXPORTS = (
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
-    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_verify_step",
-    "replay_set_flush_skipping", "replay_get_error",
+    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_step_static",
+    "replay_verify_step", "replay_set_flush_skipping", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 )
 
@@ -83,6 +83,7 @@ def _load():
     L.replay_verify_step.argtypes = [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
     L.replay_get_error.argtypes = [_VP, ctypes.POINTER(_I32), _VP, _VP]
     L.replay_set_flush_skipping.argtypes = [_VP, _I32, _VP]
+    L.replay_step_static.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
     L.replay_eager_step.argtypes = [ctypes.POINTER(ReplayConfig)] + [_VP] * 9
     L.replay_eager_select.argtypes = [ctypes.POINTER(ReplayConfig), _VP, _I32, _VP, _VP, _VP]
     L.replay_stream_probe.argtypes = [_I32, _VP, _VP, ctypes.c_size_t, _VP]
@@ -175,6 +176,11 @@ def replay_step(h, q, k, v, dt, a, y, flush_at, stream=None):
                            _stream(stream)), "replay_step")
 
 
+def replay_step_static(h, q, k, v, dt, a, y, flush_at, stream=None):
+    _check(lib.replay_step_static(h, _ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a), _ptr(y), int(flush_at),
+                                  _stream(stream)), "replay_step_static")
+
+
 def replay_verify_step(h, W, q, k, v, dt, a, y, flush_at, stream=None):
     _check(lib.replay_verify_step(h, W, _ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a), _ptr(y), flush_at,
                                   _stream(stream)), "replay_verify_step")
@@ -220,11 +226,12 @@ class ReplayLayer:
     read_copy is set), s_scale [B,H] f32 (e4m3) or [B,H,P*N/32] uint8 E8M0
     (FP4), ring_q/ring_k [B,G,L,N], ring_v [B,H,L,P] (io
     dtype), ring_dt/ring_a [B,L,H] f32 (slot-major), pos/base [B] int32, err [B+1] int32,
-    sync [B, G+1, 32] int32 (arrival counters, one per 128-byte line).
+    sync [B, G+1, 32] int32 (arrival counters, one per 128-byte line; not
+    allocated with counters=False, for a layer stepped by step_static only).
     """
 
     def __init__(self, batch, heads, groups, head_dim, state_dim, ring_len, io_dtype="bf16",
-                 read_copy=None, shared_lowp=False, device="cuda", stream=None):
+                 read_copy=None, shared_lowp=False, device="cuda", stream=None, counters=True):
         import torch
         self.cfg = ReplayConfig(batch, heads, groups, head_dim, state_dim, ring_len,
                                 _DTYPE_CODE[io_dtype], _DTYPE_CODE[read_copy], int(bool(shared_lowp)))
@@ -247,7 +254,7 @@ class ReplayLayer:
         }
         self.t = {}
         for name in BUFFER_FIELDS:
-            if nbytes[name] == 0:
+            if nbytes[name] == 0 or (name == "sync" and not counters):
                 self.t[name] = None
                 continue
             shape, dt = shapes[name]
@@ -280,6 +287,10 @@ class ReplayLayer:
 
     def step(self, q, k, v, dt, a, y, flush_at=None, stream=None):
         replay_step(self.h, q, k, v, dt, a, y, self.cfg.ring_len if flush_at is None else flush_at, stream)
+
+    def step_static(self, q, k, v, dt, a, y, flush_at=None, stream=None):
+        """replay_step with the library's static arrival counters (no `sync` buffer needed)."""
+        replay_step_static(self.h, q, k, v, dt, a, y, self.cfg.ring_len if flush_at is None else flush_at, stream)
 
     def verify_step(self, W, q, k, v, dt, a, y, flush_at=None, stream=None):
         """Fold if due (count >= flush_at, default L - W + 1), append W drafts, score them."""

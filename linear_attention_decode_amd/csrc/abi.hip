@@ -8,6 +8,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "count_bound.h"
@@ -15,17 +16,53 @@
 
 using namespace replay;
 
+// Arrival counters owned by the library, for replay_step_static (callers
+// that cannot allocate device memory).  Every GPU the library runs on holds
+// its own copy of this array until the process ends.  Host code never uses
+// the name as an address: replay_init resolves the current device's copy
+// with hipGetSymbolAddress, once per device, and kernels get that pointer.
+constexpr size_t kStaticCounterBytes = size_t(2) << 20;
+static __device__ __align__(256) int32_t scratch[kStaticCounterBytes / sizeof(int32_t)];
+
 struct replay_handle {
     replay_config cfg;
     replay_buffers bufs;
     CountBound bound;   // upper bounds on every sequence's count and pos
     bool graphed = false;   // a call that moves the pointers was recorded into a graph
     bool untracked = false; // the caller moves pos / base itself (replay_set_flush_skipping(0))
+    int32_t *static_sync = nullptr;   // this device's copy of `scratch` (nullptr if it could not be resolved)
 };
 
 namespace {
 
 constexpr int kNumBufferFields = 12;
+constexpr int kSyncField = 11;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, resolved on first use on that device.
+hipError_t static_counters(int32_t **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<int32_t *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// bytes of arrival counters a configuration needs ([B][G + 1][kSyncStride] int32)
+size_t counter_bytes(const replay_config &c) {
+    return (size_t)c.batch * (size_t)(c.groups + 1) * kSyncStride * sizeof(int32_t);
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -121,14 +158,14 @@ void note_capture(replay_handle *h, hipStream_t s) {
 }
 
 // Fold (or load) into the checkpoint and rewrite the copy, then move base.
-replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_count, hipStream_t s) {
+replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_count, hipStream_t s, int32_t *sync) {
     const replay_config &c = h->cfg;
     FlushArgs a;
     a.r = ring_view(h);
     a.min_count = min_count;
     a.force_empty = load_src != nullptr;
     a.base_out = h->bufs.base;
-    a.sync = h->bufs.sync;
+    a.sync = sync;
     a.S_out = c.shared_lowp ? nullptr : h->bufs.s_master;
     a.copy_out = c.read_copy == REPLAY_NONE ? nullptr : h->bufs.s_copy;
     a.scale_out = (c.read_copy == REPLAY_FP8_E4M3 || c.read_copy == REPLAY_FP4_E2M1) ? h->bufs.s_scale : nullptr;
@@ -197,6 +234,7 @@ const char *replay_status_string(replay_status s) {
         case REPLAY_ERR_INVALID_ARG: return "invalid argument";
         case REPLAY_ERR_UNSUPPORTED: return "unsupported shape or dtype";
         case REPLAY_ERR_HIP: return "HIP runtime error";
+        case REPLAY_ERR_TOO_LARGE: return "batch too large for the library's static counters";
     }
     return "unknown status";
 }
@@ -221,6 +259,7 @@ replay_status replay_init(const replay_config *cfg, const replay_buffers *bufs, 
     for (int i = 0; i < kNumBufferFields; ++i) {
         const void *p = field(*bufs, i);
         if (need[i] == 0) continue;
+        if (i == kSyncField && !p) continue;   // no counters: only replay_step_static steps this layer
         if (!p || !aligned16(p)) return REPLAY_ERR_INVALID_ARG;
     }
     replay_handle *h = new (std::nothrow) replay_handle;
@@ -231,6 +270,7 @@ replay_status replay_init(const replay_config *cfg, const replay_buffers *bufs, 
     if (cfg->shared_lowp) h->bufs.s_master = nullptr;
     if (cfg->read_copy == REPLAY_NONE) h->bufs.s_copy = nullptr;
     if (cfg->read_copy != REPLAY_FP8_E4M3 && cfg->read_copy != REPLAY_FP4_E2M1) h->bufs.s_scale = nullptr;
+    if (static_counters(&h->static_sync) != hipSuccess) h->static_sync = nullptr;
 
     hipStream_t s = as_stream(stream);
     hipError_t e = hipSuccess;
@@ -242,7 +282,7 @@ replay_status replay_init(const replay_config *cfg, const replay_buffers *bufs, 
     if (e == hipSuccess) e = launch_fill_u32(h->bufs.pos, 0u, need[8] / 4, s);
     if (e == hipSuccess) e = launch_fill_u32(h->bufs.base, 0u, need[9] / 4, s);
     if (e == hipSuccess) e = launch_fill_u32(h->bufs.err, 0u, need[10] / 4, s);
-    if (e == hipSuccess) e = launch_fill_u32(h->bufs.sync, 0u, need[11] / 4, s);
+    if (e == hipSuccess && h->bufs.sync) e = launch_fill_u32(h->bufs.sync, 0u, need[kSyncField] / 4, s);
     if (e != hipSuccess) {
         delete h;
         return REPLAY_ERR_HIP;
@@ -259,27 +299,41 @@ replay_status replay_destroy(replay_handle *h, void *stream) {
 }
 
 replay_status replay_load_checkpoint(replay_handle *h, const float *s_src, void *stream) {
-    if (!h || !s_src || !aligned16(s_src)) return REPLAY_ERR_INVALID_ARG;
-    return run_flush(h, s_src, 0, as_stream(stream));
+    if (!h || !s_src || !aligned16(s_src) || !h->bufs.sync) return REPLAY_ERR_INVALID_ARG;
+    return run_flush(h, s_src, 0, as_stream(stream), h->bufs.sync);
 }
 
-replay_status replay_append(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
-                            const float *dt, const float *a, void *stream) {
-    if (!h || !q || !k || !v || !dt || !a) return REPLAY_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+replay_status append_impl(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
+                          const float *dt, const float *a, hipStream_t s, int32_t *sync) {
+    if (!q || !k || !v || !dt || !a) return REPLAY_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a))
         return REPLAY_ERR_INVALID_ARG;
     if (W < 1 || W > h->cfg.ring_len) return REPLAY_ERR_INVALID_ARG;
-    note_capture(h, as_stream(stream));
+    note_capture(h, s);
     const RingView r = ring_view(h);
     const hipError_t e = launch_append(h->cfg.head_dim, h->cfg.state_dim, r, h->bufs.ring_q, h->bufs.ring_k,
-                                       h->bufs.ring_v, h->bufs.ring_dt, h->bufs.ring_a, h->bufs.pos, h->bufs.sync,
-                                       W, q, k, v, dt, a, as_stream(stream));
+                                       h->bufs.ring_v, h->bufs.ring_dt, h->bufs.ring_a, h->bufs.pos, sync,
+                                       W, q, k, v, dt, a, s);
     if (e != hipSuccess) {
         h->bound.unknown();
         return REPLAY_ERR_HIP;
     }
     h->bound.append(W);
     return REPLAY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+replay_status replay_append(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
+                            const float *dt, const float *a, void *stream) {
+    if (!h || !h->bufs.sync) return REPLAY_ERR_INVALID_ARG;
+    return append_impl(h, W, q, k, v, dt, a, as_stream(stream), h->bufs.sync);
 }
 
 replay_status replay_decode(replay_handle *h, float *y, void *stream) {
@@ -300,12 +354,12 @@ replay_status replay_rollback(replay_handle *h, const int32_t *n_reject, void *s
 }
 
 replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream) {
-    if (!h) return REPLAY_ERR_INVALID_ARG;
-    return run_flush(h, nullptr, min_count, as_stream(stream));
+    if (!h || !h->bufs.sync) return REPLAY_ERR_INVALID_ARG;
+    return run_flush(h, nullptr, min_count, as_stream(stream), h->bufs.sync);
 }
 
 static StepArgs step_args(replay_handle *h, const void *q, const void *k, const void *v, const float *dt,
-                          const float *a, float *y, int32_t flush_at, int32_t W) {
+                          const float *a, float *y, int32_t flush_at, int32_t W, int32_t *sync) {
     const replay_config &c = h->cfg;
     StepArgs sa;
     sa.ring_q = h->bufs.ring_q;
@@ -316,7 +370,7 @@ static StepArgs step_args(replay_handle *h, const void *q, const void *k, const 
     sa.pos = h->bufs.pos;
     sa.base = h->bufs.base;
     sa.err = h->bufs.err;
-    sa.sync = h->bufs.sync;
+    sa.sync = sync;
     sa.S = h->bufs.s_master;
     sa.q = q;
     sa.k = k;
@@ -337,15 +391,12 @@ static StepArgs step_args(replay_handle *h, const void *q, const void *k, const 
     return sa;
 }
 
-replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v, const float *dt,
-                          const float *a, float *y, int32_t flush_at, void *stream) {
-    if (!h || !q || !k || !v || !dt || !a || !y) return REPLAY_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a) || !aligned4(y))
-        return REPLAY_ERR_INVALID_ARG;
+// One standard decode step with the arrival counters at `sync`.
+static replay_status step_impl(replay_handle *h, const void *q, const void *k, const void *v, const float *dt,
+                               const float *a, float *y, int32_t flush_at, hipStream_t s, int32_t *sync) {
     const replay_config &c = h->cfg;
-    hipStream_t s = as_stream(stream);
     note_capture(h, s);
-    const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, 1);
+    const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, 1, sync);
     if (c.read_copy != REPLAY_NONE) {
         // copies: append + decode from an e4m3 or FP4 copy in one launch
         // (bf16 io), or the append and decode kernels in turn (a bf16 copy:
@@ -358,11 +409,11 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
             else
                 h->bound.unknown();
         } else {
-            st = replay_append(h, 1, q, k, v, dt, a, stream);
+            st = append_impl(h, 1, q, k, v, dt, a, s, sync);
             if (st == REPLAY_OK) st = run_verify(h, 1, y, s);
         }
         if (st != REPLAY_OK) return st;
-        return run_flush(h, nullptr, flush_at, s);
+        return run_flush(h, nullptr, flush_at, s, sync);
     }
     const hipError_t e = launch_step(c.head_dim, c.state_dim, sa, s);
     if (e != hipSuccess) {
@@ -373,21 +424,44 @@ replay_status replay_step(replay_handle *h, const void *q, const void *k, const 
     return REPLAY_OK;
 }
 
+static bool step_args_ok(const void *q, const void *k, const void *v, const float *dt, const float *a,
+                         const float *y) {
+    if (!q || !k || !v || !dt || !a || !y) return false;
+    return aligned16(q) && aligned16(k) && aligned16(v) && aligned4(dt) && aligned4(a) && aligned4(y);
+}
+
+replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v, const float *dt,
+                          const float *a, float *y, int32_t flush_at, void *stream) {
+    if (!h || !h->bufs.sync || !step_args_ok(q, k, v, dt, a, y)) return REPLAY_ERR_INVALID_ARG;
+    return step_impl(h, q, k, v, dt, a, y, flush_at, as_stream(stream), h->bufs.sync);
+}
+
+replay_status replay_step_static(replay_handle *h, const void *q, const void *k, const void *v, const float *dt,
+                                 const float *a, float *y, int32_t flush_at, void *stream) {
+    if (!h || !step_args_ok(q, k, v, dt, a, y)) return REPLAY_ERR_INVALID_ARG;
+    if (counter_bytes(h->cfg) > kStaticCounterBytes) return REPLAY_ERR_TOO_LARGE;
+    if (!h->static_sync) return REPLAY_ERR_HIP;
+    hipStream_t s = as_stream(stream);
+    // the array keeps whatever the last call on this GPU left: clear the
+    // counters this call uses (a fill kernel, no memset node in a graph)
+    if (launch_fill_u32(h->static_sync, 0u, counter_bytes(h->cfg) / sizeof(int32_t), s) != hipSuccess)
+        return REPLAY_ERR_HIP;
+    return step_impl(h, q, k, v, dt, a, y, flush_at, s, h->static_sync);
+}
+
 replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
                                  const float *dt, const float *a, float *y, int32_t flush_at, void *stream) {
-    if (!h || !q || !k || !v || !dt || !a || !y) return REPLAY_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(dt) || !aligned4(a) || !aligned4(y))
-        return REPLAY_ERR_INVALID_ARG;
+    if (!h || !h->bufs.sync || !step_args_ok(q, k, v, dt, a, y)) return REPLAY_ERR_INVALID_ARG;
     const replay_config &c = h->cfg;
     if (W < 1 || W > kMaxWideWindow || W > c.ring_len) return REPLAY_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     note_capture(h, s);
-    const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, W);
+    const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, W, h->bufs.sync);
     if (c.read_copy != REPLAY_NONE || !verify_step_fused(c.head_dim, c.state_dim, sa)) {
         // the flush, append and verify kernels in turn
-        replay_status st = run_flush(h, nullptr, flush_at, s);
+        replay_status st = run_flush(h, nullptr, flush_at, s, h->bufs.sync);
         if (st != REPLAY_OK) return st;
-        st = replay_append(h, W, q, k, v, dt, a, stream);
+        st = append_impl(h, W, q, k, v, dt, a, s, h->bufs.sync);
         if (st != REPLAY_OK) return st;
         return run_verify(h, W, y, s);
     }

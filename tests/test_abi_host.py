@@ -34,8 +34,8 @@ def test_every_declared_symbol_is_exported(lad):
 
 
 def test_version_and_status_strings(lad):
-    assert lad.replay_abi_version() == 5
-    for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "HIP")]:
+    assert lad.replay_abi_version() == 6
+    for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "HIP"), (4, "static counters")]:
         assert text in lad.replay_status_string(s)
     assert lad.replay_status_string(99) == "unknown status"
 
@@ -100,6 +100,7 @@ def test_calls_validate_before_touching_the_device(lad):
                      (lad.lib.replay_load_checkpoint, (None, 0x1000, None)),
                      (lad.lib.replay_append, (None, 1, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None)),
                      (lad.lib.replay_step, (None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 16, None)),
+                     (lad.lib.replay_step_static, (None, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 16, None)),
                      (lad.lib.replay_set_flush_skipping, (None, 0, None)),
                      (lad.lib.replay_set_flush_skipping, (None, 1, None))]:
         assert fn(*args) == 1
