@@ -653,8 +653,16 @@ def bench_stacked(args):
         layers = [lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16") for _ in range(8)]
         y = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
 
+        ys = [torch.empty((B, H, P), dtype=torch.float32, device="cuda") for _ in range(8)]
+
         def step(t):
             i = t % pool_n
+            if args.api == "layers":
+                # one launch steps all 8 layers
+                lad.replay_step_layers([x.h for x in layers], [p["q"][i] for p in pools], [p["k"][i] for p in pools],
+                                       [p["v"][i] for p in pools], [p["dt"][i] for p in pools],
+                                       [p["a"][i] for p in pools], ys, L)
+                return
             for li in range(8):
                 p = pools[li]
                 layers[li].step(p["q"][i], p["k"][i], p["v"][i], p["dt"][i], p["a"][i], y, flush_at=L)
@@ -707,9 +715,84 @@ def bench_stacked(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": f"synthetic (seeded, {pool_n} distinct steps per layer cycled)",
         "config": {"workload": "8 stacked SSM layers", "batch": 512, "heads": 64, "groups": 8,
-                   "head_dim": 128, "state_dim": 128, "ring_len": "8/16/32", "value_is": "L=16"},
+                   "head_dim": 128, "state_dim": 128, "ring_len": "8/16/32", "value_is": "L=16",
+                   "api": "one launch for all layers" if args.api == "layers" else "one launch per layer"},
         "per_ring_len": res, "eager": eager,
         "speedup_vs_eager_L16": res.get("L=16", best)["tokens_per_s"] / eager["tokens_per_s"],
+    }
+
+
+def bench_stacked_latency(args):
+    """Stacked layers (8 layers, H=64, G=8, P=N=128, L=16) at batch 1, 16 and
+    512: time per 8-layer decode step for the 8 per-layer launches
+    (replay_step) and for the single launch over all layers
+    (replay_step_layers), each issued eagerly and replayed from a HIP graph
+    of one step (inputs copied into the captured buffers before each replay
+    are not timed: the graph reads a pool slot the loop rotates)."""
+    import torch
+    import linear_attention_decode_amd as lad
+    L, NL = 16, 8
+    out = {}
+    for B in args.batches:
+        T = 32 if B >= 256 else (64 if B >= 64 else 256)
+        ws = [synth.named("stacked", batch=B, layer=li) for li in range(NL)]
+        w = ws[0]
+        H, G, P, N = w.heads, w.groups, w.head_dim, w.state_dim
+        pools = [input_pool(x, 16) for x in ws]
+        res = {}
+        for api in ("step", "layers"):
+            for graphed in (False, True):
+                layers = [lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16") for _ in range(NL)]
+                y = [torch.empty((B, H, P), dtype=torch.float32, device="cuda") for _ in range(NL)]
+                slot = [{k: v[0].clone() for k, v in p.items()} for p in pools]
+
+                def one(src):
+                    if api == "step":
+                        for li in range(NL):
+                            layers[li].step(src[li]["q"], src[li]["k"], src[li]["v"], src[li]["dt"], src[li]["a"],
+                                            y[li], flush_at=L)
+                    else:
+                        lad.replay_step_layers([x.h for x in layers], [src[li]["q"] for li in range(NL)],
+                                               [src[li]["k"] for li in range(NL)], [src[li]["v"] for li in range(NL)],
+                                               [src[li]["dt"] for li in range(NL)], [src[li]["a"] for li in range(NL)],
+                                               y, L)
+                pool_t = lambda t: [{k: v[t % 16] for k, v in p.items()} for p in pools]
+                for t in range(L):          # warm up one window
+                    one(pool_t(t))
+                torch.cuda.synchronize()
+                if graphed:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        one(slot)
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    for t in range(T):
+                        g.replay()
+                    torch.cuda.synchronize()
+                else:
+                    t0 = time.perf_counter()
+                    for t in range(T):
+                        one(pool_t(t))
+                    torch.cuda.synchronize()
+                el = time.perf_counter() - t0
+                for x in layers:
+                    assert x.get_error()[0] == 0
+                    x.close()
+                del layers
+                torch.cuda.empty_cache()
+                res[f"{api}{'-graph' if graphed else ''}"] = 1e6 * el / T
+        res["tokens_per_s_best"] = B * 1e6 / min(v for k, v in res.items())
+        out[f"B={B}"] = res
+    return {
+        "metric": "8-layer stacked decode step time (us) by launch form, per batch",
+        "value": out[f"B={args.batches[0]}"]["layers-graph"], "unit": "us per 8-layer step", "n_gpus": 1,
+        "steps": None, "warmup": 16, "ms_per_step": out[f"B={args.batches[0]}"]["layers-graph"] / 1e3,
+        "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded, 16 steps per layer cycled)",
+        "config": {"workload": "8 stacked SSM layers, step latency", "heads": 64, "groups": 8, "head_dim": 128,
+                   "state_dim": 128, "ring_len": L,
+                   "value_is": f"B={args.batches[0]}, one launch for all layers, graph"},
+        "us_per_step": out,
     }
 
 
@@ -718,20 +801,23 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="decode", choices=["decode", "verify", "dual", "stacked"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "verify", "dual", "stacked", "stacked-latency"])
     ap.add_argument("--quick", action="store_true", help="dual/stacked: one variant only")
     ap.add_argument("--window", type=int, default=5,
                     help="verify: drafts per round (5 is the benchmarked workload; up to 16, windows past 8 "
                          "on the matrix cores through the separate calls)")
-    ap.add_argument("--api", default="step", choices=["step", "calls"],
+    ap.add_argument("--api", default="step", choices=["step", "calls", "layers"],
                     help="step: one fused launch per decode step (replay_step) or verify round "
-                         "(replay_verify_step); calls: the append, decode/verify and flush kernels")
+                         "(replay_verify_step); calls: the append, decode/verify and flush kernels; "
+                         "layers (stacked): one launch steps all layers (replay_step_layers)")
     ap.add_argument("--read", default="f32", choices=["f32", "bf16", "fp8"],
                     help="checkpoint the outputs read: the float32 master or a bf16 / e4m3 copy")
     ap.add_argument("--event-stride", type=int, default=0,
                     help="verify: bracket every n-th round's launch with HIP events (default 4)")
     ap.add_argument("--roofline-windows", type=int, default=4,
                     help="decode: whole windows run back to back after the timed region for the roofline")
+    ap.add_argument("--batches", type=lambda t: [int(x) for x in t.split(",")], default=[1, 16, 512],
+                    help="stacked-latency: batch sizes, comma-separated")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true", help="skip the eager baseline timing")
     ap.add_argument("--probe-copy-gib", type=float, default=0.0,
@@ -756,7 +842,7 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     out = {"decode": bench_decode, "verify": bench_verify, "dual": bench_dual,
-           "stacked": bench_stacked}[args.workload](args)
+           "stacked": bench_stacked, "stacked-latency": bench_stacked_latency}[args.workload](args)
     print(json.dumps(out))
 
 

@@ -234,6 +234,23 @@ replay_status replay_flush(replay_handle *h, int32_t min_count, void *stream);
 replay_status replay_step(replay_handle *h, const void *q, const void *k, const void *v,
                           const float *dt, const float *a, float *y, int32_t flush_at, void *stream);
 
+/* replay_step for n stacked layers of one shape in a single launch (page
+   "ReplaySSM: Cachear Inputs, No Estado", "Resultados": decode is served
+   under CUDA Graphs, where launch gaps between layers matter; here the
+   layers' steps share one grid).  layers: host array of n distinct handles,
+   1 <= n <= 16, whose configs agree in every shape field and io dtype, each
+   with a float32 checkpoint read (read_copy NONE; else UNSUPPORTED) and its
+   `sync` buffer; q, k, v, dt, a, y: host arrays of n device pointers, entry
+   i laid out as replay_step's arguments for layer i.  Results equal
+   replay_step on each layer in turn, bit for bit (the same kernel code; the
+   layers are independent).  Errors as replay_step, per layer.  One launch
+   covers all layers while a layer has at most 8192 compute workgroups
+   (B * H, doubled for 128-row heads with bf16 io); larger layers are
+   stepped by one launch each, which measured faster there. */
+replay_status replay_step_layers(replay_handle *const *layers, int32_t n, const void *const *q,
+                                 const void *const *k, const void *const *v, const float *const *dt,
+                                 const float *const *a, float *const *y, int32_t flush_at, void *stream);
+
 /* replay_step for callers that cannot allocate device memory (code under
    HIP graph capture, serving loops that forbid allocation): the same
    kernels, results equal replay_step's bit for bit, but the arrival counters

@@ -20,7 +20,7 @@ __all__ = [
     "SEQERR_TOO_FEW", "SEQERR_POS_OVERFLOW", "EXPORTS",
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
-    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_step_static",
+    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_step_layers", "replay_step_static",
     "replay_verify_step", "replay_set_flush_skipping", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 ]
@@ -34,7 +34,7 @@ SEQERR_RING_OVERFLOW, SEQERR_ROLLBACK_RANGE, SEQERR_TOO_FEW, SEQERR_POS_OVERFLOW
 EXPORTS = (
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
-    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_step_static",
+    "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_step_layers", "replay_step_static",
     "replay_verify_step", "replay_set_flush_skipping", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 )
@@ -84,6 +84,7 @@ def _load():
     L.replay_get_error.argtypes = [_VP, ctypes.POINTER(_I32), _VP, _VP]
     L.replay_set_flush_skipping.argtypes = [_VP, _I32, _VP]
     L.replay_step_static.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
+    L.replay_step_layers.argtypes = [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
     L.replay_eager_step.argtypes = [ctypes.POINTER(ReplayConfig)] + [_VP] * 9
     L.replay_eager_select.argtypes = [ctypes.POINTER(ReplayConfig), _VP, _I32, _VP, _VP, _VP]
     L.replay_stream_probe.argtypes = [_I32, _VP, _VP, ctypes.c_size_t, _VP]
@@ -174,6 +175,14 @@ def replay_flush(h, min_count, stream=None):
 def replay_step(h, q, k, v, dt, a, y, flush_at, stream=None):
     _check(lib.replay_step(h, _ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a), _ptr(y), flush_at,
                            _stream(stream)), "replay_step")
+
+
+def replay_step_layers(handles, q, k, v, dt, a, y, flush_at, stream=None):
+    """handles, q, k, v, dt, a, y: sequences of n entries (one per layer)."""
+    n = len(handles)
+    arr = lambda xs: (_VP * n)(*[_ptr(x) for x in xs])
+    _check(lib.replay_step_layers((_VP * n)(*handles), n, arr(q), arr(k), arr(v), arr(dt), arr(a), arr(y),
+                                  int(flush_at), _stream(stream)), "replay_step_layers")
 
 
 def replay_step_static(h, q, k, v, dt, a, y, flush_at, stream=None):

@@ -449,6 +449,47 @@ replay_status replay_step_static(replay_handle *h, const void *q, const void *k,
     return step_impl(h, q, k, v, dt, a, y, flush_at, s, h->static_sync);
 }
 
+replay_status replay_step_layers(replay_handle *const *layers, int32_t n, const void *const *q,
+                                 const void *const *k, const void *const *v, const float *const *dt,
+                                 const float *const *a, float *const *y, int32_t flush_at, void *stream) {
+    if (!layers || !q || !k || !v || !dt || !a || !y || n < 1 || n > kMaxStepLayers) return REPLAY_ERR_INVALID_ARG;
+    const replay_handle *h0 = layers[0];
+    if (!h0) return REPLAY_ERR_INVALID_ARG;
+    const replay_config &c0 = h0->cfg;
+    for (int i = 0; i < n; ++i) {
+        const replay_handle *h = layers[i];
+        if (!h || !h->bufs.sync || !step_args_ok(q[i], k[i], v[i], dt[i], a[i], y[i])) return REPLAY_ERR_INVALID_ARG;
+        const replay_config &c = h->cfg;
+        if (c.batch != c0.batch || c.heads != c0.heads || c.groups != c0.groups || c.head_dim != c0.head_dim ||
+            c.state_dim != c0.state_dim || c.ring_len != c0.ring_len || c.io_dtype != c0.io_dtype)
+            return REPLAY_ERR_INVALID_ARG;
+        if (c.read_copy != REPLAY_NONE) return REPLAY_ERR_UNSUPPORTED;
+        for (int j = 0; j < i; ++j)
+            if (layers[j] == h) return REPLAY_ERR_INVALID_ARG;   // one layer twice in one launch would race
+    }
+    hipStream_t s = as_stream(stream);
+    StepLayersArgs la;
+    la.n = n;
+    for (int i = 0; i < n; ++i) {
+        replay_handle *h = layers[i];
+        note_capture(h, s);
+        la.l[i] = step_args(h, q[i], k[i], v[i], dt[i], a[i], y[i], flush_at, 1, h->bufs.sync);
+    }
+    hipError_t e = hipSuccess;
+    if (step_workgroups_per_layer(c0.head_dim, la.l[0]) <= kLayersOneLaunchMax) {
+        e = launch_step_layers(c0.head_dim, c0.state_dim, la, s);
+    } else {
+        for (int i = 0; i < n && e == hipSuccess; ++i) e = launch_step(c0.head_dim, c0.state_dim, la.l[i], s);
+    }
+    for (int i = 0; i < n; ++i) {
+        if (e != hipSuccess)
+            layers[i]->bound.unknown();
+        else
+            layers[i]->bound.step(flush_at);
+    }
+    return from_hip(e);
+}
+
 replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
                                  const float *dt, const float *a, float *y, int32_t flush_at, void *stream) {
     if (!h || !h->bufs.sync || !step_args_ok(q, k, v, dt, a, y)) return REPLAY_ERR_INVALID_ARG;

@@ -86,6 +86,14 @@ struct StepArgs {
     int32_t copy_st;                  // StateKind of the copy (ST_BF16, ST_FP8, ST_FP4)
 };
 
+// n layers of one shape stepped in one launch (step_layers_kernel); passed
+// by value in the kernel arguments.
+constexpr int kMaxStepLayers = 16;
+struct StepLayersArgs {
+    StepArgs l[kMaxStepLayers];
+    int32_t n;
+};
+
 struct EagerArgs {
     const float *S_in;
     float *S_out;
@@ -109,6 +117,12 @@ hipError_t launch_rollback(const RingView &r, int32_t *pos, const int32_t *n_rej
 hipError_t launch_fill_u32(void *dst, uint32_t value, size_t count, hipStream_t s);
 hipError_t launch_eager(int P, int N, const EagerArgs &a, hipStream_t s);
 hipError_t launch_step(int P, int N, const StepArgs &a, hipStream_t s);
+hipError_t launch_step_layers(int P, int N, const StepLayersArgs &a, hipStream_t s);   // 1 <= a.n <= kMaxStepLayers
+int step_workgroups_per_layer(int P, const StepArgs &a);   // compute workgroups of one layer's step
+// Layers with more compute workgroups than this are stepped one launch
+// each: there the single launch measured slower (8 layers, 128 x 128 heads:
+// -4 % at 8192 workgroups a layer, +1.3 % at 16384, +5 % at 65536).
+constexpr int kLayersOneLaunchMax = 8192;
 hipError_t launch_verify_step(int P, int N, const StepArgs &a, hipStream_t s);
 hipError_t launch_step_copy(int P, int N, const StepArgs &a, hipStream_t s);   // append + decode from the copy
 bool verify_step_fused(int P, int N, const StepArgs &a);   // the fused round covers this case

@@ -167,10 +167,11 @@ constexpr int step_ring_waves() { return IOB ? LM / 16 : 1; }
 template <int P, bool IOB>
 constexpr int step_row_splits() { return IOB && P == 128 ? 2 : 1; }
 
+// One compute workgroup of the fused step: logical workgroup `bid` of the
+// `ncomp` = B * H * RS of one layer.
 // PH = rows of the head, RS = workgroups per head (rows P = PH / RS each).
 template <int PH, int N, int LM, bool IOB, int RS>
-__global__ __launch_bounds__((StepShape<PH / RS, N>::NTS + 64 * step_ring_waves<LM, IOB>()))
-__attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void step_kernel(StepArgs args) {
+__device__ __forceinline__ void step_body(const StepArgs &args, int bid, int ncomp) {
     constexpr int P = PH / RS;
     static_assert(RS == 1 || IOB, "row splits need the bf16 ring wavefront");
     using Sh = StepShape<P, N>;
@@ -186,12 +187,7 @@ __attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void ste
     __shared__ __align__(16) float s_sw[1][IOB ? LM : 4];
 
     const int H = args.H, L = args.L;
-    const int ncomp = args.B * H * RS;   // compute workgroups; one writer per sequence follows
-    if ((int)blockIdx.x >= ncomp) {
-        step_token_writer<PH, N, IOB, true>(args, (int)blockIdx.x - ncomp, threadIdx.x, blockDim.x);
-        return;
-    }
-    const int lid = xcd_remap(blockIdx.x, ncomp);
+    const int lid = xcd_remap(bid, ncomp);
     const int b = lid / (H * RS), h = (lid / RS) % H, p0 = (lid % RS) * P;   // rows p0 .. p0+P-1
     const int g = (h * args.G) / H;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -317,6 +313,67 @@ __attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void ste
         atomicExch(args.sync + ((size_t)b * (args.G + 1) + g) * kSyncStride, 0);
         step_seq_arrive(args, b, pos, route == 1);
     }
+}
+
+template <int PH, int N, int LM, bool IOB, int RS>
+__global__ __launch_bounds__((StepShape<PH / RS, N>::NTS + 64 * step_ring_waves<LM, IOB>()))
+__attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void step_kernel(StepArgs args) {
+    const int ncomp = args.B * args.H * RS;   // compute workgroups; one writer per sequence follows
+    if ((int)blockIdx.x >= ncomp) {
+        step_token_writer<PH, N, IOB, true>(args, (int)blockIdx.x - ncomp, threadIdx.x, blockDim.x);
+        return;
+    }
+    step_body<PH, N, LM, IOB, RS>(args, blockIdx.x, ncomp);
+}
+
+// The same step for n layers of one shape in one launch: the compute
+// workgroups of layer 0, 1, ..., n-1, then the writer workgroups of every
+// layer (B per layer).  The layers are independent; each keeps its own
+// counters and pointers.
+template <int PH, int N, int LM, bool IOB, int RS>
+__global__ __launch_bounds__((StepShape<PH / RS, N>::NTS + 64 * step_ring_waves<LM, IOB>()))
+__attribute__((amdgpu_waves_per_eu(step_waves<PH / RS, N, LM, IOB>()))) void step_layers_kernel(StepLayersArgs la) {
+    const int B = la.l[0].B;
+    const int ncomp = B * la.l[0].H * RS;
+    const int bid = blockIdx.x, n = la.n;
+    if (bid >= n * ncomp) {
+        const int w = bid - n * ncomp;
+        const int layer = w / B;
+        step_token_writer<PH, N, IOB, true>(la.l[layer], w - layer * B, threadIdx.x, blockDim.x);
+        return;
+    }
+    const int layer = bid / ncomp;
+    step_body<PH, N, LM, IOB, RS>(la.l[layer], bid - layer * ncomp, ncomp);
+}
+
+template <int P, int N, int LM>
+static hipError_t launch_layers_lm(const StepLayersArgs &a, hipStream_t s) {
+    const StepArgs &a0 = a.l[0];
+    if (a0.io_bf16) {
+        constexpr int RS = step_row_splits<P, true>();
+        const unsigned blocks = (unsigned)(((size_t)a0.B * a0.H * RS + a0.B) * a.n);
+        step_layers_kernel<P, N, LM, true, RS>
+            <<<blocks, StepShape<P / RS, N>::NTS + 64 * step_ring_waves<LM, true>(), 0, s>>>(a);
+    } else {
+        const unsigned blocks = (unsigned)(((size_t)a0.B * a0.H + a0.B) * a.n);
+        step_layers_kernel<P, N, LM, false, 1>
+            <<<blocks, StepShape<P, N>::NTS + 64 * step_ring_waves<LM, false>(), 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+int step_workgroups_per_layer(int P, const StepArgs &a) {
+    return a.B * a.H * (a.io_bf16 ? (P == 128 ? step_row_splits<128, true>() : 1) : 1);
+}
+
+hipError_t launch_step_layers(int P, int N, const StepLayersArgs &a, hipStream_t s) {
+    const bool small = a.l[0].L <= 16;
+    if (P == 16 && N == 16) return small ? launch_layers_lm<16, 16, 16>(a, s) : launch_layers_lm<16, 16, kMaxRing>(a, s);
+    if (P == 64 && N == 64) return small ? launch_layers_lm<64, 64, 16>(a, s) : launch_layers_lm<64, 64, kMaxRing>(a, s);
+    if (P == 64 && N == 128) return small ? launch_layers_lm<64, 128, 16>(a, s) : launch_layers_lm<64, 128, kMaxRing>(a, s);
+    if (P == 128 && N == 128)
+        return small ? launch_layers_lm<128, 128, 16>(a, s) : launch_layers_lm<128, 128, kMaxRing>(a, s);
+    return hipErrorInvalidValue;
 }
 
 template <int P, int N, int LM>
