@@ -42,24 +42,34 @@ POOL_STEPS = 32   # distinct pre-generated input steps, cycled (values do not ch
 # algorithmic byte model (bytes the method must move; cache re-reads and
 # group-shared k/q counted once per group)
 def state_bytes(w, st_bytes=4):
-    return w.batch * w.heads * w.head_dim * w.state_dim * st_bytes
+    return int(w.batch * w.heads * w.head_dim * w.state_dim * st_bytes)
+
+
+def scale_bytes(w, st_bytes):
+    """Scales of a copy: e4m3 one float per head, MX FP4 one byte per 32 values."""
+    if st_bytes == 1:
+        return w.batch * w.heads * 4
+    if st_bytes == 0.5:
+        return w.batch * w.heads * w.head_dim * w.state_dim // 32
+    return 0
 
 
 def decode_bytes(w, count, W=1, st_bytes=4, io=2):
     """One decode/verify launch with `count` live entries per sequence."""
     B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
     per_entry = H * P * io + H * 8 + G * N * io          # v, (dt, a), k
-    scale = H * 4 if st_bytes == 1 else 0
-    return (state_bytes(w, st_bytes) + scale
+    return (state_bytes(w, st_bytes) + scale_bytes(w, st_bytes)
             + B * (count * per_entry + W * G * N * io + W * H * P * 4))   # + q + y
 
 
 def flush_bytes(w, count, copy_bytes=0, io=2):
+    """Fold of `count` entries: the master read and written, the copy (and its
+    scales) written; copy_bytes = bytes per value of the copy (0: none)."""
     B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
     per_entry = H * P * io + H * 8 + G * N * io
     s = state_bytes(w)
-    return 2 * s + B * count * per_entry + (state_bytes(w, copy_bytes) if copy_bytes else 0) \
-        + (B * H * 4 if copy_bytes == 1 else 0)
+    return 2 * s + B * count * per_entry + (state_bytes(w, copy_bytes) + scale_bytes(w, copy_bytes)
+                                            if copy_bytes else 0)
 
 
 def step_bytes(w, count, fold, io=2):
@@ -69,6 +79,16 @@ def step_bytes(w, count, fold, io=2):
     per_entry = H * P * io + H * 8 + G * N * io
     token = H * P * io + H * 8 + 2 * G * N * io          # v, (dt, a), q, k of the new token
     return (state_bytes(w) * (2 if fold else 1)
+            + B * ((count - 1) * per_entry + 2 * token + H * P * 4))
+
+
+def step_copy_bytes(w, count, st_bytes, io=2):
+    """One copy-mode step launch (append + output-only decode from a copy of
+    st_bytes bytes per value); `count` includes this step's token."""
+    B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
+    per_entry = H * P * io + H * 8 + G * N * io
+    token = H * P * io + H * 8 + 2 * G * N * io
+    return (state_bytes(w, st_bytes) + scale_bytes(w, st_bytes)
             + B * ((count - 1) * per_entry + 2 * token + H * P * 4))
 
 
@@ -186,6 +206,11 @@ STEP_SOURCES = ["linear_attention_decode_amd/csrc/step.hip",
                 "linear_attention_decode_amd/csrc/step_common.h",
                 "linear_attention_decode_amd/csrc/ring_mx.h",
                 "linear_attention_decode_amd/csrc/device_common.h"]
+STEP_COPY_SOURCES = ["linear_attention_decode_amd/csrc/step_copy.hip",
+                     "linear_attention_decode_amd/csrc/step_common.h",
+                     "linear_attention_decode_amd/csrc/decode_impl.h",
+                     "linear_attention_decode_amd/csrc/ring_mx.h",
+                     "linear_attention_decode_amd/csrc/device_common.h"]
 VERIFY_STEP_SOURCES = ["linear_attention_decode_amd/csrc/verify_step.hip",
                        "linear_attention_decode_amd/csrc/wide_mx.h",
                        "linear_attention_decode_amd/csrc/step_common.h",
@@ -255,8 +280,9 @@ def bench_decode(args):
 
     w = synth.named("decode")
     B, H, G, P, N, L = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len
-    rc = {"f32": None, "bf16": "bf16", "fp8": "fp8"}[args.read]
-    st_bytes = {"f32": 4, "bf16": 2, "fp8": 1}[args.read]
+    rc = {"f32": None, "bf16": "bf16", "fp8": "fp8", "fp4": "fp4"}[args.read]
+    st_bytes = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 0.5}[args.read]
+    copy_step = args.api == "step" and rc is not None   # the copy-mode step (+ the flush kernel on folds)
     pool = input_pool(w, POOL_STEPS)
     layer = lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16", read_copy=rc)
     y = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
@@ -330,10 +356,17 @@ def bench_decode(args):
     word, _ = layer.get_error()
     assert word == 0, f"device error bits {word}"
     counts = list(range(1, L + 1))
+    if copy_step:
+        # launches of the copy-mode step; the fold step's bracket holds the flush kernel too
+        def launch_bytes(c, fold):
+            return step_copy_bytes(w, c, st_bytes) + (flush_bytes(w, c, st_bytes) if fold else 0)
+    else:
+        def launch_bytes(c, fold):
+            return step_bytes(w, c, fold)
     if args.api == "step":
         # the dominant kernel is the fused step kernel itself
         pass_s = p0.elapsed_time(p1) / 1e3
-        kernel_bytes = reps * sum(step_bytes(w, c, c >= L) for c in counts)
+        kernel_bytes = reps * sum(launch_bytes(c, c >= L) for c in counts)
         kernel_time = pass_s
         n_launch = reps * L
         avg_us = 1e6 * pass_s / n_launch
@@ -341,15 +374,17 @@ def bench_decode(args):
         folds = [c >= L for c in counts]
         dec_ms = [m for m, f in zip(step_ms, folds) if not f]
         fl_ms = [m for m, f in zip(step_ms, folds) if f]
-        kernel_name = "step (append + output-only decode, or append + fold on full rings)"
+        kernel_name = ("copy-mode step (append + output-only decode from the copy; the flush kernel after it "
+                       "on full rings)" if copy_step else
+                       "step (append + output-only decode, or append + fold on full rings)")
         by_route = {}
         for route, sel in (("output_only", False), ("fold", True)):
-            b_r = sum(step_bytes(w, c, f) for c, f in zip(counts, folds) if f == sel)
+            b_r = sum(launch_bytes(c, f) for c, f in zip(counts, folds) if f == sel)
             t_r = sum(m for m, f in zip(step_ms, folds) if f == sel) / 1e3
             by_route[route] = {"achieved": b_r / t_r / 1e9, "frac": b_r / t_r / 1e9 / HBM_PEAK_GBS,
                                "launches": sum(1 for f in folds if f == sel),
                                "avg_launch_us": 1e6 * t_r / sum(1 for f in folds if f == sel)}
-        region_bytes = sum(step_bytes(w, c, c >= L) for c in timed_counts)
+        region_bytes = sum(launch_bytes(c, c >= L) for c in timed_counts)
     else:
         dec_ms = [e[0].elapsed_time(e[1]) for e in route_evs]
         fl_ms = [route_evs[L - 1][2].elapsed_time(route_evs[L - 1][3])]
@@ -372,7 +407,9 @@ def bench_decode(args):
         + flush_bytes(w, L, 0 if st_bytes == 4 else st_bytes) \
         + B * L * 2 * (H * P * 2 + H * 8 + 2 * G * N * 2)            # appends: read input + write ring
     window_eager = L * eager_bytes(w)
-    if args.api == "step":
+    if copy_step:
+        traffic = _counter_traffic(STEP_COPY_SOURCES, f"step_copy_kernel_{args.read}_b256_h128_counters.txt")
+    elif args.api == "step":
         traffic = _counter_traffic(STEP_SOURCES, "step_kernel_f32_b256_h128_counters.txt")
     else:
         traffic = _counter_traffic(DECODE_SOURCES, f"decode_kernel_{args.read}_b256_h128_counters.txt")
@@ -810,8 +847,8 @@ def main():
                     help="step: one fused launch per decode step (replay_step) or verify round "
                          "(replay_verify_step); calls: the append, decode/verify and flush kernels; "
                          "layers (stacked): one launch steps all layers (replay_step_layers)")
-    ap.add_argument("--read", default="f32", choices=["f32", "bf16", "fp8"],
-                    help="checkpoint the outputs read: the float32 master or a bf16 / e4m3 copy")
+    ap.add_argument("--read", default="f32", choices=["f32", "bf16", "fp8", "fp4"],
+                    help="checkpoint the outputs read: the float32 master or a bf16 / e4m3 / MX FP4 copy")
     ap.add_argument("--event-stride", type=int, default=0,
                     help="verify: bracket every n-th round's launch with HIP events (default 4)")
     ap.add_argument("--roofline-windows", type=int, default=4,
