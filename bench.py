@@ -116,6 +116,21 @@ def flop_model(P, N):
             "ratio": P * N / (P + N), "ratio_at_128x128": 128 * 128 / 256}
 
 
+def verify_step_copy_bytes(w, before, W, st_bytes, io=2):
+    """One fused verify-round launch with a low-precision read copy: a
+    sequence without a fold reads the copy (and its scales); one that folds
+    reads and writes the float32 master and writes the copy (and scales).
+    Ring entries, drafts and outputs as for verify_step_bytes."""
+    B, H, G, P, N, L = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len
+    per_entry = H * P * io + H * 8 + G * N * io
+    token = H * P * io + H * 8 + 2 * G * N * io
+    folds = int(np.sum(before >= L - W + 1))
+    copy_seq = (state_bytes(w, st_bytes) + scale_bytes(w, st_bytes)) / B
+    fold_seq = 2 * state_bytes(w) / B + copy_seq
+    return (folds * fold_seq + (B - folds) * copy_seq
+            + float(np.sum(before)) * per_entry + B * (2 * W * token + W * H * P * 4))
+
+
 def eager_bytes(w, io=2):
     B, H, G, P, N = w.batch, w.heads, w.groups, w.head_dim, w.state_dim
     return 2 * state_bytes(w) + B * (H * P * io + H * 8 + 2 * G * N * io + H * P * 4)
@@ -483,7 +498,9 @@ def bench_verify(args):
     accept = torch.from_numpy(acc_np).cuda()
     nrej = (W - accept).to(torch.int32).contiguous()
     win = {k: v.view((R + WU), W, *v.shape[1:]).transpose(1, 2).contiguous() for k, v in toks.items()}
-    layer = lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16")
+    rc = {"f32": None, "bf16": "bf16", "fp8": "fp8", "fp4": "fp4"}[args.read]
+    st_bytes = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 0.5}[args.read]
+    layer = lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16", read_copy=rc)
     y = torch.empty((B, W, H, P), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -523,11 +540,14 @@ def bench_verify(args):
     ver_ms = [evs[k][0].elapsed_time(evs[k][1]) for k in sampled]
     # ring counts at the start of every round and at verify time (host side)
     before, at_verify = _verify_counts(B, L, W, acc_np)
-    if api == "step":
+    if api == "step" and rc is not None:
+        vbytes = sum(verify_step_copy_bytes(w, before[WU + k], W, st_bytes) for k in sampled)
+        kernel_name = f"verify round, {args.read} read copy (fold + copy rewrite if due, append, verify; W={W})"
+    elif api == "step":
         vbytes = sum(verify_step_bytes(w, before[WU + k], W) for k in sampled)
         kernel_name = f"verify round (fold if due + append + verify, W={W})"
     else:
-        vbytes = sum(float(np.mean([decode_bytes(w, c, W) / B for c in at_verify[WU + k]])) * B
+        vbytes = sum(float(np.mean([decode_bytes(w, c, W, st_bytes) / B for c in at_verify[WU + k]])) * B
                      for k in sampled)
         kernel_name = f"verify (W={W}{', matrix cores' if W >= 6 else ''})"
     achieved = vbytes / (sum(ver_ms) / 1e3) / 1e9
@@ -567,12 +587,13 @@ def bench_verify(args):
         "ms_per_step": 1e3 * el / R, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": f"synthetic (seeded), accepted drafts ~ Uniform{{0..{W}}}",
         "config": {"workload": "speculative verify, one SSM layer", "batch": B, "heads": H, "groups": G,
-                   "head_dim": P, "state_dim": N, "ring_len": L, "window": W, "rounds": R, "api": api},
+                   "head_dim": P, "state_dim": N, "ring_len": L, "window": W, "rounds": R, "api": api,
+                   "read_copy": args.read},
         "accepted_tokens_per_s": acc_total / el,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (_counter_traffic(VERIFY_STEP_SOURCES, "verify_step_kernel_b256_h64_w5_counters.txt")
-                                 if api == "step" and W == 5 else
+                                 if api == "step" and W == 5 and rc is None else
                                  _counter_traffic(VERIFY_WIDE_SOURCES, "verify_wide_kernel_b256_h64_w16_counters.txt")
                                  if W == 16 else None),
                      "kernel": kernel_name,

@@ -281,8 +281,14 @@ replay_status replay_step_static(replay_handle *h, const void *q, const void *k,
    [B][W][H] f32; y: [B][W][H][P] f32, draft w at [b][w].  1 <= W <= min(16, L)
    (windows past 8 as for replay_verify, through the kernels in turn).
    With a float32 checkpoint read, bf16 io, L <= 16 and W <= 8 it is one kernel
-   launch that reads each checkpoint once and writes it only where it folds;
-   otherwise it runs the flush, append and verify kernels in turn.  A
+   launch that reads each checkpoint once and writes it only where it folds.
+   With an e4m3 or FP4 read copy (separated precisions), bf16 io, L <= 16,
+   2 <= W <= 5 and (P, N) in {(16,16), (64,64), (64,128)} it is one launch
+   too: a sequence that does not fold is scored from the copy, one that folds
+   reads the master, writes the new master and copy (and scales) and is
+   scored from the new codes (abstract page: output-only verification with a
+   low-precision checkpoint serving the outputs).  Otherwise it runs the
+   flush, append and verify kernels in turn.  A
    sequence whose drafts do not fit after the fold (count + W > L with
    count < flush_at) or whose pointer would pass 2^31 - 1 gets RING_OVERFLOW
    or POS_OVERFLOW, is left unchanged and its y is NaN (in the single-launch

@@ -498,6 +498,16 @@ replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, con
     hipStream_t s = as_stream(stream);
     note_capture(h, s);
     const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, W, h->bufs.sync);
+    if (c.read_copy != REPLAY_NONE && !c.shared_lowp && verify_step_copy_fused(c.head_dim, c.state_dim, sa)) {
+        // an e4m3 or FP4 read copy: fold, copy rewrite, append and verify in one launch
+        const hipError_t e = launch_verify_step_copy(c.head_dim, c.state_dim, sa, s);
+        if (e != hipSuccess) {
+            h->bound.unknown();
+            return REPLAY_ERR_HIP;
+        }
+        h->bound.verify_round(flush_at, W);
+        return REPLAY_OK;
+    }
     if (c.read_copy != REPLAY_NONE || !verify_step_fused(c.head_dim, c.state_dim, sa)) {
         // the flush, append and verify kernels in turn
         replay_status st = run_flush(h, nullptr, flush_at, s, h->bufs.sync);

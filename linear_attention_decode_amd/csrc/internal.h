@@ -126,6 +126,8 @@ constexpr int kLayersOneLaunchMax = 8192;
 hipError_t launch_verify_step(int P, int N, const StepArgs &a, hipStream_t s);
 hipError_t launch_step_copy(int P, int N, const StepArgs &a, hipStream_t s);   // append + decode from the copy
 bool verify_step_fused(int P, int N, const StepArgs &a);   // the fused round covers this case
+hipError_t launch_verify_step_copy(int P, int N, const StepArgs &a, hipStream_t s);   // the round with an e4m3 / FP4 read
+bool verify_step_copy_fused(int P, int N, const StepArgs &a);
 hipError_t launch_eager_select(const float *snaps, int32_t W, const int32_t *n_accept, float *s,
                                int32_t B, size_t head_elems_per_seq, hipStream_t st);
 hipError_t launch_probe(int mode, const void *src, void *dst, size_t bytes, hipStream_t s);

@@ -34,6 +34,7 @@
 // returned.  The pointer moves when the sequence's last group arrives.
 #include "step_common.h"
 #include "wide_mx.h"
+#include "decode_impl.h"
 
 namespace replay {
 
@@ -545,6 +546,347 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// The same round when the outputs read a low-precision copy (e4m3 or MX FP4)
+// of the float32 master (separated precisions; page "ReplaySSM: Cache SSM
+// Inputs, Not State", Abstract: output-only verification with a
+// low-precision checkpoint serving the outputs, the higher-precision one
+// taking the updates).  Equivalent to replay_flush(flush_at) (fold into the
+// master, rewrite the copy), replay_append(W), replay_verify(W) from the
+// copy, bit for bit:
+//   - a round without a fold scores the drafts from the copy with the
+//     register verify kernel's tiling and sums (decode_impl.h: bf16-pair
+//     dot products of the codes, the e4m3 head scale or the FP4 block scales
+//     applied as there);
+//   - a folding head reads the master instead, folds it as the flush kernel
+//     does (same tiling and order), writes the master and the new copy with
+//     the flush kernel's quantisers (e4m3: one scale per head = amax / 448;
+//     FP4: E8M0 scale per 32 values), stages the new codes in LDS and scores
+//     the drafts from them with the same tiling and sums as the verify kernel
+//     reading that copy.
+// The ring wavefronts are the float32 round's (term, fold).  Four barriers:
+// route; ring terms and fold staging; the e4m3 head maximum; the staged codes.
+template <int P, int N, int ST>
+struct VsCopyShape {
+    using C = DecodeShape<P, N, ST, 2>;   // the verify kernel's copy tiling (any window past 1)
+    using M = StepShape<P, N>;            // the fold's master tiling (the flush kernel's)
+    static constexpr int NTS = M::NTS;
+    static constexpr bool OK = (int)C::NTS == (int)M::NTS;
+    static constexpr int CODE_BYTES = ST == ST_FP4 ? P * N / 2 : P * N;
+};
+
+template <int P, int N, int ST, int W>
+__global__ __launch_bounds__((VsCopyShape<P, N, ST>::NTS + 128))
+__attribute__((amdgpu_waves_per_eu(8))) void verify_step_copy_kernel(StepArgs args) {
+    using VS = VsCopyShape<P, N, ST>;
+    using SC = DecodeShape<P, N, ST, W>;
+    using SM = typename VS::M;
+    static_assert(VS::OK && (int)SC::NTS == VS::NTS, "copy and master tilings need the same streaming threads");
+    constexpr int NTS = VS::NTS;
+    constexpr int CVEC = SC::VEC, CITER = SC::ITER, CLPR = SC::LPR, CRPI = SC::RPI;
+    constexpr int MVEC = SM::VEC, MITER = SM::ITER, MLPR = SM::LPR, MRPI = SM::RPI;
+    constexpr int LM = kVsRing;
+    using RR = RowReduce<CITER, CLPR>;
+    using Ch = Chunk<ST, CVEC>;
+
+    __shared__ float s_r[W][P];
+    __shared__ float s_abar[W];
+    __shared__ __align__(16) float s_sw[W][LM];
+    __shared__ float s_U[P][LM + 1];
+    __shared__ __align__(16) float s_K[LM][N];
+    __shared__ __align__(16) uint8_t s_code[VS::CODE_BYTES];          // a folded head's new codes
+    __shared__ uint8_t s_scl[ST == ST_FP4 ? P * N / 32 : 4];          // and its FP4 block scales
+    __shared__ float s_red[NTS / 64];
+    __shared__ __align__(16) uint32_t s_qw[W * N / 2];                // the drafts' query rows, bf16 pairs
+    __shared__ float s_fabar;
+    __shared__ int s_route;   // 0 keep the ring, 1 fold first, 2 error (sequence left unchanged)
+    __shared__ int s_fcount;
+
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int H = args.H, G = args.G, L = args.L;
+    const int b = __builtin_amdgcn_readfirstlane(lid / H), h = __builtin_amdgcn_readfirstlane(lid % H);
+    const int g = (h * G) / H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool streamer = wave < NTS / 64;
+    const int rw = wave - NTS / 64;
+    const size_t bh = (size_t)b * H + h;
+    const size_t tile = bh * (size_t)(P * N);
+
+    if (streamer) {
+        // the drafts' query rows (bf16 pairs) into LDS, published by the first
+        // barrier; they are loaded before the copy tile (loads complete in
+        // order, so the wait before the LDS write does not wait for the tile)
+        constexpr int QW = CVEC / 2;
+        constexpr int QROW = N / 2, QALL = W * QROW, QI = (QALL + NTS - 1) / NTS;
+        const int ccol0 = (tid % CLPR) * CVEC;
+        uint32_t qword[QI];
+#pragma unroll
+        for (int i = 0; i < QI; ++i) {
+            const int k = tid + i * NTS < QALL ? tid + i * NTS : QALL - 1;
+            qword[i] = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(args.q) +
+                                                          (((size_t)b * W + k / QROW) * G + g) * N)[k % QROW];
+        }
+        asm volatile("" ::: "memory");
+        Ch cc[CITER];
+#pragma unroll
+        for (int i = 0; i < CITER; ++i) {
+            if constexpr (ST == ST_FP4)
+                cc[i].load_mx(args.copy, args.copy_scale, tile + (size_t)(i * NTS + tid) * CVEC);
+            else
+                cc[i].load(args.copy, tile + (size_t)(i * NTS + tid) * CVEC);
+        }
+#pragma unroll
+        for (int i = 0; i < QI; ++i)
+            if (tid + i * NTS < QALL) s_qw[tid + i * NTS] = qword[i];
+        float part[CITER][W];
+        // each partial sum as the verify kernel forms it (one draft's words at a time here)
+        auto sums = [&]() {
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                uint32_t qw[QW];
+#pragma unroll
+                for (int e = 0; e < QW; ++e) qw[e] = s_qw[w * QROW + ccol0 / 2 + e];
+#pragma unroll
+                for (int i = 0; i < CITER; ++i) {
+                    float acc = cc[i].dot_bf16(qw);
+                    if constexpr (ST == ST_FP4) acc = ldexpf(acc, cc[i].se);   // the block's scale, exact
+                    part[i][w] = acc;
+                }
+            }
+            RR::template run<W>(part, lane);
+        };
+        // y_w = abar_w (scale * sums) + ring term, as the verify kernel writes it
+        auto emit = [&](float sc) {
+            if (RR::writer(lane)) {
+                const int hi = RR::halving_index(lane);
+#pragma unroll
+                for (int e = 0; e < RR::FINAL; ++e) {
+                    const int row = (e + RR::FINAL * hi) * CRPI + tid / CLPR;
+#pragma unroll
+                    for (int w = 0; w < W; ++w)
+                        args.y[(((size_t)b * W + w) * H + h) * P + row] = s_abar[w] * (sc * part[e][w]) + s_r[w][row];
+                }
+            }
+        };
+        lds_barrier();   // 1: the route, the queries
+        const int route = s_route;
+        // a folding head reads the master as soon as the route is known (its
+        // loads fly while the ring wavefronts stage the fold)
+        f32x4 x[MITER];   // the master chunks, folded in place
+        if (route == 0) {
+            sums();
+        } else if (route == 1) {
+#pragma unroll
+            for (int i = 0; i < MITER; ++i)
+                x[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(args.S + tile + (size_t)(i * NTS + tid) * MVEC));
+        }
+        lds_barrier();   // 2: the ring terms and the fold's staging
+        // a round without a fold is finished here (its sums need not live on)
+        if (route == 0) emit(ST == ST_FP8 ? static_cast<const float *>(args.copy_scale)[bh] : 1.0f);
+        float sc = 1.0f;   // e4m3: the new head scale
+        const int mcol0 = (tid % MLPR) * MVEC;
+        if (route == 1) {
+            // fold the master as the flush kernel does: x = abar_c S0, then the
+            // entries' products one after another
+            const float abar = s_fabar;
+#pragma unroll
+            for (int i = 0; i < MITER; ++i)
+#pragma unroll
+                for (int e = 0; e < MVEC; ++e) x[i][e] *= abar;
+            const int c = s_fcount;
+#pragma unroll 1
+            for (int j = 0; j < c; ++j) {
+                const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_K[j][mcol0]);
+#pragma unroll
+                for (int i = 0; i < MITER; ++i) {
+                    const float u = s_U[i * MRPI + tid / MLPR][j];
+                    x[i][0] = fmaf(u, kk.x, x[i][0]);
+                    x[i][1] = fmaf(u, kk.y, x[i][1]);
+                    x[i][2] = fmaf(u, kk.z, x[i][2]);
+                    x[i][3] = fmaf(u, kk.w, x[i][3]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < MITER; ++i)
+                __builtin_nontemporal_store(x[i], reinterpret_cast<f32x4 *>(args.S + tile + (size_t)(i * NTS + tid) * MVEC));
+            if constexpr (ST == ST_FP8) {
+                float amax = 0.f;
+#pragma unroll
+                for (int i = 0; i < MITER; ++i)
+#pragma unroll
+                    for (int e = 0; e < MVEC; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+#pragma unroll
+                for (int bit = 5; bit >= 0; --bit) amax = fmaxf(amax, lane_partner(amax, bit));
+                if (lane == 0) s_red[wave] = amax;
+            }
+        }
+        lds_barrier();   // 3: the head's maximum (e4m3)
+        if (route == 1) {
+            // the new copy, written to memory and staged in LDS
+            if constexpr (ST == ST_FP8) {
+                float amax = s_red[0];
+#pragma unroll
+                for (int i = 1; i < NTS / 64; ++i) amax = fmaxf(amax, s_red[i]);
+                const float sig = amax > 0.f ? amax / 448.0f : 1.0f;   // correctly rounded divide
+                uint8_t *cp = static_cast<uint8_t *>(const_cast<void *>(args.copy)) + tile;
+#pragma unroll
+                for (int i = 0; i < MITER; ++i) {
+                    const uint32_t o = f32x4_to_fp8(x[i][0] / sig, x[i][1] / sig, x[i][2] / sig, x[i][3] / sig);
+                    const size_t e0 = (size_t)(i * NTS + tid) * MVEC;
+                    __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(cp + e0));
+                    *reinterpret_cast<uint32_t *>(&s_code[e0]) = o;
+                }
+                if (tid == 0) static_cast<float *>(const_cast<void *>(args.copy_scale))[bh] = sig;
+                sc = sig;
+            } else {
+                uint8_t *cp = static_cast<uint8_t *>(const_cast<void *>(args.copy));
+                uint8_t *scl = static_cast<uint8_t *>(const_cast<void *>(args.copy_scale));
+#pragma unroll
+                for (int i = 0; i < MITER; ++i) {
+                    float amax = fmaxf(fmaxf(fabsf(x[i][0]), fabsf(x[i][1])), fmaxf(fabsf(x[i][2]), fabsf(x[i][3])));
+#pragma unroll
+                    for (int bit = 2; bit >= 0; --bit) amax = fmaxf(amax, lane_partner(amax, bit));
+                    int se = -127;
+                    if (amax > 0.f) {
+                        int ex;
+                        (void)frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1)
+                        se = ex - 3 < -127 ? -127 : (ex - 3 > 127 ? 127 : ex - 3);
+                    }
+                    const uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[i][0], -se),
+                                                                                 ldexpf(x[i][1], -se), 1.0f, 0);
+                    const uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[i][2], -se),
+                                                                                 ldexpf(x[i][3], -se), 1.0f, 0);
+                    const size_t e0 = (size_t)(i * NTS + tid) * MVEC;   // within the head's tile
+                    const uint16_t code = (uint16_t)((lo & 0xffu) | ((hi & 0xffu) << 8));
+                    *reinterpret_cast<uint16_t *>(cp + (tile + e0) / 2) = code;
+                    *reinterpret_cast<uint16_t *>(&s_code[e0 / 2]) = code;
+                    if ((tid & 7) == 0) {
+                        scl[(tile + e0) / 32] = (uint8_t)(se + 127);
+                        s_scl[e0 / 32] = (uint8_t)(se + 127);
+                    }
+                }
+            }
+        }
+        lds_barrier();   // 4: the staged codes
+        if (route == 2) {
+            for (int i = tid; i < W * P; i += NTS)
+                args.y[(((size_t)b * W + i / P) * H + h) * P + i % P] = __builtin_nanf("");
+            return;
+        }
+        if (route == 1) {
+            // the new codes in the copy tiling, as the verify kernel reads them
+#pragma unroll
+            for (int i = 0; i < CITER; ++i) {
+                const size_t e = (size_t)(i * NTS + tid) * CVEC;   // within the head's tile
+                if constexpr (ST == ST_FP4) {
+                    static_assert(CVEC == 8 || CVEC == 4, "FP4 chunks of 4 or 2 bytes");
+                    if constexpr (CVEC == 8)
+                        cc[i].raw[0] = *reinterpret_cast<const uint32_t *>(&s_code[e / 2]);
+                    else
+                        cc[i].raw[0] = *reinterpret_cast<const uint16_t *>(&s_code[e / 2]);
+                    cc[i].se = (int)s_scl[e / 32] - 127;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < CVEC / 4; ++k) cc[i].raw[k] = *reinterpret_cast<const uint32_t *>(&s_code[e + 4 * k]);
+                }
+            }
+            sums();
+            emit(sc);
+        }
+    } else {
+        const int base = args.base[b];
+        const int pos = args.pos[b];
+        const int cold = pos - base;
+        const int need = args.flush_at > 1 ? args.flush_at : 1;
+        const bool fold = cold >= need;
+        const int keep = fold ? 0 : cold;
+        const int err = keep + W > L ? REPLAY_SEQERR_RING_OVERFLOW
+                                     : ((long long)pos + W > 2147483647LL ? REPLAY_SEQERR_POS_OVERFLOW : 0);
+        if (rw == 0 && lane == 0) {
+            s_route = err ? 2 : (fold ? 1 : 0);
+            s_fcount = fold ? cold : 0;
+            if (err) raise_seq_error(args.err, b, err);
+        }
+        int prev = -1;
+        if (err) {
+            lds_barrier();   // 1
+        } else {
+            if (rw == 0)
+                prev = vs_term_wave<P, N, W>(args, lane, b, g, h, bh, base, keep, s_r, s_abar, s_sw);
+            else
+                prev = vs_fold_wave<P, N, W>(args, lane, b, g, h, bh, base, pos, cold, fold, &s_fabar, s_U, s_K);
+        }
+        lds_barrier();   // 2
+        lds_barrier();   // 3
+        lds_barrier();   // 4
+        if (__shfl(prev, 0) == 2 * (H / G) - 1) {
+            // last ring wavefront of the group: the drafts' q/k rows, then the
+            // group arrives at the sequence's counter (as in the float32 round)
+            const size_t gring = ((size_t)b * G + g) * L;
+            const int pmod = pos % L;
+            constexpr int RW = RowWords<N, true>::WORDS;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                RowWords<N, true> qrow, krow;
+                const size_t in = (((size_t)b * W + w) * G + g) * N * 2;
+                qrow.load(static_cast<const char *>(args.q) + in, lane);
+                krow.load(static_cast<const char *>(args.k) + in, lane);
+                const size_t off = (gring + ring_slot(pmod, w, L)) * (size_t)RW * 4;
+                qrow.store(static_cast<char *>(args.ring_q) + off, lane);
+                krow.store(static_cast<char *>(args.ring_k) + off, lane);
+            }
+            if (lane == 0) {
+                int32_t *seq = args.sync + (size_t)b * (G + 1) * kSyncStride;
+                atomicExch(seq + (size_t)g * kSyncStride, 0);
+                if (atomicAdd(seq + (size_t)G * kSyncStride, 1) == G - 1) {
+                    atomicExch(seq + (size_t)G * kSyncStride, 0);
+                    if (fold) args.base[b] = pos;
+                    args.pos[b] = pos + W;
+                }
+            }
+        }
+    }
+}
+
+template <int P, int N, int ST, int W>
+static hipError_t launch_vsc(const StepArgs &a, hipStream_t s) {
+    if constexpr (VsCopyShape<P, N, ST>::OK) {
+        const unsigned blocks = (unsigned)((size_t)a.B * a.H);
+        verify_step_copy_kernel<P, N, ST, W><<<blocks, VsCopyShape<P, N, ST>::NTS + 128, 0, s>>>(a);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int P, int N, int ST>
+static hipError_t launch_vsc_w(const StepArgs &a, hipStream_t s) {
+    switch (a.W) {
+        case 2: return launch_vsc<P, N, ST, 2>(a, s);
+        case 3: return launch_vsc<P, N, ST, 3>(a, s);
+        case 4: return launch_vsc<P, N, ST, 4>(a, s);
+        case 5: return launch_vsc<P, N, ST, 5>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool verify_step_copy_fused(int P, int N, const StepArgs &a) {
+    const bool shape = (P == 16 && N == 16) || (P == 64 && N == 64) || (P == 64 && N == 128);
+    const bool copy = a.copy_st == ST_FP8 || a.copy_st == ST_FP4;
+    // windows of 2 to 5 (a window of 1 is the several-head decode kernel's
+    // tiling; from kWideFrom the e4m3 verify runs on the matrix cores)
+    return shape && copy && a.S && a.io_bf16 && a.L <= kVsRing && a.W >= 2 && a.W < kWideFrom && a.W <= a.L;
+}
+
+hipError_t launch_verify_step_copy(int P, int N, const StepArgs &a, hipStream_t s) {
+    if (!verify_step_copy_fused(P, N, a)) return hipErrorInvalidValue;
+    const bool fp8 = a.copy_st == ST_FP8;
+    if (P == 16 && N == 16) return fp8 ? launch_vsc_w<16, 16, ST_FP8>(a, s) : launch_vsc_w<16, 16, ST_FP4>(a, s);
+    if (P == 64 && N == 64) return fp8 ? launch_vsc_w<64, 64, ST_FP8>(a, s) : launch_vsc_w<64, 64, ST_FP4>(a, s);
+    return fp8 ? launch_vsc_w<64, 128, ST_FP8>(a, s) : launch_vsc_w<64, 128, ST_FP4>(a, s);
 }
 
 template <int P, int N, int W>

@@ -7,8 +7,9 @@
   updates) and shared (the copy is the only checkpoint), against
   - the float64 oracle with the stated tolerances (2e-2 bf16, 6e-2 e4m3,
     read per token over the layer output), and
-  - the oracle's emulation of the same copy (tight; it differs from the
-    GPU only by float32-vs-float64 rounding of the state that is copied).
+  - the oracle's emulation of the same copy (it differs from the GPU only by
+    float32-vs-float64 rounding of the state that is copied: tests/gpu_util.py
+    assert_copy bounds the maximum and the median).
 """
 import numpy as np
 import pytest
@@ -21,7 +22,6 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 TOL_VS_EXACT = {"bf16": 2e-2, "fp8": 6e-2}
-TOL_VS_EMUL = {"bf16": 1e-3, "fp8": 1e-3}
 
 
 def _layer(w, **kw):
@@ -95,7 +95,7 @@ def test_dual_precision_workload(fmt, shared):
     print(f"  vs exact: per-token max {tok:.3e} per-head max {vec:.3e} mean {mean:.3e}; "
           f"vs emulation: per-token max {tok_e:.3e} per-head max {vec_e:.3e}")
     assert tok <= TOL_VS_EXACT[fmt]
-    assert tok_e <= TOL_VS_EMUL[fmt]
+    gu.assert_copy(y_gpu, y_emul, fmt)
     layer.close()
 
 

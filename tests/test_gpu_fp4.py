@@ -23,7 +23,7 @@ from oracle import runs
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
-TOL_VS_EMUL = 1e-3
+TOL_VS_EMUL = gu.COPY_TOL_MAX["fp4"]
 
 
 def _layer(w, **kw):
@@ -72,7 +72,7 @@ def _check(y_gpu, x, S0, L, label):
     e_emul = runs.normwise_rel_err(y_emul.astype(np.float64), y_exact)
     print(f"  {label}: vs emulation per-token max {tok_e:.3e}; vs exact max {e_gpu.max():.3e} "
           f"(the emulation's own {e_emul.max():.3e})")
-    assert tok_e <= TOL_VS_EMUL
+    gu.assert_copy(y_gpu, y_emul, "fp4", label)
     assert np.all(e_gpu <= 1.1 * e_emul + TOL_VS_EMUL)
 
 
@@ -147,6 +147,6 @@ def test_fp4_verify_rounds():
     e_emul = runs.normwise_rel_err(y_emul, y_exact)
     print(f"  verify: vs emulation per-token max {tok_e:.3e}; vs exact max {e_gpu.max():.3e} "
           f"(the emulation's own {e_emul.max():.3e})")
-    assert tok_e <= TOL_VS_EMUL
+    gu.assert_copy(y_gpu, y_emul, "fp4", "verify")
     assert np.all(e_gpu <= 1.1 * e_emul + TOL_VS_EMUL)
     layer.close()

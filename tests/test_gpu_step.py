@@ -105,13 +105,11 @@ def test_step_ragged(P, N, io, L, flush_at, B, H, G, copy):
         # with copies the step runs the separate kernels; with this few heads the
         # per-token error against exact is the format's own, so compare with the
         # oracle's emulation of the same copy
-        y_ref, tol = runs.separated(x, S0, flush_at, copy), {"bf16": 1e-3, "fp8": 1e-3}[copy]
+        y_ref, tol = runs.separated(x, S0, flush_at, copy), None
     if copy is None:
         gu.assert_f32(y.cpu().numpy(), y_ref, gu.y_abs_standard(x, (B, H, P, N)))
     else:
-        tok, vec, _ = gu.errors(y.cpu().numpy(), y_ref)
-        print(f"  per-token max {tok:.3e} per-head max {vec:.3e}")
-        assert tok <= tol
+        gu.assert_copy(y.cpu().numpy(), y_ref, copy)
     layer.close()
 
 

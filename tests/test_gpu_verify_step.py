@@ -47,7 +47,17 @@ def _layer(w, **kw):
     (64, 128, "bf16", 5, 5, 3, 4, 1, None),       # W = L: every round folds
     (64, 128, "f32", 16, 5, 3, 8, 2, None),       # f32 io: the calls in turn
     (64, 128, "bf16", 32, 6, 3, 8, 2, None),      # L > 16: the calls in turn
-    (64, 128, "bf16", 16, 5, 3, 8, 2, "bf16"),    # a read copy: the calls in turn
+    (64, 128, "bf16", 16, 5, 3, 8, 2, "bf16"),    # a bf16 read copy: the calls in turn
+    (64, 128, "bf16", 16, 5, 6, 16, 4, "fp8"),    # e4m3 copy: one launch (fold: master + copy rewrite)
+    (64, 128, "bf16", 16, 5, 6, 16, 4, "fp4"),    # FP4 copy: one launch
+    (64, 128, "bf16", 8, 3, 4, 8, 2, "fp8"),      # folds most rounds
+    (64, 64, "bf16", 12, 4, 3, 4, 2, "fp4"),
+    (64, 64, "bf16", 6, 2, 5, 6, 3, "fp8"),
+    (16, 16, "bf16", 16, 5, 3, 4, 2, "fp4"),      # FP4 chunks of 2 bytes
+    (16, 16, "bf16", 4, 3, 4, 6, 2, "fp8"),
+    (64, 128, "bf16", 5, 5, 3, 4, 1, "fp4"),      # W = L: every round folds
+    (64, 128, "bf16", 16, 7, 3, 8, 2, "fp8"),     # W past 5: the calls in turn
+    (128, 128, "bf16", 16, 4, 2, 4, 2, "fp8"),    # 128 x 128: the calls in turn
 ])
 def test_verify_step_equals_calls(P, N, io, L, W, B, H, G, rc):
     w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype=io,
@@ -68,6 +78,8 @@ def test_verify_step_equals_calls(P, N, io, L, W, B, H, G, rc):
         assert torch.equal(fused.t[name], calls.t[name]), name
     if rc is not None:
         assert torch.equal(fused.t["s_copy"], calls.t["s_copy"])
+        if fused.t["s_scale"] is not None:
+            assert torch.equal(fused.t["s_scale"], calls.t["s_scale"])
     fused.close()
     calls.close()
 
@@ -171,3 +183,27 @@ def test_verify_step_errors():
     assert torch.equal(layer.s_master[[0, 1, 3]], ref.s_master[[0, 1, 3]])
     layer.close()
     ref.close()
+
+
+@pytest.mark.parametrize("copy", ["fp8", "fp4"])
+def test_verify_step_copy_workload(copy):
+    """B=256 H=64 G=8 P=64 N=128 L=16, W=5, accepts ~ U{0..5}, 32 fused rounds
+    with an e4m3 / FP4 read copy (one launch a round): 16 sequences spread
+    over the batch against the oracle's emulation of rounds read from that
+    copy (tests/gpu_util.py assert_copy), ring integers of all 256 after every round."""
+    w = synth.named("verify")
+    R, W = 32, 5
+    gu.note(f"verify_step copy workload {copy}")
+    accept = synth.accept_counts(w, R, W)
+    dev = gu.DevInputsTorch(w, 0, R * W)
+    layer = _layer(w, read_copy=copy)
+    model = oring.RingModel(w.batch, w.ring_len)
+    y = gu.run_verify(layer, w, dev, R, W, accept, model=model, fused=True)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    seqs = list(range(0, w.batch, 16))
+    x = dev.oracle(seqs)
+    S0 = np.zeros((len(seqs), w.heads, w.head_dim, w.state_dim))
+    y_emul = runs.verify_rounds_copy(x, accept[:, seqs], W, S0, w.ring_len, copy)
+    gu.assert_copy(y.cpu().numpy()[:, seqs].transpose(0, 2, 1, 3, 4), y_emul, copy)
+    layer.close()
