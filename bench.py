@@ -645,7 +645,8 @@ def bench_dual(args):
         ys_master = None
         for mode, rc, shared in [("f32", None, False), ("bf16-separated", "bf16", False),
                                  ("fp8-separated", "fp8", False), ("fp4-separated", "fp4", False),
-                                 ("bf16-shared", "bf16", True), ("fp8-shared", "fp8", True)]:
+                                 ("bf16-shared", "bf16", True), ("fp8-shared", "fp8", True),
+                                 ("fp4-shared", "fp4", True)]:
             y = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
             sel = torch.tensor(seqs, device="cuda")
 

@@ -103,7 +103,7 @@ typedef struct {
                              serve the output reads) */
     int32_t shared_lowp;  /* 0: separated precisions (the float32 master takes every flush);
                              1: shared -- the low-precision copy is the only checkpoint and
-                             each flush starts from it (needs read_copy BF16 or FP8_E4M3) */
+                             each flush starts from it (needs a read_copy) */
 } replay_config;
 
 /* Device buffers of one layer's decode state.  Sizes in elements; use

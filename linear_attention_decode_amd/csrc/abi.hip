@@ -97,7 +97,6 @@ replay_status check_config(const replay_config *c) {
         return REPLAY_ERR_UNSUPPORTED;
     if (c->shared_lowp != 0 && c->shared_lowp != 1) return REPLAY_ERR_INVALID_ARG;
     if (c->shared_lowp && c->read_copy == REPLAY_NONE) return REPLAY_ERR_INVALID_ARG;
-    if (c->shared_lowp && c->read_copy == REPLAY_FP4_E2M1) return REPLAY_ERR_UNSUPPORTED;
     return REPLAY_OK;
 }
 
@@ -176,7 +175,7 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
         st_in = ST_F32;
     } else if (c.shared_lowp) {
         a.S_in = h->bufs.s_copy;
-        a.scale_in = static_cast<const float *>(h->bufs.s_scale);
+        a.scale_in = h->bufs.s_scale;
         st_in = state_kind(c.read_copy);
     } else {
         a.S_in = h->bufs.s_master;

@@ -92,7 +92,12 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
         const size_t bh = (size_t)b * r.H + h0 + hl;
         const size_t tile = bh * (size_t)(P * N);
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) hd.ch[i].load(args.S_in, tile + (size_t)(i * NT + tid) * VEC);
+        for (int i = 0; i < ITER; ++i) {
+            if constexpr (SIN == ST_FP4)
+                hd.ch[i].load_mx(args.S_in, args.scale_in, tile + (size_t)(i * NT + tid) * VEC);
+            else
+                hd.ch[i].load(args.S_in, tile + (size_t)(i * NT + tid) * VEC);
+        }
         hd.a = 1.f;
         hd.dt = 0.f;
         if (count > 0) {
@@ -128,7 +133,7 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     for (int hl = 0; hl < HC; ++hl) {
     const size_t bh = (size_t)b * r.H + h0 + hl;
     const size_t tile = bh * (size_t)(P * N);
-    const float sc_in = (SIN == ST_FP8) ? args.scale_in[bh] : 1.0f;
+    const float sc_in = (SIN == ST_FP8) ? static_cast<const float *>(args.scale_in)[bh] : 1.0f;
     if (hl + 1 < HC) issue(hl + 1, nxt);
 
     // 2. segment weights of the c entries
@@ -177,6 +182,10 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {
         cur.ch[i].widen(x[i], sc_in);
+        if constexpr (SIN == ST_FP4) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) x[i][e] = ldexpf(x[i][e], cur.ch[i].se);   // the block's scale, exact
+        }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[i][e] *= abar;
     }
@@ -313,11 +322,13 @@ static hipError_t launch_pn(int st_in, int st_copy, bool wm, const FlushArgs &a,
     if (st_in == ST_F32) {                 // shared mode, loading a float32 checkpoint
         if (st_copy == ST_BF16) return launch_one<P, N, ST_F32, ST_BF16, false>(a, s);
         if (st_copy == ST_FP8) return launch_one<P, N, ST_F32, ST_FP8, false>(a, s);
+        if (st_copy == ST_FP4) return launch_one<P, N, ST_F32, ST_FP4, false>(a, s);
         return hipErrorInvalidValue;
     }
     if (wm) return hipErrorInvalidValue;   // shared mode: the copy is the only checkpoint
     if (st_in == ST_BF16 && st_copy == ST_BF16) return launch_one<P, N, ST_BF16, ST_BF16, false>(a, s);
     if (st_in == ST_FP8 && st_copy == ST_FP8) return launch_one<P, N, ST_FP8, ST_FP8, false>(a, s);
+    if (st_in == ST_FP4 && st_copy == ST_FP4) return launch_one<P, N, ST_FP4, ST_FP4, false>(a, s);
     return hipErrorInvalidValue;
 }
 

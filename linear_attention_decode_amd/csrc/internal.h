@@ -57,7 +57,7 @@ struct DecodeArgs {
 struct FlushArgs {
     RingView r;
     const void *S_in;       // f32 master (separated) or the copy (shared) or a load source
-    const float *scale_in;  // old per-head scale when S_in is an e4m3 copy
+    const void *scale_in;   // old scales when S_in is a copy: float per head (e4m3), E8M0 byte per block (FP4)
     float *S_out;           // f32 master to write, or nullptr
     void *copy_out;         // copy to write, or nullptr
     void *scale_out;        // scales to write: float per head (e4m3), E8M0 byte per block (FP4), or nullptr

@@ -57,6 +57,10 @@ def test_buffer_bytes_match_the_layout(lad):
     b4 = lad.replay_buffer_bytes(c4)
     assert b4["s_master"] == 4 * 8 * 64 * 128 * 4
     assert b4["s_copy"] == 4 * 8 * 64 * 128 // 2 and b4["s_scale"] == 4 * 8 * 64 * 128 // 32
+    c4s = lad.ReplayConfig(4, 8, 2, 64, 128, 16, lad.BF16, lad.FP4_E2M1, 1)   # shared FP4: no master
+    b4s = lad.replay_buffer_bytes(c4s)
+    assert b4s["s_master"] == 0
+    assert b4s["s_copy"] == b4["s_copy"] and b4s["s_scale"] == b4["s_scale"]
 
 
 @pytest.mark.parametrize("fields,status", [
@@ -69,7 +73,7 @@ def test_buffer_bytes_match_the_layout(lad):
     ((2, 4, 1, 64, 128, 16, 2, -1, 0), 2),          # io dtype e4m3
     ((2, 4, 1, 64, 128, 16, 1, 7, 0), 2),           # unknown copy dtype
     ((2, 4, 1, 64, 128, 16, 1, -1, 1), 1),          # shared without a copy
-    ((2, 4, 1, 64, 128, 16, 1, 3, 1), 2),           # shared FP4 copy: not built
+    ((2, 4, 1, 64, 128, 16, 1, 3, 2), 1),           # shared flag neither 0 nor 1
 ])
 def test_invalid_configs_are_rejected_on_the_host(lad, fields, status):
     c = lad.ReplayConfig(*fields)

@@ -1,5 +1,6 @@
-"""MX FP4 read copy on the GPU (separated precisions: the float32 master
-takes every flush, outputs read the FP4 copy).
+"""MX FP4 read copy on the GPU: separated precisions (the float32 master
+takes every flush, outputs read the FP4 copy) and shared (the FP4 copy is
+the only checkpoint: every flush dequantises it, folds and rewrites it).
 
 * storage: the codes and E8M0 block scales the flush writes from a float32
   checkpoint equal the oracle's MX quantiser bit for bit (zero blocks,
@@ -45,13 +46,14 @@ def _crafted(w):
     return S
 
 
-@pytest.mark.parametrize("P,N", [(64, 128), (16, 16), (128, 128)])
-def test_fp4_codes_bit_exact(P, N):
+@pytest.mark.parametrize("P,N,shared", [(64, 128, False), (16, 16, False), (128, 128, False), (64, 128, True),
+                                        (16, 16, True)])
+def test_fp4_codes_bit_exact(P, N, shared):
     w = synth.Workload(batch=3, heads=4, groups=2, head_dim=P, state_dim=N, ring_len=4,
                        io_dtype="bf16", config=synth.CONFIG_ID["misc"], layer=70 + P)
-    gu.note(f"fp4 codes P={P} N={N}")
+    gu.note(f"fp4 codes P={P} N={N} shared={shared}")
     S = _crafted(w)
-    layer = _layer(w, read_copy="fp4")
+    layer = _layer(w, read_copy="fp4", shared_lowp=shared)
     layer.load_checkpoint(gu.to_dev(S))
     torch.cuda.synchronize()
     packed, scale = oracle.core.quant_blocks_mxfp4(S)
@@ -60,13 +62,15 @@ def test_fp4_codes_bit_exact(P, N):
     assert np.array_equal(got_s, scale), np.argwhere(got_s != scale)[:5]
     mism = np.argwhere(got_c != packed)
     assert mism.size == 0, (mism[:5], got_c[tuple(mism[0])], packed[tuple(mism[0])])
-    assert np.array_equal(layer.s_master.cpu().numpy(), S)
+    if not shared:
+        assert np.array_equal(layer.s_master.cpu().numpy(), S)
+    assert layer.base.cpu().tolist() == layer.pos.cpu().tolist()
     layer.close()
 
 
-def _check(y_gpu, x, S0, L, label):
+def _check(y_gpu, x, S0, L, label, shared=False):
     y_exact = runs.standard(x, S0.copy())
-    y_emul = runs.separated(x, S0.copy(), L, "fp4")
+    y_emul = (runs.shared if shared else runs.separated)(x, S0.copy(), L, "fp4")
     tok_e, vec_e, _ = gu.errors(y_gpu, y_emul)
     e_gpu = runs.normwise_rel_err(y_gpu, y_exact)
     e_emul = runs.normwise_rel_err(y_emul.astype(np.float64), y_exact)
@@ -76,14 +80,17 @@ def _check(y_gpu, x, S0, L, label):
     assert np.all(e_gpu <= 1.1 * e_emul + TOL_VS_EMUL)
 
 
-def test_fp4_dual_precision_workload():
+@pytest.mark.parametrize("shared", [False, True])
+def test_fp4_dual_precision_workload(shared):
     """Dual-precision shapes (B=256, H=128, G=8, P=64, N=128, L=16), full
-    batch, 64 steps through replay_step, 4 sampled sequences."""
+    batch, 64 steps through replay_step, 4 sampled sequences; separated (the
+    float32 master takes the folds) and shared (each fold starts from the FP4
+    copy and rewrites it)."""
     w = synth.named("dual")
     T, seqs = 64, [0, 97, 160, 255]
-    gu.note("fp4 dual precision workload")
+    gu.note(f"fp4 dual precision workload shared={shared}")
     dev = synth.step_inputs_torch(w, 0, T, device=gu.DEV)
-    layer = _layer(w, read_copy="fp4")
+    layer = _layer(w, read_copy="fp4", shared_lowp=shared)
     y = torch.empty((T, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
     for t in range(T):
         layer.step(dev["q"][t], dev["k"][t], dev["v"][t], dev["dt"][t], dev["a"][t], y[t], flush_at=w.ring_len)
@@ -91,26 +98,30 @@ def test_fp4_dual_precision_workload():
     assert layer.get_error()[0] == 0
     x = runs.widen_inputs({k: synth.to_storage(v[:, seqs]) for k, v in dev.items()}, w.io_dtype)
     _check(y.cpu().numpy()[:, seqs], x, np.zeros((len(seqs), w.heads, w.head_dim, w.state_dim)), w.ring_len,
-           "dual workload")
+           "dual workload", shared)
     layer.close()
 
 
-@pytest.mark.parametrize("P,N,io,L,B,H,G", [
-    (16, 16, "f32", 4, 3, 6, 3),
-    (64, 64, "bf16", 5, 5, 4, 2),
-    (128, 128, "bf16", 8, 3, 4, 2),
-    (64, 128, "f32", 32, 2, 8, 4),
+@pytest.mark.parametrize("P,N,io,L,B,H,G,shared", [
+    (16, 16, "f32", 4, 3, 6, 3, False),
+    (64, 64, "bf16", 5, 5, 4, 2, False),
+    (128, 128, "bf16", 8, 3, 4, 2, False),
+    (64, 128, "f32", 32, 2, 8, 4, False),
+    (16, 16, "f32", 4, 3, 6, 3, True),
+    (64, 64, "bf16", 5, 5, 4, 2, True),
+    (128, 128, "bf16", 8, 3, 4, 2, True),
 ])
-def test_fp4_ragged(P, N, io, L, B, H, G):
+def test_fp4_ragged(P, N, io, L, B, H, G, shared):
     """Decode through append / decode / flush with the FP4 copy, ragged shapes,
-    starting from a non-zero checkpoint (so the copy matters from step 0)."""
+    starting from a non-zero checkpoint (so the copy matters from step 0);
+    separated, and shared (each flush starts from the FP4 copy)."""
     w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype=io,
                        config=synth.CONFIG_ID["misc"], layer=300 + P + L)
     T = 3 * L + 2
-    gu.note(f"fp4 ragged {w}")
+    gu.note(f"fp4 ragged {w} shared={shared}")
     S0 = synth.checkpoint_state(w, scale=0.5)
     dev = gu.DevInputs(w, 0, T)
-    layer = _layer(w, read_copy="fp4")
+    layer = _layer(w, read_copy="fp4", shared_lowp=shared)
     layer.load_checkpoint(gu.to_dev(S0))
     y = torch.empty((T, B, H, P), dtype=torch.float32, device=gu.DEV)
     for t in range(T):
@@ -120,7 +131,7 @@ def test_fp4_ragged(P, N, io, L, B, H, G):
     torch.cuda.synchronize()
     assert layer.get_error()[0] == 0
     x = gu.oracle_inputs(w, 0, T, list(range(B)))
-    _check(y.cpu().numpy(), x, S0.astype(np.float64), L, f"P={P} N={N} L={L}")
+    _check(y.cpu().numpy(), x, S0.astype(np.float64), L, f"P={P} N={N} L={L}", shared)
     layer.close()
 
 
