@@ -186,7 +186,7 @@ replay_status replay_decode(replay_handle *h, float *y, void *stream);
    t only when j <= t; abstract page: output-only verification).
    Position w (0-based) is ring entry t_w = count - W + 1 + w.
    y: [B][W][H][P] f32.  1 <= W <= min(8, L) for every configuration; with
-   bf16 io and a float32, bf16 or e4m3 read also up to min(16, L), and from
+   bf16 io (any read: float32, bf16, e4m3 or FP4) also up to min(16, L), and from
    W = 6 on such windows take the window's S Q^T on the matrix cores (other
    configurations return UNSUPPORTED for W > 8).  Needs count >= W per
    sequence (else TOO_FEW, NaN outputs for that sequence). */

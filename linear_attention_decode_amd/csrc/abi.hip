@@ -210,7 +210,7 @@ replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
     a.W = W;
     const int st = state_kind(c.read_copy);
     // windows from kWideFrom on: the matrix-core kernel where it applies (bf16
-    // io; float32, bf16 or e4m3 reads), else the register kernel up to kMaxWindow
+    // io; float32, bf16, e4m3 or FP4 reads), else the register kernel up to kMaxWindow
     if (W >= kWideFrom && verify_wide_supported(st, a))
         return from_hip(launch_verify_wide(c.head_dim, c.state_dim, st, a, s));
     if (W > kMaxWindow) return REPLAY_ERR_UNSUPPORTED;

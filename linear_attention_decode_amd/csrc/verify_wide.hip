@@ -1,5 +1,6 @@
 // verify_wide.hip -- speculative verify of windows of up to 16 drafts on the
-// matrix cores, bf16 io (replay_verify takes it from W = kWideFrom on).
+// matrix cores, bf16 io, reading the float32 checkpoint or a bf16, e4m3 or
+// MX FP4 copy (replay_verify takes it from W = kWideFrom on).
 //
 // The same outputs as the verify kernel of decode_impl.h: for the W newest
 // ring entries t_w = count-W+w of every (sequence, head)
@@ -104,7 +105,7 @@ __global__ __launch_bounds__((WideShape<P, N, ST, LM>::NT)) void verify_wide_ker
     const int base = r.base[b];
     const int pos = r.pos[b];
     WideRows<P, N, ST> rows;
-    if (wave < NTS / 64) rows.load(args.S, bh * (size_t)(P * N), p0, lane);
+    if (wave < NTS / 64) rows.load(args.S, bh * (size_t)(P * N), p0, lane, args.scale);
     const int count = pos - base;
     if (count < W) {  // uniform over the workgroup
         for (int i = tid; i < W * P; i += WS::NT) args.y[(((size_t)b * W + i / P) * H + h) * P + i % P] = __builtin_nanf("");
@@ -147,7 +148,11 @@ __global__ __launch_bounds__((WideShape<P, N, ST, LM>::NT)) void verify_wide_ker
     __syncthreads();
 
     rows.transpose(s_T[WS::COAL ? wave : 0], lane);
-    const f32x4 acc = rows.dot(s_Q, lane);
+    f32x4 acc;
+    if constexpr (ST == ST_FP4 && WS::BF)
+        acc = rows.dot_mx(s_Q, lane, static_cast<const uint8_t *>(args.scale) + (bh * P + p0 + 4 * lg) * WS::NB);
+    else
+        acc = rows.dot(s_Q, lane);
     // D[p0 + 4 lg + rr][w = lr]
     const int w = lr;
     if (w < W) {
@@ -181,12 +186,13 @@ static hipError_t launch_wide_pn(int st, const DecodeArgs &a, hipStream_t s) {
         case ST_F32: return launch_wide_st<P, N, ST_F32>(a, s);
         case ST_BF16: return launch_wide_st<P, N, ST_BF16>(a, s);
         case ST_FP8: return launch_wide_st<P, N, ST_FP8>(a, s);
+        case ST_FP4: return launch_wide_st<P, N, ST_FP4>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 bool verify_wide_supported(int st, const DecodeArgs &a) {
-    return a.r.io_bf16 && (st == ST_F32 || st == ST_BF16 || st == ST_FP8) && a.W >= 1 &&
+    return a.r.io_bf16 && (st == ST_F32 || st == ST_BF16 || st == ST_FP8 || st == ST_FP4) && a.W >= 1 &&
            a.W <= kMaxWideWindow && a.W <= a.r.L;
 }
 

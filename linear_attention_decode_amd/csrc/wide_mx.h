@@ -18,8 +18,12 @@
 //       bf16 tiles: v_mfma_f32_16x16x32_bf16, columns (4 st + g) 8 .. +7;
 //       e4m3 tiles: 16 codes a lane cover two such products, turned into
 //         bf16 pairs by the hardware conversion (exact);
-//       N below 32: the bf16 and e4m3 values are widened and take the float32
-//         products;
+//       MX FP4 tiles: step st is MX block st of the row (32 codes, 8 a lane
+//         group, 4 bytes a lane), one product per block into an accumulator
+//         of its own, scaled by the block's 2^e afterwards (exact) and added
+//         block after block: no per-row scale ever meets another row's;
+//       N below 32: the bf16, e4m3 and FP4 values are widened (FP4 with its
+//         block's scale, exact) and take the float32 products;
 //   - D[p][w] sits in lane (4-row group, column w), register rr -> row
 //     16i + 4g + rr.
 #pragma once
@@ -38,12 +42,14 @@ template <int P, int N, int ST>
 struct WideTile {
     static constexpr bool BF = wide_bf16_path<ST, N>();
     static constexpr int NTS = (P / 16) * 64;                      // one wavefront per 16 rows
-    static constexpr int ESZ = ST == ST_F32 ? 4 : (ST == ST_BF16 ? 2 : 1);
-    static constexpr int CVEC = BF ? 16 / ESZ : 4;                 // elements a lane loads per step
+    static constexpr bool MX = ST == ST_FP4;
+    static constexpr int ESZ = ST == ST_F32 ? 4 : (ST == ST_BF16 ? 2 : 1);   // FP4: two codes a byte
+    static constexpr int CVEC = BF ? (MX ? 8 : 16 / ESZ) : 4;      // elements a lane loads per step
     static constexpr int STEPS = N / (4 * CVEC);                   // loads per lane (4 lane groups)
+    static constexpr int NB = N / 32;                              // MX blocks of a row (FP4)
     static constexpr int TS = N + 8;                               // LDS row stride of Q (bf16), in elements
-    static constexpr int RB = N * ESZ;                             // bytes of a tile row
-    static constexpr bool COAL = (ST == ST_F32 || BF) && RB % 128 == 0;
+    static constexpr int RB = MX ? N / 2 : N * ESZ;                // bytes of a tile row
+    static constexpr bool COAL = !MX && (ST == ST_F32 || BF) && RB % 128 == 0;
     static constexpr int TROW = 36;   // staging row stride in words (128 bytes + 16 of padding: the
                                       // column reads of 16 rows hit distinct banks)
     using TE = uint16_t;   // Q stays bf16 in LDS (widened exactly where the float32 products take it)
@@ -87,6 +93,32 @@ struct WideA<ST_FP8, false> {   // 4 e4m3 codes, widened (unscaled)
         return f32x4{x[0], x[1], x[2], x[3]};
     }
 };
+template <>
+struct WideA<ST_FP4, false> {   // 4 E2M1 codes of one MX block, widened with the block's scale (exact)
+    uint32_t v;
+    int se;
+    __device__ __forceinline__ void load_mx(const void *S, const void *scales, size_t e) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(S) + e / 2));
+        se = (int)static_cast<const uint8_t *>(scales)[e / 32] - 127;
+    }
+    __device__ __forceinline__ f32x4 f32() const {
+        float x[4];
+        fp4_pair_to_f32(v, 0, x);
+        fp4_pair_to_f32(v, 1, x + 2);
+        return f32x4{ldexpf(x[0], se), ldexpf(x[1], se), ldexpf(x[2], se), ldexpf(x[3], se)};
+    }
+};
+template <>
+struct WideA<ST_FP4, true> {   // 8 E2M1 codes (4 bytes) of one MX block, unscaled
+    uint32_t v;
+    __device__ __forceinline__ void load(const void *S, size_t e) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(S) + e / 2));
+    }
+    // the 8 codes as bf16 pairs (exact)
+    __device__ __forceinline__ uint4 bf16x8() const {
+        return uint4{fp4_pair_to_bf16(v, 0), fp4_pair_to_bf16(v, 1), fp4_pair_to_bf16(v, 2), fp4_pair_to_bf16(v, 3)};
+    }
+};
 template <int ST>
 struct WideA<ST, true> {   // 16 bytes: 8 bf16, or 16 e4m3 codes
     uint4 v;
@@ -116,8 +148,8 @@ struct WideRows {
                                         // bytes 128 (i >> 1) + 16 (lane % 8)
 
     // Issue every load of rows p0..p0+15 of the tile that starts at element
-    // `tile` of S.
-    __device__ __forceinline__ void load(const void *S, size_t tile, int p0, int lane) {
+    // `tile` of S (`scales`: the E8M0 block scales of an FP4 copy).
+    __device__ __forceinline__ void load(const void *S, size_t tile, int p0, int lane, const void *scales = nullptr) {
         if constexpr (WT::COAL) {
             const char *t = static_cast<const char *>(S) + (tile + (size_t)p0 * N) * WT::ESZ;
 #pragma unroll
@@ -129,7 +161,13 @@ struct WideRows {
         } else {
             const size_t row = tile + (size_t)(p0 + (lane & 15)) * N;
 #pragma unroll
-            for (int st = 0; st < STEPS; ++st) at[st].load(S, row + (size_t)(4 * st + (lane >> 4)) * WT::CVEC);
+            for (int st = 0; st < STEPS; ++st) {
+                const size_t e = row + (size_t)(4 * st + (lane >> 4)) * WT::CVEC;
+                if constexpr (ST == ST_FP4 && !WT::BF)
+                    at[st].load_mx(S, scales, e);
+                else
+                    at[st].load(S, e);
+            }
         }
     }
 
@@ -171,8 +209,40 @@ struct WideRows {
         }
     }
 
+    // MX FP4 (N a multiple of 32): D = S Q^T over the 16 rows, one product
+    // per block, each scaled by its 2^e; rsc = the block scales of row
+    // p0 + 4 lg (4 rows of NB bytes, this lane's output rows).
+    __device__ __forceinline__ f32x4 dot_mx(const typename WT::TE (*s_Q)[WT::TS], int lane,
+                                            const uint8_t *rsc) const {
+        static_assert(ST == ST_FP4 && WT::BF && (WT::NB == 2 || WT::NB == 4), "MX blocks");
+        const int lr = lane & 15, lg = lane >> 4;
+        uint32_t sw[WT::NB];   // the 4 rows' scale bytes, rsc[rr * NB + st]
+        if constexpr (WT::NB == 4) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(rsc);
+            sw[0] = u.x; sw[1] = u.y; sw[2] = u.z; sw[3] = u.w;
+        } else {
+            const uint2 u = *reinterpret_cast<const uint2 *>(rsc);
+            sw[0] = u.x; sw[1] = u.y;
+        }
+        auto se = [&](int rr, int st) {   // scale byte rr * NB + st
+            const int i = rr * WT::NB + st;
+            return (int)((sw[i >> 2] >> (8 * (i & 3))) & 0xffu) - 127;
+        };
+        f32x4 out = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(&s_Q[lr][(4 * st + lg) * WT::CVEC]);
+            const f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(at[st].bf16x8()), as_bf16x8(q),
+                                                                      f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) out[rr] += ldexpf(acc[rr], se(rr, st));
+        }
+        return out;
+    }
+
     // D = S Q^T over the 16 rows: register rr = D[4 lg + rr][lr]
     __device__ __forceinline__ f32x4 dot(const typename WT::TE (*s_Q)[WT::TS], int lane) const {
+        static_assert(!(ST == ST_FP4 && WT::BF), "FP4 tiles with whole blocks per row take dot_mx");
         const int lr = lane & 15, lg = lane >> 4;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll

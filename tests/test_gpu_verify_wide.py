@@ -3,13 +3,13 @@ to 16, with bf16 io).
 
 - Rounds of W drafts with rollback and flushes when the next window would
   not fit, against the float64 oracle (per token over the layer output:
-  1e-4 per head for a float32 checkpoint; bf16 / e4m3 copies against the oracle's
+  1e-4 per head for a float32 checkpoint; bf16 / e4m3 / MX FP4 copies against the oracle's
   emulation of the same copy, tests/gpu_util.py assert_copy) and the integer ring model.
 - The same state scored with W = 16 here and W = 4 by the register kernel:
   the newest four positions agree to float32 rounding (the two kernels share
   nothing but the ring term's code).
 - Errors: count < W gives NaN and TOO_FEW; configurations the matrix cores
-  do not serve (an FP4 copy, float32 io) are rejected past W = 8."""
+  do not serve (float32 io) are rejected past W = 8."""
 import numpy as np
 import pytest
 import torch
@@ -41,6 +41,11 @@ def _layer(w, **kw):
     (64, 128, 8, 8, 2, 8, 2, "bf16"),
     (128, 128, 16, 9, 2, 4, 2, "fp8"),
     (64, 64, 16, 7, 3, 4, 2, "bf16"),
+    (64, 128, 16, 16, 3, 8, 2, "fp4"),      # one product per MX block
+    (64, 64, 16, 9, 3, 4, 2, "fp4"),
+    (128, 128, 32, 12, 2, 4, 2, "fp4"),
+    (16, 16, 16, 13, 2, 4, 1, "fp4"),       # FP4 tile widened with its block scales (N < 32)
+    (64, 128, 8, 6, 2, 8, 2, "fp4"),
 ])
 def test_wide_verify_rounds(P, N, L, W, B, H, G, copy):
     w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype="bf16",
@@ -67,7 +72,7 @@ def test_wide_verify_rounds(P, N, L, W, B, H, G, copy):
     layer.close()
 
 
-@pytest.mark.parametrize("P,N,copy", [(64, 128, None), (128, 128, None), (64, 128, "fp8")])
+@pytest.mark.parametrize("P,N,copy", [(64, 128, None), (128, 128, None), (64, 128, "fp8"), (64, 128, "fp4")])
 def test_wide_window_agrees_with_register_kernel(P, N, copy):
     """16 entries in the ring: verify(16) on the matrix cores and verify(4) in
     registers score the newest four positions of the same state."""
@@ -113,7 +118,7 @@ def test_wide_verify_errors():
     with pytest.raises(lad.ReplayError):
         layer.verify(17, torch.zeros((3, 17, 4, 64), dtype=torch.float32, device=gu.DEV))
     layer.close()
-    for kw in ({"read_copy": "fp4"}, {"io_dtype": "f32"}):
+    for kw in ({"io_dtype": "f32"},):
         wl = synth.Workload(batch=2, heads=4, groups=2, head_dim=64, state_dim=128, ring_len=16,
                             io_dtype=kw.get("io_dtype", "bf16"), config=synth.CONFIG_ID["misc"], layer=342)
         lay = lad.ReplayLayer(2, 4, 2, 64, 128, 16, io_dtype=wl.io_dtype, read_copy=kw.get("read_copy"),
