@@ -185,10 +185,9 @@ replay_status replay_decode(replay_handle *h, float *y, void *stream);
    window read the same checkpoint and buffer, entry j is visible to position
    t only when j <= t; abstract page: output-only verification).
    Position w (0-based) is ring entry t_w = count - W + 1 + w.
-   y: [B][W][H][P] f32.  1 <= W <= min(8, L) for every configuration; with
-   bf16 io (any read: float32, bf16, e4m3 or FP4) also up to min(16, L), and from
-   W = 6 on such windows take the window's S Q^T on the matrix cores (other
-   configurations return UNSUPPORTED for W > 8).  Needs count >= W per
+   y: [B][W][H][P] f32.  1 <= W <= min(16, L) for every configuration;
+   windows from W = 6 on (bf16 io) or W = 9 on (float32 io) take the
+   window's S Q^T and ring term on the matrix cores.  Needs count >= W per
    sequence (else TOO_FEW, NaN outputs for that sequence). */
 replay_status replay_verify(replay_handle *h, int32_t W, float *y, void *stream);
 

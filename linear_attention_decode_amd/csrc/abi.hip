@@ -209,9 +209,10 @@ replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
     a.y = y;
     a.W = W;
     const int st = state_kind(c.read_copy);
-    // windows from kWideFrom on: the matrix-core kernel where it applies (bf16
-    // io; float32, bf16, e4m3 or FP4 reads), else the register kernel up to kMaxWindow
-    if (W >= kWideFrom && verify_wide_supported(st, a))
+    // bf16 io: the matrix-core kernel from kWideFrom on; float32 io: past the
+    // register kernel's kMaxWindow
+    const int wide_from = c.io_dtype == REPLAY_BF16 ? kWideFrom : kMaxWindow + 1;
+    if (W >= wide_from && verify_wide_supported(st, a))
         return from_hip(launch_verify_wide(c.head_dim, c.state_dim, st, a, s));
     if (W > kMaxWindow) return REPLAY_ERR_UNSUPPORTED;
     return from_hip(launch_decode(c.head_dim, c.state_dim, st, a, s));

@@ -31,19 +31,25 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_ca
 
 // One ring wavefront's share: the 16 entries j0..j0+15 (a 32-entry ring
 // has two such wavefronts; their terms are added by the caller, block 0 +
-// block 1).
-template <int P, int N, int WM, int LM>
+// block 1).  IOB false: float32 ring operands; the dots then take
+// v_mfma_f32_16x16x4_f32, eight per 32-column block (lane group g holds
+// columns 32kb + 8g .. +7, product t takes column 32kb + 8g + t), and a
+// lane's v values are float pairs.
+template <int P, int N, int WM, int LM, bool IOB = true>
 struct MxRing {
     static constexpr int KB = (N + 31) / 32;      // 32-column blocks of k . q
     static constexpr int PW = (P + 31) / 32;      // 32-column blocks of v, one bf16 pair per lane
     static constexpr int NR = LM / 16;            // ring wavefronts per (sequence, head)
     static_assert(LM % 16 == 0 && P % 16 == 0 && N % 16 == 0, "tile shape");
 
-    // Operands, filled by the caller with raw bf16 bits.  Lane l = r + 16 g:
+    // Operands, filled by the caller with raw bf16 bits (IOB) or floats.  Lane l = r + 16 g:
     int j0;                         // first entry of this wavefront's block
     uint4 ka[KB];                   // k_{j0 + r}[32kb + 8g .. +7]        (entries past the live ones: any finite row)
     uint4 qb[KB];                   // q_{t_min(r, W-1)}[32kb + 8g .. +7]
     uint32_t vw[4][PW];             // v_{j0 + 4g + kk}[32pw + 2r .. +1]   (same; pairs past P: any finite word)
+    f32x4 kf[IOB ? 1 : KB][2];      // float32 io: the same k, q and v values as floats
+    f32x4 qf[IOB ? 1 : KB][2];
+    u32x2 vf[IOB ? 1 : 4][PW];
     float aj, dtj;                  // lane j (all LM entries): a_j, dt_j; 1 and 0 for j >= count
 
     // word index of lane l's v pair in block pw, clamped into the row
@@ -63,6 +69,17 @@ struct MxRing {
 
     __device__ __forceinline__ f32x4 dots(int lane) const {
         f32x4 dk = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!IOB) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    // columns past N (only when N < 32) count zero
+                    const float a = 32 * kb + 8 * (lane >> 4) < N ? kf[kb][t >> 2][t & 3] : 0.f;
+                    dk = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[kb][t >> 2][t & 3], dk, 0, 0, 0);
+                }
+            return dk;
+        }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             uint4 a = ka[kb];
@@ -161,8 +178,10 @@ struct MxRing {
             for (int half = 0; half < 2; ++half) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cf[kk], vval(vw[kk][pw], half), acc, 0, 0, 0);
+                for (int kk = 0; kk < 4; ++kk) {
+                    const float vv = IOB ? vval(vw[kk][pw], half) : __uint_as_float(vf[IOB ? 0 : kk][pw][half]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cf[kk], vv, acc, 0, 0, 0);
+                }
                 const int p = 32 * pw + 2 * lr + half;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {

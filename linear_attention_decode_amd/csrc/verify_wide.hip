@@ -1,6 +1,8 @@
 // verify_wide.hip -- speculative verify of windows of up to 16 drafts on the
-// matrix cores, bf16 io, reading the float32 checkpoint or a bf16, e4m3 or
-// MX FP4 copy (replay_verify takes it from W = kWideFrom on).
+// matrix cores, reading the float32 checkpoint or a bf16, e4m3 or MX FP4
+// copy; bf16 io (replay_verify takes it from W = kWideFrom on) or float32 io
+// (queries kept in float32, every product on v_mfma_f32_16x16x4_f32;
+// replay_verify takes it past the register kernel's 8).
 //
 // The same outputs as the verify kernel of decode_impl.h: for the W newest
 // ring entries t_w = count-W+w of every (sequence, head)
@@ -21,18 +23,20 @@
 
 namespace replay {
 
-template <int P, int N, int ST, int LM>
+template <int P, int N, int ST, int LM, bool IOB>
 struct WideShape : WideTile<P, N, ST> {
     static constexpr int NR = LM / 16;
     static constexpr int NT = WideTile<P, N, ST>::NTS + 64 * NR;
+    static constexpr int TSF = N + 4;   // LDS row stride of float32 queries (float32 io), in floats
 };
 
 // The ring part for a window of W <= 16 positions, operands from the ring
-// (as ring_wave_mx of the decode kernel, with the window size at run time).
-template <int P, int N, int LM>
+// (as ring_wave_mx of the decode kernel, with the window size at run time;
+// float32 io: the same layout with float operands).
+template <int P, int N, int LM, bool IOB>
 __device__ __forceinline__ void wide_ring_wave(const RingView &r, int lane, int j0, int b, int g, size_t bh,
                                                int base, int count, int W, float (*s_r)[P], float *s_abar) {
-    using MX = MxRing<P, N, kWide, LM>;
+    using MX = MxRing<P, N, kWide, LM, IOB>;
     const int L = r.L;
     const size_t gring = ((size_t)b * r.G + g) * L;
     const size_t hring = bh * L;
@@ -48,23 +52,46 @@ __device__ __forceinline__ void wide_ring_wave(const RingView &r, int lane, int 
         m.aj = r.a[dta_index(b, bh, r.H, L, sl)];
         m.dtj = r.dt[dta_index(b, bh, r.H, L, sl)];
     }
+    if constexpr (IOB) {
 #pragma unroll
-    for (int kb = 0; kb < MX::KB; ++kb) {
-        const int c = MX::col(kb, lane);
-        const int j = j0 + lr;
-        m.ka[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.k) +
-                                                    (gring + slot(j < count ? j : last)) * N + c);
-        m.qb[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.q) +
-                                                    (gring + slot(t0 + (lr < W ? lr : W - 1))) * N + c);
-    }
-    const auto vres = make_rsrc(static_cast<const uint16_t *>(r.v) + hring * P, (uint32_t)(L * P * 2));
+        for (int kb = 0; kb < MX::KB; ++kb) {
+            const int c = MX::col(kb, lane);
+            const int j = j0 + lr;
+            m.ka[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.k) +
+                                                        (gring + slot(j < count ? j : last)) * N + c);
+            m.qb[kb] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.q) +
+                                                        (gring + slot(t0 + (lr < W ? lr : W - 1))) * N + c);
+        }
+        const auto vres = make_rsrc(static_cast<const uint16_t *>(r.v) + hring * P, (uint32_t)(L * P * 2));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int j = j0 + 4 * lq + kk;
-        const uint32_t row = (uint32_t)slot(j < count ? j : last) * P;
+        for (int kk = 0; kk < 4; ++kk) {
+            const int j = j0 + 4 * lq + kk;
+            const uint32_t row = (uint32_t)slot(j < count ? j : last) * P;
 #pragma unroll
-        for (int pw = 0; pw < MX::PW; ++pw)
-            m.vw[kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * 2, 0, 0);
+            for (int pw = 0; pw < MX::PW; ++pw)
+                m.vw[kk][pw] = __builtin_amdgcn_raw_buffer_load_b32(vres, (row + 2 * MX::vword(pw, lane)) * 2, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < MX::KB; ++kb) {
+            const int c = MX::col(kb, lane);
+            const int j = j0 + lr;
+            const float *kr = static_cast<const float *>(r.k) + (gring + slot(j < count ? j : last)) * N + c;
+            const float *qr = static_cast<const float *>(r.q) + (gring + slot(t0 + (lr < W ? lr : W - 1))) * N + c;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                m.kf[kb][hf] = *reinterpret_cast<const f32x4 *>(kr + 4 * hf);
+                m.qf[kb][hf] = *reinterpret_cast<const f32x4 *>(qr + 4 * hf);
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int j = j0 + 4 * lq + kk;
+            const float *vr = static_cast<const float *>(r.v) + (hring + slot(j < count ? j : last)) * P;
+#pragma unroll
+            for (int pw = 0; pw < MX::PW; ++pw)
+                m.vf[kk][pw] = *reinterpret_cast<const u32x2 *>(vr + 2 * MX::vword(pw, lane));
+        }
     }
     if (lane >= count) {
         m.aj = 1.f;
@@ -78,13 +105,15 @@ __device__ __forceinline__ void wide_ring_wave(const RingView &r, int lane, int 
     m.term_cols(lane, dk, wv, s_r);
 }
 
-template <int P, int N, int ST, int LM>
-__global__ __launch_bounds__((WideShape<P, N, ST, LM>::NT)) void verify_wide_kernel(DecodeArgs args) {
-    using WS = WideShape<P, N, ST, LM>;
-    constexpr int NTS = WS::NTS, TS = WS::TS, NR = WS::NR;
+template <int P, int N, int ST, int LM, bool IOB>
+__global__ __launch_bounds__((WideShape<P, N, ST, LM, IOB>::NT)) void verify_wide_kernel(DecodeArgs args) {
+    using WS = WideShape<P, N, ST, LM, IOB>;
+    constexpr int NTS = WS::NTS, TS = WS::TS, NR = WS::NR, TSF = WS::TSF;
     using TE = typename WS::TE;
 
-    __shared__ __align__(16) TE s_Q[kWide][TS];    // the window's queries, Q[w][n]
+    // the window's queries, Q[w][n]: bf16 (bf16 io) or float32
+    __shared__ __align__(16) TE s_Q[IOB ? kWide : 1][IOB ? TS : 8];
+    __shared__ __align__(16) float s_Qf[IOB ? 1 : kWide][IOB ? 4 : TSF];
     __shared__ float s_r[NR][kWide][P];
     __shared__ float s_abar[kWide];
     __shared__ __align__(16) uint32_t s_T[WS::COAL ? NTS / 64 : 1][16][WS::TROW];   // per-wavefront staging
@@ -118,30 +147,38 @@ __global__ __launch_bounds__((WideShape<P, N, ST, LM>::NT)) void verify_wide_ker
         // terms; no path from its code reaches the tile registers' use, so
         // they stay free for it.
         const int blk = __builtin_amdgcn_readfirstlane(wave - NTS / 64);   // 16-entry block of the ring
-        wide_ring_wave<P, N, LM>(r, lane, 16 * blk, b, g, bh, base, count, W, s_r[blk], s_abar);
+        wide_ring_wave<P, N, LM, IOB>(r, lane, 16 * blk, b, g, bh, base, count, W, s_r[blk], s_abar);
         __syncthreads();
         return;
     }
     {
-        // the queries: row w of Q is ring entry count-W+w (bf16), zero for w >= W;
-        // 8 elements (16 bytes) a thread, every load issued before any is used
+        // the queries: row w of Q is ring entry count-W+w, zero for w >= W;
+        // 16 bytes (8 bf16 or 4 floats) a thread, every load issued before any is used
         const size_t gring = ((size_t)b * r.G + g) * L;
         const int bmod = base % L;
-        constexpr int QP = kWide * N / 8, QI = (QP + NTS - 1) / NTS;
+        constexpr int QE = IOB ? 8 : 4;   // elements per 16 bytes
+        constexpr int QP = kWide * N / QE, QI = (QP + NTS - 1) / NTS;
         uint4 qraw[QI];
 #pragma unroll
         for (int i = 0; i < QI; ++i) {
-            const int e = (i * NTS + tid < QP ? i * NTS + tid : QP - 1) * 8;
+            const int e = (i * NTS + tid < QP ? i * NTS + tid : QP - 1) * QE;
             const int w = e / N, n = e % N;
-            qraw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.q) +
-                                                      (gring + ring_slot(bmod, count - W + (w < W ? w : W - 1), L)) * N + n);
+            const size_t qe = (gring + ring_slot(bmod, count - W + (w < W ? w : W - 1), L)) * N + n;
+            if constexpr (IOB)
+                qraw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(r.q) + qe);
+            else
+                qraw[i] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(r.q) + qe);
         }
 #pragma unroll
         for (int i = 0; i < QI; ++i) {
             if (i * NTS + tid < QP) {
-                const int e = (i * NTS + tid) * 8;
+                const int e = (i * NTS + tid) * QE;
                 const int w = e / N, n = e % N;
-                wide_put_q<P, N, ST>(s_Q, w, n, w < W ? qraw[i] : uint4{0u, 0u, 0u, 0u});
+                const uint4 u = w < W ? qraw[i] : uint4{0u, 0u, 0u, 0u};
+                if constexpr (IOB)
+                    wide_put_q<P, N, ST>(s_Q, w, n, u);
+                else
+                    *reinterpret_cast<uint4 *>(&s_Qf[w][n]) = u;
             }
         }
     }
@@ -149,8 +186,11 @@ __global__ __launch_bounds__((WideShape<P, N, ST, LM>::NT)) void verify_wide_ker
 
     rows.transpose(s_T[WS::COAL ? wave : 0], lane);
     f32x4 acc;
-    if constexpr (ST == ST_FP4 && WS::BF)
-        acc = rows.dot_mx(s_Q, lane, static_cast<const uint8_t *>(args.scale) + (bh * P + p0 + 4 * lg) * WS::NB);
+    const uint8_t *rsc = static_cast<const uint8_t *>(args.scale) + (bh * P + p0 + 4 * lg) * WS::NB;   // FP4 rows
+    if constexpr (!IOB)
+        acc = rows.dot_f32q(s_Qf, lane, rsc);
+    else if constexpr (ST == ST_FP4 && WS::BF)
+        acc = rows.dot_mx(s_Q, lane, rsc);
     else
         acc = rows.dot(s_Q, lane);
     // D[p0 + 4 lg + rr][w = lr]
@@ -170,14 +210,19 @@ __global__ __launch_bounds__((WideShape<P, N, ST, LM>::NT)) void verify_wide_ker
     }
 }
 
-template <int P, int N, int ST>
-static hipError_t launch_wide_st(const DecodeArgs &a, hipStream_t s) {
+template <int P, int N, int ST, bool IOB>
+static hipError_t launch_wide_io(const DecodeArgs &a, hipStream_t s) {
     const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
     if (a.r.L <= 16)
-        verify_wide_kernel<P, N, ST, 16><<<blocks, WideShape<P, N, ST, 16>::NT, 0, s>>>(a);
+        verify_wide_kernel<P, N, ST, 16, IOB><<<blocks, WideShape<P, N, ST, 16, IOB>::NT, 0, s>>>(a);
     else
-        verify_wide_kernel<P, N, ST, kMaxRing><<<blocks, WideShape<P, N, ST, kMaxRing>::NT, 0, s>>>(a);
+        verify_wide_kernel<P, N, ST, kMaxRing, IOB><<<blocks, WideShape<P, N, ST, kMaxRing, IOB>::NT, 0, s>>>(a);
     return hipGetLastError();
+}
+
+template <int P, int N, int ST>
+static hipError_t launch_wide_st(const DecodeArgs &a, hipStream_t s) {
+    return a.r.io_bf16 ? launch_wide_io<P, N, ST, true>(a, s) : launch_wide_io<P, N, ST, false>(a, s);
 }
 
 template <int P, int N>
@@ -192,8 +237,8 @@ static hipError_t launch_wide_pn(int st, const DecodeArgs &a, hipStream_t s) {
 }
 
 bool verify_wide_supported(int st, const DecodeArgs &a) {
-    return a.r.io_bf16 && (st == ST_F32 || st == ST_BF16 || st == ST_FP8 || st == ST_FP4) && a.W >= 1 &&
-           a.W <= kMaxWideWindow && a.W <= a.r.L;
+    return (st == ST_F32 || st == ST_BF16 || st == ST_FP8 || st == ST_FP4) && a.W >= 1 && a.W <= kMaxWideWindow &&
+           a.W <= a.r.L;
 }
 
 hipError_t launch_verify_wide(int P, int N, int st, const DecodeArgs &a, hipStream_t s) {

@@ -1,4 +1,5 @@
-// wide_mx.h -- S Q^T for a window of up to 16 queries on the matrix cores,
+// wide_mx.h -- S Q^T for a window of up to 16 queries on the matrix cores
+// (queries in LDS as bf16 for bf16 io; float32 io takes dot_f32q),
 // shared by the matrix-core verify kernel (verify_wide.hip) and the fused
 // verify round (verify_step.hip), so that both produce the same bits:
 //   - streaming wavefront i owns rows 16i..16i+15 of a head's tile;
@@ -118,6 +119,11 @@ struct WideA<ST_FP4, true> {   // 8 E2M1 codes (4 bytes) of one MX block, unscal
     __device__ __forceinline__ uint4 bf16x8() const {
         return uint4{fp4_pair_to_bf16(v, 0), fp4_pair_to_bf16(v, 1), fp4_pair_to_bf16(v, 2), fp4_pair_to_bf16(v, 3)};
     }
+    // the 8 codes' values (unscaled, exact)
+    __device__ __forceinline__ void widen(float *x) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fp4_pair_to_f32(v, i, x + 2 * i);
+    }
 };
 template <int ST>
 struct WideA<ST, true> {   // 16 bytes: 8 bf16, or 16 e4m3 codes
@@ -128,6 +134,19 @@ struct WideA<ST, true> {   // 16 bytes: 8 bf16, or 16 e4m3 codes
         v = uint4{w.x, w.y, w.z, w.w};
     }
     __device__ __forceinline__ void set(uint4 u) { v = u; }
+    // the values (e4m3: unscaled), widened exactly: 8 (bf16) or 16 (e4m3)
+    __device__ __forceinline__ void widen(float *x) const {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (ST == ST_BF16) {
+                x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+                x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+            } else {
+                fp8x4_to_f32(w[i], x + 4 * i);
+            }
+        }
+    }
     // e4m3: codes 8h..8h+7 as bf16 pairs (exact)
     __device__ __forceinline__ uint4 bf16_half(int h) const {
         const uint32_t w0 = h ? v.z : v.x, w1 = h ? v.w : v.y;
@@ -236,6 +255,58 @@ struct WideRows {
                                                                       f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) out[rr] += ldexpf(acc[rr], se(rr, st));
+        }
+        return out;
+    }
+
+    // float32 queries (float32 io): D = S Q^T over the 16 rows with
+    // v_mfma_f32_16x16x4_f32, every tile value widened exactly; product t of
+    // step st takes column c0 + t of the lane's CVEC columns c0 = (4 st + lg)
+    // CVEC.  MX FP4 with whole blocks per row: one accumulator per block,
+    // scaled by the block's 2^e (rsc as for dot_mx).  Register rr = D[4 lg + rr][lr].
+    template <int TSF>
+    __device__ __forceinline__ f32x4 dot_f32q(const float (*s_Qf)[TSF], int lane, const uint8_t *rsc) const {
+        constexpr bool MXB = ST == ST_FP4 && WT::BF;
+        constexpr int CV = WT::CVEC;
+        const int lr = lane & 15, lg = lane >> 4;
+        uint32_t sw[MXB ? WT::NB : 1];
+        if constexpr (MXB) {
+            static_assert(WT::NB == 2 || WT::NB == 4, "MX blocks");
+            if constexpr (WT::NB == 4) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(rsc);
+                sw[0] = u.x; sw[1] = u.y; sw[2] = u.z; sw[3] = u.w;
+            } else {
+                const uint2 u = *reinterpret_cast<const uint2 *>(rsc);
+                sw[0] = u.x; sw[1] = u.y;
+            }
+        }
+        f32x4 out = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            const int c0 = (4 * st + lg) * CV;
+            float x[CV];
+            if constexpr (!WT::BF) {
+                const f32x4 a = at[st].f32();
+                x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+            } else {
+                at[st].widen(x);
+            }
+            f32x4 acc = MXB ? f32x4{0.f, 0.f, 0.f, 0.f} : out;
+#pragma unroll
+            for (int t4 = 0; t4 < CV / 4; ++t4) {
+                const f32x4 q = *reinterpret_cast<const f32x4 *>(&s_Qf[lr][c0 + 4 * t4]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[4 * t4 + u], q[u], acc, 0, 0, 0);
+            }
+            if constexpr (MXB) {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int i = rr * WT::NB + st;
+                    out[rr] += ldexpf(acc[rr], (int)((sw[i >> 2] >> (8 * (i & 3))) & 0xffu) - 127);
+                }
+            } else {
+                out = acc;
+            }
         }
         return out;
     }

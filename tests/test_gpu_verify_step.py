@@ -46,6 +46,7 @@ def _layer(w, **kw):
     (128, 128, "bf16", 12, 4, 2, 12, 3, None),
     (64, 128, "bf16", 5, 5, 3, 4, 1, None),       # W = L: every round folds
     (64, 128, "f32", 16, 5, 3, 8, 2, None),       # f32 io: the calls in turn
+    (64, 128, "f32", 16, 12, 3, 8, 2, None),      # f32 io past 8: verify on the float32 matrix cores
     (64, 128, "bf16", 32, 6, 3, 8, 2, None),      # L > 16: the calls in turn
     (64, 128, "bf16", 16, 5, 3, 8, 2, "bf16"),    # a bf16 read copy: the calls in turn
     (64, 128, "bf16", 16, 5, 6, 16, 4, "fp8"),    # e4m3 copy: one launch (fold: master + copy rewrite)

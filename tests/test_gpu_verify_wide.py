@@ -1,5 +1,5 @@
 """Speculative verify on the matrix cores (replay_verify from W = 6 on, up
-to 16, with bf16 io).
+to 16, with bf16 io; from W = 9 on with float32 io).
 
 - Rounds of W drafts with rollback and flushes when the next window would
   not fit, against the float64 oracle (per token over the layer output:
@@ -8,8 +8,9 @@ to 16, with bf16 io).
 - The same state scored with W = 16 here and W = 4 by the register kernel:
   the newest four positions agree to float32 rounding (the two kernels share
   nothing but the ring term's code).
-- Errors: count < W gives NaN and TOO_FEW; configurations the matrix cores
-  do not serve (float32 io) are rejected past W = 8."""
+- Float32 io past W = 8: the same rounds with float32 queries on the
+  float32 matrix cores.
+- Errors: count < W gives NaN and TOO_FEW; windows past 16 are rejected."""
 import numpy as np
 import pytest
 import torch
@@ -47,8 +48,8 @@ def _layer(w, **kw):
     (16, 16, 16, 13, 2, 4, 1, "fp4"),       # FP4 tile widened with its block scales (N < 32)
     (64, 128, 8, 6, 2, 8, 2, "fp4"),
 ])
-def test_wide_verify_rounds(P, N, L, W, B, H, G, copy):
-    w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype="bf16",
+def test_wide_verify_rounds(P, N, L, W, B, H, G, copy, io="bf16"):
+    w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype=io,
                        config=synth.CONFIG_ID["misc"], layer=300 + P + L + W)
     R = 10
     gu.note(f"wide verify {w} W={W} copy={copy}")
@@ -72,13 +73,32 @@ def test_wide_verify_rounds(P, N, L, W, B, H, G, copy):
     layer.close()
 
 
-@pytest.mark.parametrize("P,N,copy", [(64, 128, None), (128, 128, None), (64, 128, "fp8"), (64, 128, "fp4")])
-def test_wide_window_agrees_with_register_kernel(P, N, copy):
+@pytest.mark.parametrize("P,N,L,W,B,H,G,copy", [
+    (64, 128, 16, 16, 3, 8, 2, None),      # the verify workload's head, W = L
+    (64, 64, 20, 9, 3, 4, 2, None),        # two ring blocks
+    (128, 128, 32, 12, 2, 4, 2, None),
+    (16, 16, 16, 11, 3, 6, 3, None),       # N < 32: half the dot columns masked
+    (64, 128, 16, 10, 3, 8, 2, "bf16"),
+    (64, 128, 16, 12, 3, 8, 2, "fp8"),
+    (16, 16, 16, 16, 2, 4, 1, "fp8"),
+    (64, 128, 16, 16, 3, 8, 2, "fp4"),
+    (128, 128, 16, 9, 2, 4, 2, "fp4"),
+    (16, 16, 16, 14, 2, 4, 1, "fp4"),
+])
+def test_wide_verify_rounds_f32_io(P, N, L, W, B, H, G, copy):
+    """Float32 io past the register kernel's 8: the queries stay float32 and
+    every product runs on the float32 matrix cores."""
+    test_wide_verify_rounds(P, N, L, W, B, H, G, copy, io="f32")
+
+
+@pytest.mark.parametrize("P,N,copy,io", [(64, 128, None, "bf16"), (128, 128, None, "bf16"), (64, 128, "fp8", "bf16"),
+                                         (64, 128, "fp4", "bf16"), (64, 128, None, "f32"), (64, 64, "fp4", "f32")])
+def test_wide_window_agrees_with_register_kernel(P, N, copy, io):
     """16 entries in the ring: verify(16) on the matrix cores and verify(4) in
     registers score the newest four positions of the same state."""
-    w = synth.Workload(batch=3, heads=8, groups=2, head_dim=P, state_dim=N, ring_len=16, io_dtype="bf16",
+    w = synth.Workload(batch=3, heads=8, groups=2, head_dim=P, state_dim=N, ring_len=16, io_dtype=io,
                        config=synth.CONFIG_ID["misc"], layer=330 + P)
-    gu.note(f"wide vs register verify P={P} N={N} copy={copy}")
+    gu.note(f"wide vs register verify P={P} N={N} copy={copy} io={io}")
     dev = gu.DevInputs(w, 0, 40)
     layer = _layer(w, **({} if copy is None else {"read_copy": copy}))
     for t in range(24):                        # a non-zero checkpoint first
@@ -118,11 +138,7 @@ def test_wide_verify_errors():
     with pytest.raises(lad.ReplayError):
         layer.verify(17, torch.zeros((3, 17, 4, 64), dtype=torch.float32, device=gu.DEV))
     layer.close()
-    for kw in ({"io_dtype": "f32"},):
-        wl = synth.Workload(batch=2, heads=4, groups=2, head_dim=64, state_dim=128, ring_len=16,
-                            io_dtype=kw.get("io_dtype", "bf16"), config=synth.CONFIG_ID["misc"], layer=342)
-        lay = lad.ReplayLayer(2, 4, 2, 64, 128, 16, io_dtype=wl.io_dtype, read_copy=kw.get("read_copy"),
-                              device=gu.DEV)
-        with pytest.raises(lad.ReplayError):
-            lay.verify(12, torch.zeros((2, 12, 4, 64), dtype=torch.float32, device=gu.DEV))
-        lay.close()
+    lay = lad.ReplayLayer(2, 4, 2, 64, 128, 16, io_dtype="f32", device=gu.DEV)
+    with pytest.raises(lad.ReplayError):
+        lay.verify(17, torch.zeros((2, 17, 4, 64), dtype=torch.float32, device=gu.DEV))
+    lay.close()
