@@ -24,12 +24,20 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
     return __uint_as_float(b16 << 16);
 }
 
-// float32 -> bf16 bits, round to nearest even, NaN kept quiet.
+// float32 -> bf16 bits, round to nearest even, NaN kept quiet (a select,
+// not a branch: the conversion sits in unrolled per-element loops).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return (u & 0x7fffffffu) > 0x7f800000u ? (u >> 16) | 0x40u : rounded;
+}
+
+// two floats -> a bf16 pair (a in the low half), round to nearest even, by
+// the hardware conversion (v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_pair_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_pair_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16_pair(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_pair_t{a, b}, bf16x2_pair_t));
 }
 
 // four e4m3 codes packed in a word -> floats (hardware OCP e4m3 conversion)
@@ -41,6 +49,39 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float *out) {
     out[2] = hi[0];
     out[3] = hi[1];
 }
+
+// x / d for many x and one divisor d, for e4m3 codes.  The correctly rounded
+// float32 division runs a reciprocal refined by one Newton step, two
+// remainder corrections and a special-case fix-up, after rescaling operands
+// whose exponents are near the ends of the range; here the divisor's part is
+// formed once.  While 2^-60 <= d <= 2^60 and |x| <= 448 d, that rescaling
+// only ever applies to quotients below 2^-43 (|x| < 2^-103, or x / d
+// subnormal), so the result has the bits of x / d wherever they can decide an
+// e4m3 code (those small quotients are +-0 in e4m3 either way, sign from
+// the fix-up).  Outside that range of d, exact division.  d must be the
+// same in every lane; run(f) calls f with the division to use, so that the
+// choice is one scalar branch around the caller's whole loop.
+struct ScaleDiv {
+    float d, y;
+    __device__ __forceinline__ explicit ScaleDiv(float d_) : d(d_) {
+        const float y0 = __builtin_amdgcn_rcpf(d);
+        y = fmaf(fmaf(-d, y0, 1.0f), y0, y0);
+    }
+    __device__ __forceinline__ float quick(float x) const {
+        float q = x * y;
+        q = fmaf(fmaf(-d, q, x), y, q);
+        q = fmaf(fmaf(-d, q, x), y, q);
+        return __builtin_amdgcn_div_fixupf(q, d, x);
+    }
+    template <class F>
+    __device__ __forceinline__ void run(F f) const {
+        const int fast = __builtin_amdgcn_readfirstlane((int)(d >= 0x1p-60f && d <= 0x1p60f));
+        if (fast)
+            f([this](float x) { return quick(x); });
+        else
+            f([this](float x) { return x / d; });
+    }
+};
 
 // four floats -> packed e4m3 codes, round to nearest even, saturating to +-448
 __device__ __forceinline__ uint32_t f32x4_to_fp8(float a, float b, float c, float d) {
@@ -488,6 +529,20 @@ struct RowReduce {
         }
     }
 };
+
+// Lanes of one wavefront exchanging data through LDS, with no workgroup
+// barrier: every lane's writes must come before any lane's reads.  Program
+// order alone does not give that, since the compiler may split the
+// wavefront at a divergent branch ahead of the exchange and run the rest
+// once per subset of lanes (the subset that runs first then reads the other
+// subset's stale data).  The wave barrier is convergent, so all lanes meet
+// it; the fences keep the LDS accesses on their side of it (within a
+// wavefront they need no wait instruction).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
 
 // ---- barriers -------------------------------------------------------------
 // Workgroup barrier that publishes LDS only.  __syncthreads() also waits for

@@ -5,18 +5,20 @@
 // (page "ReplaySSM: Cachear Inputs, No Estado", section "Los dos caminos",
 // eq. "Ruta estado y salida"; "Decodificacion estandar", step 4: the
 // buffer is folded into the checkpoint and written once), with
-// abar_c = prod_{m<=c} a_m and s_{j,c} = dt_j prod_{j<m<=c} a_m.  The new
-// checkpoint is written to the float32 master and/or a bf16 / e4m3 copy
-// (page "ReplaySSM: Cache SSM Inputs, Not State", Abstract: a low-precision
-// copy serves outputs, a higher-precision checkpoint takes the updates).
-// e4m3 copies carry one scale per head: scale = amax/448 (1 if amax = 0),
-// code = e4m3(x / scale), round to nearest even, saturating.
+// abar_c = prod_{m<=c} a_m and s_{j,c} = dt_j prod_{j<m<=c} a_m.  The fold
+// reads the float32 master (or, for a checkpoint load, a float32 source with
+// an empty ring) and writes the float32 master and/or a bf16 / e4m3 / MX FP4
+// copy (page "ReplaySSM: Cache SSM Inputs, Not State", Abstract: a
+// low-precision copy serves outputs, a higher-precision checkpoint takes the
+// updates).  e4m3 copies carry one scale per head: scale = amax/448 (1 if
+// amax = 0), code = e4m3(x / scale), round to nearest even, saturating.  A
+// shared low-precision checkpoint (no master) folds in flush_shared.hip.
 //
-// One workgroup per head.  The tile streams through registers (16-byte
+// HC heads per workgroup.  The tile streams through registers (16-byte
 // master chunks); s_j v_j (P x c) and k_j (c x N) are staged in LDS, so each
-// state element costs c FMAs against two LDS broadcasts per ring entry.
-// A second small kernel moves the base pointer once every head of the
-// sequence has read it.
+// state element costs c FMAs against two LDS broadcasts per ring entry.  The
+// last workgroup of a sequence to arrive at its counter moves the base
+// pointer, once every workgroup of the sequence has read it.
 #include "device_common.h"
 
 namespace replay {
@@ -37,7 +39,7 @@ struct FlushShape {
 // issued before the previous head is folded; the group's k rows are staged
 // once): a flush that finds nothing due costs B*H/HC workgroups that only
 // read the pointer.
-template <int P, int N, int SIN, int COPY, bool WRITE_MASTER, bool IOB, int HC>
+template <int P, int N, int COPY, bool WRITE_MASTER, bool IOB, int HC>
 __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs args) {
     using Sh = FlushShape<P, N>;
     constexpr int VEC = Sh::VEC, NT = Sh::NT, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
@@ -84,7 +86,7 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     // issued before head hl is folded, so the memory latency is paid once per
     // workgroup instead of once per head.
     struct HeadLoads {
-        Chunk<SIN, VEC> ch[ITER];
+        Chunk<ST_F32, VEC> ch[ITER];
         float a, dt;
         IoVec<IOB, 1> v[JPG];
     };
@@ -92,12 +94,7 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
         const size_t bh = (size_t)b * r.H + h0 + hl;
         const size_t tile = bh * (size_t)(P * N);
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            if constexpr (SIN == ST_FP4)
-                hd.ch[i].load_mx(args.S_in, args.scale_in, tile + (size_t)(i * NT + tid) * VEC);
-            else
-                hd.ch[i].load(args.S_in, tile + (size_t)(i * NT + tid) * VEC);
-        }
+        for (int i = 0; i < ITER; ++i) hd.ch[i].load(args.S_in, tile + (size_t)(i * NT + tid) * VEC);
         hd.a = 1.f;
         hd.dt = 0.f;
         if (count > 0) {
@@ -133,7 +130,6 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     for (int hl = 0; hl < HC; ++hl) {
     const size_t bh = (size_t)b * r.H + h0 + hl;
     const size_t tile = bh * (size_t)(P * N);
-    const float sc_in = (SIN == ST_FP8) ? static_cast<const float *>(args.scale_in)[bh] : 1.0f;
     if (hl + 1 < HC) issue(hl + 1, nxt);
 
     // 2. segment weights of the c entries
@@ -181,11 +177,7 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     float x[ITER][VEC];
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {
-        cur.ch[i].widen(x[i], sc_in);
-        if constexpr (SIN == ST_FP4) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) x[i][e] = ldexpf(x[i][e], cur.ch[i].se);   // the block's scale, exact
-        }
+        cur.ch[i].widen(x[i], 1.0f);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[i][e] *= abar;
     }
@@ -217,8 +209,8 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
 #pragma unroll
         for (int i = 0; i < ITER; ++i) {
             u32x2 o;
-            o.x = f32_to_bf16_bits(x[i][0]) | (f32_to_bf16_bits(x[i][1]) << 16);
-            o.y = f32_to_bf16_bits(x[i][2]) | (f32_to_bf16_bits(x[i][3]) << 16);
+            o.x = f32x2_to_bf16_pair(x[i][0], x[i][1]);
+            o.y = f32x2_to_bf16_pair(x[i][2], x[i][3]);
             __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(cp + (size_t)(i * NT + tid) * VEC));
         }
     } else if constexpr (COPY == ST_FP8) {
@@ -235,12 +227,15 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
 #pragma unroll
         for (int i = 1; i < NT / 64; ++i) amax = fmaxf(amax, s_red[i]);
         const float sig = amax > 0.f ? amax / 448.0f : 1.0f;   // correctly rounded divide
+        const ScaleDiv dv(sig);
         uint8_t *cp = static_cast<uint8_t *>(args.copy_out) + tile;
+        dv.run([&](auto div) {
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const uint32_t o = f32x4_to_fp8(x[i][0] / sig, x[i][1] / sig, x[i][2] / sig, x[i][3] / sig);
-            __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(cp + (size_t)(i * NT + tid) * VEC));
-        }
+            for (int i = 0; i < ITER; ++i) {
+                const uint32_t o = f32x4_to_fp8(div(x[i][0]), div(x[i][1]), div(x[i][2]), div(x[i][3]));
+                __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(cp + (size_t)(i * NT + tid) * VEC));
+            }
+        });
         if (tid == 0) static_cast<float *>(args.scale_out)[bh] = sig;
     } else if constexpr (COPY == ST_FP4) {
         // MX FP4: the 32 consecutive values of 8 neighbouring lanes share the
@@ -286,15 +281,15 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     }
 }
 
-template <int P, int N, int SIN, int COPY, bool WM, int HC>
+template <int P, int N, int COPY, bool WM, int HC>
 static hipError_t launch_hc(const FlushArgs &a, hipStream_t s) {
     using Sh = FlushShape<P, N>;
     const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H / HC);
     const size_t lds = (size_t)(P + N) * a.r.L * sizeof(float);
     if (a.r.io_bf16)
-        flush_kernel<P, N, SIN, COPY, WM, true, HC><<<blocks, Sh::NT, lds, s>>>(a);
+        flush_kernel<P, N, COPY, WM, true, HC><<<blocks, Sh::NT, lds, s>>>(a);
     else
-        flush_kernel<P, N, SIN, COPY, WM, false, HC><<<blocks, Sh::NT, lds, s>>>(a);
+        flush_kernel<P, N, COPY, WM, false, HC><<<blocks, Sh::NT, lds, s>>>(a);
     return hipGetLastError();
 }
 
@@ -303,32 +298,30 @@ static hipError_t launch_hc(const FlushArgs &a, hipStream_t s) {
 // but one step in L, where the smaller grid saves most; a flush that folds
 // part of the batch every call (speculative rounds) and a checkpoint load
 // keep one head per workgroup, which folds faster.
-template <int P, int N, int SIN, int COPY, bool WM>
+template <int P, int N, int COPY, bool WM>
 static hipError_t launch_one(const FlushArgs &a, hipStream_t s) {
     constexpr int HC = 4;
     if (!a.force_empty && a.min_count >= a.r.L && (a.r.H / a.r.G) % HC == 0)
-        return launch_hc<P, N, SIN, COPY, WM, HC>(a, s);
-    return launch_hc<P, N, SIN, COPY, WM, 1>(a, s);
+        return launch_hc<P, N, COPY, WM, HC>(a, s);
+    return launch_hc<P, N, COPY, WM, 1>(a, s);
 }
 
 template <int P, int N>
 static hipError_t launch_pn(int st_in, int st_copy, bool wm, const FlushArgs &a, hipStream_t s) {
     if (st_in == ST_F32 && wm) {           // separated: the float32 master takes the update
-        if (st_copy == ST_BF16) return launch_one<P, N, ST_F32, ST_BF16, true>(a, s);
-        if (st_copy == ST_FP8) return launch_one<P, N, ST_F32, ST_FP8, true>(a, s);
-        if (st_copy == ST_FP4) return launch_one<P, N, ST_F32, ST_FP4, true>(a, s);
-        return launch_one<P, N, ST_F32, -1, true>(a, s);
+        if (st_copy == ST_BF16) return launch_one<P, N, ST_BF16, true>(a, s);
+        if (st_copy == ST_FP8) return launch_one<P, N, ST_FP8, true>(a, s);
+        if (st_copy == ST_FP4) return launch_one<P, N, ST_FP4, true>(a, s);
+        return launch_one<P, N, -1, true>(a, s);
     }
     if (st_in == ST_F32) {                 // shared mode, loading a float32 checkpoint
-        if (st_copy == ST_BF16) return launch_one<P, N, ST_F32, ST_BF16, false>(a, s);
-        if (st_copy == ST_FP8) return launch_one<P, N, ST_F32, ST_FP8, false>(a, s);
-        if (st_copy == ST_FP4) return launch_one<P, N, ST_F32, ST_FP4, false>(a, s);
+        if (st_copy == ST_BF16) return launch_one<P, N, ST_BF16, false>(a, s);
+        if (st_copy == ST_FP8) return launch_one<P, N, ST_FP8, false>(a, s);
+        if (st_copy == ST_FP4) return launch_one<P, N, ST_FP4, false>(a, s);
         return hipErrorInvalidValue;
     }
-    if (wm) return hipErrorInvalidValue;   // shared mode: the copy is the only checkpoint
-    if (st_in == ST_BF16 && st_copy == ST_BF16) return launch_one<P, N, ST_BF16, ST_BF16, false>(a, s);
-    if (st_in == ST_FP8 && st_copy == ST_FP8) return launch_one<P, N, ST_FP8, ST_FP8, false>(a, s);
-    if (st_in == ST_FP4 && st_copy == ST_FP4) return launch_one<P, N, ST_FP4, ST_FP4, false>(a, s);
+    if (wm || a.force_empty) return hipErrorInvalidValue;   // shared mode: the copy is the only checkpoint
+    if (st_in == st_copy) return launch_flush_shared(P, N, st_in, a, s);   // flush_shared.hip
     return hipErrorInvalidValue;
 }
 

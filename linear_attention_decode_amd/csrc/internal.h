@@ -110,6 +110,8 @@ hipError_t launch_verify_wide(int P, int N, int st, const DecodeArgs &a, hipStre
 bool verify_wide_supported(int st, const DecodeArgs &a);
 hipError_t launch_flush(int P, int N, int st_in, int st_copy, bool write_master, const FlushArgs &a,
                         hipStream_t s);
+// the fold of a shared checkpoint: the copy (type st) read, folded and rewritten in place
+hipError_t launch_flush_shared(int P, int N, int st, const FlushArgs &a, hipStream_t s);
 hipError_t launch_append(int P, int N, const RingView &r, void *ring_q, void *ring_k, void *ring_v,
                          float *ring_dt, float *ring_a, int32_t *pos, int32_t *sync, int32_t W, const void *q,
                          const void *k, const void *v, const float *dt, const float *a, hipStream_t s);

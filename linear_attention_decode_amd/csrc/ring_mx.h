@@ -160,9 +160,10 @@ struct MxRing {
     }
 
     // s_r[w][p] = this block's part of R[w][p]; reads the weights this
-    // wavefront wrote to s_sw (a wavefront's own LDS accesses complete in order)
+    // wavefront wrote to s_sw (other lanes' writes: wave_lds_sync first)
     __device__ __forceinline__ void term(int lane, f32x4 dk, float (*s_r)[P], const float (*s_sw)[LM]) const {
         const int lr = lane & 15, lq = lane >> 4;
+        wave_lds_sync();
         const f32x4 wv = *reinterpret_cast<const f32x4 *>(&s_sw[lr < WM ? lr : 0][j0 + 4 * lq]);
         const f32x4 cf = lr < WM ? wv * dk : f32x4{0.f, 0.f, 0.f, 0.f};
         term_coeffs(lr, lq, cf, s_r);

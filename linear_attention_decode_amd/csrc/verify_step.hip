@@ -731,14 +731,17 @@ __attribute__((amdgpu_waves_per_eu(8))) void verify_step_copy_kernel(StepArgs ar
 #pragma unroll
                 for (int i = 1; i < NTS / 64; ++i) amax = fmaxf(amax, s_red[i]);
                 const float sig = amax > 0.f ? amax / 448.0f : 1.0f;   // correctly rounded divide
+                const ScaleDiv dv(sig);
                 uint8_t *cp = static_cast<uint8_t *>(const_cast<void *>(args.copy)) + tile;
+                dv.run([&](auto div) {
 #pragma unroll
-                for (int i = 0; i < MITER; ++i) {
-                    const uint32_t o = f32x4_to_fp8(x[i][0] / sig, x[i][1] / sig, x[i][2] / sig, x[i][3] / sig);
-                    const size_t e0 = (size_t)(i * NTS + tid) * MVEC;
-                    __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(cp + e0));
-                    *reinterpret_cast<uint32_t *>(&s_code[e0]) = o;
-                }
+                    for (int i = 0; i < MITER; ++i) {
+                        const uint32_t o = f32x4_to_fp8(div(x[i][0]), div(x[i][1]), div(x[i][2]), div(x[i][3]));
+                        const size_t e0 = (size_t)(i * NTS + tid) * MVEC;
+                        __builtin_nontemporal_store(o, reinterpret_cast<uint32_t *>(cp + e0));
+                        *reinterpret_cast<uint32_t *>(&s_code[e0]) = o;
+                    }
+                });
                 if (tid == 0) static_cast<float *>(const_cast<void *>(args.copy_scale))[bh] = sig;
                 sc = sig;
             } else {

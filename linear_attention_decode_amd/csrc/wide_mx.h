@@ -210,17 +210,19 @@ struct WideRows {
 
     // coalesced: into the operand layout, chunk by chunk through this
     // wavefront's buffer T (lane (row lr, group lg) of step st reads row lr,
-    // bytes 64 (st % 2) + 16 lg of chunk st / 2; a wavefront's own LDS
-    // accesses complete in order, so each chunk's writes follow the previous
-    // chunk's reads)
+    // bytes 64 (st % 2) + 16 lg of chunk st / 2; wave_lds_sync puts every
+    // lane's writes of a chunk before any lane's reads, and those reads
+    // before the next chunk's writes)
     __device__ __forceinline__ void transpose(uint32_t (*T)[WT::TROW], int lane) {
         if constexpr (WT::COAL) {
             const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
             for (int c = 0; c < STEPS / 2; ++c) {
+                if (c > 0) wave_lds_sync();
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
                     *reinterpret_cast<uint4 *>(&T[8 * hf + (lane >> 3)][4 * (lane & 7)]) = raw[2 * c + hf];
+                wave_lds_sync();
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
                     at[2 * c + s2].set(*reinterpret_cast<const uint4 *>(&T[lr][16 * s2 + 4 * lg]));

@@ -67,6 +67,47 @@ def test_copy_codes_bit_exact(fmt, shared):
     layer.close()
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("route", ["step", "verify_step"])
+def test_copy_codes_after_folds_bit_exact(fmt, route):
+    """Separated precisions: after folds (fused steps with the flush, or
+    fused speculative rounds), the copy's codes and scales equal the
+    oracle's quantisers applied to the float32 master the same launch wrote,
+    bit for bit (the e4m3 division by the head's scale included)."""
+    w = synth.Workload(batch=4, heads=8, groups=2, head_dim=64, state_dim=128, ring_len=8,
+                       io_dtype="bf16", config=synth.CONFIG_ID["misc"], layer=62)
+    gu.note(f"copy codes after folds {fmt} {route}")
+    layer = _layer(w, read_copy=fmt)
+    layer.load_checkpoint(gu.to_dev(synth.checkpoint_state(w, scale=0.6)))
+    if route == "step":
+        T = 27
+        dev = gu.DevInputs(w, 0, T)
+        y = torch.empty((w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
+        for t in range(T):
+            layer.step(*dev.step(t), y, flush_at=w.ring_len)
+    else:
+        R, W = 9, 4
+        gu.run_verify(layer, w, gu.DevInputs(w, 0, R * W), R, W, synth.accept_counts(w, R, W), fused=True)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    assert (layer.base.cpu() > 0).all()          # every sequence folded at least once
+    S = layer.s_master.cpu().numpy()
+    if fmt == "bf16":
+        got = layer.s_copy.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, oracle.bf16_encode(S))
+    elif fmt == "fp8":
+        codes, scale = oracle.quant_heads_e4m3(S)
+        assert np.array_equal(layer.s_scale.cpu().numpy(), scale)
+        got = layer.s_copy.cpu().numpy()
+        mism = np.argwhere(got != codes)
+        assert mism.size == 0, (mism[:5], got[tuple(mism[0])], codes[tuple(mism[0])])
+    else:
+        packed, scale = oracle.core.quant_blocks_mxfp4(S)
+        assert np.array_equal(layer.s_scale.cpu().numpy().reshape(scale.shape), scale)
+        assert np.array_equal(layer.s_copy.cpu().numpy().reshape(packed.shape), packed)
+    layer.close()
+
+
 MODES = [("bf16", False), ("fp8", False), ("bf16", True), ("fp8", True)]
 
 
@@ -96,6 +137,37 @@ def test_dual_precision_workload(fmt, shared):
           f"vs emulation: per-token max {tok_e:.3e} per-head max {vec_e:.3e}")
     assert tok <= TOL_VS_EXACT[fmt]
     gu.assert_copy(y_gpu, y_emul, fmt)
+    layer.close()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("P,N,H,G,L,io", [(64, 64, 4, 2, 5, "bf16"), (64, 64, 8, 2, 5, "f32"),
+                                          (128, 128, 4, 2, 8, "bf16"), (16, 16, 6, 3, 4, "bf16")])
+def test_shared_ragged(fmt, P, N, H, G, L, io):
+    """Shared checkpoint (the copy is the only state), ragged shapes with a
+    non-zero start: append / decode / flush(L) for 3L+2 steps against the
+    oracle's shared emulation.  Two heads of a group fold in one workgroup
+    here (H/G = 2 or 4), each wavefront staging its rows through its own LDS
+    buffer; a read-back that ran ahead of another lane's writes left old
+    codes in the copy after the first fold."""
+    w = synth.Workload(batch=5, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype=io,
+                       config=synth.CONFIG_ID["misc"], layer=300 + P + L)
+    T = 3 * L + 2
+    gu.note(f"shared ragged {fmt} {w}")
+    S0 = synth.checkpoint_state(w, scale=0.5)
+    dev = gu.DevInputs(w, 0, T)
+    layer = _layer(w, read_copy=fmt, shared_lowp=True)
+    layer.load_checkpoint(gu.to_dev(S0))
+    y = torch.empty((T, w.batch, H, P), dtype=torch.float32, device=gu.DEV)
+    for t in range(T):
+        layer.append(1, *dev.step(t))
+        layer.decode(y[t])
+        layer.flush(L)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = gu.oracle_inputs(w, 0, T, list(range(w.batch)))
+    y_emul = runs.shared(x, S0.astype(np.float64).copy(), L, fmt)
+    gu.assert_copy(y.cpu().numpy(), y_emul, fmt, f"shared {fmt} P={P} N={N}")
     layer.close()
 
 
