@@ -6,7 +6,8 @@ its Python binding) never imports, links or calls it, and the two share no
 code: the only thing both sides consume is the seeded inputs from ``synth``.
 
 Contents
-  core     float64 eager recurrence and the storage quantisers (plain C,
+  core     float64 eager recurrences (Mamba-2's and the gated delta rule's)
+           and the storage quantisers (plain C,
            ``replay_oracle.c``, loaded with ctypes; built with gcc on first use)
   forms    the history / checkpoint / output-only rewritings and the segment
            decay, written from their definitions (self-check forms)
@@ -16,9 +17,9 @@ Contents
 
 Parity status of every function is listed in its module docstring.
 """
-from .core import (build, lib, threads, set_threads, widen, eager, bf16_encode, bf16_decode,
+from .core import (build, lib, threads, set_threads, widen, eager, eager_gdn, bf16_encode, bf16_decode,
                    e4m3_encode, e4m3_decode, quant_heads_e4m3)
 from . import forms, ring, runs
 
-__all__ = ["build", "lib", "threads", "set_threads", "widen", "eager", "bf16_encode", "bf16_decode",
+__all__ = ["build", "lib", "threads", "set_threads", "widen", "eager", "eager_gdn", "bf16_encode", "bf16_decode",
            "e4m3_encode", "e4m3_decode", "quant_heads_e4m3", "forms", "ring", "runs"]

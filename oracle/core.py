@@ -47,6 +47,8 @@ def lib():
             L = ctypes.CDLL(_SO)
             L.oracle_eager.argtypes = [_I64] * 6 + [_F64P] * 7
             L.oracle_eager.restype = None
+            L.oracle_eager_gdn.argtypes = [_I64] * 6 + [_F64P] * 7
+            L.oracle_eager_gdn.restype = None
             L.oracle_threads.restype = ctypes.c_int
             L.oracle_set_threads.argtypes = [ctypes.c_int]
             L.oracle_bf16_encode_n.argtypes = [_F32P, _U16P, _I64]
@@ -180,4 +182,25 @@ def eager(S: np.ndarray, q, k, v, dt, a) -> np.ndarray:
     if T == 0 or B == 0:
         return y
     lib().oracle_eager(T, B, H, G, P, N, *[_p(x, _F64P) for x in args], _p(S, _F64P), _p(y, _F64P))
+    return y
+
+
+def eager_gdn(S: np.ndarray, q, k, v, beta, alpha) -> np.ndarray:
+    """Run the gated delta rule (replay_oracle.c oracle_eager_gdn) in float64
+    over T tokens: S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+    y_t = S_t q_t.  Shapes as eager(), beta and alpha in the dt and a slots.
+    The pages name Gated DeltaNet without its equation; this is the published
+    rule (Yang et al., ICLR 2025), pinned by tests/test_oracle_gdn.py."""
+    assert S.dtype == np.float64 and S.flags.c_contiguous
+    T, B, G, N = q.shape
+    H, P = v.shape[2], v.shape[3]
+    assert S.shape == (B, H, P, N), (S.shape, (B, H, P, N))
+    assert k.shape == q.shape and v.shape == (T, B, H, P)
+    assert beta.shape == (T, B, H) and alpha.shape == (T, B, H)
+    assert H % G == 0
+    args = [np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, beta, alpha)]
+    y = np.empty((T, B, H, P), dtype=np.float64)
+    if T == 0 or B == 0:
+        return y
+    lib().oracle_eager_gdn(T, B, H, G, P, N, *[_p(x, _F64P) for x in args], _p(S, _F64P), _p(y, _F64P))
     return y

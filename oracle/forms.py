@@ -91,3 +91,61 @@ def output_only_form(S0, q, v, k, dt, a):
             yt = yt + s[t - 1][j - 1] * v[j - 1] * float(k[j - 1] @ qt)
         y[t - 1] = yt
     return y
+
+
+# ---------------------------------------------------------------------------
+# Gated DeltaNet (the gated delta rule of core.eager_gdn).  The pages name the
+# layer and say the replay was built for it, without its equation; these are
+# the checkpoint-plus-buffer rewritings of the published rule (Yang et al.,
+# ICLR 2025), derived by unrolling it -- the reading recorded for this layer:
+#
+#   transition  A_m = alpha_m (I - beta_m k_m k_m^T)        (N x N)
+#   S_t = S0 A_1 A_2 ... A_t + sum_{j=1..t} beta_j v_j k_j^T A_{j+1} ... A_t
+#
+# and, applied to q_t from the right without forming S_t (the output-only
+# route of this layer): with w_t = q_t and w_{m-1} = A_m w_m for m = t..1,
+#
+#   y_t = S0 w_0 + sum_{j=1..t} beta_j v_j (k_j . w_j)
+#
+# A_m w = alpha_m (w - beta_m (k_m . w) k_m) costs 2N per entry, so the chain
+# is cheap next to the one pass over S0.
+
+def gdn_transition(k, beta, alpha):
+    """A = alpha (I - beta k k^T) as an explicit N x N matrix."""
+    k = np.asarray(k, dtype=np.float64)
+    return alpha * (np.eye(len(k)) - beta * np.outer(k, k))
+
+
+def gdn_product_form(S0, v, k, beta, alpha):
+    """Buffer entries 1..c after checkpoint S0, by explicit matrix products.
+    v [c][P], k [c][N], beta, alpha [c] -> S [c][P][N] (S_t, t = 1..c)."""
+    c = len(alpha)
+    out = np.zeros((c,) + S0.shape)
+    for t in range(1, c + 1):
+        prod = np.eye(S0.shape[1])
+        for m in range(1, t + 1):
+            prod = prod @ gdn_transition(k[m - 1], beta[m - 1], alpha[m - 1])
+        St = S0 @ prod
+        for j in range(1, t + 1):
+            tail = np.eye(S0.shape[1])
+            for m in range(j + 1, t + 1):
+                tail = tail @ gdn_transition(k[m - 1], beta[m - 1], alpha[m - 1])
+            St = St + beta[j - 1] * np.outer(v[j - 1], k[j - 1]) @ tail
+        out[t - 1] = St
+    return out
+
+
+def gdn_output_only_form(S0, q, v, k, beta, alpha):
+    """y_t for buffer entries t = 1..c by the backward chain, never forming
+    S_t or a transition matrix.  q [c][N] -> y [c][P]."""
+    c = len(alpha)
+    y = np.zeros((c, v.shape[1]))
+    for t in range(1, c + 1):
+        w = np.array(q[t - 1], dtype=np.float64)
+        yt = np.zeros(v.shape[1])
+        for m in range(t, 0, -1):
+            d = float(k[m - 1] @ w)                   # k_m . w_m
+            yt = yt + beta[m - 1] * d * v[m - 1]
+            w = alpha[m - 1] * (w - beta[m - 1] * d * k[m - 1])   # w_{m-1} = A_m w_m
+        y[t - 1] = yt + S0 @ w
+    return y

@@ -89,6 +89,55 @@ void oracle_eager(int64_t T, int64_t B, int64_t H, int64_t G, int64_t P, int64_t
     }
 }
 
+/*
+ * Gated DeltaNet layers (the second layer type the pages name beside Mamba-2:
+ * page "ReplaySSM: Cache SSM Inputs, Not State", Abstract; page "ReplaySSM:
+ * que cambia en los modelos hibridos de IA", section "Una integracion
+ * concreta no cubre todas las opciones").  The pages print no equation for
+ * it; this is the published gated delta rule (Yang, Kautz, Hatamizadeh,
+ * "Gated Delta Networks: Improving Mamba2 with Delta Rule", ICLR 2025), with
+ * S a P x N (value x key) matrix per (sequence, head):
+ *
+ *   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *   y_t = S_t q_t
+ *
+ * Row p of S (s, in R^N) therefore takes
+ *   s <- alpha_t (s - beta_t (s . k_t) k_t) + beta_t v_t[p] k_t
+ * with (s . k_t) taken on the row before the update.  Layout as
+ * oracle_eager; the dt slot carries beta_t and the a slot alpha_t.
+ */
+void oracle_eager_gdn(int64_t T, int64_t B, int64_t H, int64_t G, int64_t P, int64_t N,
+                      const double *q, const double *k, const double *v,
+                      const double *beta, const double *alpha, double *S, double *y)
+{
+    int64_t bh;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (bh = 0; bh < B * H; ++bh) {
+        const int64_t b = bh / H, h = bh % H;
+        const int64_t g = (h * G) / H;
+        double *St = S + bh * P * N;
+        for (int64_t t = 0; t < T; ++t) {
+            const double al = alpha[(t * B + b) * H + h];
+            const double be = beta[(t * B + b) * H + h];
+            const double *vt = v + ((t * B + b) * H + h) * P;
+            const double *kt = k + ((t * B + b) * G + g) * N;
+            const double *qt = q + ((t * B + b) * G + g) * N;
+            double *yt = y + ((t * B + b) * H + h) * P;
+            for (int64_t p = 0; p < P; ++p) {
+                double *row = St + p * N;
+                double sk = 0.0;
+                for (int64_t n = 0; n < N; ++n) sk += row[n] * kt[n];
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    row[n] = al * (row[n] - be * sk * kt[n]) + be * vt[p] * kt[n];
+                    acc += row[n] * qt[n];
+                }
+                yt[p] = acc;
+            }
+        }
+    }
+}
+
 /* Threads the OpenMP runtime will use for oracle_eager. */
 int oracle_threads(void)
 {

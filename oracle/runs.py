@@ -5,7 +5,8 @@ keeps; the ring and the checkpoint never appear (the pages state the
 rewriting does not change the result: page "ReplaySSM: Cachear Inputs, No
 Estado", sections "La solucion" and "Conclusion").
 
-* standard decode: one token per step, output y_t = S_t q_t.
+* standard decode: one token per step, output y_t = S_t q_t.  Every
+  schedule takes rule="ssd" (Mamba-2) or rule="gdn" (the gated delta rule).
 * speculative verify (same page, section "Como funciona en la practica",
   "Rollback" and "Paralelismo"; abstract page, Abstract): a round drafts W
   tokens, all W outputs are produced from the state before the round, and
@@ -51,23 +52,30 @@ def _rows(x: dict, t0: int, t1: int, seqs=None) -> dict:
     return {k: v[t0:t1][:, seqs] for k, v in x.items()}
 
 
-def standard(x: dict, S: np.ndarray) -> np.ndarray:
+def _eager(rule: str):
+    """The eager recurrence of a layer type: "ssd" (Mamba-2, core.eager) or
+    "gdn" (the gated delta rule, core.eager_gdn; dt slot beta, a slot alpha)."""
+    return {"ssd": core.eager, "gdn": core.eager_gdn}[rule]
+
+
+def standard(x: dict, S: np.ndarray, rule: str = "ssd") -> np.ndarray:
     """Eager over all rows of x; S float64 [B][H][P][N] updated in place."""
-    return core.eager(S, x["q"], x["k"], x["v"], x["dt"], x["a"])
+    return _eager(rule)(S, x["q"], x["k"], x["v"], x["dt"], x["a"])
 
 
-def verify_rounds(x: dict, accept: np.ndarray, W: int, S: np.ndarray) -> np.ndarray:
+def verify_rounds(x: dict, accept: np.ndarray, W: int, S: np.ndarray, rule: str = "ssd") -> np.ndarray:
     """Rounds of W drafts.  x holds R*W rows (round r uses rows rW..rW+W-1),
     accept int [R][B] accepted drafts per round and sequence.
     Returns y float64 [R][W][B][H][P]; S ends as the state after the
     accepted prefix of every round."""
+    eager = _eager(rule)
     R = accept.shape[0]
     B, H, P, N = S.shape
     y = np.empty((R, W, B, H, P))
     for r in range(R):
         rows = _rows(x, r * W, r * W + W)
         S_try = S.copy()
-        y[r] = core.eager(S_try, rows["q"], rows["k"], rows["v"], rows["dt"], rows["a"])
+        y[r] = eager(S_try, rows["q"], rows["k"], rows["v"], rows["dt"], rows["a"])
         for c in range(0, W + 1):
             sel = np.nonzero(accept[r] == c)[0]
             if len(sel) == 0 or c == 0:
@@ -77,7 +85,7 @@ def verify_rounds(x: dict, accept: np.ndarray, W: int, S: np.ndarray) -> np.ndar
                 continue
             Sc = np.ascontiguousarray(S[sel])
             sub = {k: v[:c][:, sel] for k, v in rows.items()}
-            core.eager(Sc, sub["q"], sub["k"], sub["v"], sub["dt"], sub["a"])
+            eager(Sc, sub["q"], sub["k"], sub["v"], sub["dt"], sub["a"])
             S[sel] = Sc
     return y
 

@@ -42,10 +42,10 @@ GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-TENSOR = {"A": 0, "q": 1, "k": 2, "v": 3, "dt": 4, "accept": 5, "S0": 6}
+TENSOR = {"A": 0, "q": 1, "k": 2, "v": 3, "dt": 4, "accept": 5, "S0": 6, "beta": 7}
 
 # workload ids used in the keys (one per named workload)
-CONFIG_ID = {"tiny": 0, "decode": 1, "verify": 2, "dual": 3, "stacked": 4, "misc": 9}
+CONFIG_ID = {"tiny": 0, "decode": 1, "verify": 2, "dual": 3, "stacked": 4, "gdn": 5, "misc": 9}
 
 
 def _mix64(z: np.ndarray) -> np.ndarray:
@@ -224,6 +224,9 @@ def named(name: str, **over) -> Workload:
         "dual": dict(batch=256, heads=128, groups=8, head_dim=64, state_dim=128, ring_len=16, io_dtype="bf16"),
         # stacked sweep: 8 layers, B=512 H=64 G=8 P=128 N=128, L in {8,16,32}
         "stacked": dict(batch=512, heads=64, groups=8, head_dim=128, state_dim=128, ring_len=16, io_dtype="bf16"),
+        # Gated DeltaNet layer (the pages give no shape): 32 value heads over 16 key heads,
+        # P = N = 128, B=256, L=16, bf16 q/k/v (gdn_inputs)
+        "gdn": dict(batch=256, heads=32, groups=16, head_dim=128, state_dim=128, ring_len=16, io_dtype="bf16"),
     }[name]
     base.update(over)
     base.setdefault("config", CONFIG_ID[name])
@@ -333,6 +336,46 @@ def step_inputs_torch(w: Workload, t0: int, t1: int, device="cuda") -> dict:
     io = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
     return {"q": q.to(torch.float32).to(io), "k": k.to(torch.float32).to(io),
             "v": v.to(torch.float32).to(io), "dt": dt32, "a": a32}
+
+
+def gdn_inputs(w: Workload, t0: int, t1: int, seqs=None) -> dict:
+    """Inputs of a Gated DeltaNet layer, same layout and streams as
+    step_inputs: q and k are the step_inputs draws scaled to unit length per
+    (token, sequence, group) row (in float64, then stored); v as
+    step_inputs; the dt slot carries beta = sigmoid(x), x ~ N(0, 1) (stream
+    "beta"), and the a slot the step_inputs decay a in (0, 1) as alpha."""
+    x = step_inputs(w, t0, t1, seqs)
+    out = dict(x)
+    for name in ("q", "k"):
+        raw = _unstore(x[name], w.io_dtype)
+        out[name] = store(raw / np.linalg.norm(raw, axis=-1, keepdims=True), w.io_dtype)
+    B, H = w.batch, w.heads
+    ts = np.arange(t0, t1, dtype=np.int64)
+    bs = np.arange(B, dtype=np.int64) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    ib = _flat_index([1 << 40, B, H], [ts, bs, np.arange(H)])
+    out["dt"] = (1.0 / (1.0 + np.exp(-normal(w.key("beta"), ib)))).astype(np.float32)
+    return out
+
+
+def _unstore(x: np.ndarray, io_dtype: str) -> np.ndarray:
+    """Storage array -> float64 values (bf16 patterns widened)."""
+    if io_dtype == "bf16":
+        return (np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def gdn_inputs_torch(w: Workload, t0: int, t1: int, device="cuda") -> dict:
+    """gdn_inputs evaluated on `device` (as step_inputs_torch)."""
+    import torch
+    x = step_inputs_torch(w, t0, t1, device)
+    out = dict(x)
+    for name in ("q", "k"):
+        raw = x[name].to(torch.float64)
+        out[name] = (raw / torch.linalg.vector_norm(raw, dim=-1, keepdim=True)).to(torch.float32).to(x[name].dtype)
+    B, H = w.batch, w.heads
+    ib = _t_index([1 << 40, B, H], [np.arange(t0, t1), np.arange(B), np.arange(H)], device)
+    out["dt"] = torch.sigmoid(_t_normal(w.key("beta"), ib)).to(torch.float32)
+    return out
 
 
 def to_storage(t) -> np.ndarray:
