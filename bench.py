@@ -151,21 +151,21 @@ def input_pool(w, nsteps, t0=0):
     return synth.step_inputs_torch(w, t0, t0 + nsteps, device="cuda")
 
 
-def cpu_baseline(w, target_s=12.0, steps=256, chunk=32):
+def cpu_baseline(w, target_s=12.0, steps=256, chunk=32, rule="ssd"):
     """The oracle, as it stands, on a bounded sample of the workload: the
     first `nseq` sequences over all `steps` decode steps, nseq chosen from a
     short calibration so the sample takes about target_s seconds of host
     time.  Inputs are generated chunk by chunk outside the timed calls."""
     import oracle
     from oracle import runs
+    gen = synth.gdn_inputs if rule == "gdn" else synth.step_inputs
 
     def run(nseq, T, S):
         total = 0.0
         for t0 in range(0, T, chunk):
-            x = runs.widen_inputs(synth.step_inputs(w, t0, min(T, t0 + chunk), seqs=list(range(nseq))),
-                                  w.io_dtype)
+            x = runs.widen_inputs(gen(w, t0, min(T, t0 + chunk), seqs=list(range(nseq))), w.io_dtype)
             c0 = time.perf_counter()
-            runs.standard(x, S)
+            runs.standard(x, S, rule=rule)
             total += time.perf_counter() - c0
         return total
 
@@ -184,7 +184,8 @@ def cpu_baseline(w, target_s=12.0, steps=256, chunk=32):
     finally:
         oracle.set_threads(cores)
     return {"value": nseq * steps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"float64 eager recurrence, first {nseq} of {w.batch} sequences x {steps} steps "
+            "sample": f"float64 eager recurrence ({'gated delta rule' if rule == 'gdn' else 'Mamba-2'}), "
+                      f"first {nseq} of {w.batch} sequences x {steps} steps "
                       f"of the same layer ({dt:.1f} s host time, input generation excluded)",
             "one_core": {"value": n1 * t1 / dt1, "unit": "tokens/s", "cores": 1,
                          "sample": f"first {n1} sequences x {t1} steps ({dt1:.1f} s host time)"}}
@@ -471,6 +472,111 @@ def bench_decode(args):
         out["cpu_baseline"] = cpu_baseline(w)
     return out
 
+
+
+# ---------------------------------------------------------------------------
+def bench_gdn(args):
+    """Gated DeltaNet layer (B=256, H=32 value heads over G=16 key heads,
+    P=N=128, L=16, bf16 q/k/v, float32 checkpoint; unit-length q, k, sigmoid
+    beta): standard decode through replay_step (append, the output-only
+    route -- the backward chain over the ring and one pass over S0 -- and
+    the fold when the ring is full), against the layer's eager step
+    (S_t written every token) on the same inputs.  The roofline pass runs one
+    more window as separate calls with HIP events around each output-only
+    launch and the fold."""
+    import torch
+    import linear_attention_decode_amd as lad
+
+    w = synth.named("gdn")
+    B, H, G, P, N, L = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len
+    pool = synth.gdn_inputs_torch(w, 0, POOL_STEPS, device="cuda")
+    layer = lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16", rule="gdn")
+    y = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def args_t(t):
+        i = t % POOL_STEPS
+        return (pool["q"][i], pool["k"][i], pool["v"][i], pool["dt"][i], pool["a"][i])
+
+    for t in range(args.warmup):
+        layer.step(*args_t(t), y, flush_at=L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        layer.step(*args_t(args.warmup + k), y, flush_at=L)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # roofline pass: to the next window start, then `reps` windows as calls
+    t = args.warmup + args.steps
+    while t % L != 0:
+        layer.step(*args_t(t), y, flush_at=L)
+        t += 1
+    reps = max(1, args.roofline_windows)
+    dec_ev, fold_ev = _events(reps * L), _events(reps)
+    for i in range(reps * L):
+        layer.append(1, *args_t(t + i))
+        dec_ev[i][0].record(stream)
+        layer.decode(y)
+        dec_ev[i][1].record(stream)
+        if (i + 1) % L == 0:
+            fold_ev[i // L][0].record(stream)
+            layer.flush(L)
+            fold_ev[i // L][1].record(stream)
+    torch.cuda.synchronize()
+    word, _ = layer.get_error()
+    assert word == 0, f"device error bits {word}"
+    dec_s = sum(e[0].elapsed_time(e[1]) for e in dec_ev) / 1e3
+    fold_s = sum(e[0].elapsed_time(e[1]) for e in fold_ev) / 1e3
+    dec_bytes = reps * sum(decode_bytes(w, c) for c in range(1, L + 1))
+    fold_bytes = reps * flush_bytes(w, L)
+    achieved = dec_bytes / dec_s / 1e9
+    layer.close()
+    del layer
+    torch.cuda.empty_cache()
+
+    # the layer's eager step on the same inputs
+    cfg = lad.ReplayConfig(B, H, G, P, N, L, lad.BF16, lad.NONE, 0, lad.GATED_DELTA)
+    S = torch.zeros((B, H, P, N), dtype=torch.float32, device="cuda")
+    eager_out = None
+    if not args.no_eager:
+        for t in range(args.warmup):
+            lad.replay_eager_step(cfg, S, S, *args_t(t), y)
+        torch.cuda.synchronize()
+        e0 = time.perf_counter()
+        for k in range(args.steps):
+            lad.replay_eager_step(cfg, S, S, *args_t(args.warmup + k), y)
+        torch.cuda.synchronize()
+        e1 = time.perf_counter()
+        eager_out = {"value": B * args.steps / (e1 - e0), "unit": "tokens/s",
+                     "ms_per_step": 1e3 * (e1 - e0) / args.steps,
+                     "achieved_GBs": eager_bytes(w) * args.steps / (e1 - e0) / 1e9}
+    del S
+    torch.cuda.empty_cache()
+    value = B * args.steps / elapsed
+    out = {
+        "metric": "Gated DeltaNet layer decode tokens/s at B=256 + achieved HBM GB/s (% peak) vs eager",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": f"synthetic (seeded; unit-length q, k; {POOL_STEPS} distinct steps cycled)",
+        "config": {"workload": "Gated DeltaNet layer, standard decode", "batch": B, "heads": H, "groups": G,
+                   "head_dim": P, "state_dim": N, "ring_len": L, "io": "bf16", "checkpoint": "f32",
+                   "flush_every": L},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gdn_verify_kernel, W=1 (output-only: backward chain + one pass over S0)",
+                     "avg_launch_us": 1e6 * dec_s / (reps * L), "timed_launches": reps * L,
+                     "launches_from": f"{reps} windows (ring counts 1..{L}) as separate calls after the timed "
+                                      "region, each output-only launch between HIP events",
+                     "algorithmic_bytes_per_launch": dec_bytes / (reps * L),
+                     "fold": {"avg_launch_us": 1e6 * fold_s / reps, "achieved": fold_bytes / fold_s / 1e9,
+                              "frac": fold_bytes / fold_s / 1e9 / HBM_PEAK_GBS}},
+        "eager": eager_out,
+        "speedup_vs_eager": value / eager_out["value"] if eager_out else None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, rule="gdn")
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -860,7 +966,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="decode", choices=["decode", "verify", "dual", "stacked", "stacked-latency"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "verify", "dual", "stacked", "stacked-latency",
+                                                             "gdn"])
     ap.add_argument("--quick", action="store_true", help="dual/stacked: one variant only")
     ap.add_argument("--window", type=int, default=5,
                     help="verify: drafts per round (5 is the benchmarked workload; up to 16, windows past 8 "
@@ -901,7 +1008,7 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
     out = {"decode": bench_decode, "verify": bench_verify, "dual": bench_dual,
-           "stacked": bench_stacked, "stacked-latency": bench_stacked_latency}[args.workload](args)
+           "stacked": bench_stacked, "stacked-latency": bench_stacked_latency, "gdn": bench_gdn}[args.workload](args)
     print(json.dumps(out))
 
 

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define REPLAY_ABI_VERSION 6
+#define REPLAY_ABI_VERSION 7
 
 typedef enum {
     REPLAY_OK = 0,
@@ -87,6 +87,23 @@ typedef enum {
                                      head's row-major tile sharing one power-of-two scale (E8M0) */
 } replay_dtype;
 
+/* The recurrence of the layer (page "ReplaySSM: Cache SSM Inputs, Not State",
+   Abstract: the replay serves Mamba-2 and Gated DeltaNet layers).
+   MAMBA2:      S_t = a_t S_{t-1} + dt_t v_t k_t^T (page "ReplaySSM: Cachear
+                Inputs, No Estado", eq. "Forma resumen").
+   GATED_DELTA: S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+                the published gated delta rule (the pages print no equation for
+                it); every dt argument and ring slot carries beta_t, every a
+                argument and slot alpha_t.  Gated-delta layers read the float32
+                master only (read_copy REPLAY_NONE, else UNSUPPORTED), verify
+                windows up to min(8, L), and step stacked layers one call each
+                (replay_step_layers: UNSUPPORTED).
+   Both: y_t = S_t q_t. */
+typedef enum {
+    REPLAY_RULE_MAMBA2 = 0,
+    REPLAY_RULE_GATED_DELTA = 1
+} replay_rule;
+
 typedef struct {
     int32_t batch;        /* B */
     int32_t heads;        /* H */
@@ -104,6 +121,8 @@ typedef struct {
     int32_t shared_lowp;  /* 0: separated precisions (the float32 master takes every flush);
                              1: shared -- the low-precision copy is the only checkpoint and
                              each flush starts from it (needs a read_copy) */
+    int32_t rule;         /* the layer's recurrence (replay_rule): REPLAY_RULE_MAMBA2 (0,
+                             a zero-initialised config) or REPLAY_RULE_GATED_DELTA */
 } replay_config;
 
 /* Device buffers of one layer's decode state.  Sizes in elements; use

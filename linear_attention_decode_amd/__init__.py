@@ -46,7 +46,7 @@ _I32 = ctypes.c_int32
 class ReplayConfig(ctypes.Structure):
     _fields_ = [("batch", _I32), ("heads", _I32), ("groups", _I32), ("head_dim", _I32),
                 ("state_dim", _I32), ("ring_len", _I32), ("io_dtype", _I32),
-                ("read_copy", _I32), ("shared_lowp", _I32)]
+                ("read_copy", _I32), ("shared_lowp", _I32), ("rule", _I32)]
 
 
 BUFFER_FIELDS = ("s_master", "s_copy", "s_scale", "ring_q", "ring_k", "ring_v", "ring_dt",
@@ -225,6 +225,10 @@ def replay_stream_probe(mode, src, dst, nbytes, stream=None):
 # ---- one layer's state, allocated with torch -------------------------------
 
 _DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1, None: NONE, "none": NONE}
+# replay_rule: the layer's recurrence ("mamba2": S = a S + dt v k^T; "gdn": the
+# gated delta rule, dt carrying beta and a carrying alpha)
+RULE_CODE = {"mamba2": 0, "gdn": 1}
+MAMBA2, GATED_DELTA = 0, 1
 
 
 class ReplayLayer:
@@ -240,10 +244,12 @@ class ReplayLayer:
     """
 
     def __init__(self, batch, heads, groups, head_dim, state_dim, ring_len, io_dtype="bf16",
-                 read_copy=None, shared_lowp=False, device="cuda", stream=None, counters=True):
+                 read_copy=None, shared_lowp=False, device="cuda", stream=None, counters=True, rule="mamba2"):
         import torch
         self.cfg = ReplayConfig(batch, heads, groups, head_dim, state_dim, ring_len,
-                                _DTYPE_CODE[io_dtype], _DTYPE_CODE[read_copy], int(bool(shared_lowp)))
+                                _DTYPE_CODE[io_dtype], _DTYPE_CODE[read_copy], int(bool(shared_lowp)),
+                                RULE_CODE[rule])
+        self.rule = rule
         self.io_dtype = io_dtype
         self.read_copy = read_copy
         nbytes = replay_buffer_bytes(self.cfg)

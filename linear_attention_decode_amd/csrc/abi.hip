@@ -84,6 +84,7 @@ replay_status check_shape(const replay_config *c) {
     if ((int64_t)c->batch * c->heads > INT32_MAX) return REPLAY_ERR_UNSUPPORTED;
     if (!shape_supported(c->head_dim, c->state_dim)) return REPLAY_ERR_UNSUPPORTED;
     if (c->io_dtype != REPLAY_F32 && c->io_dtype != REPLAY_BF16) return REPLAY_ERR_UNSUPPORTED;
+    if (c->rule != REPLAY_RULE_MAMBA2 && c->rule != REPLAY_RULE_GATED_DELTA) return REPLAY_ERR_INVALID_ARG;
     return REPLAY_OK;
 }
 
@@ -97,6 +98,7 @@ replay_status check_config(const replay_config *c) {
         return REPLAY_ERR_UNSUPPORTED;
     if (c->shared_lowp != 0 && c->shared_lowp != 1) return REPLAY_ERR_INVALID_ARG;
     if (c->shared_lowp && c->read_copy == REPLAY_NONE) return REPLAY_ERR_INVALID_ARG;
+    if (c->rule == REPLAY_RULE_GATED_DELTA && c->read_copy != REPLAY_NONE) return REPLAY_ERR_UNSUPPORTED;
     return REPLAY_OK;
 }
 
@@ -186,7 +188,21 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
     // no sequence can be due: the kernel would change nothing
     note_capture(h, s);
     if (!load_src && !h->graphed && !h->untracked && !h->bound.flush_may_fold(min_count)) return REPLAY_OK;
-    const hipError_t e = launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s);
+    hipError_t e;
+    if (c.rule == REPLAY_RULE_GATED_DELTA && !load_src) {
+        // the gated delta rule's fold (a checkpoint load, an empty ring, is the
+        // same copy for both rules)
+        GdnFoldArgs g{};
+        g.r = a.r;
+        g.S_in = h->bufs.s_master;
+        g.S_out = h->bufs.s_master;
+        g.min_count = min_count;
+        g.base_out = h->bufs.base;
+        g.sync = sync;
+        e = launch_gdn_flush(c.head_dim, c.state_dim, g, s);
+    } else {
+        e = launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s);
+    }
     if (e != hipSuccess) {
         h->bound.unknown();
         return REPLAY_ERR_HIP;
@@ -208,6 +224,10 @@ replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
     a.scale = h->bufs.s_scale;
     a.y = y;
     a.W = W;
+    if (c.rule == REPLAY_RULE_GATED_DELTA) {
+        if (W > kMaxWindow) return REPLAY_ERR_UNSUPPORTED;
+        return from_hip(launch_gdn_verify(c.head_dim, c.state_dim, a, s));
+    }
     const int st = state_kind(c.read_copy);
     // bf16 io: the matrix-core kernel from kWideFrom on; float32 io: past the
     // register kernel's kMaxWindow
@@ -396,6 +416,13 @@ static replay_status step_impl(replay_handle *h, const void *q, const void *k, c
                                const float *a, float *y, int32_t flush_at, hipStream_t s, int32_t *sync) {
     const replay_config &c = h->cfg;
     note_capture(h, s);
+    if (c.rule == REPLAY_RULE_GATED_DELTA) {
+        // the gated delta rule: append, the output-only route, the fold if due
+        replay_status st = append_impl(h, 1, q, k, v, dt, a, s, sync);
+        if (st == REPLAY_OK) st = run_verify(h, 1, y, s);
+        if (st != REPLAY_OK) return st;
+        return run_flush(h, nullptr, flush_at, s, sync);
+    }
     const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, 1, sync);
     if (c.read_copy != REPLAY_NONE) {
         // copies: append + decode from an e4m3 or FP4 copy in one launch
@@ -463,7 +490,7 @@ replay_status replay_step_layers(replay_handle *const *layers, int32_t n, const 
         if (c.batch != c0.batch || c.heads != c0.heads || c.groups != c0.groups || c.head_dim != c0.head_dim ||
             c.state_dim != c0.state_dim || c.ring_len != c0.ring_len || c.io_dtype != c0.io_dtype)
             return REPLAY_ERR_INVALID_ARG;
-        if (c.read_copy != REPLAY_NONE) return REPLAY_ERR_UNSUPPORTED;
+        if (c.read_copy != REPLAY_NONE || c.rule != REPLAY_RULE_MAMBA2) return REPLAY_ERR_UNSUPPORTED;
         for (int j = 0; j < i; ++j)
             if (layers[j] == h) return REPLAY_ERR_INVALID_ARG;   // one layer twice in one launch would race
     }
@@ -498,7 +525,8 @@ replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, con
     hipStream_t s = as_stream(stream);
     note_capture(h, s);
     const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, W, h->bufs.sync);
-    if (c.read_copy != REPLAY_NONE && !c.shared_lowp && verify_step_copy_fused(c.head_dim, c.state_dim, sa)) {
+    if (c.read_copy != REPLAY_NONE && !c.shared_lowp && c.rule == REPLAY_RULE_MAMBA2 &&
+        verify_step_copy_fused(c.head_dim, c.state_dim, sa)) {
         // an e4m3 or FP4 read copy: fold, copy rewrite, append and verify in one launch
         const hipError_t e = launch_verify_step_copy(c.head_dim, c.state_dim, sa, s);
         if (e != hipSuccess) {
@@ -508,7 +536,7 @@ replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, con
         h->bound.verify_round(flush_at, W);
         return REPLAY_OK;
     }
-    if (c.read_copy != REPLAY_NONE || !verify_step_fused(c.head_dim, c.state_dim, sa)) {
+    if (c.read_copy != REPLAY_NONE || c.rule != REPLAY_RULE_MAMBA2 || !verify_step_fused(c.head_dim, c.state_dim, sa)) {
         // the flush, append and verify kernels in turn
         replay_status st = run_flush(h, nullptr, flush_at, s, h->bufs.sync);
         if (st != REPLAY_OK) return st;
@@ -592,6 +620,23 @@ replay_status replay_eager_step(const replay_config *cfg, const float *s_in, flo
     ea.H = cfg->heads;
     ea.G = cfg->groups;
     ea.io_bf16 = cfg->io_dtype == REPLAY_BF16;
+    if (cfg->rule == REPLAY_RULE_GATED_DELTA) {
+        GdnFoldArgs g{};
+        g.r.B = cfg->batch;
+        g.r.H = cfg->heads;
+        g.r.G = cfg->groups;
+        g.r.L = 1;
+        g.r.io_bf16 = ea.io_bf16;
+        g.S_in = s_in;
+        g.S_out = s_out;
+        g.q = q;
+        g.k = k;
+        g.v = v;
+        g.beta = dt;
+        g.alpha = a;
+        g.y = y;
+        return from_hip(launch_gdn_eager(cfg->head_dim, cfg->state_dim, g, as_stream(stream)));
+    }
     return from_hip(launch_eager(cfg->head_dim, cfg->state_dim, ea, as_stream(stream)));
 }
 

@@ -112,6 +112,27 @@ hipError_t launch_flush(int P, int N, int st_in, int st_copy, bool write_master,
                         hipStream_t s);
 // the fold of a shared checkpoint: the copy (type st) read, folded and rewritten in place
 hipError_t launch_flush_shared(int P, int N, int st, const FlushArgs &a, hipStream_t s);
+
+// Gated DeltaNet layers (gdn.hip): the output-only route (decode, W = 1, and
+// verify, W <= kMaxWindow; DecodeArgs as launch_decode with a float32
+// checkpoint), the fold of the ring into the float32 master, and the eager step.
+// Where the entries of a fold come from: the ring (flush: entries 0..count-1
+// of the sequence) or the call's one token (eager step).
+struct GdnFoldArgs {
+    RingView r;              // flush: the ring; eager: B, H, G, io_bf16 used
+    const float *S_in;
+    float *S_out;
+    int32_t min_count;       // flush: fold sequences with count >= max(min_count, 1)
+    int32_t *base_out;       // flush: base, set to pos by the last workgroup of a folded sequence
+    int32_t *sync;           // flush: arrival counters [B][G + 1][kSyncStride]
+    // eager: one token per (sequence, head)
+    const void *q, *k, *v;   // [B][G][N], [B][G][N], [B][H][P]
+    const float *beta, *alpha;   // [B][H]
+    float *y;                // [B][H][P]
+};
+hipError_t launch_gdn_verify(int P, int N, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_gdn_flush(int P, int N, const GdnFoldArgs &a, hipStream_t s);
+hipError_t launch_gdn_eager(int P, int N, const GdnFoldArgs &a, hipStream_t s);
 hipError_t launch_append(int P, int N, const RingView &r, void *ring_q, void *ring_k, void *ring_v,
                          float *ring_dt, float *ring_a, int32_t *pos, int32_t *sync, int32_t W, const void *q,
                          const void *k, const void *v, const float *dt, const float *a, hipStream_t s);

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lad):
 
 
 def test_version_and_status_strings(lad):
-    assert lad.replay_abi_version() == 6
+    assert lad.replay_abi_version() == 7
     for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "HIP"), (4, "static counters")]:
         assert text in lad.replay_status_string(s)
     assert lad.replay_status_string(99) == "unknown status"
@@ -74,6 +74,8 @@ def test_buffer_bytes_match_the_layout(lad):
     ((2, 4, 1, 64, 128, 16, 1, 7, 0), 2),           # unknown copy dtype
     ((2, 4, 1, 64, 128, 16, 1, -1, 1), 1),          # shared without a copy
     ((2, 4, 1, 64, 128, 16, 1, 3, 2), 1),           # shared flag neither 0 nor 1
+    ((2, 4, 1, 64, 128, 16, 1, -1, 0, 2), 1),       # unknown rule
+    ((2, 4, 1, 64, 128, 16, 1, 2, 0, 1), 2),        # gated delta rule with a read copy
 ])
 def test_invalid_configs_are_rejected_on_the_host(lad, fields, status):
     c = lad.ReplayConfig(*fields)

@@ -44,9 +44,13 @@ MUTANTS = {
 def _mutant_eager(tmp_path, name):
     src = open(core._SRC).read()
     old, new = MUTANTS[name]
-    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    # the mistake goes into oracle_eager only (other functions share lines with it)
+    i = src.index("void oracle_eager(")
+    j = src.index("\n}\n", i) + 3
+    body = src[i:j]
+    assert body.count(old) == 1, f"mutation site for {name} not found exactly once"
     path = tmp_path / f"{name}.c"
-    path.write_text(src.replace(old, new))
+    path.write_text(src[:i] + body.replace(old, new) + src[j:])
     so = tmp_path / f"{name}.so"
     subprocess.check_call(["gcc", "-O1", "-fPIC", "-shared", "-ffp-contract=off", "-o", str(so), str(path), "-lm"])
     L = ctypes.CDLL(str(so))
