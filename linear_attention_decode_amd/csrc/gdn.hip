@@ -39,23 +39,29 @@ namespace replay {
 // ---------------------------------------------------------------------------
 // Output-only route: decode (W = 1) and verify (W <= kMaxWindow)
 
-template <int P, int N, int WM, int LM, bool IOB>
+// PR of the head's P rows per workgroup: a 128 x 128 head is streamed by two
+// workgroups of 64 rows (4 + 1 wavefronts each; six fit a compute unit where
+// three of 8 + 1 did), each running the whole chain for its own rows.
+template <int P, int N, int WM, int LM, bool IOB, int PR = P>
 struct GdnShape {
-    using Sh = DecodeShape<P, N, ST_F32, WM>;
+    using Sh = DecodeShape<PR, N, ST_F32, WM>;
+    static constexpr int SPL = P / PR;            // workgroups a head
     static constexpr int NTS = Sh::NTS;           // streaming threads
     static constexpr int NT = NTS + 64;           // + the chain wavefront
     static constexpr int E = (N + 63) / 64;       // w elements a chain lane holds (n = lane + 64 e)
-    static constexpr int VR = (P + 63) / 64;      // outputs a chain lane accumulates (p = lane + 64 r)
+    static constexpr int VR = (PR + 63) / 64;     // outputs a chain lane accumulates (p = lane + 64 r)
+    static_assert(P % PR == 0, "whole row blocks");
 };
 
 // Rows 0..count-1 (count <= ROWS) of COLS io elements each, row j read from
-// ring row `first + ring_slot(bmod, j, L)` of `src`, widened into s[j][0..COLS): 16-byte
-// pieces (8 bf16 or 4 floats) over NTHR threads, in batches of up to 8
-// pieces a thread whose loads are all issued before any is stored (one
-// memory latency a batch, a bounded number of registers).
-template <int ROWS, int COLS, int NTHR, bool IOB>
+// elements col0 .. col0 + COLS of ring row `first + ring_slot(bmod, j, L)` of
+// `src` (rows of RS elements), widened into s[j][0..COLS): 16-byte pieces (8
+// bf16 or 4 floats) over NTHR threads, in batches of up to 8 pieces a thread
+// whose loads are all issued before any is stored (one memory latency a
+// batch, a bounded number of registers).
+template <int ROWS, int COLS, int NTHR, bool IOB, int RS = COLS>
 __device__ __forceinline__ void gdn_stage_rows(const void *src, size_t first, int bmod, int L, int count, int tid,
-                                               float (*s)[COLS]) {
+                                               float (*s)[COLS], int col0 = 0) {
     auto slot = [bmod, L](int j) { return ring_slot(bmod, j, L); };
     constexpr int PE = IOB ? 8 : 4;                        // elements a piece
     constexpr int PIECES = ROWS * COLS / PE;
@@ -70,10 +76,11 @@ __device__ __forceinline__ void gdn_stage_rows(const void *src, size_t first, in
             const int c = tid + (i0 + i) * NTHR;
             const int j = c / (COLS / PE), n = (c % (COLS / PE)) * PE;
             if (c < PIECES && j < count) {
+                const size_t e = (first + slot(j)) * RS + col0 + n;
                 if constexpr (IOB)
-                    raw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + (first + slot(j)) * COLS + n);
+                    raw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src) + e);
                 else
-                    raw[i] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(src) + (first + slot(j)) * COLS + n);
+                    raw[i] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(src) + e);
             }
         }
 #pragma unroll
@@ -112,13 +119,13 @@ __device__ __forceinline__ float gdn_wave_sum(float x) {
 }
 
 // The chain wavefront: entries 0..count-1 of (b, h); window position w is
-// entry t_w = count - W + w.  Writes s_w0[w][n] = w_0 of position w and
-// s_r[w][p] = sum_{j<=t_w} beta_j (k_j . w_j) v_j[p].
-template <int P, int N, int WM, int LM, bool IOB>
+// entry t_w = count - W + w.  Writes s_w0[w][n] = w_0 of position w and, for
+// the PR rows p0 .. p0 + PR, s_r[w][p - p0] = sum_{j<=t_w} beta_j (k_j . w_j) v_j[p].
+template <int P, int N, int WM, int LM, bool IOB, int PR>
 __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int b, int g, size_t bh, int base,
-                                               int count, int W, float (*s_k)[N], float (*s_v)[P],
-                                               float (*s_w0)[N], float (*s_r)[P]) {
-    using GS = GdnShape<P, N, WM, LM, IOB>;
+                                               int count, int W, int p0, float (*s_k)[N], float (*s_v)[PR],
+                                               float (*s_w0)[N], float (*s_r)[PR]) {
+    using GS = GdnShape<P, N, WM, LM, IOB, PR>;
     constexpr int E = GS::E, VR = GS::VR;
     const int L = r.L;
     const int bmod = base % L;
@@ -151,7 +158,7 @@ __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int 
         }
     }
     gdn_stage_rows<LM, N, 64, IOB>(r.k, gring, bmod, L, count, lane, s_k);
-    gdn_stage_rows<LM, P, 64, IOB>(r.v, hring, bmod, L, count, lane, s_v);
+    gdn_stage_rows<LM, PR, 64, IOB, P>(r.v, hring, bmod, L, count, lane, s_v, p0);
     wave_lds_sync();   // every lane's k and v rows are in LDS
 
     float acc[WM][VR];
@@ -168,7 +175,7 @@ __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int 
 #pragma unroll
             for (int e = 0; e < E; ++e) km[e] = lane + 64 * e < N ? s_k[m][lane + 64 * e] : 0.f;
 #pragma unroll
-            for (int rr = 0; rr < VR; ++rr) vm[rr] = lane + 64 * rr < P ? s_v[m][lane + 64 * rr] : 0.f;
+            for (int rr = 0; rr < VR; ++rr) vm[rr] = lane + 64 * rr < PR ? s_v[m][lane + 64 * rr] : 0.f;
 #pragma unroll
             for (int w = 0; w < WM; ++w) {
                 if (w < W && m <= count - W + w) {   // uniform
@@ -193,34 +200,37 @@ __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int 
                 if (lane + 64 * e < N) s_w0[w][lane + 64 * e] = wv[w][e];
 #pragma unroll
             for (int rr = 0; rr < VR; ++rr)
-                if (lane + 64 * rr < P) s_r[w][lane + 64 * rr] = acc[w][rr];
+                if (lane + 64 * rr < PR) s_r[w][lane + 64 * rr] = acc[w][rr];
         }
     }
 }
 
-template <int P, int N, int WM, int LM, bool IOB>
-__global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB>::NT)) void gdn_verify_kernel(DecodeArgs args) {
-    using GS = GdnShape<P, N, WM, LM, IOB>;
+template <int P, int N, int WM, int LM, bool IOB, int PR>
+__global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB, PR>::NT)) void gdn_verify_kernel(DecodeArgs args) {
+    using GS = GdnShape<P, N, WM, LM, IOB, PR>;
     using Sh = typename GS::Sh;
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
     using RR = RowReduce<ITER, LPR>;
     static_assert(VEC == 4, "float32 chunks");
 
     __shared__ __align__(16) float s_k[LM][N];
-    __shared__ __align__(16) float s_v[LM][P];
+    __shared__ __align__(16) float s_v[LM][PR];
     __shared__ __align__(16) float s_w0[WM][N];
-    __shared__ float s_r[WM][P];
+    __shared__ float s_r[WM][PR];
 
     const RingView &r = args.r;
     const int W = args.W;
+    // consecutive workgroups: the row blocks of a head, then the heads of a
+    // group (same compute die, whose L2 holds the group's k rows)
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int H = r.H;
-    const int b = lid / H, h = lid % H;
+    const int hb = lid / GS::SPL, p0 = (lid % GS::SPL) * PR;
+    const int b = hb / H, h = hb % H;
     const int g = (h * r.G) / H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t bh = (size_t)b * H + h;
-    const size_t tile = bh * (size_t)(P * N);
+    const size_t tile = bh * (size_t)(P * N) + (size_t)p0 * N;
 
     const int base = r.base[b];
     const int pos = r.pos[b];
@@ -231,11 +241,13 @@ __global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB>::NT)) void gdn_verify_
         for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
     }
     if (count < W) {   // uniform over the workgroup
-        for (int i = tid; i < W * P; i += GS::NT) args.y[(((size_t)b * W + i / P) * H + h) * P + i % P] = __builtin_nanf("");
+        for (int i = tid; i < W * PR; i += GS::NT)
+            args.y[(((size_t)b * W + i / PR) * H + h) * P + p0 + i % PR] = __builtin_nanf("");
         if (tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_TOO_FEW);
         return;
     }
-    if (wave == NTS / 64) gdn_chain_wave<P, N, WM, LM, IOB>(r, lane, b, g, bh, base, count, W, s_k, s_v, s_w0, s_r);
+    if (wave == NTS / 64)
+        gdn_chain_wave<P, N, WM, LM, IOB, PR>(r, lane, b, g, bh, base, count, W, p0, s_k, s_v, s_w0, s_r);
     __syncthreads();
     if (wave == NTS / 64) return;
 
@@ -261,18 +273,19 @@ __global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB>::NT)) void gdn_verify_
             const int p = (e + RR::FINAL * hi) * RPI + tid / LPR;
 #pragma unroll
             for (int w = 0; w < WM; ++w)
-                if (w < W) args.y[(((size_t)b * W + w) * H + h) * P + p] = part[e][w] + s_r[w][p];
+                if (w < W) args.y[(((size_t)b * W + w) * H + h) * P + p0 + p] = part[e][w] + s_r[w][p];
         }
     }
 }
 
 template <int P, int N, int WM, int LM>
 static hipError_t launch_gdn_verify_lm(const DecodeArgs &a, hipStream_t s) {
-    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
+    constexpr int PR = P == 128 ? 64 : P;
+    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H * (P / PR));
     if (a.r.io_bf16)
-        gdn_verify_kernel<P, N, WM, LM, true><<<blocks, GdnShape<P, N, WM, LM, true>::NT, 0, s>>>(a);
+        gdn_verify_kernel<P, N, WM, LM, true, PR><<<blocks, GdnShape<P, N, WM, LM, true, PR>::NT, 0, s>>>(a);
     else
-        gdn_verify_kernel<P, N, WM, LM, false><<<blocks, GdnShape<P, N, WM, LM, false>::NT, 0, s>>>(a);
+        gdn_verify_kernel<P, N, WM, LM, false, PR><<<blocks, GdnShape<P, N, WM, LM, false, PR>::NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
