@@ -94,9 +94,9 @@ typedef enum {
    GATED_DELTA: S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
                 the published gated delta rule (the pages print no equation for
                 it); every dt argument and ring slot carries beta_t, every a
-                argument and slot alpha_t.  Gated-delta layers read the float32
-                master only (read_copy REPLAY_NONE, else UNSUPPORTED), verify
-                windows up to min(8, L), and step stacked layers one call each
+                argument and slot alpha_t.  Gated-delta layers take the same
+                read copies and shared mode as Mamba-2 layers, verify windows
+                up to min(8, L), and step stacked layers one call each
                 (replay_step_layers: UNSUPPORTED).
    Both: y_t = S_t q_t. */
 typedef enum {

@@ -98,7 +98,6 @@ replay_status check_config(const replay_config *c) {
         return REPLAY_ERR_UNSUPPORTED;
     if (c->shared_lowp != 0 && c->shared_lowp != 1) return REPLAY_ERR_INVALID_ARG;
     if (c->shared_lowp && c->read_copy == REPLAY_NONE) return REPLAY_ERR_INVALID_ARG;
-    if (c->rule == REPLAY_RULE_GATED_DELTA && c->read_copy != REPLAY_NONE) return REPLAY_ERR_UNSUPPORTED;
     return REPLAY_OK;
 }
 
@@ -194,12 +193,15 @@ replay_status run_flush(replay_handle *h, const float *load_src, int32_t min_cou
         // same copy for both rules)
         GdnFoldArgs g{};
         g.r = a.r;
-        g.S_in = h->bufs.s_master;
-        g.S_out = h->bufs.s_master;
+        g.S_in = a.S_in;
+        g.scale_in = a.scale_in;
+        g.S_out = a.S_out;
+        g.copy_out = a.copy_out;
+        g.scale_out = a.scale_out;
         g.min_count = min_count;
         g.base_out = h->bufs.base;
         g.sync = sync;
-        e = launch_gdn_flush(c.head_dim, c.state_dim, g, s);
+        e = launch_gdn_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, g, s);
     } else {
         e = launch_flush(c.head_dim, c.state_dim, st_in, st_copy, !c.shared_lowp, a, s);
     }
@@ -224,11 +226,11 @@ replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
     a.scale = h->bufs.s_scale;
     a.y = y;
     a.W = W;
+    const int st = state_kind(c.read_copy);
     if (c.rule == REPLAY_RULE_GATED_DELTA) {
         if (W > kMaxWindow) return REPLAY_ERR_UNSUPPORTED;
-        return from_hip(launch_gdn_verify(c.head_dim, c.state_dim, a, s));
+        return from_hip(launch_gdn_verify(c.head_dim, c.state_dim, st, a, s));
     }
-    const int st = state_kind(c.read_copy);
     // bf16 io: the matrix-core kernel from kWideFrom on; float32 io: past the
     // register kernel's kMaxWindow
     const int wide_from = c.io_dtype == REPLAY_BF16 ? kWideFrom : kMaxWindow + 1;

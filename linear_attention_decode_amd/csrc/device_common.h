@@ -94,6 +94,25 @@ __device__ __forceinline__ uint32_t f32x4_to_fp8(float a, float b, float c, floa
     return (uint32_t)w;
 }
 
+// MX FP4 block of 32 values whose largest magnitude is amax: the E8M0
+// exponent se of its scale X = 2^se = 2^(floor(log2 amax) - 2), clamped to
+// the format's range; -127 for an all-zero block.
+__device__ __forceinline__ int mxfp4_block_exp(float amax) {
+    if (!(amax > 0.f)) return -127;
+    int ex;
+    (void)frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1)
+    return ex - 3 < -127 ? -127 : (ex - 3 > 127 ? 127 : ex - 3);
+}
+
+// Four values of a block with exponent se -> two bytes of E2M1 codes of
+// value / 2^se (the division exact by ldexp; the hardware conversion rounds
+// to nearest even and saturates at 6), first value in the low nibble.
+__device__ __forceinline__ uint16_t mxfp4_codes4(float a, float b, float c, float d, int se) {
+    const uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(a, -se), ldexpf(b, -se), 1.0f, 0);
+    const uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(c, -se), ldexpf(d, -se), 1.0f, 0);
+    return (uint16_t)((lo & 0xffu) | ((hi & 0xffu) << 8));
+}
+
 // ---- io loads (q, k, v: float32 or bf16, fixed at compile time) ----------
 // Load 4 consecutive io elements starting at element index `i` (i % 4 == 0).
 template <bool BF16>

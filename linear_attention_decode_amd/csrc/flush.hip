@@ -249,16 +249,9 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
             float amax = fmaxf(fmaxf(fabsf(x[i][0]), fabsf(x[i][1])), fmaxf(fabsf(x[i][2]), fabsf(x[i][3])));
 #pragma unroll
             for (int bit = 2; bit >= 0; --bit) amax = fmaxf(amax, lane_partner(amax, bit));
-            int se = -127;
-            if (amax > 0.f) {
-                int ex;
-                (void)frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1)
-                se = ex - 3 < -127 ? -127 : (ex - 3 > 127 ? 127 : ex - 3);
-            }
-            const uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[i][0], -se), ldexpf(x[i][1], -se), 1.0f, 0);
-            const uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[i][2], -se), ldexpf(x[i][3], -se), 1.0f, 0);
+            const int se = mxfp4_block_exp(amax);
             const size_t e0 = tile + (size_t)(i * NT + tid) * VEC;
-            *reinterpret_cast<uint16_t *>(cp + e0 / 2) = (uint16_t)((lo & 0xffu) | ((hi & 0xffu) << 8));
+            *reinterpret_cast<uint16_t *>(cp + e0 / 2) = mxfp4_codes4(x[i][0], x[i][1], x[i][2], x[i][3], se);
             if ((tid & 7) == 0) scl[e0 / 32] = (uint8_t)(se + 127);
         }
     }

@@ -298,20 +298,11 @@ __global__ __launch_bounds__(P / 16 * 64) void flush_shared_kernel(FlushArgs arg
                 amax = fmaxf(amax, lane_partner(amax, 5));
                 amax = fmaxf(amax, lane_partner(amax, 4));
                 if constexpr (N < 32) amax = fmaxf(amax, lane_partner(amax, 0));
-                int se = -127;
-                if (amax > 0.f) {
-                    int ex;
-                    (void)frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1)
-                    se = ex - 3 < -127 ? -127 : (ex - 3 > 127 ? 127 : ex - 3);
-                }
+                const int se = mxfp4_block_exp(amax);
 #pragma unroll
                 for (int t = 0; t < TPB; ++t) {
                     const f32x4 x = acc[TPB * bb + t];
-                    const uint32_t lo =
-                        __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[0], -se), ldexpf(x[1], -se), 1.0f, 0);
-                    const uint32_t hi =
-                        __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[2], -se), ldexpf(x[3], -se), 1.0f, 0);
-                    code[TPB * bb + t][0] = (lo & 0xffu) | ((hi & 0xffu) << 8);
+                    code[TPB * bb + t][0] = mxfp4_codes4(x[0], x[1], x[2], x[3], se);
                 }
                 const bool first = lg == 0 && (N >= 32 || (lr & 1) == 0);
                 if (first) scl[(rowe + 16 * TPB * bb) / 32] = (uint8_t)(se + 127);

@@ -42,9 +42,9 @@ namespace replay {
 // PR of the head's P rows per workgroup: a 128 x 128 head is streamed by two
 // workgroups of 64 rows (4 + 1 wavefronts each; six fit a compute unit where
 // three of 8 + 1 did), each running the whole chain for its own rows.
-template <int P, int N, int WM, int LM, bool IOB, int PR = P>
+template <int P, int N, int WM, int LM, bool IOB, int PR = P, int ST = ST_F32>
 struct GdnShape {
-    using Sh = DecodeShape<PR, N, ST_F32, WM>;
+    using Sh = DecodeShape<PR, N, ST, WM>;
     static constexpr int SPL = P / PR;            // workgroups a head
     static constexpr int NTS = Sh::NTS;           // streaming threads
     static constexpr int NT = NTS + 64;           // + the chain wavefront
@@ -205,13 +205,18 @@ __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int 
     }
 }
 
-template <int P, int N, int WM, int LM, bool IOB, int PR>
-__global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB, PR>::NT)) void gdn_verify_kernel(DecodeArgs args) {
-    using GS = GdnShape<P, N, WM, LM, IOB, PR>;
+// ST: the state the outputs read -- the float32 checkpoint, or a bf16 / e4m3
+// / MX FP4 copy of it (page "ReplaySSM: Cache SSM Inputs, Not State",
+// Abstract: a low-precision checkpoint serves the outputs).  A copy's values
+// are widened exactly and dotted with the float32 w_0; e4m3 sums take the
+// head's scale, FP4 sums each chunk's block scale (exact powers of two).
+template <int P, int N, int WM, int LM, bool IOB, int PR, int ST>
+__global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB, PR, ST>::NT)) void gdn_verify_kernel(DecodeArgs args) {
+    using GS = GdnShape<P, N, WM, LM, IOB, PR, ST>;
     using Sh = typename GS::Sh;
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
     using RR = RowReduce<ITER, LPR>;
-    static_assert(VEC == 4, "float32 chunks");
+    static_assert(ST != ST_F32 || VEC == 4, "float32 chunks");
 
     __shared__ __align__(16) float s_k[LM][N];
     __shared__ __align__(16) float s_v[LM][PR];
@@ -235,10 +240,15 @@ __global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB, PR>::NT)) void gdn_ver
     const int base = r.base[b];
     const int pos = r.pos[b];
     const int count = pos - base;
-    Chunk<ST_F32, VEC> ch[ITER];
+    Chunk<ST, VEC> ch[ITER];
     if (wave < NTS / 64) {
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
+        for (int i = 0; i < ITER; ++i) {
+            if constexpr (ST == ST_FP4)
+                ch[i].load_mx(args.S, args.scale, tile + (size_t)(i * NTS + tid) * VEC);
+            else
+                ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
+        }
     }
     if (count < W) {   // uniform over the workgroup
         for (int i = tid; i < W * PR; i += GS::NT)
@@ -255,17 +265,41 @@ __global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB, PR>::NT)) void gdn_ver
     // the row reduction across the LPR lanes of a row
     const int col0 = (tid % LPR) * VEC;
     float part[ITER][WM];
+    if constexpr (ST == ST_F32) {
 #pragma unroll
-    for (int w = 0; w < WM; ++w) {
-        f32x4 q = {0.f, 0.f, 0.f, 0.f};
-        if (w < W) q = *reinterpret_cast<const f32x4 *>(&s_w0[w][col0]);
+        for (int w = 0; w < WM; ++w) {
+            f32x4 q = {0.f, 0.f, 0.f, 0.f};
+            if (w < W) q = *reinterpret_cast<const f32x4 *>(&s_w0[w][col0]);
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                const f32x4 x = ch[i].raw;
+                part[i][w] = fmaf(x.x, q.x, fmaf(x.y, q.y, fmaf(x.z, q.z, x.w * q.w)));
+            }
+        }
+    } else {
 #pragma unroll
         for (int i = 0; i < ITER; ++i) {
-            const f32x4 x = ch[i].raw;
-            part[i][w] = fmaf(x.x, q.x, fmaf(x.y, q.y, fmaf(x.z, q.z, x.w * q.w)));
+            float x[VEC];
+            ch[i].widen(x, 1.0f);   // the codes' values, unscaled
+#pragma unroll
+            for (int w = 0; w < WM; ++w) {
+                float acc = 0.f;
+#pragma unroll
+                for (int e4 = 0; e4 < VEC / 4; ++e4) {
+                    f32x4 q = {0.f, 0.f, 0.f, 0.f};
+                    if (w < W) q = *reinterpret_cast<const f32x4 *>(&s_w0[w][col0 + 4 * e4]);
+                    acc = fmaf(x[4 * e4], q.x, acc);
+                    acc = fmaf(x[4 * e4 + 1], q.y, acc);
+                    acc = fmaf(x[4 * e4 + 2], q.z, acc);
+                    acc = fmaf(x[4 * e4 + 3], q.w, acc);
+                }
+                if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
+                part[i][w] = acc;
+            }
         }
     }
     RR::template run<WM>(part, lane);
+    const float sc = ST == ST_FP8 ? static_cast<const float *>(args.scale)[bh] : 1.0f;   // the head's e4m3 scale
     if (RR::writer(lane)) {
         const int hi = RR::halving_index(lane);
 #pragma unroll
@@ -273,41 +307,54 @@ __global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB, PR>::NT)) void gdn_ver
             const int p = (e + RR::FINAL * hi) * RPI + tid / LPR;
 #pragma unroll
             for (int w = 0; w < WM; ++w)
-                if (w < W) args.y[(((size_t)b * W + w) * H + h) * P + p0 + p] = part[e][w] + s_r[w][p];
+                if (w < W) args.y[(((size_t)b * W + w) * H + h) * P + p0 + p] = sc * part[e][w] + s_r[w][p];
         }
     }
 }
 
-template <int P, int N, int WM, int LM>
+template <int P, int N, int ST, int WM, int LM>
 static hipError_t launch_gdn_verify_lm(const DecodeArgs &a, hipStream_t s) {
-    constexpr int PR = P == 128 ? 64 : P;
+    // float32 tiles of 128 rows: two workgroups of 64; a copy's tiles stream
+    // in four wavefronts whole
+    constexpr int PR = P == 128 && ST == ST_F32 ? 64 : P;
     const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H * (P / PR));
     if (a.r.io_bf16)
-        gdn_verify_kernel<P, N, WM, LM, true, PR><<<blocks, GdnShape<P, N, WM, LM, true, PR>::NT, 0, s>>>(a);
+        gdn_verify_kernel<P, N, WM, LM, true, PR, ST><<<blocks, GdnShape<P, N, WM, LM, true, PR, ST>::NT, 0, s>>>(a);
     else
-        gdn_verify_kernel<P, N, WM, LM, false, PR><<<blocks, GdnShape<P, N, WM, LM, false, PR>::NT, 0, s>>>(a);
+        gdn_verify_kernel<P, N, WM, LM, false, PR, ST><<<blocks, GdnShape<P, N, WM, LM, false, PR, ST>::NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
-template <int P, int N, int WM>
+template <int P, int N, int ST, int WM>
 static hipError_t launch_gdn_verify_w(const DecodeArgs &a, hipStream_t s) {
-    if (a.r.L <= 16) return launch_gdn_verify_lm<P, N, WM, 16>(a, s);
-    return launch_gdn_verify_lm<P, N, WM, kMaxRing>(a, s);
+    if (a.r.L <= 16) return launch_gdn_verify_lm<P, N, ST, WM, 16>(a, s);
+    return launch_gdn_verify_lm<P, N, ST, WM, kMaxRing>(a, s);
+}
+
+template <int P, int N, int ST>
+static hipError_t launch_gdn_verify_st(const DecodeArgs &a, hipStream_t s) {
+    if (a.W == 1) return launch_gdn_verify_w<P, N, ST, 1>(a, s);
+    if (a.W <= 4) return launch_gdn_verify_w<P, N, ST, 4>(a, s);
+    return launch_gdn_verify_w<P, N, ST, kMaxWindow>(a, s);
 }
 
 template <int P, int N>
-static hipError_t launch_gdn_verify_pn(const DecodeArgs &a, hipStream_t s) {
-    if (a.W == 1) return launch_gdn_verify_w<P, N, 1>(a, s);
-    if (a.W <= 4) return launch_gdn_verify_w<P, N, 4>(a, s);
-    return launch_gdn_verify_w<P, N, kMaxWindow>(a, s);
+static hipError_t launch_gdn_verify_pn(int st, const DecodeArgs &a, hipStream_t s) {
+    switch (st) {
+        case ST_F32: return launch_gdn_verify_st<P, N, ST_F32>(a, s);
+        case ST_BF16: return launch_gdn_verify_st<P, N, ST_BF16>(a, s);
+        case ST_FP8: return launch_gdn_verify_st<P, N, ST_FP8>(a, s);
+        case ST_FP4: return launch_gdn_verify_st<P, N, ST_FP4>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
-hipError_t launch_gdn_verify(int P, int N, const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_gdn_verify(int P, int N, int st, const DecodeArgs &a, hipStream_t s) {
     if (a.W < 1 || a.W > kMaxWindow || a.W > a.r.L) return hipErrorInvalidValue;
-    if (P == 16 && N == 16) return launch_gdn_verify_pn<16, 16>(a, s);
-    if (P == 64 && N == 64) return launch_gdn_verify_pn<64, 64>(a, s);
-    if (P == 64 && N == 128) return launch_gdn_verify_pn<64, 128>(a, s);
-    if (P == 128 && N == 128) return launch_gdn_verify_pn<128, 128>(a, s);
+    if (P == 16 && N == 16) return launch_gdn_verify_pn<16, 16>(st, a, s);
+    if (P == 64 && N == 64) return launch_gdn_verify_pn<64, 64>(st, a, s);
+    if (P == 64 && N == 128) return launch_gdn_verify_pn<64, 128>(st, a, s);
+    if (P == 128 && N == 128) return launch_gdn_verify_pn<128, 128>(st, a, s);
     return hipErrorInvalidValue;
 }
 
@@ -330,16 +377,27 @@ struct GdnFoldShape {
     static_assert(LR % NT == 0 && NT % 64 == 0 && N % (4 * LPRW) == 0, "fold tiling");
 };
 
-template <int P, int N, bool IOB, bool EMIT>
+// SIN: the state read -- the float32 checkpoint, or (the copy being the only
+// checkpoint) a bf16 / e4m3 / MX FP4 copy, widened exactly and scaled.
+// COPY: the copy written from the folded state (-1: none), with the same
+// quantisers as the Mamba-2 flush: bf16 nearest even; e4m3 with one scale
+// per head = amax / 448 and a correctly rounded division; MX FP4 blocks of
+// 32 values (8 neighbouring lanes) with E8M0 scales.  WMASTER: the float32
+// checkpoint is written.  A shared copy is rewritten in place: every lane
+// reads its own codes (and its block's scale) before the fold and writes
+// them after, and the e4m3 scale is written after the workgroup's barrier.
+template <int P, int N, bool IOB, bool EMIT, int SIN = ST_F32, int COPY = -1, bool WMASTER = true>
 __global__ __launch_bounds__((GdnFoldShape<P, N>::NT)) void gdn_fold_kernel(GdnFoldArgs args) {
     using FS = GdnFoldShape<P, N>;
     constexpr int LPRW = FS::LPRW, PPL = FS::PPL, NT = FS::NT, RPL = FS::RPL, RSTEP = FS::RSTEP;
     constexpr int LM = EMIT ? 1 : kMaxRing;
     constexpr int RBITS = __builtin_ctz(LPRW);
+    static_assert(!EMIT || (SIN == ST_F32 && COPY < 0 && WMASTER), "the eager step reads and writes float32");
     __shared__ __align__(16) float s_k[LM][N];
     __shared__ float s_v[LM][P];
     __shared__ float s_ab[2][LM];   // alpha_m, beta_m
     __shared__ __align__(16) float s_q[EMIT ? N : 4];   // eager: the token's query
+    __shared__ float s_red[COPY == ST_FP8 ? NT / 64 : 1];
 
     const RingView &r = args.r;
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -365,14 +423,50 @@ __global__ __launch_bounds__((GdnFoldShape<P, N>::NT)) void gdn_fold_kernel(GdnF
         if (tid == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
     }
 
-    // this lane's pieces of its rows
+    // this lane's pieces of its rows (element offsets within the head's tile)
+    auto piece = [&](int i, int u) -> size_t { return (size_t)(row0 + RSTEP * i) * N + 4 * (jp + LPRW * u); };
     f32x4 s[RPL][PPL];
+    if constexpr (SIN == ST_F32) {
 #pragma unroll
-    for (int i = 0; i < RPL; ++i)
+        for (int i = 0; i < RPL; ++i)
 #pragma unroll
-        for (int u = 0; u < PPL; ++u)
-            s[i][u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(
-                args.S_in + tile + (size_t)(row0 + RSTEP * i) * N + 4 * (jp + LPRW * u)));
+            for (int u = 0; u < PPL; ++u)
+                s[i][u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4 *>(static_cast<const float *>(args.S_in) + tile + piece(i, u)));
+    } else if constexpr (SIN == ST_BF16) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int u = 0; u < PPL; ++u) {
+                const u32x2 w = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(args.S_in) + tile + piece(i, u));
+                s[i][u] = f32x4{bf16_bits_to_f32(w.x & 0xffffu), bf16_bits_to_f32(w.x >> 16),
+                                bf16_bits_to_f32(w.y & 0xffffu), bf16_bits_to_f32(w.y >> 16)};
+            }
+    } else if constexpr (SIN == ST_FP8) {
+        const float sc = static_cast<const float *>(args.scale_in)[bh];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int u = 0; u < PPL; ++u) {
+                float x[4];
+                fp8x4_to_f32(*reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(args.S_in) + tile + piece(i, u)), x);
+                s[i][u] = f32x4{x[0] * sc, x[1] * sc, x[2] * sc, x[3] * sc};
+            }
+    } else {
+        static_assert(SIN == ST_FP4, "state kind");
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int u = 0; u < PPL; ++u) {
+                const size_t e0 = tile + piece(i, u);
+                const uint32_t w = *reinterpret_cast<const uint16_t *>(static_cast<const uint8_t *>(args.S_in) + e0 / 2);
+                const int se = (int)static_cast<const uint8_t *>(args.scale_in)[e0 / 32] - 127;
+                float x[4];
+                fp4_pair_to_f32(w, 0, x);
+                fp4_pair_to_f32(w, 1, x + 2);
+                s[i][u] = f32x4{ldexpf(x[0], se), ldexpf(x[1], se), ldexpf(x[2], se), ldexpf(x[3], se)};   // exact
+            }
+    }
     // the entries: k rows, v rows, alpha and beta, staged in LDS
     auto ld = [&](const void *base_ptr, size_t i) -> float {
         if constexpr (IOB) return bf16_bits_to_f32(static_cast<const uint16_t *>(base_ptr)[i]);
@@ -431,12 +525,69 @@ __global__ __launch_bounds__((GdnFoldShape<P, N>::NT)) void gdn_fold_kernel(GdnF
             }
         }
     }
+    if constexpr (WMASTER) {
 #pragma unroll
-    for (int i = 0; i < RPL; ++i)
+        for (int i = 0; i < RPL; ++i)
 #pragma unroll
-        for (int u = 0; u < PPL; ++u)
-            __builtin_nontemporal_store(s[i][u], reinterpret_cast<f32x4 *>(
-                args.S_out + tile + (size_t)(row0 + RSTEP * i) * N + 4 * (jp + LPRW * u)));
+            for (int u = 0; u < PPL; ++u)
+                __builtin_nontemporal_store(s[i][u], reinterpret_cast<f32x4 *>(args.S_out + tile + piece(i, u)));
+    }
+    if constexpr (COPY == ST_BF16) {
+        uint16_t *cp = static_cast<uint16_t *>(args.copy_out) + tile;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int u = 0; u < PPL; ++u) {
+                u32x2 o;
+                o.x = f32x2_to_bf16_pair(s[i][u].x, s[i][u].y);
+                o.y = f32x2_to_bf16_pair(s[i][u].z, s[i][u].w);
+                *reinterpret_cast<u32x2 *>(cp + piece(i, u)) = o;
+            }
+    } else if constexpr (COPY == ST_FP8) {
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int u = 0; u < PPL; ++u)
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(s[i][u].x), fabsf(s[i][u].y)), fmaxf(fabsf(s[i][u].z), fabsf(s[i][u].w))));
+#pragma unroll
+        for (int bit = 5; bit >= 0; --bit) amax = fmaxf(amax, lane_partner(amax, bit));
+        if ((tid & 63) == 0) s_red[tid / 64] = amax;
+        __syncthreads();
+        amax = s_red[0];
+#pragma unroll
+        for (int i = 1; i < NT / 64; ++i) amax = fmaxf(amax, s_red[i]);
+        const float sig = amax > 0.f ? amax / 448.0f : 1.0f;   // correctly rounded divide
+        const ScaleDiv dv(sig);
+        uint8_t *cp = static_cast<uint8_t *>(args.copy_out) + tile;
+        dv.run([&](auto div) {
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int u = 0; u < PPL; ++u)
+                    *reinterpret_cast<uint32_t *>(cp + piece(i, u)) =
+                        f32x4_to_fp8(div(s[i][u].x), div(s[i][u].y), div(s[i][u].z), div(s[i][u].w));
+        });
+        if (tid == 0) static_cast<float *>(args.scale_out)[bh] = sig;
+    } else if constexpr (COPY == ST_FP4) {
+        // a block of 32 values is one piece of each of 8 neighbouring lanes
+        // (of one row, or of two 16-value rows)
+        uint8_t *cp = static_cast<uint8_t *>(args.copy_out);
+        uint8_t *scl = static_cast<uint8_t *>(args.scale_out);
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+#pragma unroll
+            for (int u = 0; u < PPL; ++u) {
+                const f32x4 x = s[i][u];
+                float amax = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+#pragma unroll
+                for (int bit = 2; bit >= 0; --bit) amax = fmaxf(amax, lane_partner(amax, bit));
+                const int se = mxfp4_block_exp(amax);
+                const size_t e0 = tile + piece(i, u);
+                *reinterpret_cast<uint16_t *>(cp + e0 / 2) = mxfp4_codes4(x.x, x.y, x.z, x.w, se);
+                if ((tid & 7) == 0) scl[e0 / 32] = (uint8_t)(se + 127);
+            }
+    }
     if constexpr (EMIT) {
         // y_p = S_t[p] . q (the query from the call)
         f32x4 qq[PPL];
@@ -473,32 +624,56 @@ __global__ __launch_bounds__((GdnFoldShape<P, N>::NT)) void gdn_fold_kernel(GdnF
     }
 }
 
-template <int P, int N, bool EMIT>
+template <int P, int N, bool EMIT, int SIN = ST_F32, int COPY = -1, bool WMASTER = true>
 static hipError_t launch_gdn_fold_pn(const GdnFoldArgs &a, hipStream_t s) {
     const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
     if (a.r.io_bf16)
-        gdn_fold_kernel<P, N, true, EMIT><<<blocks, GdnFoldShape<P, N>::NT, 0, s>>>(a);
+        gdn_fold_kernel<P, N, true, EMIT, SIN, COPY, WMASTER><<<blocks, GdnFoldShape<P, N>::NT, 0, s>>>(a);
     else
-        gdn_fold_kernel<P, N, false, EMIT><<<blocks, GdnFoldShape<P, N>::NT, 0, s>>>(a);
+        gdn_fold_kernel<P, N, false, EMIT, SIN, COPY, WMASTER><<<blocks, GdnFoldShape<P, N>::NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
-template <bool EMIT>
-static hipError_t launch_gdn_fold_any(int P, int N, const GdnFoldArgs &a, hipStream_t s) {
-    if (P == 16 && N == 16) return launch_gdn_fold_pn<16, 16, EMIT>(a, s);
-    if (P == 64 && N == 64) return launch_gdn_fold_pn<64, 64, EMIT>(a, s);
-    if (P == 64 && N == 128) return launch_gdn_fold_pn<64, 128, EMIT>(a, s);
-    if (P == 128 && N == 128) return launch_gdn_fold_pn<128, 128, EMIT>(a, s);
+// the fold's configurations: float32 only; separated (float32 in, float32
+// and a copy out); shared (a copy in, the same copy out)
+template <int P, int N>
+static hipError_t launch_gdn_flush_pn(int st_in, int st_copy, bool wm, const GdnFoldArgs &a, hipStream_t s) {
+    if (st_in == ST_F32 && wm) {
+        switch (st_copy) {
+            case -1: return launch_gdn_fold_pn<P, N, false>(a, s);
+            case ST_BF16: return launch_gdn_fold_pn<P, N, false, ST_F32, ST_BF16>(a, s);
+            case ST_FP8: return launch_gdn_fold_pn<P, N, false, ST_F32, ST_FP8>(a, s);
+            case ST_FP4: return launch_gdn_fold_pn<P, N, false, ST_F32, ST_FP4>(a, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (!wm && st_in == st_copy) {
+        switch (st_in) {
+            case ST_BF16: return launch_gdn_fold_pn<P, N, false, ST_BF16, ST_BF16, false>(a, s);
+            case ST_FP8: return launch_gdn_fold_pn<P, N, false, ST_FP8, ST_FP8, false>(a, s);
+            case ST_FP4: return launch_gdn_fold_pn<P, N, false, ST_FP4, ST_FP4, false>(a, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gdn_flush(int P, int N, const GdnFoldArgs &a, hipStream_t s) {
+hipError_t launch_gdn_flush(int P, int N, int st_in, int st_copy, bool write_master, const GdnFoldArgs &a,
+                            hipStream_t s) {
     if (a.r.L > kMaxRing || !a.sync || !a.base_out) return hipErrorInvalidValue;
-    return launch_gdn_fold_any<false>(P, N, a, s);
+    if (P == 16 && N == 16) return launch_gdn_flush_pn<16, 16>(st_in, st_copy, write_master, a, s);
+    if (P == 64 && N == 64) return launch_gdn_flush_pn<64, 64>(st_in, st_copy, write_master, a, s);
+    if (P == 64 && N == 128) return launch_gdn_flush_pn<64, 128>(st_in, st_copy, write_master, a, s);
+    if (P == 128 && N == 128) return launch_gdn_flush_pn<128, 128>(st_in, st_copy, write_master, a, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gdn_eager(int P, int N, const GdnFoldArgs &a, hipStream_t s) {
-    return launch_gdn_fold_any<true>(P, N, a, s);
+    if (P == 16 && N == 16) return launch_gdn_fold_pn<16, 16, true>(a, s);
+    if (P == 64 && N == 64) return launch_gdn_fold_pn<64, 64, true>(a, s);
+    if (P == 64 && N == 128) return launch_gdn_fold_pn<64, 128, true>(a, s);
+    if (P == 128 && N == 128) return launch_gdn_fold_pn<128, 128, true>(a, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace replay

@@ -120,8 +120,11 @@ hipError_t launch_flush_shared(int P, int N, int st, const FlushArgs &a, hipStre
 // of the sequence) or the call's one token (eager step).
 struct GdnFoldArgs {
     RingView r;              // flush: the ring; eager: B, H, G, io_bf16 used
-    const float *S_in;
-    float *S_out;
+    const void *S_in;        // float32 checkpoint, or (shared) the low-precision copy
+    const void *scale_in;    // shared: the copy's scales (e4m3 [B][H], FP4 one byte a block)
+    float *S_out;            // float32 checkpoint written, or null (shared)
+    void *copy_out;          // copy rewritten from the folded state, or null
+    void *scale_out;         // its scales (e4m3, FP4), or null
     int32_t min_count;       // flush: fold sequences with count >= max(min_count, 1)
     int32_t *base_out;       // flush: base, set to pos by the last workgroup of a folded sequence
     int32_t *sync;           // flush: arrival counters [B][G + 1][kSyncStride]
@@ -130,8 +133,12 @@ struct GdnFoldArgs {
     const float *beta, *alpha;   // [B][H]
     float *y;                // [B][H][P]
 };
-hipError_t launch_gdn_verify(int P, int N, const DecodeArgs &a, hipStream_t s);
-hipError_t launch_gdn_flush(int P, int N, const GdnFoldArgs &a, hipStream_t s);
+// st: the state read (ST_F32 for the master, else the copy's kind)
+hipError_t launch_gdn_verify(int P, int N, int st, const DecodeArgs &a, hipStream_t s);
+// st_in: ST_F32, or the copy's kind when the copy is the only checkpoint;
+// st_copy: the copy written (-1: none); write_master: the float32 checkpoint is written
+hipError_t launch_gdn_flush(int P, int N, int st_in, int st_copy, bool write_master, const GdnFoldArgs &a,
+                            hipStream_t s);
 hipError_t launch_gdn_eager(int P, int N, const GdnFoldArgs &a, hipStream_t s);
 hipError_t launch_append(int P, int N, const RingView &r, void *ring_q, void *ring_k, void *ring_v,
                          float *ring_dt, float *ring_a, int32_t *pos, int32_t *sync, int32_t W, const void *q,

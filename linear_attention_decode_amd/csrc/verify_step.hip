@@ -752,18 +752,9 @@ __attribute__((amdgpu_waves_per_eu(8))) void verify_step_copy_kernel(StepArgs ar
                     float amax = fmaxf(fmaxf(fabsf(x[i][0]), fabsf(x[i][1])), fmaxf(fabsf(x[i][2]), fabsf(x[i][3])));
 #pragma unroll
                     for (int bit = 2; bit >= 0; --bit) amax = fmaxf(amax, lane_partner(amax, bit));
-                    int se = -127;
-                    if (amax > 0.f) {
-                        int ex;
-                        (void)frexpf(amax, &ex);   // amax = f 2^ex, f in [0.5, 1)
-                        se = ex - 3 < -127 ? -127 : (ex - 3 > 127 ? 127 : ex - 3);
-                    }
-                    const uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[i][0], -se),
-                                                                                 ldexpf(x[i][1], -se), 1.0f, 0);
-                    const uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, ldexpf(x[i][2], -se),
-                                                                                 ldexpf(x[i][3], -se), 1.0f, 0);
+                    const int se = mxfp4_block_exp(amax);
                     const size_t e0 = (size_t)(i * NTS + tid) * MVEC;   // within the head's tile
-                    const uint16_t code = (uint16_t)((lo & 0xffu) | ((hi & 0xffu) << 8));
+                    const uint16_t code = mxfp4_codes4(x[i][0], x[i][1], x[i][2], x[i][3], se);
                     *reinterpret_cast<uint16_t *>(cp + (tile + e0) / 2) = code;
                     *reinterpret_cast<uint16_t *>(&s_code[e0 / 2]) = code;
                     if ((tid & 7) == 0) {

@@ -106,29 +106,31 @@ def quant_dequant(S: np.ndarray, fmt: str) -> np.ndarray:
     raise ValueError(fmt)
 
 
-def separated(x: dict, S: np.ndarray, L: int, fmt: str) -> np.ndarray:
+def separated(x: dict, S: np.ndarray, L: int, fmt: str, rule: str = "ssd") -> np.ndarray:
     """Outputs read from the copy of the last flushed exact state."""
+    eager = _eager(rule)
     T = x["q"].shape[0]
     S_read = quant_dequant(S, fmt)
     ys = []
     for t0 in range(0, T, L):
         rows = _rows(x, t0, min(T, t0 + L))
-        ys.append(core.eager(S_read, rows["q"], rows["k"], rows["v"], rows["dt"], rows["a"]))
-        core.eager(S, rows["q"], rows["k"], rows["v"], rows["dt"], rows["a"])
+        ys.append(eager(S_read, rows["q"], rows["k"], rows["v"], rows["dt"], rows["a"]))
+        eager(S, rows["q"], rows["k"], rows["v"], rows["dt"], rows["a"])
         if t0 + L <= T:
             S_read = quant_dequant(S, fmt)
     return np.concatenate(ys, axis=0)
 
 
-def shared(x: dict, S: np.ndarray, L: int, fmt: str) -> np.ndarray:
+def shared(x: dict, S: np.ndarray, L: int, fmt: str, rule: str = "ssd") -> np.ndarray:
     """The rounded copy is the only checkpoint: every flush starts from it.
     S ends as the (unrounded) state after the last token."""
+    eager = _eager(rule)
     T = x["q"].shape[0]
     S[...] = quant_dequant(S, fmt)
     ys = []
     for t0 in range(0, T, L):
         rows = _rows(x, t0, min(T, t0 + L))
-        ys.append(core.eager(S, rows["q"], rows["k"], rows["v"], rows["dt"], rows["a"]))
+        ys.append(eager(S, rows["q"], rows["k"], rows["v"], rows["dt"], rows["a"]))
         if t0 + L <= T:
             S[...] = quant_dequant(S, fmt)
     return np.concatenate(ys, axis=0)
@@ -144,13 +146,15 @@ def normwise_rel_err(y: np.ndarray, ref: np.ndarray, axes=(-2, -1)) -> np.ndarra
     return num / den
 
 
-def verify_rounds_copy(x: dict, accept: np.ndarray, W: int, S0: np.ndarray, L: int, fmt: str) -> np.ndarray:
+def verify_rounds_copy(x: dict, accept: np.ndarray, W: int, S0: np.ndarray, L: int, fmt: str,
+                       rule: str = "ssd") -> np.ndarray:
     """Speculative rounds whose outputs read a low-precision copy of the last
     flushed state (separated precisions), per sequence: before each round a
     ring holding >= L-W+1 accepted tokens is folded into the exact state;
     the round's W outputs come from the copy of that state followed by the
     accepted tokens since the fold and the W drafts; the accepted drafts join
     the ring.  Returns y float64 [R][W][B][H][P]."""
+    eager = _eager(rule)
     R = accept.shape[0]
     B = S0.shape[0]
     H, P = x["v"].shape[2], x["v"].shape[3]
@@ -161,12 +165,12 @@ def verify_rounds_copy(x: dict, accept: np.ndarray, W: int, S0: np.ndarray, L: i
         for r in range(R):
             if len(live) >= L - W + 1:
                 sub = {k: v[live][:, b:b + 1] for k, v in x.items()}
-                core.eager(S_fl, sub["q"], sub["k"], sub["v"], sub["dt"], sub["a"])
+                eager(S_fl, sub["q"], sub["k"], sub["v"], sub["dt"], sub["a"])
                 live = []
             Sq = np.ascontiguousarray(quant_dequant(S_fl, fmt))
             rows = live + [r * W + i for i in range(W)]
             sub = {k: v[rows][:, b:b + 1] for k, v in x.items()}
-            yy = core.eager(Sq, sub["q"], sub["k"], sub["v"], sub["dt"], sub["a"])
+            yy = eager(Sq, sub["q"], sub["k"], sub["v"], sub["dt"], sub["a"])
             y[r, :, b] = yy[len(live):, 0]
             live += [r * W + i for i in range(int(accept[r, b]))]
     return y

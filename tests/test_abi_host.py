@@ -61,6 +61,11 @@ def test_buffer_bytes_match_the_layout(lad):
     b4s = lad.replay_buffer_bytes(c4s)
     assert b4s["s_master"] == 0
     assert b4s["s_copy"] == b4["s_copy"] and b4s["s_scale"] == b4["s_scale"]
+    # a gated-delta layer with a copy holds the same buffers as a Mamba-2 layer
+    for cp, sh in ((lad.FP4_E2M1, 0), (lad.FP8_E4M3, 1), (lad.BF16, 0)):
+        m2 = lad.replay_buffer_bytes(lad.ReplayConfig(4, 8, 2, 64, 128, 16, lad.BF16, cp, sh))
+        gd = lad.replay_buffer_bytes(lad.ReplayConfig(4, 8, 2, 64, 128, 16, lad.BF16, cp, sh, lad.GATED_DELTA))
+        assert gd == m2
 
 
 @pytest.mark.parametrize("fields,status", [
@@ -75,7 +80,7 @@ def test_buffer_bytes_match_the_layout(lad):
     ((2, 4, 1, 64, 128, 16, 1, -1, 1), 1),          # shared without a copy
     ((2, 4, 1, 64, 128, 16, 1, 3, 2), 1),           # shared flag neither 0 nor 1
     ((2, 4, 1, 64, 128, 16, 1, -1, 0, 2), 1),       # unknown rule
-    ((2, 4, 1, 64, 128, 16, 1, 2, 0, 1), 2),        # gated delta rule with a read copy
+    ((2, 4, 1, 64, 128, 16, 1, -1, 1, 1), 1),       # gated delta rule, shared without a copy
 ])
 def test_invalid_configs_are_rejected_on_the_host(lad, fields, status):
     c = lad.ReplayConfig(*fields)

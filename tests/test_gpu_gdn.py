@@ -10,6 +10,11 @@ tests/test_oracle_gdn.py).
 - Speculative rounds (W = 1..8) with rollback, by separate calls and by
   replay_verify_step (the same kernels: equal bit for bit).
 - The eager step of this layer (replay_eager_step) against the oracle.
+- Low-precision copies (bf16, e4m3, MX FP4), separated and shared: outputs
+  against the oracle's emulation of the same copy (oracle.runs.separated /
+  shared / verify_rounds_copy with the gated delta rule), and, separated,
+  the copy's codes and scales against the oracle's quantisers applied to the
+  float32 checkpoint the same flush wrote, bit for bit.
 - The Gated DeltaNet workload's shapes (B=256, H=32, G=16, P=N=128, L=16,
   bf16), 64 steps, sampled sequences across the batch.
 - Errors: windows past 8 are UNSUPPORTED, count < W gives NaN and TOO_FEW.
@@ -203,5 +208,73 @@ def test_gdn_errors():
     torch.cuda.synchronize()
     assert layer.get_error()[0] == 0 and torch.isfinite(y8).all()
     layer.close()
-    with pytest.raises(lad.ReplayError):
-        _layer(w, read_copy="fp8")
+
+
+def _check_codes(layer, fmt):
+    """The copy equals the oracle's quantisers applied to the float32 checkpoint, bit for bit."""
+    import oracle
+    S = layer.s_master.cpu().numpy()
+    if fmt == "bf16":
+        got = layer.s_copy.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, oracle.bf16_encode(S))
+    elif fmt == "fp8":
+        codes, scale = oracle.quant_heads_e4m3(S)
+        assert np.array_equal(layer.s_scale.cpu().numpy(), scale)
+        assert np.array_equal(layer.s_copy.cpu().numpy(), codes)
+    else:
+        packed, scale = oracle.core.quant_blocks_mxfp4(S)
+        assert np.array_equal(layer.s_scale.cpu().numpy().reshape(scale.shape), scale)
+        assert np.array_equal(layer.s_copy.cpu().numpy().reshape(packed.shape), packed)
+
+
+COPIES = [(f, sh, P, N) for f in ("bf16", "fp8", "fp4") for sh in (False, True)
+          for P, N in ((64, 128), (128, 128))] + [("fp4", False, 16, 16), ("fp8", True, 64, 64)]
+
+
+@pytest.mark.parametrize("fmt,shared,P,N", COPIES,
+                         ids=[f"{f}-{'shared' if sh else 'separated'}-{P}x{N}" for f, sh, P, N in COPIES])
+def test_gdn_copy_decode(fmt, shared, P, N):
+    """Standard decode through replay_step reading a bf16 / e4m3 / FP4 copy
+    (L = 8, 3L + 2 steps from a non-zero checkpoint loaded through the copy's
+    quantisers), against the oracle's emulation of the same copy."""
+    w = synth.Workload(batch=3, heads=4, groups=2, head_dim=P, state_dim=N, ring_len=8, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=460 + P + N)
+    T = 3 * w.ring_len + 2
+    gu.note(f"gdn copy decode {fmt} shared={shared} {w}")
+    S0 = synth.checkpoint_state(w, scale=0.5)
+    dev = DevGdn(w, 0, T)
+    layer = _layer(w, read_copy=fmt, shared_lowp=shared)
+    layer.load_checkpoint(gu.to_dev(S0))
+    y = torch.empty((T, w.batch, w.heads, P), dtype=torch.float32, device=gu.DEV)
+    for t in range(T):
+        layer.step(*dev.step(t), y[t], flush_at=w.ring_len)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = dev.oracle()
+    S = S0.astype(np.float64).copy()
+    emul = (runs.shared if shared else runs.separated)(x, S, w.ring_len, fmt, rule="gdn")
+    gu.assert_copy(y.cpu().numpy(), emul, fmt, what=f"gdn {fmt} shared={shared} P={P} N={N}")
+    if not shared:
+        _check_codes(layer, fmt)
+    layer.close()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp4"])
+def test_gdn_copy_verify_rounds(fmt):
+    """Speculative rounds (W = 4, rollback) reading a copy, separated, by
+    replay_verify_step, against the oracle's emulation of the copy."""
+    w = synth.Workload(batch=3, heads=4, groups=2, head_dim=64, state_dim=128, ring_len=8, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=470)
+    R, W = 10, 4
+    gu.note(f"gdn copy verify {fmt} {w}")
+    accept = synth.accept_counts(w, R, W)
+    dev = DevGdn(w, 0, R * W)
+    layer = _layer(w, read_copy=fmt)
+    y = gu.run_verify(layer, w, dev, R, W, accept, fused=True)
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = dev.oracle()
+    emul = runs.verify_rounds_copy(x, accept, W, np.zeros((w.batch, w.heads, 64, 128)), w.ring_len, fmt, rule="gdn")
+    gu.assert_copy(y.cpu().numpy().transpose(0, 2, 1, 3, 4), emul, fmt, what=f"gdn verify {fmt}")
+    _check_codes(layer, fmt)
+    layer.close()

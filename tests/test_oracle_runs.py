@@ -127,3 +127,32 @@ def test_verify_rounds_copy_limits():
     assert np.allclose(y4, y_exact, rtol=1e-13, atol=1e-15)
     y4 = runs.verify_rounds_copy(x, acc, W, _S0(W_TINY), 4, "fp4")
     assert float(np.max(runs.normwise_rel_err(y4, y_exact))) > 1e-3   # folded states are read rounded
+
+
+def test_copy_emulations_gated_delta_rule():
+    """The copy emulations under the gated delta rule: a copy that only
+    rounds the state to float32 reproduces the exact run (to that rounding)
+    in standard decode and speculative rounds; shared and separated agree
+    before the first flush; an e4m3 copy's rounding is really applied."""
+    w = W_TINY
+    T, L = 12, 4
+    x = runs.widen_inputs(synth.gdn_inputs(w, 0, T), w.io_dtype)
+    y_exact = runs.standard(x, _S0(w), rule="gdn")
+    y32 = runs.separated(x, _S0(w), L, "f32", rule="gdn")
+    assert float(np.max(runs.normwise_rel_err(y32, y_exact))) < 1e-6
+    S_init = np.random.default_rng(4).standard_normal((3, 4, 8, 16)) * 0.5
+    for fmt in ("bf16", "fp8", "fp4"):
+        ysep = runs.separated(x, S_init.copy(), T, fmt, rule="gdn")
+        ysh = runs.shared(x, S_init.copy(), T, fmt, rule="gdn")
+        assert np.array_equal(ysep, ysh)
+    y8 = runs.separated(x, _S0(w), L, "fp8", rule="gdn")
+    assert 1e-4 < float(np.max(runs.normwise_rel_err(y8, y_exact))) < 6e-2
+    # the rule really is the gated delta rule: the Mamba-2 emulation differs
+    assert float(np.max(runs.normwise_rel_err(runs.separated(x, _S0(w), L, "f32"), y_exact))) > 1e-2
+    W, R = 3, 6
+    xv = runs.widen_inputs(synth.gdn_inputs(w, 0, R * W), w.io_dtype)
+    acc = synth.accept_counts(w, R, W)
+    yv = runs.verify_rounds(xv, acc, W, _S0(w), rule="gdn")
+    for Lv in (3, 4, 8):
+        y32v = runs.verify_rounds_copy(xv, acc, W, _S0(w), Lv, "f32", rule="gdn")
+        assert float(np.max(runs.normwise_rel_err(y32v, yv))) <= 1e-6, Lv
