@@ -481,16 +481,20 @@ def bench_gdn(args):
     beta): standard decode through replay_step (append, the output-only
     route -- the backward chain over the ring and one pass over S0 -- and
     the fold when the ring is full), against the layer's eager step
-    (S_t written every token) on the same inputs.  The roofline pass runs one
-    more window as separate calls with HIP events around each output-only
-    launch and the fold."""
+    (S_t written every token) on the same inputs.  With --read bf16/fp8/fp4
+    the outputs read a copy of that precision (separated: the fold writes the
+    float32 checkpoint and the copy).  The roofline pass runs one more window
+    as separate calls with HIP events around each output-only launch and the
+    fold."""
     import torch
     import linear_attention_decode_amd as lad
 
     w = synth.named("gdn")
     B, H, G, P, N, L = w.batch, w.heads, w.groups, w.head_dim, w.state_dim, w.ring_len
     pool = synth.gdn_inputs_torch(w, 0, POOL_STEPS, device="cuda")
-    layer = lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16", rule="gdn")
+    read = None if args.read == "f32" else args.read
+    st_bytes = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 0.5}[args.read]
+    layer = lad.ReplayLayer(B, H, G, P, N, L, io_dtype="bf16", rule="gdn", read_copy=read)
     y = torch.empty((B, H, P), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -527,8 +531,8 @@ def bench_gdn(args):
     assert word == 0, f"device error bits {word}"
     dec_s = sum(e[0].elapsed_time(e[1]) for e in dec_ev) / 1e3
     fold_s = sum(e[0].elapsed_time(e[1]) for e in fold_ev) / 1e3
-    dec_bytes = reps * sum(decode_bytes(w, c) for c in range(1, L + 1))
-    fold_bytes = reps * flush_bytes(w, L)
+    dec_bytes = reps * sum(decode_bytes(w, c, st_bytes=st_bytes) for c in range(1, L + 1))
+    fold_bytes = reps * flush_bytes(w, L, copy_bytes=0 if read is None else st_bytes)
     achieved = dec_bytes / dec_s / 1e9
     layer.close()
     del layer
@@ -561,7 +565,7 @@ def bench_gdn(args):
         "data": f"synthetic (seeded; unit-length q, k; {POOL_STEPS} distinct steps cycled)",
         "config": {"workload": "Gated DeltaNet layer, standard decode", "batch": B, "heads": H, "groups": G,
                    "head_dim": P, "state_dim": N, "ring_len": L, "io": "bf16", "checkpoint": "f32",
-                   "flush_every": L},
+                   "read": args.read, "flush_every": L},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "kernel": "gdn_verify_kernel, W=1 (output-only: backward chain + one pass over S0)",

@@ -314,9 +314,12 @@ __global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB, PR, ST>::NT)) void gdn
 
 template <int P, int N, int ST, int WM, int LM>
 static hipError_t launch_gdn_verify_lm(const DecodeArgs &a, hipStream_t s) {
-    // float32 tiles of 128 rows: two workgroups of 64; a copy's tiles stream
-    // in four wavefronts whole
-    constexpr int PR = P == 128 && ST == ST_F32 ? 64 : P;
+    // heads of 128 rows: two workgroups of 64 (with whole heads the copy
+    // kernels took 78 to 99 registers, three or four workgroups to a compute
+    // unit), except for FP4 copies, whose 4 KiB halves stream too little per chain
+    // (measured, B=256 H=32: bf16 85.9 -> 64.7 us, e4m3 59.0 -> 55.3 us,
+    // FP4 46.9 -> 51.8 us a launch)
+    constexpr int PR = P == 128 && ST != ST_FP4 ? 64 : P;
     const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H * (P / PR));
     if (a.r.io_bf16)
         gdn_verify_kernel<P, N, WM, LM, true, PR, ST><<<blocks, GdnShape<P, N, WM, LM, true, PR, ST>::NT, 0, s>>>(a);
