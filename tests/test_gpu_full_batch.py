@@ -14,7 +14,12 @@ is covered here on all of them:
 * speculative verify (B=256, H=64, W=5, accepted drafts ~ U{0..5}), 32 fused
   rounds through replay_verify_step: every draft's output of every sequence
   within 1e-4 per head, the ring integers of every sequence after every
-  round equal to the integer model's.
+  round equal to the integer model's;
+* a Gated DeltaNet layer (B=256, H=32, G=16, P=N=128, L=16, bf16 q/k/v,
+  float32 checkpoint; the gated delta rule, oracle.core.eager_gdn), 48 steps
+  (3 folds) through replay_step: every output of every sequence within 1e-4
+  per head (the floor's term magnitude as in tests/test_gpu_gdn.py), every
+  checkpoint after the last fold within 1e-4 of the oracle state.
 
 Page "ReplaySSM: Cachear Inputs, No Estado", "Los dos caminos": the
 output of a head is y_t = S_t q_t, and the rewriting changes no result.
@@ -81,4 +86,42 @@ def test_verify_step_every_sequence_verify_workload():
     y_ref = runs.verify_rounds(x, accept, W, S)                       # [R][W][B][H][P]
     y_abs = gu.y_abs_verify(x, accept, W, S.shape)
     gu.assert_f32(y.cpu().numpy().transpose(0, 2, 1, 3, 4), y_ref, y_abs, what="all 256 sequences:")
+    layer.close()
+
+
+class _GdnInputsTorch(gu.DevInputsTorch):
+    """Gated DeltaNet inputs (synth.gdn_inputs_torch) generated on the device."""
+
+    def __init__(self, w, t0, t1):
+        self.w = w
+        self.t0 = t0
+        self.t = synth.gdn_inputs_torch(w, t0, t1, device=gu.DEV)
+
+
+def test_step_every_sequence_gdn_workload():
+    from tests import parity
+    w = synth.named("gdn")
+    T, L = 48, w.ring_len
+    gu.note(f"full batch: gated delta rule {w} T={T}")
+    dev = _GdnInputsTorch(w, 0, T)
+    layer = _layer(w, rule="gdn")
+    model = oring.RingModel(w.batch, L)
+    y = torch.empty((T, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
+    for t in range(T):
+        layer.step(*dev.step(t), y[t], flush_at=L)
+        model.append(1)
+        model.flush(L)
+    gu.check_ring(layer, model, "gated delta rule, last step")
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = dev.oracle()
+    S = np.zeros((w.batch, w.heads, w.head_dim, w.state_dim))
+    y_ref = runs.standard(x, S, rule="gdn")
+    y_abs = runs.standard(parity.abs_inputs(x), np.zeros_like(S), rule="ssd")
+    gu.assert_f32(y.cpu().numpy(), y_ref, y_abs, what="all 256 sequences:")
+    del y_ref, y_abs
+    S_gpu = layer.s_master.cpu().numpy()
+    e = runs.normwise_rel_err(S_gpu, S, axes=(-2, -1))
+    print(f"  checkpoint per-head max {float(e.max()):.3e}", flush=True)
+    assert float(e.max()) <= gu.TOL_F32
     layer.close()
