@@ -217,26 +217,36 @@ def _counter_traffic(kernel_files, summary_name):
 
 DECODE_SOURCES = ["linear_attention_decode_amd/csrc/decode_impl.h",
                   "linear_attention_decode_amd/csrc/ring_mx.h",
-                  "linear_attention_decode_amd/csrc/device_common.h"]
+                  "linear_attention_decode_amd/csrc/device_common.h",
+    "linear_attention_decode_amd/csrc/internal.h"]
 STEP_SOURCES = ["linear_attention_decode_amd/csrc/step.hip",
                 "linear_attention_decode_amd/csrc/step_common.h",
                 "linear_attention_decode_amd/csrc/ring_mx.h",
-                "linear_attention_decode_amd/csrc/device_common.h"]
+                "linear_attention_decode_amd/csrc/device_common.h",
+    "linear_attention_decode_amd/csrc/internal.h"]
 STEP_COPY_SOURCES = ["linear_attention_decode_amd/csrc/step_copy.hip",
                      "linear_attention_decode_amd/csrc/step_common.h",
                      "linear_attention_decode_amd/csrc/decode_impl.h",
                      "linear_attention_decode_amd/csrc/ring_mx.h",
-                     "linear_attention_decode_amd/csrc/device_common.h"]
+                     "linear_attention_decode_amd/csrc/device_common.h",
+    "linear_attention_decode_amd/csrc/internal.h"]
+GDN_SOURCES = ["linear_attention_decode_amd/csrc/gdn.hip",
+               "linear_attention_decode_amd/csrc/decode_impl.h",
+               "linear_attention_decode_amd/csrc/ring_mx.h",
+               "linear_attention_decode_amd/csrc/device_common.h",
+    "linear_attention_decode_amd/csrc/internal.h"]
 VERIFY_STEP_SOURCES = ["linear_attention_decode_amd/csrc/verify_step.hip",
                        "linear_attention_decode_amd/csrc/wide_mx.h",
                        "linear_attention_decode_amd/csrc/step_common.h",
                        "linear_attention_decode_amd/csrc/ring_mx.h",
-                       "linear_attention_decode_amd/csrc/device_common.h"]
+                       "linear_attention_decode_amd/csrc/device_common.h",
+    "linear_attention_decode_amd/csrc/internal.h"]
 VERIFY_WIDE_SOURCES = ["linear_attention_decode_amd/csrc/verify_wide.hip",
                        "linear_attention_decode_amd/csrc/wide_mx.h",
                        "linear_attention_decode_amd/csrc/decode_impl.h",
                        "linear_attention_decode_amd/csrc/ring_mx.h",
-                       "linear_attention_decode_amd/csrc/device_common.h"]
+                       "linear_attention_decode_amd/csrc/device_common.h",
+    "linear_attention_decode_amd/csrc/internal.h"]
 
 
 def read_ceiling_gbs(nbytes=1 << 30, reps=7):
@@ -567,7 +577,9 @@ def bench_gdn(args):
                    "head_dim": P, "state_dim": N, "ring_len": L, "io": "bf16", "checkpoint": "f32",
                    "read": args.read, "flush_every": L},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": (_counter_traffic(GDN_SOURCES, "gdn_verify_kernel_f32_b256_h32_counters.txt")
+                                 if read is None else None),
                      "kernel": "gdn_verify_kernel, W=1 (output-only: backward chain + one pass over S0)",
                      "avg_launch_us": 1e6 * dec_s / (reps * L), "timed_launches": reps * L,
                      "launches_from": f"{reps} windows (ring counts 1..{L}) as separate calls after the timed "
