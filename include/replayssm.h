@@ -95,8 +95,8 @@ typedef enum {
                 the published gated delta rule (the pages print no equation for
                 it); every dt argument and ring slot carries beta_t, every a
                 argument and slot alpha_t.  Gated-delta layers take the same
-                read copies and shared mode as Mamba-2 layers, verify windows
-                up to min(8, L), and step stacked layers one call each
+                read copies, shared mode and verify windows (up to min(16, L))
+                as Mamba-2 layers, and step stacked layers one call each
                 (replay_step_layers: UNSUPPORTED).
    Both: y_t = S_t q_t. */
 typedef enum {

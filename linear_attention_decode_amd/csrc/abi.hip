@@ -227,10 +227,7 @@ replay_status run_verify(replay_handle *h, int32_t W, float *y, hipStream_t s) {
     a.y = y;
     a.W = W;
     const int st = state_kind(c.read_copy);
-    if (c.rule == REPLAY_RULE_GATED_DELTA) {
-        if (W > kMaxWindow) return REPLAY_ERR_UNSUPPORTED;
-        return from_hip(launch_gdn_verify(c.head_dim, c.state_dim, st, a, s));
-    }
+    if (c.rule == REPLAY_RULE_GATED_DELTA) return from_hip(launch_gdn_verify(c.head_dim, c.state_dim, st, a, s));
     // bf16 io: the matrix-core kernel from kWideFrom on; float32 io: past the
     // register kernel's kMaxWindow
     const int wide_from = c.io_dtype == REPLAY_BF16 ? kWideFrom : kMaxWindow + 1;

@@ -33,6 +33,7 @@
 //                      is the eager step of this layer (one entry from the
 //                      call, y = S_t q_t).
 #include "decode_impl.h"
+#include "wide_mx.h"
 
 namespace replay {
 
@@ -48,8 +49,6 @@ struct GdnShape {
     static constexpr int SPL = P / PR;            // workgroups a head
     static constexpr int NTS = Sh::NTS;           // streaming threads
     static constexpr int NT = NTS + 64;           // + the chain wavefront
-    static constexpr int E = (N + 63) / 64;       // w elements a chain lane holds (n = lane + 64 e)
-    static constexpr int VR = (PR + 63) / 64;     // outputs a chain lane accumulates (p = lane + 64 r)
     static_assert(P % PR == 0, "whole row blocks");
 };
 
@@ -119,14 +118,17 @@ __device__ __forceinline__ float gdn_wave_sum(float x) {
 }
 
 // The chain wavefront: entries 0..count-1 of (b, h); window position w is
-// entry t_w = count - W + w.  Writes s_w0[w][n] = w_0 of position w and, for
-// the PR rows p0 .. p0 + PR, s_r[w][p - p0] = sum_{j<=t_w} beta_j (k_j . w_j) v_j[p].
-template <int P, int N, int WM, int LM, bool IOB, int PR>
+// entry t_w = count - W + w.  For the WM positions w_lo .. w_lo + WM - 1
+// below W, writes s_w0[w][n] = w_0 of position w and, for the PR rows
+// p0 .. p0 + PR, s_r[w][p - p0] = sum_{j<=t_w} beta_j (k_j . w_j) v_j[p].
+// STAGE: this wavefront stages the entries' k and v rows itself (else the
+// caller has staged them and synchronised); ZROW: rows w_lo.. of s_w0 past
+// W are written as zeros.  QS: the row stride of s_w0.
+template <int P, int N, int WM, int LM, bool IOB, int PR, bool STAGE = true, bool ZROW = false, int QS = N>
 __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int b, int g, size_t bh, int base,
                                                int count, int W, int p0, float (*s_k)[N], float (*s_v)[PR],
-                                               float (*s_w0)[N], float (*s_r)[PR]) {
-    using GS = GdnShape<P, N, WM, LM, IOB, PR>;
-    constexpr int E = GS::E, VR = GS::VR;
+                                               float (*s_w0)[QS], float (*s_r)[PR], int w_lo = 0) {
+    constexpr int E = (N + 63) / 64, VR = (PR + 63) / 64;
     const int L = r.L;
     const int bmod = base % L;
     auto slot = [&](int j) { return ring_slot(bmod, j, L); };
@@ -143,7 +145,7 @@ __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int 
     float wv[WM][E];
 #pragma unroll
     for (int w = 0; w < WM; ++w) {
-        const int t = count - W + (w < W ? w : W - 1);
+        const int t = count - W + (w_lo + w < W ? w_lo + w : W - 1);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int n = lane + 64 * e;
@@ -157,9 +159,11 @@ __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int 
             wv[w][e] = x;
         }
     }
-    gdn_stage_rows<LM, N, 64, IOB>(r.k, gring, bmod, L, count, lane, s_k);
-    gdn_stage_rows<LM, PR, 64, IOB, P>(r.v, hring, bmod, L, count, lane, s_v, p0);
-    wave_lds_sync();   // every lane's k and v rows are in LDS
+    if constexpr (STAGE) {
+        gdn_stage_rows<LM, N, 64, IOB>(r.k, gring, bmod, L, count, lane, s_k);
+        gdn_stage_rows<LM, PR, 64, IOB, P>(r.v, hring, bmod, L, count, lane, s_v, p0);
+        wave_lds_sync();   // every lane's k and v rows are in LDS
+    }
 
     float acc[WM][VR];
 #pragma unroll
@@ -178,7 +182,7 @@ __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int 
             for (int rr = 0; rr < VR; ++rr) vm[rr] = lane + 64 * rr < PR ? s_v[m][lane + 64 * rr] : 0.f;
 #pragma unroll
             for (int w = 0; w < WM; ++w) {
-                if (w < W && m <= count - W + w) {   // uniform
+                if (w_lo + w < W && m <= count - W + w_lo + w) {   // uniform
                     float d = 0.f;
 #pragma unroll
                     for (int e = 0; e < E; ++e) d = fmaf(km[e], wv[w][e], d);
@@ -194,13 +198,17 @@ __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int 
     }
 #pragma unroll
     for (int w = 0; w < WM; ++w) {
-        if (w < W) {
+        if (w_lo + w < W) {
 #pragma unroll
             for (int e = 0; e < E; ++e)
-                if (lane + 64 * e < N) s_w0[w][lane + 64 * e] = wv[w][e];
+                if (lane + 64 * e < N) s_w0[w_lo + w][lane + 64 * e] = wv[w][e];
 #pragma unroll
             for (int rr = 0; rr < VR; ++rr)
-                if (lane + 64 * rr < PR) s_r[w][lane + 64 * rr] = acc[w][rr];
+                if (lane + 64 * rr < PR) s_r[w_lo + w][lane + 64 * rr] = acc[w][rr];
+        } else if constexpr (ZROW) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (lane + 64 * e < N) s_w0[w_lo + w][lane + 64 * e] = 0.f;
         }
     }
 }
@@ -334,30 +342,137 @@ static hipError_t launch_gdn_verify_w(const DecodeArgs &a, hipStream_t s) {
     return launch_gdn_verify_lm<P, N, ST, WM, kMaxRing>(a, s);
 }
 
-template <int P, int N, int ST>
-static hipError_t launch_gdn_verify_st(const DecodeArgs &a, hipStream_t s) {
-    if (a.W == 1) return launch_gdn_verify_w<P, N, ST, 1>(a, s);
-    if (a.W <= 4) return launch_gdn_verify_w<P, N, ST, 4>(a, s);
-    return launch_gdn_verify_w<P, N, ST, kMaxWindow>(a, s);
-}
-
 template <int P, int N>
-static hipError_t launch_gdn_verify_pn(int st, const DecodeArgs &a, hipStream_t s) {
+static hipError_t launch_gdn_decode_pn(int st, const DecodeArgs &a, hipStream_t s) {
     switch (st) {
-        case ST_F32: return launch_gdn_verify_st<P, N, ST_F32>(a, s);
-        case ST_BF16: return launch_gdn_verify_st<P, N, ST_BF16>(a, s);
-        case ST_FP8: return launch_gdn_verify_st<P, N, ST_FP8>(a, s);
-        case ST_FP4: return launch_gdn_verify_st<P, N, ST_FP4>(a, s);
+        case ST_F32: return launch_gdn_verify_w<P, N, ST_F32, 1>(a, s);
+        case ST_BF16: return launch_gdn_verify_w<P, N, ST_BF16, 1>(a, s);
+        case ST_FP8: return launch_gdn_verify_w<P, N, ST_FP8, 1>(a, s);
+        case ST_FP4: return launch_gdn_verify_w<P, N, ST_FP4, 1>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
+// ---------------------------------------------------------------------------
+// Windows past the register kernel's 8 (up to 16): S0 W_0^T on the matrix
+// cores.  The streaming wavefronts are the matrix-core verify's (wide_mx.h:
+// one per 16 rows, coalesced tile reads transposed per wavefront in LDS,
+// v_mfma_f32_16x16x4_f32 against float32 query rows), the query rows being
+// the window positions' w_0 from the chains; two chain wavefronts run eight
+// positions each.  Each stages every k and v row into the one buffer itself
+// (the two write the same values), so neither waits for the other.
+
+template <int P, int N, int ST, int LM>
+struct GdnWideShape : WideTile<P, N, ST> {
+    static constexpr int NC = kWide / 8;                   // chain wavefronts, 8 positions each
+    static constexpr int NT = WideTile<P, N, ST>::NTS + 64 * NC;
+    static constexpr int TSF = N + 4;                      // LDS row stride of the w_0 rows, in floats
+};
+
+template <int P, int N, int ST, int LM, bool IOB>
+__global__ __launch_bounds__((GdnWideShape<P, N, ST, LM>::NT)) void gdn_wide_kernel(DecodeArgs args) {
+    using WS = GdnWideShape<P, N, ST, LM>;
+    constexpr int NTS = WS::NTS, TSF = WS::TSF;
+
+    __shared__ __align__(16) float s_Qf[kWide][TSF];   // w_0 of window position w (rows past W zero)
+    __shared__ float s_r[kWide][P];
+    __shared__ __align__(16) float s_k[LM][N];
+    __shared__ __align__(16) float s_v[LM][P];
+    __shared__ __align__(16) uint32_t s_T[WS::COAL ? NTS / 64 : 1][16][WS::TROW];   // per-wavefront staging
+
+    const RingView &r = args.r;
+    const int W = args.W;
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    const int H = r.H, L = r.L;
+    const int b = lid / H, h = lid % H;
+    const int g = (h * r.G) / H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const size_t bh = (size_t)b * H + h;
+    const int p0 = 16 * wave;   // rows of a streaming wavefront
+
+    const int base = r.base[b];
+    const int pos = r.pos[b];
+    WideRows<P, N, ST> rows;
+    if (wave < NTS / 64) rows.load(args.S, bh * (size_t)(P * N), p0, lane, args.scale);
+    const int count = pos - base;
+    if (count < W) {  // uniform over the workgroup
+        for (int i = tid; i < W * P; i += WS::NT) args.y[(((size_t)b * W + i / P) * H + h) * P + i % P] = __builtin_nanf("");
+        if (tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_TOO_FEW);
+        return;
+    }
+    if (wave >= NTS / 64) {
+        // chain wavefront c: positions 8c .. 8c + 7
+        const int c = __builtin_amdgcn_readfirstlane(wave - NTS / 64);
+        gdn_chain_wave<P, N, 8, LM, IOB, P, true, true, TSF>(r, lane, b, g, bh, base, count, W, 0, s_k, s_v, s_Qf,
+                                                             s_r, 8 * c);
+        __syncthreads();   // the w_0 rows and the ring terms
+        return;
+    }
+    rows.transpose(s_T[WS::COAL ? wave : 0], lane);
+    __syncthreads();   // the w_0 rows and the ring terms
+    const uint8_t *rsc = static_cast<const uint8_t *>(args.scale) + (bh * P + p0 + 4 * lg) * WS::NB;   // FP4 rows
+    const f32x4 acc = rows.dot_f32q(s_Qf, lane, rsc);
+    // D[p0 + 4 lg + rr][w = lr]
+    const int w = lr;
+    if (w < W) {
+        const float sc = (ST == ST_FP8) ? static_cast<const float *>(args.scale)[bh] : 1.0f;
+        f32x4 o;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) o[rr] = sc * acc[rr] + s_r[w][p0 + 4 * lg + rr];
+        *reinterpret_cast<f32x4 *>(&args.y[(((size_t)b * W + w) * H + h) * P + p0 + 4 * lg]) = o;
+    }
+}
+
+template <int P, int N, int ST>
+static hipError_t launch_gdn_wide_st(const DecodeArgs &a, hipStream_t s) {
+    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
+    if (a.r.L <= 16) {
+        if (a.r.io_bf16)
+            gdn_wide_kernel<P, N, ST, 16, true><<<blocks, GdnWideShape<P, N, ST, 16>::NT, 0, s>>>(a);
+        else
+            gdn_wide_kernel<P, N, ST, 16, false><<<blocks, GdnWideShape<P, N, ST, 16>::NT, 0, s>>>(a);
+    } else {
+        if (a.r.io_bf16)
+            gdn_wide_kernel<P, N, ST, kMaxRing, true><<<blocks, GdnWideShape<P, N, ST, kMaxRing>::NT, 0, s>>>(a);
+        else
+            gdn_wide_kernel<P, N, ST, kMaxRing, false><<<blocks, GdnWideShape<P, N, ST, kMaxRing>::NT, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+template <int P, int N>
+static hipError_t launch_gdn_wide_pn(int st, const DecodeArgs &a, hipStream_t s) {
+    switch (st) {
+        case ST_F32: return launch_gdn_wide_st<P, N, ST_F32>(a, s);
+        case ST_BF16: return launch_gdn_wide_st<P, N, ST_BF16>(a, s);
+        case ST_FP8: return launch_gdn_wide_st<P, N, ST_FP8>(a, s);
+        case ST_FP4: return launch_gdn_wide_st<P, N, ST_FP4>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+static hipError_t launch_gdn_wide(int P, int N, int st, const DecodeArgs &a, hipStream_t s) {
+    if (P == 16 && N == 16) return launch_gdn_wide_pn<16, 16>(st, a, s);
+    if (P == 64 && N == 64) return launch_gdn_wide_pn<64, 64>(st, a, s);
+    if (P == 64 && N == 128) return launch_gdn_wide_pn<64, 128>(st, a, s);
+    if (P == 128 && N == 128) return launch_gdn_wide_pn<128, 128>(st, a, s);
+    return hipErrorInvalidValue;
+}
+
+// W = 1: the register kernel; windows of 2 and more: the matrix cores (the
+// register kernel's per-row sums for several positions took 68 to 256
+// registers and measured 175 / 518 us at W = 4 / 8 with a float32
+// checkpoint, 426 / 867 us with an e4m3 copy, against 218 - 243 us for the
+// matrix cores at W = 9 .. 16; B=256, H=32, P=N=128)
 hipError_t launch_gdn_verify(int P, int N, int st, const DecodeArgs &a, hipStream_t s) {
-    if (a.W < 1 || a.W > kMaxWindow || a.W > a.r.L) return hipErrorInvalidValue;
-    if (P == 16 && N == 16) return launch_gdn_verify_pn<16, 16>(st, a, s);
-    if (P == 64 && N == 64) return launch_gdn_verify_pn<64, 64>(st, a, s);
-    if (P == 64 && N == 128) return launch_gdn_verify_pn<64, 128>(st, a, s);
-    if (P == 128 && N == 128) return launch_gdn_verify_pn<128, 128>(st, a, s);
+    if (a.W < 1 || a.W > kMaxWideWindow || a.W > a.r.L) return hipErrorInvalidValue;
+    if (a.W > 1) return launch_gdn_wide(P, N, st, a, s);
+    if (P == 16 && N == 16) return launch_gdn_decode_pn<16, 16>(st, a, s);
+    if (P == 64 && N == 64) return launch_gdn_decode_pn<64, 64>(st, a, s);
+    if (P == 64 && N == 128) return launch_gdn_decode_pn<64, 128>(st, a, s);
+    if (P == 128 && N == 128) return launch_gdn_decode_pn<128, 128>(st, a, s);
     return hipErrorInvalidValue;
 }
 

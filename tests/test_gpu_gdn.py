@@ -7,8 +7,9 @@ tests/test_oracle_gdn.py).
   ring is full), ragged shapes, both io dtypes, rings of 16 and 32 entries,
   from a non-zero checkpoint; the checkpoint after a final fold against the
   oracle's state.
-- Speculative rounds (W = 1..8) with rollback, by separate calls and by
-  replay_verify_step (the same kernels: equal bit for bit).
+- Speculative rounds with rollback, by separate calls and by
+  replay_verify_step (the same kernels: equal bit for bit): W = 1..8 (register
+  sums) and W = 9..16 (S0 W_0^T on the matrix cores).
 - The eager step of this layer (replay_eager_step) against the oracle.
 - Low-precision copies (bf16, e4m3, MX FP4), separated and shared: outputs
   against the oracle's emulation of the same copy (oracle.runs.separated /
@@ -17,7 +18,7 @@ tests/test_oracle_gdn.py).
   float32 checkpoint the same flush wrote, bit for bit.
 - The Gated DeltaNet workload's shapes (B=256, H=32, G=16, P=N=128, L=16,
   bf16), 64 steps, sampled sequences across the batch.
-- Errors: windows past 8 are UNSUPPORTED, count < W gives NaN and TOO_FEW.
+- Errors: windows past 16 are rejected, count < W gives NaN and TOO_FEW.
 
 Metric: the float32 per-head metric of tests/parity.py (1e-4).  Its
 conditioning floor takes as term magnitude the Mamba-2 recurrence run on
@@ -113,6 +114,10 @@ def test_gdn_decode_ragged(P, N, H, G, L, io, B):
     (16, 16, 8, 3, 3, 4, 1),
     (64, 64, 32, 4, 2, 4, 2),
     (64, 128, 16, 1, 3, 4, 2),
+    (64, 128, 16, 12, 3, 4, 2),            # matrix cores from here on
+    (128, 128, 16, 16, 2, 4, 2),
+    (16, 16, 16, 9, 3, 4, 1),
+    (64, 64, 32, 13, 2, 4, 2),
 ])
 def test_gdn_verify_rounds(P, N, L, W, B, H, G):
     w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype="bf16",
@@ -202,11 +207,11 @@ def test_gdn_errors():
     assert torch.isnan(y).all()
     layer.append(8, *dev.window(4, 8))
     with pytest.raises(lad.ReplayError):
-        layer.verify(9, torch.zeros((3, 9, 4, 64), dtype=torch.float32, device=gu.DEV))
-    y8 = torch.zeros((3, 8, 4, 64), dtype=torch.float32, device=gu.DEV)
-    layer.verify(8, y8)
+        layer.verify(17, torch.zeros((3, 17, 4, 64), dtype=torch.float32, device=gu.DEV))
+    y12 = torch.zeros((3, 12, 4, 64), dtype=torch.float32, device=gu.DEV)
+    layer.verify(12, y12)
     torch.cuda.synchronize()
-    assert layer.get_error()[0] == 0 and torch.isfinite(y8).all()
+    assert layer.get_error()[0] == 0 and torch.isfinite(y12).all()
     layer.close()
 
 
@@ -259,13 +264,15 @@ def test_gdn_copy_decode(fmt, shared, P, N):
     layer.close()
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp4"])
-def test_gdn_copy_verify_rounds(fmt):
-    """Speculative rounds (W = 4, rollback) reading a copy, separated, by
-    replay_verify_step, against the oracle's emulation of the copy."""
-    w = synth.Workload(batch=3, heads=4, groups=2, head_dim=64, state_dim=128, ring_len=8, io_dtype="bf16",
-                       config=synth.CONFIG_ID["misc"], layer=470)
-    R, W = 10, 4
+@pytest.mark.parametrize("fmt,W", [("bf16", 4), ("fp8", 4), ("fp4", 4), ("fp8", 12), ("fp4", 16), ("bf16", 10)])
+def test_gdn_copy_verify_rounds(fmt, W):
+    """Speculative rounds (rollback) reading a copy, separated, by
+    replay_verify_step, against the oracle's emulation of the copy; windows
+    past 8 on the matrix cores."""
+    L = 8 if W <= 4 else 16
+    w = synth.Workload(batch=3, heads=4, groups=2, head_dim=64, state_dim=128, ring_len=L, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=470 + W)
+    R = 10
     gu.note(f"gdn copy verify {fmt} {w}")
     accept = synth.accept_counts(w, R, W)
     dev = DevGdn(w, 0, R * W)
@@ -277,4 +284,37 @@ def test_gdn_copy_verify_rounds(fmt):
     emul = runs.verify_rounds_copy(x, accept, W, np.zeros((w.batch, w.heads, 64, 128)), w.ring_len, fmt, rule="gdn")
     gu.assert_copy(y.cpu().numpy().transpose(0, 2, 1, 3, 4), emul, fmt, what=f"gdn verify {fmt}")
     _check_codes(layer, fmt)
+    layer.close()
+
+
+@pytest.mark.parametrize("fmt", [None, "fp8", "fp4", "bf16"])
+def test_gdn_wide_agrees_with_register_windows(fmt):
+    """The same state scored with W = 16 and W = 8 (matrix cores) and W = 1
+    (register sums): the positions the windows share agree to 1e-5 per token
+    (the copies: the same codes read by both).  Slow decay (dt x 0.01), so
+    that S0's part of the outputs stays large for the late positions."""
+    w = synth.Workload(batch=3, heads=4, groups=2, head_dim=128, state_dim=128, ring_len=16, io_dtype="bf16",
+                       config=synth.CONFIG_ID["misc"], layer=480, dt_scale=0.01)
+    gu.note(f"gdn wide vs register windows {fmt}")
+    S0 = synth.checkpoint_state(w, scale=0.5)
+    dev = DevGdn(w, 0, 16)
+    layer = _layer(w, read_copy=fmt)
+    layer.load_checkpoint(gu.to_dev(S0))
+    layer.append(16, *dev.window(0, 16))
+    ys = {}
+    for W in (16, 8, 1):
+        ys[W] = torch.empty((3, W, 4, 128), dtype=torch.float32, device=gu.DEV)
+        layer.verify(W, ys[W])
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = dev.oracle()
+    S = S0.astype(np.float64).copy()
+    y_ref = runs.standard(x, S, rule="gdn").transpose(1, 0, 2, 3)     # [B][16][H][P]
+    e_s0 = runs.normwise_rel_err(runs.standard(x, np.zeros_like(S), rule="gdn").transpose(1, 0, 2, 3), y_ref)
+    print(f"  S0's share of the outputs: per-token min {float(e_s0.min()):.3e}", flush=True)
+    assert float(e_s0.min()) > 1e-3                   # S0 enters every position's output
+    for W in (8, 1):
+        e = runs.normwise_rel_err(ys[16][:, 16 - W:].cpu().numpy(), ys[W].cpu().numpy().astype(np.float64))
+        print(f"  W=16 against W={W}: per-token max {float(e.max()):.3e}", flush=True)
+        assert float(e.max()) <= 1e-5
     layer.close()
