@@ -353,6 +353,107 @@ static hipError_t launch_gdn_decode_pn(int st, const DecodeArgs &a, hipStream_t 
     }
 }
 
+// The chains of eight window positions w_lo .. w_lo + 7 in one wavefront,
+// positions on the wavefront's 16-lane rows: lane (row rw, column c) holds
+// elements NE c .. NE c + NE - 1 of positions rw and rw + 4 (w vectors and the
+// ring term's rows VR c .. VR c + VR - 1), so an entry's dot k_m . w_m is a sum
+// over the 16 lanes of a row (DPP steps, no cross-row traffic).  A position
+// not yet reached by entry m (m > t_w), or past W, takes alpha = 1, beta = 0
+// for it: w and the ring term stay unchanged exactly.  Every lane stages the
+// entries' k and v rows (stride 64 threads) as gdn_chain_wave does; rows of
+// s_w0 past W are written as zeros.  The ring term covers rows r0 .. r0 + PR
+// of the head.  The w_0 rows are written after a workgroup barrier (s_w0 may
+// overlay s_k, which every chain wavefront reads until then); the caller's
+// other wavefronts take that barrier too.
+template <int P, int N, int LM, bool IOB, int QS, int PR>
+__device__ __forceinline__ void gdn_chain_rows(const RingView &r, int lane, int b, int g, size_t bh, int base,
+                                               int count, int W, int w_lo, int r0, float (*s_k)[N],
+                                               float (*s_v)[PR], float (*s_w0)[QS], float (*s_r)[PR]) {
+    constexpr int NE = N / 16, VR = PR / 16, PPR = 2;   // elements, outputs, positions of a lane
+    static_assert(N % 16 == 0 && PR % 16 == 0, "whole 16-lane rows");
+    const int L = r.L;
+    const int bmod = base % L;
+    auto slot = [&](int j) { return ring_slot(bmod, j, L); };
+    const size_t gring = ((size_t)b * r.G + g) * L;
+    const int rw = lane >> 4, c = lane & 15;
+
+    float aj = 1.f, bj = 0.f;
+    if (lane < count) {
+        aj = r.a[dta_index(b, bh, r.H, L, slot(lane))];
+        bj = r.dt[dta_index(b, bh, r.H, L, slot(lane))];
+    }
+    int gw[PPR];
+    float wv[PPR][NE];
+#pragma unroll
+    for (int s = 0; s < PPR; ++s) {
+        gw[s] = w_lo + rw + 4 * s;
+        const int t = count - W + (gw[s] < W ? gw[s] : W - 1);
+        const size_t q0 = (gring + slot(t)) * N + NE * c;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            if constexpr (IOB)
+                wv[s][e] = bf16_bits_to_f32(static_cast<const uint16_t *>(r.q)[q0 + e]);
+            else
+                wv[s][e] = static_cast<const float *>(r.q)[q0 + e];
+        }
+    }
+    gdn_stage_rows<LM, N, 64, IOB>(r.k, gring, bmod, L, count, lane, s_k);
+    gdn_stage_rows<LM, PR, 64, IOB, P>(r.v, bh * L, bmod, L, count, lane, s_v, r0);
+    wave_lds_sync();   // every lane's k and v rows are in LDS
+
+    float acc[PPR][VR];
+#pragma unroll
+    for (int s = 0; s < PPR; ++s)
+#pragma unroll
+        for (int i = 0; i < VR; ++i) acc[s][i] = 0.f;
+    // the entries from the newest down (unrolled over the ring's bound, uniform guards)
+#pragma unroll
+    for (int m = LM - 1; m >= 0; --m) {
+      if (m < count) {
+        const float am = bcast(aj, m), bm = bcast(bj, m);
+        float km[NE], vm[VR];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) km[e] = s_k[m][NE * c + e];
+#pragma unroll
+        for (int i = 0; i < VR; ++i) vm[i] = s_v[m][VR * c + i];
+#pragma unroll
+        for (int s = 0; s < PPR; ++s) {
+            if (w_lo + 4 * s >= W) continue;   // uniform: no position of this slot is in the window
+            const bool act = gw[s] < W && m <= count - W + gw[s];
+            const float as = act ? am : 1.f, bs = act ? bm : 0.f;
+            float d0 = 0.f, d1 = 0.f;   // two partial sums: a shorter dependent chain
+#pragma unroll
+            for (int e = 0; e < NE; e += 2) {
+                d0 = fmaf(km[e], wv[s][e], d0);
+                if (e + 1 < NE) d1 = fmaf(km[e + 1], wv[s][e + 1], d1);
+            }
+            float d = d0 + d1;
+#pragma unroll
+            for (int bit = 3; bit >= 0; --bit) d += lane_partner(d, bit);   // over the row's 16 lanes
+            const float cf = bs * d;
+#pragma unroll
+            for (int i = 0; i < VR; ++i) acc[s][i] = fmaf(cf, vm[i], acc[s][i]);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) wv[s][e] = as * fmaf(-cf, km[e], wv[s][e]);   // w_{m-1} = A_m w_m
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < PPR; ++s) {
+        if (gw[s] < W) {
+#pragma unroll
+            for (int i = 0; i < VR; ++i) s_r[gw[s]][VR * c + i] = acc[s][i];
+        }
+    }
+    __syncthreads();   // every chain wavefront of the workgroup is done with s_k, which s_w0 overlays
+#pragma unroll
+    for (int s = 0; s < PPR; ++s) {
+        const bool live = gw[s] < W;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) s_w0[gw[s]][NE * c + e] = live ? wv[s][e] : 0.f;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Windows past the register kernel's 8 (up to 16): S0 W_0^T on the matrix
 // cores.  The streaming wavefronts are the matrix-core verify's (wide_mx.h:
@@ -362,35 +463,43 @@ static hipError_t launch_gdn_decode_pn(int st, const DecodeArgs &a, hipStream_t 
 // positions each.  Each stages every k and v row into the one buffer itself
 // (the two write the same values), so neither waits for the other.
 
-template <int P, int N, int ST, int LM>
-struct GdnWideShape : WideTile<P, N, ST> {
+// PR of the head's P rows per workgroup (128-row heads: two workgroups of
+// 64, each running both chain wavefronts for its own rows).  The w_0 rows
+// overlay the staged k rows once every chain has finished reading them.
+template <int P, int N, int ST, int LM, int PR>
+struct GdnWideShape : WideTile<PR, N, ST> {
+    static constexpr int SPL = P / PR;                     // workgroups a head
     static constexpr int NC = kWide / 8;                   // chain wavefronts, 8 positions each
-    static constexpr int NT = WideTile<P, N, ST>::NTS + 64 * NC;
+    static constexpr int NT = WideTile<PR, N, ST>::NTS + 64 * NC;
     static constexpr int TSF = N + 4;                      // LDS row stride of the w_0 rows, in floats
+    static constexpr int KQ = LM * N > kWide * TSF ? LM * N : kWide * TSF;   // floats of the k / w_0 buffer
 };
 
-template <int P, int N, int ST, int LM, bool IOB>
-__global__ __launch_bounds__((GdnWideShape<P, N, ST, LM>::NT)) void gdn_wide_kernel(DecodeArgs args) {
-    using WS = GdnWideShape<P, N, ST, LM>;
+template <int P, int N, int ST, int LM, bool IOB, int PR>
+__global__ __launch_bounds__((GdnWideShape<P, N, ST, LM, PR>::NT)) void gdn_wide_kernel(DecodeArgs args) {
+    using WS = GdnWideShape<P, N, ST, LM, PR>;
     constexpr int NTS = WS::NTS, TSF = WS::TSF;
 
-    __shared__ __align__(16) float s_Qf[kWide][TSF];   // w_0 of window position w (rows past W zero)
-    __shared__ float s_r[kWide][P];
-    __shared__ __align__(16) float s_k[LM][N];
-    __shared__ __align__(16) float s_v[LM][P];
+    __shared__ __align__(16) float s_kq[WS::KQ];        // the entries' k rows, then w_0 of each window position
+    __shared__ float s_r[kWide][PR];
+    __shared__ __align__(16) float s_v[LM][PR];
     __shared__ __align__(16) uint32_t s_T[WS::COAL ? NTS / 64 : 1][16][WS::TROW];   // per-wavefront staging
+    float (*s_k)[N] = reinterpret_cast<float (*)[N]>(s_kq);
+    float (*s_Qf)[TSF] = reinterpret_cast<float (*)[TSF]>(s_kq);
 
     const RingView &r = args.r;
     const int W = args.W;
+    // consecutive workgroups: the row blocks of a head, then the heads of a group
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int H = r.H, L = r.L;
-    const int b = lid / H, h = lid % H;
+    const int H = r.H;
+    const int hb = lid / WS::SPL, r0 = (lid % WS::SPL) * PR;
+    const int b = hb / H, h = hb % H;
     const int g = (h * r.G) / H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t bh = (size_t)b * H + h;
-    const int p0 = 16 * wave;   // rows of a streaming wavefront
+    const int p0 = r0 + 16 * wave;   // rows of a streaming wavefront
 
     const int base = r.base[b];
     const int pos = r.pos[b];
@@ -398,19 +507,20 @@ __global__ __launch_bounds__((GdnWideShape<P, N, ST, LM>::NT)) void gdn_wide_ker
     if (wave < NTS / 64) rows.load(args.S, bh * (size_t)(P * N), p0, lane, args.scale);
     const int count = pos - base;
     if (count < W) {  // uniform over the workgroup
-        for (int i = tid; i < W * P; i += WS::NT) args.y[(((size_t)b * W + i / P) * H + h) * P + i % P] = __builtin_nanf("");
+        for (int i = tid; i < W * PR; i += WS::NT)
+            args.y[(((size_t)b * W + i / PR) * H + h) * P + r0 + i % PR] = __builtin_nanf("");
         if (tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_TOO_FEW);
         return;
     }
     if (wave >= NTS / 64) {
-        // chain wavefront c: positions 8c .. 8c + 7
+        // chain wavefront c: positions 8c .. 8c + 7 (two barriers inside and here)
         const int c = __builtin_amdgcn_readfirstlane(wave - NTS / 64);
-        gdn_chain_wave<P, N, 8, LM, IOB, P, true, true, TSF>(r, lane, b, g, bh, base, count, W, 0, s_k, s_v, s_Qf,
-                                                             s_r, 8 * c);
+        gdn_chain_rows<P, N, LM, IOB, TSF, PR>(r, lane, b, g, bh, base, count, W, 8 * c, r0, s_k, s_v, s_Qf, s_r);
         __syncthreads();   // the w_0 rows and the ring terms
         return;
     }
     rows.transpose(s_T[WS::COAL ? wave : 0], lane);
+    __syncthreads();   // the chains are done with the k rows
     __syncthreads();   // the w_0 rows and the ring terms
     const uint8_t *rsc = static_cast<const uint8_t *>(args.scale) + (bh * P + p0 + 4 * lg) * WS::NB;   // FP4 rows
     const f32x4 acc = rows.dot_f32q(s_Qf, lane, rsc);
@@ -420,26 +530,26 @@ __global__ __launch_bounds__((GdnWideShape<P, N, ST, LM>::NT)) void gdn_wide_ker
         const float sc = (ST == ST_FP8) ? static_cast<const float *>(args.scale)[bh] : 1.0f;
         f32x4 o;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) o[rr] = sc * acc[rr] + s_r[w][p0 + 4 * lg + rr];
+        for (int rr = 0; rr < 4; ++rr) o[rr] = sc * acc[rr] + s_r[w][p0 - r0 + 4 * lg + rr];
         *reinterpret_cast<f32x4 *>(&args.y[(((size_t)b * W + w) * H + h) * P + p0 + 4 * lg]) = o;
     }
 }
 
+template <int P, int N, int ST, int LM, int PR>
+static hipError_t launch_gdn_wide_lm(const DecodeArgs &a, hipStream_t s) {
+    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H * (P / PR));
+    if (a.r.io_bf16)
+        gdn_wide_kernel<P, N, ST, LM, true, PR><<<blocks, GdnWideShape<P, N, ST, LM, PR>::NT, 0, s>>>(a);
+    else
+        gdn_wide_kernel<P, N, ST, LM, false, PR><<<blocks, GdnWideShape<P, N, ST, LM, PR>::NT, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 template <int P, int N, int ST>
 static hipError_t launch_gdn_wide_st(const DecodeArgs &a, hipStream_t s) {
-    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H);
-    if (a.r.L <= 16) {
-        if (a.r.io_bf16)
-            gdn_wide_kernel<P, N, ST, 16, true><<<blocks, GdnWideShape<P, N, ST, 16>::NT, 0, s>>>(a);
-        else
-            gdn_wide_kernel<P, N, ST, 16, false><<<blocks, GdnWideShape<P, N, ST, 16>::NT, 0, s>>>(a);
-    } else {
-        if (a.r.io_bf16)
-            gdn_wide_kernel<P, N, ST, kMaxRing, true><<<blocks, GdnWideShape<P, N, ST, kMaxRing>::NT, 0, s>>>(a);
-        else
-            gdn_wide_kernel<P, N, ST, kMaxRing, false><<<blocks, GdnWideShape<P, N, ST, kMaxRing>::NT, 0, s>>>(a);
-    }
-    return hipGetLastError();
+    constexpr int PR = P == 128 ? 64 : P;
+    if (a.r.L <= 16) return launch_gdn_wide_lm<P, N, ST, 16, PR>(a, s);
+    return launch_gdn_wide_lm<P, N, ST, kMaxRing, PR>(a, s);
 }
 
 template <int P, int N>
