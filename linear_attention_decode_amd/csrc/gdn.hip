@@ -40,16 +40,18 @@ namespace replay {
 // ---------------------------------------------------------------------------
 // Output-only route: decode (W = 1) and verify (W <= kMaxWindow)
 
-// PR of the head's P rows per workgroup: a 128 x 128 head is streamed by two
-// workgroups of 64 rows (4 + 1 wavefronts each; six fit a compute unit where
-// three of 8 + 1 did), each running the whole chain for its own rows.
-template <int P, int N, int WM, int LM, bool IOB, int PR = P, int ST = ST_F32>
+// The decode kernel's shape: PR of the head's P rows per workgroup (a 128 x
+// 128 float32 head is streamed by two workgroups of 64 rows, 4 + 1 wavefronts
+// each; six fit a compute unit where three of 8 + 1 did), or HPW whole heads
+// of one group (low-precision copies: their small tiles streamed as one
+// taller tile, one chain wavefront a head).
+template <int P, int N, int LM, bool IOB, int PR, int ST, int HPW>
 struct GdnShape {
-    using Sh = DecodeShape<PR, N, ST, WM>;
+    static_assert(P % PR == 0 && (HPW == 1 || PR == P), "row blocks of one head, or whole heads");
+    using Sh = DecodeShape<PR * HPW, N, ST, 1>;
     static constexpr int SPL = P / PR;            // workgroups a head
     static constexpr int NTS = Sh::NTS;           // streaming threads
-    static constexpr int NT = NTS + 64;           // + the chain wavefront
-    static_assert(P % PR == 0, "whole row blocks");
+    static constexpr int NT = NTS + 64 * HPW;     // + a chain wavefront a head
 };
 
 // Rows 0..count-1 (count <= ROWS) of COLS io elements each, row j read from
@@ -218,32 +220,31 @@ __device__ __forceinline__ void gdn_chain_wave(const RingView &r, int lane, int 
 // Abstract: a low-precision checkpoint serves the outputs).  A copy's values
 // are widened exactly and dotted with the float32 w_0; e4m3 sums take the
 // head's scale, FP4 sums each chunk's block scale (exact powers of two).
-template <int P, int N, int WM, int LM, bool IOB, int PR, int ST>
-__global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB, PR, ST>::NT)) void gdn_verify_kernel(DecodeArgs args) {
-    using GS = GdnShape<P, N, WM, LM, IOB, PR, ST>;
+template <int P, int N, int LM, bool IOB, int PR, int ST, int HPW>
+__global__ __launch_bounds__((GdnShape<P, N, LM, IOB, PR, ST, HPW>::NT)) void gdn_verify_kernel(DecodeArgs args) {
+    using GS = GdnShape<P, N, LM, IOB, PR, ST, HPW>;
     using Sh = typename GS::Sh;
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
     using RR = RowReduce<ITER, LPR>;
     static_assert(ST != ST_F32 || VEC == 4, "float32 chunks");
 
-    __shared__ __align__(16) float s_k[LM][N];
-    __shared__ __align__(16) float s_v[LM][PR];
-    __shared__ __align__(16) float s_w0[WM][N];
-    __shared__ float s_r[WM][PR];
+    __shared__ __align__(16) float s_k[HPW][LM][N];
+    __shared__ __align__(16) float s_v[HPW][LM][PR];
+    __shared__ __align__(16) float s_w0[HPW][1][N];
+    __shared__ float s_r[HPW][1][PR];
 
     const RingView &r = args.r;
-    const int W = args.W;
-    // consecutive workgroups: the row blocks of a head, then the heads of a
-    // group (same compute die, whose L2 holds the group's k rows)
+    // consecutive workgroups: the row blocks of a head (or the head pairs),
+    // then the heads of a group (same compute die, whose L2 holds the
+    // group's k rows)
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
     const int H = r.H;
-    const int hb = lid / GS::SPL, p0 = (lid % GS::SPL) * PR;
-    const int b = hb / H, h = hb % H;
-    const int g = (h * r.G) / H;
+    const int hb = lid / GS::SPL, p0 = (lid % GS::SPL) * PR;   // (HPW > 1: SPL = 1, p0 = 0)
+    const int b = hb / (H / HPW), h0 = (hb % (H / HPW)) * HPW;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const size_t bh = (size_t)b * H + h;
-    const size_t tile = bh * (size_t)(P * N) + (size_t)p0 * N;
+    const size_t bh0 = (size_t)b * H + h0;
+    const size_t tile = bh0 * (size_t)(P * N) + (size_t)p0 * N;
 
     const int base = r.base[b];
     const int pos = r.pos[b];
@@ -258,97 +259,96 @@ __global__ __launch_bounds__((GdnShape<P, N, WM, LM, IOB, PR, ST>::NT)) void gdn
                 ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
         }
     }
-    if (count < W) {   // uniform over the workgroup
-        for (int i = tid; i < W * PR; i += GS::NT)
-            args.y[(((size_t)b * W + i / PR) * H + h) * P + p0 + i % PR] = __builtin_nanf("");
+    if (count < 1) {   // uniform over the workgroup
+        for (int i = tid; i < HPW * PR; i += GS::NT) args.y[(bh0 + i / PR) * P + p0 + i % PR] = __builtin_nanf("");
         if (tid == 0) raise_seq_error(r.err, b, REPLAY_SEQERR_TOO_FEW);
         return;
     }
-    if (wave == NTS / 64)
-        gdn_chain_wave<P, N, WM, LM, IOB, PR>(r, lane, b, g, bh, base, count, W, p0, s_k, s_v, s_w0, s_r);
+    if (wave >= NTS / 64) {
+        const int hl = wave - NTS / 64;
+        const int h = h0 + hl;
+        gdn_chain_wave<P, N, 1, LM, IOB, PR>(r, lane, b, (h * r.G) / H, bh0 + hl, base, count, 1, p0, s_k[hl],
+                                             s_v[hl], s_w0[hl], s_r[hl]);
+    }
     __syncthreads();
-    if (wave == NTS / 64) return;
+    if (wave >= NTS / 64) return;
 
-    // S0 w_0 for every position: partial sums over this lane's chunks, then
-    // the row reduction across the LPR lanes of a row
+    // S0 w_0: partial sums over this lane's chunks (each chunk's rows are of
+    // one head: w_0 of that head), then the row reduction across the LPR lanes
     const int col0 = (tid % LPR) * VEC;
-    float part[ITER][WM];
-    if constexpr (ST == ST_F32) {
+    float part[ITER][1];
 #pragma unroll
-        for (int w = 0; w < WM; ++w) {
-            f32x4 q = {0.f, 0.f, 0.f, 0.f};
-            if (w < W) q = *reinterpret_cast<const f32x4 *>(&s_w0[w][col0]);
-#pragma unroll
-            for (int i = 0; i < ITER; ++i) {
-                const f32x4 x = ch[i].raw;
-                part[i][w] = fmaf(x.x, q.x, fmaf(x.y, q.y, fmaf(x.z, q.z, x.w * q.w)));
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) {
+    for (int i = 0; i < ITER; ++i) {
+        const int hl = HPW == 1 ? 0 : (i * RPI + tid / LPR) / PR;
+        if constexpr (ST == ST_F32) {
+            const f32x4 q = *reinterpret_cast<const f32x4 *>(&s_w0[hl][0][col0]);
+            const f32x4 x = ch[i].raw;
+            part[i][0] = fmaf(x.x, q.x, fmaf(x.y, q.y, fmaf(x.z, q.z, x.w * q.w)));
+        } else {
             float x[VEC];
             ch[i].widen(x, 1.0f);   // the codes' values, unscaled
+            float acc = 0.f;
 #pragma unroll
-            for (int w = 0; w < WM; ++w) {
-                float acc = 0.f;
-#pragma unroll
-                for (int e4 = 0; e4 < VEC / 4; ++e4) {
-                    f32x4 q = {0.f, 0.f, 0.f, 0.f};
-                    if (w < W) q = *reinterpret_cast<const f32x4 *>(&s_w0[w][col0 + 4 * e4]);
-                    acc = fmaf(x[4 * e4], q.x, acc);
-                    acc = fmaf(x[4 * e4 + 1], q.y, acc);
-                    acc = fmaf(x[4 * e4 + 2], q.z, acc);
-                    acc = fmaf(x[4 * e4 + 3], q.w, acc);
-                }
-                if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
-                part[i][w] = acc;
+            for (int e4 = 0; e4 < VEC / 4; ++e4) {
+                const f32x4 q = *reinterpret_cast<const f32x4 *>(&s_w0[hl][0][col0 + 4 * e4]);
+                acc = fmaf(x[4 * e4], q.x, acc);
+                acc = fmaf(x[4 * e4 + 1], q.y, acc);
+                acc = fmaf(x[4 * e4 + 2], q.z, acc);
+                acc = fmaf(x[4 * e4 + 3], q.w, acc);
             }
+            if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
+            part[i][0] = acc;
         }
     }
-    RR::template run<WM>(part, lane);
-    const float sc = ST == ST_FP8 ? static_cast<const float *>(args.scale)[bh] : 1.0f;   // the head's e4m3 scale
+    RR::template run<1>(part, lane);
     if (RR::writer(lane)) {
         const int hi = RR::halving_index(lane);
 #pragma unroll
         for (int e = 0; e < RR::FINAL; ++e) {
-            const int p = (e + RR::FINAL * hi) * RPI + tid / LPR;
-#pragma unroll
-            for (int w = 0; w < WM; ++w)
-                if (w < W) args.y[(((size_t)b * W + w) * H + h) * P + p0 + p] = sc * part[e][w] + s_r[w][p];
+            const int row = (e + RR::FINAL * hi) * RPI + tid / LPR;   // of the HPW stacked row blocks
+            const int hl = HPW == 1 ? 0 : row / PR, p = HPW == 1 ? row : row % PR;
+            const float sc = ST == ST_FP8 ? static_cast<const float *>(args.scale)[bh0 + hl] : 1.0f;   // e4m3 head scale
+            args.y[(bh0 + hl) * P + p0 + p] = sc * part[e][0] + s_r[hl][0][p];
         }
     }
 }
 
-template <int P, int N, int ST, int WM, int LM>
-static hipError_t launch_gdn_verify_lm(const DecodeArgs &a, hipStream_t s) {
-    // heads of 128 rows: two workgroups of 64 (with whole heads the copy
-    // kernels took 78 to 99 registers, three or four workgroups to a compute
-    // unit), except for FP4 copies, whose 4 KiB halves stream too little per chain
-    // (measured, B=256 H=32: bf16 85.9 -> 64.7 us, e4m3 59.0 -> 55.3 us,
-    // FP4 46.9 -> 51.8 us a launch)
-    constexpr int PR = P == 128 && ST != ST_FP4 ? 64 : P;
-    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H * (P / PR));
+template <int P, int N, int ST, int LM, int PR, int HPW>
+static hipError_t launch_gdn_decode_lm(const DecodeArgs &a, hipStream_t s) {
+    const unsigned blocks = (unsigned)((size_t)a.r.B * a.r.H * (P / PR) / HPW);
     if (a.r.io_bf16)
-        gdn_verify_kernel<P, N, WM, LM, true, PR, ST><<<blocks, GdnShape<P, N, WM, LM, true, PR, ST>::NT, 0, s>>>(a);
+        gdn_verify_kernel<P, N, LM, true, PR, ST, HPW><<<blocks, GdnShape<P, N, LM, true, PR, ST, HPW>::NT, 0, s>>>(a);
     else
-        gdn_verify_kernel<P, N, WM, LM, false, PR, ST><<<blocks, GdnShape<P, N, WM, LM, false, PR, ST>::NT, 0, s>>>(a);
+        gdn_verify_kernel<P, N, LM, false, PR, ST, HPW><<<blocks, GdnShape<P, N, LM, false, PR, ST, HPW>::NT, 0, s>>>(a);
     return hipGetLastError();
 }
 
-template <int P, int N, int ST, int WM>
-static hipError_t launch_gdn_verify_w(const DecodeArgs &a, hipStream_t s) {
-    if (a.r.L <= 16) return launch_gdn_verify_lm<P, N, ST, WM, 16>(a, s);
-    return launch_gdn_verify_lm<P, N, ST, WM, kMaxRing>(a, s);
+// Float32 and bf16 tiles of 128 rows: two workgroups of 64 (with whole heads
+// the copy kernels took 78 to 99 registers, three or four workgroups to a
+// compute unit; bf16 85.9 -> 64.7 us a launch at B=256 H=32).  e4m3 and FP4
+// copies: two heads of a group a workgroup, whole (their 8 and 16 KiB tiles
+// stream in less time than a head's chain takes).
+template <int P, int N, int ST, int LM>
+static hipError_t launch_gdn_decode_st(const DecodeArgs &a, hipStream_t s) {
+    constexpr bool PAIR = ST == ST_FP8 || ST == ST_FP4;
+    if (PAIR && (a.r.H / a.r.G) % 2 == 0) return launch_gdn_decode_lm<P, N, ST, LM, P, 2>(a, s);
+    constexpr int PR = P == 128 && !PAIR ? 64 : P;
+    return launch_gdn_decode_lm<P, N, ST, LM, PR, 1>(a, s);
+}
+
+template <int P, int N, int ST>
+static hipError_t launch_gdn_decode_l(const DecodeArgs &a, hipStream_t s) {
+    if (a.r.L <= 16) return launch_gdn_decode_st<P, N, ST, 16>(a, s);
+    return launch_gdn_decode_st<P, N, ST, kMaxRing>(a, s);
 }
 
 template <int P, int N>
 static hipError_t launch_gdn_decode_pn(int st, const DecodeArgs &a, hipStream_t s) {
     switch (st) {
-        case ST_F32: return launch_gdn_verify_w<P, N, ST_F32, 1>(a, s);
-        case ST_BF16: return launch_gdn_verify_w<P, N, ST_BF16, 1>(a, s);
-        case ST_FP8: return launch_gdn_verify_w<P, N, ST_FP8, 1>(a, s);
-        case ST_FP4: return launch_gdn_verify_w<P, N, ST_FP4, 1>(a, s);
+        case ST_F32: return launch_gdn_decode_l<P, N, ST_F32>(a, s);
+        case ST_BF16: return launch_gdn_decode_l<P, N, ST_BF16>(a, s);
+        case ST_FP8: return launch_gdn_decode_l<P, N, ST_FP8>(a, s);
+        case ST_FP4: return launch_gdn_decode_l<P, N, ST_FP4>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
