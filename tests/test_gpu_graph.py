@@ -8,7 +8,10 @@ work and a synchronisation in between, the outputs, pos, base and the error
 bits must equal the twin's bit for bit, and at the end an eager flush of
 both must leave identical checkpoints.  The copy-mode steps end in a flush
 kernel that the handle may skip on its host-side count bounds, so a capture
-taken while no sequence was due must still record it."""
+taken while no sequence was due must still record it.  Gated DeltaNet
+layers (their step is the append, output-only and fold launches in turn;
+their rounds the flush, append and matrix-core verify) are recorded the
+same way."""
 import numpy as np
 import pytest
 import torch
@@ -26,12 +29,25 @@ def _workload(layer, P=64, N=128):
                           config=synth.CONFIG_ID["misc"], layer=500 + layer)
 
 
-def _pair(w, rc):
+def _pair(w, rc, rule="mamba2"):
     import linear_attention_decode_amd as lad
     kw = {} if rc is None else {"read_copy": rc}
     mk = lambda: lad.ReplayLayer(w.batch, w.heads, w.groups, w.head_dim, w.state_dim, L, io_dtype="bf16",
-                                 device=gu.DEV, **kw)
+                                 device=gu.DEV, rule=rule, **kw)
     return mk(), mk()
+
+
+class _GdnInputs(gu.DevInputs):
+    """Gated DeltaNet inputs (unit-length q, k; beta in the dt slot, alpha in the a slot)."""
+
+    def __init__(self, w, t0, t1):
+        self.w = w
+        self.t0 = t0
+        self.t = {k: gu.to_dev(v) for k, v in synth.gdn_inputs(w, t0, t1).items()}
+
+
+def _inputs(w, t0, t1, rule):
+    return _GdnInputs(w, t0, t1) if rule == "gdn" else gu.DevInputs(w, t0, t1)
 
 
 def _same_state(e, g, what):
@@ -41,15 +57,17 @@ def _same_state(e, g, what):
     assert (we, pe) == (wg, pg), (what, pe, pg)
 
 
-@pytest.mark.parametrize("rc,layers,P,N", [(None, 1, 64, 128), ("fp8", 1, 64, 128), ("bf16", 1, 64, 128),
-                                           (None, 3, 64, 128), (None, 2, 128, 128), ("fp8", 1, 128, 128)])
-def test_graph_steps(rc, layers, P, N):
+@pytest.mark.parametrize("rc,layers,P,N,rule", [(None, 1, 64, 128, "mamba2"), ("fp8", 1, 64, 128, "mamba2"),
+                                                ("bf16", 1, 64, 128, "mamba2"), (None, 3, 64, 128, "mamba2"),
+                                                (None, 2, 128, 128, "mamba2"), ("fp8", 1, 128, 128, "mamba2"),
+                                                (None, 2, 128, 128, "gdn"), ("fp4", 1, 64, 128, "gdn")])
+def test_graph_steps(rc, layers, P, N, rule):
     """128 x 128 heads: two workgroups per head in the single-launch step."""
-    gu.note(f"graph of steps copy={rc} layers={layers} P={P} N={N}")
+    gu.note(f"graph of steps copy={rc} layers={layers} P={P} N={N} rule={rule}")
     T0, T = 2, 3 * L + 3
     ws = [_workload(i, P, N) for i in range(layers)]
-    devs = [gu.DevInputs(w, 0, T) for w in ws]
-    pairs = [_pair(w, rc) for w in ws]
+    devs = [_inputs(w, 0, T, rule) for w in ws]
+    pairs = [_pair(w, rc, rule) for w in ws]
     B, H, P = ws[0].batch, ws[0].heads, ws[0].head_dim
     ys = [(torch.empty((B, H, P), dtype=torch.float32, device=gu.DEV),
            torch.empty((B, H, P), dtype=torch.float32, device=gu.DEV)) for _ in ws]
@@ -90,18 +108,19 @@ def test_graph_steps(rc, layers, P, N):
         g.close()
 
 
-@pytest.mark.parametrize("rc,W", [(None, 4), (None, 6), ("fp8", 4)])
-def test_graph_verify_rounds(rc, W):
+@pytest.mark.parametrize("rc,W,rule", [(None, 4, "mamba2"), (None, 6, "mamba2"), ("fp8", 4, "mamba2"),
+                                       (None, 4, "gdn"), ("fp8", 5, "gdn")])
+def test_graph_verify_rounds(rc, W, rule):
     """A verify round + rollback in one graph; accepted counts change per
     replay.  W = 4 and 6: the single-launch round (register sums, matrix
     cores); an e4m3 copy: flush, append and verify in turn, where the flush
     is one the bounds would skip at capture."""
     R = 12
-    gu.note(f"graph of verify rounds copy={rc} W={W}")
+    gu.note(f"graph of verify rounds copy={rc} W={W} rule={rule}")
     w = _workload(7)
     B, H, P = w.batch, w.heads, w.head_dim
-    dev = gu.DevInputs(w, 0, (R + 1) * W)
-    e, g = _pair(w, rc)
+    dev = _inputs(w, 0, (R + 1) * W, rule)
+    e, g = _pair(w, rc, rule)
     accept = np.random.default_rng(3).integers(0, W + 1, size=(R + 1, B))
     nrej = [torch.from_numpy((W - a).astype(np.int32)).to(gu.DEV) for a in accept]
     ye = torch.empty((B, W, H, P), dtype=torch.float32, device=gu.DEV)

@@ -4,8 +4,10 @@ instead of the layer's `sync` buffer.  Through the C ABI, against
 replay_step on the same inputs: outputs, checkpoints, copies and pointers
 bit for bit, step after step (folds included), for a layer of 6 sequences
 and then, on the same static array, a smaller layer of 2; a float32
-checkpoint (one fused launch) and an e4m3 copy (the copy-mode launch, then
-the flush kernel, both on the static counters).  A layer needing more
+checkpoint (one fused launch), an e4m3 copy (the copy-mode launch, then
+the flush kernel, both on the static counters) and a Gated DeltaNet layer
+(append, output-only and fold launches, the append and the fold on the
+static counters).  A layer needing more
 counters than the array holds is refused before any launch; a layer built
 without counters refuses the calls that need them."""
 import numpy as np
@@ -24,15 +26,24 @@ def _layer(w, **kw):
                            io_dtype=w.io_dtype, device=gu.DEV, **kw)
 
 
-@pytest.mark.parametrize("copy", [None, "fp8"])
-def test_step_static_equals_step(copy):
+class _GdnInputs(gu.DevInputs):
+    """Gated DeltaNet inputs (unit-length q, k; beta in the dt slot, alpha in the a slot)."""
+
+    def __init__(self, w, t0, t1):
+        self.w = w
+        self.t0 = t0
+        self.t = {k: gu.to_dev(v) for k, v in synth.gdn_inputs(w, t0, t1).items()}
+
+
+@pytest.mark.parametrize("copy,rule", [(None, "mamba2"), ("fp8", "mamba2"), (None, "gdn")])
+def test_step_static_equals_step(copy, rule):
     for B in (6, 2):                      # two layers in a row, the second smaller
         w = synth.Workload(batch=B, heads=8, groups=2, head_dim=64, state_dim=128, ring_len=4, io_dtype="bf16",
                            config=synth.CONFIG_ID["misc"], layer=400 + B)
         T = 3 * w.ring_len + 1
-        gu.note(f"step_static vs step B={B} copy={copy}")
-        dev = gu.DevInputs(w, 0, T)
-        kw = {} if copy is None else {"read_copy": copy}
+        gu.note(f"step_static vs step B={B} copy={copy} rule={rule}")
+        dev = _GdnInputs(w, 0, T) if rule == "gdn" else gu.DevInputs(w, 0, T)
+        kw = {"rule": rule} if copy is None else {"read_copy": copy, "rule": rule}
         st = _layer(w, counters=False, **kw)
         ref = _layer(w, **kw)
         assert st.sync is None
