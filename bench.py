@@ -434,7 +434,7 @@ def bench_decode(args):
         + B * L * 2 * (H * P * 2 + H * 8 + 2 * G * N * 2)            # appends: read input + write ring
     window_eager = L * eager_bytes(w)
     if copy_step:
-        traffic = _counter_traffic(STEP_COPY_SOURCES, f"step_copy_kernel_{args.read}_b256_h128_counters.txt")
+        traffic = _counter_traffic(STEP_COPY_SOURCES, f"step_copy_fused_kernel_{args.read}_b256_h128_counters.txt")
     elif args.api == "step":
         traffic = _counter_traffic(STEP_SOURCES, "step_kernel_f32_b256_h128_counters.txt")
     else:

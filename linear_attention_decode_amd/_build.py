@@ -21,12 +21,12 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-I", os.path.join(HERE, "..", "include")]
 
 
-# Per-file extra flags.  step.hip, verify_step.hip, flush.hip, flush_shared.hip: one lane per
-# workgroup adds to an arrival counter and needs the old value only at its very end; the atomic
-# optimizer would rewrite that add into a wave-wide form whose readfirstlane
-# waits for the atomic where it is issued.
+# Per-file extra flags.  step.hip, step_copy.hip, verify_step.hip, flush.hip, flush_shared.hip,
+# gdn.hip: one lane per wavefront or workgroup adds to an arrival counter and needs the old value
+# only at its very end; the atomic optimizer would rewrite that add into a wave-wide form whose
+# readfirstlane waits for the atomic (and every load before it) where it is issued.
 EXTRA = {f: ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
-         for f in ("step.hip", "verify_step.hip", "flush.hip", "flush_shared.hip")}
+         for f in ("step.hip", "step_copy.hip", "verify_step.hip", "flush.hip", "flush_shared.hip", "gdn.hip")}
 # flush_shared.hip: MFMA accumulators in VGPRs (the AGPR form copied every
 # element in and out of the accumulators).
 EXTRA["flush_shared.hip"] += ["-mllvm", "-amdgpu-mfma-vgpr-form"]

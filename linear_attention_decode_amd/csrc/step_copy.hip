@@ -17,7 +17,9 @@
 // takes this step's token from the inputs and arrives at its group's
 // counter.  A writer workgroup per sequence, after all of them in the grid,
 // copies the token into ring slot pos mod L and arrives too; the last
-// arrival moves pos.
+// arrival moves pos.  Where the stacked tiles stream with one wavefront per
+// head (L <= 16, P <= 64), step_copy_fused_kernel gives each streaming
+// wavefront its head's ring work instead.
 // Outputs equal those of the append and decode kernels run in turn, bit for
 // bit.
 #include "step_common.h"
@@ -144,9 +146,123 @@ __global__ __launch_bounds__((StepCopyLaunch<P, N, ST, LM, HPW>::NT)) void step_
     }
 }
 
+// The same step with no wavefront set aside for the ring (L <= 16, P <= 64,
+// and copy tiles that stream with one wavefront per head): every wavefront
+// reads the pointer, issues its share of the stacked tiles, then its head's
+// ring loads, and forms the row dot products while those fly.  A workgroup
+// is half as many wavefronts, so a CU holds more of them (register-bound:
+// 5 to 8 per SIMD instead of 4 workgroups of 8 wavefronts).  The streaming
+// and ring arithmetic is the kernel's above, value for value.
+template <int P, int N, int ST, int HPW>
+struct StepCopyFused {
+    using Sh = DecodeShape<P * HPW, N, ST, 1, false>;
+    static constexpr int NT = Sh::NTS;
+    static constexpr bool fits = HPW > 1 && P <= 64 && Sh::NTS == 64 * HPW;
+};
+
+template <int P, int N, int ST, int HPW>
+__global__ __launch_bounds__(64 * HPW) __attribute__((amdgpu_waves_per_eu(5))) void step_copy_fused_kernel(StepArgs args) {
+    using Sh = typename StepCopyFused<P, N, ST, HPW>::Sh;
+    constexpr int LM = 16;
+    constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+    static_assert(NTS == 64 * HPW, "one wavefront per head");
+    using RR = RowReduce<ITER, LPR>;
+
+    __shared__ float s_r[HPW][P];
+    __shared__ float s_abar[HPW];
+    __shared__ __align__(16) float s_sw[HPW][LM];
+
+    const int H = args.H, G = args.G, L = args.L;
+    const int HW = H / HPW;
+    const int ncomp = args.B * HW;   // compute workgroups; one writer per sequence follows
+    if ((int)blockIdx.x >= ncomp) {
+        step_token_writer<P, N, true, false>(args, (int)blockIdx.x - ncomp, threadIdx.x, blockDim.x);
+        return;
+    }
+    const int lid = xcd_remap(blockIdx.x, ncomp);
+    const int b = lid / HW, h0 = (lid % HW) * HPW;
+    const int g = (h0 * G) / H;   // the HPW heads share this group
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int hl = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wavefront's ring head
+    const size_t bh0 = (size_t)b * H + h0;
+    const size_t tile = bh0 * (size_t)(P * N);
+
+    const int base = args.base[b];
+    const int pos = args.pos[b];
+    // the copy's tile chunks and the (group-shared) query as bf16 pairs
+    Chunk<ST, VEC> ch[ITER];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        if constexpr (ST == ST_FP4)
+            ch[i].load_mx(args.copy, args.copy_scale, tile + (size_t)(i * NTS + tid) * VEC);
+        else
+            ch[i].load(args.copy, tile + (size_t)(i * NTS + tid) * VEC);
+    }
+    const int col0 = (tid % LPR) * VEC;
+    constexpr int QW = VEC / 2;
+    uint32_t qw[QW];
+    const uint32_t *row = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(args.q) +
+                                                              ((size_t)b * G + g) * N + col0);
+    if constexpr (QW % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < QW / 4; ++e) {
+            const uint4 u = reinterpret_cast<const uint4 *>(row)[e];
+            qw[4 * e] = u.x; qw[4 * e + 1] = u.y; qw[4 * e + 2] = u.z; qw[4 * e + 3] = u.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < QW; ++e) qw[e] = row[e];
+    }
+    const int cold = pos - base;
+    const bool bad = cold + 1 > L || pos == 2147483647;
+    StepRingMx<P, N, LM> sr;
+    if (!bad) sr.load(args, lane, 0, b, g, h0 + hl, bh0 + hl, base, cold);
+
+    float part[ITER][1];
+#pragma unroll
+    for (int i = 0; i < ITER; ++i) {
+        float acc = ch[i].dot_bf16(qw);
+        if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
+        part[i][0] = acc;
+    }
+    RR::template run<1>(part, lane);
+
+    if (bad) {   // sequence left unchanged
+        if (tid == 0) raise_seq_error(args.err, b, cold + 1 > L ? REPLAY_SEQERR_RING_OVERFLOW : REPLAY_SEQERR_POS_OVERFLOW);
+        for (int i = tid; i < P * HPW; i += NTS) args.y[bh0 * P + i] = __builtin_nanf("");
+        return;
+    }
+    const int prev = sr.finish(args, lane, b, g, cold, false, &s_r[hl], &s_abar[hl],
+                               static_cast<float (*)[LM + 1]>(nullptr), static_cast<float (*)[N]>(nullptr), &s_sw[hl]);
+    // LDS-only barrier: the arrival atomics finish in the background
+    lds_barrier();
+    if (RR::writer(lane)) {
+        const int hi = RR::halving_index(lane);
+#pragma unroll
+        for (int e = 0; e < RR::FINAL; ++e) {
+            const int row_ = (e + RR::FINAL * hi) * RPI + tid / LPR;   // of the HPW stacked tiles
+            const int hr = row_ / P, p = row_ % P;
+            const float sc = (ST == ST_FP8) ? static_cast<const float *>(args.copy_scale)[bh0 + hr] : 1.0f;
+            args.y[bh0 * P + row_] = s_abar[hr] * (sc * part[e][0]) + s_r[hr][p];
+        }
+    }
+    if (lane == 0 && prev == H / G - 1) {
+        // last wavefront of the group: the group arrives at the sequence's counter
+        atomicExch(args.sync + ((size_t)b * (G + 1) + g) * kSyncStride, 0);
+        step_seq_arrive(args, b, pos, false);
+    }
+}
+
 template <int P, int N, int ST, int LM>
 static hipError_t launch_sc_lm(const StepArgs &a, hipStream_t s) {
     constexpr int HPW = heads_per_wg<ST, 1>();
+    if constexpr (LM == 16 && StepCopyFused<P, N, ST, HPW>::fits) {
+        if ((a.H / a.G) % HPW == 0) {
+            const unsigned blocks = (unsigned)((size_t)a.B * a.H / HPW + a.B);
+            step_copy_fused_kernel<P, N, ST, HPW><<<blocks, StepCopyFused<P, N, ST, HPW>::NT, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
     if (HPW > 1 && (a.H / a.G) % HPW == 0) {
         const unsigned blocks = (unsigned)((size_t)a.B * a.H / HPW + a.B);
         step_copy_kernel<P, N, ST, LM, HPW><<<blocks, StepCopyLaunch<P, N, ST, LM, HPW>::NT, 0, s>>>(a);

@@ -231,6 +231,7 @@ def test_step_ignores_nan_in_unused_slots():
     (64, 128, 8, 5, 2, 12, 2, "fp8", False),       # 6 heads per group: one head per workgroup
     (128, 128, 32, 32, 2, 8, 2, "fp4", False),     # two ring wavefronts per head
     (16, 16, 4, 4, 3, 4, 1, "fp8", False),
+    (64, 64, 12, 12, 2, 8, 2, "fp4", False),       # ring shorter than 16, 64 x 64 tiles
     (64, 64, 6, 6, 2, 8, 2, "bf16", True),         # shared: the copy is the only checkpoint
     (64, 128, 16, 16, 2, 16, 2, "fp8", True),
 ])
