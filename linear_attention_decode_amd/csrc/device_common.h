@@ -428,6 +428,11 @@ struct Chunk<ST_FP4, VEC> {
     int se;
     // e: element index of the chunk's first value; scales: one byte per block of 32
     __device__ __forceinline__ void load_mx(const void *S, const void *scales, size_t e) {
+        load_codes(S, e);
+        se = (int)static_cast<const uint8_t *>(scales)[e / 32] - 127;
+    }
+    // the codes alone (the caller sets se)
+    __device__ __forceinline__ void load_codes(const void *S, size_t e) {
         const uint8_t *p = static_cast<const uint8_t *>(S) + e / 2;
         if constexpr (VEC == 32) {
             u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
@@ -440,7 +445,6 @@ struct Chunk<ST_FP4, VEC> {
         } else {
             raw[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
         }
-        se = (int)static_cast<const uint8_t *>(scales)[e / 32] - 127;
     }
     __device__ __forceinline__ void widen(float *out, float) const {
 #pragma unroll

@@ -65,7 +65,21 @@ struct StepRingMx {
 
     __device__ __forceinline__ void load(const StepArgs &A, int lane, int rw, int b, int g, int h, size_t bh,
                                          int base, int cold, int p0_ = 0) {
+        load_token(A, lane, b, g, bh, p0_);
+        load_ring(A, lane, rw, b, g, bh, base, cold);
+    }
+
+    // this step's token: a, dt and the query row (none depends on the pointer)
+    __device__ __forceinline__ void load_token(const StepArgs &A, int lane, int b, int g, size_t bh, int p0_ = 0) {
         p0 = p0_;
+        a_in = A.a[bh];
+        dt_in = A.dt[bh];
+        qrow.load(static_cast<const char *>(A.q) + ((size_t)b * A.G + g) * N * ES, lane);
+    }
+
+    // the ring's entries (and this step's v row, which joins them as entry cold)
+    __device__ __forceinline__ void load_ring(const StepArgs &A, int lane, int rw, int b, int g, size_t bh,
+                                              int base, int cold) {
         const int L = A.L;
         const size_t gring = ((size_t)b * A.G + g) * L;
         const size_t hring = bh * L;
@@ -75,10 +89,6 @@ struct StepRingMx {
         const int lastr = cold > 0 ? cold - 1 : 0;   // clamp for ring loads (never used when cold == 0)
         const int lr = lane & 15, lq = lane >> 4;
         m.j0 = 16 * rw;
-        // this step's token first, then the ring
-        a_in = A.a[bh];
-        dt_in = A.dt[bh];
-        qrow.load(static_cast<const char *>(A.q) + gin * N * ES, lane);
         const int sla = slot(lane < cold ? lane : lastr);
         a_r = A.ring_a[dta_index(b, bh, A.H, L, sla)];
         dt_r = A.ring_dt[dta_index(b, bh, A.H, L, sla)];

@@ -58,8 +58,7 @@ __global__ __launch_bounds__((StepCopyLaunch<P, N, ST, LM, HPW>::NT)) void step_
     const int b = lid / HW, h0 = (lid % HW) * HPW;
     const int g = (h0 * G) / H;   // the HPW heads share this group
     const int tid = threadIdx.x, lane = tid & 63;
-    // wave-uniform role: scalar branches, and the ring wavefronts' pointer
-    // reads go through the scalar cache
+    // wave-uniform role: scalar branches
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool streamer = wave < NTS / 64;
     const int rw = wave - NTS / 64;
@@ -187,36 +186,48 @@ __global__ __launch_bounds__(64 * HPW) __attribute__((amdgpu_waves_per_eu(5))) v
     const size_t bh0 = (size_t)b * H + h0;
     const size_t tile = bh0 * (size_t)(P * N);
 
-    const int base = args.base[b];
-    const int pos = args.pos[b];
-    // the copy's tile chunks and the (group-shared) query as bf16 pairs
+    // the pointer through the scalar cache (b is uniform; nothing in this
+    // launch writes pos or base before every wavefront of the sequence has
+    // read them)
+    using cint = const __attribute__((address_space(4))) int;
+    const int base = *((cint *)args.base + b);
+    const int pos = *((cint *)args.pos + b);
+    // this step's token (the group's query row, one word a lane, serves the
+    // ring and the tile's dot products), then the copy's tile chunks
+    StepRingMx<P, N, LM> sr;
+    sr.load_token(args, lane, b, g, bh0 + hl);
     Chunk<ST, VEC> ch[ITER];
 #pragma unroll
     for (int i = 0; i < ITER; ++i) {
         if constexpr (ST == ST_FP4)
-            ch[i].load_mx(args.copy, args.copy_scale, tile + (size_t)(i * NTS + tid) * VEC);
+            ch[i].load_codes(args.copy, tile + (size_t)(i * NTS + tid) * VEC);
         else
             ch[i].load(args.copy, tile + (size_t)(i * NTS + tid) * VEC);
     }
-    const int col0 = (tid % LPR) * VEC;
-    constexpr int QW = VEC / 2;
-    uint32_t qw[QW];
-    const uint32_t *row = reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(args.q) +
-                                                              ((size_t)b * G + g) * N + col0);
-    if constexpr (QW % 4 == 0) {
-#pragma unroll
-        for (int e = 0; e < QW / 4; ++e) {
-            const uint4 u = reinterpret_cast<const uint4 *>(row)[e];
-            qw[4 * e] = u.x; qw[4 * e + 1] = u.y; qw[4 * e + 2] = u.z; qw[4 * e + 3] = u.w;
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < QW; ++e) qw[e] = row[e];
+    // FP4: the wavefront's ITER runs of 64 block scales (one byte per lane and
+    // chunk), one word a lane
+    uint32_t sword = 0;
+    if constexpr (ST == ST_FP4) {
+        static_assert(VEC == 32 && ITER <= 4, "one scale byte per lane and chunk, one word per lane in all");
+        const int seg = lane >> 4;
+        const size_t sb = tile / 32 + (size_t)(seg < ITER ? seg : 0) * NTS + (size_t)(tid & ~63) + 4 * (lane & 15);
+        sword = *reinterpret_cast<const uint32_t *>(static_cast<const uint8_t *>(args.copy_scale) + sb);
     }
     const int cold = pos - base;
     const bool bad = cold + 1 > L || pos == 2147483647;
-    StepRingMx<P, N, LM> sr;
-    if (!bad) sr.load(args, lane, 0, b, g, h0 + hl, bh0 + hl, base, cold);
+    if (!bad) sr.load_ring(args, lane, 0, b, g, bh0 + hl, base, cold);
+
+    // the query as bf16 pairs at this lane's columns: words (tid % LPR) QW .. + QW - 1 of the row
+    constexpr int QW = VEC / 2;
+    static_assert(RowWords<N, true>::WPL == 1, "one word of the row per lane");
+    uint32_t qw[QW];
+#pragma unroll
+    for (int e = 0; e < QW; ++e) qw[e] = (uint32_t)__shfl((int)sr.qrow.w[0], (tid % LPR) * QW + e);
+    if constexpr (ST == ST_FP4) {
+#pragma unroll
+        for (int i = 0; i < ITER; ++i)
+            ch[i].se = (int)((((uint32_t)__shfl((int)sword, 16 * i + (lane >> 2))) >> (8 * (lane & 3))) & 0xffu) - 127;
+    }
 
     float part[ITER][1];
 #pragma unroll
