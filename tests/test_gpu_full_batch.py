@@ -11,6 +11,14 @@ is covered here on all of them:
   head within 1e-4 per head (max_p |y - y_ref| / max_p |y_ref|, floored at
   1 % of the head's term magnitude: tests/parity.py), and every checkpoint
   after the last fold within 1e-4 of the oracle state;
+* the same decode layer reading an e4m3 or MX-FP4 copy of its float32
+  checkpoint (separated precisions: the copy-mode step, then the flush), 32
+  steps (2 folds): every output of every sequence against the oracle's
+  emulation of the same copy (tests/gpu_util.py assert_copy), the ring
+  integers after every step, and the float32 checkpoint after the last fold
+  within 1e-4 per head of the oracle state (page "ReplaySSM: Cache SSM
+  Inputs, Not State", Abstract: a low-precision copy serves the outputs
+  while the float32 checkpoint takes the updates);
 * speculative verify (B=256, H=64, W=5, accepted drafts ~ U{0..5}), 32 fused
   rounds through replay_verify_step: every draft's output of every sequence
   within 1e-4 per head, the ring integers of every sequence after every
@@ -65,6 +73,33 @@ def test_step_every_sequence_decode_workload():
     # T is a multiple of L: the last step folded, so the checkpoint is the state after token T
     S_gpu = layer.s_master.cpu().numpy()
     e = runs.normwise_rel_err(S_gpu, S, axes=(-2, -1))
+    print(f"  checkpoint per-head max {float(e.max()):.3e}", flush=True)
+    assert float(e.max()) <= gu.TOL_F32
+    layer.close()
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_copy_step_every_sequence_decode_workload(fmt):
+    w = synth.named("decode")
+    T, L = 32, w.ring_len
+    gu.note(f"full batch: copy-mode step, {fmt} copy, {w} T={T}")
+    dev = gu.DevInputsTorch(w, 0, T)
+    layer = _layer(w, read_copy=fmt)
+    model = oring.RingModel(w.batch, L)
+    y = torch.empty((T, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=gu.DEV)
+    for t in range(T):
+        layer.step(*dev.step(t), y[t], flush_at=L)
+        model.append(1)
+        model.flush(L)
+        gu.check_ring(layer, model, f"step {t}")
+    torch.cuda.synchronize()
+    assert layer.get_error()[0] == 0
+    x = dev.oracle()
+    S = np.zeros((w.batch, w.heads, w.head_dim, w.state_dim))
+    y_emul = runs.separated(x, S, L, fmt)   # S ends as the exact state after token T
+    gu.assert_copy(y.cpu().numpy(), y_emul, fmt, "all 256 sequences:")
+    del y_emul
+    e = runs.normwise_rel_err(layer.s_master.cpu().numpy(), S, axes=(-2, -1))
     print(f"  checkpoint per-head max {float(e.max()):.3e}", flush=True)
     assert float(e.max()) <= gu.TOL_F32
     layer.close()
