@@ -40,11 +40,26 @@ struct DecodeShape {
     // streaming threads: at most 8 chunks a lane (4096 chunks: 8 wavefronts)
     static constexpr int NTS = CHUNKS >= 4096 ? 512 : (CHUNKS < 256 ? CHUNKS : 256);
     static constexpr int ITER = CHUNKS / NTS;
-    static constexpr int LPR = N / VEC;     // lanes per state row
-    static constexpr int RPI = NTS / LPR;   // rows per iteration
+    // Lanes per state row: N / VEC, except for a float32 tile scored for a
+    // window of WM >= 2 queries.  There 8 lanes share a row and lane jp holds
+    // the row's 16-byte pieces jp, jp + 8, ... (PPL of them): a load
+    // instruction still reads whole 128-byte lines (of 8 rows), a lane adds
+    // its pieces of a row before any lane exchange, and each query's row
+    // reduction takes 3 lane steps (DPP only) in place of 5.
+    static constexpr int LPR = (ST == ST_F32 && WM >= 2 && N / VEC > 8) ? 8 : N / VEC;
+    static constexpr int PPL = N / VEC / LPR;   // pieces of one row a lane holds
+    static constexpr int RPL = ITER / PPL;      // rows a lane holds
+    static constexpr int RPI = NTS / LPR;       // rows between a lane's rows
     static_assert(VEC >= 4, "chunk too small");
     static_assert(CHUNKS % NTS == 0 && NTS % 64 == 0, "bad tiling");
     static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row group must sit in a wavefront");
+    static_assert(ITER % PPL == 0, "a lane holds whole rows");
+    // Element offset within the tile of chunk i of streaming thread tid: row
+    // (i / PPL) * RPI + tid / LPR, piece tid % LPR + LPR * (i % PPL).  With
+    // PPL = 1 this is (i * NTS + tid) * VEC: NTS contiguous chunks per i.
+    static __device__ __forceinline__ int offset(int i, int tid) {
+        return ((i / PPL) * RPI + tid / LPR) * N + VEC * (tid % LPR + LPR * (i % PPL));
+    }
 };
 
 // The ring wavefront's work for one (sequence, head): group dots, segment
@@ -251,12 +266,17 @@ __global__ __launch_bounds__((DecodeLaunch<P, N, ST, WM, LM, IOB, HPW>::NT)) voi
     using Sh = typename DL::Sh;
     constexpr int W = WM, PT = P * HPW;
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+    constexpr int PPL = Sh::PPL, RPL = Sh::RPL;
     constexpr int NR = DL::NR, NT = DL::NT;
-    using RR = RowReduce<ITER, LPR>;
+    using RR = RowReduce<RPL, LPR>;
+    // float32 tile with several pieces of a row per lane: the window's
+    // queries widened into LDS, one copy per streaming wavefront
+    constexpr bool QLDS = ST == ST_F32 && PPL > 1;
 
     __shared__ float s_r[NR][HPW][WM][P];
     __shared__ float s_abar[HPW][WM];
     __shared__ __align__(16) float s_sw[HPW][IOB ? WM : 1][IOB ? LM : 4];
+    __shared__ __align__(16) float s_qw[QLDS ? NTS / 64 : 1][QLDS ? WM : 1][QLDS ? N : 4];
 
     const RingView &r = args.r;
     const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -276,9 +296,9 @@ __global__ __launch_bounds__((DecodeLaunch<P, N, ST, WM, LM, IOB, HPW>::NT)) voi
 #pragma unroll
         for (int i = 0; i < ITER; ++i) {
             if constexpr (ST == ST_FP4)
-                ch[i].load_mx(args.S, args.scale, tile + (size_t)(i * NTS + tid) * VEC);
+                ch[i].load_mx(args.S, args.scale, tile + (size_t)Sh::offset(i, tid));
             else
-                ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
+                ch[i].load(args.S, tile + (size_t)Sh::offset(i, tid));
         }
     }
     const int count = pos - base;
@@ -291,7 +311,7 @@ __global__ __launch_bounds__((DecodeLaunch<P, N, ST, WM, LM, IOB, HPW>::NT)) voi
         return;
     }
 
-    float part[ITER][WM];
+    float part[RPL][WM];
     if (tid < NTS) {
         // queries of the window positions at this lane's columns
         const int col0 = (tid % LPR) * VEC;
@@ -326,6 +346,39 @@ __global__ __launch_bounds__((DecodeLaunch<P, N, ST, WM, LM, IOB, HPW>::NT)) voi
                     float acc = ch[i].dot_bf16(qw[w]);
                     if constexpr (ST == ST_FP4) acc = ldexpf(acc, ch[i].se);   // the block's scale, exact
                     part[i][w] = acc;
+                }
+            }
+        } else if constexpr (QLDS) {
+            // This wavefront widens the window's queries into its own LDS
+            // rows (a wavefront-level exchange, no workgroup barrier), then
+            // forms the row sums one query at a time from its pieces.
+            float *sq = &s_qw[tid >> 6][0][0];
+            constexpr int QP = WM * N / 4;   // 4-element pieces of the queries
+#pragma unroll
+            for (int k0 = 0; k0 < QP; k0 += 64) {
+                const int k = k0 + lane;
+                if (k < QP) {
+                    const int w = k / (N / 4), c = 4 * (k % (N / 4));
+                    IoVec<IOB, 4> t;
+                    t.load(r.q, (gring + ring_slot(bmod, count - W + w, L)) * N + c);
+                    float f[4];
+                    t.widen(f);
+                    *reinterpret_cast<f32x4 *>(sq + w * N + c) = f32x4{f[0], f[1], f[2], f[3]};
+                }
+            }
+            wave_lds_sync();
+            const int jp = tid % LPR;
+#pragma unroll
+            for (int w = 0; w < WM; ++w) {
+                f32x4 qp[PPL];
+#pragma unroll
+                for (int u = 0; u < PPL; ++u) qp[u] = *reinterpret_cast<const f32x4 *>(sq + w * N + VEC * (jp + LPR * u));
+#pragma unroll
+                for (int rr = 0; rr < RPL; ++rr) {
+                    f32x4 xp[PPL];
+#pragma unroll
+                    for (int u = 0; u < PPL; ++u) xp[u] = ch[rr * PPL + u].raw;
+                    part[rr][w] = pieces_dot<PPL>(xp, qp);
                 }
             }
         } else {

@@ -553,6 +553,23 @@ struct RowReduce {
     }
 };
 
+// A lane's partial sum of one state row against one query: its PPL float32
+// pieces of the row dotted with the query's matching pieces, piece by piece
+// and element by element.  Every kernel whose row sums must agree bit for bit
+// forms them with this one function.
+template <int PPL>
+__device__ __forceinline__ float pieces_dot(const f32x4 (&x)[PPL], const f32x4 (&q)[PPL]) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < PPL; ++u) {
+        acc = fmaf(x[u].x, q[u].x, acc);
+        acc = fmaf(x[u].y, q[u].y, acc);
+        acc = fmaf(x[u].z, q[u].z, acc);
+        acc = fmaf(x[u].w, q[u].w, acc);
+    }
+    return acc;
+}
+
 // Lanes of one wavefront exchanging data through LDS, with no workgroup
 // barrier: every lane's writes must come before any lane's reads.  Program
 // order alone does not give that, since the compiler may split the

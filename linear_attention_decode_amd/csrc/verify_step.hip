@@ -336,10 +336,14 @@ constexpr int vs_waves() { return P == 64 && N == 128 ? 8 : 1; }
 
 template <int P, int N, int W>
 __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu_waves_per_eu(vs_waves<P, N>()))) void verify_step_kernel(StepArgs args) {
-    using Sh = StepShape<P, N>;
+    // the register route tiles the checkpoint as the register verify kernel
+    // does for this window (decode_impl.h), so that their row sums agree
+    using Sh = DecodeShape<P, N, ST_F32, W>;
+    static_assert(Sh::NTS == StepShape<P, N>::NTS && Sh::VEC == 4, "verify tiling");
     constexpr int VEC = Sh::VEC, NTS = Sh::NTS, ITER = Sh::ITER, LPR = Sh::LPR, RPI = Sh::RPI;
+    constexpr int PPL = Sh::PPL, RPL = Sh::RPL;
     constexpr int LM = kVsRing;
-    using RR = RowReduce<ITER, LPR>;
+    using RR = RowReduce<RPL, LPR>;
 
     __shared__ float s_r[W][P];
     __shared__ float s_abar[W];
@@ -370,7 +374,7 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
     const int rw = wave - NTS / 64;
     const size_t bh = (size_t)b * H + h;
     const size_t tile = bh * (size_t)(P * N);
-    const int col0 = (tid % LPR) * VEC;
+    const int jp = tid % LPR;   // piece of a row: chunk i covers columns VEC * (jp + LPR * (i % PPL))
 
     // Only the ring wavefronts read the pointer (each arrives after its
     // read).  They publish the route in LDS at a first barrier, which the
@@ -404,7 +408,7 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
         asm volatile("" ::: "memory");
         Chunk<ST_F32, VEC> ch[ITER];
 #pragma unroll
-        for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)(i * NTS + tid) * VEC);
+        for (int i = 0; i < ITER; ++i) ch[i].load(args.S, tile + (size_t)Sh::offset(i, tid));
 #pragma unroll
         for (int i = 0; i < QI; ++i) {
             const int piece = tid + i * NTS < QP ? tid + i * NTS : QP - 1;
@@ -418,18 +422,20 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
         auto sums = [&](const auto &tile_chunk, Fin &fin) {
 #pragma unroll
             for (int w = 0; w < W; ++w) {
-                const f32x4 qw = *reinterpret_cast<const f32x4 *>(&s_q[w][col0]);
-                float part[ITER][1];
+                f32x4 qp[PPL];
 #pragma unroll
-                for (int i = 0; i < ITER; ++i) {
-                    float x[VEC];
-                    tile_chunk(i, x);
-                    float acc = 0.f;
-                    acc = fmaf(x[0], qw.x, acc);
-                    acc = fmaf(x[1], qw.y, acc);
-                    acc = fmaf(x[2], qw.z, acc);
-                    acc = fmaf(x[3], qw.w, acc);
-                    part[i][0] = acc;
+                for (int u = 0; u < PPL; ++u) qp[u] = *reinterpret_cast<const f32x4 *>(&s_q[w][VEC * (jp + LPR * u)]);
+                float part[RPL][1];
+#pragma unroll
+                for (int rr = 0; rr < RPL; ++rr) {
+                    f32x4 xp[PPL];
+#pragma unroll
+                    for (int u = 0; u < PPL; ++u) {
+                        float x[VEC];
+                        tile_chunk(rr * PPL + u, x);
+                        xp[u] = f32x4{x[0], x[1], x[2], x[3]};
+                    }
+                    part[rr][0] = pieces_dot<PPL>(xp, qp);
                 }
                 RR::template run<1>(part, lane);
 #pragma unroll
@@ -459,20 +465,26 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
             const int c = s_fcount;
 #pragma unroll 1   // keeps the LDS operands of one entry in registers at a time
             for (int j = 0; j < c; ++j) {
-                const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_K[j][col0]);
+                float uu[RPL];
 #pragma unroll
-                for (int i = 0; i < ITER; ++i) {
-                    const float u = s_U[i * RPI + tid / LPR][j];
-                    x[i][0] = fmaf(u, kk.x, x[i][0]);
-                    x[i][1] = fmaf(u, kk.y, x[i][1]);
-                    x[i][2] = fmaf(u, kk.z, x[i][2]);
-                    x[i][3] = fmaf(u, kk.w, x[i][3]);
+                for (int rr = 0; rr < RPL; ++rr) uu[rr] = s_U[rr * RPI + tid / LPR][j];
+#pragma unroll
+                for (int q = 0; q < PPL; ++q) {
+                    const f32x4 kk = *reinterpret_cast<const f32x4 *>(&s_K[j][VEC * (jp + LPR * q)]);
+#pragma unroll
+                    for (int rr = 0; rr < RPL; ++rr) {
+                        const int i = rr * PPL + q;
+                        x[i][0] = fmaf(uu[rr], kk.x, x[i][0]);
+                        x[i][1] = fmaf(uu[rr], kk.y, x[i][1]);
+                        x[i][2] = fmaf(uu[rr], kk.z, x[i][2]);
+                        x[i][3] = fmaf(uu[rr], kk.w, x[i][3]);
+                    }
                 }
             }
 #pragma unroll
             for (int i = 0; i < ITER; ++i) {
                 f32x4 o = {x[i][0], x[i][1], x[i][2], x[i][3]};
-                __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(args.S + tile + (size_t)(i * NTS + tid) * VEC));
+                __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(args.S + tile + (size_t)Sh::offset(i, tid)));
             }
             sums([&](int i, float *xo) {
 #pragma unroll
