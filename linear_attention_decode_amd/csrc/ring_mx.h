@@ -97,20 +97,23 @@ struct MxRing {
         const int t0 = count - W;
         float sw[WM], ab[WM];
         float prod = dtj, run = 1.f;
+        // entries before the window (a loop over the wave-uniform count),
+        // then the window's W entries, each taking its weights once formed
+        for (int m = 0; m < t0; ++m) {
+            const float am = bcast(aj, m);
+            if (m > lane) prod *= am;
+            run *= am;
+        }
 #pragma unroll
-        for (int w = 0; w < WM; ++w) sw[w] = ab[w] = 0.f;
-#pragma unroll
-        for (int m = 0; m < LM; ++m) {
-            if (m < count) {
+        for (int w = 0; w < WM; ++w) {
+            sw[w] = ab[w] = 0.f;
+            if (w < W) {
+                const int m = t0 + w;
                 const float am = bcast(aj, m);
                 if (m > lane) prod *= am;
                 run *= am;
-#pragma unroll
-                for (int w = 0; w < WM; ++w)
-                    if (m == t0 + w) {
-                        sw[w] = prod;
-                        ab[w] = run;
-                    }
+                sw[w] = prod;
+                ab[w] = run;
             }
         }
         if (lane >= j0 && lane < j0 + 16) {
