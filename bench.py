@@ -261,9 +261,10 @@ VERIFY_WIDE_SOURCES = ["linear_attention_decode_amd/csrc/verify_wide.hip",
     "linear_attention_decode_amd/csrc/internal.h"]
 
 
-def read_ceiling_gbs(nbytes=1 << 30, reps=7):
+def read_ceiling_gbs(nbytes=1 << 30, reps=96):
     """Read-bandwidth ceiling measured by the library's stream probe (mode 0:
-    32 KiB tiles, all loads in flight, non-temporal), median of reps."""
+    32 KiB tiles, all loads in flight, non-temporal), median of reps passes
+    (96 x 1 GiB: about 15 ms of sustained reads)."""
     import torch
     import linear_attention_decode_amd as lad
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -439,7 +440,7 @@ def bench_decode(args):
     torch.cuda.empty_cache()
 
     eager_out = None if args.no_eager else _bench_eager(args, w, pool, y)
-    ceiling = read_ceiling_gbs()
+    ceiling = args.read_ceiling
 
     window_replay = sum(decode_bytes(w, c, 1, st_bytes) for c in range(1, L + 1)) \
         + flush_bytes(w, L, 0 if st_bytes == 4 else st_bytes) \
@@ -1035,6 +1036,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         torch.cuda.empty_cache()
+    # The decode workload reports its kernel against the chip's measured read
+    # ceiling.  That probe runs first, before the layer is built: the timed
+    # steps then start on a GPU that has been streaming for some milliseconds,
+    # as it is in service, instead of paying the clocks' ramp from idle
+    # (about 4 us a step over the first hundred steps of a cold start).
+    args.read_ceiling = read_ceiling_gbs() if args.workload == "decode" else None
     out = {"decode": bench_decode, "verify": bench_verify, "dual": bench_dual,
            "stacked": bench_stacked, "stacked-latency": bench_stacked_latency, "gdn": bench_gdn}[args.workload](args)
     print(json.dumps(out))
