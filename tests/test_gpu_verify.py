@@ -57,6 +57,12 @@ def test_verify_workload():
     (64, 128, "f32", 32, 7, 2, 16, 4),
     (128, 128, "bf16", 9, 6, 2, 4, 2),
     (64, 128, "bf16", 3, 1, 4, 16, 8),
+    # register sums with several pieces of a row a lane: 64-column rows (two
+    # pieces), 128 x 128 tiles (512 streaming threads), float32 io
+    (64, 64, "bf16", 8, 3, 3, 4, 2),
+    (64, 64, "f32", 9, 5, 2, 6, 3),
+    (128, 128, "bf16", 8, 4, 2, 4, 2),
+    (128, 128, "f32", 7, 2, 3, 2, 1),
 ])
 def test_verify_ragged(P, N, io, L, W, B, H, G):
     w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L,

@@ -43,6 +43,7 @@ def _layer(w, **kw):
     (64, 64, "bf16", 12, 6, 4, 4, 2, None),       # matrix cores, 256-byte rows
     (16, 16, "bf16", 4, 3, 4, 6, 2, None),        # W close to L: folds most rounds
     (64, 64, "bf16", 8, 1, 5, 4, 2, None),
+    (64, 64, "bf16", 9, 3, 4, 6, 3, None),        # register sums, two pieces of a row a lane
     (128, 128, "bf16", 12, 4, 2, 12, 3, None),
     (64, 128, "bf16", 5, 5, 3, 4, 1, None),       # W = L: every round folds
     (64, 128, "f32", 16, 5, 3, 8, 2, None),       # f32 io: the calls in turn
