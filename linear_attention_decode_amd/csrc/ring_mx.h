@@ -107,7 +107,7 @@ struct MxRing {
 #pragma unroll
         for (int w = 0; w < WM; ++w) {
             sw[w] = ab[w] = 0.f;
-            if (w < W) {
+            if (w < W && t0 + w >= 0) {   // (count >= W at every call: the second test never fails)
                 const int m = t0 + w;
                 const float am = bcast(aj, m);
                 if (m > lane) prod *= am;
