@@ -70,10 +70,12 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
         const int need = args.min_count > 1 ? args.min_count : 1;
         if (count < need) return;  // uniform: nothing to fold for this sequence
     }
-    // Arrival of this workgroup at its group's counter (after its pointer
-    // read); the last arrival of the sequence moves base at the very end.
+    // Every wavefront arrives at its group's counter right after its own
+    // pointer read (the counter expects one arrival per wavefront), so no
+    // wavefront can read a base the sequence's last arrival has moved; that
+    // last arrival moves base at its very end.
     int prev = -1;
-    if (tid == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
+    if (lane == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
 
     const int bmod = base % L;
     auto slot = [&](int j) { return ring_slot(bmod, j, L); };   // entry j (0-based) of the ring
@@ -262,9 +264,9 @@ __global__ __launch_bounds__((FlushShape<P, N>::NT)) void flush_kernel(FlushArgs
     }
     }
 
-    // Last workgroup of its group: the group arrives at the sequence's
-    // counter; the last group means every workgroup of the sequence has read base.
-    if (tid == 0 && prev == r.H / r.G / HC - 1) {
+    // Last wavefront of its group: the group arrives at the sequence's
+    // counter; the last group means every wavefront of the sequence has read base.
+    if (lane == 0 && prev == r.H / r.G / HC * (NT / 64) - 1) {
         int32_t *seq = args.sync + (size_t)b * (r.G + 1) * kSyncStride;
         atomicExch(seq + (size_t)g * kSyncStride, 0);
         if (atomicAdd(seq + (size_t)r.G * kSyncStride, 1) == r.G - 1) {

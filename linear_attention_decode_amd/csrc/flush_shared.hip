@@ -82,8 +82,10 @@ __global__ __launch_bounds__(P / 16 * 64) void flush_shared_kernel(FlushArgs arg
     const int pos = r.pos[b];
     const int count = pos - base;
     if (count < (args.min_count > 1 ? args.min_count : 1)) return;   // uniform: nothing to fold
+    // every wavefront arrives at its group's counter right after its own
+    // pointer read (one arrival per wavefront)
     int prev = -1;
-    if (tid == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
+    if (lane == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
 
     const int p = 16 * wave + lr;
     const int bmod = base % L;
@@ -347,9 +349,9 @@ __global__ __launch_bounds__(P / 16 * 64) void flush_shared_kernel(FlushArgs arg
         }
     }
 
-    // Last workgroup of its group: the group arrives at the sequence's
-    // counter; the last group means every workgroup of the sequence has read base.
-    if (tid == 0 && prev == r.H / r.G / HC - 1) {
+    // Last wavefront of its group: the group arrives at the sequence's
+    // counter; the last group means every wavefront of the sequence has read base.
+    if (lane == 0 && prev == r.H / r.G / HC * NW - 1) {
         int32_t *seq = args.sync + (size_t)b * (r.G + 1) * kSyncStride;
         atomicExch(seq + (size_t)g * kSyncStride, 0);
         if (atomicAdd(seq + (size_t)r.G * kSyncStride, 1) == r.G - 1) {

@@ -646,9 +646,11 @@ __global__ __launch_bounds__((GdnFoldShape<P, N>::NT)) void gdn_fold_kernel(GdnF
         count = pos - base;
         if (count < (args.min_count > 1 ? args.min_count : 1)) return;   // uniform: nothing to fold
     }
+    // every wavefront of a fold arrives at its group's counter right after
+    // its own pointer read (one arrival per wavefront)
     int prev = -1;
     if constexpr (!EMIT) {
-        if (tid == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
+        if ((tid & 63) == 0) prev = atomicAdd(&args.sync[((size_t)b * (r.G + 1) + g) * kSyncStride], 1);
     }
 
     // this lane's pieces of its rows (element offsets within the head's tile)
@@ -839,9 +841,9 @@ __global__ __launch_bounds__((GdnFoldShape<P, N>::NT)) void gdn_fold_kernel(GdnF
             for (int i = 0; i < RPL; ++i) args.y[bh * P + row0 + RSTEP * i] = yq[i];
         }
     } else {
-        // last workgroup of its group: the group arrives at the sequence's
-        // counter; the last group means every workgroup has read base
-        if (tid == 0 && prev == r.H / r.G - 1) {
+        // last wavefront of its group: the group arrives at the sequence's
+        // counter; the last group means every wavefront has read base
+        if ((tid & 63) == 0 && prev == r.H / r.G * (NT / 64) - 1) {
             int32_t *seq = args.sync + (size_t)b * (r.G + 1) * kSyncStride;
             atomicExch(seq + (size_t)g * kSyncStride, 0);
             if (atomicAdd(seq + (size_t)r.G * kSyncStride, 1) == r.G - 1) {
