@@ -2,8 +2,11 @@
 // launch configuration and the handle.  Every compute step runs in the
 // kernels of decode*.hip (output-only decode and register verify),
 // verify_wide.hip (matrix-core verify), step.hip and step_copy.hip (the
-// fused decode step), verify_step.hip (the fused speculative round),
-// flush.hip, ring.hip (append, rollback, fills), eager.hip and probe.hip.
+// fused decode step, one layer or stacked layers), verify_step.hip (the
+// fused speculative round), flush.hip and flush_shared.hip (the folds of a
+// float32 master and of a shared low-precision checkpoint), gdn.hip (Gated
+// DeltaNet layers), ring.hip (append, rollback, fills), eager.hip and
+// probe.hip.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
