@@ -484,7 +484,9 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
 #pragma unroll
             for (int i = 0; i < ITER; ++i) {
                 f32x4 o = {x[i][0], x[i][1], x[i][2], x[i][3]};
-                __builtin_nontemporal_store(o, reinterpret_cast<f32x4 *>(args.S + tile + (size_t)Sh::offset(i, tid)));
+                // (plain stores: with 8-row store instructions they measured
+                // faster than non-temporal ones, 133-135 against 137 us a round)
+                *reinterpret_cast<f32x4 *>(args.S + tile + (size_t)Sh::offset(i, tid)) = o;
             }
             sums([&](int i, float *xo) {
 #pragma unroll
