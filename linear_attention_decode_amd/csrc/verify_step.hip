@@ -329,7 +329,8 @@ __device__ __forceinline__ void verify_step_streamer_mx(const StepArgs &args, in
 }
 
 // Waves per SIMD to ask the register allocator for: 8 (64 registers) for the
-// 64 x 128 tile, which then fits with a few spilled words (measured faster
+// 64 x 128 tile, which then fits: 61-63 registers for W = 2..5 (row pieces),
+// a few spilled words for W = 1 and the matrix-core windows (measured faster
 // than 67 registers at 7 waves); the other tiles fit or spill too much.
 template <int P, int N>
 constexpr int vs_waves() { return P == 64 && N == 128 ? 8 : 1; }
