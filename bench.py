@@ -618,7 +618,9 @@ def bench_verify(args):
     """Speculative verify: B=256, H=64, G=8, P=64, N=128, L=16, W=5 drafts per
     round (--window: up to 16), accepted drafts ~ Uniform{0..W}; each round =
     flush(L-W+1), append(W), verify(W) (one fused launch with --api step,
-    three launches with --api calls or W > 8), then rollback(W - accepted).
+    three launches with --api calls or W > 8), then rollback(W - accepted)
+    (with --api step that rollback rides on the next round's launch,
+    replay_rollback_verify_step).
     The eager baseline drafts with W per-token steps into snapshots and
     restores the accepted one."""
     import torch
@@ -642,12 +644,18 @@ def bench_verify(args):
     def round_(r, ev=None):
         drafts = (win["q"][r], win["k"][r], win["v"][r], win["dt"][r], win["a"][r])
         if api == "step":
-            # one fused launch: fold if due, append the drafts, score them
+            # one fused launch: the previous round's rollback, fold if due,
+            # append the drafts, score them (this round's rollback rides on
+            # the next launch; the last one is a plain rollback)
             if ev is not None:
                 ev[0].record(stream)
-            layer.verify_step(W, *drafts, y, flush_at=L - W + 1)
+            if r == 0:
+                layer.verify_step(W, *drafts, y, flush_at=L - W + 1)
+            else:
+                layer.rollback_verify_step(nrej[r - 1], W, *drafts, y, flush_at=L - W + 1)
             if ev is not None:
                 ev[1].record(stream)
+            return
         else:
             layer.flush(L - W + 1)
             layer.append(W, *drafts)
@@ -669,6 +677,8 @@ def bench_verify(args):
     t0 = time.perf_counter()
     for k in range(R):
         round_(WU + k, evs.get(k))
+    if api == "step":
+        layer.rollback(nrej[WU + R - 1])   # the last round's rollback, inside the timed region
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     assert layer.get_error()[0] == 0

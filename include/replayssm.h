@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define REPLAY_ABI_VERSION 7
+#define REPLAY_ABI_VERSION 8
 
 typedef enum {
     REPLAY_OK = 0,
@@ -315,6 +315,23 @@ replay_status replay_step_static(replay_handle *h, const void *q, const void *k,
 replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, const void *k,
                                  const void *v, const float *dt, const float *a, float *y,
                                  int32_t flush_at, void *stream);
+
+/* The previous round's rollback followed by the next speculative round
+   (page "ReplaySSM: Cachear Inputs, No Estado", section "Rollback": the
+   rejected drafts are dropped by moving the pointer back; section
+   "Paralelismo" for the round): equivalent to replay_rollback(n_reject) then
+   replay_verify_step(W, ...), bit for bit, error bits included (an
+   out-of-range n_reject[b] flags ROLLBACK_RANGE and leaves that sequence's
+   pointer where it was, then the round runs).  n_reject: device int32 [B],
+   caller-owned, read before any pointer moves.  Where replay_verify_step is
+   one kernel launch, this is the same launch (its ring wavefronts apply the
+   rollback to the pointer they read), which spares a serving loop the
+   rollback kernel between rounds; elsewhere the rollback kernel runs first.
+   The last round's rollback is a plain replay_rollback.  n_reject NULL or
+   misaligned: REPLAY_ERR_INVALID_ARG, nothing enqueued. */
+replay_status replay_rollback_verify_step(replay_handle *h, const int32_t *n_reject, int32_t W,
+                                          const void *q, const void *k, const void *v, const float *dt,
+                                          const float *a, float *y, int32_t flush_at, void *stream);
 
 /* The host-side count bounds that let replay_flush skip launches (see
    replay_flush) hold only while pos and base change through this library.

@@ -21,7 +21,7 @@ __all__ = [
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
     "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_step_layers", "replay_step_static",
-    "replay_verify_step", "replay_set_flush_skipping", "replay_get_error",
+    "replay_verify_step", "replay_rollback_verify_step", "replay_set_flush_skipping", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 ]
 
@@ -35,7 +35,7 @@ EXPORTS = (
     "replay_status_string", "replay_abi_version", "replay_buffer_bytes", "replay_init",
     "replay_destroy", "replay_load_checkpoint", "replay_append", "replay_decode",
     "replay_verify", "replay_rollback", "replay_flush", "replay_step", "replay_step_layers", "replay_step_static",
-    "replay_verify_step", "replay_set_flush_skipping", "replay_get_error",
+    "replay_verify_step", "replay_rollback_verify_step", "replay_set_flush_skipping", "replay_get_error",
     "replay_eager_step", "replay_eager_select", "replay_stream_probe",
 )
 
@@ -81,6 +81,7 @@ def _load():
     L.replay_flush.argtypes = [_VP, _I32, _VP]
     L.replay_step.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
     L.replay_verify_step.argtypes = [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
+    L.replay_rollback_verify_step.argtypes = [_VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
     L.replay_get_error.argtypes = [_VP, ctypes.POINTER(_I32), _VP, _VP]
     L.replay_set_flush_skipping.argtypes = [_VP, _I32, _VP]
     L.replay_step_static.argtypes = [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]
@@ -188,6 +189,11 @@ def replay_step_layers(handles, q, k, v, dt, a, y, flush_at, stream=None):
 def replay_step_static(h, q, k, v, dt, a, y, flush_at, stream=None):
     _check(lib.replay_step_static(h, _ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a), _ptr(y), int(flush_at),
                                   _stream(stream)), "replay_step_static")
+
+
+def replay_rollback_verify_step(h, n_reject, W, q, k, v, dt, a, y, flush_at, stream=None):
+    _check(lib.replay_rollback_verify_step(h, _ptr(n_reject), W, _ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a),
+                                           _ptr(y), flush_at, _stream(stream)), "replay_rollback_verify_step")
 
 
 def replay_verify_step(h, W, q, k, v, dt, a, y, flush_at, stream=None):
@@ -311,6 +317,11 @@ class ReplayLayer:
         """Fold if due (count >= flush_at, default L - W + 1), append W drafts, score them."""
         fa = self.cfg.ring_len - W + 1 if flush_at is None else flush_at
         replay_verify_step(self.h, W, q, k, v, dt, a, y, fa, stream)
+
+    def rollback_verify_step(self, n_reject, W, q, k, v, dt, a, y, flush_at=None, stream=None):
+        """rollback(n_reject), then verify_step(W, ...), fused where the round is one launch."""
+        fa = self.cfg.ring_len - W + 1 if flush_at is None else flush_at
+        replay_rollback_verify_step(self.h, n_reject, W, q, k, v, dt, a, y, fa, stream)
 
     def load_checkpoint(self, s_src, stream=None):
         replay_load_checkpoint(self.h, s_src, stream)

@@ -410,6 +410,7 @@ static StepArgs step_args(replay_handle *h, const void *q, const void *k, const 
     sa.copy = h->bufs.s_copy;
     sa.copy_scale = h->bufs.s_scale;
     sa.copy_st = c.read_copy == REPLAY_NONE ? -1 : state_kind(c.read_copy);
+    sa.n_reject = nullptr;
     return sa;
 }
 
@@ -519,26 +520,46 @@ replay_status replay_step_layers(replay_handle *const *layers, int32_t n, const 
     return from_hip(e);
 }
 
-replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
-                                 const float *dt, const float *a, float *y, int32_t flush_at, void *stream) {
+// One speculative round, after the rollback n_reject when it is given: in
+// the fused kernels the rollback is applied to the pointer they read; else
+// the rollback kernel runs first and the round's calls follow.
+static replay_status verify_round_impl(replay_handle *h, const int32_t *n_reject, int32_t W, const void *q,
+                                       const void *k, const void *v, const float *dt, const float *a, float *y,
+                                       int32_t flush_at, void *stream) {
     if (!h || !h->bufs.sync || !step_args_ok(q, k, v, dt, a, y)) return REPLAY_ERR_INVALID_ARG;
+    if (n_reject && !aligned4(n_reject)) return REPLAY_ERR_INVALID_ARG;
     const replay_config &c = h->cfg;
     if (W < 1 || W > kMaxWideWindow || W > c.ring_len) return REPLAY_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     note_capture(h, s);
-    const StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, W, h->bufs.sync);
-    if (c.read_copy != REPLAY_NONE && !c.shared_lowp && c.rule == REPLAY_RULE_MAMBA2 &&
-        verify_step_copy_fused(c.head_dim, c.state_dim, sa)) {
-        // an e4m3 or FP4 read copy: fold, copy rewrite, append and verify in one launch
-        const hipError_t e = launch_verify_step_copy(c.head_dim, c.state_dim, sa, s);
+    StepArgs sa = step_args(h, q, k, v, dt, a, y, flush_at, W, h->bufs.sync);
+    sa.n_reject = n_reject;
+    const bool copy_fused = c.read_copy != REPLAY_NONE && !c.shared_lowp && c.rule == REPLAY_RULE_MAMBA2 &&
+                            verify_step_copy_fused(c.head_dim, c.state_dim, sa);
+    const bool fused = c.read_copy == REPLAY_NONE && c.rule == REPLAY_RULE_MAMBA2 &&
+                       verify_step_fused(c.head_dim, c.state_dim, sa);
+    if (copy_fused || fused) {
+        // one launch: (rollback,) fold if due, append the drafts, score them;
+        // with an e4m3 or FP4 read copy the fold also rewrites the copy
+        const hipError_t e = copy_fused ? launch_verify_step_copy(c.head_dim, c.state_dim, sa, s)
+                                        : launch_verify_step(c.head_dim, c.state_dim, sa, s);
         if (e != hipSuccess) {
             h->bound.unknown();
             return REPLAY_ERR_HIP;
         }
+        if (n_reject) h->bound.rollback();
         h->bound.verify_round(flush_at, W);
         return REPLAY_OK;
     }
-    if (c.read_copy != REPLAY_NONE || c.rule != REPLAY_RULE_MAMBA2 || !verify_step_fused(c.head_dim, c.state_dim, sa)) {
+    {
+        if (n_reject) {
+            h->bound.rollback();
+            const hipError_t e = launch_rollback(ring_view(h), h->bufs.pos, n_reject, s);
+            if (e != hipSuccess) {
+                h->bound.unknown();
+                return REPLAY_ERR_HIP;
+            }
+        }
         // the flush, append and verify kernels in turn
         replay_status st = run_flush(h, nullptr, flush_at, s, h->bufs.sync);
         if (st != REPLAY_OK) return st;
@@ -546,13 +567,18 @@ replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, con
         if (st != REPLAY_OK) return st;
         return run_verify(h, W, y, s);
     }
-    const hipError_t e = launch_verify_step(c.head_dim, c.state_dim, sa, s);
-    if (e != hipSuccess) {
-        h->bound.unknown();
-        return REPLAY_ERR_HIP;
-    }
-    h->bound.verify_round(flush_at, W);
-    return REPLAY_OK;
+}
+
+replay_status replay_verify_step(replay_handle *h, int32_t W, const void *q, const void *k, const void *v,
+                                 const float *dt, const float *a, float *y, int32_t flush_at, void *stream) {
+    return verify_round_impl(h, nullptr, W, q, k, v, dt, a, y, flush_at, stream);
+}
+
+replay_status replay_rollback_verify_step(replay_handle *h, const int32_t *n_reject, int32_t W, const void *q,
+                                          const void *k, const void *v, const float *dt, const float *a, float *y,
+                                          int32_t flush_at, void *stream) {
+    if (!n_reject) return REPLAY_ERR_INVALID_ARG;
+    return verify_round_impl(h, n_reject, W, q, k, v, dt, a, y, flush_at, stream);
 }
 
 replay_status replay_set_flush_skipping(replay_handle *h, int32_t enable, void *stream) {

@@ -84,6 +84,7 @@ struct StepArgs {
     const void *copy;                 // low-precision checkpoint copy the step reads (copy modes)
     const void *copy_scale;           // its scales: e4m3 float [B][H], FP4 E8M0 bytes [B][H][P*N/32]
     int32_t copy_st;                  // StateKind of the copy (ST_BF16, ST_FP8, ST_FP4)
+    const int32_t *n_reject;          // verify round only: [B] rollback applied first, or null
 };
 
 // n layers of one shape stepped in one launch (step_layers_kernel); passed

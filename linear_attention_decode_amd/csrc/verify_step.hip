@@ -507,7 +507,18 @@ __global__ __launch_bounds__((StepShape<P, N>::NTS + 128)) __attribute__((amdgpu
       }
     } else {
         const int base = args.base[b];
-        const int pos = args.pos[b];
+        int pos = args.pos[b];
+        if (args.n_reject) {
+            // the previous round's rollback first, as replay_rollback applies
+            // it (page "ReplaySSM: Cachear Inputs, No Estado", "Rollback":
+            // the pointer moves back); out of range: flagged, pointer kept
+            const int r = args.n_reject[b];
+            if (r < 0 || r > pos - base) {
+                if (rw == 0 && lane == 0) raise_seq_error(args.err, b, REPLAY_SEQERR_ROLLBACK_RANGE);
+            } else {
+                pos -= r;
+            }
+        }
         const int cold = pos - base;
         const int need = args.flush_at > 1 ? args.flush_at : 1;
         const bool fold = cold >= need;
@@ -807,7 +818,18 @@ __attribute__((amdgpu_waves_per_eu(8))) void verify_step_copy_kernel(StepArgs ar
         }
     } else {
         const int base = args.base[b];
-        const int pos = args.pos[b];
+        int pos = args.pos[b];
+        if (args.n_reject) {
+            // the previous round's rollback first, as replay_rollback applies
+            // it (page "ReplaySSM: Cachear Inputs, No Estado", "Rollback":
+            // the pointer moves back); out of range: flagged, pointer kept
+            const int r = args.n_reject[b];
+            if (r < 0 || r > pos - base) {
+                if (rw == 0 && lane == 0) raise_seq_error(args.err, b, REPLAY_SEQERR_ROLLBACK_RANGE);
+            } else {
+                pos -= r;
+            }
+        }
         const int cold = pos - base;
         const int need = args.flush_at > 1 ? args.flush_at : 1;
         const bool fold = cold >= need;

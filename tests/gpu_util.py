@@ -157,14 +157,36 @@ def assert_f32(y_gpu: np.ndarray, y_ref: np.ndarray, y_abs: np.ndarray, tol: flo
 
 
 def run_verify(layer, w: synth.Workload, dev: DevInputs, R: int, W: int, accept: np.ndarray, model=None,
-               fused: bool = False):
+               fused: bool = False, rollback_fused: bool = False, nrej=None):
     """Speculative rounds: flush(L-W+1); append(W drafts); verify(W) -- as
     three calls, or as one replay_verify_step with fused=True -- then
-    rollback(W - accepted).  Round r drafts tokens rW..rW+W-1.
+    rollback(W - accepted).  Round r drafts tokens rW..rW+W-1.  With
+    rollback_fused=True round r > 0 is one replay_rollback_verify_step
+    carrying round r-1's rollback, and a plain rollback ends the run.
+    nrej (int32 [R][B]) overrides the rejected counts W - accept.
     Returns y [R][B][W][H][P] (device)."""
     B, H, P, L = w.batch, w.heads, w.head_dim, w.ring_len
     y = torch.empty((R, B, W, H, P), dtype=torch.float32, device=DEV)
-    nrej = torch.from_numpy((W - accept).astype(np.int32)).to(DEV)
+    nrej_np = (W - accept).astype(np.int32) if nrej is None else np.asarray(nrej, dtype=np.int32)
+    nrej = torch.from_numpy(nrej_np).to(DEV)
+    if rollback_fused:
+        for rd in range(R):
+            if rd == 0:
+                layer.verify_step(W, *dev.window(0, W), y[0], flush_at=L - W + 1)
+            else:
+                layer.rollback_verify_step(nrej[rd - 1], W, *dev.window(rd * W, W), y[rd], flush_at=L - W + 1)
+            if model is not None:
+                if rd > 0:
+                    model.rollback(nrej_np[rd - 1])
+                model.flush(L - W + 1)
+                model.append(W)
+                model.read(W)
+                check_ring(layer, model, f"round {rd}")
+        layer.rollback(nrej[R - 1])
+        if model is not None:
+            model.rollback(nrej_np[R - 1])
+            check_ring(layer, model, "last rollback")
+        return y
     for rd in range(R):
         if fused:
             layer.verify_step(W, *dev.window(rd * W, W), y[rd], flush_at=L - W + 1)
@@ -177,6 +199,6 @@ def run_verify(layer, w: synth.Workload, dev: DevInputs, R: int, W: int, accept:
             model.flush(L - W + 1)
             model.append(W)
             model.read(W)
-            model.rollback(W - accept[rd])
+            model.rollback(nrej_np[rd])
             check_ring(layer, model, f"round {rd}")
     return y

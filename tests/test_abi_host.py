@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lad):
 
 
 def test_version_and_status_strings(lad):
-    assert lad.replay_abi_version() == 7
+    assert lad.replay_abi_version() == 8
     for s, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported"), (3, "HIP"), (4, "static counters")]:
         assert text in lad.replay_status_string(s)
     assert lad.replay_status_string(99) == "unknown status"

@@ -86,6 +86,53 @@ def test_verify_step_equals_calls(P, N, io, L, W, B, H, G, rc):
     calls.close()
 
 
+@pytest.mark.parametrize("P,N,io,L,W,B,H,G,rc,bad", [
+    (64, 128, "bf16", 16, 5, 6, 16, 4, None, False),   # the float32 round: one launch
+    (64, 128, "bf16", 16, 5, 6, 16, 4, None, True),    # with an out-of-range rollback
+    (128, 128, "bf16", 12, 4, 2, 12, 3, None, False),
+    (64, 128, "bf16", 16, 5, 6, 16, 4, "fp8", True),   # e4m3 copy: one launch
+    (64, 64, "bf16", 12, 4, 3, 4, 2, "fp4", False),    # FP4 copy: one launch
+    (64, 128, "bf16", 16, 5, 3, 8, 2, "bf16", True),   # bf16 copy: rollback kernel, then the calls
+    (64, 128, "bf16", 32, 6, 3, 8, 2, None, False),    # L > 16: rollback kernel, then the calls
+])
+def test_rollback_verify_step_equals_calls(P, N, io, L, W, B, H, G, rc, bad):
+    """replay_rollback_verify_step(n_reject of round r-1, round r) equals
+    replay_rollback then the round's three calls, bit for bit: outputs,
+    checkpoint, copy and scales, pointers, ring slots and error bits (with
+    bad=True one sequence's rollback is out of range in one round: flagged,
+    its pointer kept, the round run); pointers checked against the ring
+    model after every launch."""
+    w = synth.Workload(batch=B, heads=H, groups=G, head_dim=P, state_dim=N, ring_len=L, io_dtype=io,
+                       config=synth.CONFIG_ID["misc"], layer=170 + P + L + W)
+    R = 12
+    gu.note(f"rollback_verify_step vs calls {w} W={W} copy={rc} bad={bad}")
+    accept = synth.accept_counts(w, R, W)
+    nrej = (W - accept).astype(np.int32)
+    if bad:
+        nrej[4, 1] = L + 1   # more than any count
+    dev = gu.DevInputs(w, 0, R * W)
+    kw = {} if rc is None else {"read_copy": rc}
+    fused, calls = _layer(w, **kw), _layer(w, **kw)
+    model = oring.RingModel(w.batch, w.ring_len)
+    y_f = gu.run_verify(fused, w, dev, R, W, accept, model=model, rollback_fused=True, nrej=nrej)
+    y_c = gu.run_verify(calls, w, dev, R, W, accept, nrej=nrej)
+    torch.cuda.synchronize()
+    e_f, s_f = fused.get_error()
+    e_c, s_c = calls.get_error()
+    assert e_f == e_c and np.array_equal(np.asarray(s_f), np.asarray(s_c))
+    assert (e_f != 0) == bad
+    assert np.array_equal(y_f.cpu().numpy(), y_c.cpu().numpy())
+    for name in ("s_master", "pos", "base") + RING:
+        if fused.t[name] is not None:
+            assert torch.equal(fused.t[name], calls.t[name]), name
+    if rc is not None:
+        assert torch.equal(fused.t["s_copy"], calls.t["s_copy"])
+        if fused.t["s_scale"] is not None:
+            assert torch.equal(fused.t["s_scale"], calls.t["s_scale"])
+    fused.close()
+    calls.close()
+
+
 def test_verify_step_workload():
     """B=256 H=64 G=8 P=64 N=128 L=16, W=5, accepted drafts ~ Uniform{0..5},
     128 fused rounds (the launch sequence bench.py times); 6 sampled
