@@ -160,3 +160,53 @@ def test_graph_verify_rounds(rc, W, rule):
     del graph
     e.close()
     g.close()
+
+
+@pytest.mark.parametrize("rc,W", [(None, 4), (None, 6), ("fp8", 4)])
+def test_graph_rollback_verify_rounds(rc, W):
+    """replay_rollback_verify_step in a graph: each replay rolls back the
+    previous round (the reject counts change per replay) and runs the next
+    round in one launch (register sums at W = 4, matrix cores at W = 6, an
+    e4m3 copy's round); an eager twin runs replay_rollback then
+    replay_verify_step.  Outputs, pointers and error bits equal after every
+    replay, checkpoints after a final flush."""
+    R = 10
+    gu.note(f"graph of rollback + verify rounds copy={rc} W={W}")
+    w = _workload(9)
+    B, H, P = w.batch, w.heads, w.head_dim
+    dev = _inputs(w, 0, (R + 1) * W, "mamba2")
+    e, g = _pair(w, rc, "mamba2")
+    accept = np.random.default_rng(5).integers(0, W + 1, size=(R + 1, B))
+    nrej = [torch.from_numpy((W - a).astype(np.int32)).to(gu.DEV) for a in accept]
+    ye = torch.empty((B, W, H, P), dtype=torch.float32, device=gu.DEV)
+    yg = torch.empty_like(ye)
+    fa = L - W + 1
+    for x in (e, g):   # one eager round on both; its rollback is pending
+        x.verify_step(W, *dev.window(0, W), ye if x is e else yg, flush_at=fa)
+    static = tuple(x.clone() for x in dev.window(W, W))
+    s_rej = nrej[0].clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.rollback_verify_step(s_rej, W, *static, yg, flush_at=fa)
+    for r in range(1, R + 1):
+        for dst, src in zip(static, dev.window(r * W, W)):
+            dst.copy_(src)
+        s_rej.copy_(nrej[r - 1])
+        graph.replay()
+        e.rollback(nrej[r - 1])
+        e.verify_step(W, *dev.window(r * W, W), ye, flush_at=fa)
+        torch.cuda.synchronize()
+        assert torch.equal(ye, yg), r
+        _same_state(e, g, r)
+    for x in (e, g):
+        x.rollback(nrej[R])
+        x.flush(1)
+    torch.cuda.synchronize()
+    _same_state(e, g, "final flush")
+    for name in ("s_master", "s_copy", "s_scale"):
+        if e.t[name] is not None:
+            assert torch.equal(e.t[name], g.t[name]), name
+    del graph
+    e.close()
+    g.close()
